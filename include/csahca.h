@@ -1,0 +1,264 @@
+/*
+ * csahca.h -- C ABI of the MI355X (gfx950) library for compressed sparse
+ * attention (CSA) and heavily compressed attention (HCA), prefill and decode,
+ * over a paged compressed-KV cache.
+ *
+ * The method is the one described in the DeepSeek-V4 technical-report
+ * walkthrough book (slop-6tp.pages.dev/papers-html-argon/dsv4.html, "dsv4
+ * book" below), chapters 5-8.  Each entry point cites the passage that defines
+ * the operation it runs.
+ *
+ * Conventions shared by every call:
+ *  - Pointers are DEVICE pointers owned by the caller unless a comment says
+ *    "host".  The library never allocates memory: scratch space is passed in
+ *    (`ws`, `ws_bytes`) after asking the matching *_workspace function.
+ *  - `stream` is a hipStream_t passed as void*; every call only enqueues work
+ *    on it (no host synchronisation), so calls can be captured in HIP graphs.
+ *  - Every call returns a ca_status.  Arguments are validated on the host
+ *    before anything is launched; on error nothing is launched and
+ *    ca_last_error() (thread-local) describes the problem.
+ *  - Row-major layouts throughout.  "bf16" is bfloat16, "e4m3" is OCP FP8
+ *    E4M3 (fn variant: no infinities, max 448).
+ *  - Results are bitwise deterministic and, for decode, independent of which
+ *    other sequences share the batch.
+ */
+#ifndef CSAHCA_H
+#define CSAHCA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CA_OK = 0,
+  CA_ERR_ARG = -1,          /* null pointer, negative size, inconsistent shape */
+  CA_ERR_DTYPE = -2,        /* unsupported storage format for this argument */
+  CA_ERR_UNSUPPORTED = -3,  /* valid but not implemented (e.g. dim not a multiple of 64) */
+  CA_ERR_WORKSPACE = -4,    /* workspace too small */
+  CA_ERR_HIP = -5           /* a HIP launch failed */
+} ca_status;
+
+/* Storage formats. */
+typedef enum {
+  CA_F32 = 0,     /* float32 */
+  CA_BF16 = 1,    /* bfloat16 */
+  CA_FP8MIX = 2,  /* main-KV record: e4m3 content channels + bf16 rotary channels (see ca_cache) */
+  CA_E4M3 = 3     /* indexer-key page: e4m3 codes + one fp32 power-of-two scale per entry */
+} ca_format;
+
+/* Thread-local description of the last error (empty string if none). */
+const char* ca_last_error(void);
+
+/* ------------------------------------------------------------------------ */
+/* Paged compressed cache (dsv4 book Ch.5 "Decode-time cache state"; Ch.8    */
+/* "V4 compressed-entry payload" and "Quantization scales and bounded tail   */
+/* buffers").  Completed entries are append-only; entry i of sequence s lives */
+/* in page page_table[s * max_pages + i / page_size], slot i % page_size.     */
+/*                                                                           */
+/* Record formats (one entry = one record; a page is page_size records):     */
+/*   CA_F32    : dim float32 (stride 4*dim bytes)                            */
+/*   CA_BF16   : dim bf16   (stride 2*dim bytes)                             */
+/*   CA_FP8MIX : bytes [0, dim-R)          e4m3 codes of content channels     */
+/*               bytes [dim-R, dim+R)      bf16 rotary channels (R = rope_dim)*/
+/*               bytes [dim+R, +(dim-R)/64) int8 exponent e of each 64-channel*/
+/*                                         content tile (value = code * 2^e)  */
+/*               zero padding up to a multiple of 128 bytes (640 for 512/64). */
+/*   CA_E4M3   : indexer pages, structure of arrays: page_size*dim codes,     */
+/*               then page_size float32 scales (powers of two).              */
+/* A page table entry < 0 or >= n_pages marks a missing page: entries in it  */
+/* are never read (kernels skip them) and never written.                     */
+/* ------------------------------------------------------------------------ */
+typedef struct ca_cache {
+  int32_t format;             /* ca_format of the records in `pool` */
+  int32_t dim;                /* D (main KV) or c_I (indexer keys) */
+  int32_t rope_dim;           /* R, the rotary channels at the end of each main entry; 0 for indexer pools */
+  int32_t page_size;          /* entries per page (64 in the presets) */
+  void* pool;                 /* device, n_pages * ca_page_bytes(format, dim, rope_dim, page_size) bytes */
+  int64_t n_pages;
+  const int32_t* page_table;  /* device, [n_seqs, max_pages] int32 */
+  int32_t n_seqs;
+  int32_t max_pages;
+} ca_cache;
+
+/* Bytes of one record / one page of a pool (host helpers, no device work).
+ * Return -1 for an unsupported combination. */
+int64_t ca_record_stride(int32_t format, int32_t dim, int32_t rope_dim);
+int64_t ca_page_bytes(int32_t format, int32_t dim, int32_t rope_dim, int32_t page_size);
+
+/* ------------------------------------------------------------------------ */
+/* Entry epilogue + store (dsv4 book Ch.7 "Query and KV RMSNorm", "Partial   */
+/* RoPE and output de-rotation"; Ch.8 "V4 compressed-entry payload").        */
+/* For k in [0, n): x = src[k] (float32 [n, dim]); optionally               */
+/* x <- x / sqrt(mean(x^2) + eps) * gain; optionally rotate the last        */
+/* rope_dim channels pairwise (2p, 2p+1) by angle (pos_stride*i)*base^(-2p/R)*/
+/* with i = first + k; then encode into entry i of sequence `seq`.          */
+/* gain == NULL skips the norm.  Used to build caches directly from vectors. */
+/* ------------------------------------------------------------------------ */
+int ca_store_entries(const ca_cache* cache, int32_t seq, int64_t first, int64_t n, const float* src,
+                     const float* gain, float eps, int32_t apply_rope, double rope_base, int32_t pos_stride,
+                     void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Sequence compressor (dsv4 book Ch.5 "The four compression projections",  */
+/* "Coordinate-wise softmax pooling", "Receptive field versus compression   */
+/* stride"; Ch.7 "HCA's 128:1 non-overlapping compressor").                 */
+/* overlap = 1 (CSA): entry i, channel r = softmax over the 2m logits        */
+/*   Za[m*i+j, r] + Ba[j, r] and Zb[m*(i-1)+j, r] + Bb[j, r] (j < m) of the  */
+/*   matching Ca / Cb contents; for i = 0 the b-branch is absent.            */
+/* overlap = 0 (HCA): softmax over the m rows Za[m*i+j, r] + Ba[j, r] of Ca. */
+/* Only completed blocks are emitted.  The epilogue (RMSNorm with `gain`,    */
+/* RoPE at position ratio*i) follows when enabled, then the record encode.   */
+/* ------------------------------------------------------------------------ */
+typedef struct ca_compress_params {
+  int32_t ratio;       /* m (CSA) or m' (HCA) */
+  int32_t overlap;     /* 1: CSA overlapping 2m window, 0: disjoint blocks */
+  int32_t in_format;   /* CA_F32 or CA_BF16: storage of the projection rows */
+  int32_t apply_norm;  /* 1: RMSNorm with gain (main KV); 0: none (indexer keys) */
+  int32_t apply_rope;  /* 1: RoPE of the last rope_dim channels at position ratio*i */
+  float eps;
+  double rope_base;
+} ca_compress_params;
+
+/* Prefill: rows [L, cache->dim] of Ca, Za (and Cb, Zb when overlap) in
+ * in_format; Ba, Bb float32 [ratio, dim]; writes entries 0..floor(L/ratio)-1
+ * of sequence `seq`.  Cb, Zb, Bb may be NULL when overlap == 0. */
+int ca_compress_prefill(const ca_compress_params* p, const void* Ca, const void* Za, const void* Cb,
+                        const void* Zb, const float* Ba, const float* Bb, const float* gain, int64_t L,
+                        int32_t seq, const ca_cache* cache, void* stream);
+
+/* Decode (dsv4 book Ch.5 "Decode-time cache state": bounded tail buffers).
+ * For each sequence b: the new token at position pos[b] brings rows
+ * new_rows[b] ([narr, dim], in_format; narr = 4 for CSA in the order
+ * Ca, Cb, Za, Zb, and 2 for HCA in the order C, Z).  They are written to the
+ * float32 tail ring tail[b, pos[b] % span, :, :] ([B, span, narr, dim], span =
+ * 2m for CSA, m for HCA).  When (pos[b] + 1) % ratio == 0 the completed entry
+ * i = (pos[b] + 1) / ratio - 1 is pooled from the ring and stored in sequence
+ * b of the cache (usable from position pos[b] + 1 on). */
+int ca_compress_decode(const ca_compress_params* p, const void* new_rows, const int32_t* pos, int32_t B,
+                       float* tail, const float* Ba, const float* Bb, const float* gain, const ca_cache* cache,
+                       void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Sliding window (dsv4 book Ch.7 "The 128-token uncompressed sliding       */
+/* window"): each raw token KV row is RMSNorm-ed with `gain`, its last      */
+/* rope_dim channels rotated at the token's own position, and stored at     */
+/* window[seq, pos % W, :] (window is [S, W, dim] in win_format).  Prefill  */
+/* uses W >= L (one slot per position); decode uses a ring of W = n_win.    */
+/* ------------------------------------------------------------------------ */
+typedef struct ca_window_params {
+  int32_t dim;
+  int32_t rope_dim;
+  int32_t in_format;   /* CA_F32 or CA_BF16 raw rows */
+  int32_t win_format;  /* CA_F32 or CA_BF16 window storage */
+  float eps;
+  double rope_base;
+} ca_window_params;
+
+/* kv_raw [T, dim]; pos [T] int32 (NULL: pos = row index); seq [T] int32
+ * (NULL: every row is sequence 0). */
+int ca_window_append(const ca_window_params* p, const void* kv_raw, const float* gain, const int32_t* pos,
+                     const int32_t* seq, int32_t T, void* window, int32_t W, int32_t S, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Lightning indexer + top-k (dsv4 book Ch.6 "The lightning indexer",       */
+/* "Top-k selection and asymptotic scaling"; Ch.5 "Causal availability").   */
+/* For query row r at position t: for every block s < floor(t/m),           */
+/*   I[r, s] = sum_h w[r, h] * ReLU(qI[r, h, :] . K[s, :])                   */
+/* with K read from the indexer pool.  For CA_E4M3 pools the query is first */
+/* quantized to e4m3 with one power-of-two scale per (row, head), exactly.  */
+/* The min(k, floor(t/m)) blocks with the largest score are kept (ties: the */
+/* lower block index), written ascending to out_idx[r, :], padded with -1;  */
+/* out_cnt[r] is their number.  out_score (optional, [rows, k]) receives    */
+/* the score of each kept block; all_scores (optional, [rows,               */
+/* all_scores_stride]) receives every eligible score.                       */
+/* ------------------------------------------------------------------------ */
+typedef struct ca_index_params {
+  int32_t n_heads;   /* n_I */
+  int32_t dim;       /* c_I (must equal idx_cache->dim) */
+  int32_t ratio;     /* m */
+  int32_t k;         /* top-k */
+  int32_t q_format;  /* CA_F32 or CA_BF16 storage of qI */
+} ca_index_params;
+
+/* Workspace for either indexer call with n_rows query rows whose positions
+ * are at most max_pos. */
+size_t ca_index_topk_workspace(const ca_index_params* p, int32_t n_rows, int64_t max_pos);
+
+/* Prefill: rows are positions 0..L-1 of sequence `seq`; qI [L, n_I, c_I],
+ * w float32 [L, n_I]. */
+int ca_index_topk_prefill(const ca_index_params* p, const void* qI, const float* w, int64_t L, int32_t seq,
+                          const ca_cache* idx_cache, int32_t* out_idx, int32_t* out_cnt, float* out_score,
+                          float* all_scores, int64_t all_scores_stride, void* ws, size_t ws_bytes, void* stream);
+
+/* Decode: row b is sequence b at position pos[b] (device int32 [B]);
+ * max_pos (host) bounds every pos[b]. */
+int ca_index_topk_decode(const ca_index_params* p, const void* qI, const float* w, const int32_t* pos,
+                         int32_t B, int64_t max_pos, const ca_cache* idx_cache, int32_t* out_idx,
+                         int32_t* out_cnt, float* out_score, float* all_scores, int64_t all_scores_stride,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Core attention (dsv4 book Ch.6 "Shared key-value MQA"; Ch.7 "Dense       */
+/* attention over heavily compressed history", "The 128-token uncompressed  */
+/* sliding window", "Query and KV RMSNorm", "Partial RoPE and output        */
+/* de-rotation", "Learned attention sinks"; Ch.2 "What an attention head    */
+/* computes" for the 1/sqrt(c) logit scale).  For query row r at position t */
+/* and head h:                                                              */
+/*   q^ = RoPE_t(RMSNorm(q[r, h, :]; q_gain))                                */
+/*   X  = {compressed entries} U {window tokens max(0, t-n_win+1) .. t}      */
+/*        CSA: entries idx[r, 0..cnt[r]);  HCA: entries 0..floor(t/m')-1     */
+/*   o  = sum_x e^{scale q^.x} x / (sum_x e^{scale q^.x} + e^{sink[h]})      */
+/*   out[r, h, :] = o with its last rope_dim channels rotated by R_{-t}.     */
+/* Every entry is both key and value.  Window tokens are read as stored by  */
+/* ca_window_append.  CSA indices outside [0, floor(t/m)) or in missing     */
+/* pages are skipped.  lse (optional, float32 [rows, n_heads]) receives     */
+/* log(sum_x e^{scale q^.x} + e^{sink}).                                   */
+/* ------------------------------------------------------------------------ */
+typedef struct ca_attend_params {
+  int32_t n_heads;
+  int32_t dim;         /* D (must equal kv->dim) */
+  int32_t rope_dim;    /* R */
+  int32_t n_win;
+  int32_t q_format;    /* CA_F32 or CA_BF16 */
+  int32_t win_format;  /* CA_F32 or CA_BF16 */
+  int32_t out_format;  /* CA_F32 or CA_BF16 */
+  float scale;         /* logit scale, 1/sqrt(D) */
+  float eps;           /* RMSNorm eps of the query */
+  double rope_base;
+} ca_attend_params;
+
+/* Workspace for an attention call over n_rows rows whose positions are at
+ * most max_pos; k = top-k for CSA, 0 for HCA; ratio = m or m'. */
+size_t ca_attend_workspace(const ca_attend_params* p, int32_t n_rows, int64_t max_pos, int32_t k, int32_t ratio);
+
+/* CSA prefill: q [L, n_heads, D]; idx [L, k], cnt [L]; window [1, W, D]. */
+int ca_csa_attend_prefill(const ca_attend_params* p, const void* q, const float* q_gain, const ca_cache* kv,
+                          int32_t seq, const int32_t* idx, const int32_t* cnt, int32_t k, int32_t ratio,
+                          const void* window, int32_t W, const float* sink, int64_t L, void* out, float* lse,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* CSA decode: row b is sequence b at position pos[b]; q [B, n_heads, D];
+ * idx [B, k], cnt [B]; window ring [B, W, D]; max_pos (host) bounds pos. */
+int ca_csa_attend_decode(const ca_attend_params* p, const void* q, const float* q_gain, const ca_cache* kv,
+                         const int32_t* idx, const int32_t* cnt, int32_t k, int32_t ratio, const int32_t* pos,
+                         int32_t B, int64_t max_pos, const void* window, int32_t W, const float* sink, void* out,
+                         float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* HCA prefill: entries 0..floor(t/ratio)-1 of sequence `seq` for row t. */
+int ca_hca_attend_prefill(const ca_attend_params* p, const void* q, const float* q_gain, const ca_cache* kv,
+                          int32_t seq, int32_t ratio, const void* window, int32_t W, const float* sink, int64_t L,
+                          void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* HCA decode: row b is sequence b at position pos[b]. */
+int ca_hca_attend_decode(const ca_attend_params* p, const void* q, const float* q_gain, const ca_cache* kv,
+                         int32_t ratio, const int32_t* pos, int32_t B, int64_t max_pos, const void* window,
+                         int32_t W, const float* sink, void* out, float* lse, void* ws, size_t ws_bytes,
+                         void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSAHCA_H */

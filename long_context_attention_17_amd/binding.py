@@ -1,0 +1,235 @@
+"""ctypes binding of libcsahca.so, the MI355X (gfx950) CSA / HCA attention library.
+
+Argument marshalling only: every function below forwards device pointers of
+torch tensors (and torch's current HIP stream) to the C entry point of the same
+name in include/csahca.h and raises CAError on a non-zero status.  All
+computation happens in the library's HIP kernels.  Importing this package
+fails loudly when the library has not been built (see build.py).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcsahca.so")
+
+F32, BF16, FP8MIX, E4M3 = 0, 1, 2, 3
+FORMATS = {"f32": F32, "bf16": BF16, "fp8mix": FP8MIX, "e4m3": E4M3}
+
+
+class CAError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"csahca error {code}: {msg}")
+        self.code = code
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m long_context_attention_17_amd.build` "
+                      "(or __graft_entry__.build()) before using the HIP path")
+_lib = ctypes.CDLL(LIB_PATH)
+
+_P, _I32, _I64, _F, _D, _SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_double,
+                               ctypes.c_size_t)
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [("format", _I32), ("dim", _I32), ("rope_dim", _I32), ("page_size", _I32), ("pool", _P),
+                ("n_pages", _I64), ("page_table", _P), ("n_seqs", _I32), ("max_pages", _I32)]
+
+
+class CompressParams(ctypes.Structure):
+    _fields_ = [("ratio", _I32), ("overlap", _I32), ("in_format", _I32), ("apply_norm", _I32),
+                ("apply_rope", _I32), ("eps", _F), ("rope_base", _D)]
+
+
+class WindowParams(ctypes.Structure):
+    _fields_ = [("dim", _I32), ("rope_dim", _I32), ("in_format", _I32), ("win_format", _I32), ("eps", _F),
+                ("rope_base", _D)]
+
+
+class IndexParams(ctypes.Structure):
+    _fields_ = [("n_heads", _I32), ("dim", _I32), ("ratio", _I32), ("k", _I32), ("q_format", _I32)]
+
+
+class AttendParams(ctypes.Structure):
+    _fields_ = [("n_heads", _I32), ("dim", _I32), ("rope_dim", _I32), ("n_win", _I32), ("q_format", _I32),
+                ("win_format", _I32), ("out_format", _I32), ("scale", _F), ("eps", _F), ("rope_base", _D)]
+
+
+_PC = ctypes.POINTER(_Cache)
+_SIGS = {
+    "ca_last_error": (ctypes.c_char_p, []),
+    "ca_record_stride": (_I64, [_I32, _I32, _I32]),
+    "ca_page_bytes": (_I64, [_I32, _I32, _I32, _I32]),
+    "ca_store_entries": (ctypes.c_int, [_PC, _I32, _I64, _I64, _P, _P, _F, _I32, _D, _I32, _P]),
+    "ca_compress_prefill": (ctypes.c_int, [ctypes.POINTER(CompressParams), _P, _P, _P, _P, _P, _P, _P, _I64, _I32,
+                                           _PC, _P]),
+    "ca_compress_decode": (ctypes.c_int, [ctypes.POINTER(CompressParams), _P, _P, _I32, _P, _P, _P, _P, _PC, _P]),
+    "ca_window_append": (ctypes.c_int, [ctypes.POINTER(WindowParams), _P, _P, _P, _P, _I32, _P, _I32, _I32, _P]),
+    "ca_index_topk_workspace": (_SZ, [ctypes.POINTER(IndexParams), _I32, _I64]),
+    "ca_index_topk_prefill": (ctypes.c_int, [ctypes.POINTER(IndexParams), _P, _P, _I64, _I32, _PC, _P, _P, _P, _P,
+                                             _I64, _P, _SZ, _P]),
+    "ca_index_topk_decode": (ctypes.c_int, [ctypes.POINTER(IndexParams), _P, _P, _P, _I32, _I64, _PC, _P, _P, _P,
+                                            _P, _I64, _P, _SZ, _P]),
+    "ca_attend_workspace": (_SZ, [ctypes.POINTER(AttendParams), _I32, _I64, _I32, _I32]),
+    "ca_csa_attend_prefill": (ctypes.c_int, [ctypes.POINTER(AttendParams), _P, _P, _PC, _I32, _P, _P, _I32, _I32,
+                                             _P, _I32, _P, _I64, _P, _P, _P, _SZ, _P]),
+    "ca_csa_attend_decode": (ctypes.c_int, [ctypes.POINTER(AttendParams), _P, _P, _PC, _P, _P, _I32, _I32, _P, _I32,
+                                            _I64, _P, _I32, _P, _P, _P, _P, _SZ, _P]),
+    "ca_hca_attend_prefill": (ctypes.c_int, [ctypes.POINTER(AttendParams), _P, _P, _PC, _I32, _I32, _P, _I32, _P,
+                                             _I64, _P, _P, _P, _SZ, _P]),
+    "ca_hca_attend_decode": (ctypes.c_int, [ctypes.POINTER(AttendParams), _P, _P, _PC, _I32, _P, _I32, _I64, _P,
+                                            _I32, _P, _P, _P, _P, _SZ, _P]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+
+def lib():
+    return _lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise CAError(rc, _lib.ca_last_error().decode())
+
+
+def record_stride(fmt: int, dim: int, rope_dim: int) -> int:
+    return int(_lib.ca_record_stride(fmt, dim, rope_dim))
+
+
+def page_bytes(fmt: int, dim: int, rope_dim: int, page_size: int) -> int:
+    return int(_lib.ca_page_bytes(fmt, dim, rope_dim, page_size))
+
+
+class Cache:
+    """A paged compressed cache: a uint8 page pool plus an int32 page table [n_seqs, max_pages]."""
+
+    def __init__(self, fmt: int, dim: int, rope_dim: int, page_size: int, pool: torch.Tensor,
+                 page_table: torch.Tensor):
+        if pool.dtype != torch.uint8 or page_table.dtype != torch.int32 or page_table.dim() != 2:
+            raise TypeError("pool must be uint8 and page_table int32 [n_seqs, max_pages]")
+        pb = page_bytes(fmt, dim, rope_dim, page_size)
+        self.fmt, self.dim, self.rope_dim, self.page_size = fmt, dim, rope_dim, page_size
+        self.pool, self.page_table = pool, page_table
+        self.n_pages = pool.numel() // pb
+        self.desc = _Cache(fmt, dim, rope_dim, page_size, pool.data_ptr(), self.n_pages, page_table.data_ptr(),
+                           page_table.shape[0], page_table.shape[1])
+
+    @classmethod
+    def allocate(cls, fmt, dim, rope_dim, page_size, n_pages, page_table, device="cuda"):
+        pool = torch.zeros(n_pages * page_bytes(fmt, dim, rope_dim, page_size), dtype=torch.uint8, device=device)
+        return cls(fmt, dim, rope_dim, page_size, pool, page_table.to(device=device, dtype=torch.int32).contiguous())
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.desc)
+
+
+def store_entries(cache: Cache, seq: int, first: int, src: torch.Tensor, gain=None, eps=1e-6, apply_rope=True,
+                  rope_base=1e4, pos_stride=1, stream=None):
+    assert src.dtype == torch.float32
+    _check(_lib.ca_store_entries(cache.ref, seq, first, src.shape[0], _ptr(src), _ptr(gain), eps, int(apply_rope),
+                                 rope_base, pos_stride, _stream(stream)))
+
+
+def compress_prefill(p: CompressParams, Ca, Za, Cb, Zb, Ba, Bb, gain, L: int, seq: int, cache: Cache, stream=None):
+    _check(_lib.ca_compress_prefill(ctypes.byref(p), _ptr(Ca), _ptr(Za), _ptr(Cb), _ptr(Zb), _ptr(Ba), _ptr(Bb),
+                                    _ptr(gain), L, seq, cache.ref, _stream(stream)))
+
+
+def compress_decode(p: CompressParams, new_rows, pos, tail, Ba, Bb, gain, cache: Cache, stream=None):
+    _check(_lib.ca_compress_decode(ctypes.byref(p), _ptr(new_rows), _ptr(pos), pos.shape[0], _ptr(tail), _ptr(Ba),
+                                   _ptr(Bb), _ptr(gain), cache.ref, _stream(stream)))
+
+
+def window_append(p: WindowParams, kv_raw, gain, window, pos=None, seq=None, stream=None):
+    S, W = window.shape[0], window.shape[1]
+    _check(_lib.ca_window_append(ctypes.byref(p), _ptr(kv_raw), _ptr(gain), _ptr(pos), _ptr(seq), kv_raw.shape[0],
+                                 _ptr(window), W, S, _stream(stream)))
+
+
+def index_topk_workspace(p: IndexParams, n_rows: int, max_pos: int) -> int:
+    return int(_lib.ca_index_topk_workspace(ctypes.byref(p), n_rows, max_pos))
+
+
+def index_topk_prefill(p: IndexParams, qI, w, seq: int, idx_cache: Cache, out_idx, out_cnt, out_score=None,
+                       all_scores=None, ws=None, stream=None):
+    L = qI.shape[0]
+    if ws is None and all_scores is None:
+        ws = torch.empty(max(1, index_topk_workspace(p, L, max(L - 1, 0))), dtype=torch.uint8, device=qI.device)
+    st = all_scores.shape[1] if all_scores is not None else 0
+    _check(_lib.ca_index_topk_prefill(ctypes.byref(p), _ptr(qI), _ptr(w), L, seq, idx_cache.ref, _ptr(out_idx),
+                                      _ptr(out_cnt), _ptr(out_score), _ptr(all_scores), st, _ptr(ws),
+                                      0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def index_topk_decode(p: IndexParams, qI, w, pos, max_pos: int, idx_cache: Cache, out_idx, out_cnt,
+                      out_score=None, all_scores=None, ws=None, stream=None):
+    B = qI.shape[0]
+    if ws is None and all_scores is None:
+        ws = torch.empty(max(1, index_topk_workspace(p, B, max_pos)), dtype=torch.uint8, device=qI.device)
+    st = all_scores.shape[1] if all_scores is not None else 0
+    _check(_lib.ca_index_topk_decode(ctypes.byref(p), _ptr(qI), _ptr(w), _ptr(pos), B, max_pos, idx_cache.ref,
+                                     _ptr(out_idx), _ptr(out_cnt), _ptr(out_score), _ptr(all_scores), st, _ptr(ws),
+                                     0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def attend_workspace(p: AttendParams, n_rows: int, max_pos: int, k: int, ratio: int) -> int:
+    return int(_lib.ca_attend_workspace(ctypes.byref(p), n_rows, max_pos, k, ratio))
+
+
+def csa_attend_prefill(p: AttendParams, q, q_gain, kv: Cache, seq: int, idx, cnt, ratio: int, window, sink, out,
+                       lse=None, stream=None):
+    L, k = q.shape[0], idx.shape[1]
+    _check(_lib.ca_csa_attend_prefill(ctypes.byref(p), _ptr(q), _ptr(q_gain), kv.ref, seq, _ptr(idx), _ptr(cnt), k,
+                                      ratio, _ptr(window), window.shape[1], _ptr(sink), L, _ptr(out), _ptr(lse), None,
+                                      0, _stream(stream)))
+
+
+def csa_attend_decode(p: AttendParams, q, q_gain, kv: Cache, idx, cnt, ratio: int, pos, max_pos: int, window, sink,
+                      out, lse=None, ws=None, stream=None):
+    B, k = q.shape[0], idx.shape[1]
+    if ws is None:
+        ws = torch.empty(max(1, attend_workspace(p, B, max_pos, k, ratio)), dtype=torch.uint8, device=q.device)
+    _check(_lib.ca_csa_attend_decode(ctypes.byref(p), _ptr(q), _ptr(q_gain), kv.ref, _ptr(idx), _ptr(cnt), k, ratio,
+                                     _ptr(pos), B, max_pos, _ptr(window), window.shape[1], _ptr(sink), _ptr(out),
+                                     _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def hca_attend_prefill(p: AttendParams, q, q_gain, kv: Cache, seq: int, ratio: int, window, sink, out, lse=None,
+                       stream=None):
+    L = q.shape[0]
+    _check(_lib.ca_hca_attend_prefill(ctypes.byref(p), _ptr(q), _ptr(q_gain), kv.ref, seq, ratio, _ptr(window),
+                                      window.shape[1], _ptr(sink), L, _ptr(out), _ptr(lse), None, 0,
+                                      _stream(stream)))
+
+
+def hca_attend_decode(p: AttendParams, q, q_gain, kv: Cache, ratio: int, pos, max_pos: int, window, sink, out,
+                      lse=None, ws=None, stream=None):
+    B = q.shape[0]
+    if ws is None:
+        ws = torch.empty(max(1, attend_workspace(p, B, max_pos, 0, ratio)), dtype=torch.uint8, device=q.device)
+    _check(_lib.ca_hca_attend_decode(ctypes.byref(p), _ptr(q), _ptr(q_gain), kv.ref, ratio, _ptr(pos), B, max_pos,
+                                     _ptr(window), window.shape[1], _ptr(sink), _ptr(out), _ptr(lse), _ptr(ws),
+                                     ws.numel(), _stream(stream)))

@@ -1,0 +1,347 @@
+// C ABI of the CSA / HCA library: host-side validation, workspace layout and
+// dispatch to the kernels.  No allocation, no host synchronisation.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/csahca.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = 0;
+  return CA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(CA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool is_act(int f) { return f == CA_F32 || f == CA_BF16; }
+
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int ilog2(int x) {
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
+}
+
+// Validate a cache descriptor and build its device view.
+int make_view(const ca_cache* c, ca::CacheView* v, const char* what) {
+  if (c == nullptr) return fail(CA_ERR_ARG, "%s: cache descriptor is NULL", what);
+  if (c->format < CA_F32 || c->format > CA_E4M3) return fail(CA_ERR_DTYPE, "%s: unknown cache format %d", what, c->format);
+  if (c->dim <= 0 || c->dim > 1024) return fail(CA_ERR_UNSUPPORTED, "%s: dim %d outside 1..1024", what, c->dim);
+  if (c->rope_dim < 0 || c->rope_dim > c->dim || (c->rope_dim & 1))
+    return fail(CA_ERR_ARG, "%s: rope_dim %d must be even and <= dim", what, c->rope_dim);
+  if (c->format == CA_FP8MIX && ((c->dim - c->rope_dim) % 64 != 0))
+    return fail(CA_ERR_UNSUPPORTED, "%s: fp8-mixed records need (dim - rope_dim) %% 64 == 0", what);
+  if (c->format == CA_E4M3 && c->rope_dim != 0) return fail(CA_ERR_ARG, "%s: indexer pools have rope_dim 0", what);
+  if (!pow2(c->page_size)) return fail(CA_ERR_ARG, "%s: page_size %d must be a power of two", what, c->page_size);
+  if (c->n_pages < 0 || c->n_seqs < 0 || c->max_pages < 0) return fail(CA_ERR_ARG, "%s: negative sizes", what);
+  if (c->n_pages > 0 && c->pool == nullptr) return fail(CA_ERR_ARG, "%s: pool is NULL", what);
+  if (c->n_seqs > 0 && c->max_pages > 0 && c->page_table == nullptr) return fail(CA_ERR_ARG, "%s: page_table is NULL", what);
+  v->pool = (uint8_t*)c->pool;
+  v->page_table = c->page_table;
+  v->n_pages = c->n_pages;
+  v->page_bytes = ca::page_bytes(c->format, c->dim, c->rope_dim, c->page_size);
+  v->stride = ca::record_stride(c->format, c->dim, c->rope_dim);
+  v->max_pages = c->max_pages;
+  v->page_shift = ilog2(c->page_size);
+  v->fmt = c->format;
+  v->dim = c->dim;
+  v->rope = c->rope_dim;
+  return CA_OK;
+}
+
+hipStream_t S(void* s) { return (hipStream_t)s; }
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+int64_t score_stride(int64_t max_pos, int ratio) {
+  int64_t ne = max_pos / ratio;
+  if (ne < 1) ne = 1;
+  return (ne + 63) / 64 * 64;
+}
+
+int max_splits_for(int64_t max_pos, int n_win, int k, int ratio) {
+  int64_t entries = k > 0 ? k : max_pos / ratio;
+  int64_t items = entries + n_win;
+  return (int)((items + ca::kDecodeSplitItems - 1) / ca::kDecodeSplitItems);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ca_last_error(void) { return g_err; }
+
+int64_t ca_record_stride(int32_t format, int32_t dim, int32_t rope_dim) {
+  if (format < CA_F32 || format > CA_E4M3 || dim <= 0) return -1;
+  return ca::record_stride(format, dim, rope_dim);
+}
+
+int64_t ca_page_bytes(int32_t format, int32_t dim, int32_t rope_dim, int32_t page_size) {
+  if (format < CA_F32 || format > CA_E4M3 || dim <= 0 || page_size <= 0) return -1;
+  return ca::page_bytes(format, dim, rope_dim, page_size);
+}
+
+int ca_store_entries(const ca_cache* cache, int32_t seq, int64_t first, int64_t n, const float* src,
+                     const float* gain, float eps, int32_t apply_rope, double rope_base, int32_t pos_stride,
+                     void* stream) {
+  ca::CacheView cv;
+  if (int e = make_view(cache, &cv, "ca_store_entries")) return e;
+  if (n < 0 || first < 0) return fail(CA_ERR_ARG, "ca_store_entries: negative first/n");
+  if (n > 0 && src == nullptr) return fail(CA_ERR_ARG, "ca_store_entries: src is NULL");
+  if (seq < 0 || seq >= cache->n_seqs) return fail(CA_ERR_ARG, "ca_store_entries: seq %d out of range", seq);
+  if (first + n > (int64_t)cache->max_pages * cache->page_size)
+    return fail(CA_ERR_ARG, "ca_store_entries: entries beyond the page table");
+  if (n > 0x7FFFFFFF) return fail(CA_ERR_UNSUPPORTED, "ca_store_entries: n too large");
+  return hip_status(ca::launch_store_entries(cv, seq, first, n, src, gain, eps, apply_rope, rope_base, pos_stride,
+                                             S(stream)),
+                    "ca_store_entries");
+}
+
+static int check_compress(const ca_compress_params* p, const ca_cache* cache, ca::CacheView* cv, const char* w) {
+  if (p == nullptr) return fail(CA_ERR_ARG, "%s: params NULL", w);
+  if (int e = make_view(cache, cv, w)) return e;
+  if (p->ratio <= 0) return fail(CA_ERR_ARG, "%s: ratio must be positive", w);
+  if (p->overlap != 0 && p->overlap != 1) return fail(CA_ERR_ARG, "%s: overlap must be 0 or 1", w);
+  if (!is_act(p->in_format)) return fail(CA_ERR_DTYPE, "%s: in_format must be F32 or BF16", w);
+  return CA_OK;
+}
+
+int ca_compress_prefill(const ca_compress_params* p, const void* Ca, const void* Za, const void* Cb,
+                        const void* Zb, const float* Ba, const float* Bb, const float* gain, int64_t L,
+                        int32_t seq, const ca_cache* cache, void* stream) {
+  ca::CacheView cv;
+  if (int e = check_compress(p, cache, &cv, "ca_compress_prefill")) return e;
+  if (L < 0) return fail(CA_ERR_ARG, "ca_compress_prefill: negative L");
+  if (L / p->ratio == 0) return ok();
+  if (!Ca || !Za || !Ba) return fail(CA_ERR_ARG, "ca_compress_prefill: Ca/Za/Ba NULL");
+  if (p->overlap && (!Cb || !Zb || !Bb)) return fail(CA_ERR_ARG, "ca_compress_prefill: Cb/Zb/Bb NULL with overlap");
+  if (p->apply_norm && !gain) return fail(CA_ERR_ARG, "ca_compress_prefill: gain NULL with apply_norm");
+  if (seq < 0 || seq >= cache->n_seqs) return fail(CA_ERR_ARG, "ca_compress_prefill: seq out of range");
+  if (L / p->ratio > (int64_t)cache->max_pages * cache->page_size)
+    return fail(CA_ERR_ARG, "ca_compress_prefill: page table holds fewer than L/ratio entries");
+  return hip_status(ca::launch_compress_prefill(cv, seq, *p, Ca, Za, Cb, Zb, Ba, Bb, gain, L, S(stream)),
+                    "ca_compress_prefill");
+}
+
+int ca_compress_decode(const ca_compress_params* p, const void* new_rows, const int32_t* pos, int32_t B,
+                       float* tail, const float* Ba, const float* Bb, const float* gain, const ca_cache* cache,
+                       void* stream) {
+  ca::CacheView cv;
+  if (int e = check_compress(p, cache, &cv, "ca_compress_decode")) return e;
+  if (B < 0) return fail(CA_ERR_ARG, "ca_compress_decode: negative B");
+  if (B == 0) return ok();
+  if (!new_rows || !pos || !tail || !Ba) return fail(CA_ERR_ARG, "ca_compress_decode: NULL argument");
+  if (p->overlap && !Bb) return fail(CA_ERR_ARG, "ca_compress_decode: Bb NULL with overlap");
+  if (p->apply_norm && !gain) return fail(CA_ERR_ARG, "ca_compress_decode: gain NULL with apply_norm");
+  if (B > cache->n_seqs) return fail(CA_ERR_ARG, "ca_compress_decode: B exceeds the page table rows");
+  return hip_status(ca::launch_compress_decode(cv, *p, new_rows, pos, B, tail, Ba, Bb, gain, S(stream)),
+                    "ca_compress_decode");
+}
+
+int ca_window_append(const ca_window_params* p, const void* kv_raw, const float* gain, const int32_t* pos,
+                     const int32_t* seq, int32_t T, void* window, int32_t W, int32_t S_, void* stream) {
+  if (p == nullptr) return fail(CA_ERR_ARG, "ca_window_append: params NULL");
+  if (p->dim <= 0 || p->dim > 1024) return fail(CA_ERR_UNSUPPORTED, "ca_window_append: dim outside 1..1024");
+  if (p->rope_dim < 0 || p->rope_dim > p->dim || (p->rope_dim & 1)) return fail(CA_ERR_ARG, "ca_window_append: bad rope_dim");
+  if (!is_act(p->in_format) || !is_act(p->win_format)) return fail(CA_ERR_DTYPE, "ca_window_append: formats must be F32/BF16");
+  if (T < 0 || W <= 0 || S_ <= 0) return fail(CA_ERR_ARG, "ca_window_append: bad T/W/S");
+  if (T == 0) return ok();
+  if (!kv_raw || !gain || !window) return fail(CA_ERR_ARG, "ca_window_append: NULL argument");
+  return hip_status(ca::launch_window_append(*p, kv_raw, gain, pos, seq, T, window, W, S_, S(stream)),
+                    "ca_window_append");
+}
+
+// ------------------------------------------------------------------ indexer
+size_t ca_index_topk_workspace(const ca_index_params* p, int32_t n_rows, int64_t max_pos) {
+  if (p == nullptr || p->ratio <= 0 || n_rows <= 0 || max_pos < 0) return 0;
+  return align256((size_t)n_rows * score_stride(max_pos, p->ratio) * sizeof(float));
+}
+
+static int index_common(const ca_index_params* p, const void* qI, const float* w, const int32_t* pos, int seq_fixed,
+                        int64_t n_rows, int64_t max_pos, const ca_cache* idx_cache, int32_t* out_idx,
+                        int32_t* out_cnt, float* out_score, float* all_scores, int64_t all_stride, void* ws,
+                        size_t ws_bytes, void* stream, const char* what) {
+  if (p == nullptr) return fail(CA_ERR_ARG, "%s: params NULL", what);
+  ca::CacheView cv;
+  if (int e = make_view(idx_cache, &cv, what)) return e;
+  if (idx_cache->format != CA_F32 && idx_cache->format != CA_E4M3)
+    return fail(CA_ERR_DTYPE, "%s: indexer pool must be F32 or E4M3", what);
+  if (p->dim != idx_cache->dim) return fail(CA_ERR_ARG, "%s: params dim %d != cache dim %d", what, p->dim, idx_cache->dim);
+  if (p->n_heads <= 0 || p->dim <= 0 || p->ratio <= 0 || p->k <= 0) return fail(CA_ERR_ARG, "%s: bad params", what);
+  if ((int64_t)p->n_heads * p->dim > 16384) return fail(CA_ERR_UNSUPPORTED, "%s: n_heads*dim > 16384", what);
+  if (!is_act(p->q_format)) return fail(CA_ERR_DTYPE, "%s: q_format must be F32/BF16", what);
+  if (n_rows < 0 || n_rows > 0x7FFFFFFF) return fail(CA_ERR_ARG, "%s: bad row count", what);
+  if (n_rows == 0) return ok();
+  if (!qI || !w || !out_idx || !out_cnt) return fail(CA_ERR_ARG, "%s: NULL argument", what);
+  if (max_pos / p->ratio > (int64_t)idx_cache->max_pages * idx_cache->page_size)
+    return fail(CA_ERR_ARG, "%s: page table holds fewer entries than floor(max_pos/ratio)", what);
+  float* scores;
+  int64_t stride;
+  if (all_scores != nullptr) {
+    if (all_stride < max_pos / p->ratio) return fail(CA_ERR_ARG, "%s: all_scores_stride too small", what);
+    scores = all_scores;
+    stride = all_stride;
+  } else {
+    size_t need = ca_index_topk_workspace(p, (int32_t)n_rows, max_pos);
+    if (ws_bytes < need || (need > 0 && ws == nullptr))
+      return fail(CA_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", what, ws_bytes, need);
+    scores = (float*)ws;
+    stride = score_stride(max_pos, p->ratio);
+  }
+  hipError_t e = ca::launch_index_scores(cv, *p, qI, w, pos, seq_fixed, (int)n_rows, max_pos, scores, stride,
+                                         S(stream));
+  if (e != hipSuccess) return hip_status(e, what);
+  e = ca::launch_topk(scores, stride, pos, p->ratio, p->k, (int)n_rows, out_idx, out_cnt, out_score, S(stream));
+  return hip_status(e, what);
+}
+
+int ca_index_topk_prefill(const ca_index_params* p, const void* qI, const float* w, int64_t L, int32_t seq,
+                          const ca_cache* idx_cache, int32_t* out_idx, int32_t* out_cnt, float* out_score,
+                          float* all_scores, int64_t all_scores_stride, void* ws, size_t ws_bytes, void* stream) {
+  if (idx_cache && (seq < 0 || seq >= idx_cache->n_seqs)) return fail(CA_ERR_ARG, "ca_index_topk_prefill: seq out of range");
+  return index_common(p, qI, w, nullptr, seq, L, L > 0 ? L - 1 : 0, idx_cache, out_idx, out_cnt, out_score,
+                      all_scores, all_scores_stride, ws, ws_bytes, stream, "ca_index_topk_prefill");
+}
+
+int ca_index_topk_decode(const ca_index_params* p, const void* qI, const float* w, const int32_t* pos,
+                         int32_t B, int64_t max_pos, const ca_cache* idx_cache, int32_t* out_idx,
+                         int32_t* out_cnt, float* out_score, float* all_scores, int64_t all_scores_stride,
+                         void* ws, size_t ws_bytes, void* stream) {
+  if (pos == nullptr && B > 0) return fail(CA_ERR_ARG, "ca_index_topk_decode: pos NULL");
+  if (idx_cache && B > idx_cache->n_seqs) return fail(CA_ERR_ARG, "ca_index_topk_decode: B exceeds page table rows");
+  if (max_pos < 0) return fail(CA_ERR_ARG, "ca_index_topk_decode: negative max_pos");
+  return index_common(p, qI, w, pos, -1, B, max_pos, idx_cache, out_idx, out_cnt, out_score, all_scores,
+                      all_scores_stride, ws, ws_bytes, stream, "ca_index_topk_decode");
+}
+
+// ------------------------------------------------------------------ attention
+size_t ca_attend_workspace(const ca_attend_params* p, int32_t n_rows, int64_t max_pos, int32_t k, int32_t ratio) {
+  if (p == nullptr || n_rows <= 0 || ratio <= 0) return 0;
+  size_t ms = (size_t)max_splits_for(max_pos, p->n_win, k, ratio);
+  size_t po = (size_t)n_rows * ms * p->n_heads * p->dim * sizeof(float);
+  size_t pm = (size_t)n_rows * ms * p->n_heads * 2 * sizeof(float);
+  return align256(po) + align256(pm);
+}
+
+static int attend_common(const ca_attend_params* p, const void* q, const float* q_gain, const ca_cache* kv,
+                         int mode, int seq_fixed, const int32_t* pos, int64_t n_rows, int64_t max_pos,
+                         const int32_t* idx, const int32_t* cnt, int k, int ratio, const void* window, int W,
+                         int win_rows, const float* sink, void* out, float* lse, void* ws, size_t ws_bytes,
+                         void* stream, bool decode, const char* what) {
+  if (p == nullptr) return fail(CA_ERR_ARG, "%s: params NULL", what);
+  ca::AttendArgs a;
+  if (int e = make_view(kv, &a.kv, what)) return e;
+  if (kv->format != CA_F32 && kv->format != CA_BF16 && kv->format != CA_FP8MIX)
+    return fail(CA_ERR_DTYPE, "%s: main KV pool must be F32, BF16 or FP8MIX", what);
+  if (p->dim != kv->dim || p->rope_dim != kv->rope_dim)
+    return fail(CA_ERR_ARG, "%s: params dim/rope_dim differ from the cache", what);
+  if (p->dim % 64 != 0 || (p->dim / 64 != 1 && p->dim / 64 != 2 && p->dim / 64 != 4 && p->dim / 64 != 8))
+    return fail(CA_ERR_UNSUPPORTED, "%s: dim must be 64, 128, 256 or 512", what);
+  if (p->n_heads <= 0 || p->n_win < 1) return fail(CA_ERR_ARG, "%s: n_heads and n_win must be positive", what);
+  if (!is_act(p->q_format) || !is_act(p->win_format) || !is_act(p->out_format))
+    return fail(CA_ERR_DTYPE, "%s: q/window/out formats must be F32 or BF16", what);
+  if (ratio <= 0) return fail(CA_ERR_ARG, "%s: ratio must be positive", what);
+  if (mode == 0 && k <= 0) return fail(CA_ERR_ARG, "%s: k must be positive", what);
+  if (n_rows < 0 || n_rows > 0x7FFFFFFF || W <= 0) return fail(CA_ERR_ARG, "%s: bad sizes", what);
+  if (n_rows == 0) return ok();
+  if (!q || !q_gain || !window || !sink || !out) return fail(CA_ERR_ARG, "%s: NULL argument", what);
+  if (mode == 0 && (!idx || !cnt)) return fail(CA_ERR_ARG, "%s: idx/cnt NULL", what);
+  if (decode && !pos) return fail(CA_ERR_ARG, "%s: pos NULL", what);
+  if (!decode && W < n_rows) return fail(CA_ERR_ARG, "%s: prefill window needs W >= L", what);
+  if (decode && n_rows > kv->n_seqs) return fail(CA_ERR_ARG, "%s: more rows than page table rows", what);
+  if (mode == 1 && max_pos / ratio > (int64_t)kv->max_pages * kv->page_size)
+    return fail(CA_ERR_ARG, "%s: page table holds fewer than floor(max_pos/ratio) entries", what);
+  (void)win_rows;
+  a.q = q;
+  a.q_gain = q_gain;
+  a.q_fmt = p->q_format;
+  a.n_heads = p->n_heads;
+  a.D = p->dim;
+  a.R = p->rope_dim;
+  a.n_win = p->n_win;
+  a.scale_log2 = p->scale * ca::kLog2e;
+  a.eps = p->eps;
+  a.base = p->rope_base;
+  a.pos = pos;
+  a.seq_fixed = seq_fixed;
+  a.n_rows = (int)n_rows;
+  a.mode = mode;
+  a.ratio = ratio;
+  a.idx = idx;
+  a.cnt = cnt;
+  a.k = k;
+  a.win = window;
+  a.win_fmt = p->win_format;
+  a.W = W;
+  a.sink = sink;
+  a.out = out;
+  a.out_fmt = p->out_format;
+  a.lse = lse;
+  a.split_items = 0;
+  a.max_splits = 1;
+  a.part_o = nullptr;
+  a.part_ml = nullptr;
+  if (decode) {
+    size_t need = ca_attend_workspace(p, (int32_t)n_rows, max_pos, mode == 0 ? k : 0, ratio);
+    if (ws_bytes < need || ws == nullptr) return fail(CA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", what, ws_bytes, need);
+    a.split_items = ca::kDecodeSplitItems;
+    a.max_splits = max_splits_for(max_pos, p->n_win, mode == 0 ? k : 0, ratio);
+    size_t ms = (size_t)a.max_splits;
+    a.part_o = (float*)ws;
+    a.part_ml = (float*)((char*)ws + align256((size_t)n_rows * ms * p->n_heads * p->dim * sizeof(float)));
+  }
+  return hip_status(ca::launch_attend(a, S(stream)), what);
+}
+
+int ca_csa_attend_prefill(const ca_attend_params* p, const void* q, const float* q_gain, const ca_cache* kv,
+                          int32_t seq, const int32_t* idx, const int32_t* cnt, int32_t k, int32_t ratio,
+                          const void* window, int32_t W, const float* sink, int64_t L, void* out, float* lse,
+                          void* ws, size_t ws_bytes, void* stream) {
+  if (kv && (seq < 0 || seq >= kv->n_seqs)) return fail(CA_ERR_ARG, "ca_csa_attend_prefill: seq out of range");
+  return attend_common(p, q, q_gain, kv, 0, seq, nullptr, L, L - 1, idx, cnt, k, ratio, window, W, 1, sink, out, lse,
+                       ws, ws_bytes, stream, false, "ca_csa_attend_prefill");
+}
+
+int ca_csa_attend_decode(const ca_attend_params* p, const void* q, const float* q_gain, const ca_cache* kv,
+                         const int32_t* idx, const int32_t* cnt, int32_t k, int32_t ratio, const int32_t* pos,
+                         int32_t B, int64_t max_pos, const void* window, int32_t W, const float* sink, void* out,
+                         float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return attend_common(p, q, q_gain, kv, 0, -1, pos, B, max_pos, idx, cnt, k, ratio, window, W, B, sink, out, lse, ws,
+                       ws_bytes, stream, true, "ca_csa_attend_decode");
+}
+
+int ca_hca_attend_prefill(const ca_attend_params* p, const void* q, const float* q_gain, const ca_cache* kv,
+                          int32_t seq, int32_t ratio, const void* window, int32_t W, const float* sink, int64_t L,
+                          void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (kv && (seq < 0 || seq >= kv->n_seqs)) return fail(CA_ERR_ARG, "ca_hca_attend_prefill: seq out of range");
+  return attend_common(p, q, q_gain, kv, 1, seq, nullptr, L, L - 1, nullptr, nullptr, 0, ratio, window, W, 1, sink,
+                       out, lse, ws, ws_bytes, stream, false, "ca_hca_attend_prefill");
+}
+
+int ca_hca_attend_decode(const ca_attend_params* p, const void* q, const float* q_gain, const ca_cache* kv,
+                         int32_t ratio, const int32_t* pos, int32_t B, int64_t max_pos, const void* window,
+                         int32_t W, const float* sink, void* out, float* lse, void* ws, size_t ws_bytes,
+                         void* stream) {
+  return attend_common(p, q, q_gain, kv, 1, -1, pos, B, max_pos, nullptr, nullptr, 0, ratio, window, W, B, sink, out,
+                       lse, ws, ws_bytes, stream, true, "ca_hca_attend_decode");
+}
+
+}  // extern "C"

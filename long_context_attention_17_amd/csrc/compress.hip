@@ -1,0 +1,244 @@
+// Sequence compressors (CSA overlapping 2m softmax pooling, HCA disjoint
+// pooling), the entry epilogue (RMSNorm -> partial RoPE -> record encode), the
+// decode-time tail ring, and the sliding-window append.
+//
+// dsv4 book Ch.5 "The four compression projections", "Coordinate-wise softmax
+// pooling", "Receptive field versus compression stride", "Decode-time cache
+// state"; Ch.7 "HCA's 128:1 non-overlapping compressor", "The 128-token
+// uncompressed sliding window", "Query and KV RMSNorm", "Partial RoPE and
+// output de-rotation"; Ch.8 "V4 compressed-entry payload".
+//
+// Work layout: one workgroup per entry (or window token), one thread per
+// channel; blockDim = dim rounded up to a multiple of 64, so every 64-channel
+// content tile of a mixed record is exactly one wavefront and its amax is a
+// wavefront reduction.  These kernels read each projection row once and are
+// bound by HBM reads of the rows; they are a small share of any step.
+#include "common.h"
+#include "kernels.h"
+
+namespace ca {
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float s = 0.0f;
+  for (int i = 0; i < nw; ++i) s += red[i];
+  return s;
+}
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+  v = wave_max(v);
+  int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float s = red[0];
+  for (int i = 1; i < nw; ++i) s = fmaxf(s, red[i]);
+  return s;
+}
+
+// RMSNorm (when gain != nullptr) then rotation of the last R channels at
+// position `pos`.  Thread j holds channel j (x is ignored for j >= D).
+__device__ float norm_rope(float x, int j, int D, int R, const float* gain, float eps, bool rope, double pos,
+                           double base, float* red) {
+  bool act = j < D;
+  if (gain != nullptr) {
+    float ss = block_sum(act ? x * x : 0.0f, red);
+    float inv = 1.0f / sqrtf(ss / (float)D + eps);
+    x = act ? x * inv * gain[j] : 0.0f;
+  }
+  if (rope && R > 0) {
+    float other = __shfl_xor(x, 1, 64);  // pair partner (pairs start at even channels)
+    if (act && j >= D - R) {
+      int p = (j - (D - R)) >> 1;
+      float s, c;
+      rope_sincos(pos, p, R, base, &s, &c);
+      x = (j & 1) ? other * s + x * c : x * c - other * s;
+    }
+  }
+  return x;
+}
+
+// Encode channel j of entry i of sequence `seq` into the pool.
+__device__ void store_record(const CacheView& cv, int seq, int64_t i, float x, int j, float* red) {
+  const int D = cv.dim, R = cv.rope;
+  bool act = j < D;
+  uint8_t* page = cv.page_of(seq, i);
+  int slot = cv.slot_of(i);
+  if (cv.fmt == CA_FP8MIX) {
+    const int C = D - R;
+    // one wavefront == one 64-channel content tile
+    float amax = wave_max((act && j < C) ? fabsf(x) : 0.0f);
+    if (page == nullptr || !act) return;
+    uint8_t* rec = page + slot * cv.stride;
+    if (j < C) {
+      int e = pow2_exponent(amax);
+      rec[j] = (uint8_t)e4m3_encode(ldexpf(x, -e));
+      if ((j & 63) == 0) rec[C + 2 * R + (j >> 6)] = (uint8_t)(int8_t)e;
+    } else {
+      ((uint16_t*)(rec + C))[j - C] = f32_to_bf16_bits(x);
+    }
+  } else if (cv.fmt == CA_E4M3) {
+    float amax = block_max(act ? fabsf(x) : 0.0f, red);
+    if (page == nullptr || !act) return;
+    int e = pow2_exponent(amax);
+    page[(int64_t)slot * D + j] = (uint8_t)e4m3_encode(ldexpf(x, -e));
+    if (j == 0) ((float*)(page + ((int64_t)D << cv.page_shift)))[slot] = ldexpf(1.0f, e);
+  } else if (cv.fmt == CA_BF16) {
+    if (page && act) ((uint16_t*)(page + slot * cv.stride))[j] = f32_to_bf16_bits(x);
+  } else {
+    if (page && act) ((float*)(page + slot * cv.stride))[j] = x;
+  }
+}
+
+// Online softmax-weighted sum over pooled source positions (one channel).
+struct Pool1 {
+  float mx = -INFINITY, den = 0.0f, num = 0.0f;
+  __device__ __forceinline__ void add(float z, float c) {
+    if (z > mx) {
+      float s = __expf(mx - z);
+      den *= s;
+      num *= s;
+      mx = z;
+    }
+    float w = __expf(z - mx);
+    den += w;
+    num += w * c;
+  }
+  __device__ __forceinline__ float value() const { return num / den; }
+};
+
+__global__ void compress_prefill_kernel(CacheView cv, int seq, int m, int overlap, int in_fmt, const void* Ca,
+                                        const void* Za, const void* Cb, const void* Zb, const float* Ba,
+                                        const float* Bb, const float* gain, float eps, int apply_rope,
+                                        double base) {
+  __shared__ float red[16];
+  const int D = cv.dim, j = threadIdx.x;
+  const int64_t i = blockIdx.x;
+  float x = 0.0f;
+  if (j < D) {
+    Pool1 acc;
+    for (int t = 0; t < m; ++t) {
+      int64_t row = (int64_t)m * i + t;
+      acc.add(load_act(Za, in_fmt, row * D + j) + Ba[t * D + j], load_act(Ca, in_fmt, row * D + j));
+    }
+    if (overlap && i > 0) {
+      for (int t = 0; t < m; ++t) {
+        int64_t row = (int64_t)m * (i - 1) + t;
+        acc.add(load_act(Zb, in_fmt, row * D + j) + Bb[t * D + j], load_act(Cb, in_fmt, row * D + j));
+      }
+    }
+    x = acc.value();
+  }
+  x = norm_rope(x, j, D, cv.rope, gain, eps, apply_rope != 0, (double)m * (double)i, base, red);
+  store_record(cv, seq, i, x, j, red);
+}
+
+// Tail ring: tail[b, slot, a, ch] (float32), narr arrays per slot.
+__global__ void compress_decode_kernel(CacheView cv, int m, int overlap, int in_fmt, const void* new_rows,
+                                       const int32_t* pos, float* tail, const float* Ba, const float* Bb,
+                                       const float* gain, float eps, int apply_rope, double base) {
+  __shared__ float red[16];
+  const int D = cv.dim, j = threadIdx.x, b = blockIdx.x;
+  const int narr = overlap ? 4 : 2;
+  const int span = overlap ? 2 * m : m;
+  const int t = pos[b];
+  float* ring = tail + (int64_t)b * span * narr * D;
+  if (j < D && t >= 0) {
+    for (int a = 0; a < narr; ++a)
+      ring[((int64_t)(t % span) * narr + a) * D + j] = load_act(new_rows, in_fmt, ((int64_t)b * narr + a) * D + j);
+  }
+  if (t < 0 || (t + 1) % m != 0) return;  // uniform across the block
+  const int64_t i = (t + 1) / m - 1;
+  float x = 0.0f;
+  if (j < D) {
+    Pool1 acc;
+    // a-branch (CSA arrays 0 = Ca, 2 = Za; HCA arrays 0 = C, 1 = Z)
+    for (int u = 0; u < m; ++u) {
+      int64_t p = (int64_t)m * i + u;
+      const float* slot = ring + (p % span) * narr * D;
+      acc.add(slot[(overlap ? 2 : 1) * D + j] + Ba[u * D + j], slot[j]);
+    }
+    if (overlap && i > 0) {
+      for (int u = 0; u < m; ++u) {
+        int64_t p = (int64_t)m * (i - 1) + u;
+        const float* slot = ring + (p % span) * narr * D;
+        acc.add(slot[3 * D + j] + Bb[u * D + j], slot[1 * D + j]);
+      }
+    }
+    x = acc.value();
+  }
+  x = norm_rope(x, j, D, cv.rope, gain, eps, apply_rope != 0, (double)m * (double)i, base, red);
+  store_record(cv, b, i, x, j, red);
+}
+
+__global__ void store_entries_kernel(CacheView cv, int seq, int64_t first, const float* src, const float* gain,
+                                     float eps, int apply_rope, double base, int pos_stride) {
+  __shared__ float red[16];
+  const int D = cv.dim, j = threadIdx.x;
+  const int64_t k = blockIdx.x, i = first + k;
+  float x = j < D ? src[k * D + j] : 0.0f;
+  x = norm_rope(x, j, D, cv.rope, gain, eps, apply_rope != 0, (double)pos_stride * (double)i, base, red);
+  store_record(cv, seq, i, x, j, red);
+}
+
+__global__ void window_append_kernel(int D, int R, int in_fmt, int win_fmt, const void* raw, const float* gain,
+                                     const int32_t* pos, const int32_t* seq, void* window, int W, int S, float eps,
+                                     double base) {
+  __shared__ float red[16];
+  const int j = threadIdx.x, r = blockIdx.x;
+  const int t = pos ? pos[r] : r;
+  const int s = seq ? seq[r] : 0;
+  float x = j < D ? load_act(raw, in_fmt, (int64_t)r * D + j) : 0.0f;
+  x = norm_rope(x, j, D, R, gain, eps, true, (double)t, base, red);
+  if (j >= D || t < 0 || s < 0 || s >= S) return;
+  int64_t o = ((int64_t)s * W + (t % W)) * D + j;
+  if (win_fmt == CA_F32) ((float*)window)[o] = x;
+  else ((uint16_t*)window)[o] = f32_to_bf16_bits(x);
+}
+
+// ----------------------------------------------------------------- launchers
+static int block_for(int D) { return (D + 63) / 64 * 64; }
+
+hipError_t launch_compress_prefill(const CacheView& cv, int seq, const ca_compress_params& p, const void* Ca,
+                                   const void* Za, const void* Cb, const void* Zb, const float* Ba,
+                                   const float* Bb, const float* gain, int64_t L, hipStream_t st) {
+  int64_t n = L / p.ratio;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(compress_prefill_kernel, dim3((unsigned)n), dim3(block_for(cv.dim)), 0, st, cv, seq, p.ratio,
+                     p.overlap, p.in_format, Ca, Za, Cb, Zb, Ba, Bb, p.apply_norm ? gain : nullptr, p.eps,
+                     p.apply_rope, p.rope_base);
+  return hipGetLastError();
+}
+
+hipError_t launch_compress_decode(const CacheView& cv, const ca_compress_params& p, const void* new_rows,
+                                  const int32_t* pos, int B, float* tail, const float* Ba, const float* Bb,
+                                  const float* gain, hipStream_t st) {
+  if (B == 0) return hipSuccess;
+  hipLaunchKernelGGL(compress_decode_kernel, dim3(B), dim3(block_for(cv.dim)), 0, st, cv, p.ratio, p.overlap,
+                     p.in_format, new_rows, pos, tail, Ba, Bb, p.apply_norm ? gain : nullptr, p.eps, p.apply_rope,
+                     p.rope_base);
+  return hipGetLastError();
+}
+
+hipError_t launch_store_entries(const CacheView& cv, int seq, int64_t first, int64_t n, const float* src,
+                                const float* gain, float eps, int apply_rope, double base, int pos_stride,
+                                hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(store_entries_kernel, dim3((unsigned)n), dim3(block_for(cv.dim)), 0, st, cv, seq, first, src,
+                     gain, eps, apply_rope, base, pos_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_window_append(const ca_window_params& p, const void* raw, const float* gain, const int32_t* pos,
+                                const int32_t* seq, int T, void* window, int W, int S, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(window_append_kernel, dim3(T), dim3(block_for(p.dim)), 0, st, p.dim, p.rope_dim, p.in_format,
+                     p.win_format, raw, gain, pos, seq, window, W, S, p.eps, p.rope_base);
+  return hipGetLastError();
+}
+
+}  // namespace ca

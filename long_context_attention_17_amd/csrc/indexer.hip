@@ -1,0 +1,323 @@
+// Lightning indexer scores and per-row top-k selection.
+//
+// dsv4 book Ch.6 "The lightning indexer": I[t,s] = sum_h w[t,h] ReLU(qI[t,h] . K[s])
+// over blocks s < floor(t/m) (Ch.5 "Causal availability"); Ch.6 "Top-k selection
+// and asymptotic scaling": keep the k best blocks per query.
+//
+// Scoring is the one real contraction here: for e4m3 keys it runs on the
+// gfx950 fp8 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4, unit scales) with the
+// query rows as the A operand (4 queries x 8 heads = 32 rows, or 1 query
+// padded for decode) and 32 keys per instruction as the B operand; each lane
+// loads 32 contiguous key bytes, so a wavefront streams 2 KB of key codes per
+// instruction.  The head combine (weights, ReLU) and the per-key power-of-two
+// scales are applied to the fp32 accumulators.
+//
+// Top-k is exact and deterministic: fp32 scores map to order-preserving
+// 32-bit keys (-0 folded onto +0), a 4 x 8-bit radix select finds the k-th
+// largest key T and how many keys equal to T are needed, and an ordered
+// compaction (ballot prefix counts) emits every key > T plus the lowest-index
+// keys == T, in ascending index order.
+#include "common.h"
+#include "kernels.h"
+
+namespace ca {
+
+__device__ __forceinline__ uint32_t order_key(float v) {
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0;                 // -0 == +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ------------------------------------------------------------------ scores, generic (fp32 math)
+// One thread per (row, key).  Query heads for the row sit in LDS (quantized to
+// e4m3 first when the pool is e4m3).
+__global__ void index_scores_generic_kernel(CacheView cv, int nI, int cI, int m, int q_fmt, const void* qI,
+                                            const float* w, const int32_t* pos, int seq_fixed, float* scores,
+                                            int64_t stride) {
+  extern __shared__ float qs[];                // [nI * cI] query values as the indexer sees them
+  const int r = blockIdx.x;
+  const int t = pos ? pos[r] : r;
+  const int seq = seq_fixed >= 0 ? seq_fixed : r;
+  const int64_t ne = t / m < stride ? t / m : stride;   // never beyond the score row
+  for (int h = threadIdx.x >> 6; h < nI; h += blockDim.x >> 6) {
+    // one wavefront per head: load, optionally quantize exactly like the MFMA path
+    int lane = threadIdx.x & 63;
+    float amax = 0.0f;
+    for (int c = lane; c < cI; c += 64) amax = fmaxf(amax, fabsf(load_act(qI, q_fmt, ((int64_t)r * nI + h) * cI + c)));
+    amax = wave_max(amax);
+    int e = pow2_exponent(amax);
+    for (int c = lane; c < cI; c += 64) {
+      float v = load_act(qI, q_fmt, ((int64_t)r * nI + h) * cI + c);
+      if (cv.fmt == CA_E4M3) {
+        uint32_t code = e4m3_encode(ldexpf(v, -e));
+        v = ldexpf(e4m3x2_to_f32(code)[0], e);
+      }
+      qs[h * cI + c] = v;
+    }
+  }
+  __syncthreads();
+  const int64_t s = (int64_t)blockIdx.y * blockDim.x + threadIdx.x;
+  if (s >= ne) return;
+  uint8_t* page = cv.page_of(seq, s);
+  float out = -INFINITY;
+  if (page != nullptr) {
+    int slot = cv.slot_of(s);
+    float acc = 0.0f;
+    if (cv.fmt == CA_E4M3) {
+      const uint8_t* kp = page + (int64_t)slot * cI;
+      float ks = ((const float*)(page + ((int64_t)cI << cv.page_shift)))[slot];
+      for (int h = 0; h < nI; ++h) {
+        float d = 0.0f;
+        for (int c = 0; c < cI; c += 2) {
+          f32x2 kv = e4m3x2_to_f32((uint32_t)kp[c] | ((uint32_t)kp[c + 1] << 8));
+          d += qs[h * cI + c] * kv[0] + qs[h * cI + c + 1] * kv[1];
+        }
+        acc += w[(int64_t)r * nI + h] * fmaxf(d * ks, 0.0f);
+      }
+    } else {
+      const float* kp = (const float*)(page + slot * cv.stride);
+      for (int h = 0; h < nI; ++h) {
+        float d = 0.0f;
+        for (int c = 0; c < cI; ++c) d += qs[h * cI + c] * kp[c];
+        acc += w[(int64_t)r * nI + h] * fmaxf(d, 0.0f);
+      }
+    }
+    out = acc;
+  }
+  scores[(int64_t)r * stride + s] = out;
+}
+
+// ------------------------------------------------------------------ scores, fp8 MFMA (nI = 8, cI = 64)
+// Block: 256 threads (4 waves).  blockIdx.x = group of QPW query rows,
+// blockIdx.y = chunk of kChunk keys; wave w takes key blocks w, w+4, ...
+template <int QPW>
+__global__ void __launch_bounds__(256) index_scores_fp8_kernel(CacheView cv, int m, int q_fmt, const void* qI,
+                                                               const float* w, const int32_t* pos, int seq_fixed,
+                                                               int n_rows, float* scores, int64_t stride) {
+  constexpr int nI = 8, cI = 64, kChunk = 1024;
+  __shared__ __attribute__((aligned(16))) uint8_t qcodes[32 * cI];  // A operand rows: (query, head)
+  __shared__ float wq[32];                                          // w * query scale per row
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r0 = blockIdx.x * QPW;
+
+  // prologue: quantize QPW*8 query-head rows (one wavefront per row, 64 channels)
+  for (int row = wave; row < 32; row += 4) {
+    int qq = row / nI, h = row % nI, r = r0 + qq;
+    bool valid = qq < QPW && r < n_rows;
+    float v = valid ? load_act(qI, q_fmt, ((int64_t)r * nI + h) * cI + lane) : 0.0f;
+    int e = pow2_exponent(wave_max(fabsf(v)));
+    qcodes[row * cI + lane] = valid ? (uint8_t)e4m3_encode(ldexpf(v, -e)) : 0;
+    if (lane == 0) wq[row] = valid ? w[(int64_t)r * nI + h] * ldexpf(1.0f, e) : 0.0f;
+  }
+  __syncthreads();
+
+  int64_t ne[QPW];
+  int64_t ne_max = 0;
+#pragma unroll
+  for (int qq = 0; qq < QPW; ++qq) {
+    int r = r0 + qq;
+    int t = r < n_rows ? (pos ? pos[r] : r) : 0;
+    ne[qq] = r < n_rows ? (t / m < stride ? t / m : stride) : 0;
+    ne_max = ne[qq] > ne_max ? ne[qq] : ne_max;
+  }
+  const int64_t k0 = (int64_t)blockIdx.y * kChunk;
+  if (k0 >= ne_max) return;
+  const int64_t k1 = (k0 + kChunk < ne_max) ? k0 + kChunk : ne_max;
+  const int seq = seq_fixed >= 0 ? seq_fixed : r0;   // decode: one row per group, row == sequence
+
+  // A operand: row lane%32, bytes [32*(lane/32), +32)
+  i32x8 a;
+  {
+    const int* src = (const int*)(qcodes + (lane & 31) * cI + 32 * (lane >> 5));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = src[i];
+  }
+  float wl[QPW][4];
+#pragma unroll
+  for (int qq = 0; qq < QPW; ++qq)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) wl[qq][v] = wq[qq * nI + 4 * (lane >> 5) + v];
+
+  for (int64_t kb = k0 + 32 * wave; kb < k1; kb += 128) {
+    const int64_t s = kb + (lane & 31);
+    uint8_t* page = s < k1 ? cv.page_of(seq, s) : nullptr;
+    i32x8 bop = {0, 0, 0, 0, 0, 0, 0, 0};
+    float ks = 0.0f;
+    if (page != nullptr) {
+      int slot = cv.slot_of(s);
+      const u32x4* kp = (const u32x4*)(page + slot * cI + 32 * (lane >> 5));
+      u32x4 v0 = kp[0], v1 = kp[1];
+      bop[0] = v0[0]; bop[1] = v0[1]; bop[2] = v0[2]; bop[3] = v0[3];
+      bop[4] = v1[0]; bop[5] = v1[1]; bop[6] = v1[2]; bop[7] = v1[3];
+      ks = ((const float*)(page + (cI << cv.page_shift)))[slot];
+    }
+    f32x16 acc = {};
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bop, acc, 0, 0, 0, 127, 0, 127);
+    // acc[v]: row 8*(v/4) + 4*(lane/32) + v%4 = (query v/4, head 4*(lane/32) + v%4), key lane%32
+#pragma unroll
+    for (int qq = 0; qq < QPW; ++qq) {
+      float part = 0.0f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) part += wl[qq][v] * fmaxf(acc[4 * qq + v], 0.0f);
+      part += __shfl_xor(part, 32, 64);
+      if (lane < 32 && s < ne[qq]) {
+        float sc = page != nullptr ? part * ks : -INFINITY;
+        scores[(int64_t)(r0 + qq) * stride + s] = sc;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ top-k
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkLdsKeys = 16384;
+
+struct TopkShared {
+  uint32_t keys[kTopkLdsKeys];
+  uint32_t hist[256];
+  uint32_t wsum[kTopkThreads / 64];
+  uint32_t wsum2[kTopkThreads / 64];
+  uint32_t sel_digit, sel_krem;
+};
+
+__device__ __forceinline__ uint32_t get_key(const TopkShared& sh, bool in_lds, const float* row, int64_t s) {
+  return in_lds ? sh.keys[s] : order_key(row[s]);
+}
+
+// Exclusive prefix of 0/1 flags over the block (index order = thread order).
+// Returns the prefix for this thread; *total receives the block total.
+__device__ __forceinline__ uint32_t block_flag_prefix(bool f, uint32_t* wsum, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  uint64_t b = __ballot(f);
+  uint32_t in_wave = __popcll(b & ((1ull << lane) - 1ull));
+  if (lane == 0) wsum[wave] = __popcll(b);
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+  for (int i = 0; i < nw; ++i) {
+    uint32_t c = wsum[i];
+    before += i < wave ? c : 0;
+    tot += c;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + in_wave;
+}
+
+__global__ void __launch_bounds__(kTopkThreads) topk_rows_kernel(const float* scores, int64_t stride,
+                                                                 const int32_t* pos, int m, int k, int32_t* out_idx,
+                                                                 int32_t* out_cnt, float* out_score) {
+  __shared__ TopkShared sh;
+  const int r = blockIdx.x;
+  const int t = pos ? pos[r] : r;
+  const int64_t n = t / m < stride ? t / m : stride;
+  const float* row = scores + (int64_t)r * stride;
+  int32_t* oi = out_idx + (int64_t)r * k;
+  float* os = out_score ? out_score + (int64_t)r * k : nullptr;
+  const int tid = threadIdx.x;
+
+  if (n <= k) {  // every eligible block is kept
+    for (int j = tid; j < k; j += blockDim.x) {
+      oi[j] = j < n ? j : -1;
+      if (os) os[j] = j < n ? row[j] : -INFINITY;
+    }
+    if (tid == 0) out_cnt[r] = (int32_t)n;
+    return;
+  }
+  const bool in_lds = n <= kTopkLdsKeys;
+  if (in_lds)
+    for (int64_t s = tid; s < n; s += blockDim.x) sh.keys[s] = order_key(row[s]);
+
+  uint32_t prefix = 0, krem = (uint32_t)k;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
+    for (int i = tid; i < 256; i += blockDim.x) sh.hist[i] = 0;
+    __syncthreads();
+    for (int64_t s = tid; s < n; s += blockDim.x) {
+      uint32_t key = get_key(sh, in_lds, row, s);
+      if ((key & hi_mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // lane L owns digits 4L..4L+3; suffix counts from the top digit down
+      uint32_t c0 = sh.hist[4 * tid], c1 = sh.hist[4 * tid + 1], c2 = sh.hist[4 * tid + 2], c3 = sh.hist[4 * tid + 3];
+      uint32_t lsum = c0 + c1 + c2 + c3;
+      uint32_t incl = lsum;  // inclusive suffix sum over lanes >= tid
+      for (int o = 1; o < 64; o <<= 1) {
+        uint32_t v = __shfl_down(incl, o, 64);
+        if (tid + o < 64) incl += v;
+      }
+      uint32_t suffix_above = incl - lsum;
+      uint32_t cnts[4] = {c0, c1, c2, c3};
+      uint32_t cum = suffix_above;  // keys with digit > 4*tid+3
+      for (int d = 3; d >= 0; --d) {
+        uint32_t nc = cum + cnts[d];
+        if (cum < krem && nc >= krem) {
+          sh.sel_digit = 4 * tid + d;
+          sh.sel_krem = krem - cum;
+        }
+        cum = nc;
+      }
+    }
+    __syncthreads();
+    prefix |= sh.sel_digit << shift;
+    krem = sh.sel_krem;
+    __syncthreads();
+  }
+  // prefix == T (the k-th largest key); krem == how many keys equal to T to keep
+  const uint32_t T = prefix, need_eq = krem;
+  uint32_t eq_seen = 0, taken = 0;
+  for (int64_t base = 0; base < n; base += blockDim.x) {
+    int64_t s = base + tid;
+    uint32_t key = s < n ? get_key(sh, in_lds, row, s) : 0u;
+    bool gt = s < n && key > T, eq = s < n && key == T;
+    uint32_t eq_tot, tk_tot;
+    uint32_t eq_rank = eq_seen + block_flag_prefix(eq, sh.wsum, &eq_tot);
+    bool take = gt || (eq && eq_rank < need_eq);
+    uint32_t o = taken + block_flag_prefix(take, sh.wsum2, &tk_tot);
+    if (take && o < (uint32_t)k) {
+      oi[o] = (int32_t)s;
+      if (os) os[o] = row[s];
+    }
+    eq_seen += eq_tot;
+    taken += tk_tot;
+  }
+  if (tid == 0) out_cnt[r] = k;
+}
+
+// ------------------------------------------------------------------ launchers
+hipError_t launch_index_scores(const CacheView& cv, const ca_index_params& p, const void* qI, const float* w,
+                               const int32_t* pos, int seq_fixed, int n_rows, int64_t max_pos, float* scores,
+                               int64_t stride, hipStream_t st) {
+  if (n_rows == 0) return hipSuccess;
+  int64_t max_ne = max_pos / p.ratio;
+  if (max_ne == 0) return hipSuccess;
+  if (cv.fmt == CA_E4M3 && p.n_heads == 8 && p.dim == 64) {
+    const int64_t chunks = (max_ne + 1023) / 1024;
+    if (seq_fixed >= 0) {
+      dim3 grid((unsigned)((n_rows + 3) / 4), (unsigned)chunks);
+      hipLaunchKernelGGL(index_scores_fp8_kernel<4>, grid, dim3(256), 0, st, cv, p.ratio, p.q_format, qI, w, pos,
+                         seq_fixed, n_rows, scores, stride);
+    } else {
+      dim3 grid((unsigned)n_rows, (unsigned)chunks);
+      hipLaunchKernelGGL(index_scores_fp8_kernel<1>, grid, dim3(256), 0, st, cv, p.ratio, p.q_format, qI, w, pos,
+                         seq_fixed, n_rows, scores, stride);
+    }
+  } else {
+    dim3 grid((unsigned)n_rows, (unsigned)((max_ne + 255) / 256));
+    size_t sm = sizeof(float) * p.n_heads * p.dim;
+    hipLaunchKernelGGL(index_scores_generic_kernel, grid, dim3(256), sm, st, cv, p.n_heads, p.dim, p.ratio,
+                       p.q_format, qI, w, pos, seq_fixed, scores, stride);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const float* scores, int64_t stride, const int32_t* pos, int m, int k, int n_rows,
+                       int32_t* out_idx, int32_t* out_cnt, float* out_score, hipStream_t st) {
+  if (n_rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_rows_kernel, dim3(n_rows), dim3(kTopkThreads), 0, st, scores, stride,
+                     pos, m, k, out_idx, out_cnt, out_score);
+  return hipGetLastError();
+}
+
+}  // namespace ca

@@ -1,0 +1,61 @@
+// Internal launcher declarations of the CSA / HCA kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+
+namespace ca {
+
+hipError_t launch_compress_prefill(const CacheView& cv, int seq, const ca_compress_params& p, const void* Ca,
+                                   const void* Za, const void* Cb, const void* Zb, const float* Ba,
+                                   const float* Bb, const float* gain, int64_t L, hipStream_t st);
+hipError_t launch_compress_decode(const CacheView& cv, const ca_compress_params& p, const void* new_rows,
+                                  const int32_t* pos, int B, float* tail, const float* Ba, const float* Bb,
+                                  const float* gain, hipStream_t st);
+hipError_t launch_store_entries(const CacheView& cv, int seq, int64_t first, int64_t n, const float* src,
+                                const float* gain, float eps, int apply_rope, double base, int pos_stride,
+                                hipStream_t st);
+hipError_t launch_window_append(const ca_window_params& p, const void* raw, const float* gain, const int32_t* pos,
+                                const int32_t* seq, int T, void* window, int W, int S, hipStream_t st);
+
+hipError_t launch_index_scores(const CacheView& cv, const ca_index_params& p, const void* qI, const float* w,
+                               const int32_t* pos, int seq_fixed, int n_rows, int64_t max_pos, float* scores,
+                               int64_t stride, hipStream_t st);
+hipError_t launch_topk(const float* scores, int64_t stride, const int32_t* pos, int m, int k, int n_rows,
+                       int32_t* out_idx, int32_t* out_cnt, float* out_score, hipStream_t st);
+
+// Everything an attention launch needs (CSA or HCA, prefill or decode).
+struct AttendArgs {
+  const void* q;
+  const float* q_gain;
+  int q_fmt, n_heads, D, R, n_win;
+  float scale_log2;  // logit scale * log2(e)
+  float eps;
+  double base;
+  const int32_t* pos;  // nullptr: position == row (prefill)
+  int seq_fixed;       // >= 0: every row is this cache sequence (prefill); < 0: row r is sequence r
+  int n_rows;
+  CacheView kv;
+  int mode;            // 0: CSA list idx/cnt, 1: HCA dense
+  int ratio;
+  const int32_t* idx;
+  const int32_t* cnt;
+  int k;
+  const void* win;
+  int win_fmt, W;
+  const float* sink;
+  void* out;
+  int out_fmt;
+  float* lse;
+  int split_items;     // 0: one split per row (direct epilogue)
+  int max_splits;
+  float* part_o;       // [rows, max_splits, n_heads, D]
+  float* part_ml;      // [rows, max_splits, n_heads, 2]
+};
+
+constexpr int kDecodeSplitItems = 128;
+
+bool attend_mfma_supported(const AttendArgs& a);
+hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
+
+}  // namespace ca

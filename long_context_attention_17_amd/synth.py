@@ -130,7 +130,8 @@ def decode_layer(cfg, layer: str, device, ctx: torch.Tensor | None = None) -> di
         offs.append(offs[-1] + n)
     out["entry_offsets"] = offs
     out["entries"] = normal((offs[-1], D), sd, s, "entries", device)
-    pt, n_pool = page_table(n_ent, cfg.page, s, device)
+    # one spare slot per sequence for the entry the new token may complete
+    pt, n_pool = page_table([n + 1 for n in n_ent], cfg.page, s, device)
     out["page_table"], out["n_pool_pages"] = pt, n_pool
     if layer == "csa":
         si = 1.0 / math.sqrt(cfg.cI)

@@ -1,0 +1,388 @@
+"""GPU parity at sizes the oracle finishes in seconds (full comparison of every
+row), covering several tiles and ragged tails of every kernel, both record
+formats of the MFMA attention path, the fp32 generic path, and the decode
+split/combine path."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import pipeline as opl
+from gpu_util import (check_out, check_stored, check_topk, f64, gpu_cache_from, log, pool_values, to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+def _ca():
+    from long_context_attention_17_amd import binding, configs, layers, synth
+    return binding, configs, layers, synth
+
+
+def _cfg(**kw):
+    from long_context_attention_17_amd.configs import Config
+    base = dict(name="small", phase="prefill", D=512, R=64, n_h=64, act="bf16", kv="bf16", csa=True, m=4, k=64,
+                n_win=128, nI=8, cI=64, idx="e4m3", hca=True, m_hca=128, L=777, seed=4242)
+    base.update(kw)
+    return Config(**base)
+
+
+def _prefill_case(cfg, layer):
+    ca, configs, layers, synth = _ca()
+    inp = synth.prefill_layer(cfg, layer, "cuda")
+    ratio = cfg.m if layer == "csa" else cfg.m_hca
+    pt, n_pool = synth.page_table([cfg.L // ratio], cfg.page, cfg.seed)
+    return inp, pt, n_pool
+
+
+def run_csa_prefill(cfg):
+    ca, configs, layers, synth = _ca()
+    log(f"[csa prefill] {cfg.name} L={cfg.L} D={cfg.D} n_h={cfg.n_h} kv={cfg.kv} idx={cfg.idx}")
+    inp, pt, n_pool = _prefill_case(cfg, "csa")
+    n_e = cfg.L // cfg.m
+    orc = opl.csa_prefill(cfg, inp, to_np(pt)[0], n_pool)
+    gp = layers.CSAPrefill(cfg, inp, pt.cuda(), n_pool)
+    # stage 1: compressors (main KV with epilogue, indexer keys)
+    gp.compress()
+    gv = pool_values(gp.kv, 0, n_e)
+    ov = oracle.load_entries(oracle.FMT_BY_NAME[cfg.kv], cfg.D, cfg.R, cfg.page, orc["pool"], to_np(pt)[0], 0, n_e)
+    check_stored(gv, ov, cfg.kv, cfg.D, cfg.R, "csa main entries")
+    gk = pool_values(gp.ik, 0, n_e)
+    ok = oracle.load_entries(oracle.FMT_BY_NAME[cfg.idx], cfg.cI, 0, cfg.page, orc["ipool"], to_np(pt)[0], 0, n_e)
+    check_stored(gk, ok, cfg.idx, what="indexer keys")
+    # stage 2: window
+    gp.window_append()
+    gw = f64(gp.window) if cfg.act == "f32" else oracle.bf16_decode(to_np(gp.window.view(torch.int16)).view(np.uint16))
+    ow = orc["window"].astype(np.float64) if cfg.act == "f32" else oracle.bf16_decode(orc["window"])
+    check_stored(gw[0], ow[0], cfg.act, what="window")
+    # stage 3: indexer + top-k on the oracle's key bytes
+    ik_o = gpu_cache_from(orc["ipool"], to_np(pt), oracle.FMT_BY_NAME[cfg.idx], cfg.cI, 0, cfg.page)
+    all_s = torch.full((cfg.L, max(1, n_e)), float("nan"), device="cuda")
+    gidx = torch.empty(cfg.L, cfg.k, dtype=torch.int32, device="cuda")
+    gcnt = torch.empty(cfg.L, dtype=torch.int32, device="cuda")
+    ca.index_topk_prefill(layers.index_params(cfg), inp["qI"], inp["w"], 0, ik_o, gidx, gcnt, all_scores=all_s)
+    torch.cuda.synchronize()
+    gsc = to_np(all_s)
+    sc_err = np.nanmax(np.abs(gsc - orc["scores"])) if n_e else 0.0
+    log(f"  indexer scores max-abs vs oracle: {sc_err:.3e}")
+    swaps = check_topk(to_np(gidx), to_np(gcnt), orc["idx"], orc["cnt"], gsc, orc["scores"], cfg.k)
+    log(f"  top-k: {swaps} boundary swaps over {cfg.L} rows")
+    # stage 4: attention on the oracle's entry bytes, window and index sets
+    kv_o = gpu_cache_from(orc["pool"], to_np(pt), oracle.FMT_BY_NAME[cfg.kv], cfg.D, cfg.R, cfg.page)
+    win_o = torch.from_numpy(orc["window"].view(np.int16) if cfg.act == "bf16" else orc["window"]).cuda()
+    if cfg.act == "bf16":
+        win_o = win_o.view(torch.bfloat16)
+    out = torch.empty_like(gp.out)
+    lse = torch.empty(cfg.L, cfg.n_h, device="cuda")
+    ca.csa_attend_prefill(gp.ap, inp["q"], inp["g_q"], kv_o, 0, torch.from_numpy(orc["idx"]).cuda(),
+                          torch.from_numpy(orc["cnt"]).cuda(), cfg.m, win_o, inp["sink"], out, lse)
+    torch.cuda.synchronize()
+    check_out(f64(out), orc["out"], cfg.act, "csa attention (stage inputs from the oracle)")
+    assert np.isfinite(to_np(lse)).all()
+    # end to end on the GPU's own intermediates
+    gp.index_topk()
+    gp.attend()
+    torch.cuda.synchronize()
+    swaps = check_topk(to_np(gp.idx), to_np(gp.cnt), orc["idx"], orc["cnt"], gsc, orc["scores"], cfg.k,
+                       what="end-to-end top-k")
+    same = np.array([np.array_equal(to_np(gp.idx)[r], orc["idx"][r]) for r in range(cfg.L)])
+    check_out(f64(gp.out)[same], orc["out"][same], cfg.act, f"csa end-to-end ({same.sum()} rows with equal sets)")
+    return gp, orc
+
+
+def run_hca_prefill(cfg):
+    ca, configs, layers, synth = _ca()
+    log(f"[hca prefill] {cfg.name} L={cfg.L} D={cfg.D} n_h={cfg.n_h} kv={cfg.kv} m'={cfg.m_hca}")
+    inp, pt, n_pool = _prefill_case(cfg, "hca")
+    n_e = cfg.L // cfg.m_hca
+    orc = opl.hca_prefill(cfg, inp, to_np(pt)[0], n_pool)
+    gp = layers.HCAPrefill(cfg, inp, pt.cuda(), n_pool)
+    gp.compress()
+    if n_e:
+        gv = pool_values(gp.kv, 0, n_e)
+        ov = oracle.load_entries(oracle.FMT_BY_NAME[cfg.kv], cfg.D, cfg.R, cfg.page, orc["pool"], to_np(pt)[0], 0, n_e)
+        check_stored(gv, ov, cfg.kv, cfg.D, cfg.R, "hca entries", max_frac=0.05)
+    gp.window_append()
+    kv_o = gpu_cache_from(orc["pool"], to_np(pt), oracle.FMT_BY_NAME[cfg.kv], cfg.D, cfg.R, cfg.page)
+    win_o = torch.from_numpy(orc["window"].view(np.int16) if cfg.act == "bf16" else orc["window"]).cuda()
+    if cfg.act == "bf16":
+        win_o = win_o.view(torch.bfloat16)
+    out = torch.empty_like(gp.out)
+    ca.hca_attend_prefill(gp.ap, inp["q"], inp["g_q"], kv_o, 0, cfg.m_hca, win_o, inp["sink"], out)
+    torch.cuda.synchronize()
+    check_out(f64(out), orc["out"], cfg.act, "hca attention (stage inputs from the oracle)")
+    gp.attend()
+    torch.cuda.synchronize()
+    check_out(f64(gp.out), orc["out"], cfg.act, "hca end-to-end")
+    return gp, orc
+
+
+def test_cfg1_tiny_fp32_prefill():
+    from long_context_attention_17_amd.configs import CONFIGS
+    cfg = CONFIGS[1]
+    run_csa_prefill(cfg)
+    run_hca_prefill(cfg)
+
+
+def test_mfma_csa_prefill_bf16_ragged():
+    run_csa_prefill(_cfg(L=777))
+
+
+def test_mfma_hca_prefill_bf16_ragged():
+    run_hca_prefill(_cfg(L=1500, n_h=128))
+
+
+def test_generic_path_bf16_small_dim():
+    """D = 128 bf16 takes the generic kernels (MFMA path needs D = 512)."""
+    run_csa_prefill(_cfg(D=128, R=16, n_h=4, L=300, k=16, n_win=32))
+    run_hca_prefill(_cfg(D=128, R=16, n_h=4, L=300, m_hca=32, n_win=32))
+
+
+def _decode_case(cfg):
+    ca, configs, layers, synth = _ca()
+    ctx = synth.decode_contexts(cfg)
+    out = {}
+    for layer in ("csa", "hca"):
+        inp = synth.decode_layer(cfg, layer, "cuda", ctx)
+        out[layer] = inp
+    return ctx, out
+
+
+def run_decode(cfg, seqs=None, check_batch_invariance=True):
+    ca, configs, layers, synth = _ca()
+    ctx, inps = _decode_case(cfg)
+    log(f"[decode] {cfg.name} B={cfg.B} ctx={ctx.tolist()[:8]} n_h={cfg.n_h} kv={cfg.kv}")
+    results = {}
+    for layer in ("csa", "hca"):
+        inp = inps[layer]
+        st = opl.decode_state(cfg, inp)
+        gl = layers.DecodeLayer(cfg, inp)
+        torch.cuda.synchronize()
+        B = cfg.B
+        # cache contents written by the store kernel vs the oracle encoder
+        for b in range(min(B, 3)):
+            n = inp["n_entries"][b]
+            gv = pool_values(gl.kv, b, n)
+            ov = oracle.load_entries(oracle.FMT_BY_NAME[cfg.kv], cfg.D, cfg.R, cfg.page, st["pool"],
+                                     st["page_table"][b], 0, n)
+            check_stored(gv, ov, cfg.kv, cfg.D, cfg.R, f"{layer} cache seq {b}")
+        # window ring after the step's append
+        gl.append_token()
+        torch.cuda.synchronize()
+        gw = oracle.bf16_decode(to_np(gl.window.view(torch.int16)).view(np.uint16)) if cfg.act == "bf16" else f64(gl.window)
+        ow = oracle.bf16_decode(st["window"]) if cfg.act == "bf16" else st["window"].astype(np.float64)
+        check_stored(gw, ow, cfg.act, what=f"{layer} window ring")
+        # compressor tail ring + emitted entries
+        gl.compress()
+        torch.cuda.synchronize()
+        for b in range(B):
+            em = opl.decode_compress(cfg, inp, b)
+            if em is None:
+                continue
+            i, e_main, e_idx = em
+            for fmt_name, vals_raw, cache, dim, rope_dim, main in (
+                    (cfg.kv, e_main, gl.kv, cfg.D, cfg.R, True),
+                    (cfg.idx, e_idx, gl.ik, cfg.cI, 0, False)):
+                if vals_raw is None:
+                    continue
+                fmtn = oracle.FMT_BY_NAME[fmt_name]
+                tmp = np.zeros(oracle.page_bytes(fmtn, dim, rope_dim, cfg.page), np.uint8)
+                ptr = np.zeros(i // cfg.page + 1, np.int32)
+                oracle.finish_store(fmtn, dim, rope_dim, cfg.page, tmp, ptr, i, vals_raw[None],
+                                    f64(inp["g_kv"])[:dim] if main else None, cfg.eps, cfg.rope_base, inp["ratio"],
+                                    main, main)
+                ov = oracle.load_entries(fmtn, dim, rope_dim, cfg.page, tmp, ptr, i, 1)
+                gv = pool_values(cache, b, i + 1)[i:i + 1]
+                check_stored(gv, ov, fmt_name, dim, rope_dim, f"{layer} decode-emitted entry seq {b}", max_frac=0.05)
+        if layer == "csa":
+            step = opl.csa_decode_step(cfg, inp, st)
+            ik_o = gpu_cache_from(st["ipool"], st["page_table"], oracle.FMT_BY_NAME[cfg.idx], cfg.cI, 0, cfg.page)
+            n_cols = step["scores"].shape[1]
+            all_s = torch.full((B, n_cols), float("nan"), device="cuda")
+            gidx = torch.empty(B, cfg.k, dtype=torch.int32, device="cuda")
+            gcnt = torch.empty(B, dtype=torch.int32, device="cuda")
+            ca.index_topk_decode(gl.ip, inp["qI"], inp["w"], gl.pos, gl.max_pos, ik_o, gidx, gcnt, all_scores=all_s)
+            torch.cuda.synchronize()
+            gsc = to_np(all_s)
+            log(f"  indexer scores max-abs vs oracle: {np.nanmax(np.abs(gsc - step['scores'])):.3e}")
+            swaps = check_topk(to_np(gidx), to_np(gcnt), step["idx"], step["cnt"], gsc, step["scores"], cfg.k)
+            log(f"  top-k: {swaps} boundary swaps")
+        else:
+            step = opl.hca_decode_step(cfg, inp, st)
+        kv_o = gpu_cache_from(st["pool"], st["page_table"], oracle.FMT_BY_NAME[cfg.kv], cfg.D, cfg.R, cfg.page)
+        win_o = torch.from_numpy(st["window"].view(np.int16) if cfg.act == "bf16" else st["window"]).cuda()
+        if cfg.act == "bf16":
+            win_o = win_o.view(torch.bfloat16)
+        out = torch.empty_like(gl.out)
+        if layer == "csa":
+            ca.csa_attend_decode(gl.ap, inp["q"], inp["g_q"], kv_o, torch.from_numpy(step["idx"]).cuda(),
+                                 torch.from_numpy(step["cnt"]).cuda(), cfg.m, gl.pos, gl.max_pos, win_o, inp["sink"],
+                                 out)
+        else:
+            ca.hca_attend_decode(gl.ap, inp["q"], inp["g_q"], kv_o, cfg.m_hca, gl.pos, gl.max_pos, win_o, inp["sink"],
+                                 out)
+        torch.cuda.synchronize()
+        check_out(f64(out), step["out"], cfg.act, f"{layer} decode attention (stage inputs from the oracle)")
+        # determinism + batch invariance of the attention
+        if check_batch_invariance:
+            out2 = torch.empty_like(out)
+            if layer == "csa":
+                ca.csa_attend_decode(gl.ap, inp["q"], inp["g_q"], kv_o, torch.from_numpy(step["idx"]).cuda(),
+                                     torch.from_numpy(step["cnt"]).cuda(), cfg.m, gl.pos, gl.max_pos, win_o,
+                                     inp["sink"], out2)
+            else:
+                ca.hca_attend_decode(gl.ap, inp["q"], inp["g_q"], kv_o, cfg.m_hca, gl.pos, gl.max_pos, win_o,
+                                     inp["sink"], out2)
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int16) if cfg.act == "bf16" else out,
+                               out2.view(torch.int16) if cfg.act == "bf16" else out2), "decode attention not deterministic"
+        # end to end (GPU's own caches and top-k)
+        if layer == "csa":
+            gl.index_topk()
+        gl.attend()
+        torch.cuda.synchronize()
+        if layer == "csa":
+            same = np.array([np.array_equal(to_np(gl.idx)[b], step["idx"][b]) for b in range(B)])
+        else:
+            same = np.ones(B, bool)
+        check_out(f64(gl.out)[same], step["out"][same], cfg.act, f"{layer} decode end-to-end ({same.sum()} rows)")
+        results[layer] = (gl, st, step)
+    return results
+
+
+def test_mfma_decode_fp8_small():
+    cfg = _cfg(name="small_decode", phase="decode", kv="fp8mix", n_h=128, k=64, B=5, ctx_lo=300, ctx_hi=3000,
+               L=0, seed=5151)
+    run_decode(cfg)
+
+
+def test_generic_decode_fp32_small():
+    cfg = _cfg(name="small_decode_f32", phase="decode", D=64, R=8, n_h=8, act="f32", kv="f32", idx="f32", nI=4,
+               cI=32, k=16, n_win=64, m_hca=64, B=4, ctx_lo=100, ctx_hi=900, L=0, seed=6161)
+    run_decode(cfg)
+
+
+def test_decode_batch_invariance():
+    """A sequence decoded alone gives bitwise the same output as inside a batch."""
+    ca, configs, layers, synth = _ca()
+    cfg = _cfg(name="bi", phase="decode", kv="fp8mix", n_h=64, k=64, B=4, ctx_lo=500, ctx_hi=2500, L=0, seed=777)
+    ctx = synth.decode_contexts(cfg)
+    inp = synth.decode_layer(cfg, "hca", "cuda", ctx)
+    full = layers.DecodeLayer(cfg, inp)
+    full.append_token()
+    full.attend()
+    b = 2
+    sub = dict(inp)
+    for key in ("q", "kv_raw", "tail", "new_rows"):
+        sub[key] = inp[key][b:b + 1].contiguous()
+    sub["pos"], sub["ctx"] = inp["pos"][b:b + 1], inp["ctx"][b:b + 1]
+    a, e = inp["entry_offsets"][b], inp["entry_offsets"][b + 1]
+    sub["entries"] = inp["entries"][a:e]
+    sub["entry_offsets"] = [0, e - a]
+    sub["n_entries"] = [inp["n_entries"][b]]
+    sub["page_table"] = inp["page_table"][b:b + 1]
+    one = layers.DecodeLayer(cfg, sub)
+    one.append_token()
+    one.attend()
+    torch.cuda.synchronize()
+    assert torch.equal(full.out[b].view(torch.int16), one.out[0].view(torch.int16))
+
+
+def test_edge_cases_prefill():
+    """Ragged and degenerate prefill shapes: fewer tokens than one block (no entries), a length
+    that is not a multiple of the ratio, and k larger than every row's eligible count."""
+    for L in (3, 5, 130):
+        run_csa_prefill(_cfg(L=L, k=512))
+        run_hca_prefill(_cfg(L=L))
+
+
+def test_missing_pages_are_skipped():
+    """Entries in pages marked missing (-1) are never read: attention equals the oracle with
+    those entries removed from the index lists."""
+    ca, configs, layers, synth = _ca()
+    cfg = _cfg(L=520, k=200)
+    inp, pt, n_pool = _prefill_case(cfg, "csa")
+    orc = opl.csa_prefill(cfg, inp, to_np(pt)[0], n_pool)
+    pt_miss = to_np(pt).copy()
+    pt_miss[0, 1] = -1                               # entries 64..127 become unavailable
+    kv_o = gpu_cache_from(orc["pool"], pt_miss, oracle.FMT_BY_NAME[cfg.kv], cfg.D, cfg.R, cfg.page)
+    win_o = torch.from_numpy(orc["window"].view(np.int16)).cuda().view(torch.bfloat16)
+    idx = orc["idx"].copy()
+    cnt = orc["cnt"].copy()
+    out = torch.empty(cfg.L, cfg.n_h, cfg.D, dtype=torch.bfloat16, device="cuda")
+    ap = layers.attend_params(cfg)
+    ca.csa_attend_prefill(ap, inp["q"], inp["g_q"], kv_o, 0, torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda(),
+                          cfg.m, win_o, inp["sink"], out)
+    torch.cuda.synchronize()
+    idx2 = np.full_like(idx, -1)
+    cnt2 = np.zeros_like(cnt)
+    for r in range(cfg.L):
+        keep = [e for e in idx[r, :cnt[r]] if not (64 <= e < 128)]
+        idx2[r, :len(keep)] = keep
+        cnt2[r] = len(keep)
+    ref = oracle.attend(f64(inp["q"]), np.arange(cfg.L), oracle.FMT_BY_NAME[cfg.kv], cfg.page, orc["pool"], to_np(pt),
+                        [cfg.L // cfg.m], 0, cfg.m, orc["window"], cfg.n_win, f64(inp["sink"]), cfg.R, idx=idx2,
+                        cnt=cnt2)
+    check_out(f64(out), ref, "bf16", "attention with a missing page")
+
+
+def test_topk_ties_lowest_index():
+    """Planted duplicate indexer keys give exactly equal scores; the lower index must win."""
+    ca, configs, layers, synth = _ca()
+    cfg = _cfg(L=900, k=37)
+    inp, pt, n_pool = _prefill_case(cfg, "csa")
+    n_e = cfg.L // cfg.m
+    keys = synth.normal((n_e, cfg.cI), 1 / 8, 99, "ikeys", "cpu")
+    keys[100:160] = keys[40]                        # 61 identical keys
+    keys[30:35] = keys[200]
+    pool = opl.new_pool(n_pool, oracle.FMT_E4M3, cfg.cI, 0, cfg.page)
+    oracle.finish_store(oracle.FMT_E4M3, cfg.cI, 0, cfg.page, pool, to_np(pt)[0], 0, f64(keys), norm=False, rope=False)
+    rows = np.arange(cfg.L)
+    qv = opl.indexer_query_values(f64(inp["qI"]), "e4m3")
+    sc, ne = oracle.index_scores(qv, f64(inp["w"]), rows, cfg.m, oracle.FMT_E4M3, cfg.page, pool, to_np(pt), [n_e],
+                                 n_cols=n_e)
+    oidx, ocnt = oracle.topk(sc, ne, cfg.k)
+    ik = gpu_cache_from(pool, to_np(pt), oracle.FMT_E4M3, cfg.cI, 0, cfg.page)
+    gidx = torch.empty(cfg.L, cfg.k, dtype=torch.int32, device="cuda")
+    gcnt = torch.empty(cfg.L, dtype=torch.int32, device="cuda")
+    all_s = torch.full((cfg.L, n_e), float("nan"), device="cuda")
+    ca.index_topk_prefill(layers.index_params(cfg), inp["qI"], inp["w"], 0, ik, gidx, gcnt, all_scores=all_s)
+    torch.cuda.synchronize()
+    gs = to_np(all_s)
+    # tied scores are bitwise equal on the GPU too
+    for r in range(cfg.L):
+        if ne[r] > 160:
+            assert len(set(gs[r, 100:160].tolist())) == 1 and gs[r, 40] == gs[r, 100]
+    exact = check_topk(to_np(gidx), to_np(gcnt), oidx, ocnt, gs, sc, cfg.k, what="ties")
+    log(f"  ties: {exact} boundary swaps")
+    # where the tie straddles the boundary, the lowest indices of the tied group are kept
+    gi = to_np(gidx)
+    for r in range(cfg.L):
+        sel = set(gi[r, :gcnt[r].item()].tolist())
+        tied = [40] + list(range(100, 160))
+        tied = [s for s in tied if s < ne[r]]
+        chosen = [s for s in tied if s in sel]
+        assert chosen == tied[:len(chosen)], f"row {r}: tied keys not taken lowest-index first"
+
+
+def test_prefill_row_equals_decode_step():
+    """Decode at position t (split/combine path) reproduces prefill row t (single-pass path)."""
+    ca, configs, layers, synth = _ca()
+    cfg = _cfg(L=700, n_h=64, kv="bf16")
+    inp, pt, n_pool = _prefill_case(cfg, "hca")
+    gp = layers.HCAPrefill(cfg, inp, pt.cuda(), n_pool)
+    gp.run()
+    rows = [0, 127, 128, 400, 699]
+    B = len(rows)
+    pos = torch.tensor(rows, dtype=torch.int32, device="cuda")
+    pt_b = pt.repeat(B, 1).cuda().contiguous()
+    kv_b = ca.Cache(gp.kv.fmt, cfg.D, cfg.R, cfg.page, gp.kv.pool, pt_b)
+    win_b = gp.window.expand(B, -1, -1).contiguous()
+    out = torch.empty(B, cfg.n_h, cfg.D, dtype=torch.bfloat16, device="cuda")
+    ca.hca_attend_decode(gp.ap, inp["q"][rows].contiguous(), inp["g_q"], kv_b, cfg.m_hca, pos, max(rows), win_b,
+                         inp["sink"], out)
+    torch.cuda.synchronize()
+    d = (out.float() - gp.out[rows].float()).abs().max().item()
+    log(f"  decode vs prefill rows: max-abs {d:.3e}")
+    assert d <= 8e-3
