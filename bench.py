@@ -1,0 +1,378 @@
+"""Benchmark of the CSA + HCA hot path on one MI355X.
+
+Default workload: the million-token decode step (batch 8, context 2^20, 128
+query heads, D = 512, fp8-mixed pages): one CSA layer step (window append,
+compressor tail update, lightning indexer + top-k over 262,144 compressed
+entries, gathered attention over 2,048 + 128 items) and one HCA layer step
+(window append, compressor tail update, dense attention over 8,192 + 128
+items).  Other presets: --workload decode_mixed | prefill_csa_32k |
+prefill_hca_128k | tiny.
+
+Prints ONE JSON line.  Inputs are resident in HBM before the timed region; the
+timed region rotates independent replicas of every cache (so the per-step
+working set is not served from the 256 MB Infinity Cache).  Per-stage times
+come from HIP events recorded on the stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import copy
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "CSA+HCA attention tokens/s (prefill, decode) at 128K–1M ctx; % HBM/MFMA peak"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
+WORKLOADS = {"decode_1m": 5, "decode_mixed": 4, "prefill_csa_32k": 2, "prefill_hca_128k": 3, "tiny": 1}
+KERNEL_SOURCES = ["compress.hip", "indexer.hip", "attend.hip", "api.hip", "common.h", "kernels.h"]
+
+
+def progress(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "long_context_attention_17_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# ------------------------------------------------------------------ algorithmic work
+def decode_work(cfg, pos):
+    """Per-step algorithmic bytes / flops of each stage, summed over the batch."""
+    D, R, nh = cfg.D, cfg.R, cfg.n_h
+    rec = 584 if cfg.kv == "fp8mix" else (2 * D if cfg.kv == "bf16" else 4 * D)
+    w = {"index_bytes": 0, "index_flops": 0, "csa_flops": 0, "csa_bytes": 0, "hca_flops": 0, "hca_bytes": 0}
+    for t in pos:
+        ne = t // cfg.m
+        nw = min(t + 1, cfg.n_win)
+        w["index_bytes"] += ne * (cfg.cI + 4)
+        w["index_flops"] += 2 * cfg.nI * cfg.cI * ne
+        sel = min(ne, cfg.k)
+        w["csa_flops"] += 4 * nh * D * (sel + nw)
+        w["csa_bytes"] += sel * rec + nw * 2 * D + 2 * (2 * nh * D)
+        nh_e = t // cfg.m_hca
+        w["hca_flops"] += 4 * nh * D * (nh_e + nw)
+        w["hca_bytes"] += nh_e * rec + nw * 2 * D + 2 * (2 * nh * D)
+    return w
+
+
+def prefill_work(cfg):
+    L, D, nh = cfg.L, cfg.D, cfg.n_h
+    t = torch.arange(L, dtype=torch.float64)
+    nw = torch.clamp(t + 1, max=cfg.n_win)
+    w = {}
+    if cfg.csa:
+        ne = torch.floor(t / cfg.m)
+        w["csa_flops"] = float((4 * nh * D * (torch.clamp(ne, max=cfg.k) + nw)).sum())
+        w["index_flops"] = float((2 * cfg.nI * cfg.cI * ne).sum())
+    if cfg.hca:
+        w["hca_flops"] = float((4 * nh * D * (torch.floor(t / cfg.m_hca) + nw)).sum())
+    return w
+
+
+# ------------------------------------------------------------------ timing helpers
+class StageTimer:
+    """HIP events around each stage, on the current (kernel) stream."""
+
+    def __init__(self):
+        self.pairs = {}
+
+    def run(self, name, fn):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        self.pairs.setdefault(name, []).append((s, e))
+
+    def means_ms(self):
+        return {k: sum(s.elapsed_time(e) for s, e in v) / len(v) for k, v in self.pairs.items()}
+
+
+def replicate_decode_layer(dl, n):
+    """Independent copies of a decode layer's caches and state (same values, new memory)."""
+    from long_context_attention_17_amd import binding as ca
+    reps = [dl]
+    for _ in range(n - 1):
+        r = copy.copy(dl)
+        r.kv = ca.Cache(dl.kv.fmt, dl.kv.dim, dl.kv.rope_dim, dl.kv.page_size, dl.kv.pool.clone(), dl.kv.page_table)
+        if dl.ik is not None:
+            r.ik = ca.Cache(dl.ik.fmt, dl.ik.dim, dl.ik.rope_dim, dl.ik.page_size, dl.ik.pool.clone(),
+                            dl.ik.page_table)
+        r.window = dl.window.clone()
+        r.tail = dl.tail.clone()
+        if dl.layer == "csa":
+            r.itail = dl.itail.clone()
+        reps.append(r)
+    return reps
+
+
+# ------------------------------------------------------------------ workloads
+def bench_decode(cfg, steps, warmup, replicas, args):
+    from long_context_attention_17_amd import layers, synth
+    ctx = synth.decode_contexts(cfg)
+    layer_objs = {}
+    for name in ("csa", "hca"):
+        progress(f"building {name} decode state")
+        inp = synth.decode_layer(cfg, name, "cuda", ctx)
+        dl = layers.DecodeLayer(cfg, inp)
+        torch.cuda.synchronize()
+        del inp["entries"]
+        inp.pop("ikeys", None)
+        layer_objs[name] = replicate_decode_layer(dl, replicas)
+        torch.cuda.empty_cache()
+    torch.cuda.synchronize()
+
+    def step(i, timer=None):
+        c = layer_objs["csa"][i % replicas]
+        h = layer_objs["hca"][i % replicas]
+        stages = [("csa_window_append", c.append_token), ("csa_compress", c.compress),
+                  ("csa_index_topk", c.index_topk), ("csa_attend", c.attend),
+                  ("hca_window_append", h.append_token), ("hca_compress", h.compress), ("hca_attend", h.attend)]
+        for name, fn in stages:
+            if timer is None:
+                fn()
+            else:
+                timer.run(name, fn)
+
+    progress("warmup")
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    progress("timed steps")
+    # pass 1: whole-step timing with no per-stage events
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t0.record()
+    for i in range(steps):
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = t0.elapsed_time(t1) / steps
+    # pass 2: per-stage events
+    timer = StageTimer()
+    for i in range(steps):
+        step(i, timer)
+    torch.cuda.synchronize()
+    st = timer.means_ms()
+    pos = [int(x) for x in ctx.tolist()]
+    work = decode_work(cfg, pos)
+    value = cfg.B / (ms_step / 1e3)
+    # dominant stage and its roofline
+    roof_of = {
+        "csa_index_topk": ("hbm", work["index_bytes"], "GB/s"),
+        "csa_attend": ("mfma", work["csa_flops"], "TFLOP/s"),
+        "hca_attend": ("mfma", work["hca_flops"], "TFLOP/s"),
+    }
+    dom = max(roof_of, key=lambda k: st[k])
+    bound, units, unit = roof_of[dom]
+    if bound == "hbm":
+        achieved = units / (st[dom] / 1e3) / 1e9
+        peak = PEAK_HBM_GBS
+    else:
+        achieved = units / (st[dom] / 1e3) / 1e12
+        peak = PEAK_BF16_TFLOPS
+    step_bytes = work["index_bytes"] + work["csa_bytes"] + work["hca_bytes"]
+    extra = {
+        "stages_ms": {k: round(v, 5) for k, v in st.items()},
+        "step_hbm_bytes_algorithmic": step_bytes,
+        "step_hbm_frac_of_peak": round(step_bytes / (ms_step / 1e3) / (PEAK_HBM_GBS * 1e9), 4),
+        "stage_rooflines": {
+            "csa_index_topk": {"bound": "hbm", "achieved_GBs": round(work["index_bytes"] / st["csa_index_topk"] / 1e6, 1)},
+            "csa_attend": {"bound": "mfma", "achieved_TFLOPs": round(work["csa_flops"] / st["csa_attend"] / 1e9, 2)},
+            "hca_attend": {"bound": "mfma", "achieved_TFLOPs": round(work["hca_flops"] / st["hca_attend"] / 1e9, 2)},
+        },
+        "wall_s_timed": round(wall, 4),
+    }
+    config = {"workload": f"{cfg.name}: decode step of one CSA + one HCA layer, batch {cfg.B}, "
+                          f"context {cfg.ctx_lo}-{cfg.ctx_hi}, {cfg.n_h} heads, D={cfg.D}, kv {cfg.kv}, "
+                          f"k={cfg.k}, window {cfg.n_win}, m={cfg.m}, m'={cfg.m_hca}",
+              "batch": cfg.B, "context": [min(pos), max(pos)], "replicas": replicas}
+    roof = {"kernel": dom, "bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4)}
+    return value, ms_step, config, roof, extra, (ctx, layer_objs)
+
+
+def bench_prefill(cfg, steps, warmup, replicas, args):
+    from long_context_attention_17_amd import layers, synth
+    objs = []
+    if cfg.csa:
+        inp = synth.prefill_layer(cfg, "csa", "cuda")
+        pt, n_pool = synth.page_table([cfg.L // cfg.m], cfg.page, cfg.seed)
+        objs.append(("csa", layers.CSAPrefill(cfg, inp, pt.cuda(), n_pool)))
+    if cfg.hca:
+        inp = synth.prefill_layer(cfg, "hca", "cuda")
+        pt, n_pool = synth.page_table([cfg.L // cfg.m_hca], cfg.page, cfg.seed)
+        objs.append(("hca", layers.HCAPrefill(cfg, inp, pt.cuda(), n_pool)))
+
+    def step(timer=None):
+        for name, o in objs:
+            stages = [(f"{name}_compress", o.compress), (f"{name}_window_append", o.window_append)]
+            if name == "csa":
+                stages.append(("csa_index_topk", o.index_topk))
+            stages.append((f"{name}_attend", o.attend))
+            for sname, fn in stages:
+                timer.run(sname, fn) if timer else fn()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    t0.record()
+    for _ in range(steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = t0.elapsed_time(t1) / steps
+    timer = StageTimer()
+    for _ in range(steps):
+        step(timer)
+    torch.cuda.synchronize()
+    st = timer.means_ms()
+    work = prefill_work(cfg)
+    value = cfg.L / (ms_step / 1e3)
+    cands = {k: v for k, v in st.items() if k.endswith("_attend")}
+    dom = max(cands, key=cands.get)
+    flops = work["csa_flops"] if dom == "csa_attend" else work["hca_flops"]
+    achieved = flops / (st[dom] / 1e3) / 1e12
+    roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    extra = {"stages_ms": {k: round(v, 4) for k, v in st.items()}, "wall_s_timed": round(wall, 4),
+             "algorithmic_flops": work}
+    config = {"workload": f"{cfg.name}: prefill of {'CSA' if cfg.csa else ''}{'+' if cfg.csa and cfg.hca else ''}"
+                          f"{'HCA' if cfg.hca else ''}, L={cfg.L}, {cfg.n_h} heads, D={cfg.D}, kv {cfg.kv}",
+              "seq_len": cfg.L}
+    return value, ms_step, config, roof, extra, objs
+
+
+# ------------------------------------------------------------------ CPU baseline (oracle)
+def cpu_baseline_decode(cfg, ctx_state, budget_s=12.0):
+    """The oracle's decode step (indexer + top-k + CSA attention + HCA attention) for a
+    sample of the batch's sequences, timed on the host cores."""
+    import oracle
+    from oracle import pipeline as opl
+    from long_context_attention_17_amd import synth
+    ctx, _ = ctx_state
+    seqs = [0, 1] if cfg.B >= 2 else [0]
+    states = {}
+    progress("cpu baseline: building the oracle's state for the sampled sequences")
+    for name in ("csa", "hca"):
+        # draw on the GPU (fast), keep only the sampled sequences' cache rows on the host
+        inp = synth.decode_layer(cfg, name, "cuda", ctx)
+        last = inp["entry_offsets"][len(seqs)]
+        host = {}
+        for key, v in inp.items():
+            if key in ("entries", "ikeys"):
+                host[key] = v[:last].cpu()
+            elif isinstance(v, torch.Tensor):
+                host[key] = v.cpu()
+            else:
+                host[key] = v
+        del inp
+        torch.cuda.empty_cache()
+        states[name] = (host, opl.decode_state(cfg, host, seqs=seqs))
+    reps, t_total = 0, 0.0
+    progress("cpu baseline: timing the oracle")
+    while t_total < budget_s or reps == 0:
+        t0 = time.perf_counter()
+        opl.csa_decode_step(cfg, states["csa"][0], states["csa"][1], seqs=seqs)
+        opl.hca_decode_step(cfg, states["hca"][0], states["hca"][1], seqs=seqs)
+        t_total += time.perf_counter() - t0
+        reps += 1
+        if reps >= 50:
+            break
+    tok_s = len(seqs) * reps / t_total
+    cores = min(oracle.num_threads(), len(seqs))
+    return {"value": round(tok_s, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(seqs)} of {cfg.B} sequences (both layers' indexer, top-k and attention), {reps} repeat(s), "
+                      f"{t_total:.1f} s; the oracle parallelizes over query rows, so {cores} of "
+                      f"{oracle.num_threads()} host threads were busy"}
+
+
+def cpu_baseline_prefill(cfg, budget_s=12.0):
+    import numpy as np
+    import oracle
+    from oracle import pipeline as opl
+    from long_context_attention_17_amd import synth
+    rows = np.unique(np.linspace(cfg.L // 2, cfg.L - 1, 64).astype(np.int64))
+    t_total, n_rows = 0.0, 0
+    for name in (["csa"] if cfg.csa else []) + (["hca"] if cfg.hca else []):
+        inp = synth.prefill_layer(cfg, name, "cpu")
+        ratio = cfg.m if name == "csa" else cfg.m_hca
+        pt, n_pool = synth.page_table([cfg.L // ratio], cfg.page, cfg.seed)
+        t0 = time.perf_counter()
+        (opl.csa_prefill if name == "csa" else opl.hca_prefill)(cfg, inp, pt.numpy()[0], n_pool, rows=rows)
+        t_total += time.perf_counter() - t0
+    n_rows = len(rows)
+    return {"value": round(n_rows / t_total, 4), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n_rows} query rows from the second half of the sequence (compression of the whole "
+                      f"sequence included), {t_total:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_1m", choices=sorted(WORKLOADS))
+    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share of the workload; runs on more than one GPU are not "
+              "part of this build (see the sharding notes in DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+    from long_context_attention_17_amd.configs import CONFIGS
+    cfg = CONFIGS[WORKLOADS[args.workload]]
+    torch.cuda.set_device(0)
+    if cfg.phase == "decode":
+        value, ms, config, roof, extra, state = bench_decode(cfg, args.steps, args.warmup, args.replicas, args)
+    else:
+        value, ms, config, roof, extra, state = bench_prefill(cfg, args.steps, args.warmup, args.replicas, args)
+    # HBM traffic of the dominant kernel from committed rocprofv3 counter runs (null if stale)
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tpath):
+        with open(tpath) as f:
+            tj = json.load(f)
+        ent = tj.get(args.workload, {}).get(roof["kernel"])
+        if ent and ent.get("source_hash") == kernel_source_hash():
+            traffic = ent.get("bytes_per_launch")
+    roof["traffic"] = traffic
+    line = {"metric": METRIC, "value": round(value, 3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": config, "roofline": roof}
+    del state
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = (cpu_baseline_decode(cfg, (synth_ctx(cfg), None)) if cfg.phase == "decode"
+                                else cpu_baseline_prefill(cfg))
+    line.update(extra)
+    line["kernel_source_hash"] = kernel_source_hash()
+    print(json.dumps(line), flush=True)
+
+
+def synth_ctx(cfg):
+    from long_context_attention_17_amd import synth
+    return synth.decode_contexts(cfg)
+
+
+if __name__ == "__main__":
+    main()
