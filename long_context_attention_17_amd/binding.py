@@ -176,7 +176,7 @@ def index_topk_workspace(p: IndexParams, n_rows: int, max_pos: int) -> int:
 def index_topk_prefill(p: IndexParams, qI, w, seq: int, idx_cache: Cache, out_idx, out_cnt, out_score=None,
                        all_scores=None, ws=None, stream=None):
     L = qI.shape[0]
-    if ws is None and all_scores is None:
+    if ws is None:
         ws = torch.empty(max(1, index_topk_workspace(p, L, max(L - 1, 0))), dtype=torch.uint8, device=qI.device)
     st = all_scores.shape[1] if all_scores is not None else 0
     _check(_lib.ca_index_topk_prefill(ctypes.byref(p), _ptr(qI), _ptr(w), L, seq, idx_cache.ref, _ptr(out_idx),
@@ -187,7 +187,7 @@ def index_topk_prefill(p: IndexParams, qI, w, seq: int, idx_cache: Cache, out_id
 def index_topk_decode(p: IndexParams, qI, w, pos, max_pos: int, idx_cache: Cache, out_idx, out_cnt,
                       out_score=None, all_scores=None, ws=None, stream=None):
     B = qI.shape[0]
-    if ws is None and all_scores is None:
+    if ws is None:   # also with all_scores: the long-row top-k state lives in the workspace
         ws = torch.empty(max(1, index_topk_workspace(p, B, max_pos)), dtype=torch.uint8, device=qI.device)
     st = all_scores.shape[1] if all_scores is not None else 0
     _check(_lib.ca_index_topk_decode(ctypes.byref(p), _ptr(qI), _ptr(w), _ptr(pos), B, max_pos, idx_cache.ref,

@@ -170,9 +170,13 @@ int ca_window_append(const ca_window_params* p, const void* kv_raw, const float*
 }
 
 // ------------------------------------------------------------------ indexer
+// Workspace: the score rows, then (for long rows) the multi-workgroup top-k state.
 size_t ca_index_topk_workspace(const ca_index_params* p, int32_t n_rows, int64_t max_pos) {
   if (p == nullptr || p->ratio <= 0 || n_rows <= 0 || max_pos < 0) return 0;
-  return align256((size_t)n_rows * score_stride(max_pos, p->ratio) * sizeof(float));
+  int64_t stride = score_stride(max_pos, p->ratio);
+  size_t bytes = align256((size_t)n_rows * stride * sizeof(float));
+  if (ca::topk_use_long(stride, p->k)) bytes += align256(ca::topk_long_workspace(n_rows, stride));
+  return bytes;
 }
 
 static int index_common(const ca_index_params* p, const void* qI, const float* w, const int32_t* pos, int seq_fixed,
@@ -195,21 +199,29 @@ static int index_common(const ca_index_params* p, const void* qI, const float* w
     return fail(CA_ERR_ARG, "%s: page table holds fewer entries than floor(max_pos/ratio)", what);
   float* scores;
   int64_t stride;
+  void* ws_long = nullptr;
   if (all_scores != nullptr) {
-    if (all_stride < max_pos / p->ratio) return fail(CA_ERR_ARG, "%s: all_scores_stride too small", what);
+    if (all_stride < max_pos / p->ratio || all_stride < 1) return fail(CA_ERR_ARG, "%s: all_scores_stride too small", what);
     scores = all_scores;
     stride = all_stride;
+    if (ca::topk_use_long(stride, p->k)) {
+      size_t need = align256(ca::topk_long_workspace((int)n_rows, stride));
+      if (ws != nullptr && ws_bytes >= need) ws_long = ws;
+    }
   } else {
     size_t need = ca_index_topk_workspace(p, (int32_t)n_rows, max_pos);
     if (ws_bytes < need || (need > 0 && ws == nullptr))
       return fail(CA_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", what, ws_bytes, need);
     scores = (float*)ws;
     stride = score_stride(max_pos, p->ratio);
+    if (ca::topk_use_long(stride, p->k))
+      ws_long = (char*)ws + align256((size_t)n_rows * stride * sizeof(float));
   }
   hipError_t e = ca::launch_index_scores(cv, *p, qI, w, pos, seq_fixed, (int)n_rows, max_pos, scores, stride,
                                          S(stream));
   if (e != hipSuccess) return hip_status(e, what);
-  e = ca::launch_topk(scores, stride, pos, p->ratio, p->k, (int)n_rows, out_idx, out_cnt, out_score, S(stream));
+  e = ca::launch_topk(scores, stride, pos, p->ratio, p->k, (int)n_rows, out_idx, out_cnt, out_score, ws_long,
+                      S(stream));
   return hip_status(e, what);
 }
 

@@ -285,6 +285,270 @@ __global__ void __launch_bounds__(kTopkThreads) topk_rows_kernel(const float* sc
   if (tid == 0) out_cnt[r] = k;
 }
 
+// ------------------------------------------------------------------ top-k, long rows (decode)
+// Rows with more candidates than one workgroup should stream (decode at long
+// context: 262,144 per row at 2^20 tokens) are selected in three passes that
+// spread the scan over many workgroups:
+//   1. histogram of the top 12 key bits per row (LDS histogram per chunk,
+//      nonzero bins added to the row's global histogram: integer atomics, so
+//      the counts are order independent);
+//   2. every chunk finds the bin b* holding the k-th largest key from the row
+//      histogram and appends its keys with bin >= b* (about k plus one bin's
+//      population) to a per-row candidate list;
+//   3. one workgroup per row selects exactly among the candidates (radix select
+//      on the full key, then the lowest indices among keys equal to the
+//      threshold) and sorts the kept indices ascending.
+// The candidate list is filled in arbitrary order, but pass 3 depends only on
+// the set of (key, index) pairs, so the result is deterministic.
+constexpr int kHistBins = 4096;
+constexpr int kChunk = 4096;
+constexpr int kResolveThreads = 1024;
+constexpr int kResolveLds = 8192;     // candidates held in LDS (more spill to the global list)
+constexpr int kSortMax = 8192;        // largest k the resolve pass sorts in LDS
+
+__global__ void topk_zero_kernel(uint32_t* p, int64_t n) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+__device__ __forceinline__ int64_t row_len(const int32_t* pos, int r, int m, int64_t stride) {
+  int t = pos ? pos[r] : r;
+  int64_t n = t / m;
+  return n < stride ? n : stride;
+}
+
+__global__ void __launch_bounds__(256) topk_hist_kernel(const float* scores, int64_t stride, const int32_t* pos,
+                                                        int m, int k, uint32_t* hist) {
+  __shared__ uint32_t h[kHistBins];
+  const int r = blockIdx.x;
+  const int64_t n = row_len(pos, r, m, stride);
+  const int64_t c0 = (int64_t)blockIdx.y * kChunk;
+  if (n <= k || c0 >= n) return;
+  for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) h[i] = 0;
+  __syncthreads();
+  const float* row = scores + (int64_t)r * stride;
+  const int64_t c1 = c0 + kChunk < n ? c0 + kChunk : n;
+  for (int64_t s = c0 + threadIdx.x; s < c1; s += blockDim.x) atomicAdd(&h[order_key(row[s]) >> 20], 1u);
+  __syncthreads();
+  uint32_t* g = hist + (int64_t)r * kHistBins;
+  for (int i = threadIdx.x; i < kHistBins; i += blockDim.x)
+    if (h[i]) atomicAdd(&g[i], h[i]);
+}
+
+// Bin holding the k-th largest key of a row, from its histogram (block-wide).
+__device__ uint32_t threshold_bin(const uint32_t* g, int k, uint32_t* part) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int per = kHistBins / nt;
+  uint32_t sum = 0;
+  for (int i = 0; i < per; ++i) sum += g[tid * per + i];
+  part[tid] = sum;
+  __syncthreads();
+  // suffix of the per-thread sums (threads above this one), serial over <= 256 entries per thread is
+  // avoided: one pass by wave 0 over the partial sums
+  __shared__ uint32_t sel;
+  if (tid == 0) {
+    uint32_t cum = 0;
+    int owner = 0;
+    for (int i = nt - 1; i >= 0; --i) {
+      if (cum + part[i] >= (uint32_t)k) { owner = i; break; }
+      cum += part[i];
+    }
+    for (int b = owner * per + per - 1; b >= owner * per; --b) {
+      if (cum + g[b] >= (uint32_t)k) { sel = (uint32_t)b; break; }
+      cum += g[b];
+    }
+  }
+  __syncthreads();
+  return sel;
+}
+
+__global__ void __launch_bounds__(256) topk_gather_kernel(const float* scores, int64_t stride, const int32_t* pos,
+                                                          int m, int k, const uint32_t* hist, uint32_t* cand_n,
+                                                          uint32_t* cand_key, uint32_t* cand_idx) {
+  __shared__ uint32_t part[256];
+  const int r = blockIdx.x;
+  const int64_t n = row_len(pos, r, m, stride);
+  const int64_t c0 = (int64_t)blockIdx.y * kChunk;
+  if (n <= k || c0 >= n) return;
+  const uint32_t bstar = threshold_bin(hist + (int64_t)r * kHistBins, k, part);
+  const float* row = scores + (int64_t)r * stride;
+  const int64_t c1 = c0 + kChunk < n ? c0 + kChunk : n;
+  const int lane = threadIdx.x & 63;
+  for (int64_t base = c0; base < c1; base += blockDim.x) {
+    int64_t s = base + threadIdx.x;
+    uint32_t key = s < c1 ? order_key(row[s]) : 0u;
+    bool keep = s < c1 && (key >> 20) >= bstar;
+    uint64_t b = __ballot(keep);
+    if (b == 0) continue;
+    uint32_t first = 0;
+    if (lane == 0) first = atomicAdd(&cand_n[r], (uint32_t)__popcll(b));
+    first = __shfl(first, 0, 64);
+    if (keep) {
+      uint32_t o = first + (uint32_t)__popcll(b & ((1ull << lane) - 1ull));
+      cand_key[(int64_t)r * stride + o] = key;
+      cand_idx[(int64_t)r * stride + o] = (uint32_t)s;
+    }
+  }
+}
+
+struct ResolveShared {
+  uint32_t key[kResolveLds];
+  uint32_t idx[kResolveLds];
+  uint32_t hist[256];
+  uint32_t wsum[kResolveThreads / 64];
+  uint32_t sel_digit, sel_krem, n_eq, n_out;
+};
+
+// In-LDS bitonic sort (ascending) of n_pow2 32-bit values.
+__device__ void bitonic_sort(uint32_t* v, int n_pow2) {
+  for (int size = 2; size <= n_pow2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < n_pow2 / 2; i += blockDim.x) {
+        int lo = 2 * i - (i & (stride - 1));
+        int hi = lo + stride;
+        bool up = (lo & size) == 0;
+        uint32_t a = v[lo], b = v[hi];
+        if ((a > b) == up) {
+          v[lo] = b;
+          v[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__global__ void __launch_bounds__(kResolveThreads) topk_resolve_kernel(const float* scores, int64_t stride,
+                                                                       const int32_t* pos, int m, int k,
+                                                                       const uint32_t* cand_n,
+                                                                       const uint32_t* cand_key,
+                                                                       const uint32_t* cand_idx, int32_t* out_idx,
+                                                                       int32_t* out_cnt, float* out_score) {
+  __shared__ ResolveShared sh;
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int64_t n = row_len(pos, r, m, stride);
+  const float* row = scores + (int64_t)r * stride;
+  int32_t* oi = out_idx + (int64_t)r * k;
+  float* os = out_score ? out_score + (int64_t)r * k : nullptr;
+  if (n <= k) {
+    for (int j = tid; j < k; j += blockDim.x) {
+      oi[j] = j < n ? j : -1;
+      if (os) os[j] = j < n ? row[j] : -INFINITY;
+    }
+    if (tid == 0) out_cnt[r] = (int32_t)n;
+    return;
+  }
+  const uint32_t nc = cand_n[r];
+  const bool in_lds = nc <= (uint32_t)kResolveLds;
+  const uint32_t* gk = cand_key + (int64_t)r * stride;
+  const uint32_t* gi = cand_idx + (int64_t)r * stride;
+  if (in_lds)
+    for (uint32_t i = tid; i < nc; i += blockDim.x) {
+      sh.key[i] = gk[i];
+      sh.idx[i] = gi[i];
+    }
+  // radix select of the k-th largest key among the candidates
+  uint32_t prefix = 0, krem = (uint32_t)k;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
+    for (int i = tid; i < 256; i += blockDim.x) sh.hist[i] = 0;
+    __syncthreads();
+    for (uint32_t i = tid; i < nc; i += blockDim.x) {
+      uint32_t key = in_lds ? sh.key[i] : gk[i];
+      if ((key & hi_mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      uint32_t c[4] = {sh.hist[4 * tid], sh.hist[4 * tid + 1], sh.hist[4 * tid + 2], sh.hist[4 * tid + 3]};
+      uint32_t lsum = c[0] + c[1] + c[2] + c[3];
+      uint32_t incl = lsum;
+      for (int o = 1; o < 64; o <<= 1) {
+        uint32_t v = __shfl_down(incl, o, 64);
+        if (tid + o < 64) incl += v;
+      }
+      uint32_t cum = incl - lsum;
+      for (int d = 3; d >= 0; --d) {
+        uint32_t nxt = cum + c[d];
+        if (cum < krem && nxt >= krem) {
+          sh.sel_digit = 4 * tid + d;
+          sh.sel_krem = krem - cum;
+        }
+        cum = nxt;
+      }
+    }
+    __syncthreads();
+    prefix |= sh.sel_digit << shift;
+    krem = sh.sel_krem;
+    __syncthreads();
+  }
+  const uint32_t T = prefix, need_eq = krem;
+  // kept set: every candidate above T, then the need_eq lowest indices equal to T.
+  // sh.idx is reused as the output buffer once the candidates are consumed from wherever they live.
+  __shared__ uint32_t outbuf[kSortMax];
+  __shared__ uint32_t eqbuf[kSortMax];
+  if (tid == 0) {
+    sh.n_eq = 0;
+    sh.n_out = 0;
+  }
+  __syncthreads();
+  for (uint32_t i = tid; i < nc; i += blockDim.x) {
+    uint32_t key = in_lds ? sh.key[i] : gk[i];
+    uint32_t id = in_lds ? sh.idx[i] : gi[i];
+    if (key > T) {
+      uint32_t o = atomicAdd(&sh.n_out, 1u);
+      if (o < (uint32_t)kSortMax) outbuf[o] = id;
+    } else if (key == T) {
+      uint32_t o = atomicAdd(&sh.n_eq, 1u);
+      if (o < (uint32_t)kSortMax) eqbuf[o] = id;
+    }
+  }
+  __syncthreads();
+  const uint32_t n_gt = sh.n_out, n_eq = sh.n_eq;
+  if (n_eq <= (uint32_t)kSortMax) {
+    int p2 = 1;
+    while (p2 < (int)n_eq) p2 <<= 1;
+    for (int i = (int)n_eq + tid; i < p2; i += blockDim.x) eqbuf[i] = 0xFFFFFFFFu;
+    __syncthreads();
+    bitonic_sort(eqbuf, p2);
+    for (uint32_t j = tid; j < need_eq; j += blockDim.x) outbuf[n_gt + j] = eqbuf[j];
+  } else {
+    // pathological tie count: take the need_eq smallest equal indices one at a time
+    __shared__ uint32_t last, best;
+    if (tid == 0) last = 0xFFFFFFFFu;
+    __syncthreads();
+    for (uint32_t j = 0; j < need_eq; ++j) {
+      if (tid == 0) best = 0xFFFFFFFFu;
+      __syncthreads();
+      uint32_t mine = 0xFFFFFFFFu;
+      for (uint32_t i = tid; i < nc; i += blockDim.x) {
+        uint32_t key = in_lds ? sh.key[i] : gk[i];
+        uint32_t id = in_lds ? sh.idx[i] : gi[i];
+        if (key == T && (last == 0xFFFFFFFFu || id > last) && id < mine) mine = id;
+      }
+      atomicMin(&best, mine);
+      __syncthreads();
+      if (tid == 0) {
+        outbuf[n_gt + j] = best;
+        last = best;
+      }
+      __syncthreads();
+    }
+  }
+  __syncthreads();
+  int p2 = 1;
+  while (p2 < k) p2 <<= 1;
+  for (int i = k + tid; i < p2; i += blockDim.x) outbuf[i] = 0xFFFFFFFFu;
+  __syncthreads();
+  bitonic_sort(outbuf, p2);
+  for (int j = tid; j < k; j += blockDim.x) {
+    uint32_t id = outbuf[j];
+    oi[j] = (int32_t)id;
+    if (os) os[j] = row[id];
+  }
+  if (tid == 0) out_cnt[r] = k;
+}
+
 // ------------------------------------------------------------------ launchers
 hipError_t launch_index_scores(const CacheView& cv, const ca_index_params& p, const void* qI, const float* w,
                                const int32_t* pos, int seq_fixed, int n_rows, int64_t max_pos, float* scores,
@@ -312,9 +576,30 @@ hipError_t launch_index_scores(const CacheView& cv, const ca_index_params& p, co
   return hipGetLastError();
 }
 
+size_t topk_long_workspace(int n_rows, int64_t stride) {
+  return (size_t)n_rows * kHistBins * 4 + (size_t)n_rows * 4 + 2 * (size_t)n_rows * stride * 4 + 256;
+}
+
+bool topk_use_long(int64_t stride, int k) { return stride > kTopkLdsKeys && k <= kSortMax; }
+
 hipError_t launch_topk(const float* scores, int64_t stride, const int32_t* pos, int m, int k, int n_rows,
-                       int32_t* out_idx, int32_t* out_cnt, float* out_score, hipStream_t st) {
+                       int32_t* out_idx, int32_t* out_cnt, float* out_score, void* ws_long, hipStream_t st) {
   if (n_rows == 0) return hipSuccess;
+  if (ws_long != nullptr && topk_use_long(stride, k)) {
+    uint32_t* hist = (uint32_t*)ws_long;
+    uint32_t* cand_n = hist + (int64_t)n_rows * kHistBins;
+    uint32_t* cand_key = cand_n + n_rows;
+    uint32_t* cand_idx = cand_key + (int64_t)n_rows * stride;
+    const int64_t nz = (int64_t)n_rows * (kHistBins + 1);
+    hipLaunchKernelGGL(topk_zero_kernel, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, st, hist, nz);
+    const unsigned chunks = (unsigned)((stride + kChunk - 1) / kChunk);
+    hipLaunchKernelGGL(topk_hist_kernel, dim3(n_rows, chunks), dim3(256), 0, st, scores, stride, pos, m, k, hist);
+    hipLaunchKernelGGL(topk_gather_kernel, dim3(n_rows, chunks), dim3(256), 0, st, scores, stride, pos, m, k, hist,
+                       cand_n, cand_key, cand_idx);
+    hipLaunchKernelGGL(topk_resolve_kernel, dim3(n_rows), dim3(kResolveThreads), 0, st, scores, stride, pos, m, k,
+                       cand_n, cand_key, cand_idx, out_idx, out_cnt, out_score);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(topk_rows_kernel, dim3(n_rows), dim3(kTopkThreads), 0, st, scores, stride,
                      pos, m, k, out_idx, out_cnt, out_score);
   return hipGetLastError();

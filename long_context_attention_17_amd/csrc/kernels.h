@@ -21,8 +21,12 @@ hipError_t launch_window_append(const ca_window_params& p, const void* raw, cons
 hipError_t launch_index_scores(const CacheView& cv, const ca_index_params& p, const void* qI, const float* w,
                                const int32_t* pos, int seq_fixed, int n_rows, int64_t max_pos, float* scores,
                                int64_t stride, hipStream_t st);
+// Top-k over score rows.  With ws_long (topk_long_workspace bytes) and rows longer than
+// one workgroup's LDS, the multi-workgroup histogram / gather / resolve path runs.
+size_t topk_long_workspace(int n_rows, int64_t stride);
+bool topk_use_long(int64_t stride, int k);
 hipError_t launch_topk(const float* scores, int64_t stride, const int32_t* pos, int m, int k, int n_rows,
-                       int32_t* out_idx, int32_t* out_cnt, float* out_score, hipStream_t st);
+                       int32_t* out_idx, int32_t* out_cnt, float* out_score, void* ws_long, hipStream_t st);
 
 // Everything an attention launch needs (CSA or HCA, prefill or decode).
 struct AttendArgs {
