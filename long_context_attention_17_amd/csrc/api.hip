@@ -245,6 +245,8 @@ int ca_index_topk_decode(const ca_index_params* p, const void* qI, const float* 
 }
 
 // ------------------------------------------------------------------ attention
+// Bytes for the split partials (o, m, l) of every row: an upper bound for both decode
+// and prefill (prefill needs them only for rows longer than one workgroup's item table).
 size_t ca_attend_workspace(const ca_attend_params* p, int32_t n_rows, int64_t max_pos, int32_t k, int32_t ratio) {
   if (p == nullptr || n_rows <= 0 || ratio <= 0) return 0;
   size_t ms = (size_t)max_splits_for(max_pos, p->n_win, k, ratio);
@@ -311,14 +313,24 @@ static int attend_common(const ca_attend_params* p, const void* q, const float* 
   a.max_splits = 1;
   a.part_o = nullptr;
   a.part_ml = nullptr;
-  if (decode) {
-    size_t need = ca_attend_workspace(p, (int32_t)n_rows, max_pos, mode == 0 ? k : 0, ratio);
-    if (ws_bytes < need || ws == nullptr) return fail(CA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", what, ws_bytes, need);
-    a.split_items = ca::kDecodeSplitItems;
-    a.max_splits = max_splits_for(max_pos, p->n_win, mode == 0 ? k : 0, ratio);
-    size_t ms = (size_t)a.max_splits;
+  // Split the item list of each row into fixed chunks: always for decode (a plan that
+  // depends on the sequence alone), and for prefill rows longer than one MFMA
+  // workgroup's item table.
+  const int64_t max_items = (mode == 0 ? (int64_t)k : max_pos / ratio) + p->n_win;
+  int split = 0;
+  if (decode) split = ca::kDecodeSplitItems;
+  else if (ca::attend_mfma_supported(a) && max_items > ca::attend_mfma_max_items()) split = ca::attend_mfma_max_items();
+  if (split > 0) {
+    const int ms = (int)((max_items + split - 1) / split);
+    const size_t po = align256((size_t)n_rows * ms * p->n_heads * p->dim * sizeof(float));
+    const size_t need = po + align256((size_t)n_rows * ms * p->n_heads * 2 * sizeof(float));
+    if (ws_bytes < need || ws == nullptr)
+      return fail(CA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes (rows of up to %lld items are split)", what,
+                  ws_bytes, need, (long long)max_items);
+    a.split_items = split;
+    a.max_splits = ms;
     a.part_o = (float*)ws;
-    a.part_ml = (float*)((char*)ws + align256((size_t)n_rows * ms * p->n_heads * p->dim * sizeof(float)));
+    a.part_ml = (float*)((char*)ws + po);
   }
   return hip_status(ca::launch_attend(a, S(stream)), what);
 }

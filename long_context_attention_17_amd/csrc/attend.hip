@@ -216,81 +216,184 @@ __global__ void attend_combine_kernel(AttendArgs a) {
 
 // ======================================================================== MFMA (D = 512)
 constexpr int kD = 512;
-constexpr int kTile = 32;          // items per tile
-constexpr int kPitch = kD + 8;     // bf16 elements per LDS row (16 B pad against bank conflicts)
+constexpr int kR = 64;
+constexpr int kTile = 32;               // items per tile
+constexpr int kPitch = kD + 8;          // bf16 elements per LDS tile row (16 B pad against bank conflicts)
+constexpr int kRawPitch = 1024;         // bytes per raw (fp8 record or bf16 window) staging row
+constexpr int kMaxItems = 2176;         // item pointers cached in LDS per workgroup (k + window <= 2048 + 128)
 
-struct TileRegs {
-  u32x4 raw[8];
-  int kind[8];   // 0: skipped item (zeros), 1: bf16 row (entry or window), 2: fp8-mixed entry
-  float scale[8];
+template <int KV_FMT>
+struct MfmaShared {
+  static constexpr int kStages = KV_FMT == CA_FP8MIX ? 3 : 4;
+  // bf16 records: the ring holds bf16 tiles directly.  fp8 records: the ring holds raw
+  // bytes and one bf16 tile receives the dequantized copy.
+  static constexpr int kRingBytes = KV_FMT == CA_FP8MIX ? kTile * kRawPitch : kTile * kPitch * 2;
+  __attribute__((aligned(16))) uint8_t ring[kStages][kRingBytes];
+  __attribute__((aligned(16))) __bf16 tile[KV_FMT == CA_FP8MIX ? kTile * kPitch : 8];
+  const uint8_t* items[kMaxItems];
+  int kind[kStages][kTile];             // 0: skipped item, 1: bf16 row, 2: fp8 record
+  float rope_cs[kR];                    // (cos, sin) of t * theta_p, p < R/2
 };
 
-// Issue the global loads of tile `j_begin .. j_begin+31` of this row.
-// Wave w handles items w, w+4, ..., lane q its 16-byte chunk q of the item.
+// Issue the async (global -> LDS) loads of tile `tile_no` into ring stage `st`.
+// Every wave issues exactly 8 load instructions (one per item it owns, items
+// wave, wave+4, ...), so outstanding-load counts are the same for all tiles.
 template <int KV_FMT>
-__device__ __forceinline__ void tile_load(const AttendArgs& a, const RowInfo& ri, int r, int j_begin, int j_end,
-                                          TileRegs& tr) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int j = j_begin + wave + 4 * u;
-    bool is_win = false;
-    const uint8_t* p = j < j_end ? item_ptr(a, ri, r, j, &is_win) : nullptr;
-    tr.kind[u] = p == nullptr ? 0 : ((KV_FMT == CA_FP8MIX && !is_win) ? 2 : 1);
-    tr.raw[u] = u32x4{0, 0, 0, 0};
-    tr.scale[u] = 1.0f;
-    if (tr.kind[u] == 1) {
-      tr.raw[u] = ((const u32x4*)p)[lane];
-    } else if (tr.kind[u] == 2) {
-      if (lane < 28) {
-        tr.raw[u] = ((const u32x4*)p)[lane];                         // 16 content codes
-        tr.scale[u] = ldexpf(1.0f, (int)(int8_t)p[kD + 64 + (lane >> 2)]);   // exponents after codes + rope
-      } else if (lane < 36) {
-        tr.raw[u] = ((const u32x4*)(p + 448))[lane - 28];            // 8 rotary bf16
-      }
-    }
-  }
-}
-
-// Dequantize / copy the loaded tile into LDS buffer `kt`, and its item mask.
-__device__ __forceinline__ void tile_store(__bf16* kt, int* valid, const TileRegs& tr) {
+__device__ __forceinline__ void issue_tile(const AttendArgs& a, const RowInfo& ri, int r, int j0, int j1,
+                                           int tile_no, int st, MfmaShared<KV_FMT>& sh, const uint8_t* dummy) {
+  typedef __attribute__((address_space(3))) void lds_void;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
     const int it = wave + 4 * u;
-    __bf16* row = kt + it * kPitch;
-    if (tr.kind[u] == 2) {
-      if (lane < 28) {
-        bf16x8 lo, hi;
-        const u32x4 w = tr.raw[u];
-        const float sc = tr.scale[u];
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          bf16x2 a0 = e4m3x2_to_bf16_scaled<false>(w[2 * k], sc), a1 = e4m3x2_to_bf16_scaled<true>(w[2 * k], sc);
-          bf16x2 b0 = e4m3x2_to_bf16_scaled<false>(w[2 * k + 1], sc), b1 = e4m3x2_to_bf16_scaled<true>(w[2 * k + 1], sc);
-          bf16x8& dst = k == 0 ? lo : hi;
-          dst[0] = a0[0]; dst[1] = a0[1]; dst[2] = a1[0]; dst[3] = a1[1];
-          dst[4] = b0[0]; dst[5] = b0[1]; dst[6] = b1[0]; dst[7] = b1[1];
-        }
-        *(bf16x8*)(row + 16 * lane) = lo;
-        *(bf16x8*)(row + 16 * lane + 8) = hi;
-      } else if (lane < 36) {
-        *(u32x4*)(row + 448 + 8 * (lane - 28)) = tr.raw[u];
-      }
+    const int j = j0 + tile_no * kTile + it;
+    // the host guarantees j1 - j0 <= kMaxItems (longer rows are split)
+    const uint8_t* p = j < j1 ? sh.items[j - j0] : nullptr;
+    const bool is_win = j >= ri.n_c;
+    const int kind = p == nullptr ? 0 : ((KV_FMT == CA_FP8MIX && !is_win) ? 2 : 1);
+    const uint8_t* src = p == nullptr ? dummy : p;
+    uint8_t* dst = KV_FMT == CA_FP8MIX ? sh.ring[st] + it * kRawPitch : sh.ring[st] + it * kPitch * 2;
+    if (kind == 2) {
+      if (lane < 37) __builtin_amdgcn_global_load_lds(src + 16 * lane, (lds_void*)dst, 16, 0, 0);
     } else {
-      *(u32x4*)(row + 8 * lane) = tr.raw[u];   // bf16 row, or zeros for a skipped item
+      __builtin_amdgcn_global_load_lds(src + 16 * lane, (lds_void*)dst, 16, 0, 0);
     }
-    if (lane == 0) valid[it] = tr.kind[u] != 0;
+    if (lane == 0) sh.kind[st][it] = kind;
+  }
+}
+
+// Wait until at most 8*ahead of this wave's async loads are still in flight.
+__device__ __forceinline__ void wait_loads(int ahead) {
+  switch (ahead) {
+    case 0: __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 1: __asm__ volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    case 2: __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+    default: __asm__ volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
+  }
+}
+
+// fp8 records: dequantize the raw stage into the bf16 tile (each thread: 8 slots
+// of 8 channels; content channels scaled by their tile exponent, rotary and
+// window rows copied; skipped items zeroed).
+__device__ __forceinline__ void convert_tile(const uint8_t* raw, const int* kind, __bf16* tile) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int sid = threadIdx.x + 256 * u;
+    const int it = sid >> 6, sl = sid & 63;
+    const uint8_t* row = raw + it * kRawPitch;
+    __bf16* dst = tile + it * kPitch + 8 * sl;
+    const int kd = kind[it];
+    u32x4 out = {0u, 0u, 0u, 0u};
+    if (kd == 1) {
+      out = *(const u32x4*)(row + 16 * sl);
+    } else if (kd == 2) {
+      if (sl < 56) {            // channels 8*sl .. 8*sl+7 < 448: e4m3 codes
+        const u32x2 w = *(const u32x2*)(row + 8 * sl);
+        const float sc = ldexpf(1.0f, (int)(int8_t)row[kD + kR + (sl >> 3)]);
+        bf16x2 c0 = e4m3x2_to_bf16_scaled<false>(w[0], sc), c1 = e4m3x2_to_bf16_scaled<true>(w[0], sc);
+        bf16x2 c2 = e4m3x2_to_bf16_scaled<false>(w[1], sc), c3 = e4m3x2_to_bf16_scaled<true>(w[1], sc);
+        out[0] = __builtin_bit_cast(uint32_t, c0);
+        out[1] = __builtin_bit_cast(uint32_t, c1);
+        out[2] = __builtin_bit_cast(uint32_t, c2);
+        out[3] = __builtin_bit_cast(uint32_t, c3);
+      } else {                  // rotary channels, bf16
+        out = *(const u32x4*)(row + 448 + 16 * (sl - 56));
+      }
+    }
+    *(u32x4*)dst = out;
+  }
+}
+
+// S^T = K Q^T for one 32-item tile: two 16-item blocks x two halves of the 512-dim
+// contraction (four independent accumulator chains).  The K fragments are read one
+// step ahead of their MFMAs; sched_barrier keeps the compiler from hoisting all 32
+// reads at once.  Output: this lane's 8 scaled log2 logits (head li, items 4g..4g+3
+// and 16+4g..16+4g+3; -inf for skipped items) and the per-head tile max.
+__device__ __forceinline__ void attend_scores(const __bf16* kt, const int* kind, const bf16x8* qreg,
+                                              float scale_log2, int li, int g, float* sv, float& tmax) {
+  f32x4 s0a = {0.0f, 0.0f, 0.0f, 0.0f}, s1a = s0a, s0b = s0a, s1b = s0a;
+  const __bf16* r0 = kt + li * kPitch + 8 * g;
+  const __bf16* r1 = kt + (16 + li) * kPitch + 8 * g;
+  bf16x8 k0 = *(const bf16x8*)(r0), k1 = *(const bf16x8*)(r1);
+  bf16x8 k2 = *(const bf16x8*)(r0 + 256), k3 = *(const bf16x8*)(r1 + 256);
+#pragma unroll
+  for (int kb = 0; kb < 8; ++kb) {
+    bf16x8 n0, n1, n2, n3;
+    if (kb < 7) {
+      n0 = *(const bf16x8*)(r0 + 32 * (kb + 1));
+      n1 = *(const bf16x8*)(r1 + 32 * (kb + 1));
+      n2 = *(const bf16x8*)(r0 + 256 + 32 * (kb + 1));
+      n3 = *(const bf16x8*)(r1 + 256 + 32 * (kb + 1));
+    }
+    s0a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qreg[kb], s0a, 0, 0, 0);
+    s1a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qreg[kb], s1a, 0, 0, 0);
+    s0b = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k2, qreg[kb + 8], s0b, 0, 0, 0);
+    s1b = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k3, qreg[kb + 8], s1b, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kb < 7) {
+      k0 = n0;
+      k1 = n1;
+      k2 = n2;
+      k3 = n3;
+    }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    sv[v] = kind[4 * g + v] ? (s0a[v] + s0b[v]) * scale_log2 : -INFINITY;
+    sv[4 + v] = kind[16 + 4 * g + v] ? (s1a[v] + s1b[v]) * scale_log2 : -INFINITY;
+    mx = fmaxf(mx, fmaxf(sv[v], sv[4 + v]));
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+  tmax = fmaxf(mx, __shfl_xor(mx, 32, 64));
+}
+
+// P = 2^(s - m_run) (bf16 A operand, straight from this lane's logits) and O += P V,
+// V^T fragments via LDS transpose loads in the same item order, read one column
+// block ahead of their MFMA.
+__device__ __forceinline__ void attend_pv(const __bf16* kt, const float* sv, float m_run, float& l_part, int li,
+                                          int g, f32x4* oacc) {
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  bf16x8 pa;
+  float psum = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float p = m_run == -INFINITY ? 0.0f : exp2f(sv[e] - m_run);
+    psum += p;
+    pa[e] = __builtin_bit_cast(__bf16, f32_to_bf16_bits(p));
+  }
+  l_part += psum;
+  const int vrow = 4 * g + (li >> 2), vcol = 4 * (li & 3);
+  const __bf16* vbase = kt + vrow * kPitch + vcol;
+  bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vbase));
+  bf16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vbase + 16 * kPitch));
+#pragma unroll
+  for (int cb = 0; cb < 32; ++cb) {
+    bf16x4 na, nb;
+    if (cb < 31) {
+      na = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vbase + 16 * (cb + 1)));
+      nb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vbase + 16 * kPitch + 16 * (cb + 1)));
+    }
+    bf16x8 vv;
+    vv[0] = va[0]; vv[1] = va[1]; vv[2] = va[2]; vv[3] = va[3];
+    vv[4] = vb[0]; vv[5] = vb[1]; vv[6] = vb[2]; vv[7] = vb[3];
+    oacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vv, oacc[cb], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (cb < 31) {
+      va = na;
+      vb = nb;
+    }
   }
 }
 
 template <int KV_FMT>
 __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a) {
-  __shared__ __attribute__((aligned(16))) __bf16 ktile[2][kTile * kPitch];
-  __shared__ int valid[2][kTile];
+  typedef MfmaShared<KV_FMT> Sh;
+  constexpr int NS = Sh::kStages;
+  __shared__ Sh sh;
 
   const int r = blockIdx.x, hg = blockIdx.y, split = blockIdx.z;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, g = lane >> 4;
   const RowInfo ri = row_info(a, r);
   const int ns = n_splits_of(a, ri.total);
@@ -302,130 +405,123 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a) {
   }
   const int ntiles = (j1 - j0 + kTile - 1) / kTile;
   const int head_s = hg * 64 + wave * 16 + li;      // head this lane scores (S^T column)
+  constexpr int C = kD - kR;
 
-  TileRegs tr;
-  if (ntiles > 0) tile_load<KV_FMT>(a, ri, r, j0, j1, tr);
+  // ---- prologue: RoPE table for position t, item source table, first async tiles
+  if (tid < kR / 2) {
+    float sn, cs;
+    rope_sincos((double)ri.t, tid, kR, a.base, &sn, &cs);
+    sh.rope_cs[2 * tid] = cs;
+    sh.rope_cs[2 * tid + 1] = sn;
+  }
+  const int n_tab = (j1 - j0) < kMaxItems ? (j1 - j0) : kMaxItems;
+  for (int i = tid; i < n_tab; i += 256) {
+    bool w;
+    sh.items[i] = item_ptr(a, ri, r, j0 + i, &w);
+  }
+  // a valid, finite row used as the source of loads for skipped items: the window token at t
+  const uint8_t* dummy = (const uint8_t*)a.win + ((int64_t)ri.win_seq * a.W + ri.t % a.W) * kD * 2;
+  __syncthreads();
+  for (int t = 0; t < NS - 1; ++t)
+    if (t < ntiles) issue_tile<KV_FMT>(a, ri, r, j0, j1, t, t, sh, dummy);
 
-  // ---- query prologue: RMSNorm, gain, RoPE at t, to bf16 B-operand fragments
+  // ---- query: RMSNorm with gain, RoPE at t, bf16 B-operand fragments (lane: head li, dims 32kb+8g..+7)
   bf16x8 qreg[16];
   {
     const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)r * a.n_heads + head_s) * kD;
-    float qf[16][8];
     float ss = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < 16; ++kb) {
       u32x4 w = *(const u32x4*)(qrow + 32 * kb + 8 * g);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        qf[kb][2 * e] = __uint_as_float(w[e] << 16);
-        qf[kb][2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+        float x0 = __uint_as_float(w[e] << 16), x1 = __uint_as_float(w[e] & 0xFFFF0000u);
+        ss += x0 * x0 + x1 * x1;
       }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss += qf[kb][e] * qf[kb][e];
     }
     ss += __shfl_xor(ss, 16, 64);
     ss += __shfl_xor(ss, 32, 64);
     const float inv = 1.0f / sqrtf(ss / (float)kD + a.eps);
-    const int C = kD - a.R;
 #pragma unroll
     for (int kb = 0; kb < 16; ++kb) {
+      const int d0 = 32 * kb + 8 * g;
+      u32x4 w = *(const u32x4*)(qrow + d0);
+      f32x4 g0 = *(const f32x4*)(a.q_gain + d0), g1 = *(const f32x4*)(a.q_gain + d0 + 4);
+      float x[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        int d = 32 * kb + 8 * g + e;
-        qf[kb][e] *= inv * a.q_gain[d];
+      for (int e = 0; e < 4; ++e) {
+        x[2 * e] = __uint_as_float(w[e] << 16);
+        x[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
       }
-      if (32 * kb + 8 * g + 8 > C) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] *= inv * (e < 4 ? g0[e] : g1[e - 4]);
+      if (d0 >= C) {
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-          int d = 32 * kb + 8 * g + e;
-          if (d >= C) {
-            float s, c;
-            rope_sincos((double)ri.t, (d - C) >> 1, a.R, a.base, &s, &c);
-            float x0 = qf[kb][e], x1 = qf[kb][e + 1];
-            qf[kb][e] = x0 * c - x1 * s;
-            qf[kb][e + 1] = x0 * s + x1 * c;
-          }
+          const int p = (d0 + e - C) >> 1;
+          const float c = sh.rope_cs[2 * p], sn = sh.rope_cs[2 * p + 1];
+          const float x0 = x[e], x1 = x[e + 1];
+          x[e] = x0 * c - x1 * sn;
+          x[e + 1] = x0 * sn + x1 * c;
         }
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qreg[kb][e] = __builtin_bit_cast(__bf16, f32_to_bf16_bits(qf[kb][e]));
+      for (int e = 0; e < 8; ++e) qreg[kb][e] = __builtin_bit_cast(__bf16, f32_to_bf16_bits(x[e]));
     }
   }
 
   f32x4 oacc[32];
 #pragma unroll
   for (int cb = 0; cb < 32; ++cb) oacc[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  // Softmax reference: m_run is fixed by the first tile with a valid item and moves only
+  // when a logit exceeds it by more than kBump (log2 units).  Probabilities relative to
+  // it stay <= 2^kBump, far inside fp32/bf16 range, so the hot loop never rescales O
+  // (no vector ALU work on the accumulators, which then stay in their registers); the
+  // rare move leaves the hot loop, rescales O once and finishes the tile.
+  constexpr float kBump = 60.0f;
   float m_run = -INFINITY, l_part = 0.0f;
-
-  if (ntiles > 0) tile_store(ktile[0], valid[0], tr);
-  __syncthreads();
-
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int buf = tile & 1;
-    const int jb = j0 + tile * kTile;
-    if (tile + 1 < ntiles) tile_load<KV_FMT>(a, ri, r, jb + kTile, j1, tr);
-    const __bf16* kt = ktile[buf];
-
-    // S^T = K Q^T : two 16-item blocks, contraction over 512 dims
-    f32x4 s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int kb = 0; kb < 16; ++kb) {
-      bf16x8 k0 = *(const bf16x8*)(kt + li * kPitch + 32 * kb + 8 * g);
-      bf16x8 k1 = *(const bf16x8*)(kt + (16 + li) * kPitch + 32 * kb + 8 * g);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qreg[kb], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qreg[kb], s1, 0, 0, 0);
-    }
-    // lane: head li, items 4g+v (block 0) and 16+4g+v (block 1)
-    float sv[8];
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      sv[v] = valid[buf][4 * g + v] ? s0[v] * a.scale_log2 : -INFINITY;
-      sv[4 + v] = valid[buf][16 + 4 * g + v] ? s1[v] * a.scale_log2 : -INFINITY;
-      tmax = fmaxf(tmax, fmaxf(sv[v], sv[4 + v]));
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run, tmax);
-    float alpha = 1.0f;
-    bf16x8 pa;
-    if (m_new == -INFINITY) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pa[e] = __builtin_bit_cast(__bf16, (uint16_t)0);
-    } else {
-      alpha = exp2f(m_run - m_new);
-      float psum = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float p = exp2f(sv[e] - m_new);
-        psum += p;
-        pa[e] = __builtin_bit_cast(__bf16, f32_to_bf16_bits(p));
+  float sv[8];
+  float tmax = -INFINITY;
+  int tile = 0;
+  while (tile < ntiles) {
+    bool pending = false;
+    const __bf16* kt = nullptr;
+    for (; tile < ntiles; ++tile) {
+      const int st = tile % NS;
+      const int ahead = (ntiles - 1 - tile) < (NS - 2) ? (ntiles - 1 - tile) : (NS - 2);
+      wait_loads(ahead);
+      __syncthreads();                                   // tile `tile` landed for every wave
+      if (tile + NS - 1 < ntiles)
+        issue_tile<KV_FMT>(a, ri, r, j0, j1, tile + NS - 1, (tile + NS - 1) % NS, sh, dummy);
+      if (KV_FMT == CA_FP8MIX) {
+        convert_tile(sh.ring[st], sh.kind[st], sh.tile);
+        __syncthreads();
+        kt = sh.tile;
+      } else {
+        kt = (const __bf16*)sh.ring[st];
       }
-      l_part = l_part * alpha + psum;
-      m_run = m_new;
+      attend_scores(kt, sh.kind[st], qreg, a.scale_log2, li, g, sv, tmax);
+      if (__builtin_expect(__any(tmax > m_run + kBump), 0)) {
+        pending = true;
+        break;
+      }
+      attend_pv(kt, sv, m_run, l_part, li, g, oacc);
     }
-    // O rows held by this lane are heads 4g+v: fetch their rescale factors
+    if (!pending) break;
+    // rare path: move the reference up to this tile's max and rescale O
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = m_run == -INFINITY ? 0.0f : exp2f(m_run - m_new);
+    l_part *= alpha;
+    m_run = m_new;
     float al[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) al[v] = __shfl(alpha, 4 * g + v, 64);
-
-    // O += P V ; V^T fragments via LDS transpose loads in the same item order
-    const int vrow = 4 * g + (li >> 2), vcol = 4 * (li & 3);
-    const __bf16* vbase = kt + vrow * kPitch + vcol;
 #pragma unroll
-    for (int cb = 0; cb < 32; ++cb) {
-      typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-      bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vbase + 16 * cb));
-      bf16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vbase + 16 * kPitch + 16 * cb));
-      bf16x8 vv;
-      vv[0] = va[0]; vv[1] = va[1]; vv[2] = va[2]; vv[3] = va[3];
-      vv[4] = vb[0]; vv[5] = vb[1]; vv[6] = vb[2]; vv[7] = vb[3];
+    for (int cb = 0; cb < 32; ++cb)
 #pragma unroll
       for (int v = 0; v < 4; ++v) oacc[cb][v] *= al[v];
-      oacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vv, oacc[cb], 0, 0, 0);
-    }
-    if (tile + 1 < ntiles) tile_store(ktile[buf ^ 1], valid[buf ^ 1], tr);
-    __syncthreads();
+    attend_pv(kt, sv, m_run, l_part, li, g, oacc);
+    ++tile;
   }
 
   // ---- epilogue
@@ -454,28 +550,17 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a) {
   float fv[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) fv[v] = __shfl(f_own, 4 * g + v, 64);
-  const int C = kD - a.R;
-  float rs[4], rc[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {   // the 4 rotary column blocks 28..31 (dims 448..511 when R = 64)
-    int d = 16 * (28 + q) + li;
-    rs[q] = 0.0f;
-    rc[q] = 1.0f;
-    if (d >= C) rope_sincos((double)ri.t, (d - C) >> 1, a.R, a.base, &rs[q], &rc[q]);
-  }
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int64_t obase = ((int64_t)r * a.n_heads + head_base + 4 * g + v) * kD;
 #pragma unroll
     for (int cb = 0; cb < 32; ++cb) {
       float x = oacc[cb][v] * fv[v];
-      if (cb >= 28) {
+      if (cb >= 28) {                                  // rotary channels 448..511: rotate by R_{-t}
         float other = __shfl_xor(x, 1, 64);
-        int d = 16 * cb + li;
-        if (d >= C) {
-          float s = rs[cb - 28], c = rc[cb - 28];
-          x = (li & 1) ? x * c - other * s : x * c + other * s;
-        }
+        const int p = (16 * cb + li - C) >> 1;
+        const float c = sh.rope_cs[2 * p], sn = sh.rope_cs[2 * p + 1];
+        x = (li & 1) ? x * c - other * sn : x * c + other * sn;
       }
       if (a.out_fmt == CA_F32) ((float*)a.out)[obase + 16 * cb + li] = x;
       else ((uint16_t*)a.out)[obase + 16 * cb + li] = f32_to_bf16_bits(x);
@@ -484,8 +569,10 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a) {
 }
 
 // ======================================================================== dispatch
+int attend_mfma_max_items() { return kMaxItems; }
+
 bool attend_mfma_supported(const AttendArgs& a) {
-  return a.D == kD && a.R == 64 && a.n_heads % 64 == 0 && a.q_fmt == CA_BF16 &&
+  return a.D == kD && a.R == kR && a.n_heads % 64 == 0 && a.q_fmt == CA_BF16 &&
          a.win_fmt == CA_BF16 && (a.kv.fmt == CA_BF16 || a.kv.fmt == CA_FP8MIX);
 }
 

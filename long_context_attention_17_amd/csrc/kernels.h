@@ -57,9 +57,10 @@ struct AttendArgs {
   float* part_ml;      // [rows, max_splits, n_heads, 2]
 };
 
-constexpr int kDecodeSplitItems = 128;
+constexpr int kDecodeSplitItems = 256;
 
 bool attend_mfma_supported(const AttendArgs& a);
+int attend_mfma_max_items();  // items one MFMA workgroup handles without splitting
 hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
 
 }  // namespace ca
