@@ -135,41 +135,69 @@ def bench_decode(cfg, steps, warmup, replicas, args):
         torch.cuda.empty_cache()
     torch.cuda.synchronize()
 
-    def step(i, timer=None):
+    def stages_of(i):
         c = layer_objs["csa"][i % replicas]
         h = layer_objs["hca"][i % replicas]
-        stages = [("csa_window_append", c.append_token), ("csa_compress", c.compress),
-                  ("csa_index_topk", c.index_topk), ("csa_attend", c.attend),
-                  ("hca_window_append", h.append_token), ("hca_compress", h.compress), ("hca_attend", h.attend)]
-        for name, fn in stages:
-            if timer is None:
-                fn()
-            else:
-                timer.run(name, fn)
+        return [("csa_window_append", c.append_token), ("csa_compress", c.compress),
+                ("csa_index_topk", c.index_topk), ("csa_attend", c.attend),
+                ("hca_window_append", h.append_token), ("hca_compress", h.compress), ("hca_attend", h.attend)]
 
-    progress("warmup")
+    def step(i):
+        for _, fn in stages_of(i):
+            fn()
+
+    progress("warmup (eager)")
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
+    # One HIP graph per replica for the whole step (the library only enqueues kernels on the
+    # current stream, never allocates or synchronizes, so its calls capture as they are).
+    progress("capturing step graphs")
+    graphs = []
+    for i in range(replicas):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(i)
+        graphs.append(g)
+    for i in range(warmup):
+        graphs[i % replicas].replay()
+    torch.cuda.synchronize()
     progress("timed steps")
-    # pass 1: whole-step timing with no per-stage events
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     w0 = time.perf_counter()
     t0.record()
     for i in range(steps):
-        step(i)
+        graphs[i % replicas].replay()
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms_step = t0.elapsed_time(t1) / steps
-    # pass 2: per-stage events
-    timer = StageTimer()
-    for i in range(steps):
-        step(i, timer)
-    torch.cuda.synchronize()
-    st = timer.means_ms()
+    # per-stage device time: each stage captured on its own, replayed back to back between
+    # two events on the stream the kernels run on (rotating replicas like the step)
+    progress("per-stage timing")
+    names = [n for n, _ in stages_of(0)]
+    stage_graphs = {n: [] for n in names}
+    for i in range(replicas):
+        for n, fn in stages_of(i):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            stage_graphs[n].append(g)
+    st = {}
+    reps = max(steps, 20)
+    for n in names:
+        for i in range(replicas):
+            stage_graphs[n][i].replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            stage_graphs[n][i % replicas].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        st[n] = e0.elapsed_time(e1) / reps
+    # the stages leave the caches exactly as the step does (idempotent at a fixed position)
     pos = [int(x) for x in ctx.tolist()]
     work = decode_work(cfg, pos)
     value = cfg.B / (ms_step / 1e3)
@@ -198,6 +226,8 @@ def bench_decode(cfg, steps, warmup, replicas, args):
             "hca_attend": {"bound": "mfma", "achieved_TFLOPs": round(work["hca_flops"] / st["hca_attend"] / 1e9, 2)},
         },
         "wall_s_timed": round(wall, 4),
+        "timing": "whole step: HIP-graph replays (one graph per cache replica); stages: per-stage graphs "
+                  "replayed back to back between HIP events",
     }
     config = {"workload": f"{cfg.name}: decode step of one CSA + one HCA layer, batch {cfg.B}, "
                           f"context {cfg.ctx_lo}-{cfg.ctx_hi}, {cfg.n_h} heads, D={cfg.D}, kv {cfg.kv}, "

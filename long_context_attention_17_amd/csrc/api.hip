@@ -218,7 +218,7 @@ static int index_common(const ca_index_params* p, const void* qI, const float* w
       ws_long = (char*)ws + align256((size_t)n_rows * stride * sizeof(float));
   }
   hipError_t e = ca::launch_index_scores(cv, *p, qI, w, pos, seq_fixed, (int)n_rows, max_pos, scores, stride,
-                                         S(stream));
+                                         ws_long, S(stream));
   if (e != hipSuccess) return hip_status(e, what);
   e = ca::launch_topk(scores, stride, pos, p->ratio, p->k, (int)n_rows, out_idx, out_cnt, out_score, ws_long,
                       S(stream));

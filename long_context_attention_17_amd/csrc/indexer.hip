@@ -89,27 +89,52 @@ __global__ void index_scores_generic_kernel(CacheView cv, int nI, int cI, int m,
 
 // ------------------------------------------------------------------ scores, fp8 MFMA (nI = 8, cI = 64)
 // Block: 256 threads (4 waves).  blockIdx.x = group of QPW query rows,
-// blockIdx.y = chunk of kChunk keys; wave w takes key blocks w, w+4, ...
+// blockIdx.y = chunk of kScoreChunk keys (64 pages); wave w owns 1,024
+// consecutive keys (16 pages) as 32 MFMA blocks of 32 keys, processed in groups
+// of 4 blocks with a register double buffer: the loads of group g+1 are in
+// flight while group g is scored.  The chunk's slice of the page table is
+// staged in LDS once, so key loads never wait on a page-table load.
+constexpr int kScoreChunk = 4096;
+constexpr int kHistBins = 4096;
+
+struct KeyGroup {
+  i32x4 v0[4], v1[4];
+  float ks[4];
+  bool ok[4];
+};
+
+__device__ __forceinline__ void load_key_group(const CacheView& cv, const int* pt_s, int64_t k0, int64_t k1,
+                                               int64_t gbase, int lane, KeyGroup& kg) {
+  constexpr int cI = 64;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t s = gbase + 32 * u + (lane & 31);
+    const int pg = s < k1 ? pt_s[(int)((s - k0) >> cv.page_shift)] : -1;
+    kg.ok[u] = pg >= 0;
+    kg.v0[u] = i32x4{0, 0, 0, 0};
+    kg.v1[u] = kg.v0[u];
+    kg.ks[u] = 0.0f;
+    if (kg.ok[u]) {
+      const uint8_t* base = cv.pool + (int64_t)pg * cv.page_bytes;
+      const int slot = cv.slot_of(s);
+      const i32x4* kp = (const i32x4*)(base + slot * cI + 32 * (lane >> 5));
+      kg.v0[u] = kp[0];
+      kg.v1[u] = kp[1];
+      kg.ks[u] = ((const float*)(base + (cI << cv.page_shift)))[slot];
+    }
+  }
+}
+
 template <int QPW>
 __global__ void __launch_bounds__(256) index_scores_fp8_kernel(CacheView cv, int m, int q_fmt, const void* qI,
                                                                const float* w, const int32_t* pos, int seq_fixed,
                                                                int n_rows, float* scores, int64_t stride) {
-  constexpr int nI = 8, cI = 64, kChunk = 1024;
+  constexpr int nI = 8, cI = 64;
   __shared__ __attribute__((aligned(16))) uint8_t qcodes[32 * cI];  // A operand rows: (query, head)
   __shared__ float wq[32];                                          // w * query scale per row
+  __shared__ int pt_s[kScoreChunk / 16];                            // page ids of the chunk (>= 64 pages)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r0 = blockIdx.x * QPW;
-
-  // prologue: quantize QPW*8 query-head rows (one wavefront per row, 64 channels)
-  for (int row = wave; row < 32; row += 4) {
-    int qq = row / nI, h = row % nI, r = r0 + qq;
-    bool valid = qq < QPW && r < n_rows;
-    float v = valid ? load_act(qI, q_fmt, ((int64_t)r * nI + h) * cI + lane) : 0.0f;
-    int e = pow2_exponent(wave_max(fabsf(v)));
-    qcodes[row * cI + lane] = valid ? (uint8_t)e4m3_encode(ldexpf(v, -e)) : 0;
-    if (lane == 0) wq[row] = valid ? w[(int64_t)r * nI + h] * ldexpf(1.0f, e) : 0.0f;
-  }
-  __syncthreads();
 
   int64_t ne[QPW];
   int64_t ne_max = 0;
@@ -120,10 +145,31 @@ __global__ void __launch_bounds__(256) index_scores_fp8_kernel(CacheView cv, int
     ne[qq] = r < n_rows ? (t / m < stride ? t / m : stride) : 0;
     ne_max = ne[qq] > ne_max ? ne[qq] : ne_max;
   }
-  const int64_t k0 = (int64_t)blockIdx.y * kChunk;
-  if (k0 >= ne_max) return;
-  const int64_t k1 = (k0 + kChunk < ne_max) ? k0 + kChunk : ne_max;
-  const int seq = seq_fixed >= 0 ? seq_fixed : r0;   // decode: one row per group, row == sequence
+  const int64_t k0 = (int64_t)blockIdx.y * kScoreChunk;
+  if (k0 >= ne_max) return;                            // uniform over the block
+  const int64_t k1 = (k0 + kScoreChunk < ne_max) ? k0 + kScoreChunk : ne_max;
+  const int seq = seq_fixed >= 0 ? seq_fixed : r0;     // decode: one row per group, row == sequence
+
+  // prologue: the chunk's page ids, and QPW*8 query-head rows quantized to e4m3
+  const int n_pg = kScoreChunk >> cv.page_shift;
+  for (int i = threadIdx.x; i < n_pg; i += 256) {
+    const int64_t pi = (k0 >> cv.page_shift) + i;
+    int pg = -1;
+    if (pi < cv.max_pages) {
+      pg = cv.page_table[(int64_t)seq * cv.max_pages + pi];
+      if (pg >= cv.n_pages) pg = -1;
+    }
+    pt_s[i] = pg;
+  }
+  for (int row = wave; row < 32; row += 4) {
+    int qq = row / nI, hh = row % nI, r = r0 + qq;
+    bool valid = qq < QPW && r < n_rows;
+    float v = valid ? load_act(qI, q_fmt, ((int64_t)r * nI + hh) * cI + lane) : 0.0f;
+    int e = pow2_exponent(wave_max(fabsf(v)));
+    qcodes[row * cI + lane] = valid ? (uint8_t)e4m3_encode(ldexpf(v, -e)) : 0;
+    if (lane == 0) wq[row] = valid ? w[(int64_t)r * nI + hh] * ldexpf(1.0f, e) : 0.0f;
+  }
+  __syncthreads();
 
   // A operand: row lane%32, bytes [32*(lane/32), +32)
   i32x8 a;
@@ -138,33 +184,31 @@ __global__ void __launch_bounds__(256) index_scores_fp8_kernel(CacheView cv, int
 #pragma unroll
     for (int v = 0; v < 4; ++v) wl[qq][v] = wq[qq * nI + 4 * (lane >> 5) + v];
 
-  for (int64_t kb = k0 + 32 * wave; kb < k1; kb += 128) {
-    const int64_t s = kb + (lane & 31);
-    uint8_t* page = s < k1 ? cv.page_of(seq, s) : nullptr;
-    i32x8 bop = {0, 0, 0, 0, 0, 0, 0, 0};
-    float ks = 0.0f;
-    if (page != nullptr) {
-      int slot = cv.slot_of(s);
-      const u32x4* kp = (const u32x4*)(page + slot * cI + 32 * (lane >> 5));
-      u32x4 v0 = kp[0], v1 = kp[1];
-      bop[0] = v0[0]; bop[1] = v0[1]; bop[2] = v0[2]; bop[3] = v0[3];
-      bop[4] = v1[0]; bop[5] = v1[1]; bop[6] = v1[2]; bop[7] = v1[3];
-      ks = ((const float*)(page + (cI << cv.page_shift)))[slot];
-    }
-    f32x16 acc = {};
-    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bop, acc, 0, 0, 0, 127, 0, 127);
-    // acc[v]: row 8*(v/4) + 4*(lane/32) + v%4 = (query v/4, head 4*(lane/32) + v%4), key lane%32
+  const int64_t wbase = k0 + (kScoreChunk / 4) * wave;
+  constexpr int kGroups = kScoreChunk / 4 / 128;       // groups of 4 x 32 keys per wave
+  KeyGroup cur, nxt;
+  load_key_group(cv, pt_s, k0, k1, wbase, lane, cur);
+  for (int grp = 0; grp < kGroups; ++grp) {
+    const int64_t gbase = wbase + 128 * grp;
+    if (gbase >= k1) break;
+    if (grp + 1 < kGroups) load_key_group(cv, pt_s, k0, k1, gbase + 128, lane, nxt);
 #pragma unroll
-    for (int qq = 0; qq < QPW; ++qq) {
-      float part = 0.0f;
+    for (int u = 0; u < 4; ++u) {
+      const int64_t s = gbase + 32 * u + (lane & 31);
+      const i32x8 bop = __builtin_shufflevector(cur.v0[u], cur.v1[u], 0, 1, 2, 3, 4, 5, 6, 7);
+      f32x16 acc = {};
+      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bop, acc, 0, 0, 0, 127, 0, 127);
+      // acc[v]: row 8*(v/4) + 4*(lane/32) + v%4 = (query v/4, head 4*(lane/32) + v%4), key lane%32
 #pragma unroll
-      for (int v = 0; v < 4; ++v) part += wl[qq][v] * fmaxf(acc[4 * qq + v], 0.0f);
-      part += __shfl_xor(part, 32, 64);
-      if (lane < 32 && s < ne[qq]) {
-        float sc = page != nullptr ? part * ks : -INFINITY;
-        scores[(int64_t)(r0 + qq) * stride + s] = sc;
+      for (int qq = 0; qq < QPW; ++qq) {
+        float part = 0.0f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) part += wl[qq][v] * fmaxf(acc[4 * qq + v], 0.0f);
+        part += __shfl_xor(part, 32, 64);
+        if (lane < 32 && s < ne[qq]) scores[(int64_t)(r0 + qq) * stride + s] = cur.ok[u] ? part * cur.ks[u] : -INFINITY;
       }
     }
+    cur = nxt;
   }
 }
 
@@ -300,7 +344,6 @@ __global__ void __launch_bounds__(kTopkThreads) topk_rows_kernel(const float* sc
 //      threshold) and sorts the kept indices ascending.
 // The candidate list is filled in arbitrary order, but pass 3 depends only on
 // the set of (key, index) pairs, so the result is deterministic.
-constexpr int kHistBins = 4096;
 constexpr int kChunk = 4096;
 constexpr int kResolveThreads = 1024;
 constexpr int kResolveLds = 8192;     // candidates held in LDS (more spill to the global list)
@@ -335,58 +378,101 @@ __global__ void __launch_bounds__(256) topk_hist_kernel(const float* scores, int
     if (h[i]) atomicAdd(&g[i], h[i]);
 }
 
-// Bin holding the k-th largest key of a row, from its histogram (block-wide).
-__device__ uint32_t threshold_bin(const uint32_t* g, int k, uint32_t* part) {
-  const int tid = threadIdx.x, nt = blockDim.x;
-  const int per = kHistBins / nt;
+// Bin holding the k-th largest key of a row, from its histogram (block of 256
+// threads): the histogram is staged in LDS, each thread sums 16 bins, wave 0
+// finds the thread whose bins hold the k-th key by a suffix scan, and that
+// thread walks its 16 bins from the top.
+__device__ uint32_t threshold_bin(const uint32_t* g, int k, uint32_t* hb, uint32_t* part) {
+  __shared__ uint32_t sel_owner, sel_above, sel_bin;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kHistBins; i += 256) hb[i] = g[i];
+  __syncthreads();
   uint32_t sum = 0;
-  for (int i = 0; i < per; ++i) sum += g[tid * per + i];
+  for (int i = 0; i < 16; ++i) sum += hb[16 * tid + i];
   part[tid] = sum;
   __syncthreads();
-  // suffix of the per-thread sums (threads above this one), serial over <= 256 entries per thread is
-  // avoided: one pass by wave 0 over the partial sums
-  __shared__ uint32_t sel;
-  if (tid == 0) {
-    uint32_t cum = 0;
-    int owner = 0;
-    for (int i = nt - 1; i >= 0; --i) {
-      if (cum + part[i] >= (uint32_t)k) { owner = i; break; }
-      cum += part[i];
+  if (tid < 64) {
+    // lane L owns threads 4L..4L+3; suffix sums from the top thread down
+    uint32_t c[4] = {part[4 * tid], part[4 * tid + 1], part[4 * tid + 2], part[4 * tid + 3]};
+    uint32_t lsum = c[0] + c[1] + c[2] + c[3];
+    uint32_t incl = lsum;
+    for (int o = 1; o < 64; o <<= 1) {
+      uint32_t v = __shfl_down(incl, o, 64);
+      if (tid + o < 64) incl += v;
     }
-    for (int b = owner * per + per - 1; b >= owner * per; --b) {
-      if (cum + g[b] >= (uint32_t)k) { sel = (uint32_t)b; break; }
-      cum += g[b];
+    uint32_t cum = incl - lsum;
+    for (int d = 3; d >= 0; --d) {
+      uint32_t nxt = cum + c[d];
+      if (cum < (uint32_t)k && nxt >= (uint32_t)k) {
+        sel_owner = 4 * tid + d;
+        sel_above = cum;
+      }
+      cum = nxt;
     }
   }
   __syncthreads();
-  return sel;
+  if (tid == (int)sel_owner) {
+    uint32_t cum = sel_above;
+    for (int b = 16 * tid + 15; b >= 16 * tid; --b) {
+      if (cum + hb[b] >= (uint32_t)k) {
+        sel_bin = (uint32_t)b;
+        break;
+      }
+      cum += hb[b];
+    }
+  }
+  __syncthreads();
+  return sel_bin;
 }
 
 __global__ void __launch_bounds__(256) topk_gather_kernel(const float* scores, int64_t stride, const int32_t* pos,
                                                           int m, int k, const uint32_t* hist, uint32_t* cand_n,
                                                           uint32_t* cand_key, uint32_t* cand_idx) {
   __shared__ uint32_t part[256];
-  const int r = blockIdx.x;
+  __shared__ uint32_t hb[kHistBins];
+  __shared__ uint32_t base_s;
+  const int r = blockIdx.x, tid = threadIdx.x;
   const int64_t n = row_len(pos, r, m, stride);
   const int64_t c0 = (int64_t)blockIdx.y * kChunk;
   if (n <= k || c0 >= n) return;
-  const uint32_t bstar = threshold_bin(hist + (int64_t)r * kHistBins, k, part);
+  const uint32_t bstar = threshold_bin(hist + (int64_t)r * kHistBins, k, hb, part);
   const float* row = scores + (int64_t)r * stride;
-  const int64_t c1 = c0 + kChunk < n ? c0 + kChunk : n;
-  const int lane = threadIdx.x & 63;
-  for (int64_t base = c0; base < c1; base += blockDim.x) {
-    int64_t s = base + threadIdx.x;
-    uint32_t key = s < c1 ? order_key(row[s]) : 0u;
-    bool keep = s < c1 && (key >> 20) >= bstar;
-    uint64_t b = __ballot(keep);
-    if (b == 0) continue;
-    uint32_t first = 0;
-    if (lane == 0) first = atomicAdd(&cand_n[r], (uint32_t)__popcll(b));
-    first = __shfl(first, 0, 64);
-    if (keep) {
-      uint32_t o = first + (uint32_t)__popcll(b & ((1ull << lane) - 1ull));
-      cand_key[(int64_t)r * stride + o] = key;
+  // each thread owns 16 consecutive keys of the chunk
+  constexpr int kPer = kChunk / 256;
+  const int64_t s0 = c0 + (int64_t)tid * kPer;
+  uint32_t keys[kPer];
+  uint32_t mine = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int64_t s = s0 + i;
+    keys[i] = s < n ? order_key(row[s]) : 0u;
+    mine += (s < n && (keys[i] >> 20) >= bstar) ? 1u : 0u;
+  }
+  // block-wide exclusive prefix of the per-thread counts, one reservation per block
+  const int lane = tid & 63, wave = tid >> 6;
+  uint32_t incl = mine;
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  __syncthreads();
+  if (lane == 63) part[wave] = incl;
+  __syncthreads();
+  uint32_t before = incl - mine, total = 0;
+  for (int w = 0; w < 4; ++w) {
+    before += w < wave ? part[w] : 0u;
+    total += part[w];
+  }
+  if (tid == 0) base_s = total ? atomicAdd(&cand_n[r], total) : 0u;
+  __syncthreads();
+  uint32_t o = base_s + before;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int64_t s = s0 + i;
+    if (s < n && (keys[i] >> 20) >= bstar) {
+      cand_key[(int64_t)r * stride + o] = keys[i];
       cand_idx[(int64_t)r * stride + o] = (uint32_t)s;
+      ++o;
     }
   }
 }
@@ -552,12 +638,18 @@ __global__ void __launch_bounds__(kResolveThreads) topk_resolve_kernel(const flo
 // ------------------------------------------------------------------ launchers
 hipError_t launch_index_scores(const CacheView& cv, const ca_index_params& p, const void* qI, const float* w,
                                const int32_t* pos, int seq_fixed, int n_rows, int64_t max_pos, float* scores,
-                               int64_t stride, hipStream_t st) {
+                               int64_t stride, void* ws_long, hipStream_t st) {
   if (n_rows == 0) return hipSuccess;
   int64_t max_ne = max_pos / p.ratio;
   if (max_ne == 0) return hipSuccess;
-  if (cv.fmt == CA_E4M3 && p.n_heads == 8 && p.dim == 64) {
-    const int64_t chunks = (max_ne + 1023) / 1024;
+  const bool long_rows = ws_long != nullptr && topk_use_long(stride, p.k);
+  uint32_t* hist = long_rows ? (uint32_t*)ws_long : nullptr;
+  if (long_rows) {  // clear the histograms and candidate counters of the multi-workgroup top-k
+    const int64_t nz = (int64_t)n_rows * (kHistBins + 1);
+    hipLaunchKernelGGL(topk_zero_kernel, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, st, hist, nz);
+  }
+  if (cv.fmt == CA_E4M3 && p.n_heads == 8 && p.dim == 64 && cv.page_shift >= 4) {
+    const int64_t chunks = (max_ne + kScoreChunk - 1) / kScoreChunk;
     if (seq_fixed >= 0) {
       dim3 grid((unsigned)((n_rows + 3) / 4), (unsigned)chunks);
       hipLaunchKernelGGL(index_scores_fp8_kernel<4>, grid, dim3(256), 0, st, cv, p.ratio, p.q_format, qI, w, pos,
@@ -572,6 +664,11 @@ hipError_t launch_index_scores(const CacheView& cv, const ca_index_params& p, co
     size_t sm = sizeof(float) * p.n_heads * p.dim;
     hipLaunchKernelGGL(index_scores_generic_kernel, grid, dim3(256), sm, st, cv, p.n_heads, p.dim, p.ratio,
                        p.q_format, qI, w, pos, seq_fixed, scores, stride);
+  }
+  if (hist != nullptr) {  // scores written without a fused histogram: count them now
+    const unsigned chunks = (unsigned)((stride + kChunk - 1) / kChunk);
+    hipLaunchKernelGGL(topk_hist_kernel, dim3(n_rows, chunks), dim3(256), 0, st, scores, stride, pos, p.ratio, p.k,
+                       hist);
   }
   return hipGetLastError();
 }
@@ -590,10 +687,8 @@ hipError_t launch_topk(const float* scores, int64_t stride, const int32_t* pos, 
     uint32_t* cand_n = hist + (int64_t)n_rows * kHistBins;
     uint32_t* cand_key = cand_n + n_rows;
     uint32_t* cand_idx = cand_key + (int64_t)n_rows * stride;
-    const int64_t nz = (int64_t)n_rows * (kHistBins + 1);
-    hipLaunchKernelGGL(topk_zero_kernel, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, st, hist, nz);
+    // the histogram was filled by the scoring launch (see launch_index_scores)
     const unsigned chunks = (unsigned)((stride + kChunk - 1) / kChunk);
-    hipLaunchKernelGGL(topk_hist_kernel, dim3(n_rows, chunks), dim3(256), 0, st, scores, stride, pos, m, k, hist);
     hipLaunchKernelGGL(topk_gather_kernel, dim3(n_rows, chunks), dim3(256), 0, st, scores, stride, pos, m, k, hist,
                        cand_n, cand_key, cand_idx);
     hipLaunchKernelGGL(topk_resolve_kernel, dim3(n_rows), dim3(kResolveThreads), 0, st, scores, stride, pos, m, k,

@@ -18,9 +18,11 @@ hipError_t launch_store_entries(const CacheView& cv, int seq, int64_t first, int
 hipError_t launch_window_append(const ca_window_params& p, const void* raw, const float* gain, const int32_t* pos,
                                 const int32_t* seq, int T, void* window, int W, int S, hipStream_t st);
 
+// Scores of every eligible block.  With ws_long (the multi-workgroup top-k state,
+// used when the rows are long) the per-row key histograms are also cleared and filled.
 hipError_t launch_index_scores(const CacheView& cv, const ca_index_params& p, const void* qI, const float* w,
                                const int32_t* pos, int seq_fixed, int n_rows, int64_t max_pos, float* scores,
-                               int64_t stride, hipStream_t st);
+                               int64_t stride, void* ws_long, hipStream_t st);
 // Top-k over score rows.  With ws_long (topk_long_workspace bytes) and rows longer than
 // one workgroup's LDS, the multi-workgroup histogram / gather / resolve path runs.
 size_t topk_long_workspace(int n_rows, int64_t stride);
