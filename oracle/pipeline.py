@@ -28,6 +28,16 @@ def f64(x) -> np.ndarray:
     return np.ascontiguousarray(x, dtype=np.float64)
 
 
+def take_rows(x, rows) -> np.ndarray:
+    """float64 copy of x[rows] (rows selected before the conversion, so a large device
+    tensor is never converted whole)."""
+    if hasattr(x, "detach"):
+        import torch
+        idx = torch.as_tensor(np.asarray(rows, np.int64), device=x.device)
+        return f64(x[idx])
+    return f64(np.asarray(x)[np.asarray(rows)])
+
+
 def store_window(values: np.ndarray, act: str) -> np.ndarray:
     """Round processed window rows to their storage format (fp32 or bf16 bits)."""
     if act == "f32":
@@ -71,13 +81,13 @@ def csa_prefill(cfg, inp: dict, pt_row, n_pool_pages: int, rows=None, idx_overri
     res["window"] = win
     rows = pos_all if rows is None else np.asarray(rows, np.int64)
     res["rows"] = rows
-    qI = indexer_query_values(f64(inp["qI"])[rows], cfg.idx)
-    scores, n_elig = index_scores(qI, f64(inp["w"])[rows], rows, m, idx_fmt, P, ipool, pt_row[None],
+    qI = indexer_query_values(take_rows(inp["qI"], rows), cfg.idx)
+    scores, n_elig = index_scores(qI, take_rows(inp["w"], rows), rows, m, idx_fmt, P, ipool, pt_row[None],
                                   [E.shape[0]], n_cols=max(1, E.shape[0]))
     idx, cnt = topk(scores, n_elig, cfg.k)
     res.update(scores=scores, n_elig=n_elig, idx=idx, cnt=cnt)
     a_idx, a_cnt = (idx, cnt) if idx_override is None else idx_override
-    res["out"] = attend(f64(inp["q"])[rows], rows, kv_fmt, P, pool, pt_row[None], [E.shape[0]], 0, m, win,
+    res["out"] = attend(take_rows(inp["q"], rows), rows, kv_fmt, P, pool, pt_row[None], [E.shape[0]], 0, m, win,
                         cfg.n_win, f64(inp["sink"]), R, gq=f64(inp["g_q"]), idx=a_idx, cnt=a_cnt,
                         base=cfg.rope_base, eps=cfg.eps)
     return res
@@ -94,7 +104,7 @@ def hca_prefill(cfg, inp: dict, pt_row, n_pool_pages: int, rows=None) -> dict:
     win = store_window(window_prep(f64(inp["kv_raw"]), pos_all, R, f64(inp["g_w"]), cfg.eps, cfg.rope_base),
                        cfg.act)[None]
     rows = pos_all if rows is None else np.asarray(rows, np.int64)
-    out = attend(f64(inp["q"])[rows], rows, kv_fmt, P, pool, pt_row[None], [E.shape[0]], 1, m, win, cfg.n_win,
+    out = attend(take_rows(inp["q"], rows), rows, kv_fmt, P, pool, pt_row[None], [E.shape[0]], 1, m, win, cfg.n_win,
                  f64(inp["sink"]), R, gq=f64(inp["g_q"]), base=cfg.rope_base, eps=cfg.eps)
     return dict(entries_raw=E, pool=pool, window=win, rows=rows, out=out, n_entries=E.shape[0])
 
@@ -203,5 +213,5 @@ def hca_decode_step(cfg, inp: dict, state: dict, seqs=None) -> dict:
     return dict(out=out, seqs=seqs)
 
 
-__all__ = ["f64", "csa_prefill", "hca_prefill", "decode_state", "decode_compress", "csa_decode_step",
+__all__ = ["f64", "take_rows", "csa_prefill", "hca_prefill", "decode_state", "decode_compress", "csa_decode_step",
            "hca_decode_step", "indexer_query_values", "store_window", "new_pool", "FMT_E4M3", "FMT_F32"]

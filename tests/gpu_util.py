@@ -50,6 +50,16 @@ def pool_values(cache, seq: int, n: int) -> np.ndarray:
     return oracle.load_entries(cache.fmt, cache.dim, cache.rope_dim, cache.page_size, pool, pt, 0, n)
 
 
+def pow2_exponents(amax: np.ndarray) -> np.ndarray:
+    """Vectorized smallest e with amax <= 448 * 2^e (0 for amax == 0), exact."""
+    amax = np.asarray(amax, np.float64)
+    with np.errstate(divide="ignore"):
+        e = np.where(amax > 0, np.ceil(np.log2(np.where(amax > 0, amax, 1.0) / 448.0)), 0.0)
+    e = np.where((amax > 0) & (amax > 448.0 * np.exp2(e)), e + 1, e)
+    e = np.where((amax > 0) & (amax <= 448.0 * np.exp2(e - 1)), e - 1, e)
+    return e
+
+
 def format_step(fmt: str, ref: np.ndarray, D: int = 0, R: int = 0) -> np.ndarray:
     """One step of the storage format at each reference value."""
     a = np.abs(ref)
@@ -64,30 +74,42 @@ def format_step(fmt: str, ref: np.ndarray, D: int = 0, R: int = 0) -> np.ndarray
         C = D - R
         for t in range(C // 64):
             blk = a[..., 64 * t:64 * t + 64]
-            e = np.array([[oracle.pow2_exponent(x) for x in row] for row in blk.max(-1, keepdims=True).reshape(-1, 1)])
-            e = e.reshape(blk.shape[:-1] + (1,)).astype(float)
+            e = pow2_exponents(blk.max(-1, keepdims=True))
             rel = np.maximum(blk / 2.0 ** e, 2.0 ** -6)
             step[..., 64 * t:64 * t + 64] = 2.0 ** (np.floor(np.log2(rel)) - 3 + e)
         step[..., C:] = 2.0 ** (np.floor(np.log2(np.maximum(a[..., C:], 1e-30))) - 7)
         return step
     if fmt == "e4m3":
-        e = np.array([oracle.pow2_exponent(x) for x in a.max(-1)], float)[:, None]
+        e = pow2_exponents(a.max(-1, keepdims=True))
         rel = np.maximum(a / 2.0 ** e, 2.0 ** -6)
         return 2.0 ** (np.floor(np.log2(rel)) - 3 + e)
     raise ValueError(fmt)
 
 
 def check_stored(gpu_vals, orc_vals, fmt, D=0, R=0, what="entries", max_frac=0.02):
-    """Stored entries: every element within one storage step (two for rare tile-scale flips),
-    and only a small fraction of elements may differ at all."""
+    """Stored entries: every element within one storage step at its magnitude (two for rare
+    fp8 tile-scale flips) plus a few fp32 ulps of its row's largest value, and only a small
+    fraction of elements may differ at all."""
     if np.size(orc_vals) == 0:
         return 0.0
-    step = format_step(fmt, orc_vals, D, R)
+    # the step is taken at the larger magnitude of the two values (a value rounded up
+    # across a binade boundary is one step of the upper binade away)
+    big = np.where(np.abs(gpu_vals) > np.abs(orc_vals), gpu_vals, orc_vals)
+    step = np.maximum(format_step(fmt, orc_vals, D, R), format_step(fmt, big, D, R))
+    # plus the GPU's fp32 arithmetic before the rounding: a value that results from
+    # cancellation (a rotation, a norm) carries an error relative to its row's scale,
+    # not to itself -- a few fp32 ulps of the row maximum
+    step = step + np.abs(orc_vals).max(-1, keepdims=True) * 2.0 ** -19
     diff = np.abs(gpu_vals - orc_vals)
     bad = diff > 1.01 * step + 1e-30
     frac_diff = float((diff > 0).mean())
+    if bad.any():
+        where = np.argwhere(bad)[:6]
+        log(f"  {what}: {int(bad.sum())} elements beyond one step; e.g. " + "; ".join(
+            f"{tuple(int(i) for i in w)}: gpu {gpu_vals[tuple(w)]:.8g} oracle {orc_vals[tuple(w)]:.8g} "
+            f"step {step[tuple(w)]:.3g}" for w in where))
     if fmt in ("fp8mix", "e4m3"):
-        assert (diff <= 2.01 * step + 1e-30).all(), f"{what}: {int(bad.sum())} elements beyond two format steps"
+        assert (diff <= 2.01 * step + 1e-30).all(), f"{what}: {int((diff > 2.01 * step).sum())} elements beyond two format steps"
         assert bad.mean() < 1e-3, f"{what}: {bad.mean():.2e} of elements beyond one format step"
     else:
         assert not bad.any(), f"{what}: {int(bad.sum())} elements beyond one format step (max {diff.max():.3e})"

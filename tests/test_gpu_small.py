@@ -161,7 +161,7 @@ def run_decode(cfg, seqs=None, check_batch_invariance=True):
         torch.cuda.synchronize()
         B = cfg.B
         # cache contents written by the store kernel vs the oracle encoder
-        for b in range(min(B, 3)):
+        for b in range(min(B, 2)):
             n = inp["n_entries"][b]
             gv = pool_values(gl.kv, b, n)
             ov = oracle.load_entries(oracle.FMT_BY_NAME[cfg.kv], cfg.D, cfg.R, cfg.page, st["pool"],
