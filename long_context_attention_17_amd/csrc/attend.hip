@@ -215,79 +215,162 @@ __global__ void attend_combine_kernel(AttendArgs a) {
 }
 
 // ======================================================================== MFMA (D = 512)
+// v_mfma_f32_32x32x16_bf16 lane layouts (l = lane, 0..63):
+//   A (32 x 16): lane l holds row l%32, k = 8*(l/32) .. +7
+//   B (16 x 32): lane l holds column l%32, k = 8*(l/32) .. +7
+//   C (32 x 32): element v of lane l is row 8*(v/4) + 4*(l/32) + v%4, column l%32
+// Workgroup = one query row x 64 heads = two wavefront pairs; a pair shares 32
+// heads.  Ring tiles hold 64 items.  Wavefront `half` of a pair
+//   * scores the items 32*half .. +31 of the tile over all 512 channels:
+//     S^T = K Q^T, items on the rows, so element v of lane l is the logit of head
+//     l%32 for item 8*(v/4) + 4*(l/32) + v%4 (queries stay in registers);
+//   * accumulates O for the channels 256*half .. +255 over all 64 items, with its
+//     own probabilities and its partner's, swapped through LDS as bf16 A
+//     fragments.  The lane's 16 probabilities are directly the A operand for the
+//     k-slot order {items 0-3, 8-11 | 4-7, 12-15} (and +16); V is fed in the same
+//     order with LDS transpose loads (ds_read_b64_tr_b16: a 16-lane group reading
+//     a 4-row x 16-column block gets one column per lane).
+// A pair keeps one softmax reference max; the rare move of it is decided
+// workgroup-wide so that its extra exchange can use a barrier.
 constexpr int kD = 512;
 constexpr int kR = 64;
-constexpr int kTile = 32;               // items per tile
-constexpr int kPitch = kD + 8;          // bf16 elements per LDS tile row (16 B pad against bank conflicts)
-constexpr int kRawPitch = 1024;         // bytes per raw (fp8 record or bf16 window) staging row
-constexpr int kMaxItems = 2176;         // item pointers cached in LDS per workgroup (k + window <= 2048 + 128)
+constexpr int kRows = 64;               // items per ring tile
+constexpr int kPitch = kD + 8;          // bf16 elements per LDS tile row (1040 B)
+constexpr int kRawPitch = 592;          // bytes per raw fp8 staging row (584 B record, 16 B granules)
+constexpr int kMaxItems = 2176;         // items per workgroup (k + window <= 2048 + 128); longer rows are split
+constexpr uint32_t kNoItem = 0xFFFFFFFFu;
+constexpr uint32_t kWinFlag = 0x80000000u;
+constexpr float kNoMax = -1.0e30f;      // running max before any valid item (finite: no inf - inf)
+
+// LDS row of tile item i: within each 16-item block the 4x4 (i%4, i/4) index is
+// transposed, so that the 16 rows a quarter-wavefront reads for a K fragment and
+// the 4 rows a 16-lane group reads for a V transpose load (items 4a..4a+3) all sit
+// in different LDS banks at the 1040 B row pitch.
+__device__ __forceinline__ int mx_row(int i) { return (i & ~15) | ((i & 3) << 2) | ((i >> 2) & 3); }
 
 template <int KV_FMT>
-struct MfmaShared {
-  static constexpr int kStages = KV_FMT == CA_FP8MIX ? 3 : 4;
-  // bf16 records: the ring holds bf16 tiles directly.  fp8 records: the ring holds raw
-  // bytes and one bf16 tile receives the dequantized copy.
-  static constexpr int kRingBytes = KV_FMT == CA_FP8MIX ? kTile * kRawPitch : kTile * kPitch * 2;
-  __attribute__((aligned(16))) uint8_t ring[kStages][kRingBytes];
-  __attribute__((aligned(16))) __bf16 tile[KV_FMT == CA_FP8MIX ? kTile * kPitch : 8];
-  const uint8_t* items[kMaxItems];
-  int kind[kStages][kTile];             // 0: skipped item, 1: bf16 row, 2: fp8 record
+struct MxCfg {
+  static constexpr bool kFp8 = KV_FMT == CA_FP8MIX;
+  // bf16 entries: the ring holds the tiles the MFMAs read.  fp8 entries: the ring
+  // holds raw records and one bf16 tile receives the dequantized copy.
+  static constexpr int kStages = 2;
+  static constexpr int kStageBytes = kFp8 ? kRows * kRawPitch : kRows * kPitch * 2;
+  static constexpr int kLoadsPerWave = kRows / 4;       // one row per load instruction
+};
+
+template <int KV_FMT>
+struct MxShared {
+  typedef MxCfg<KV_FMT> C;
+  __attribute__((aligned(16))) uint8_t ring[C::kStages][C::kStageBytes];
+  __attribute__((aligned(16))) __bf16 tile[C::kFp8 ? kRows * kPitch : 8];
+  __attribute__((aligned(16))) bf16x8 pex[4][64][2];    // probabilities of each wavefront (A fragments)
+  uint32_t items[kMaxItems];            // item sources: 16 B units from the pool, | kWinFlag for the window
+  uint32_t valid[C::kStages][4];        // bit u of valid[st][w]: ring row w + 4u holds a real item
+  float tmx[4][32];                     // per-head tile max of each wavefront
+  int bump[4];                          // wavefront wants to move its reference max
+  float lsum[4][32];                    // epilogue: per-head probability sums
   float rope_cs[kR];                    // (cos, sin) of t * theta_p, p < R/2
 };
 
-// Issue the async (global -> LDS) loads of tile `tile_no` into ring stage `st`.
-// Every wave issues exactly 8 load instructions (one per item it owns, items
-// wave, wave+4, ...), so outstanding-load counts are the same for all tiles.
+// Item j of a row as a 16-byte-unit offset (kNoItem: skip it).
+__device__ __forceinline__ uint32_t item_off(const AttendArgs& a, const RowInfo& ri, int r, int j) {
+  bool w;
+  const uint8_t* p = item_ptr(a, ri, r, j, &w);
+  if (p == nullptr) return kNoItem;
+  return w ? kWinFlag | (uint32_t)((p - (const uint8_t*)a.win) >> 4) : (uint32_t)((p - a.kv.pool) >> 4);
+}
+
+__device__ __forceinline__ const uint8_t* item_src(const AttendArgs& a, uint32_t off) {
+  return (off & kWinFlag) ? (const uint8_t*)a.win + ((uint64_t)(off & ~kWinFlag) << 4)
+                          : (const uint8_t*)a.kv.pool + ((uint64_t)off << 4);
+}
+
+// One async global -> LDS load of 16 B per lane (lane l: g + 16 l -> LDS d + 16 l),
+// with the wavefront-uniform addresses in scalar registers.  Written as asm so that
+// the compiler does not treat it as an LDS event of unknown order (which would force
+// full drains of the LDS read counter in the MFMA loops).  It writes no register;
+// its completion is awaited with explicit vmcnt waits, and a compiler-inserted vmcnt
+// wait can only count it as extra, i.e. wait longer.  m0 is restored afterwards.
+__device__ __forceinline__ void lds_load16(uint64_t g, uint32_t d) {
+  const uint32_t lane16 = 16u * (threadIdx.x & 63u);
+  uint32_t saved;
+  __asm__ volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(d), "v"(lane16), "s"(g)
+      : "memory");
+}
+
+// Async (global -> LDS) loads of ring tile `tile_no` into stage `st`, split so
+// that the load instructions can be spread between MFMAs.  Row w + 4u belongs to
+// wavefront w, which issues exactly kLoadsPerWave instructions per tile, so
+// outstanding-load counts are the same for all tiles.  Rows without an item load
+// a finite dummy row and are masked.  fp8 stages take the first 592 B of every row
+// (a whole record); window rows of an fp8 workgroup are read by the dequantizer.
 template <int KV_FMT>
-__device__ __forceinline__ void issue_tile(const AttendArgs& a, const RowInfo& ri, int r, int j0, int j1,
-                                           int tile_no, int st, MfmaShared<KV_FMT>& sh, const uint8_t* dummy) {
-  typedef __attribute__((address_space(3))) void lds_void;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int it = wave + 4 * u;
-    const int j = j0 + tile_no * kTile + it;
-    // the host guarantees j1 - j0 <= kMaxItems (longer rows are split)
-    const uint8_t* p = j < j1 ? sh.items[j - j0] : nullptr;
-    const bool is_win = j >= ri.n_c;
-    const int kind = p == nullptr ? 0 : ((KV_FMT == CA_FP8MIX && !is_win) ? 2 : 1);
-    const uint8_t* src = p == nullptr ? dummy : p;
-    uint8_t* dst = KV_FMT == CA_FP8MIX ? sh.ring[st] + it * kRawPitch : sh.ring[st] + it * kPitch * 2;
-    if (kind == 2) {
-      if (lane < 37) __builtin_amdgcn_global_load_lds(src + 16 * lane, (lds_void*)dst, 16, 0, 0);
-    } else {
-      __builtin_amdgcn_global_load_lds(src + 16 * lane, (lds_void*)dst, 16, 0, 0);
+struct MxIssue {
+  uint64_t src;       // lane u < kLoadsPerWave: source of row w + 4u
+  uint32_t dst;       // LDS address of the ring stage (wavefront-uniform)
+  int wave;           // wavefront index (uniform)
+  bool on;            // wavefront-uniform: a tile is being loaded
+
+  // Row sources of this wavefront, and its valid bits in sh.valid[st][w].
+  __device__ __forceinline__ void prepare(const AttendArgs& a, int j0, int j1, int tile_no, int st,
+                                          MxShared<KV_FMT>& sh, const uint8_t* dummy, bool enable) {
+    typedef MxCfg<KV_FMT> C;
+    typedef __attribute__((address_space(3))) uint8_t lds_u8;
+    const int lane = threadIdx.x & 63;
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    on = enable;
+    dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_u8*)sh.ring[st]);
+    if (!enable) return;
+    uint32_t off = kNoItem;
+    if (lane < C::kLoadsPerWave) {
+      const int j = j0 + tile_no * kRows + wave + 4 * lane;
+      // the host guarantees j1 - j0 <= kMaxItems (longer rows are split)
+      off = j < j1 ? sh.items[j - j0] : kNoItem;
     }
-    if (lane == 0) sh.kind[st][it] = kind;
+    const uint64_t ok = __ballot(off != kNoItem);
+    if (lane == 0) sh.valid[st][wave] = (uint32_t)ok;
+    src = (uint64_t)(uintptr_t)(off == kNoItem ? dummy : item_src(a, off));
   }
-}
 
-// Wait until at most 8*ahead of this wave's async loads are still in flight.
-__device__ __forceinline__ void wait_loads(int ahead) {
-  switch (ahead) {
-    case 0: __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    case 1: __asm__ volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
-    case 2: __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
-    default: __asm__ volatile("s_waitcnt vmcnt(24)" ::: "memory"); break;
+  // (callers test `on` once, outside their instruction stream)
+  __device__ __forceinline__ void row(int u) const {
+    typedef MxCfg<KV_FMT> C;
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)src, u);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(src >> 32), u);
+    const int it = wave + 4 * u;
+    const uint32_t d = C::kFp8 ? dst + it * kRawPitch : dst + mx_row(it) * (kPitch * 2);
+    if (C::kFp8 && (threadIdx.x & 63) >= kRawPitch / 16) return;
+    lds_load16(((uint64_t)hi << 32) | lo, d);
   }
-}
 
-// fp8 records: dequantize the raw stage into the bf16 tile (each thread: 8 slots
-// of 8 channels; content channels scaled by their tile exponent, rotary and
-// window rows copied; skipped items zeroed).
-__device__ __forceinline__ void convert_tile(const uint8_t* raw, const int* kind, __bf16* tile) {
+  __device__ __forceinline__ void all() const {
+    if (!on) return;
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int sid = threadIdx.x + 256 * u;
-    const int it = sid >> 6, sl = sid & 63;
+    for (int u = 0; u < MxCfg<KV_FMT>::kLoadsPerWave; ++u) row(u);
+  }
+};
+
+// fp8 records: dequantize a raw stage into the bf16 tile.  Thread slots of 8
+// channels, one row per wavefront and step; content channels scaled by their tile
+// exponent, rotary channels copied, window rows read from global memory, rows
+// without an item zeroed.
+__device__ __forceinline__ void mx_convert(const AttendArgs& a, const uint8_t* raw, const uint32_t* valid,
+                                           const uint32_t* items, int jt, int j0, int n_c, __bf16* tile) {
+  const int wave = threadIdx.x >> 6, sl = threadIdx.x & 63;
+#pragma unroll 4
+  for (int u = 0; u < kRows / 4; ++u) {
+    const int it = 4 * u + wave;
     const uint8_t* row = raw + it * kRawPitch;
-    __bf16* dst = tile + it * kPitch + 8 * sl;
-    const int kd = kind[it];
+    __bf16* dst = tile + mx_row(it) * kPitch + 8 * sl;
+    const bool ok = (valid[wave] >> u) & 1u;
     u32x4 out = {0u, 0u, 0u, 0u};
-    if (kd == 1) {
-      out = *(const u32x4*)(row + 16 * sl);
-    } else if (kd == 2) {
-      if (sl < 56) {            // channels 8*sl .. 8*sl+7 < 448: e4m3 codes
+    if (ok) {
+      if (jt + it >= n_c) {
+        out = *(const u32x4*)(item_src(a, items[jt + it - j0]) + 16 * sl);
+      } else if (sl < 56) {     // channels 8*sl .. 8*sl+7 < 448: e4m3 codes
         const u32x2 w = *(const u32x2*)(row + 8 * sl);
         const float sc = ldexpf(1.0f, (int)(int8_t)row[kD + kR + (sl >> 3)]);
         bf16x2 c0 = e4m3x2_to_bf16_scaled<false>(w[0], sc), c1 = e4m3x2_to_bf16_scaled<true>(w[0], sc);
@@ -304,97 +387,103 @@ __device__ __forceinline__ void convert_tile(const uint8_t* raw, const int* kind
   }
 }
 
-// S^T = K Q^T for one 32-item tile: two 16-item blocks x two halves of the 512-dim
-// contraction (four independent accumulator chains).  The K fragments are read one
-// step ahead of their MFMAs; sched_barrier keeps the compiler from hoisting all 32
-// reads at once.  Output: this lane's 8 scaled log2 logits (head li, items 4g..4g+3
-// and 16+4g..16+4g+3; -inf for skipped items) and the per-head tile max.
-__device__ __forceinline__ void attend_scores(const __bf16* kt, const int* kind, const bf16x8* qreg,
-                                              float scale_log2, int li, int g, float* sv, float& tmax) {
-  f32x4 s0a = {0.0f, 0.0f, 0.0f, 0.0f}, s1a = s0a, s0b = s0a, s1b = s0a;
-  const __bf16* r0 = kt + li * kPitch + 8 * g;
-  const __bf16* r1 = kt + (16 + li) * kPitch + 8 * g;
-  bf16x8 k0 = *(const bf16x8*)(r0), k1 = *(const bf16x8*)(r1);
-  bf16x8 k2 = *(const bf16x8*)(r0 + 256), k3 = *(const bf16x8*)(r1 + 256);
+// S^T (32 items x 32 heads) = K Q^T over the 512 channels: 32 MFMAs in two
+// accumulation chains, K fragments (row l%32, 16 B at channel 16s + 8(l/32)) read
+// kPf steps ahead; between(u) runs after every second MFMA (u = 0..15).
+constexpr int kPf = 4;
+template <class F>
+__device__ __forceinline__ void mx_scores(const __bf16* kt, const bf16x8* qf, f32x16& s_out, const F& between) {
+  const int lane = threadIdx.x & 63;
+  const __bf16* krow = kt + mx_row(lane & 31) * kPitch + 8 * (lane >> 5);
+  f32x16 acc[2];
 #pragma unroll
-  for (int kb = 0; kb < 8; ++kb) {
-    bf16x8 n0, n1, n2, n3;
-    if (kb < 7) {
-      n0 = *(const bf16x8*)(r0 + 32 * (kb + 1));
-      n1 = *(const bf16x8*)(r1 + 32 * (kb + 1));
-      n2 = *(const bf16x8*)(r0 + 256 + 32 * (kb + 1));
-      n3 = *(const bf16x8*)(r1 + 256 + 32 * (kb + 1));
-    }
-    s0a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qreg[kb], s0a, 0, 0, 0);
-    s1a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qreg[kb], s1a, 0, 0, 0);
-    s0b = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k2, qreg[kb + 8], s0b, 0, 0, 0);
-    s1b = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k3, qreg[kb + 8], s1b, 0, 0, 0);
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[c][v] = 0.0f;
+  bf16x8 kf[kPf];
+#pragma unroll
+  for (int s = 0; s < kPf; ++s) kf[s] = *(const bf16x8*)(krow + 16 * s);
+#pragma unroll
+  for (int s = 0; s < 32; ++s) {
+    acc[s & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s % kPf], qf[s], acc[s & 1], 0, 0, 0);
+    if (s + kPf < 32) kf[s % kPf] = *(const bf16x8*)(krow + 16 * (s + kPf));
+    if (s & 1) between(s >> 1);
     __builtin_amdgcn_sched_barrier(0);
-    if (kb < 7) {
-      k0 = n0;
-      k1 = n1;
-      k2 = n2;
-      k3 = n3;
-    }
   }
-  float mx = -INFINITY;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    sv[v] = kind[4 * g + v] ? (s0a[v] + s0b[v]) * scale_log2 : -INFINITY;
-    sv[4 + v] = kind[16 + 4 * g + v] ? (s1a[v] + s1b[v]) * scale_log2 : -INFINITY;
-    mx = fmaxf(mx, fmaxf(sv[v], sv[4 + v]));
-  }
-  mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-  tmax = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  for (int v = 0; v < 16; ++v) s_out[v] = acc[0][v] + acc[1][v];
 }
 
-// P = 2^(s - m_run) (bf16 A operand, straight from this lane's logits) and O += P V,
-// V^T fragments via LDS transpose loads in the same item order, read one column
-// block ahead of their MFMA.
-__device__ __forceinline__ void attend_pv(const __bf16* kt, const float* sv, float m_run, float& l_part, int li,
-                                          int g, f32x4* oacc) {
+// O (32 heads x 256 channels, 8 column blocks) += P V over the 64 items of a
+// tile: for each 32-item half (pown: this wavefront's items, ppar: its partner's),
+// two k-steps of 16 items x 8 column blocks; V fragments (two transpose loads
+// each) read kPf MFMAs ahead.
+__device__ __forceinline__ void mx_pv(const __bf16* tile, int half, const bf16x8* pown, const bf16x8* ppar,
+                                      f32x16* o) {
   typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-  bf16x8 pa;
+  const int lane = threadIdx.x & 63, G = lane >> 4, i = lane & 15;
+  const int col = 256 * half + 16 * (G & 1) + 4 * (i & 3);
+  const __bf16* va0 = tile + mx_row(4 * (G >> 1) + (i >> 2)) * kPitch + col;      // items e, e + 8 of a
+  const __bf16* vc0 = tile + mx_row(4 * (G >> 1) + (i >> 2) + 8) * kPitch + col;  // 16-item k-step
+  // step n: item half ih = n >> 4 (0: own, 1: partner), k-step ks = (n >> 3) & 1, column block cb = n & 7
+  auto rowbase = [&](int n) { return 32 * ((n >> 4) ? 1 - half : half) + 16 * ((n >> 3) & 1); };
+  bf16x4 va[kPf], vc[kPf];
+#pragma unroll
+  for (int n = 0; n < kPf; ++n) {
+    va[n] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(va0 + rowbase(n) * kPitch + 32 * (n & 7)));
+    vc[n] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vc0 + rowbase(n) * kPitch + 32 * (n & 7)));
+  }
+#pragma unroll
+  for (int n = 0; n < 32; ++n) {
+    bf16x8 vv;
+    vv[0] = va[n % kPf][0]; vv[1] = va[n % kPf][1]; vv[2] = va[n % kPf][2]; vv[3] = va[n % kPf][3];
+    vv[4] = vc[n % kPf][0]; vv[5] = vc[n % kPf][1]; vv[6] = vc[n % kPf][2]; vv[7] = vc[n % kPf][3];
+    if (n + kPf < 32) {
+      const int m = n + kPf;
+      va[n % kPf] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(va0 + rowbase(m) * kPitch + 32 * (m & 7)));
+      vc[n % kPf] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vc0 + rowbase(m) * kPitch + 32 * (m & 7)));
+    }
+    const bf16x8 pa = (n >> 4) ? ppar[(n >> 3) & 1] : pown[(n >> 3) & 1];
+    o[n & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, vv, o[n & 7], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// O = 0, written by MFMAs (zero operands) so that the accumulators are only ever
+// defined by MFMAs and stay in the accumulation registers across the tile loop.
+__device__ __forceinline__ void mx_zero(f32x16* o) {
+  bf16x8 z;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) z[e] = (__bf16)0.0f;
+  const f32x16 zc = {};
+#pragma unroll
+  for (int cb = 0; cb < 8; ++cb) o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(z, z, zc, 0, 0, 0);
+}
+
+// Head (within a 32-head block) of element v of a C-layout accumulator in `lane`.
+__device__ __forceinline__ int mx_row_of(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
+
+// exp2 of the masked logits against the reference, as bf16 A fragments; returns the fp32 sum.
+__device__ __forceinline__ float mx_probs(const float* sv, float m_run, bf16x8* pa) {
   float psum = 0.0f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float p = m_run == -INFINITY ? 0.0f : exp2f(sv[e] - m_run);
+  for (int v = 0; v < 16; ++v) {
+    const float p = __builtin_amdgcn_exp2f(sv[v] - m_run);
     psum += p;
-    pa[e] = __builtin_bit_cast(__bf16, f32_to_bf16_bits(p));
+    pa[v >> 3][v & 7] = (__bf16)p;
   }
-  l_part += psum;
-  const int vrow = 4 * g + (li >> 2), vcol = 4 * (li & 3);
-  const __bf16* vbase = kt + vrow * kPitch + vcol;
-  bf16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vbase));
-  bf16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vbase + 16 * kPitch));
-#pragma unroll
-  for (int cb = 0; cb < 32; ++cb) {
-    bf16x4 na, nb;
-    if (cb < 31) {
-      na = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vbase + 16 * (cb + 1)));
-      nb = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vbase + 16 * kPitch + 16 * (cb + 1)));
-    }
-    bf16x8 vv;
-    vv[0] = va[0]; vv[1] = va[1]; vv[2] = va[2]; vv[3] = va[3];
-    vv[4] = vb[0]; vv[5] = vb[1]; vv[6] = vb[2]; vv[7] = vb[3];
-    oacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vv, oacc[cb], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (cb < 31) {
-      va = na;
-      vb = nb;
-    }
-  }
+  return psum;
 }
 
 template <int KV_FMT>
-__global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a) {
-  typedef MfmaShared<KV_FMT> Sh;
-  constexpr int NS = Sh::kStages;
+__global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
+  typedef MxCfg<KV_FMT> C;
+  typedef MxShared<KV_FMT> Sh;
   __shared__ Sh sh;
 
   const int r = blockIdx.x, hg = blockIdx.y, split = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int li = lane & 15, g = lane >> 4;
+  const int pair = wave >> 1, half = wave & 1, partner = wave ^ 1;
   const RowInfo ri = row_info(a, r);
   const int ns = n_splits_of(a, ri.total);
   if (split >= ns) return;
@@ -403,11 +492,22 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a) {
     j0 = split * a.split_items;
     j1 = j0 + a.split_items < ri.total ? j0 + a.split_items : ri.total;
   }
-  const int ntiles = (j1 - j0 + kTile - 1) / kTile;
-  const int head_s = hg * 64 + wave * 16 + li;      // head this lane scores (S^T column)
-  constexpr int C = kD - kR;
+  const int ntiles = (j1 - j0 + kRows - 1) / kRows;
+  const int head0 = hg * 64 + 32 * pair;               // first head of this pair
+  const int hl = lane & 31;                            // head (within the block) of this lane's S^T column
+  constexpr int CC = kD - kR;
 
-  // ---- prologue: RoPE table for position t, item source table, first async tiles
+  // ---- prologue.  The query loads go first: their latency overlaps the RoPE, gain
+  // and item tables, and being older than the tile loads, waiting for them never
+  // waits for a tile.  B fragments: lane = head l%32, channels 16s + 8(l/32) .. +7.
+  bf16x8 qf[32];
+  {
+    const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)r * a.n_heads + head0 + hl) * kD + 8 * (lane >> 5);
+#pragma unroll
+    for (int s = 0; s < 32; ++s) qf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * s));
+  }
+  float* gain_s = (float*)&sh.pex[0][0][0];            // the exchange buffer is free until the loop
+  for (int i = tid; i < kD; i += 256) gain_s[i] = a.q_gain[i];
   if (tid < kR / 2) {
     float sn, cs;
     rope_sincos((double)ri.t, tid, kR, a.base, &sn, &cs);
@@ -415,38 +515,36 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a) {
     sh.rope_cs[2 * tid + 1] = sn;
   }
   const int n_tab = (j1 - j0) < kMaxItems ? (j1 - j0) : kMaxItems;
-  for (int i = tid; i < n_tab; i += 256) {
-    bool w;
-    sh.items[i] = item_ptr(a, ri, r, j0 + i, &w);
-  }
-  // a valid, finite row used as the source of loads for skipped items: the window token at t
+  for (int i = tid; i < n_tab; i += 256) sh.items[i] = item_off(a, ri, r, j0 + i);
+  // a valid, finite row used as the source of loads for rows without an item: the window token at t
   const uint8_t* dummy = (const uint8_t*)a.win + ((int64_t)ri.win_seq * a.W + ri.t % a.W) * kD * 2;
   __syncthreads();
-  for (int t = 0; t < NS - 1; ++t)
-    if (t < ntiles) issue_tile<KV_FMT>(a, ri, r, j0, j1, t, t, sh, dummy);
+  constexpr int kPrologueTiles = C::kFp8 ? 2 : 1;
+  for (int t = 0; t < kPrologueTiles; ++t) {
+    MxIssue<KV_FMT> is;
+    is.prepare(a, j0, j1, t, t, sh, dummy, t < ntiles);
+    is.all();
+  }
 
-  // ---- query: RMSNorm with gain, RoPE at t, bf16 B-operand fragments (lane: head li, dims 32kb+8g..+7)
-  bf16x8 qreg[16];
+  // ---- query: RMSNorm with gain, RoPE at t, logit scale * log2(e)
   {
-    const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)r * a.n_heads + head_s) * kD;
     float ss = 0.0f;
 #pragma unroll
-    for (int kb = 0; kb < 16; ++kb) {
-      u32x4 w = *(const u32x4*)(qrow + 32 * kb + 8 * g);
+    for (int s = 0; s < 32; ++s) {
+      const u32x4 w = __builtin_bit_cast(u32x4, qf[s]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float x0 = __uint_as_float(w[e] << 16), x1 = __uint_as_float(w[e] & 0xFFFF0000u);
+        const float x0 = __uint_as_float(w[e] << 16), x1 = __uint_as_float(w[e] & 0xFFFF0000u);
         ss += x0 * x0 + x1 * x1;
       }
     }
-    ss += __shfl_xor(ss, 16, 64);
     ss += __shfl_xor(ss, 32, 64);
     const float inv = 1.0f / sqrtf(ss / (float)kD + a.eps);
 #pragma unroll
-    for (int kb = 0; kb < 16; ++kb) {
-      const int d0 = 32 * kb + 8 * g;
-      u32x4 w = *(const u32x4*)(qrow + d0);
-      f32x4 g0 = *(const f32x4*)(a.q_gain + d0), g1 = *(const f32x4*)(a.q_gain + d0 + 4);
+    for (int s = 0; s < 32; ++s) {
+      const int d0 = 16 * s + 8 * (lane >> 5);
+      const f32x4 g0 = *(const f32x4*)(gain_s + d0), g1 = *(const f32x4*)(gain_s + d0 + 4);
+      const u32x4 w = __builtin_bit_cast(u32x4, qf[s]);
       float x[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -455,10 +553,10 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a) {
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] *= inv * (e < 4 ? g0[e] : g1[e - 4]);
-      if (d0 >= C) {
+      if (d0 >= CC) {
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-          const int p = (d0 + e - C) >> 1;
+          const int p = (d0 + e - CC) >> 1;
           const float c = sh.rope_cs[2 * p], sn = sh.rope_cs[2 * p + 1];
           const float x0 = x[e], x1 = x[e + 1];
           x[e] = x0 * c - x1 * sn;
@@ -466,104 +564,171 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a) {
         }
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qreg[kb][e] = __builtin_bit_cast(__bf16, f32_to_bf16_bits(x[e]));
+      for (int e = 0; e < 8; ++e) qf[s][e] = (__bf16)(x[e] * a.scale_log2);
     }
   }
 
-  f32x4 oacc[32];
-#pragma unroll
-  for (int cb = 0; cb < 32; ++cb) oacc[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  // Softmax reference: m_run is fixed by the first tile with a valid item and moves only
-  // when a logit exceeds it by more than kBump (log2 units).  Probabilities relative to
-  // it stay <= 2^kBump, far inside fp32/bf16 range, so the hot loop never rescales O
-  // (no vector ALU work on the accumulators, which then stay in their registers); the
-  // rare move leaves the hot loop, rescales O once and finishes the tile.
+  // Softmax reference: m_run is set by the first tile with a valid item (O is still
+  // zero then) and never moves afterwards; probabilities relative to it stay below
+  // 2^kBump, far inside fp32/bf16 range, unless a later logit exceeds it by more
+  // than kBump.  That (practically unreachable) case sets `redo` and the row is
+  // recomputed with the exact maximum m_true seen on the first pass, so the loop
+  // never rescales O and the accumulators never leave their registers.
   constexpr float kBump = 60.0f;
-  float m_run = -INFINITY, l_part = 0.0f;
-  float sv[8];
-  float tmax = -INFINITY;
-  int tile = 0;
-  while (tile < ntiles) {
-    bool pending = false;
-    const __bf16* kt = nullptr;
-    for (; tile < ntiles; ++tile) {
-      const int st = tile % NS;
-      const int ahead = (ntiles - 1 - tile) < (NS - 2) ? (ntiles - 1 - tile) : (NS - 2);
-      wait_loads(ahead);
-      __syncthreads();                                   // tile `tile` landed for every wave
-      if (tile + NS - 1 < ntiles)
-        issue_tile<KV_FMT>(a, ri, r, j0, j1, tile + NS - 1, (tile + NS - 1) % NS, sh, dummy);
-      if (KV_FMT == CA_FP8MIX) {
-        convert_tile(sh.ring[st], sh.kind[st], sh.tile);
-        __syncthreads();
-        kt = sh.tile;
+  f32x16 oacc[8];
+  mx_zero(oacc);
+  float m_run = kNoMax, l_part = 0.0f, m_true = kNoMax;
+  bool redo = false, second = false;
+  {
+    for (int tile = 0; tile < ntiles; ++tile) {
+      const int st = tile & 1;
+      if constexpr (C::kFp8) {
+        if (tile + 1 < ntiles) __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
       } else {
-        kt = (const __bf16*)sh.ring[st];
+        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
-      attend_scores(kt, sh.kind[st], qreg, a.scale_log2, li, g, sv, tmax);
-      if (__builtin_expect(__any(tmax > m_run + kBump), 0)) {
-        pending = true;
-        break;
+      __syncthreads();                                   // tile landed for every wavefront
+      const u32x4 vw = *(const u32x4*)sh.valid[st];      // (fp8: read before the stage is refilled)
+      const __bf16* tl;
+      MxIssue<KV_FMT> is;
+      if constexpr (C::kFp8) {
+        mx_convert(a, sh.ring[st], sh.valid[st], sh.items, j0 + tile * kRows, j0, ri.n_c, sh.tile);
+        __syncthreads();
+        is.prepare(a, j0, j1, tile + 2, st, sh, dummy, tile + 2 < ntiles);
+        tl = sh.tile;
+      } else {
+        is.prepare(a, j0, j1, tile + 1, st ^ 1, sh, dummy, tile + 1 < ntiles);
+        tl = (const __bf16*)sh.ring[st];
       }
-      attend_pv(kt, sv, m_run, l_part, li, g, oacc);
+      f32x16 s;
+      if (is.on) mx_scores(tl + 32 * half * kPitch, qf, s, [&](int u) { is.row(u); });
+      else mx_scores(tl + 32 * half * kPitch, qf, s, [](int) {});
+      float sv[16];
+      float mx = -INFINITY;
+      if ((vw[0] & vw[1] & vw[2] & vw[3] & 0xFFFFu) == 0xFFFFu) {      // every row holds an item
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          sv[v] = s[v];
+          mx = fmaxf(mx, sv[v]);
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const bool ok = (vw[v & 3] >> (8 * half + 2 * (v >> 2) + (lane >> 5))) & 1u;
+          sv[v] = ok ? s[v] : -INFINITY;
+          mx = fmaxf(mx, sv[v]);
+        }
+      }
+      const float tmax = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const bool bump = __any(tmax > m_run + kBump);
+      bf16x8 pown[2];
+      float psum = mx_probs(sv, m_run, pown);
+      *(bf16x8*)&sh.pex[wave][lane][0] = pown[0];
+      *(bf16x8*)&sh.pex[wave][lane][1] = pown[1];
+      if (lane < 32) sh.tmx[wave][lane] = tmax;
+      if (lane == 0) sh.bump[wave] = bump;
+      __syncthreads();
+      const float tmax_pair = fmaxf(tmax, sh.tmx[partner][hl]);
+      m_true = fmaxf(m_true, tmax_pair);
+      if (sh.bump[0] | sh.bump[1] | sh.bump[2] | sh.bump[3]) {   // workgroup-uniform
+        if (m_run == kNoMax) {
+          // first tile with valid items (the same tile for every head): set the reference
+          m_run = tmax_pair;
+          psum = mx_probs(sv, m_run, pown);
+          __syncthreads();                               // every wavefront has read the flags
+          *(bf16x8*)&sh.pex[wave][lane][0] = pown[0];
+          *(bf16x8*)&sh.pex[wave][lane][1] = pown[1];
+          __syncthreads();
+        } else {
+          redo = true;
+        }
+      }
+      l_part += psum;
+      bf16x8 ppar[2];
+      ppar[0] = *(const bf16x8*)&sh.pex[partner][lane][0];
+      ppar[1] = *(const bf16x8*)&sh.pex[partner][lane][1];
+      mx_pv(tl, half, pown, ppar, oacc);
+      if (__builtin_expect(redo && !second && tile == ntiles - 1, 0)) {   // workgroup-uniform
+        // recompute the row against the exact maximum of the first pass
+        second = true;
+        m_run = m_true;
+        l_part = 0.0f;
+        mx_zero(oacc);
+        __syncthreads();                                 // every wavefront is done with the ring
+        for (int t = 0; t < kPrologueTiles; ++t) {
+          MxIssue<KV_FMT> is2;
+          is2.prepare(a, j0, j1, t, t, sh, dummy, t < ntiles);
+          is2.all();
+        }
+        tile = -1;
+      }
     }
-    if (!pending) break;
-    // rare path: move the reference up to this tile's max and rescale O
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = m_run == -INFINITY ? 0.0f : exp2f(m_run - m_new);
-    l_part *= alpha;
-    m_run = m_new;
-    float al[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) al[v] = __shfl(alpha, 4 * g + v, 64);
-#pragma unroll
-    for (int cb = 0; cb < 32; ++cb)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) oacc[cb][v] *= al[v];
-    attend_pv(kt, sv, m_run, l_part, li, g, oacc);
-    ++tile;
   }
 
-  // ---- epilogue
-  float l_tot = l_part + __shfl_xor(l_part, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
-  const int head_base = hg * 64 + wave * 16;
-  if (a.split_items > 0) {
-    int64_t pbase = ((int64_t)r * a.max_splits + split) * a.n_heads;
-    if (lane < 16) {
-      a.part_ml[2 * (pbase + head_base + lane)] = m_run;
-      a.part_ml[2 * (pbase + head_base + lane) + 1] = l_tot;
+  // ---- epilogue: per-head sum over the pair's items
+  const float l_own = l_part + __shfl_xor(l_part, 32, 64);
+  if (lane < 32) sh.lsum[wave][lane] = l_own;
+  __syncthreads();                                     // also: every wavefront is done with the tiles
+  const float l_tot = l_own + sh.lsum[partner][hl];
+  const int c0 = 256 * half;                           // first channel of this wavefront's O
+  // O goes out through an LDS staging block per wavefront ([32 heads][256 channels]
+  // fp32, row pitch kStage floats; the ring is free now), so that global stores are
+  // whole 16 B (fp32) or 8 B (bf16) runs along the channels.
+  constexpr int kStage = 260;
+  static_assert(sizeof(sh.ring) + sizeof(sh.tile) >= 4 * 32 * kStage * 4, "staging buffer");
+  float* stage = (float*)&sh.ring[0][0] + wave * 32 * kStage;
+  const bool split_out = a.split_items > 0;
+  float fv[16];
+  if (split_out) {
+    const int64_t pbase = ((int64_t)r * a.max_splits + split) * a.n_heads + head0;
+    if (half == 0 && lane < 32) {
+      a.part_ml[2 * (pbase + hl)] = m_run;
+      a.part_ml[2 * (pbase + hl) + 1] = l_tot;
     }
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      float* dst = a.part_o + (pbase + head_base + 4 * g + v) * kD + li;
+    for (int v = 0; v < 16; ++v) fv[v] = 1.0f;
+  } else {
+    const float sk_own = a.sink[head0 + hl] * kLog2e;
+    const float M_own = fmaxf(m_run, sk_own);
+    const float den_own = l_tot * __builtin_amdgcn_exp2f(m_run - M_own) + __builtin_amdgcn_exp2f(sk_own - M_own);
+    const float f_own = __builtin_amdgcn_exp2f(m_run - M_own) / den_own;
+    if (a.lse && half == 0 && lane < 32) a.lse[(int64_t)r * a.n_heads + head0 + hl] = (M_own + log2f(den_own)) / kLog2e;
 #pragma unroll
-      for (int cb = 0; cb < 32; ++cb) dst[16 * cb] = oacc[cb][v];
-    }
-    return;
+    for (int v = 0; v < 16; ++v) fv[v] = __shfl(f_own, mx_row_of(v, lane), 64);
   }
-  const float sk_own = a.sink[head_s] * kLog2e;
-  const float M_own = fmaxf(m_run, sk_own);
-  const float den_own = l_tot * exp2f(m_run - M_own) + exp2f(sk_own - M_own);
-  const float f_own = exp2f(m_run - M_own) / den_own;
-  if (a.lse && lane < 16) a.lse[(int64_t)r * a.n_heads + head_s] = (M_own + log2f(den_own)) / kLog2e;
-  float fv[4];
 #pragma unroll
-  for (int v = 0; v < 4; ++v) fv[v] = __shfl(f_own, 4 * g + v, 64);
+  for (int v = 0; v < 16; ++v) {
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int64_t obase = ((int64_t)r * a.n_heads + head_base + 4 * g + v) * kD;
-#pragma unroll
-    for (int cb = 0; cb < 32; ++cb) {
+    for (int cb = 0; cb < 8; ++cb) {
       float x = oacc[cb][v] * fv[v];
-      if (cb >= 28) {                                  // rotary channels 448..511: rotate by R_{-t}
-        float other = __shfl_xor(x, 1, 64);
-        const int p = (16 * cb + li - C) >> 1;
+      if (!split_out && c0 + 32 * cb >= CC) {          // rotary channels 448..511: rotate by R_{-t}
+        const float other = __shfl_xor(x, 1, 64);
+        const int p = (c0 + 32 * cb + (lane & 31) - CC) >> 1;
         const float c = sh.rope_cs[2 * p], sn = sh.rope_cs[2 * p + 1];
-        x = (li & 1) ? x * c - other * sn : x * c + other * sn;
+        x = (lane & 1) ? x * c - other * sn : x * c + other * sn;
       }
-      if (a.out_fmt == CA_F32) ((float*)a.out)[obase + 16 * cb + li] = x;
-      else ((uint16_t*)a.out)[obase + 16 * cb + li] = f32_to_bf16_bits(x);
+      stage[mx_row_of(v, lane) * kStage + 32 * cb + (lane & 31)] = x;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);                  // lgkmcnt(0): this wavefront's staging writes
+  __builtin_amdgcn_wave_barrier();
+  // row h: 64 lanes x 4 channels
+  for (int h = 0; h < 32; ++h) {
+    const f32x4 x = *(const f32x4*)(stage + h * kStage + 4 * lane);
+    if (split_out) {
+      const int64_t pbase = ((int64_t)r * a.max_splits + split) * a.n_heads + head0;
+      *(f32x4*)(a.part_o + (pbase + h) * kD + c0 + 4 * lane) = x;
+    } else {
+      const int64_t ob = ((int64_t)r * a.n_heads + head0 + h) * kD + c0 + 4 * lane;
+      if (a.out_fmt == CA_F32) {
+        *(f32x4*)((float*)a.out + ob) = x;
+      } else {
+        u32x2 w;
+        w[0] = (uint32_t)f32_to_bf16_bits(x[0]) | ((uint32_t)f32_to_bf16_bits(x[1]) << 16);
+        w[1] = (uint32_t)f32_to_bf16_bits(x[2]) | ((uint32_t)f32_to_bf16_bits(x[3]) << 16);
+        *(u32x2*)((uint16_t*)a.out + ob) = w;
+      }
     }
   }
 }
@@ -572,8 +737,11 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(AttendArgs a) {
 int attend_mfma_max_items() { return kMaxItems; }
 
 bool attend_mfma_supported(const AttendArgs& a) {
-  return a.D == kD && a.R == kR && a.n_heads % 64 == 0 && a.q_fmt == CA_BF16 &&
-         a.win_fmt == CA_BF16 && (a.kv.fmt == CA_BF16 || a.kv.fmt == CA_FP8MIX);
+  // item sources are 31-bit offsets in 16 B units
+  const bool fits = (uint64_t)a.kv.n_pages * (uint64_t)a.kv.page_bytes < (1ull << 35) &&
+                    (uint64_t)a.W * (uint64_t)(a.seq_fixed >= 0 ? 1 : a.n_rows) * kD * 2 < (1ull << 35);
+  return a.D == kD && a.R == kR && a.n_heads % 64 == 0 && a.q_fmt == CA_BF16 && a.win_fmt == CA_BF16 &&
+         (a.kv.fmt == CA_BF16 || a.kv.fmt == CA_FP8MIX) && fits;
 }
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
@@ -582,9 +750,9 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
   if (attend_mfma_supported(a)) {
     dim3 grid(a.n_rows, a.n_heads / 64, splits);
     if (a.kv.fmt == CA_FP8MIX)
-      hipLaunchKernelGGL(attend_mfma_kernel<CA_FP8MIX>, grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL(attend_mx_kernel<CA_FP8MIX>, grid, dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL(attend_mfma_kernel<CA_BF16>, grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL(attend_mx_kernel<CA_BF16>, grid, dim3(256), 0, st, a);
   } else {
     dim3 grid(a.n_rows, a.n_heads, splits);
     switch (a.D / 64) {
