@@ -77,10 +77,21 @@ int64_t score_stride(int64_t max_pos, int ratio) {
   return (ne + 63) / 64 * 64;
 }
 
+// Divisor of the split plan for rows of up to max_items items: kDecodeMaxSplits,
+// raised only when a chunk would exceed one MFMA workgroup's item table.
+int split_div_for(int64_t max_items) {
+  const int64_t cap = ca::attend_mfma_max_items();
+  const int64_t need = (max_items + cap - 1) / cap;
+  return (int)(need > ca::kDecodeMaxSplits ? need : ca::kDecodeMaxSplits);
+}
+
+// Splits per row of the decode plan (an upper bound for the prefill split too).
 int max_splits_for(int64_t max_pos, int n_win, int k, int ratio) {
   int64_t entries = k > 0 ? k : max_pos / ratio;
   int64_t items = entries + n_win;
-  return (int)((items + ca::kDecodeSplitItems - 1) / ca::kDecodeSplitItems);
+  const int64_t by_len = (items + ca::kDecodeSplitItems - 1) / ca::kDecodeSplitItems;
+  const int64_t div = split_div_for(items);
+  return (int)(by_len < div ? (by_len > 0 ? by_len : 1) : div);
 }
 
 }  // namespace
@@ -310,6 +321,7 @@ static int attend_common(const ca_attend_params* p, const void* q, const float* 
   a.out_fmt = p->out_format;
   a.lse = lse;
   a.split_items = 0;
+  a.split_div = 1;
   a.max_splits = 1;
   a.part_o = nullptr;
   a.part_ml = nullptr;
@@ -317,17 +329,24 @@ static int attend_common(const ca_attend_params* p, const void* q, const float* 
   // depends on the sequence alone), and for prefill rows longer than one MFMA
   // workgroup's item table.
   const int64_t max_items = (mode == 0 ? (int64_t)k : max_pos / ratio) + p->n_win;
-  int split = 0;
-  if (decode) split = ca::kDecodeSplitItems;
-  else if (ca::attend_mfma_supported(a) && max_items > ca::attend_mfma_max_items()) split = ca::attend_mfma_max_items();
+  int split = 0, div = 1, ms = 1;
+  if (decode) {
+    split = ca::kDecodeSplitItems;
+    div = split_div_for(max_items);
+    ms = max_splits_for(max_pos, p->n_win, mode == 0 ? k : 0, ratio);
+  } else if (ca::attend_mfma_supported(a) && max_items > ca::attend_mfma_max_items()) {
+    split = ca::attend_mfma_max_items();
+    ms = (int)((max_items + split - 1) / split);
+    div = ms;
+  }
   if (split > 0) {
-    const int ms = (int)((max_items + split - 1) / split);
     const size_t po = align256((size_t)n_rows * ms * p->n_heads * p->dim * sizeof(float));
     const size_t need = po + align256((size_t)n_rows * ms * p->n_heads * 2 * sizeof(float));
     if (ws_bytes < need || ws == nullptr)
       return fail(CA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes (rows of up to %lld items are split)", what,
                   ws_bytes, need, (long long)max_items);
     a.split_items = split;
+    a.split_div = div;
     a.max_splits = ms;
     a.part_o = (float*)ws;
     a.part_ml = (float*)((char*)ws + po);

@@ -74,13 +74,33 @@ __device__ __forceinline__ const uint8_t* item_ptr(const AttendArgs& a, const Ro
   return (const uint8_t*)a.win + ((int64_t)ri.win_seq * a.W + p % a.W) * a.D * esz;
 }
 
+// Split length of a row of `total` items: a function of the row alone.
+__device__ __forceinline__ int split_len_of(const AttendArgs& a, int total) {
+  int len = (total + a.split_div - 1) / a.split_div;
+  len = (len + 63) & ~63;
+  return len > a.split_items ? len : a.split_items;
+}
+
 // Splits of a row; never more than the workspace holds (a row whose position
 // exceeds the caller's max_pos is truncated rather than overrunning it).
 __device__ __forceinline__ int n_splits_of(const AttendArgs& a, int total) {
   if (a.split_items <= 0) return 1;
-  int n = (total + a.split_items - 1) / a.split_items;
+  const int len = split_len_of(a, total);
+  int n = (total + len - 1) / len;
   n = n > 0 ? n : 1;
   return n < a.max_splits ? n : a.max_splits;
+}
+
+// Item range [j0, j1) of split `split` of a row.
+__device__ __forceinline__ void split_range(const AttendArgs& a, int total, int split, int* j0, int* j1) {
+  if (a.split_items <= 0) {
+    *j0 = 0;
+    *j1 = total;
+    return;
+  }
+  const int len = split_len_of(a, total);
+  *j0 = split * len;
+  *j1 = *j0 + len < total ? *j0 + len : total;
 }
 
 // ======================================================================== generic
@@ -91,11 +111,8 @@ __global__ void __launch_bounds__(64) attend_generic_kernel(AttendArgs a) {
   const RowInfo ri = row_info(a, r);
   const int ns = n_splits_of(a, ri.total);
   if (split >= ns) return;
-  int j0 = 0, j1 = ri.total;
-  if (a.split_items > 0) {
-    j0 = split * a.split_items;
-    j1 = j0 + a.split_items < ri.total ? j0 + a.split_items : ri.total;
-  }
+  int j0, j1;
+  split_range(a, ri.total, split, &j0, &j1);
   float qv[NPL], o[NPL];
   float ss = 0.0f;
 #pragma unroll
@@ -267,9 +284,10 @@ struct MxShared {
   uint32_t items[kMaxItems];            // item sources: 16 B units from the pool, | kWinFlag for the window
   uint32_t valid[C::kStages][4];        // bit u of valid[st][w]: ring row w + 4u holds a real item
   float tmx[4][32];                     // per-head tile max of each wavefront
-  int bump[4];                          // wavefront wants to move its reference max
+  __attribute__((aligned(16))) int bump[4];   // wavefront wants to move its reference max
   float lsum[4][32];                    // epilogue: per-head probability sums
   float rope_cs[kR];                    // (cos, sin) of t * theta_p, p < R/2
+  __attribute__((aligned(16))) float gain[kD];   // query RMSNorm gain
 };
 
 // Item j of a row as a 16-byte-unit offset (kNoItem: skip it).
@@ -481,53 +499,30 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
   typedef MxShared<KV_FMT> Sh;
   __shared__ Sh sh;
 
-  const int r = blockIdx.x, hg = blockIdx.y, split = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int pair = wave >> 1, half = wave & 1, partner = wave ^ 1;
-  const RowInfo ri = row_info(a, r);
-  const int ns = n_splits_of(a, ri.total);
-  if (split >= ns) return;
-  int j0 = 0, j1 = ri.total;
-  if (a.split_items > 0) {
-    j0 = split * a.split_items;
-    j1 = j0 + a.split_items < ri.total ? j0 + a.split_items : ri.total;
-  }
-  const int ntiles = (j1 - j0 + kRows - 1) / kRows;
-  const int head0 = hg * 64 + 32 * pair;               // first head of this pair
-  const int hl = lane & 31;                            // head (within the block) of this lane's S^T column
+  // Persistent workgroups: unit = (row, head group of 64, split), taken with a
+  // static stride so that the work of a launch does not depend on scheduling.
+  const int n_hg = a.n_heads / 64, n_sp = a.split_items > 0 ? a.max_splits : 1;
+  const int n_units = a.n_rows * n_hg * n_sp;
   constexpr int CC = kD - kR;
+  for (int i = tid; i < kD; i += 256) sh.gain[i] = a.q_gain[i];
 
-  // ---- prologue.  The query loads go first: their latency overlaps the RoPE, gain
-  // and item tables, and being older than the tile loads, waiting for them never
-  // waits for a tile.  B fragments: lane = head l%32, channels 16s + 8(l/32) .. +7.
+  // Raw query rows (bf16 bits as B fragments: lane = head l%32, channels 16s + 8(l/32)
+  // .. +7).  The next unit's rows are fetched right after the current unit's last
+  // QK, so their latency hides behind its last tile and epilogue.
   bf16x8 qf[32];
-  {
-    const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)r * a.n_heads + head0 + hl) * kD + 8 * (lane >> 5);
+  int q_row = -1, q_hg = -1;                           // rows held in qf
+  auto load_q = [&](int rr, int hh) {
+    const uint16_t* qrow =
+        (const uint16_t*)a.q + ((int64_t)rr * a.n_heads + hh * 64 + 32 * pair + (lane & 31)) * kD + 8 * (lane >> 5);
 #pragma unroll
     for (int s = 0; s < 32; ++s) qf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * s));
-  }
-  float* gain_s = (float*)&sh.pex[0][0][0];            // the exchange buffer is free until the loop
-  for (int i = tid; i < kD; i += 256) gain_s[i] = a.q_gain[i];
-  if (tid < kR / 2) {
-    float sn, cs;
-    rope_sincos((double)ri.t, tid, kR, a.base, &sn, &cs);
-    sh.rope_cs[2 * tid] = cs;
-    sh.rope_cs[2 * tid + 1] = sn;
-  }
-  const int n_tab = (j1 - j0) < kMaxItems ? (j1 - j0) : kMaxItems;
-  for (int i = tid; i < n_tab; i += 256) sh.items[i] = item_off(a, ri, r, j0 + i);
-  // a valid, finite row used as the source of loads for rows without an item: the window token at t
-  const uint8_t* dummy = (const uint8_t*)a.win + ((int64_t)ri.win_seq * a.W + ri.t % a.W) * kD * 2;
-  __syncthreads();
-  constexpr int kPrologueTiles = C::kFp8 ? 2 : 1;
-  for (int t = 0; t < kPrologueTiles; ++t) {
-    MxIssue<KV_FMT> is;
-    is.prepare(a, j0, j1, t, t, sh, dummy, t < ntiles);
-    is.all();
-  }
-
-  // ---- query: RMSNorm with gain, RoPE at t, logit scale * log2(e)
-  {
+    q_row = rr;
+    q_hg = hh;
+  };
+  // RMSNorm with gain, RoPE at t (table in sh.rope_cs), logit scale * log2(e), in place.
+  auto transform_q = [&]() {
     float ss = 0.0f;
 #pragma unroll
     for (int s = 0; s < 32; ++s) {
@@ -543,7 +538,7 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
 #pragma unroll
     for (int s = 0; s < 32; ++s) {
       const int d0 = 16 * s + 8 * (lane >> 5);
-      const f32x4 g0 = *(const f32x4*)(gain_s + d0), g1 = *(const f32x4*)(gain_s + d0 + 4);
+      const f32x4 g0 = *(const f32x4*)(sh.gain + d0), g1 = *(const f32x4*)(sh.gain + d0 + 4);
       const u32x4 w = __builtin_bit_cast(u32x4, qf[s]);
       float x[8];
 #pragma unroll
@@ -566,105 +561,143 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) qf[s][e] = (__bf16)(x[e] * a.scale_log2);
     }
+  };
+
+  constexpr int kPrologueTiles = C::kFp8 ? 2 : 1;
+  float m_force = kNoMax;                              // != kNoMax: recompute the unit with this reference
+  for (int unit = blockIdx.x; unit < n_units; unit += gridDim.x) {
+  const int r = unit / (n_hg * n_sp), hg = (unit / n_sp) % n_hg, split = unit % n_sp;
+  const RowInfo ri = row_info(a, r);
+  const int ns = n_splits_of(a, ri.total);
+  if (split >= ns) continue;
+  int j0, j1;
+  split_range(a, ri.total, split, &j0, &j1);
+  const int ntiles = (j1 - j0 + kRows - 1) / kRows;
+  const int head0 = hg * 64 + 32 * pair;               // first head of this pair
+  const int hl = lane & 31;                            // head (within the block) of this lane's S^T column
+
+  // ---- prologue.  Query loads (unless prefetched) go first: their latency overlaps
+  // the RoPE and item tables, and being older than the tile loads, waiting for them
+  // never waits for a tile.
+  if (q_row != r || q_hg != hg) load_q(r, hg);
+  if (tid < kR / 2) {
+    float sn, cs;
+    rope_sincos((double)ri.t, tid, kR, a.base, &sn, &cs);
+    sh.rope_cs[2 * tid] = cs;
+    sh.rope_cs[2 * tid + 1] = sn;
   }
+  const int n_tab = (j1 - j0) < kMaxItems ? (j1 - j0) : kMaxItems;
+  for (int i = tid; i < n_tab; i += 256) sh.items[i] = item_off(a, ri, r, j0 + i);
+  // a valid, finite row used as the source of loads for rows without an item: the window token at t
+  const uint8_t* dummy = (const uint8_t*)a.win + ((int64_t)ri.win_seq * a.W + ri.t % a.W) * kD * 2;
+  __syncthreads();
+  for (int t = 0; t < kPrologueTiles; ++t) {
+    MxIssue<KV_FMT> is;
+    is.prepare(a, j0, j1, t, t, sh, dummy, t < ntiles);
+    is.all();
+  }
+
+  transform_q();
+  q_row = -1;                                          // qf now holds transformed queries
 
   // Softmax reference: m_run is set by the first tile with a valid item (O is still
   // zero then) and never moves afterwards; probabilities relative to it stay below
   // 2^kBump, far inside fp32/bf16 range, unless a later logit exceeds it by more
-  // than kBump.  That (practically unreachable) case sets `redo` and the row is
+  // than kBump.  That (practically unreachable) case sets `redo` and the unit is
   // recomputed with the exact maximum m_true seen on the first pass, so the loop
   // never rescales O and the accumulators never leave their registers.
   constexpr float kBump = 60.0f;
   f32x16 oacc[8];
   mx_zero(oacc);
-  float m_run = kNoMax, l_part = 0.0f, m_true = kNoMax;
-  bool redo = false, second = false;
-  {
-    for (int tile = 0; tile < ntiles; ++tile) {
-      const int st = tile & 1;
-      if constexpr (C::kFp8) {
-        if (tile + 1 < ntiles) __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory");
-        else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      } else {
-        __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      }
-      __syncthreads();                                   // tile landed for every wavefront
-      const u32x4 vw = *(const u32x4*)sh.valid[st];      // (fp8: read before the stage is refilled)
-      const __bf16* tl;
-      MxIssue<KV_FMT> is;
-      if constexpr (C::kFp8) {
-        mx_convert(a, sh.ring[st], sh.valid[st], sh.items, j0 + tile * kRows, j0, ri.n_c, sh.tile);
-        __syncthreads();
-        is.prepare(a, j0, j1, tile + 2, st, sh, dummy, tile + 2 < ntiles);
-        tl = sh.tile;
-      } else {
-        is.prepare(a, j0, j1, tile + 1, st ^ 1, sh, dummy, tile + 1 < ntiles);
-        tl = (const __bf16*)sh.ring[st];
-      }
-      f32x16 s;
-      if (is.on) mx_scores(tl + 32 * half * kPitch, qf, s, [&](int u) { is.row(u); });
-      else mx_scores(tl + 32 * half * kPitch, qf, s, [](int) {});
-      float sv[16];
-      float mx = -INFINITY;
-      if ((vw[0] & vw[1] & vw[2] & vw[3] & 0xFFFFu) == 0xFFFFu) {      // every row holds an item
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          sv[v] = s[v];
-          mx = fmaxf(mx, sv[v]);
-        }
-      } else {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const bool ok = (vw[v & 3] >> (8 * half + 2 * (v >> 2) + (lane >> 5))) & 1u;
-          sv[v] = ok ? s[v] : -INFINITY;
-          mx = fmaxf(mx, sv[v]);
-        }
-      }
-      const float tmax = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const bool bump = __any(tmax > m_run + kBump);
-      bf16x8 pown[2];
-      float psum = mx_probs(sv, m_run, pown);
-      *(bf16x8*)&sh.pex[wave][lane][0] = pown[0];
-      *(bf16x8*)&sh.pex[wave][lane][1] = pown[1];
-      if (lane < 32) sh.tmx[wave][lane] = tmax;
-      if (lane == 0) sh.bump[wave] = bump;
+  float m_run = m_force, l_part = 0.0f, m_true = kNoMax;
+  bool redo = false;
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int st = tile & 1;
+    if constexpr (C::kFp8) {
+      if (tile + 1 < ntiles) __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();                                   // tile landed for every wavefront
+    const u32x4 vw = *(const u32x4*)sh.valid[st];      // (fp8: read before the stage is refilled)
+    const __bf16* tl;
+    MxIssue<KV_FMT> is;
+    if constexpr (C::kFp8) {
+      mx_convert(a, sh.ring[st], sh.valid[st], sh.items, j0 + tile * kRows, j0, ri.n_c, sh.tile);
       __syncthreads();
-      const float tmax_pair = fmaxf(tmax, sh.tmx[partner][hl]);
-      m_true = fmaxf(m_true, tmax_pair);
-      if (sh.bump[0] | sh.bump[1] | sh.bump[2] | sh.bump[3]) {   // workgroup-uniform
-        if (m_run == kNoMax) {
-          // first tile with valid items (the same tile for every head): set the reference
-          m_run = tmax_pair;
-          psum = mx_probs(sv, m_run, pown);
-          __syncthreads();                               // every wavefront has read the flags
-          *(bf16x8*)&sh.pex[wave][lane][0] = pown[0];
-          *(bf16x8*)&sh.pex[wave][lane][1] = pown[1];
-          __syncthreads();
-        } else {
-          redo = true;
-        }
+      is.prepare(a, j0, j1, tile + 2, st, sh, dummy, tile + 2 < ntiles);
+      tl = sh.tile;
+    } else {
+      is.prepare(a, j0, j1, tile + 1, st ^ 1, sh, dummy, tile + 1 < ntiles);
+      tl = (const __bf16*)sh.ring[st];
+    }
+    f32x16 s;
+    is.all();                                          // the next tile gets the whole tile period
+    mx_scores(tl + 32 * half * kPitch, qf, s, [](int) {});
+    if (tile == ntiles - 1 && unit + (int)gridDim.x < n_units) {
+      const int un = unit + gridDim.x;                 // prefetch the next unit's queries
+      load_q(un / (n_hg * n_sp), (un / n_sp) % n_hg);
+    }
+    float sv[16];
+    float mx = -INFINITY;
+    if ((vw[0] & vw[1] & vw[2] & vw[3] & 0xFFFFu) == 0xFFFFu) {      // every row holds an item
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        sv[v] = s[v];
+        mx = fmaxf(mx, sv[v]);
       }
-      l_part += psum;
-      bf16x8 ppar[2];
-      ppar[0] = *(const bf16x8*)&sh.pex[partner][lane][0];
-      ppar[1] = *(const bf16x8*)&sh.pex[partner][lane][1];
-      mx_pv(tl, half, pown, ppar, oacc);
-      if (__builtin_expect(redo && !second && tile == ntiles - 1, 0)) {   // workgroup-uniform
-        // recompute the row against the exact maximum of the first pass
-        second = true;
-        m_run = m_true;
-        l_part = 0.0f;
-        mx_zero(oacc);
-        __syncthreads();                                 // every wavefront is done with the ring
-        for (int t = 0; t < kPrologueTiles; ++t) {
-          MxIssue<KV_FMT> is2;
-          is2.prepare(a, j0, j1, t, t, sh, dummy, t < ntiles);
-          is2.all();
-        }
-        tile = -1;
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const bool ok = (vw[v & 3] >> (8 * half + 2 * (v >> 2) + (lane >> 5))) & 1u;
+        sv[v] = ok ? s[v] : -INFINITY;
+        mx = fmaxf(mx, sv[v]);
       }
     }
+    const float tmax = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const bool bump = __any(tmax > m_run + kBump);
+    bf16x8 pown[2];
+    float psum = mx_probs(sv, m_run, pown);
+    *(bf16x8*)&sh.pex[wave][lane][0] = pown[0];
+    *(bf16x8*)&sh.pex[wave][lane][1] = pown[1];
+    if (lane < 32) sh.tmx[wave][lane] = tmax;
+    if (lane == 0) sh.bump[wave] = bump;
+    __syncthreads();
+    // everything the exchange delivers, read at once
+    const i32x4 bumps = *(const i32x4*)sh.bump;
+    const float tmax_pair = fmaxf(tmax, sh.tmx[partner][hl]);
+    bf16x8 ppar[2];
+    ppar[0] = *(const bf16x8*)&sh.pex[partner][lane][0];
+    ppar[1] = *(const bf16x8*)&sh.pex[partner][lane][1];
+    m_true = fmaxf(m_true, tmax_pair);
+    if (__builtin_expect(bumps[0] | bumps[1] | bumps[2] | bumps[3], 0)) {   // workgroup-uniform
+      if (m_run == kNoMax) {
+        // first tile with valid items (the same tile for every head): set the reference
+        m_run = tmax_pair;
+        psum = mx_probs(sv, m_run, pown);
+        __syncthreads();                               // every wavefront has read the exchange
+        *(bf16x8*)&sh.pex[wave][lane][0] = pown[0];
+        *(bf16x8*)&sh.pex[wave][lane][1] = pown[1];
+        __syncthreads();
+        ppar[0] = *(const bf16x8*)&sh.pex[partner][lane][0];
+        ppar[1] = *(const bf16x8*)&sh.pex[partner][lane][1];
+      } else {
+        redo = true;
+      }
+    }
+    l_part += psum;
+    mx_pv(tl, half, pown, ppar, oacc);
   }
+
+  if (__builtin_expect(redo && m_force == kNoMax, 0)) {  // workgroup-uniform
+    // a logit overflowed the reference: recompute the unit against the exact maximum
+    m_force = m_true;
+    unit -= gridDim.x;
+    __syncthreads();                                   // every wavefront is done with the ring
+    continue;
+  }
+  m_force = kNoMax;
 
   // ---- epilogue: per-head sum over the pair's items
   const float l_own = l_part + __shfl_xor(l_part, 32, 64);
@@ -725,16 +758,31 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
         *(f32x4*)((float*)a.out + ob) = x;
       } else {
         u32x2 w;
-        w[0] = (uint32_t)f32_to_bf16_bits(x[0]) | ((uint32_t)f32_to_bf16_bits(x[1]) << 16);
-        w[1] = (uint32_t)f32_to_bf16_bits(x[2]) | ((uint32_t)f32_to_bf16_bits(x[3]) << 16);
+        w[0] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)x[0], (__bf16)x[1]});
+        w[1] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)x[2], (__bf16)x[3]});
         *(u32x2*)((uint16_t*)a.out + ob) = w;
       }
     }
+  }
+  __syncthreads();                                     // the next unit reuses the LDS
   }
 }
 
 // ======================================================================== dispatch
 int attend_mfma_max_items() { return kMaxItems; }
+
+// Compute units of the current device (one persistent attention workgroup each).
+static int cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
 
 bool attend_mfma_supported(const AttendArgs& a) {
   // item sources are 31-bit offsets in 16 B units
@@ -748,7 +796,8 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
   if (a.n_rows == 0) return hipSuccess;
   const int splits = a.split_items > 0 ? a.max_splits : 1;
   if (attend_mfma_supported(a)) {
-    dim3 grid(a.n_rows, a.n_heads / 64, splits);
+    const long units = (long)a.n_rows * (a.n_heads / 64) * splits;
+    dim3 grid((unsigned)(units < cu_count() ? units : cu_count()));
     if (a.kv.fmt == CA_FP8MIX)
       hipLaunchKernelGGL(attend_mx_kernel<CA_FP8MIX>, grid, dim3(256), 0, st, a);
     else

@@ -53,13 +53,17 @@ struct AttendArgs {
   void* out;
   int out_fmt;
   float* lse;
-  int split_items;     // 0: one split per row (direct epilogue)
-  int max_splits;
+  int split_items;     // 0: one split per row (direct epilogue); else the minimum split length
+  int split_div;       // a row of n items is split into chunks of max(split_items, ceil64(n / split_div))
+  int max_splits;      // splits per row the workspace holds (never exceeded)
   float* part_o;       // [rows, max_splits, n_heads, D]
   float* part_ml;      // [rows, max_splits, n_heads, 2]
 };
 
+// Decode split plan: chunks of at least kDecodeSplitItems items, at most
+// kDecodeMaxSplits chunks per row (a function of the row alone).
 constexpr int kDecodeSplitItems = 256;
+constexpr int kDecodeMaxSplits = 16;
 
 bool attend_mfma_supported(const AttendArgs& a);
 int attend_mfma_max_items();  // items one MFMA workgroup handles without splitting

@@ -386,3 +386,51 @@ def test_prefill_row_equals_decode_step():
     d = (out.float() - gp.out[rows].float()).abs().max().item()
     log(f"  decode vs prefill rows: max-abs {d:.3e}")
     assert d <= 8e-3
+
+
+def test_reference_overflow_recompute():
+    """Logits spread far beyond the hot loop's bound on the softmax reference (2^60
+    above the reference set by the first tile): with every head's query equal to head
+    0's and a large query gain, a list ordered by ascending logit makes a later tile
+    exceed the first tile's maximum by more than 60 (log2 units), so the workgroup
+    recomputes the unit against the exact maximum; the same list in descending order
+    never does.  CSA attention does not depend on the order of the selected list, and
+    both runs use the exact maximum as reference, so the outputs agree to fp32
+    summation order."""
+    ca, configs, layers, synth = _ca()
+    cfg = _cfg(L=4300, k=1024)
+    inp, pt, n_pool = _prefill_case(cfg, "csa")
+    inp = dict(inp)
+    inp["q"] = inp["q"][:, :1, :].expand(-1, cfg.n_h, -1).contiguous()
+    inp["g_q"] = (inp["g_q"] * 16.0).contiguous()
+    gp = layers.CSAPrefill(cfg, inp, pt.cuda(), n_pool)
+    gp.compress()
+    gp.window_append()
+    torch.cuda.synchronize()
+    rows = list(range(4290, 4298))
+    n_e = 1024
+    keys = pool_values(gp.kv, 0, n_e)                               # [n_e, D] decoded entries
+    idx_up = np.full((cfg.L, cfg.k), -1, np.int32)
+    idx_dn = np.full((cfg.L, cfg.k), -1, np.int32)
+    cnt = np.zeros(cfg.L, np.int32)
+    g_q = f64(inp["g_q"])
+    q0 = f64(inp["q"][:, 0, :])
+    for r in rows:
+        qn = oracle.rope(oracle.rmsnorm(q0[r], g_q, cfg.eps), cfg.R, r, cfg.rope_base)
+        logit2 = keys @ qn / math.sqrt(cfg.D) * math.log2(math.e)
+        order = np.argsort(logit2, kind="stable").astype(np.int32)
+        assert logit2[order[64:]].max() - logit2[order[:64]].max() > 60.0   # the ascending list overflows
+        idx_up[r] = order
+        idx_dn[r] = order[::-1]
+        cnt[r] = n_e
+    outs = []
+    for idx in (idx_up, idx_dn):
+        out = torch.empty(cfg.L, cfg.n_h, cfg.D, dtype=torch.bfloat16, device="cuda")
+        ca.csa_attend_prefill(gp.ap, inp["q"], inp["g_q"], gp.kv, 0, torch.from_numpy(idx).cuda(),
+                              torch.from_numpy(cnt).cuda(), cfg.m, gp.window, inp["sink"], out)
+        torch.cuda.synchronize()
+        outs.append(f64(out)[rows])
+    assert np.isfinite(outs[0]).all() and np.isfinite(outs[1]).all()
+    err = np.abs(outs[0] - outs[1]).max()
+    log(f"  overflow recompute vs no recompute: max-abs {err:.3e}")
+    assert err <= 1e-2
