@@ -128,7 +128,8 @@ __device__ __forceinline__ void load_key_group(const CacheView& cv, const int* p
 template <int QPW>
 __global__ void __launch_bounds__(256) index_scores_fp8_kernel(CacheView cv, int m, int q_fmt, const void* qI,
                                                                const float* w, const int32_t* pos, int seq_fixed,
-                                                               int n_rows, float* scores, int64_t stride) {
+                                                               int n_rows, float* scores, int64_t stride,
+                                                               uint32_t* clear, int clear_words) {
   constexpr int nI = 8, cI = 64;
   __shared__ __attribute__((aligned(16))) uint8_t qcodes[32 * cI];  // A operand rows: (query, head)
   __shared__ float wq[32];                                          // w * query scale per row
@@ -145,6 +146,9 @@ __global__ void __launch_bounds__(256) index_scores_fp8_kernel(CacheView cv, int
     ne[qq] = r < n_rows ? (t / m < stride ? t / m : stride) : 0;
     ne_max = ne[qq] > ne_max ? ne[qq] : ne_max;
   }
+  if (clear != nullptr && blockIdx.y == 0)             // the long top-k's per-row counters (read by later launches)
+    for (int qq = 0; qq < QPW && r0 + qq < n_rows; ++qq)
+      for (int i = threadIdx.x; i < clear_words; i += 256) clear[(int64_t)(r0 + qq) * clear_words + i] = 0u;
   const int64_t k0 = (int64_t)blockIdx.y * kScoreChunk;
   if (k0 >= ne_max) return;                            // uniform over the block
   const int64_t k1 = (k0 + kScoreChunk < ne_max) ? k0 + kScoreChunk : ne_max;
@@ -334,20 +338,23 @@ __global__ void __launch_bounds__(kTopkThreads) topk_rows_kernel(const float* sc
 // context: 262,144 per row at 2^20 tokens) are selected in three passes that
 // spread the scan over many workgroups:
 //   1. histogram of the top 12 key bits per row (LDS histogram per chunk,
-//      nonzero bins added to the row's global histogram: integer atomics, so
-//      the counts are order independent);
-//   2. every chunk finds the bin b* holding the k-th largest key from the row
-//      histogram and appends its keys with bin >= b* (about k plus one bin's
-//      population) to a per-row candidate list;
-//   3. one workgroup per row selects exactly among the candidates (radix select
-//      on the full key, then the lowest indices among keys equal to the
-//      threshold) and sorts the kept indices ascending.
+//      nonzero bins added to the row's global histogram with integer atomics, so
+//      the counts are order independent), then one workgroup per row finds the bin
+//      b* holding the k-th largest key and the number of keys above it;
+//   2. every chunk appends its keys with bin >= b* to a per-row candidate list;
+//   3. one workgroup per row finishes the select among the candidates: two 10-bit
+//      radix passes over the keys in bin b* give the exact threshold key T, then
+//      the kept indices (every key above T, and the lowest-indexed keys equal to
+//      T) are set in LDS bitmaps that are read out in index order.
 // The candidate list is filled in arbitrary order, but pass 3 depends only on
 // the set of (key, index) pairs, so the result is deterministic.
 constexpr int kChunk = 4096;
 constexpr int kResolveThreads = 1024;
-constexpr int kResolveLds = 8192;     // candidates held in LDS (more spill to the global list)
-constexpr int kSortMax = 8192;        // largest k the resolve pass sorts in LDS
+constexpr int kSortMax = 8192;        // largest k of the long path
+constexpr int kMetaWords = 4;         // per row: candidates appended, (spare), b*, keys above b*
+constexpr int kRowWords = kHistBins + kMetaWords;   // per-row state: histogram, then the counters
+constexpr int kRegCand = 4;            // candidates per resolve thread held in registers
+constexpr int kBitmapLdsWords = 16384;  // two LDS bitmaps of rows up to 262,144 keys (larger rows: workspace)
 
 __global__ void topk_zero_kernel(uint32_t* p, int64_t n) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -360,33 +367,13 @@ __device__ __forceinline__ int64_t row_len(const int32_t* pos, int r, int m, int
   return n < stride ? n : stride;
 }
 
-__global__ void __launch_bounds__(256) topk_hist_kernel(const float* scores, int64_t stride, const int32_t* pos,
-                                                        int m, int k, uint32_t* hist) {
-  __shared__ uint32_t h[kHistBins];
-  const int r = blockIdx.x;
-  const int64_t n = row_len(pos, r, m, stride);
-  const int64_t c0 = (int64_t)blockIdx.y * kChunk;
-  if (n <= k || c0 >= n) return;
-  for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) h[i] = 0;
-  __syncthreads();
-  const float* row = scores + (int64_t)r * stride;
-  const int64_t c1 = c0 + kChunk < n ? c0 + kChunk : n;
-  for (int64_t s = c0 + threadIdx.x; s < c1; s += blockDim.x) atomicAdd(&h[order_key(row[s]) >> 20], 1u);
-  __syncthreads();
-  uint32_t* g = hist + (int64_t)r * kHistBins;
-  for (int i = threadIdx.x; i < kHistBins; i += blockDim.x)
-    if (h[i]) atomicAdd(&g[i], h[i]);
-}
-
-// Bin holding the k-th largest key of a row, from its histogram (block of 256
-// threads): the histogram is staged in LDS, each thread sums 16 bins, wave 0
-// finds the thread whose bins hold the k-th key by a suffix scan, and that
+// Bin of a 256-thread block's histogram hb[kHistBins] (in LDS) holding the k-th
+// largest key, and the number of keys in higher bins: each thread sums 16 bins,
+// wave 0 finds the thread whose bins hold the k-th key by a suffix scan, and that
 // thread walks its 16 bins from the top.
-__device__ uint32_t threshold_bin(const uint32_t* g, int k, uint32_t* hb, uint32_t* part) {
-  __shared__ uint32_t sel_owner, sel_above, sel_bin;
+__device__ void threshold_bin(const uint32_t* hb, int k, uint32_t* part, uint32_t* bin, uint32_t* above) {
+  __shared__ uint32_t sel_owner, sel_above, sel_bin, sel_cum;
   const int tid = threadIdx.x;
-  for (int i = tid; i < kHistBins; i += 256) hb[i] = g[i];
-  __syncthreads();
   uint32_t sum = 0;
   for (int i = 0; i < 16; ++i) sum += hb[16 * tid + i];
   part[tid] = sum;
@@ -416,26 +403,64 @@ __device__ uint32_t threshold_bin(const uint32_t* g, int k, uint32_t* hb, uint32
     for (int b = 16 * tid + 15; b >= 16 * tid; --b) {
       if (cum + hb[b] >= (uint32_t)k) {
         sel_bin = (uint32_t)b;
+        sel_cum = cum;
         break;
       }
       cum += hb[b];
     }
   }
   __syncthreads();
-  return sel_bin;
+  *bin = sel_bin;
+  *above = sel_cum;
+}
+
+__global__ void __launch_bounds__(256) topk_hist_kernel(const float* scores, int64_t stride, const int32_t* pos,
+                                                        int m, int k, uint32_t* state) {
+  __shared__ uint32_t h[kHistBins];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int64_t n = row_len(pos, r, m, stride);
+  const int64_t c0 = (int64_t)blockIdx.y * kChunk;
+  if (n <= k || c0 >= n) return;
+  for (int i = tid; i < kHistBins; i += blockDim.x) h[i] = 0;
+  __syncthreads();
+  const float* row = scores + (int64_t)r * stride;
+  const int64_t c1 = c0 + kChunk < n ? c0 + kChunk : n;
+  for (int64_t s = c0 + tid; s < c1; s += blockDim.x) atomicAdd(&h[order_key(row[s]) >> 20], 1u);
+  __syncthreads();
+  uint32_t* g = state + (int64_t)r * kRowWords;
+  for (int i = tid; i < kHistBins; i += blockDim.x)
+    if (h[i]) atomicAdd(&g[i], h[i]);
+}
+
+// One workgroup per row: the threshold bin b* and the count of keys above it.
+__global__ void __launch_bounds__(256) topk_threshold_kernel(const int32_t* pos, int m, int k, int64_t stride,
+                                                             uint32_t* state) {
+  __shared__ uint32_t h[kHistBins];
+  __shared__ uint32_t part[256];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  if (row_len(pos, r, m, stride) <= k) return;
+  uint32_t* g = state + (int64_t)r * kRowWords;
+  for (int i = tid; i < kHistBins; i += blockDim.x) h[i] = g[i];
+  __syncthreads();
+  uint32_t bin, above;
+  threshold_bin(h, k, part, &bin, &above);
+  if (tid == 0) {
+    g[kHistBins + 2] = bin;
+    g[kHistBins + 3] = above;
+  }
 }
 
 __global__ void __launch_bounds__(256) topk_gather_kernel(const float* scores, int64_t stride, const int32_t* pos,
-                                                          int m, int k, const uint32_t* hist, uint32_t* cand_n,
-                                                          uint32_t* cand_key, uint32_t* cand_idx) {
-  __shared__ uint32_t part[256];
-  __shared__ uint32_t hb[kHistBins];
+                                                          int m, int k, uint32_t* state, uint32_t* cand_key,
+                                                          uint32_t* cand_idx) {
+  __shared__ uint32_t part[4];
   __shared__ uint32_t base_s;
   const int r = blockIdx.x, tid = threadIdx.x;
   const int64_t n = row_len(pos, r, m, stride);
   const int64_t c0 = (int64_t)blockIdx.y * kChunk;
   if (n <= k || c0 >= n) return;
-  const uint32_t bstar = threshold_bin(hist + (int64_t)r * kHistBins, k, hb, part);
+  uint32_t* meta = state + (int64_t)r * kRowWords + kHistBins;
+  const uint32_t bstar = meta[2];
   const float* row = scores + (int64_t)r * stride;
   // each thread owns 16 consecutive keys of the chunk
   constexpr int kPer = kChunk / 256;
@@ -455,7 +480,6 @@ __global__ void __launch_bounds__(256) topk_gather_kernel(const float* scores, i
     uint32_t v = __shfl_up(incl, o, 64);
     if (lane >= o) incl += v;
   }
-  __syncthreads();
   if (lane == 63) part[wave] = incl;
   __syncthreads();
   uint32_t before = incl - mine, total = 0;
@@ -463,7 +487,7 @@ __global__ void __launch_bounds__(256) topk_gather_kernel(const float* scores, i
     before += w < wave ? part[w] : 0u;
     total += part[w];
   }
-  if (tid == 0) base_s = total ? atomicAdd(&cand_n[r], total) : 0u;
+  if (tid == 0) base_s = total ? atomicAdd(&meta[0], total) : 0u;
   __syncthreads();
   uint32_t o = base_s + before;
 #pragma unroll
@@ -477,40 +501,51 @@ __global__ void __launch_bounds__(256) topk_gather_kernel(const float* scores, i
   }
 }
 
-struct ResolveShared {
-  uint32_t key[kResolveLds];
-  uint32_t idx[kResolveLds];
-  uint32_t hist[256];
-  uint32_t wsum[kResolveThreads / 64];
-  uint32_t sel_digit, sel_krem, n_eq, n_out;
-};
-
-// In-LDS bitonic sort (ascending) of n_pow2 32-bit values.
-__device__ void bitonic_sort(uint32_t* v, int n_pow2) {
-  for (int size = 2; size <= n_pow2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = threadIdx.x; i < n_pow2 / 2; i += blockDim.x) {
-        int lo = 2 * i - (i & (stride - 1));
-        int hi = lo + stride;
-        bool up = (lo & size) == 0;
-        uint32_t a = v[lo], b = v[hi];
-        if ((a > b) == up) {
-          v[lo] = b;
-          v[hi] = a;
-        }
-      }
-      __syncthreads();
-    }
+// Exclusive prefix sum over the block (1024 threads) and the block total.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t incl = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
   }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  uint32_t before = incl - v, tot = 0;
+  for (int w = 0; w < kResolveThreads / 64; ++w) {
+    before += w < wave ? wsum[w] : 0u;
+    tot += wsum[w];
+  }
+  __syncthreads();
+  *total = tot;
+  return before;
+}
+
+// Digit d (0..1023) of a 1024-bin histogram (one bin per thread) holding the
+// need-th largest key, and the count of keys in higher digits.
+__device__ __forceinline__ void select_digit(uint32_t c, uint32_t need, uint32_t* wsum, uint32_t* sel) {
+  // suffix sum: count of keys in digits >= mine = total - (exclusive prefix)
+  uint32_t total;
+  const uint32_t before = block_excl_scan(c, wsum, &total);
+  const uint32_t ge = total - before, gt = ge - c;
+  if (gt < need && ge >= need) {
+    sel[0] = threadIdx.x;
+    sel[1] = gt;
+  }
+  __syncthreads();
 }
 
 __global__ void __launch_bounds__(kResolveThreads) topk_resolve_kernel(const float* scores, int64_t stride,
                                                                        const int32_t* pos, int m, int k,
-                                                                       const uint32_t* cand_n,
+                                                                       const uint32_t* state,
                                                                        const uint32_t* cand_key,
-                                                                       const uint32_t* cand_idx, int32_t* out_idx,
-                                                                       int32_t* out_cnt, float* out_score) {
-  __shared__ ResolveShared sh;
+                                                                       const uint32_t* cand_idx, uint32_t* bm_ws,
+                                                                       int32_t* out_idx, int32_t* out_cnt,
+                                                                       float* out_score) {
+  __shared__ uint32_t hist[1024];
+  __shared__ uint32_t wsum[kResolveThreads / 64];
+  __shared__ uint32_t sel[2];
+  __shared__ uint32_t bm_lds[2 * kBitmapLdsWords];
   const int r = blockIdx.x, tid = threadIdx.x;
   const int64_t n = row_len(pos, r, m, stride);
   const float* row = scores + (int64_t)r * stride;
@@ -524,113 +559,90 @@ __global__ void __launch_bounds__(kResolveThreads) topk_resolve_kernel(const flo
     if (tid == 0) out_cnt[r] = (int32_t)n;
     return;
   }
-  const uint32_t nc = cand_n[r];
-  const bool in_lds = nc <= (uint32_t)kResolveLds;
+  const uint32_t* meta = state + (int64_t)r * kRowWords + kHistBins;
+  const uint32_t nc = meta[0], bstar = meta[2], above = meta[3];
   const uint32_t* gk = cand_key + (int64_t)r * stride;
   const uint32_t* gi = cand_idx + (int64_t)r * stride;
-  if (in_lds)
-    for (uint32_t i = tid; i < nc; i += blockDim.x) {
-      sh.key[i] = gk[i];
-      sh.idx[i] = gi[i];
-    }
-  // radix select of the k-th largest key among the candidates
-  uint32_t prefix = 0, krem = (uint32_t)k;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
-    for (int i = tid; i < 256; i += blockDim.x) sh.hist[i] = 0;
+  // the first kRegCand * kResolveThreads candidates stay in registers for all three passes over them
+  uint32_t rk[kRegCand], ri[kRegCand];
+#pragma unroll
+  for (int j = 0; j < kRegCand; ++j) {
+    const uint32_t i = tid + j * kResolveThreads;
+    rk[j] = i < nc ? gk[i] : 0u;
+    ri[j] = i < nc ? gi[i] : 0u;
+  }
+  // two 10-bit radix passes over the candidates in bin b*: T and the count to take equal to T
+  uint32_t need = (uint32_t)k - above, prefix = bstar;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int shift = pass == 0 ? 10 : 0;
+    hist[tid] = 0;
     __syncthreads();
-    for (uint32_t i = tid; i < nc; i += blockDim.x) {
-      uint32_t key = in_lds ? sh.key[i] : gk[i];
-      if ((key & hi_mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (tid < 64) {
-      uint32_t c[4] = {sh.hist[4 * tid], sh.hist[4 * tid + 1], sh.hist[4 * tid + 2], sh.hist[4 * tid + 3]};
-      uint32_t lsum = c[0] + c[1] + c[2] + c[3];
-      uint32_t incl = lsum;
-      for (int o = 1; o < 64; o <<= 1) {
-        uint32_t v = __shfl_down(incl, o, 64);
-        if (tid + o < 64) incl += v;
-      }
-      uint32_t cum = incl - lsum;
-      for (int d = 3; d >= 0; --d) {
-        uint32_t nxt = cum + c[d];
-        if (cum < krem && nxt >= krem) {
-          sh.sel_digit = 4 * tid + d;
-          sh.sel_krem = krem - cum;
-        }
-        cum = nxt;
-      }
+#pragma unroll
+    for (int j = 0; j < kRegCand; ++j)
+      if (tid + j * kResolveThreads < nc && (rk[j] >> (shift + 10)) == prefix)
+        atomicAdd(&hist[(rk[j] >> shift) & 1023u], 1u);
+    for (uint32_t i = tid + kRegCand * kResolveThreads; i < nc; i += blockDim.x) {
+      const uint32_t key = gk[i];
+      if ((key >> (shift + 10)) == prefix) atomicAdd(&hist[(key >> shift) & 1023u], 1u);
     }
     __syncthreads();
-    prefix |= sh.sel_digit << shift;
-    krem = sh.sel_krem;
+    select_digit(hist[tid], need, wsum, sel);
+    prefix = (prefix << 10) | sel[0];
+    need -= sel[1];
     __syncthreads();
   }
-  const uint32_t T = prefix, need_eq = krem;
-  // kept set: every candidate above T, then the need_eq lowest indices equal to T.
-  // sh.idx is reused as the output buffer once the candidates are consumed from wherever they live.
-  __shared__ uint32_t outbuf[kSortMax];
-  __shared__ uint32_t eqbuf[kSortMax];
-  if (tid == 0) {
-    sh.n_eq = 0;
-    sh.n_out = 0;
-  }
+  const uint32_t T = prefix, need_eq = need;           // keep every key > T and the need_eq lowest indices == T
+  // bitmaps of the row's indices: kept (keys > T, then the chosen ties) and equal to T
+  const int64_t words = (n + 31) / 32;
+  uint32_t* bm = words <= kBitmapLdsWords ? bm_lds : bm_ws + (int64_t)r * 2 * ((stride + 31) / 32);
+  uint32_t* keep = bm;
+  uint32_t* eq = bm + words;
+  for (int64_t i = tid; i < 2 * words; i += blockDim.x) bm[i] = 0;
   __syncthreads();
-  for (uint32_t i = tid; i < nc; i += blockDim.x) {
-    uint32_t key = in_lds ? sh.key[i] : gk[i];
-    uint32_t id = in_lds ? sh.idx[i] : gi[i];
-    if (key > T) {
-      uint32_t o = atomicAdd(&sh.n_out, 1u);
-      if (o < (uint32_t)kSortMax) outbuf[o] = id;
-    } else if (key == T) {
-      uint32_t o = atomicAdd(&sh.n_eq, 1u);
-      if (o < (uint32_t)kSortMax) eqbuf[o] = id;
+#pragma unroll
+  for (int j = 0; j < kRegCand; ++j)
+    if (tid + j * kResolveThreads < nc && rk[j] >= T)
+      atomicOr(rk[j] > T ? &keep[ri[j] >> 5] : &eq[ri[j] >> 5], 1u << (ri[j] & 31));
+  for (uint32_t i = tid + kRegCand * kResolveThreads; i < nc; i += blockDim.x) {
+    const uint32_t key = gk[i];
+    if (key >= T) {
+      const uint32_t id = gi[i];
+      atomicOr(key > T ? &keep[id >> 5] : &eq[id >> 5], 1u << (id & 31));
     }
   }
   __syncthreads();
-  const uint32_t n_gt = sh.n_out, n_eq = sh.n_eq;
-  if (n_eq <= (uint32_t)kSortMax) {
-    int p2 = 1;
-    while (p2 < (int)n_eq) p2 <<= 1;
-    for (int i = (int)n_eq + tid; i < p2; i += blockDim.x) eqbuf[i] = 0xFFFFFFFFu;
-    __syncthreads();
-    bitonic_sort(eqbuf, p2);
-    for (uint32_t j = tid; j < need_eq; j += blockDim.x) outbuf[n_gt + j] = eqbuf[j];
-  } else {
-    // pathological tie count: take the need_eq smallest equal indices one at a time
-    __shared__ uint32_t last, best;
-    if (tid == 0) last = 0xFFFFFFFFu;
-    __syncthreads();
-    for (uint32_t j = 0; j < need_eq; ++j) {
-      if (tid == 0) best = 0xFFFFFFFFu;
-      __syncthreads();
-      uint32_t mine = 0xFFFFFFFFu;
-      for (uint32_t i = tid; i < nc; i += blockDim.x) {
-        uint32_t key = in_lds ? sh.key[i] : gk[i];
-        uint32_t id = in_lds ? sh.idx[i] : gi[i];
-        if (key == T && (last == 0xFFFFFFFFu || id > last) && id < mine) mine = id;
-      }
-      atomicMin(&best, mine);
-      __syncthreads();
-      if (tid == 0) {
-        outbuf[n_gt + j] = best;
-        last = best;
-      }
-      __syncthreads();
+  // each thread owns a contiguous run of bitmap words; ties taken in index order
+  const int64_t per = (words + kResolveThreads - 1) / kResolveThreads;
+  const int64_t w0 = (int64_t)tid * per, w1 = w0 + per < words ? w0 + per : words;
+  uint32_t cnt = 0;
+  for (int64_t w = w0; w < w1; ++w) cnt += __popc(eq[w]);
+  uint32_t tot;
+  uint32_t rank = block_excl_scan(cnt, wsum, &tot);
+  for (int64_t w = w0; w < w1 && rank < need_eq; ++w) {
+    uint32_t e = eq[w];
+    while (e && rank < need_eq) {
+      const uint32_t b = e & (0u - e);
+      keep[w] |= b;
+      e ^= b;
+      ++rank;
     }
   }
   __syncthreads();
-  int p2 = 1;
-  while (p2 < k) p2 <<= 1;
-  for (int i = k + tid; i < p2; i += blockDim.x) outbuf[i] = 0xFFFFFFFFu;
-  __syncthreads();
-  bitonic_sort(outbuf, p2);
-  for (int j = tid; j < k; j += blockDim.x) {
-    uint32_t id = outbuf[j];
-    oi[j] = (int32_t)id;
-    if (os) os[j] = row[id];
+  cnt = 0;
+  for (int64_t w = w0; w < w1; ++w) cnt += __popc(keep[w]);
+  uint32_t o = block_excl_scan(cnt, wsum, &tot);
+  for (int64_t w = w0; w < w1; ++w) {
+    uint32_t e = keep[w];
+    while (e) {
+      const int b = __ffs(e) - 1;
+      const uint32_t id = (uint32_t)(w * 32 + b);
+      if (o < (uint32_t)k) {
+        oi[o] = (int32_t)id;
+        if (os) os[o] = row[id];
+      }
+      ++o;
+      e &= e - 1;
+    }
   }
   if (tid == 0) out_cnt[r] = k;
 }
@@ -640,24 +652,25 @@ hipError_t launch_index_scores(const CacheView& cv, const ca_index_params& p, co
                                const int32_t* pos, int seq_fixed, int n_rows, int64_t max_pos, float* scores,
                                int64_t stride, void* ws_long, hipStream_t st) {
   if (n_rows == 0) return hipSuccess;
-  int64_t max_ne = max_pos / p.ratio;
-  if (max_ne == 0) return hipSuccess;
+  const int64_t max_ne = max_pos / p.ratio;
   const bool long_rows = ws_long != nullptr && topk_use_long(stride, p.k);
-  uint32_t* hist = long_rows ? (uint32_t*)ws_long : nullptr;
-  if (long_rows) {  // clear the histograms and candidate counters of the multi-workgroup top-k
-    const int64_t nz = (int64_t)n_rows * (kHistBins + 1);
-    hipLaunchKernelGGL(topk_zero_kernel, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, st, hist, nz);
+  uint32_t* state = long_rows ? (uint32_t*)ws_long : nullptr;   // per-row histograms and counters
+  const bool fp8 = max_ne > 0 && cv.fmt == CA_E4M3 && p.n_heads == 8 && p.dim == 64 && cv.page_shift >= 4;
+  if (long_rows && !fp8) {  // (the fp8 scoring kernel clears them itself)
+    const int64_t nz = (int64_t)n_rows * kRowWords;
+    hipLaunchKernelGGL(topk_zero_kernel, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, st, state, nz);
   }
-  if (cv.fmt == CA_E4M3 && p.n_heads == 8 && p.dim == 64 && cv.page_shift >= 4) {
+  if (max_ne == 0) return hipGetLastError();   // no entries yet: nothing to score
+  if (fp8) {
     const int64_t chunks = (max_ne + kScoreChunk - 1) / kScoreChunk;
     if (seq_fixed >= 0) {
       dim3 grid((unsigned)((n_rows + 3) / 4), (unsigned)chunks);
       hipLaunchKernelGGL(index_scores_fp8_kernel<4>, grid, dim3(256), 0, st, cv, p.ratio, p.q_format, qI, w, pos,
-                         seq_fixed, n_rows, scores, stride);
+                         seq_fixed, n_rows, scores, stride, state, kRowWords);
     } else {
       dim3 grid((unsigned)n_rows, (unsigned)chunks);
       hipLaunchKernelGGL(index_scores_fp8_kernel<1>, grid, dim3(256), 0, st, cv, p.ratio, p.q_format, qI, w, pos,
-                         seq_fixed, n_rows, scores, stride);
+                         seq_fixed, n_rows, scores, stride, state, kRowWords);
     }
   } else {
     dim3 grid((unsigned)n_rows, (unsigned)((max_ne + 255) / 256));
@@ -665,16 +678,21 @@ hipError_t launch_index_scores(const CacheView& cv, const ca_index_params& p, co
     hipLaunchKernelGGL(index_scores_generic_kernel, grid, dim3(256), sm, st, cv, p.n_heads, p.dim, p.ratio,
                        p.q_format, qI, w, pos, seq_fixed, scores, stride);
   }
-  if (hist != nullptr) {  // scores written without a fused histogram: count them now
+  if (state != nullptr) {  // histogram of the scores for the long top-k
     const unsigned chunks = (unsigned)((stride + kChunk - 1) / kChunk);
     hipLaunchKernelGGL(topk_hist_kernel, dim3(n_rows, chunks), dim3(256), 0, st, scores, stride, pos, p.ratio, p.k,
-                       hist);
+                       state);
   }
   return hipGetLastError();
 }
 
+// [rows][kHistBins + kMetaWords] histogram and counters, candidate keys and
+// indices [rows][stride] each, and [rows][2][stride/32] bitmaps for rows too long
+// for the LDS bitmaps.
 size_t topk_long_workspace(int n_rows, int64_t stride) {
-  return (size_t)n_rows * kHistBins * 4 + (size_t)n_rows * 4 + 2 * (size_t)n_rows * stride * 4 + 256;
+  const size_t words = (size_t)(stride + 31) / 32;
+  return (size_t)n_rows * kRowWords * 4 + 2 * (size_t)n_rows * stride * 4 +
+         2 * (size_t)n_rows * words * 4 + 256;
 }
 
 bool topk_use_long(int64_t stride, int k) { return stride > kTopkLdsKeys && k <= kSortMax; }
@@ -683,16 +701,17 @@ hipError_t launch_topk(const float* scores, int64_t stride, const int32_t* pos, 
                        int32_t* out_idx, int32_t* out_cnt, float* out_score, void* ws_long, hipStream_t st) {
   if (n_rows == 0) return hipSuccess;
   if (ws_long != nullptr && topk_use_long(stride, k)) {
-    uint32_t* hist = (uint32_t*)ws_long;
-    uint32_t* cand_n = hist + (int64_t)n_rows * kHistBins;
-    uint32_t* cand_key = cand_n + n_rows;
+    uint32_t* state = (uint32_t*)ws_long;
+    uint32_t* cand_key = state + (int64_t)n_rows * kRowWords;
     uint32_t* cand_idx = cand_key + (int64_t)n_rows * stride;
-    // the histogram was filled by the scoring launch (see launch_index_scores)
+    uint32_t* bm = cand_idx + (int64_t)n_rows * stride;
+    // the histogram was made by the scoring launch (see launch_index_scores)
+    hipLaunchKernelGGL(topk_threshold_kernel, dim3(n_rows), dim3(256), 0, st, pos, m, k, stride, state);
     const unsigned chunks = (unsigned)((stride + kChunk - 1) / kChunk);
-    hipLaunchKernelGGL(topk_gather_kernel, dim3(n_rows, chunks), dim3(256), 0, st, scores, stride, pos, m, k, hist,
-                       cand_n, cand_key, cand_idx);
+    hipLaunchKernelGGL(topk_gather_kernel, dim3(n_rows, chunks), dim3(256), 0, st, scores, stride, pos, m, k, state,
+                       cand_key, cand_idx);
     hipLaunchKernelGGL(topk_resolve_kernel, dim3(n_rows), dim3(kResolveThreads), 0, st, scores, stride, pos, m, k,
-                       cand_n, cand_key, cand_idx, out_idx, out_cnt, out_score);
+                       state, cand_key, cand_idx, bm, out_idx, out_cnt, out_score);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(topk_rows_kernel, dim3(n_rows), dim3(kTopkThreads), 0, st, scores, stride,
