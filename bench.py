@@ -34,16 +34,18 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 WORKLOADS = {"decode_1m": 5, "decode_mixed": 4, "prefill_csa_32k": 2, "prefill_hca_128k": 3, "tiny": 1}
-KERNEL_SOURCES = ["compress.hip", "indexer.hip", "attend.hip", "api.hip", "common.h", "kernels.h"]
+# sources that define each timed kernel (its counter readings go stale when they change)
+KERNEL_SOURCES = {"attend_mx_kernel": ["attend.hip", "common.h", "kernels.h"],
+                  "index_scores_fp8_kernel": ["indexer.hip", "common.h", "kernels.h"]}
 
 
 def progress(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(symbol: str) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[symbol.split("<")[0]]:
         with open(os.path.join(ROOT, "long_context_attention_17_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -99,6 +101,31 @@ class StageTimer:
 
     def means_ms(self):
         return {k: sum(s.elapsed_time(e) for s, e in v) / len(v) for k, v in self.pairs.items()}
+
+
+def time_kernels(run, kernels, reps):
+    """Average launch duration (ms) of library kernels, from the HIP events that the library
+    records around each eager launch on the launch stream (ca_timer_*).  The timed passes are
+    queued behind a GPU spin so that their kernels run back to back, as in the graph replays;
+    `queued` reports whether the spin outlasted the host's enqueueing."""
+    from long_context_attention_17_amd import binding as ca
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    run(0)
+    host_s = time.perf_counter() - h0                  # host enqueue time of one pass
+    torch.cuda.synchronize()
+    ca.timer_start(list(kernels.values()), max_launches=8 * reps)
+    try:
+        torch.cuda._sleep(int((2.0 * reps * host_s + 0.005) * 2.4e9))
+        spin_end = torch.cuda.Event()
+        spin_end.record()
+        for i in range(reps):
+            run(i)
+        queued = not spin_end.query()
+        raw = {name: ca.timer_read(k) for name, k in kernels.items()}
+    finally:
+        ca.timer_stop()
+    return {name: (ms / n if n else float("nan"), n / reps) for name, (ms, n) in raw.items()}, queued
 
 
 def replicate_decode_layer(dl, n):
@@ -201,20 +228,24 @@ def bench_decode(cfg, steps, warmup, replicas, args):
     pos = [int(x) for x in ctx.tolist()]
     work = decode_work(cfg, pos)
     value = cfg.B / (ms_step / 1e3)
-    # dominant stage and its roofline
-    roof_of = {
-        "csa_index_topk": ("hbm", work["index_bytes"], "GB/s"),
-        "csa_attend": ("mfma", work["csa_flops"], "TFLOP/s"),
-        "hca_attend": ("mfma", work["hca_flops"], "TFLOP/s"),
+    # per-kernel launch durations and the dominant kernel's roofline
+    from long_context_attention_17_amd import binding as ca
+    progress("kernel timing")
+    kt, queued = time_kernels(step, {"csa_attend": ca.TIMED_CSA_ATTEND, "hca_attend": ca.TIMED_HCA_ATTEND,
+                                     "index_scores": ca.TIMED_INDEX_SCORES}, max(steps, 20))
+    fmt = 2 if cfg.kv == "fp8mix" else 1
+    roof_of = {   # algorithmic work of one launch (the launch covers the whole batch)
+        "index_scores": ("hbm", work["index_bytes"], f"index_scores_fp8_kernel<1>"),
+        "csa_attend": ("mfma", work["csa_flops"], f"attend_mx_kernel<{fmt}, 0>"),
+        "hca_attend": ("mfma", work["hca_flops"], f"attend_mx_kernel<{fmt}, 1>"),
     }
-    dom = max(roof_of, key=lambda k: st[k])
-    bound, units, unit = roof_of[dom]
+    dom = max(roof_of, key=lambda k: kt[k][0] * kt[k][1])
+    bound, units, symbol = roof_of[dom]
+    launch_ms = kt[dom][0]
     if bound == "hbm":
-        achieved = units / (st[dom] / 1e3) / 1e9
-        peak = PEAK_HBM_GBS
+        achieved, peak, unit = units / (launch_ms / 1e3) / 1e9, PEAK_HBM_GBS, "GB/s"
     else:
-        achieved = units / (st[dom] / 1e3) / 1e12
-        peak = PEAK_BF16_TFLOPS
+        achieved, peak, unit = units / (launch_ms / 1e3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
     step_bytes = work["index_bytes"] + work["csa_bytes"] + work["hca_bytes"]
     extra = {
         "stages_ms": {k: round(v, 5) for k, v in st.items()},
@@ -225,16 +256,20 @@ def bench_decode(cfg, steps, warmup, replicas, args):
             "csa_attend": {"bound": "mfma", "achieved_TFLOPs": round(work["csa_flops"] / st["csa_attend"] / 1e9, 2)},
             "hca_attend": {"bound": "mfma", "achieved_TFLOPs": round(work["hca_flops"] / st["hca_attend"] / 1e9, 2)},
         },
+        "kernel_launch_ms": {k: round(v[0], 5) for k, v in kt.items()},
+        "kernel_timing_queued": queued,
         "wall_s_timed": round(wall, 4),
         "timing": "whole step: HIP-graph replays (one graph per cache replica); stages: per-stage graphs "
-                  "replayed back to back between HIP events",
+                  "replayed back to back between HIP events; kernels: HIP events recorded by the library "
+                  "around each eager launch on its stream",
     }
     config = {"workload": f"{cfg.name}: decode step of one CSA + one HCA layer, batch {cfg.B}, "
                           f"context {cfg.ctx_lo}-{cfg.ctx_hi}, {cfg.n_h} heads, D={cfg.D}, kv {cfg.kv}, "
                           f"k={cfg.k}, window {cfg.n_win}, m={cfg.m}, m'={cfg.m_hca}",
               "batch": cfg.B, "context": [min(pos), max(pos)], "replicas": replicas}
-    roof = {"kernel": dom, "bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 4)}
+    roof = {"kernel": symbol, "stage": dom, "bound": bound, "achieved": round(achieved, 3), "peak": peak,
+            "unit": unit, "frac": round(achieved / peak, 4), "launch_ms": round(launch_ms, 5),
+            "work_per_launch": units}
     return value, ms_step, config, roof, extra, (ctx, layer_objs)
 
 
@@ -278,14 +313,26 @@ def bench_prefill(cfg, steps, warmup, replicas, args):
     st = timer.means_ms()
     work = prefill_work(cfg)
     value = cfg.L / (ms_step / 1e3)
-    cands = {k: v for k, v in st.items() if k.endswith("_attend")}
-    dom = max(cands, key=cands.get)
+    # per-kernel launch durations (library-recorded HIP events) and the dominant kernel's roofline
+    from long_context_attention_17_amd import binding as ca
+    progress("kernel timing")
+    kernels = {}
+    if cfg.csa:
+        kernels["csa_attend"] = ca.TIMED_CSA_ATTEND
+    if cfg.hca:
+        kernels["hca_attend"] = ca.TIMED_HCA_ATTEND
+    kt, queued = time_kernels(lambda i: step(), kernels, max(steps, 3))
+    dom = max(kt, key=lambda k: kt[k][0] * kt[k][1])
     flops = work["csa_flops"] if dom == "csa_attend" else work["hca_flops"]
-    achieved = flops / (st[dom] / 1e3) / 1e12
-    roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
-    extra = {"stages_ms": {k: round(v, 4) for k, v in st.items()}, "wall_s_timed": round(wall, 4),
-             "algorithmic_flops": work}
+    launch_ms = kt[dom][0]
+    achieved = flops / (launch_ms / 1e3) / 1e12
+    fmt = 2 if cfg.kv == "fp8mix" else 1
+    roof = {"kernel": f"attend_mx_kernel<{fmt}, {0 if dom == 'csa_attend' else 1}>", "stage": dom, "bound": "mfma",
+            "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "launch_ms": round(launch_ms, 5), "work_per_launch": flops}
+    extra = {"stages_ms": {k: round(v, 4) for k, v in st.items()},
+             "kernel_launch_ms": {k: round(v[0], 5) for k, v in kt.items()}, "kernel_timing_queued": queued,
+             "wall_s_timed": round(wall, 4), "algorithmic_flops": work}
     config = {"workload": f"{cfg.name}: prefill of {'CSA' if cfg.csa else ''}{'+' if cfg.csa and cfg.hca else ''}"
                           f"{'HCA' if cfg.hca else ''}, L={cfg.L}, {cfg.n_h} heads, D={cfg.D}, kv {cfg.kv}",
               "seq_len": cfg.L}
@@ -364,6 +411,9 @@ def main():
     ap.add_argument("--workload", default="decode_1m", choices=sorted(WORKLOADS))
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run a plain device-to-device copy of this many MiB (3 times), the reference "
+                         "kernel for scaling HBM counter readings")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the workload; runs on more than one GPU are not "
@@ -372,6 +422,14 @@ def main():
     from long_context_attention_17_amd.configs import CONFIGS
     cfg = CONFIGS[WORKLOADS[args.workload]]
     torch.cuda.set_device(0)
+    if args.copy_calibration_mib > 0:
+        src = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
     if cfg.phase == "decode":
         value, ms, config, roof, extra, state = bench_decode(cfg, args.steps, args.warmup, args.replicas, args)
     else:
@@ -383,7 +441,7 @@ def main():
         with open(tpath) as f:
             tj = json.load(f)
         ent = tj.get(args.workload, {}).get(roof["kernel"])
-        if ent and ent.get("source_hash") == kernel_source_hash():
+        if ent and ent.get("source_hash") == kernel_source_hash(roof["kernel"]):
             traffic = ent.get("bytes_per_launch")
     roof["traffic"] = traffic
     line = {"metric": METRIC, "value": round(value, 3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -395,7 +453,7 @@ def main():
         line["cpu_baseline"] = (cpu_baseline_decode(cfg, (synth_ctx(cfg), None)) if cfg.phase == "decode"
                                 else cpu_baseline_prefill(cfg))
     line.update(extra)
-    line["kernel_source_hash"] = kernel_source_hash()
+    line["kernel_source_hash"] = kernel_source_hash(roof["kernel"])
     print(json.dumps(line), flush=True)
 
 

@@ -258,6 +258,32 @@ int ca_hca_attend_decode(const ca_attend_params* p, const void* q, const float* 
                          int32_t W, const float* sink, void* out, float* lse, void* ws, size_t ws_bytes,
                          void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* Launch timing (diagnostics, not part of the method).  While a kernel's   */
+/* bit is set, every eager launch of it is bracketed by two HIP events       */
+/* recorded on the stream it is launched on; launches inside a stream        */
+/* capture are not timed.  Not thread-safe: use from one host thread, with   */
+/* no other thread launching library work meanwhile.                         */
+typedef enum {
+  CA_TIMED_CSA_ATTEND = 0,    /* gathered-entry attention kernel of CSA (one launch per attend call) */
+  CA_TIMED_HCA_ATTEND = 1,    /* dense compressed-entry attention kernel of HCA */
+  CA_TIMED_INDEX_SCORES = 2,  /* indexer scoring kernel of ca_index_topk_* */
+  CA_TIMED_KERNELS = 3
+} ca_timed_kernel;
+
+/* Start timing the kernels whose bits (1 << ca_timed_kernel) are set in
+ * kernel_mask, at most max_launches launches each (later ones run untimed).
+ * Creates the HIP events (host call; no device memory).  Discards earlier
+ * timings.  CA_ERR_ARG for an unknown bit or max_launches outside 1..2^20. */
+int ca_timer_start(uint32_t kernel_mask, int64_t max_launches);
+
+/* Host: waits for the kernel's last timed launch, then returns the summed
+ * event-to-event time of its timed launches (ms) and their count. */
+int ca_timer_read(int32_t kernel, double* total_ms, int64_t* launches);
+
+/* Waits for pending timed launches, destroys the events, stops timing. */
+int ca_timer_stop(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -83,6 +83,9 @@ _SIGS = {
                                              _I64, _P, _P, _P, _SZ, _P]),
     "ca_hca_attend_decode": (ctypes.c_int, [ctypes.POINTER(AttendParams), _P, _P, _PC, _I32, _P, _I32, _I64, _P,
                                             _I32, _P, _P, _P, _P, _SZ, _P]),
+    "ca_timer_start": (ctypes.c_int, [ctypes.c_uint32, _I64]),
+    "ca_timer_read": (ctypes.c_int, [_I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64)]),
+    "ca_timer_stop": (ctypes.c_int, []),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -233,3 +236,26 @@ def hca_attend_decode(p: AttendParams, q, q_gain, kv: Cache, ratio: int, pos, ma
     _check(_lib.ca_hca_attend_decode(ctypes.byref(p), _ptr(q), _ptr(q_gain), kv.ref, ratio, _ptr(pos), B, max_pos,
                                      _ptr(window), window.shape[1], _ptr(sink), _ptr(out), _ptr(lse), _ptr(ws),
                                      ws.numel(), _stream(stream)))
+
+
+# ---------------------------------------------------------------- launch timing (diagnostics)
+TIMED_CSA_ATTEND, TIMED_HCA_ATTEND, TIMED_INDEX_SCORES = 0, 1, 2
+
+
+def timer_start(kernels, max_launches: int = 4096):
+    """Bracket every later eager launch of the given kernels with HIP events on their stream."""
+    mask = 0
+    for k in kernels:
+        mask |= 1 << k
+    _check(_lib.ca_timer_start(mask, max_launches))
+
+
+def timer_read(kernel: int):
+    """(summed milliseconds, launch count) of the kernel's timed launches; waits for the last one."""
+    ms, n = ctypes.c_double(0.0), ctypes.c_int64(0)
+    _check(_lib.ca_timer_read(kernel, ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
+
+
+def timer_stop():
+    _check(_lib.ca_timer_stop())

@@ -493,8 +493,11 @@ __device__ __forceinline__ float mx_probs(const float* sv, float m_run, bf16x8* 
   return psum;
 }
 
-template <int KV_FMT>
+// MODE 0: CSA (the row's selected entries), 1: HCA (all of the row's entries);
+// a compile-time copy of a.mode, so that the two attention kinds are distinct kernels.
+template <int KV_FMT, int MODE>
 __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
+  a.mode = MODE;
   typedef MxCfg<KV_FMT> C;
   typedef MxShared<KV_FMT> Sh;
   __shared__ Sh sh;
@@ -795,20 +798,29 @@ bool attend_mfma_supported(const AttendArgs& a) {
 hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
   if (a.n_rows == 0) return hipSuccess;
   const int splits = a.split_items > 0 ? a.max_splits : 1;
+  hipEvent_t ev0, ev1;
+  timer_events(a.mode == 0 ? CA_TIMED_CSA_ATTEND : CA_TIMED_HCA_ATTEND, st, &ev0, &ev1);
   if (attend_mfma_supported(a)) {
     const long units = (long)a.n_rows * (a.n_heads / 64) * splits;
     dim3 grid((unsigned)(units < cu_count() ? units : cu_count()));
-    if (a.kv.fmt == CA_FP8MIX)
-      hipLaunchKernelGGL(attend_mx_kernel<CA_FP8MIX>, grid, dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL(attend_mx_kernel<CA_BF16>, grid, dim3(256), 0, st, a);
+    if (a.kv.fmt == CA_FP8MIX) {
+      if (a.mode == 0)
+        CA_LAUNCH((attend_mx_kernel<CA_FP8MIX, 0>), grid, dim3(256), 0, st, ev0, ev1, a);
+      else
+        CA_LAUNCH((attend_mx_kernel<CA_FP8MIX, 1>), grid, dim3(256), 0, st, ev0, ev1, a);
+    } else {
+      if (a.mode == 0)
+        CA_LAUNCH((attend_mx_kernel<CA_BF16, 0>), grid, dim3(256), 0, st, ev0, ev1, a);
+      else
+        CA_LAUNCH((attend_mx_kernel<CA_BF16, 1>), grid, dim3(256), 0, st, ev0, ev1, a);
+    }
   } else {
     dim3 grid(a.n_rows, a.n_heads, splits);
     switch (a.D / 64) {
-      case 1: hipLaunchKernelGGL(attend_generic_kernel<1>, grid, dim3(64), 0, st, a); break;
-      case 2: hipLaunchKernelGGL(attend_generic_kernel<2>, grid, dim3(64), 0, st, a); break;
-      case 4: hipLaunchKernelGGL(attend_generic_kernel<4>, grid, dim3(64), 0, st, a); break;
-      case 8: hipLaunchKernelGGL(attend_generic_kernel<8>, grid, dim3(64), 0, st, a); break;
+      case 1: CA_LAUNCH(attend_generic_kernel<1>, grid, dim3(64), 0, st, ev0, ev1, a); break;
+      case 2: CA_LAUNCH(attend_generic_kernel<2>, grid, dim3(64), 0, st, ev0, ev1, a); break;
+      case 4: CA_LAUNCH(attend_generic_kernel<4>, grid, dim3(64), 0, st, ev0, ev1, a); break;
+      case 8: CA_LAUNCH(attend_generic_kernel<8>, grid, dim3(64), 0, st, ev0, ev1, a); break;
       default: return hipErrorInvalidValue;
     }
   }

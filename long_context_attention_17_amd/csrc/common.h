@@ -1,5 +1,6 @@
 // Shared device helpers of the CSA / HCA kernels (gfx950 / CDNA4).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

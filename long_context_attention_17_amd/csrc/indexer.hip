@@ -661,22 +661,24 @@ hipError_t launch_index_scores(const CacheView& cv, const ca_index_params& p, co
     hipLaunchKernelGGL(topk_zero_kernel, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, st, state, nz);
   }
   if (max_ne == 0) return hipGetLastError();   // no entries yet: nothing to score
+  hipEvent_t ev0, ev1;
+  timer_events(CA_TIMED_INDEX_SCORES, st, &ev0, &ev1);
   if (fp8) {
     const int64_t chunks = (max_ne + kScoreChunk - 1) / kScoreChunk;
     if (seq_fixed >= 0) {
       dim3 grid((unsigned)((n_rows + 3) / 4), (unsigned)chunks);
-      hipLaunchKernelGGL(index_scores_fp8_kernel<4>, grid, dim3(256), 0, st, cv, p.ratio, p.q_format, qI, w, pos,
-                         seq_fixed, n_rows, scores, stride, state, kRowWords);
+      CA_LAUNCH(index_scores_fp8_kernel<4>, grid, dim3(256), 0, st, ev0, ev1, cv, p.ratio, p.q_format, qI, w, pos,
+                seq_fixed, n_rows, scores, stride, state, kRowWords);
     } else {
       dim3 grid((unsigned)n_rows, (unsigned)chunks);
-      hipLaunchKernelGGL(index_scores_fp8_kernel<1>, grid, dim3(256), 0, st, cv, p.ratio, p.q_format, qI, w, pos,
-                         seq_fixed, n_rows, scores, stride, state, kRowWords);
+      CA_LAUNCH(index_scores_fp8_kernel<1>, grid, dim3(256), 0, st, ev0, ev1, cv, p.ratio, p.q_format, qI, w, pos,
+                seq_fixed, n_rows, scores, stride, state, kRowWords);
     }
   } else {
     dim3 grid((unsigned)n_rows, (unsigned)((max_ne + 255) / 256));
     size_t sm = sizeof(float) * p.n_heads * p.dim;
-    hipLaunchKernelGGL(index_scores_generic_kernel, grid, dim3(256), sm, st, cv, p.n_heads, p.dim, p.ratio,
-                       p.q_format, qI, w, pos, seq_fixed, scores, stride);
+    CA_LAUNCH(index_scores_generic_kernel, grid, dim3(256), sm, st, ev0, ev1, cv, p.n_heads, p.dim, p.ratio,
+              p.q_format, qI, w, pos, seq_fixed, scores, stride);
   }
   if (state != nullptr) {  // histogram of the scores for the long top-k
     const unsigned chunks = (unsigned)((stride + kChunk - 1) / kChunk);

@@ -69,4 +69,17 @@ bool attend_mfma_supported(const AttendArgs& a);
 int attend_mfma_max_items();  // items one MFMA workgroup handles without splitting
 hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
 
+// Launch timing of the timed kernels (ids: ca_timed_kernel): the start / stop
+// events for the next launch of `kernel` on `st`, or false (both null) when it
+// is not being timed.  CA_LAUNCH launches through hipExtLaunchKernelGGL with
+// the events when they are set, else with hipLaunchKernelGGL.
+bool timer_events(int kernel, hipStream_t st, hipEvent_t* start, hipEvent_t* stop);
+#define CA_LAUNCH(kernel, grid, block, smem, st, ev0, ev1, ...)                       \
+  do {                                                                              \
+    if (ev0 != nullptr)                                                             \
+      hipExtLaunchKernelGGL(kernel, grid, block, smem, st, ev0, ev1, 0, __VA_ARGS__); \
+    else                                                                            \
+      hipLaunchKernelGGL(kernel, grid, block, smem, st, __VA_ARGS__);               \
+  } while (0)
+
 }  // namespace ca
