@@ -1,5 +1,6 @@
 // C ABI of the CSA / HCA library: host-side validation, workspace layout and
 // dispatch to the kernels.  No allocation, no host synchronisation.
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -305,6 +306,7 @@ static int attend_common(const ca_attend_params* p, const void* q, const float* 
   a.scale_log2 = p->scale * ca::kLog2e;
   a.eps = p->eps;
   a.base = p->rope_base;
+  a.rope_step = p->rope_dim > 0 ? pow(p->rope_base, -2.0 / (double)p->rope_dim) : 1.0;
   a.pos = pos;
   a.seq_fixed = seq_fixed;
   a.n_rows = (int)n_rows;

@@ -372,36 +372,56 @@ struct MxIssue {
 };
 
 // fp8 records: dequantize a raw stage into the bf16 tile.  Thread slots of 8
-// channels, one row per wavefront and step; content channels scaled by their tile
-// exponent, rotary channels copied, window rows read from global memory, rows
-// without an item zeroed.
+// channels (lane sl: channels 8sl .. 8sl+7), one row per wavefront and step.
+// Record rows first, in batches of four whose LDS reads are all issued before
+// any conversion: content lanes (sl < 56) scale their 8 e4m3 codes by the tile
+// exponent of their 64-channel tile, rotary lanes copy 8 bf16 channels; rows
+// without an item are zeroed.  Window rows (bf16 in global memory) follow in a
+// pass of their own that runs only for tiles holding some, so that the record
+// pass has no global loads (and no waits on the loads in flight).
 __device__ __forceinline__ void mx_convert(const AttendArgs& a, const uint8_t* raw, const uint32_t* valid,
                                            const uint32_t* items, int jt, int j0, int n_c, __bf16* tile) {
   const int wave = threadIdx.x >> 6, sl = threadIdx.x & 63;
-#pragma unroll 4
-  for (int u = 0; u < kRows / 4; ++u) {
-    const int it = 4 * u + wave;
-    const uint8_t* row = raw + it * kRawPitch;
-    __bf16* dst = tile + mx_row(it) * kPitch + 8 * sl;
-    const bool ok = (valid[wave] >> u) & 1u;
-    u32x4 out = {0u, 0u, 0u, 0u};
-    if (ok) {
-      if (jt + it >= n_c) {
-        out = *(const u32x4*)(item_src(a, items[jt + it - j0]) + 16 * sl);
-      } else if (sl < 56) {     // channels 8*sl .. 8*sl+7 < 448: e4m3 codes
-        const u32x2 w = *(const u32x2*)(row + 8 * sl);
-        const float sc = ldexpf(1.0f, (int)(int8_t)row[kD + kR + (sl >> 3)]);
-        bf16x2 c0 = e4m3x2_to_bf16_scaled<false>(w[0], sc), c1 = e4m3x2_to_bf16_scaled<true>(w[0], sc);
-        bf16x2 c2 = e4m3x2_to_bf16_scaled<false>(w[1], sc), c3 = e4m3x2_to_bf16_scaled<true>(w[1], sc);
-        out[0] = __builtin_bit_cast(uint32_t, c0);
-        out[1] = __builtin_bit_cast(uint32_t, c1);
-        out[2] = __builtin_bit_cast(uint32_t, c2);
-        out[3] = __builtin_bit_cast(uint32_t, c3);
-      } else {                  // rotary channels, bf16
-        out = *(const u32x4*)(row + 448 + 16 * (sl - 56));
-      }
+  const bool code = sl < (kD - kR) / 8;
+  const int rd = code ? 8 * sl : 16 * sl - (kD - kR);   // this lane's input bytes within a record
+  const int ex = kD + kR + (sl >> 3);                    // its tile exponent byte (content lanes)
+  const uint32_t vb = __builtin_amdgcn_readfirstlane(valid[wave]);
+  const int n_rec = n_c - jt;                            // rows it < n_rec hold records (if valid)
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    u32x2 x0[4], x1[4];
+    int e[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint8_t* row = raw + (4 * (4 * b + i) + wave) * kRawPitch;
+      x0[i] = *(const u32x2*)(row + rd);
+      x1[i] = *(const u32x2*)(row + rd + 8);
+      e[i] = (int)(int8_t)row[ex];
     }
-    *(u32x4*)dst = out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int u = 4 * b + i, it = 4 * u + wave;
+      if (it >= n_rec && ((vb >> u) & 1u)) continue;     // window row: second pass (uniform)
+      const float sc = ldexpf(1.0f, e[i]);
+      const bf16x2 c0 = e4m3x2_to_bf16_scaled<false>(x0[i][0], sc), c1 = e4m3x2_to_bf16_scaled<true>(x0[i][0], sc);
+      const bf16x2 c2 = e4m3x2_to_bf16_scaled<false>(x0[i][1], sc), c3 = e4m3x2_to_bf16_scaled<true>(x0[i][1], sc);
+      u32x4 out;
+      out[0] = code ? __builtin_bit_cast(uint32_t, c0) : x0[i][0];
+      out[1] = code ? __builtin_bit_cast(uint32_t, c1) : x0[i][1];
+      out[2] = code ? __builtin_bit_cast(uint32_t, c2) : x1[i][0];
+      out[3] = code ? __builtin_bit_cast(uint32_t, c3) : x1[i][1];
+      if (!((vb >> u) & 1u)) out = u32x4{0u, 0u, 0u, 0u};
+      *(u32x4*)(tile + mx_row(it) * kPitch + 8 * sl) = out;
+    }
+  }
+  if (jt + kRows > n_c) {                                // the tile reaches the window (uniform)
+#pragma unroll 4
+    for (int u = 0; u < kRows / 4; ++u) {
+      const int it = 4 * u + wave;
+      if (it < n_rec || !((vb >> u) & 1u)) continue;
+      const u32x4 out = *(const u32x4*)(item_src(a, items[jt + it - j0]) + 16 * sl);
+      *(u32x4*)(tile + mx_row(it) * kPitch + 8 * sl) = out;
+    }
   }
 }
 
@@ -584,10 +604,18 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
   // never waits for a tile.
   if (q_row != r || q_hg != hg) load_q(r, hg);
   if (tid < kR / 2) {
-    float sn, cs;
-    rope_sincos((double)ri.t, tid, kR, a.base, &sn, &cs);
-    sh.rope_cs[2 * tid] = cs;
-    sh.rope_cs[2 * tid + 1] = sn;
+    // angle t * theta_p with theta_p = rope_step^p (binary powering in fp64), taken in
+    // revolutions and reduced exactly in fp64; the hardware sin / cos take revolutions
+    double th = 1.0, bp = a.rope_step;
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+      th = ((tid >> k) & 1) ? th * bp : th;
+      bp *= bp;
+    }
+    const double rev = (double)ri.t * th * 0.15915494309189535;   // 1 / (2 pi)
+    const float fr = (float)(rev - floor(rev));
+    sh.rope_cs[2 * tid] = __builtin_amdgcn_cosf(fr);
+    sh.rope_cs[2 * tid + 1] = __builtin_amdgcn_sinf(fr);
   }
   const int n_tab = (j1 - j0) < kMaxItems ? (j1 - j0) : kMaxItems;
   for (int i = tid; i < n_tab; i += 256) sh.items[i] = item_off(a, ri, r, j0 + i);

@@ -38,6 +38,7 @@ struct AttendArgs {
   float scale_log2;  // logit scale * log2(e)
   float eps;
   double base;
+  double rope_step;    // base^(-2/R): the rotary frequency of pair p is rope_step^p
   const int32_t* pos;  // nullptr: position == row (prefill)
   int seq_fixed;       // >= 0: every row is this cache sequence (prefill); < 0: row r is sequence r
   int n_rows;
