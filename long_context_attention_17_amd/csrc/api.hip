@@ -264,7 +264,8 @@ size_t ca_attend_workspace(const ca_attend_params* p, int32_t n_rows, int64_t ma
   size_t ms = (size_t)max_splits_for(max_pos, p->n_win, k, ratio);
   size_t po = (size_t)n_rows * ms * p->n_heads * p->dim * sizeof(float);
   size_t pm = (size_t)n_rows * ms * p->n_heads * 2 * sizeof(float);
-  return align256(po) + align256(pm);
+  size_t pq = (size_t)n_rows * p->n_heads * p->dim * 2;   // prepared bf16 queries
+  return align256(po) + align256(pm) + align256(pq);
 }
 
 static int attend_common(const ca_attend_params* p, const void* q, const float* q_gain, const ca_cache* kv,
@@ -327,6 +328,7 @@ static int attend_common(const ca_attend_params* p, const void* q, const float* 
   a.max_splits = 1;
   a.part_o = nullptr;
   a.part_ml = nullptr;
+  a.q_prep = nullptr;
   // Split the item list of each row into fixed chunks: always for decode (a plan that
   // depends on the sequence alone), and for prefill rows longer than one MFMA
   // workgroup's item table.
@@ -343,7 +345,9 @@ static int attend_common(const ca_attend_params* p, const void* q, const float* 
   }
   if (split > 0) {
     const size_t po = align256((size_t)n_rows * ms * p->n_heads * p->dim * sizeof(float));
-    const size_t need = po + align256((size_t)n_rows * ms * p->n_heads * 2 * sizeof(float));
+    const size_t pm = align256((size_t)n_rows * ms * p->n_heads * 2 * sizeof(float));
+    const size_t pq = align256((size_t)n_rows * p->n_heads * p->dim * 2);
+    const size_t need = po + pm + pq;
     if (ws_bytes < need || ws == nullptr)
       return fail(CA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes (rows of up to %lld items are split)", what,
                   ws_bytes, need, (long long)max_items);
@@ -352,6 +356,7 @@ static int attend_common(const ca_attend_params* p, const void* q, const float* 
     a.max_splits = ms;
     a.part_o = (float*)ws;
     a.part_ml = (float*)((char*)ws + po);
+    if (ca::attend_mfma_supported(a)) a.q_prep = (uint16_t*)((char*)ws + po + pm);
   }
   return hip_status(ca::launch_attend(a, S(stream)), what);
 }

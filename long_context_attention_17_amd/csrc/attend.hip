@@ -255,6 +255,7 @@ constexpr int kRows = 64;               // items per ring tile
 constexpr int kPitch = kD + 8;          // bf16 elements per LDS tile row (1040 B)
 constexpr int kRawPitch = 592;          // bytes per raw fp8 staging row (584 B record, 16 B granules)
 constexpr int kMaxItems = 2176;         // items per workgroup (k + window <= 2048 + 128); longer rows are split
+constexpr int kWaitVm0 = 0x0F70;        // s_waitcnt immediate: vmcnt(0), other counters unconstrained
 constexpr uint32_t kNoItem = 0xFFFFFFFFu;
 constexpr uint32_t kWinFlag = 0x80000000u;
 constexpr float kNoMax = -1.0e30f;      // running max before any valid item (finite: no inf - inf)
@@ -503,19 +504,73 @@ __device__ __forceinline__ int mx_row_of(int v, int lane) { return 8 * (v >> 2) 
 
 // exp2 of the masked logits against the reference, as bf16 A fragments; returns the fp32 sum.
 __device__ __forceinline__ float mx_probs(const float* sv, float m_run, bf16x8* pa) {
-  float psum = 0.0f;
+  float p[16];
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
-    const float p = __builtin_amdgcn_exp2f(sv[v] - m_run);
-    psum += p;
-    pa[v >> 3][v & 7] = (__bf16)p;
+    p[v] = __builtin_amdgcn_exp2f(sv[v] - m_run);
+    pa[v >> 3][v & 7] = (__bf16)p[v];
   }
-  return psum;
+#pragma unroll
+  for (int w = 8; w >= 1; w >>= 1)                     // pairwise sum (short dependency chain)
+#pragma unroll
+    for (int v = 0; v < w; ++v) p[v] += p[v + w];
+  return p[0];
+}
+
+// Queries of every (row, head) prepared once per row for rows whose items are
+// split over several workgroups: RMSNorm with gain, RoPE at the row's position,
+// logit scale * log2(e), in bf16 (the arithmetic of the MFMA kernel's own query
+// transform).  One wavefront per (row, head), lane l holding channels 8l .. 8l+7.
+__global__ void __launch_bounds__(256) attend_qprep_kernel(AttendArgs a) {
+  const int r = blockIdx.x, h = blockIdx.y * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (h >= a.n_heads) return;
+  constexpr int CC = kD - kR;
+  const int t = a.pos ? a.pos[r] : r;
+  const int64_t off = ((int64_t)r * a.n_heads + h) * kD + 8 * lane;
+  const u32x4 w = *(const u32x4*)((const uint16_t*)a.q + off);
+  float x[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[2 * e] = __uint_as_float(w[e] << 16);
+    x[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+  }
+  float ss = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  const float inv = 1.0f / sqrtf(ss / (float)kD + a.eps);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] *= inv * a.q_gain[8 * lane + e];
+  if (8 * lane >= CC) {
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const int p = (8 * lane + e - CC) >> 1;
+      double th = 1.0, bp = a.rope_step;
+#pragma unroll
+      for (int k = 0; k < 5; ++k) {
+        th = ((p >> k) & 1) ? th * bp : th;
+        bp *= bp;
+      }
+      const double rev = (double)t * th * 0.15915494309189535;   // 1 / (2 pi)
+      const float fr = (float)(rev - floor(rev));
+      const float c = __builtin_amdgcn_cosf(fr), sn = __builtin_amdgcn_sinf(fr);
+      const float x0 = x[e], x1 = x[e + 1];
+      x[e] = x0 * c - x1 * sn;
+      x[e + 1] = x0 * sn + x1 * c;
+    }
+  }
+  u32x4 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    o[e] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)(x[2 * e] * a.scale_log2), (__bf16)(x[2 * e + 1] * a.scale_log2)});
+  *(u32x4*)(a.q_prep + off) = o;
 }
 
 // MODE 0: CSA (the row's selected entries), 1: HCA (all of the row's entries);
 // a compile-time copy of a.mode, so that the two attention kinds are distinct kernels.
-template <int KV_FMT, int MODE>
+// QP: the queries come prepared in a.q_prep (no per-workgroup transform).
+template <int KV_FMT, int MODE, bool QP>
 __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
   a.mode = MODE;
   typedef MxCfg<KV_FMT> C;
@@ -531,14 +586,15 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
   constexpr int CC = kD - kR;
   for (int i = tid; i < kD; i += 256) sh.gain[i] = a.q_gain[i];
 
-  // Raw query rows (bf16 bits as B fragments: lane = head l%32, channels 16s + 8(l/32)
-  // .. +7).  The next unit's rows are fetched right after the current unit's last
-  // QK, so their latency hides behind its last tile and epilogue.
+  // Raw (or prepared) query rows (bf16 bits as B fragments: lane = head l%32, channels
+  // 16s + 8(l/32) .. +7).  The next unit's rows are fetched early (after the last QK,
+  // or after the tile loop), so their latency hides behind the unit's end.
   bf16x8 qf[32];
   int q_row = -1, q_hg = -1;                           // rows held in qf
+  constexpr bool qp = QP;                              // queries come prepared (split rows)
   auto load_q = [&](int rr, int hh) {
-    const uint16_t* qrow =
-        (const uint16_t*)a.q + ((int64_t)rr * a.n_heads + hh * 64 + 32 * pair + (lane & 31)) * kD + 8 * (lane >> 5);
+    const uint16_t* qrow = (qp ? a.q_prep : (const uint16_t*)a.q) +
+                           ((int64_t)rr * a.n_heads + hh * 64 + 32 * pair + (lane & 31)) * kD + 8 * (lane >> 5);
 #pragma unroll
     for (int s = 0; s < 32; ++s) qf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * s));
     q_row = rr;
@@ -603,7 +659,7 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
   // the RoPE and item tables, and being older than the tile loads, waiting for them
   // never waits for a tile.
   if (q_row != r || q_hg != hg) load_q(r, hg);
-  if (tid < kR / 2) {
+  if (!qp && tid < kR / 2) {                           // (the table serves the transform and de-rotation)
     // angle t * theta_p with theta_p = rope_step^p (binary powering in fp64), taken in
     // revolutions and reduced exactly in fp64; the hardware sin / cos take revolutions
     double th = 1.0, bp = a.rope_step;
@@ -622,13 +678,17 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
   // a valid, finite row used as the source of loads for rows without an item: the window token at t
   const uint8_t* dummy = (const uint8_t*)a.win + ((int64_t)ri.win_seq * a.W + ri.t % a.W) * kD * 2;
   __syncthreads();
+  // vmcnt(0), as a builtin the compiler understands: the query loads (older than the
+  // item-table loads just awaited) are complete, so no wait for them is placed inside
+  // the MFMA loops, where the tile loads in flight would make it a real stall
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
   for (int t = 0; t < kPrologueTiles; ++t) {
     MxIssue<KV_FMT> is;
     is.prepare(a, j0, j1, t, t, sh, dummy, t < ntiles);
     is.all();
   }
 
-  transform_q();
+  if constexpr (!qp) transform_q();
   q_row = -1;                                          // qf now holds transformed queries
 
   // Softmax reference: m_run is set by the first tile with a valid item (O is still
@@ -640,7 +700,7 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
   constexpr float kBump = 60.0f;
   f32x16 oacc[8];
   mx_zero(oacc);
-  float m_run = m_force, l_part = 0.0f, m_true = kNoMax;
+  float m_run = m_force, l_part = 0.0f, m_loc = kNoMax;   // m_loc: max logit of this lane's items
   bool redo = false;
   for (int tile = 0; tile < ntiles; ++tile) {
     const int st = tile & 1;
@@ -648,7 +708,7 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
       if (tile + 1 < ntiles) __asm__ volatile("s_waitcnt vmcnt(16)" ::: "memory");
       else __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     } else {
-      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
     }
     __syncthreads();                                   // tile landed for every wavefront
     const u32x4 vw = *(const u32x4*)sh.valid[st];      // (fp8: read before the stage is refilled)
@@ -663,12 +723,16 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
       is.prepare(a, j0, j1, tile + 1, st ^ 1, sh, dummy, tile + 1 < ntiles);
       tl = (const __bf16*)sh.ring[st];
     }
+    // the next tile's row loads go out between the QK MFMAs (one row after every
+    // second MFMA), so that their issue overlaps the matrix work
     f32x16 s;
-    is.all();                                          // the next tile gets the whole tile period
-    mx_scores(tl + 32 * half * kPitch, qf, s, [](int) {});
-    if (tile == ntiles - 1 && unit + (int)gridDim.x < n_units) {
-      const int un = unit + gridDim.x;                 // prefetch the next unit's queries
-      load_q(un / (n_hg * n_sp), (un / n_sp) % n_hg);
+    if (is.on)
+      mx_scores(tl + 32 * half * kPitch, qf, s, [&](int u) { is.row(u); });
+    else
+      mx_scores(tl + 32 * half * kPitch, qf, s, [](int) {});
+    if (!C::kFp8 && tile == ntiles - 1 && unit + (int)gridDim.x < n_units) {
+      const int un = unit + gridDim.x;                 // prefetch the next unit's queries (bf16:
+      load_q(un / (n_hg * n_sp), (un / n_sp) % n_hg);  // right after the last QK)
     }
     float sv[16];
     float mx = -INFINITY;
@@ -686,28 +750,30 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
         mx = fmaxf(mx, sv[v]);
       }
     }
-    const float tmax = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const bool bump = __any(tmax > m_run + kBump);
+    // a logit above the reference by more than kBump anywhere in the workgroup?  (Any
+    // lane's own maximum will do: no per-head maximum is formed on the common path.)
+    const bool bump = __any(mx > m_run + kBump);
+    m_loc = fmaxf(m_loc, mx);
     bf16x8 pown[2];
     float psum = mx_probs(sv, m_run, pown);
     *(bf16x8*)&sh.pex[wave][lane][0] = pown[0];
     *(bf16x8*)&sh.pex[wave][lane][1] = pown[1];
-    if (lane < 32) sh.tmx[wave][lane] = tmax;
     if (lane == 0) sh.bump[wave] = bump;
     __syncthreads();
     // everything the exchange delivers, read at once
     const i32x4 bumps = *(const i32x4*)sh.bump;
-    const float tmax_pair = fmaxf(tmax, sh.tmx[partner][hl]);
     bf16x8 ppar[2];
     ppar[0] = *(const bf16x8*)&sh.pex[partner][lane][0];
     ppar[1] = *(const bf16x8*)&sh.pex[partner][lane][1];
-    m_true = fmaxf(m_true, tmax_pair);
     if (__builtin_expect(bumps[0] | bumps[1] | bumps[2] | bumps[3], 0)) {   // workgroup-uniform
       if (m_run == kNoMax) {
-        // first tile with valid items (the same tile for every head): set the reference
-        m_run = tmax_pair;
-        psum = mx_probs(sv, m_run, pown);
+        // first tile with valid items (the same tile for every head): the reference is the
+        // pair's maximum logit of each head over this tile
+        const float tmax = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        if (lane < 32) sh.tmx[wave][lane] = tmax;
         __syncthreads();                               // every wavefront has read the exchange
+        m_run = fmaxf(tmax, sh.tmx[partner][hl]);
+        psum = mx_probs(sv, m_run, pown);
         *(bf16x8*)&sh.pex[wave][lane][0] = pown[0];
         *(bf16x8*)&sh.pex[wave][lane][1] = pown[1];
         __syncthreads();
@@ -721,9 +787,17 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
     mx_pv(tl, half, pown, ppar, oacc);
   }
 
+  if (C::kFp8 && unit + (int)gridDim.x < n_units) {   // prefetch the next unit's queries (fp8:
+    const int un = unit + gridDim.x;                   // after the loop, whose top wait the
+    load_q(un / (n_hg * n_sp), (un / n_sp) % n_hg);    // compiler cannot see)
+  }
   if (__builtin_expect(redo && m_force == kNoMax, 0)) {  // workgroup-uniform
     // a logit overflowed the reference: recompute the unit against the exact maximum
-    m_force = m_true;
+    // of each head over the pair's items
+    const float mt = fmaxf(m_loc, __shfl_xor(m_loc, 32, 64));
+    if (lane < 32) sh.tmx[wave][lane] = mt;
+    __syncthreads();
+    m_force = fmaxf(mt, sh.tmx[partner][hl]);
     unit -= gridDim.x;
     __syncthreads();                                   // every wavefront is done with the ring
     continue;
@@ -829,18 +903,27 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
   hipEvent_t ev0, ev1;
   timer_events(a.mode == 0 ? CA_TIMED_CSA_ATTEND : CA_TIMED_HCA_ATTEND, st, &ev0, &ev1);
   if (attend_mfma_supported(a)) {
+    if (a.q_prep != nullptr)
+      hipLaunchKernelGGL(attend_qprep_kernel, dim3(a.n_rows, a.n_heads / 4), dim3(256), 0, st, a);
     const long units = (long)a.n_rows * (a.n_heads / 64) * splits;
     dim3 grid((unsigned)(units < cu_count() ? units : cu_count()));
+    const bool qp = a.q_prep != nullptr;
     if (a.kv.fmt == CA_FP8MIX) {
-      if (a.mode == 0)
-        CA_LAUNCH((attend_mx_kernel<CA_FP8MIX, 0>), grid, dim3(256), 0, st, ev0, ev1, a);
-      else
-        CA_LAUNCH((attend_mx_kernel<CA_FP8MIX, 1>), grid, dim3(256), 0, st, ev0, ev1, a);
+      if (a.mode == 0) {
+        if (qp) CA_LAUNCH((attend_mx_kernel<CA_FP8MIX, 0, true>), grid, dim3(256), 0, st, ev0, ev1, a);
+        else CA_LAUNCH((attend_mx_kernel<CA_FP8MIX, 0, false>), grid, dim3(256), 0, st, ev0, ev1, a);
+      } else {
+        if (qp) CA_LAUNCH((attend_mx_kernel<CA_FP8MIX, 1, true>), grid, dim3(256), 0, st, ev0, ev1, a);
+        else CA_LAUNCH((attend_mx_kernel<CA_FP8MIX, 1, false>), grid, dim3(256), 0, st, ev0, ev1, a);
+      }
     } else {
-      if (a.mode == 0)
-        CA_LAUNCH((attend_mx_kernel<CA_BF16, 0>), grid, dim3(256), 0, st, ev0, ev1, a);
-      else
-        CA_LAUNCH((attend_mx_kernel<CA_BF16, 1>), grid, dim3(256), 0, st, ev0, ev1, a);
+      if (a.mode == 0) {
+        if (qp) CA_LAUNCH((attend_mx_kernel<CA_BF16, 0, true>), grid, dim3(256), 0, st, ev0, ev1, a);
+        else CA_LAUNCH((attend_mx_kernel<CA_BF16, 0, false>), grid, dim3(256), 0, st, ev0, ev1, a);
+      } else {
+        if (qp) CA_LAUNCH((attend_mx_kernel<CA_BF16, 1, true>), grid, dim3(256), 0, st, ev0, ev1, a);
+        else CA_LAUNCH((attend_mx_kernel<CA_BF16, 1, false>), grid, dim3(256), 0, st, ev0, ev1, a);
+      }
     }
   } else {
     dim3 grid(a.n_rows, a.n_heads, splits);
