@@ -236,8 +236,8 @@ def bench_decode(cfg, steps, warmup, replicas, args):
     fmt = 2 if cfg.kv == "fp8mix" else 1
     roof_of = {   # algorithmic work of one launch (the launch covers the whole batch)
         "index_scores": ("hbm", work["index_bytes"], f"index_scores_fp8_kernel<1>"),
-        "csa_attend": ("mfma", work["csa_flops"], f"attend_mx_kernel<{fmt}, 0>"),
-        "hca_attend": ("mfma", work["hca_flops"], f"attend_mx_kernel<{fmt}, 1>"),
+        "csa_attend": ("mfma", work["csa_flops"], f"attend_mx_kernel<{fmt}, 0, true>"),
+        "hca_attend": ("mfma", work["hca_flops"], f"attend_mx_kernel<{fmt}, 1, true>"),
     }
     dom = max(roof_of, key=lambda k: kt[k][0] * kt[k][1])
     bound, units, symbol = roof_of[dom]
@@ -327,7 +327,7 @@ def bench_prefill(cfg, steps, warmup, replicas, args):
     launch_ms = kt[dom][0]
     achieved = flops / (launch_ms / 1e3) / 1e12
     fmt = 2 if cfg.kv == "fp8mix" else 1
-    roof = {"kernel": f"attend_mx_kernel<{fmt}, {0 if dom == 'csa_attend' else 1}>", "stage": dom, "bound": "mfma",
+    roof = {"kernel": f"attend_mx_kernel<{fmt}, {0 if dom == 'csa_attend' else 1}, false>", "stage": dom, "bound": "mfma",
             "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "launch_ms": round(launch_ms, 5), "work_per_launch": flops}
     extra = {"stages_ms": {k: round(v, 4) for k, v in st.items()},

@@ -10,26 +10,14 @@
 //
 // A query row reads an ordered list of "items": its compressed entries
 // (idx[r, 0..cnt) for CSA, 0..floor(t/m')-1 for HCA) followed by its window
-// tokens max(0, t-n_win+1)..t.  Decode splits the list into fixed chunks of
-// kDecodeSplitItems items (a function of the sequence alone, so a sequence's
-// result does not depend on the batch it is in) and a combine kernel merges the
-// partial (m, l, o) in split order.
+// tokens max(0, t-n_win+1)..t.  Decode splits the list into chunks whose length
+// is a function of the row alone (so a sequence's result does not depend on the
+// batch it is in), and a combine kernel merges the partial (m, l, o) in split
+// order.
 //
 // MFMA path (D = 512, bf16 queries, bf16 or fp8-mixed entries, bf16 window):
-//   one workgroup = one query row x 64 heads (4 wavefronts x 16 heads).
-//   Entry tiles of 32 items are staged in LDS as bf16 (fp8 codes dequantized
-//   exactly with the per-tile power-of-two scale during staging), double
-//   buffered, the next tile's global loads in flight during the current
-//   tile's math.  Because every item is both key and value, the same LDS tile
-//   feeds both contractions:
-//     S^T = K Q^T  (v_mfma_f32_16x16x32_bf16, A = K rows from LDS, B = the
-//                   wavefront's 16 normalized query heads held in registers)
-//     O  += P V    (A = P straight from the S^T accumulators: lane l holds head
-//                   l%16 and items {4g..4g+3, 16+4g..16+4g+3}, g = l/16, which
-//                   is a valid k-slot order as long as V uses the same order;
-//                   B = V read with ds_read_b64_tr_b16, the gfx950 LDS
-//                   transpose load, from the row-major tile)
-//   so P never leaves registers and no transposed copy of the tile is kept.
+// persistent workgroups of 4 wavefronts, one unit (row, 64 heads, split) at a
+// time; the MFMA section below describes the tiling.
 // Generic path (any D multiple of 64 up to 512, fp32 math): one wavefront
 //   per (row, head), items streamed from global memory; used for fp32 caches.
 #include "common.h"
