@@ -189,33 +189,85 @@ __global__ void __launch_bounds__(64) attend_generic_kernel(AttendArgs a) {
 }
 
 // ======================================================================== combine
-__global__ void attend_combine_kernel(AttendArgs a) {
-  const int r = blockIdx.x, hh = blockIdx.y, d = threadIdx.x;
-  const int D = a.D, C = a.D - a.R;
+// Merge of a row's split partials (m, l, o) in split order, with the sink in the
+// denominator, then de-rotation of the rotary channels.  A thread owns 4 channels
+// of one head (D/4 threads per head, 512 / (D/4) heads per workgroup); the partials
+// of up to kCombineUnroll splits are all loaded before any is combined.
+constexpr int kCombineUnroll = 16;
+
+__global__ void __launch_bounds__(512) attend_combine_kernel(AttendArgs a) {
+  const int D = a.D, C = a.D - a.R, tph = D / 4;
+  const int r = blockIdx.x, hh = blockIdx.y * (512 / tph) + threadIdx.x / tph, d = 4 * (threadIdx.x % tph);
+  if (hh >= a.n_heads) return;
   const RowInfo ri = row_info(a, r);
   const int ns = n_splits_of(a, ri.total);
+  const int64_t base0 = (int64_t)r * a.max_splits * a.n_heads + hh;   // (split s: + s * n_heads)
   const float sk = a.sink[hh] * kLog2e;
+  float ms[kCombineUnroll], ls[kCombineUnroll];
+  f32x4 os[kCombineUnroll];
+#pragma unroll
+  for (int s = 0; s < kCombineUnroll; ++s) {
+    if (s < ns) {
+      const int64_t b = base0 + (int64_t)s * a.n_heads;
+      const f32x2 ml = *(const f32x2*)(a.part_ml + 2 * b);
+      ms[s] = ml[0];
+      ls[s] = ml[1];
+      os[s] = *(const f32x4*)(a.part_o + b * D + d);
+    }
+  }
   float M = sk;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_ml[2 * (((int64_t)r * a.max_splits + s) * a.n_heads + hh)]);
-  float den = exp2f(sk - M), acc = 0.0f;
-  for (int s = 0; s < ns; ++s) {
-    int64_t base = ((int64_t)r * a.max_splits + s) * a.n_heads + hh;
-    float ms = a.part_ml[2 * base], ls = a.part_ml[2 * base + 1];
-    float wgt = exp2f(ms - M);
-    den += ls * wgt;
-    if (d < D) acc += a.part_o[base * D + d] * wgt;
+#pragma unroll
+  for (int s = 0; s < kCombineUnroll; ++s)
+    if (s < ns) M = fmaxf(M, ms[s]);
+  for (int s = kCombineUnroll; s < ns; ++s) M = fmaxf(M, a.part_ml[2 * (base0 + (int64_t)s * a.n_heads)]);
+  float den = exp2f(sk - M);
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int s = 0; s < kCombineUnroll; ++s) {
+    if (s < ns) {
+      const float w = exp2f(ms[s] - M);
+      den += ls[s] * w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += os[s][e] * w;
+    }
   }
-  float v = acc / den;
-  float other = __shfl_xor(v, 1, 64);
-  if (d >= D) return;
-  if (d >= C) {
-    float s, c;
-    rope_sincos((double)ri.t, (d - C) >> 1, a.R, a.base, &s, &c);
-    v = (d & 1) ? v * c - other * s : v * c + other * s;
+  for (int s = kCombineUnroll; s < ns; ++s) {
+    const int64_t b = base0 + (int64_t)s * a.n_heads;
+    const float w = exp2f(a.part_ml[2 * b] - M);
+    den += a.part_ml[2 * b + 1] * w;
+    const f32x4 o = *(const f32x4*)(a.part_o + b * D + d);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += o[e] * w;
   }
-  int64_t oi = ((int64_t)r * a.n_heads + hh) * D + d;
-  if (a.out_fmt == CA_F32) ((float*)a.out)[oi] = v;
-  else ((uint16_t*)a.out)[oi] = f32_to_bf16_bits(v);
+  f32x4 v;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = acc[e] / den;
+  if (d >= C) {                                        // rotary pairs (d, d+1), (d+2, d+3): rotate by R_{-t}
+#pragma unroll
+    for (int e = 0; e < 4; e += 2) {
+      const int p = (d + e - C) >> 1;
+      double th = 1.0, bp = a.rope_step;
+      for (int k = 0; (p >> k) != 0; ++k) {
+        th = ((p >> k) & 1) ? th * bp : th;
+        bp *= bp;
+      }
+      const double rev = (double)ri.t * th * 0.15915494309189535;   // 1 / (2 pi)
+      const float fr = (float)(rev - floor(rev));
+      const float c = __builtin_amdgcn_cosf(fr), sn = __builtin_amdgcn_sinf(fr);
+      const float x0 = v[e], x1 = v[e + 1];
+      v[e] = x0 * c + x1 * sn;
+      v[e + 1] = x1 * c - x0 * sn;
+    }
+  }
+  const int64_t oi = ((int64_t)r * a.n_heads + hh) * D + d;
+  if (a.out_fmt == CA_F32) {
+    *(f32x4*)((float*)a.out + oi) = v;
+  } else {
+    u32x2 w;
+    w[0] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)v[0], (__bf16)v[1]});
+    w[1] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)v[2], (__bf16)v[3]});
+    *(u32x2*)((uint16_t*)a.out + oi) = w;
+  }
   if (a.lse && d == 0) a.lse[(int64_t)r * a.n_heads + hh] = (M + log2f(den)) / kLog2e;
 }
 
@@ -925,8 +977,8 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.split_items <= 0) return e;
-  int threads = (a.D + 63) / 64 * 64;
-  hipLaunchKernelGGL(attend_combine_kernel, dim3(a.n_rows, a.n_heads), dim3(threads), 0, st, a);
+  const int hpb = 512 / (a.D / 4);                     // heads per combine workgroup
+  hipLaunchKernelGGL(attend_combine_kernel, dim3(a.n_rows, (a.n_heads + hpb - 1) / hpb), dim3(512), 0, st, a);
   return hipGetLastError();
 }
 
