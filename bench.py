@@ -235,7 +235,7 @@ def bench_decode(cfg, steps, warmup, replicas, args):
                                      "index_scores": ca.TIMED_INDEX_SCORES}, max(steps, 20))
     fmt = 2 if cfg.kv == "fp8mix" else 1
     roof_of = {   # algorithmic work of one launch (the launch covers the whole batch)
-        "index_scores": ("hbm", work["index_bytes"], f"index_scores_fp8_kernel<1>"),
+        "index_scores": ("hbm", work["index_bytes"], "index_scores_fp8_kernel<1>"),
         "csa_attend": ("mfma", work["csa_flops"], f"attend_mx_kernel<{fmt}, 0, true>"),
         "hca_attend": ("mfma", work["hca_flops"], f"attend_mx_kernel<{fmt}, 1, true>"),
     }

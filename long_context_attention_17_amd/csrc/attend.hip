@@ -271,6 +271,101 @@ __global__ void __launch_bounds__(512) attend_combine_kernel(AttendArgs a) {
   if (a.lse && d == 0) a.lse[(int64_t)r * a.n_heads + hh] = (M + log2f(den)) / kLog2e;
 }
 
+// The same merge for partials of the MFMA path, which its epilogue writes in the
+// accumulator layout: per (row, split, 64-head group) a block
+// [pair][half][cb][v/4][lane][v%4] of fp32, element v of `lane` being head
+// 32*pair + 8(v/4) + 4(lane/32) + v%4 of the group and channel 256*half + 32*cb +
+// lane%32.  Workgroup = (row, head group, half, cb); thread (pair, v/4, lane) reads
+// one 16-byte run per split (heads h0 .. h0+3, one channel), so every wavefront
+// load is 1 KB contiguous.
+__global__ void __launch_bounds__(512) attend_combine_acc_kernel(AttendArgs a) {
+  constexpr int D = 512, C = D - 64;
+  const int r = blockIdx.x, n_hg = a.n_heads >> 6;
+  const int hg = blockIdx.y >> 4, half = (blockIdx.y >> 3) & 1, cb = blockIdx.y & 7;
+  const int t = threadIdx.x, pair = t >> 8, vq = (t >> 6) & 3, lane = t & 63;
+  const int h0 = hg * 64 + 32 * pair + 8 * vq + 4 * (lane >> 5);   // heads h0 .. h0+3
+  const int c = 256 * half + 32 * cb + (lane & 31);
+  const RowInfo ri = row_info(a, r);
+  const int ns = n_splits_of(a, ri.total);
+  const f32x4 sk = *(const f32x4*)(a.sink + h0) * kLog2e;
+  f32x4 M = sk, den = {0.0f, 0.0f, 0.0f, 0.0f}, acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  float ms[kCombineUnroll][4], ls[kCombineUnroll][4];
+  f32x4 os[kCombineUnroll];
+#pragma unroll
+  for (int s = 0; s < kCombineUnroll; ++s) {
+    if (s < ns) {
+      const int64_t b = ((int64_t)r * a.max_splits + s) * a.n_heads + h0;
+      const f32x4 ml0 = *(const f32x4*)(a.part_ml + 2 * b), ml1 = *(const f32x4*)(a.part_ml + 2 * b + 4);
+      ms[s][0] = ml0[0]; ls[s][0] = ml0[1]; ms[s][1] = ml0[2]; ls[s][1] = ml0[3];
+      ms[s][2] = ml1[0]; ls[s][2] = ml1[1]; ms[s][3] = ml1[2]; ls[s][3] = ml1[3];
+      os[s] = *(const f32x4*)(a.part_o + (((int64_t)r * a.max_splits + s) * n_hg + hg) * (64 * D) +
+                              (pair * 2 + half) * 8192 + (cb * 4 + vq) * 256 + 4 * lane);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < kCombineUnroll; ++s)
+    if (s < ns)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) M[e] = fmaxf(M[e], ms[s][e]);
+  for (int s = kCombineUnroll; s < ns; ++s) {
+    const int64_t b = ((int64_t)r * a.max_splits + s) * a.n_heads + h0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) M[e] = fmaxf(M[e], a.part_ml[2 * (b + e)]);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) den[e] = exp2f(sk[e] - M[e]);
+#pragma unroll
+  for (int s = 0; s < kCombineUnroll; ++s) {
+    if (s < ns) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float w = exp2f(ms[s][e] - M[e]);
+        den[e] += ls[s][e] * w;
+        acc[e] += os[s][e] * w;
+      }
+    }
+  }
+  for (int s = kCombineUnroll; s < ns; ++s) {
+    const int64_t b = ((int64_t)r * a.max_splits + s) * a.n_heads + h0;
+    const f32x4 o = *(const f32x4*)(a.part_o + (((int64_t)r * a.max_splits + s) * n_hg + hg) * (64 * D) +
+                                    (pair * 2 + half) * 8192 + (cb * 4 + vq) * 256 + 4 * lane);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float w = exp2f(a.part_ml[2 * (b + e)] - M[e]);
+      den[e] += a.part_ml[2 * (b + e) + 1] * w;
+      acc[e] += o[e] * w;
+    }
+  }
+  f32x4 v;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = acc[e] / den[e];
+  if (c >= C) {                                        // rotary pair (c & ~1, c | 1) sits in lanes l, l^1
+    const int p = (c - C) >> 1;
+    double th = 1.0, bp = a.rope_step;
+    for (int k = 0; (p >> k) != 0; ++k) {
+      th = ((p >> k) & 1) ? th * bp : th;
+      bp *= bp;
+    }
+    const double rev = (double)ri.t * th * 0.15915494309189535;   // 1 / (2 pi)
+    const float fr = (float)(rev - floor(rev));
+    const float co = __builtin_amdgcn_cosf(fr), sn = __builtin_amdgcn_sinf(fr);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float other = __shfl_xor(v[e], 1, 64);
+      v[e] = (lane & 1) ? v[e] * co - other * sn : v[e] * co + other * sn;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int64_t oi = ((int64_t)r * a.n_heads + h0 + e) * D + c;
+    if (a.out_fmt == CA_F32) ((float*)a.out)[oi] = v[e];
+    else ((uint16_t*)a.out)[oi] = f32_to_bf16_bits(v[e]);
+  }
+  if (a.lse && half == 0 && cb == 0 && (lane & 31) == 0)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a.lse[(int64_t)r * a.n_heads + h0 + e] = (M[e] + log2f(den[e])) / kLog2e;
+}
+
 // ======================================================================== MFMA (D = 512)
 // v_mfma_f32_32x32x16_bf16 lane layouts (l = lane, 0..63):
 //   A (32 x 16): lane l holds row l%32, k = 8*(l/32) .. +7
@@ -857,16 +952,28 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
   static_assert(sizeof(sh.ring) + sizeof(sh.tile) >= 4 * 32 * kStage * 4, "staging buffer");
   float* stage = (float*)&sh.ring[0][0] + wave * 32 * kStage;
   const bool split_out = a.split_items > 0;
-  float fv[16];
   if (split_out) {
+    // split partials go out in the accumulator layout (the combine kernel reads it):
+    // per (row, split, head group) a block [pair][half][cb][v/4][lane][v%4] of fp32,
+    // so that each store instruction writes 1 KB contiguous and nothing is staged
     const int64_t pbase = ((int64_t)r * a.max_splits + split) * a.n_heads + head0;
     if (half == 0 && lane < 32) {
       a.part_ml[2 * (pbase + hl)] = m_run;
       a.part_ml[2 * (pbase + hl) + 1] = l_tot;
     }
+    float* blk = a.part_o + (((int64_t)r * a.max_splits + split) * n_hg + hg) * (64 * kD) +
+                 (pair * 2 + half) * (8 * 4 * 64 * 4) + 4 * lane;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) fv[v] = 1.0f;
-  } else {
+    for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+      for (int vq = 0; vq < 4; ++vq)
+        *(f32x4*)(blk + (cb * 4 + vq) * 256) =
+            f32x4{oacc[cb][4 * vq], oacc[cb][4 * vq + 1], oacc[cb][4 * vq + 2], oacc[cb][4 * vq + 3]};
+    __syncthreads();                                   // the next unit reuses the LDS
+    continue;
+  }
+  float fv[16];
+  {
     const float sk_own = a.sink[head0 + hl] * kLog2e;
     const float M_own = fmaxf(m_run, sk_own);
     const float den_own = l_tot * __builtin_amdgcn_exp2f(m_run - M_own) + __builtin_amdgcn_exp2f(sk_own - M_own);
@@ -880,7 +987,7 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) {
       float x = oacc[cb][v] * fv[v];
-      if (!split_out && c0 + 32 * cb >= CC) {          // rotary channels 448..511: rotate by R_{-t}
+      if (c0 + 32 * cb >= CC) {                        // rotary channels 448..511: rotate by R_{-t}
         const float other = __shfl_xor(x, 1, 64);
         const int p = (c0 + 32 * cb + (lane & 31) - CC) >> 1;
         const float c = sh.rope_cs[2 * p], sn = sh.rope_cs[2 * p + 1];
@@ -894,10 +1001,7 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
   // row h: 64 lanes x 4 channels
   for (int h = 0; h < 32; ++h) {
     const f32x4 x = *(const f32x4*)(stage + h * kStage + 4 * lane);
-    if (split_out) {
-      const int64_t pbase = ((int64_t)r * a.max_splits + split) * a.n_heads + head0;
-      *(f32x4*)(a.part_o + (pbase + h) * kD + c0 + 4 * lane) = x;
-    } else {
+    {
       const int64_t ob = ((int64_t)r * a.n_heads + head0 + h) * kD + c0 + 4 * lane;
       if (a.out_fmt == CA_F32) {
         *(f32x4*)((float*)a.out + ob) = x;
@@ -937,8 +1041,10 @@ bool attend_mfma_supported(const AttendArgs& a) {
          (a.kv.fmt == CA_BF16 || a.kv.fmt == CA_FP8MIX) && fits;
 }
 
-hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
-  if (a.n_rows == 0) return hipSuccess;
+hipError_t launch_attend(const AttendArgs& args, hipStream_t st) {
+  if (args.n_rows == 0) return hipSuccess;
+  AttendArgs a = args;
+  a.part_acc = attend_mfma_supported(a) ? 1 : 0;
   const int splits = a.split_items > 0 ? a.max_splits : 1;
   hipEvent_t ev0, ev1;
   timer_events(a.mode == 0 ? CA_TIMED_CSA_ATTEND : CA_TIMED_HCA_ATTEND, st, &ev0, &ev1);
@@ -977,8 +1083,12 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.split_items <= 0) return e;
-  const int hpb = 512 / (a.D / 4);                     // heads per combine workgroup
-  hipLaunchKernelGGL(attend_combine_kernel, dim3(a.n_rows, (a.n_heads + hpb - 1) / hpb), dim3(512), 0, st, a);
+  if (a.part_acc) {
+    hipLaunchKernelGGL(attend_combine_acc_kernel, dim3(a.n_rows, (a.n_heads / 64) * 16), dim3(512), 0, st, a);
+  } else {
+    const int hpb = 512 / (a.D / 4);                   // heads per combine workgroup
+    hipLaunchKernelGGL(attend_combine_kernel, dim3(a.n_rows, (a.n_heads + hpb - 1) / hpb), dim3(512), 0, st, a);
+  }
   return hipGetLastError();
 }
 

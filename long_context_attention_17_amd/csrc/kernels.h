@@ -59,6 +59,7 @@ struct AttendArgs {
   int max_splits;      // splits per row the workspace holds (never exceeded)
   float* part_o;       // [rows, max_splits, n_heads, D]
   float* part_ml;      // [rows, max_splits, n_heads, 2]
+  int part_acc;        // 1: part_o is in the MFMA kernel's accumulator layout (see attend_combine_kernel)
   uint16_t* q_prep;    // nullptr, or bf16 [rows, n_heads, D]: queries normalized, rotated and scaled
                        // once per row by a prep kernel (split rows of the MFMA path)
 };
