@@ -91,23 +91,25 @@ __global__ void index_scores_generic_kernel(CacheView cv, int nI, int cI, int m,
 // Block: 256 threads (4 waves).  blockIdx.x = group of QPW query rows,
 // blockIdx.y = chunk of kScoreChunk keys (64 pages); wave w owns 1,024
 // consecutive keys (16 pages) as 32 MFMA blocks of 32 keys, processed in groups
-// of 4 blocks with a register double buffer: the loads of group g+1 are in
-// flight while group g is scored.  The chunk's slice of the page table is
+// of kGroupBlocks blocks with a register double buffer: the loads of group g+1
+// are in flight while group g is scored.  The chunk's slice of the page table is
 // staged in LDS once, so key loads never wait on a page-table load.
 constexpr int kScoreChunk = 4096;
 constexpr int kHistBins = 4096;
 
+constexpr int kGroupBlocks = 8;          // MFMA blocks of 32 keys per load group (and per buffer)
+
 struct KeyGroup {
-  i32x4 v0[4], v1[4];
-  float ks[4];
-  bool ok[4];
+  i32x4 v0[kGroupBlocks], v1[kGroupBlocks];
+  float ks[kGroupBlocks];
+  bool ok[kGroupBlocks];
 };
 
 __device__ __forceinline__ void load_key_group(const CacheView& cv, const int* pt_s, int64_t k0, int64_t k1,
                                                int64_t gbase, int lane, KeyGroup& kg) {
   constexpr int cI = 64;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
+  for (int u = 0; u < kGroupBlocks; ++u) {
     const int64_t s = gbase + 32 * u + (lane & 31);
     const int pg = s < k1 ? pt_s[(int)((s - k0) >> cv.page_shift)] : -1;
     kg.ok[u] = pg >= 0;
@@ -166,12 +168,16 @@ __global__ void __launch_bounds__(256) index_scores_fp8_kernel(CacheView cv, int
     pt_s[i] = pg;
   }
   for (int row = wave; row < 32; row += 4) {
-    int qq = row / nI, hh = row % nI, r = r0 + qq;
-    bool valid = qq < QPW && r < n_rows;
-    float v = valid ? load_act(qI, q_fmt, ((int64_t)r * nI + hh) * cI + lane) : 0.0f;
-    int e = pow2_exponent(wave_max(fabsf(v)));
-    qcodes[row * cI + lane] = valid ? (uint8_t)e4m3_encode(ldexpf(v, -e)) : 0;
-    if (lane == 0) wq[row] = valid ? w[(int64_t)r * nI + hh] * ldexpf(1.0f, e) : 0.0f;
+    const int qq = row / nI, h = row % nI, r = r0 + qq;
+    if (qq < QPW && r < n_rows) {                      // (uniform) rows past the group's queries stay zero
+      const float v = load_act(qI, q_fmt, ((int64_t)r * nI + h) * cI + lane);
+      const int e = pow2_exponent(wave_max(fabsf(v)));
+      qcodes[row * cI + lane] = (uint8_t)e4m3_encode(ldexpf(v, -e));
+      if (lane == 0) wq[row] = w[(int64_t)r * nI + h] * ldexpf(1.0f, e);
+    } else {
+      qcodes[row * cI + lane] = 0;
+      if (lane == 0) wq[row] = 0.0f;
+    }
   }
   __syncthreads();
 
@@ -189,15 +195,16 @@ __global__ void __launch_bounds__(256) index_scores_fp8_kernel(CacheView cv, int
     for (int v = 0; v < 4; ++v) wl[qq][v] = wq[qq * nI + 4 * (lane >> 5) + v];
 
   const int64_t wbase = k0 + (kScoreChunk / 4) * wave;
-  constexpr int kGroups = kScoreChunk / 4 / 128;       // groups of 4 x 32 keys per wave
+  constexpr int kGroupKeys = 32 * kGroupBlocks;
+  constexpr int kGroups = kScoreChunk / 4 / kGroupKeys;  // groups per wave
   KeyGroup cur, nxt;
   load_key_group(cv, pt_s, k0, k1, wbase, lane, cur);
   for (int grp = 0; grp < kGroups; ++grp) {
-    const int64_t gbase = wbase + 128 * grp;
+    const int64_t gbase = wbase + kGroupKeys * grp;
     if (gbase >= k1) break;
-    if (grp + 1 < kGroups) load_key_group(cv, pt_s, k0, k1, gbase + 128, lane, nxt);
+    if (grp + 1 < kGroups) load_key_group(cv, pt_s, k0, k1, gbase + kGroupKeys, lane, nxt);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kGroupBlocks; ++u) {
       const int64_t s = gbase + 32 * u + (lane & 31);
       const i32x8 bop = __builtin_shufflevector(cur.v0[u], cur.v1[u], 0, 1, 2, 3, 4, 5, 6, 7);
       f32x16 acc = {};
