@@ -507,56 +507,81 @@ struct MxIssue {
   }
 };
 
-// fp8 records: dequantize a raw stage into the bf16 tile.  Thread slots of 8
-// channels (lane sl: channels 8sl .. 8sl+7), one row per wavefront and step.
-// Record rows first, in batches of four whose LDS reads are all issued before
-// any conversion: content lanes (sl < 56) scale their 8 e4m3 codes by the tile
-// exponent of their 64-channel tile, rotary lanes copy 8 bf16 channels; rows
-// without an item are zeroed.  Window rows (bf16 in global memory) follow in a
-// pass of their own that runs only for tiles holding some, so that the record
-// pass has no global loads (and no waits on the loads in flight).
+// fp8 records: dequantize a raw stage into the bf16 tile; wavefront w handles the
+// rows it = 4u + w (u < 16), whose LDS row is mx_row(it) = 16(u/4) + 4w + u%4.
+// Passes, each without a branch per row (a wavefront's LDS accesses take effect
+// in program order, so later passes overwrite earlier ones):
+//  1. content channels: lanes sl < 56 scale the 8 e4m3 codes of channels 8sl..8sl+7
+//     by the tile exponent of their 64-channel tile, in batches of four rows whose
+//     LDS reads are all issued before any conversion;
+//  2. rotary channels: the 16 rows' 128 B of bf16 copied by all 64 lanes;
+//  3. only for tiles with rows without an item: those rows are zeroed (finite V);
+//  4. only for tiles reaching the window: window rows (bf16 in global memory) are
+//     copied in, so that passes 1-3 have no global loads (nor waits on the loads
+//     in flight).
 __device__ __forceinline__ void mx_convert(const AttendArgs& a, const uint8_t* raw, const uint32_t* valid,
                                            const uint32_t* items, int jt, int j0, int n_c, __bf16* tile) {
-  const int wave = threadIdx.x >> 6, sl = threadIdx.x & 63;
-  const bool code = sl < (kD - kR) / 8;
-  const int rd = code ? 8 * sl : 16 * sl - (kD - kR);   // this lane's input bytes within a record
-  const int ex = kD + kR + (sl >> 3);                    // its tile exponent byte (content lanes)
-  const uint32_t vb = __builtin_amdgcn_readfirstlane(valid[wave]);
-  const int n_rec = n_c - jt;                            // rows it < n_rec hold records (if valid)
+  constexpr int CC = kD - kR;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), sl = threadIdx.x & 63;
+  const uint32_t vb = __builtin_amdgcn_readfirstlane(valid[wave]) & 0xFFFFu;
+  const uint8_t* rw = raw + wave * kRawPitch;            // row u of this wavefront: + 4u * kRawPitch
+  __bf16* tw = tile + 4 * wave * kPitch;                 // row u: + (16(u/4) + u%4) * kPitch
+  auto trow = [](int u) { return (16 * (u >> 2) + (u & 3)) * kPitch; };
+  if (sl < CC / 8) {
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    u32x2 x0[4], x1[4];
-    int e[4];
+    for (int b = 0; b < 4; ++b) {
+      u32x2 x[4];
+      int e[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint8_t* row = raw + (4 * (4 * b + i) + wave) * kRawPitch;
-      x0[i] = *(const u32x2*)(row + rd);
-      x1[i] = *(const u32x2*)(row + rd + 8);
-      e[i] = (int)(int8_t)row[ex];
-    }
+      for (int i = 0; i < 4; ++i) {
+        const uint8_t* row = rw + 4 * (4 * b + i) * kRawPitch;
+        x[i] = *(const u32x2*)(row + 8 * sl);
+        e[i] = (int)(int8_t)row[kD + kR + (sl >> 3)];
+      }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int u = 4 * b + i, it = 4 * u + wave;
-      if (it >= n_rec && ((vb >> u) & 1u)) continue;     // window row: second pass (uniform)
-      const float sc = ldexpf(1.0f, e[i]);
-      const bf16x2 c0 = e4m3x2_to_bf16_scaled<false>(x0[i][0], sc), c1 = e4m3x2_to_bf16_scaled<true>(x0[i][0], sc);
-      const bf16x2 c2 = e4m3x2_to_bf16_scaled<false>(x0[i][1], sc), c3 = e4m3x2_to_bf16_scaled<true>(x0[i][1], sc);
-      u32x4 out;
-      out[0] = code ? __builtin_bit_cast(uint32_t, c0) : x0[i][0];
-      out[1] = code ? __builtin_bit_cast(uint32_t, c1) : x0[i][1];
-      out[2] = code ? __builtin_bit_cast(uint32_t, c2) : x1[i][0];
-      out[3] = code ? __builtin_bit_cast(uint32_t, c3) : x1[i][1];
-      if (!((vb >> u) & 1u)) out = u32x4{0u, 0u, 0u, 0u};
-      *(u32x4*)(tile + mx_row(it) * kPitch + 8 * sl) = out;
+      for (int i = 0; i < 4; ++i) {
+        const float sc = ldexpf(1.0f, e[i]);
+        u32x4 out;
+        out[0] = __builtin_bit_cast(uint32_t, e4m3x2_to_bf16_scaled<false>(x[i][0], sc));
+        out[1] = __builtin_bit_cast(uint32_t, e4m3x2_to_bf16_scaled<true>(x[i][0], sc));
+        out[2] = __builtin_bit_cast(uint32_t, e4m3x2_to_bf16_scaled<false>(x[i][1], sc));
+        out[3] = __builtin_bit_cast(uint32_t, e4m3x2_to_bf16_scaled<true>(x[i][1], sc));
+        *(u32x4*)(tw + trow(4 * b + i) + 8 * sl) = out;
+      }
     }
   }
+  {
+    // lane l: rows u = l/8 and l/8 + 8, 16 B chunk l%8 of the 128 B rotary part
+    const int c = sl & 7, u0 = sl >> 3;
+    const u32x4 r0 = *(const u32x4*)(rw + 4 * u0 * kRawPitch + CC + 16 * c);
+    const u32x4 r1 = *(const u32x4*)(rw + 4 * (u0 + 8) * kRawPitch + CC + 16 * c);
+    *(u32x4*)(tw + trow(u0) + CC + 8 * c) = r0;
+    *(u32x4*)(tw + trow(u0 + 8) + CC + 8 * c) = r1;
+  }
+  if (vb != 0xFFFFu) {                                   // rows without an item (uniform)
+#pragma unroll
+    for (int u = 0; u < kRows / 4; ++u)
+      if (!((vb >> u) & 1u)) *(u32x4*)(tw + trow(u) + 8 * sl) = u32x4{0u, 0u, 0u, 0u};
+  }
+  const int n_rec = n_c - jt;                            // rows it < n_rec hold records (if valid)
   if (jt + kRows > n_c) {                                // the tile reaches the window (uniform)
-#pragma unroll 4
-    for (int u = 0; u < kRows / 4; ++u) {
-      const int it = 4 * u + wave;
-      if (it < n_rec || !((vb >> u) & 1u)) continue;
-      const u32x4 out = *(const u32x4*)(item_src(a, items[jt + it - j0]) + 16 * sl);
-      *(u32x4*)(tile + mx_row(it) * kPitch + 8 * sl) = out;
+    // groups of four rows: four unconditional loads (rows that are not window rows
+    // read the window's first row) out before the first store
+#pragma unroll 1
+    for (int b = 0; b < kRows / 16; ++b) {
+      u32x4 w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int u = 4 * b + i, it = 4 * u + wave;
+        const bool win = it >= n_rec && ((vb >> u) & 1u);
+        const uint32_t off = items[win ? jt + it - j0 : 0];
+        w[i] = *(const u32x4*)(item_src(a, win ? off : kWinFlag) + 16 * sl);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int u = 4 * b + i, it = 4 * u + wave;
+        if (it >= n_rec && ((vb >> u) & 1u)) *(u32x4*)(tw + trow(u) + 8 * sl) = w[i];
+      }
     }
   }
 }

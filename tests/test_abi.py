@@ -76,3 +76,20 @@ def test_argument_errors_are_reported_without_launching():
     p = ca.CompressParams(4, 1, ca.BF16, 1, 1, 1e-6, 1e4)
     assert lib.ca_compress_prefill(ctypes.byref(p), None, None, None, None, None, None, None, 3, 0,
                                    ctypes.byref(cache), None) == 0
+
+
+def test_timer_argument_errors_need_no_device():
+    """The launch timer rejects bad arguments before it creates any HIP event."""
+    from long_context_attention_17_amd import binding as ca
+    lib = ca.lib()
+    assert lib.ca_timer_start(1 << 3, 16) == -1           # unknown kernel bit
+    assert lib.ca_timer_start(1, 0) == -1                 # no launches to time
+    assert lib.ca_timer_start(1, (1 << 20) + 1) == -1     # above the launch cap
+    ms, n = ctypes.c_double(-1.0), ctypes.c_int64(-1)
+    assert lib.ca_timer_read(-1, ctypes.byref(ms), ctypes.byref(n)) == -1
+    assert lib.ca_timer_read(ca.TIMED_INDEX_SCORES + 1, ctypes.byref(ms), ctypes.byref(n)) == -1
+    assert lib.ca_timer_read(ca.TIMED_HCA_ATTEND, None, ctypes.byref(n)) == -1
+    # nothing was timed: reading reports zero launches without touching the device
+    assert lib.ca_timer_read(ca.TIMED_HCA_ATTEND, ctypes.byref(ms), ctypes.byref(n)) == 0
+    assert (ms.value, n.value) == (0.0, 0)
+    assert lib.ca_timer_stop() == 0

@@ -434,3 +434,42 @@ def test_reference_overflow_recompute():
     err = np.abs(outs[0] - outs[1]).max()
     log(f"  overflow recompute vs no recompute: max-abs {err:.3e}")
     assert err <= 1e-2
+
+
+def test_launch_timer_counts_and_caps_launches():
+    """Timed launches (hipExtLaunchKernelGGL with events) compute the same bytes as
+    untimed ones; each attend/index call is one timed launch, capped at max_launches."""
+    ca, configs, layers, synth = _ca()
+    cfg = _cfg(name="tm", phase="decode", kv="fp8mix", n_h=64, k=64, B=3, ctx_lo=900, ctx_hi=3000, L=0, seed=91)
+    ctx = synth.decode_contexts(cfg)
+    outs = {}
+    for layer in ("hca", "csa"):
+        lay = layers.DecodeLayer(cfg, synth.decode_layer(cfg, layer, "cuda", ctx))
+        lay.append_token()
+        if layer == "csa":
+            lay.index_topk()
+        lay.attend()
+        torch.cuda.synchronize()
+        outs[layer] = (lay, lay.out.clone())
+    hca, ref_h = outs["hca"]
+    csa, ref_c = outs["csa"]
+    ca.timer_start([ca.TIMED_HCA_ATTEND, ca.TIMED_INDEX_SCORES], max_launches=2)
+    try:
+        for _ in range(3):
+            hca.attend()
+        csa.index_topk()
+        csa.attend()                                   # CSA attention is not in the mask
+        ms_h, n_h = ca.timer_read(ca.TIMED_HCA_ATTEND)
+        ms_i, n_i = ca.timer_read(ca.TIMED_INDEX_SCORES)
+        ms_c, n_c = ca.timer_read(ca.TIMED_CSA_ATTEND)
+    finally:
+        ca.timer_stop()
+    torch.cuda.synchronize()
+    assert (n_h, n_i, n_c) == (2, 1, 0)
+    assert ms_h > 0 and ms_i > 0 and ms_c == 0
+    assert ms_h < 1000 and ms_i < 1000
+    assert torch.equal(hca.out.view(torch.int16), ref_h.view(torch.int16))
+    assert torch.equal(csa.out.view(torch.int16), ref_c.view(torch.int16))
+    # after stop nothing is timed and reads report zero
+    hca.attend()
+    assert ca.timer_read(ca.TIMED_HCA_ATTEND) == (0.0, 0)
