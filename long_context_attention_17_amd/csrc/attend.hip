@@ -434,6 +434,69 @@ __device__ __forceinline__ uint32_t item_off(const AttendArgs& a, const RowInfo&
   return w ? kWinFlag | (uint32_t)((p - (const uint8_t*)a.win) >> 4) : (uint32_t)((p - a.kv.pool) >> 4);
 }
 
+// Item table of a unit: items j0 .. j0 + n_tab - 1 as item_off gives them, built
+// in groups of kTabGroup items per thread, in phases, so that the dependent loads
+// of a group overlap (entry indices, CSA: the selected ones; then page-table
+// entries; then offsets).
+constexpr int kTabGroup = 3;
+template <int MODE>
+__device__ __forceinline__ void mx_item_table(const AttendArgs& a, const RowInfo& ri, int r, int j0, int n_tab,
+                                              uint32_t* items) {
+  const int tid = threadIdx.x;
+  n_tab = __builtin_amdgcn_readfirstlane(n_tab);
+  for (int g0 = 0; g0 < n_tab; g0 += 256 * kTabGroup) {
+    int32_t e[kTabGroup], pg[kTabGroup];
+    // loads are unconditional (from clamped, in-range addresses) inside one
+    // workgroup-uniform branch, and kept apart from their uses, so that no wait
+    // separates them
+#pragma unroll
+    for (int k = 0; k < kTabGroup; ++k) {
+      const int i = g0 + tid + 256 * k, j = j0 + i;
+      e[k] = i < n_tab && j < ri.n_c ? j : -1;
+    }
+    if (MODE == 0 && a.k > 0) {
+      int32_t x[kTabGroup];
+#pragma unroll
+      for (int k = 0; k < kTabGroup; ++k) x[k] = a.idx[(int64_t)r * a.k + (e[k] >= 0 ? e[k] : 0)];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < kTabGroup; ++k) e[k] = e[k] >= 0 ? x[k] : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < kTabGroup; ++k) pg[k] = -1;
+    if (a.kv.max_pages > 0) {
+      int32_t x[kTabGroup];
+      bool ok[kTabGroup];
+#pragma unroll
+      for (int k = 0; k < kTabGroup; ++k) {
+        const int v = e[k], pi = v >> a.kv.page_shift;
+        ok[k] = v >= 0 && (MODE != 0 || v < ri.t / a.ratio) && pi < a.kv.max_pages;
+        x[k] = a.kv.page_table[(int64_t)ri.seq * a.kv.max_pages + (ok[k] ? pi : 0)];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < kTabGroup; ++k) pg[k] = ok[k] ? x[k] : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < kTabGroup; ++k) {
+      const int i = g0 + tid + 256 * k, j = j0 + i;
+      if (i < n_tab) {
+        uint32_t off;
+        if (j < ri.n_c) {
+          const int32_t p = pg[k];
+          off = (p < 0 || p >= a.kv.n_pages)
+                    ? kNoItem
+                    : (uint32_t)(((int64_t)p * a.kv.page_bytes + (int64_t)a.kv.slot_of(e[k]) * a.kv.stride) >> 4);
+        } else {
+          const int w = ri.w0 + (j - ri.n_c);
+          off = kWinFlag | (uint32_t)((((int64_t)ri.win_seq * a.W + w % a.W) * kD * 2) >> 4);
+        }
+        items[i] = off;
+      }
+    }
+  }
+}
+
 __device__ __forceinline__ const uint8_t* item_src(const AttendArgs& a, uint32_t off) {
   return (off & kWinFlag) ? (const uint8_t*)a.win + ((uint64_t)(off & ~kWinFlag) << 4)
                           : (const uint8_t*)a.kv.pool + ((uint64_t)off << 4);
@@ -586,31 +649,28 @@ __device__ __forceinline__ void mx_convert(const AttendArgs& a, const uint8_t* r
   }
 }
 
-// S^T (32 items x 32 heads) = K Q^T over the 512 channels: 32 MFMAs in two
-// accumulation chains, K fragments (row l%32, 16 B at channel 16s + 8(l/32)) read
+// S^T (32 items x 32 heads) = K Q^T over the 512 channels: 32 MFMAs in one
+// accumulation chain, K fragments (row l%32, 16 B at channel 16s + 8(l/32)) read
 // kPf steps ahead; between(u) runs after every second MFMA (u = 0..15).
 constexpr int kPf = 4;
 template <class F>
 __device__ __forceinline__ void mx_scores(const __bf16* kt, const bf16x8* qf, f32x16& s_out, const F& between) {
   const int lane = threadIdx.x & 63;
   const __bf16* krow = kt + mx_row(lane & 31) * kPitch + 8 * (lane >> 5);
-  f32x16 acc[2];
+  f32x16 acc;
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[c][v] = 0.0f;
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
   bf16x8 kf[kPf];
 #pragma unroll
   for (int s = 0; s < kPf; ++s) kf[s] = *(const bf16x8*)(krow + 16 * s);
 #pragma unroll
   for (int s = 0; s < 32; ++s) {
-    acc[s & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s % kPf], qf[s], acc[s & 1], 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s % kPf], qf[s], acc, 0, 0, 0);
     if (s + kPf < 32) kf[s % kPf] = *(const bf16x8*)(krow + 16 * (s + kPf));
     if (s & 1) between(s >> 1);
     __builtin_amdgcn_sched_barrier(0);
   }
-#pragma unroll
-  for (int v = 0; v < 16; ++v) s_out[v] = acc[0][v] + acc[1][v];
+  s_out = acc;
 }
 
 // O (32 heads x 256 channels, 8 column blocks) += P V over the 64 items of a
@@ -834,7 +894,7 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
     sh.rope_cs[2 * tid + 1] = __builtin_amdgcn_sinf(fr);
   }
   const int n_tab = (j1 - j0) < kMaxItems ? (j1 - j0) : kMaxItems;
-  for (int i = tid; i < n_tab; i += 256) sh.items[i] = item_off(a, ri, r, j0 + i);
+  mx_item_table<MODE>(a, ri, r, j0, n_tab, sh.items);
   // a valid, finite row used as the source of loads for rows without an item: the window token at t
   const uint8_t* dummy = (const uint8_t*)a.win + ((int64_t)ri.win_seq * a.W + ri.t % a.W) * kD * 2;
   __syncthreads();
