@@ -22,8 +22,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-FMT_F32, FMT_BF16, FMT_FP8MIX, FMT_E4M3 = 0, 1, 2, 3
-FMT_BY_NAME = {"f32": FMT_F32, "bf16": FMT_BF16, "fp8mix": FMT_FP8MIX, "e4m3": FMT_E4M3}
+FMT_F32, FMT_BF16, FMT_FP8MIX, FMT_E4M3, FMT_FP4 = 0, 1, 2, 3, 4
+FMT_BY_NAME = {"f32": FMT_F32, "bf16": FMT_BF16, "fp8mix": FMT_FP8MIX, "e4m3": FMT_E4M3, "fp4": FMT_FP4}
 
 
 def build(force: bool = False) -> str:
@@ -54,6 +54,10 @@ def lib():
             "orc_encode_bf16_array": (None, [I64, P, P]),
             "orc_decode_bf16_array": (None, [I64, P, P]),
             "orc_decode_e4m3_array": (None, [I64, P, P]),
+            "orc_e2m1_decode": (D, [ctypes.c_uint8]),
+            "orc_e2m1_encode": (ctypes.c_uint8, [D]),
+            "orc_fp4_block_exponent": (I, [D]),
+            "orc_decode_e2m1_array": (None, [I64, P, P]),
             "orc_quantize_rows_e4m3": (None, [I64, I, P, P, P]),
             "orc_record_stride": (I64, [I, I, I]),
             "orc_page_bytes": (I64, [I, I, I, I]),
@@ -102,6 +106,21 @@ def e4m3_decode(codes) -> np.ndarray:
 
 def e4m3_encode_scalar(x: float) -> int:
     return int(lib().orc_e4m3_encode(float(x)))
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(codes.shape, np.float64)
+    lib().orc_decode_e2m1_array(codes.size, _p(codes), _p(out))
+    return out
+
+
+def e2m1_encode_scalar(x: float) -> int:
+    return int(lib().orc_e2m1_encode(float(x)))
+
+
+def fp4_block_exponent(amax: float) -> int:
+    return int(lib().orc_fp4_block_exponent(float(amax)))
 
 
 def bf16_encode(x) -> np.ndarray:

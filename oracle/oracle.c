@@ -7,7 +7,8 @@
  * Everything is computed in double precision with plain loops, in the order
  * the definitions are written, so a reader can check it against the source
  * pages by eye.  The only roundings are the storage formats (bf16, OCP e4m3
- * with power-of-two scales) that the method itself stores its cache in.
+ * with power-of-two scales, OCP e2m1 with E8M0 block scales) that the method
+ * itself stores its cache in.
  *
  * Sources (all on the "DeepSeek-V4" technical-report walkthrough book, page
  * slop-6tp.pages.dev/papers-html-argon/dsv4.html, hereafter "dsv4 book"):
@@ -136,6 +137,51 @@ void orc_quantize_rows_e4m3(int64_t n, int c, const double* x, uint8_t* codes, i
   }
 }
 
+/* OCP FP4 E2M1 (MX element format, the indexer-key precision of the
+ * dsv4 book Ch.6 "The lightning indexer" and Ch.8 "Quantization scales and
+ * bounded tail buffers"): 1 sign bit, 2 exponent bits (bias 1), 1 mantissa
+ * bit, no infinities or NaN.  Code bits: [3] sign, [2:1] exponent, [0]
+ * mantissa; exponent 0 is subnormal (0 or 0.5). */
+double orc_e2m1_decode(uint8_t code) {
+  int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+  double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+  return s ? -v : v;
+}
+
+/* Nearest E2M1 value by exhaustive search over the 8 magnitudes, ties to the
+ * even code (mantissa bit 0); beyond 6 the nearest is 6 (saturation).  A
+ * result of magnitude 0 is encoded +0. */
+uint8_t orc_e2m1_encode(double x) {
+  double a = fabs(x);
+  int best = 0;
+  double bd = INFINITY;
+  for (int c = 0; c < 8; ++c) {
+    double d = fabs(a - orc_e2m1_decode((uint8_t)c));
+    if (d < bd || (d == bd && (c & 1) == 0 && (best & 1) == 1)) {
+      bd = d;
+      best = c;
+    }
+  }
+  return (uint8_t)((x < 0 && best != 0) ? (best | 8) : best);
+}
+
+/* Block exponent of an FP4 block: the smallest e with amax <= 6 * 2^e (so no
+ * element saturates), 0 when amax == 0, clamped to the E8M0 range
+ * [-127, 127].  Stored as the E8M0 byte e + 127 (value 2^e). */
+int orc_fp4_block_exponent(double amax) {
+  if (!(amax > 0)) return 0;
+  int e = (int)ceil(log2(amax / 6.0));
+  while (amax > ldexp(6.0, e)) e++;
+  while (amax <= ldexp(6.0, e - 1)) e--;
+  if (e < -127) e = -127;
+  if (e > 127) e = 127;
+  return e;
+}
+
+void orc_decode_e2m1_array(int64_t n, const uint8_t* x, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_e2m1_decode(x[i]);
+}
+
 /* ------------------------------------------------------------------ */
 /* Record and page layout of the compressed caches                     */
 /* ------------------------------------------------------------------ */
@@ -147,6 +193,10 @@ void orc_quantize_rows_e4m3(int64_t n, int c, const double* x, uint8_t* codes, i
  *        Bytes: [codes D-R][bf16 2R][exponents (D-R)/64][zero pad] with the
  *        record stride rounded up to 128 bytes (640 B for D=512, R=64).
  * fmt 3: indexer key page, structure of arrays: [P*D e4m3 codes][P fp32 scales].
+ * fmt 4: indexer key page in FP4 (dsv4 book Ch.8: 0.5 byte per scalar plus a
+ *        1-byte scale per 32 elements): [P*D/2 bytes of E2M1 codes, channel
+ *        2k in the low nibble of byte k, channel 2k+1 in the high nibble]
+ *        [P*D/32 E8M0 block-scale bytes, block b of slot i at i*D/32 + b].
  * A page holds P entries; entry i of a sequence is in page
  * page_table_row[i / P] at slot i % P. */
 
@@ -159,12 +209,14 @@ int64_t orc_record_stride(int fmt, int D, int R) {
       return (raw + 127) / 128 * 128;
     }
     case 3: return D;  /* codes only; scales live at the end of the page */
+    case 4: return D / 2;
   }
   return -1;
 }
 
 int64_t orc_page_bytes(int fmt, int D, int R, int P) {
   if (fmt == 3) return (int64_t)P * D + 4 * (int64_t)P;
+  if (fmt == 4) return (int64_t)P * (D / 2) + (int64_t)P * (D / 32);
   return (int64_t)P * orc_record_stride(fmt, D, R);
 }
 
@@ -201,6 +253,20 @@ void orc_store_entry(int fmt, int D, int R, int P, uint8_t* pool, const int32_t*
     uint8_t* sc = pool + page * orc_page_bytes(fmt, D, R, P) + (int64_t)P * D + 4 * (i % P);
     float f = (float)ldexp(1.0, e);
     memcpy(sc, &f, 4);
+  } else if (fmt == 4) {
+    int64_t page = pt_row[i / P];
+    uint8_t* sc = pool + page * orc_page_bytes(fmt, D, R, P) + (int64_t)P * (D / 2) + (i % P) * (D / 32);
+    for (int b = 0; b < D / 32; ++b) {
+      double amax = 0;
+      for (int j = 0; j < 32; ++j) amax = fmax(amax, fabs(x[32 * b + j]));
+      int e = orc_fp4_block_exponent(amax);
+      sc[b] = (uint8_t)(e + 127);
+      for (int j = 0; j < 32; j += 2) {
+        uint8_t lo = orc_e2m1_encode(ldexp(x[32 * b + j], -e));
+        uint8_t hi = orc_e2m1_encode(ldexp(x[32 * b + j + 1], -e));
+        p[(32 * b + j) / 2] = (uint8_t)(lo | (hi << 4));
+      }
+    }
   }
 }
 
@@ -224,6 +290,13 @@ void orc_load_entry(int fmt, int D, int R, int P, const uint8_t* pool, const int
     float f;
     memcpy(&f, sc, 4);
     for (int j = 0; j < D; ++j) x[j] = orc_e4m3_decode(p[j]) * (double)f;
+  } else if (fmt == 4) {
+    int64_t page = pt_row[i / P];
+    const uint8_t* sc = pool + page * orc_page_bytes(fmt, D, R, P) + (int64_t)P * (D / 2) + (i % P) * (D / 32);
+    for (int j = 0; j < D; ++j) {
+      uint8_t code = (j & 1) ? (p[j / 2] >> 4) : (p[j / 2] & 15);
+      x[j] = ldexp(orc_e2m1_decode(code), (int)sc[j / 32] - 127);
+    }
   }
 }
 
@@ -355,7 +428,7 @@ void orc_window_prep(int64_t n, int D, int R, double base, double eps, const dou
  * every block s < floor(t/m) (Ch.5 "Causal availability"),
  *   I[t,s] = sum_h w[t,h] * ReLU( qI[t,h,:] . K[s,:] ).
  * qI holds the (dequantized) indexer query values [n_rows, nI, cI]; keys are
- * read from the indexer pool (fmt 0 or 3).  Scores beyond the eligible count
+ * read from the indexer pool (fmt 0, 3 or 4).  Scores beyond the eligible count
  * are left untouched.  n_elig[r] = min(floor(t/m), n_avail[seq]). */
 int orc_index_scores(int64_t n_rows, int nI, int cI, int m, const double* qI, const double* w,
                      const int64_t* pos, const int32_t* seq, int idx_fmt, int P, const uint8_t* pool,

@@ -47,7 +47,9 @@ def store_window(values: np.ndarray, act: str) -> np.ndarray:
 
 def indexer_query_values(qI: np.ndarray, idx_fmt: str) -> np.ndarray:
     """The indexer query as the indexer sees it: e4m3 with one power-of-two
-    scale per (token, head) for fp8 indexers, unchanged for fp32 ones."""
+    scale per (token, head) for e4m3 and FP4 key pools (FP4 keys meet fp8
+    queries, the mixed FP4 x FP8 product of the dsv4 book Ch.8 "FLOP
+    comparison" note), unchanged for fp32 ones."""
     if idx_fmt == "f32":
         return qI
     codes, exps = quantize_rows_e4m3(qI)

@@ -477,3 +477,129 @@ def test_decode_state_reproduces_prefill_rows(orc):
                     np.testing.assert_allclose(e_idx, pre["ikeys_raw"][i], atol=1e-13)
             else:
                 assert emitted is None
+
+
+# ------------------------------------------------------------------ FP4 indexer keys
+# OCP Microscaling (MX) v1.0 element format E2M1: the 8 non-negative magnitudes of
+# codes 0..7 (sign in bit 3).  Written out here from the format's definition.
+E2M1_MAGNITUDES = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_e2m1_decode_table(orc):
+    vals = orc.e2m1_decode(np.arange(16))
+    np.testing.assert_array_equal(vals[:8], E2M1_MAGNITUDES)
+    np.testing.assert_array_equal(vals[8:], [-v for v in E2M1_MAGNITUDES])
+
+
+def test_e2m1_encode_rne_and_saturation(orc):
+    # every representable value encodes to its own code (+0 for -0)
+    for c in range(16):
+        v = E2M1_MAGNITUDES[c & 7] * (-1 if c & 8 else 1)
+        assert orc.e2m1_encode_scalar(v) == (0 if c == 8 else c)
+    # the midpoint between codes L and L+1 goes to the one with mantissa bit 0;
+    # just below it to L, just above it to L+1
+    for lo in range(7):
+        x = 0.5 * (E2M1_MAGNITUDES[lo] + E2M1_MAGNITUDES[lo + 1])
+        even = lo if lo % 2 == 0 else lo + 1
+        assert orc.e2m1_encode_scalar(x) == even
+        assert orc.e2m1_encode_scalar(-x) == (even | 8 if even else 0)
+        assert orc.e2m1_encode_scalar(x * (1 - 1e-9)) == lo
+        assert orc.e2m1_encode_scalar(x * (1 + 1e-9)) == lo + 1
+    # saturation to 6, and the bound of the rounding error everywhere below it
+    assert orc.e2m1_encode_scalar(7.0) == 7 and orc.e2m1_encode_scalar(-1e9) == 15
+    x = np.random.default_rng(31).uniform(-6, 6, 20000)
+    dec = orc.e2m1_decode(np.array([orc.e2m1_encode_scalar(v) for v in x], np.uint8))
+    gaps = np.diff(E2M1_MAGNITUDES)
+    half_gap = np.array([gaps[min(np.searchsorted(E2M1_MAGNITUDES, abs(v), side="right") - 1, 6)] / 2 for v in x])
+    assert (np.abs(dec - x) <= half_gap + 1e-15).all()
+    assert (np.sign(dec) * np.sign(x) >= 0).all()
+
+
+def test_fp4_block_exponent_is_smallest_covering_power(orc):
+    rng = np.random.default_rng(32)
+    for a in np.concatenate([rng.uniform(1e-6, 1e4, 500), 6.0 * 2.0 ** np.arange(-20, 10)]):
+        e = orc.fp4_block_exponent(a)
+        assert a <= 6 * 2.0 ** e and a > 6 * 2.0 ** (e - 1)
+    assert orc.fp4_block_exponent(0.0) == 0
+
+
+def test_fp4_page_payload_matches_pages(orc):
+    g = gold("fp4_indexer_payload.json")["stated"]
+    c = g["indexer_key_dim"]
+    assert c * g["bytes_per_fp4_scalar"] == g["indexer_key_payload_bytes"]
+    assert g["indexer_key_payload_bytes"] / 4 == g["csa_indexer_bytes_per_token_m4"]
+    scale_bytes = c // g["scale_block_elements"] * g["scale_bytes_per_block"]
+    assert scale_bytes == g["scale_bytes_per_key"]
+    assert 100.0 * scale_bytes / g["indexer_key_payload_bytes"] == g["scale_overhead_percent"]
+    for P in (1, 64):
+        assert orc.page_bytes(oracle.FMT_FP4, c, 0, P) == P * (g["indexer_key_payload_bytes"] + scale_bytes)
+    assert orc.record_stride(oracle.FMT_FP4, 64, 0) == 32
+
+
+def test_fp4_page_layout_decodes_by_hand(orc):
+    """A page written byte by byte per the layout decodes to code value x 2^(scale-127);
+    the E8M0 scale byte is checked against torch's float8_e8m0fnu."""
+    c, P = 64, 4
+    rng = np.random.default_rng(33)
+    pb = orc.page_bytes(oracle.FMT_FP4, c, 0, P)
+    pool = rng.integers(0, 256, size=2 * pb, dtype=np.uint8)
+    sc = pool[pb + P * c // 2: pb + P * c // 2 + P * c // 32]
+    sc[:] = rng.integers(100, 150, size=sc.size)          # finite, moderate scales
+    pt = np.array([1, 0], np.int32)                        # entries 0..3 live in page 1
+    back = orc.load_entries(oracle.FMT_FP4, c, 0, P, pool, pt, 0, P)
+    e8m0 = torch.from_numpy(sc.copy()).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    for i in range(P):
+        codes = pool[pb + i * c // 2: pb + (i + 1) * c // 2]
+        for j in range(c):
+            code = codes[j // 2] & 15 if j % 2 == 0 else codes[j // 2] >> 4
+            mag = E2M1_MAGNITUDES[code & 7] * (-1 if code & 8 else 1)
+            assert back[i, j] == mag * e8m0[i * (c // 32) + j // 32]
+
+
+def test_fp4_store_round_trip(orc):
+    c, P = 64, 4
+    rng = np.random.default_rng(34)
+    x = rng.normal(size=(6, c)) * np.exp(rng.normal(size=(6, 1)) * 3)
+    x[2, :32] = 0.0                                           # an all-zero block: scale 2^0, codes 0
+    pool = np.zeros(2 * orc.page_bytes(oracle.FMT_FP4, c, 0, P), np.uint8)
+    pt = np.array([1, 0], np.int32)
+    oracle.finish_store(oracle.FMT_FP4, c, 0, P, pool, pt, 0, x, norm=False, rope=False)
+    back = orc.load_entries(oracle.FMT_FP4, c, 0, P, pool, pt, 0, 6)
+    for i in range(6):
+        for b in range(c // 32):
+            blk = x[i, 32 * b:32 * b + 32]
+            e = orc.fp4_block_exponent(np.abs(blk).max())
+            # each element is the nearest E2M1 value of x / 2^e, times 2^e
+            ref = np.array([orc.e2m1_decode(np.array([orc.e2m1_encode_scalar(v / 2.0 ** e)], np.uint8))[0]
+                            for v in blk]) * 2.0 ** e
+            np.testing.assert_array_equal(back[i, 32 * b:32 * b + 32], ref)
+            assert np.abs(back[i, 32 * b:32 * b + 32] - blk).max() <= 2.0 ** e    # half of the widest gap (2)
+    assert (back[2, :32] == 0).all()
+    # values already on the grid of their block survive exactly
+    grid = np.array(E2M1_MAGNITUDES * 8)[:c] * 2.0 ** -3
+    grid[:32] *= np.where(np.arange(32) % 3 == 0, -1, 1)
+    pool2 = np.zeros(orc.page_bytes(oracle.FMT_FP4, c, 0, P), np.uint8)
+    oracle.finish_store(oracle.FMT_FP4, c, 0, P, pool2, np.array([0], np.int32), 0, grid[None], norm=False, rope=False)
+    np.testing.assert_array_equal(orc.load_entries(oracle.FMT_FP4, c, 0, P, pool2, np.array([0], np.int32), 0, 1)[0], grid)
+
+
+def test_fp4_indexer_equals_f32_on_representable_keys(orc):
+    """Keys on the FP4 grid of their blocks score identically from an FP4 pool and an fp32 pool."""
+    rng = np.random.default_rng(35)
+    nI, c, n, m = 4, 64, 12, 4
+    mags = np.array(E2M1_MAGNITUDES)
+    keys = rng.choice(mags, size=(n, c)) * rng.choice([-1.0, 1.0], size=(n, c))
+    keys[:, ::32] = 6.0                                        # every block's maximum is 6 -> scale 2^0
+    keys *= 2.0 ** rng.integers(-3, 3, size=(n, 1))
+    q = rng.normal(size=(2, nI, c))
+    w = rng.normal(size=(2, nI))
+    P = 4
+    pool32, pt = _index_pool(orc, keys)
+    pool4 = np.zeros(len(pt) * orc.page_bytes(oracle.FMT_FP4, c, 0, P), np.uint8)
+    oracle.finish_store(oracle.FMT_FP4, c, 0, P, pool4, pt, 0, keys, norm=False, rope=False)
+    np.testing.assert_array_equal(orc.load_entries(oracle.FMT_FP4, c, 0, P, pool4, pt, 0, n), keys)
+    t = [n * m, n * m - 5]
+    s32, ne32 = orc.index_scores(q, w, t, m, oracle.FMT_F32, P, pool32, np.stack([pt, pt]), [n, n], seq=[0, 1])
+    s4, ne4 = orc.index_scores(q, w, t, m, oracle.FMT_FP4, P, pool4, np.stack([pt, pt]), [n, n], seq=[0, 1])
+    assert list(ne32) == list(ne4)
+    np.testing.assert_array_equal(np.nan_to_num(s32, nan=7.0), np.nan_to_num(s4, nan=7.0))
