@@ -17,6 +17,7 @@ from __future__ import annotations
 
 import argparse
 import copy
+import dataclasses
 import hashlib
 import json
 import math
@@ -33,7 +34,10 @@ METRIC = "CSA+HCA attention tokens/s (prefill, decode) at 128K–1M ctx; % HBM/M
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
-WORKLOADS = {"decode_1m": 5, "decode_mixed": 4, "prefill_csa_32k": 2, "prefill_hca_128k": 3, "tiny": 1}
+# workload -> config number, or (config number, overrides): decode_1m_fp4idx is the million-token
+# decode with the indexer keys stored in FP4 (e2m1 + E8M0 per 32 channels) instead of e4m3
+WORKLOADS = {"decode_1m": 5, "decode_mixed": 4, "prefill_csa_32k": 2, "prefill_hca_128k": 3, "tiny": 1,
+             "decode_1m_fp4idx": (5, {"idx": "fp4", "name": "million_decode_b8_fp4idx"})}
 # sources that define each timed kernel (its counter readings go stale when they change)
 KERNEL_SOURCES = {"attend_mx_kernel": ["attend.hip", "common.h", "kernels.h"],
                   "index_scores_fp8_kernel": ["indexer.hip", "common.h", "kernels.h"]}
@@ -52,6 +56,16 @@ def kernel_source_hash(symbol: str) -> str:
 
 
 # ------------------------------------------------------------------ algorithmic work
+def index_key_bytes(cfg):
+    """Bytes of one indexer key in its page: e4m3 codes + fp32 scale, e2m1 codes + one
+    E8M0 byte per 32 channels, or fp32."""
+    return {"e4m3": cfg.cI + 4, "fp4": cfg.cI // 2 + cfg.cI // 32, "f32": 4 * cfg.cI}[cfg.idx]
+
+
+def index_kernel_symbol(cfg, qpw):
+    return f"index_scores_fp8_kernel<{qpw}, {4 if cfg.idx == 'fp4' else 3}>"
+
+
 def decode_work(cfg, pos):
     """Per-step algorithmic bytes / flops of each stage, summed over the batch."""
     D, R, nh = cfg.D, cfg.R, cfg.n_h
@@ -60,7 +74,7 @@ def decode_work(cfg, pos):
     for t in pos:
         ne = t // cfg.m
         nw = min(t + 1, cfg.n_win)
-        w["index_bytes"] += ne * (cfg.cI + 4)
+        w["index_bytes"] += ne * index_key_bytes(cfg)
         w["index_flops"] += 2 * cfg.nI * cfg.cI * ne
         sel = min(ne, cfg.k)
         w["csa_flops"] += 4 * nh * D * (sel + nw)
@@ -235,7 +249,7 @@ def bench_decode(cfg, steps, warmup, replicas, args):
                                      "index_scores": ca.TIMED_INDEX_SCORES}, max(steps, 20))
     fmt = 2 if cfg.kv == "fp8mix" else 1
     roof_of = {   # algorithmic work of one launch (the launch covers the whole batch)
-        "index_scores": ("hbm", work["index_bytes"], "index_scores_fp8_kernel<1>"),
+        "index_scores": ("hbm", work["index_bytes"], index_kernel_symbol(cfg, 1)),
         "csa_attend": ("mfma", work["csa_flops"], f"attend_mx_kernel<{fmt}, 0, true>"),
         "hca_attend": ("mfma", work["hca_flops"], f"attend_mx_kernel<{fmt}, 1, true>"),
     }
@@ -420,7 +434,8 @@ def main():
               "part of this build (see the sharding notes in DESIGN.md).", file=sys.stderr)
         sys.exit(2)
     from long_context_attention_17_amd.configs import CONFIGS
-    cfg = CONFIGS[WORKLOADS[args.workload]]
+    wl = WORKLOADS[args.workload]
+    cfg = CONFIGS[wl] if isinstance(wl, int) else dataclasses.replace(CONFIGS[wl[0]], **wl[1])
     torch.cuda.set_device(0)
     if args.copy_calibration_mib > 0:
         src = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)

@@ -46,7 +46,8 @@ typedef enum {
   CA_F32 = 0,     /* float32 */
   CA_BF16 = 1,    /* bfloat16 */
   CA_FP8MIX = 2,  /* main-KV record: e4m3 content channels + bf16 rotary channels (see ca_cache) */
-  CA_E4M3 = 3     /* indexer-key page: e4m3 codes + one fp32 power-of-two scale per entry */
+  CA_E4M3 = 3,    /* indexer-key page: e4m3 codes + one fp32 power-of-two scale per entry */
+  CA_FP4 = 4      /* indexer-key page: e2m1 codes + one E8M0 scale per 32 channels */
 } ca_format;
 
 /* Thread-local description of the last error (empty string if none). */
@@ -68,6 +69,13 @@ const char* ca_last_error(void);
 /*               zero padding up to a multiple of 128 bytes (640 for 512/64). */
 /*   CA_E4M3   : indexer pages, structure of arrays: page_size*dim codes,     */
 /*               then page_size float32 scales (powers of two).              */
+/*   CA_FP4    : indexer pages (Ch.8: FP4 keys, a 1-byte scale per 32        */
+/*               elements), structure of arrays: page_size*dim/2 bytes of    */
+/*               OCP e2m1 codes (channel 2c in the low nibble of byte c),    */
+/*               then page_size*dim/32 E8M0 bytes (block b of slot i at      */
+/*               i*dim/32 + b; value 2^(byte-127)).  Element = code * scale, */
+/*               the scale the smallest power of two with block max <= 6 *   */
+/*               scale; codes rounded to nearest, ties to even.  dim % 32 == 0*/
 /* A page table entry < 0 or >= n_pages marks a missing page: entries in it  */
 /* are never read (kernels skip them) and never written.                     */
 /* ------------------------------------------------------------------------ */

@@ -16,8 +16,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcsahca.so")
 
-F32, BF16, FP8MIX, E4M3 = 0, 1, 2, 3
-FORMATS = {"f32": F32, "bf16": BF16, "fp8mix": FP8MIX, "e4m3": E4M3}
+F32, BF16, FP8MIX, E4M3, FP4 = 0, 1, 2, 3, 4
+FORMATS = {"f32": F32, "bf16": BF16, "fp8mix": FP8MIX, "e4m3": E4M3, "fp4": FP4}
 
 
 class CAError(RuntimeError):

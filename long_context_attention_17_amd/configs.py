@@ -26,7 +26,7 @@ class Config:
     n_win: int = 128           # window of raw tokens (both layers)
     nI: int = 0                # indexer heads
     cI: int = 0                # indexer head dim
-    idx: str = "e4m3"          # indexer storage: "f32" | "e4m3"
+    idx: str = "e4m3"          # indexer storage: "f32" | "e4m3" | "fp4" (e2m1 + E8M0 scale per 32 channels)
     hca: bool = False
     m_hca: int = 128           # HCA compression ratio
     L: int = 0                 # prefill length

@@ -44,13 +44,16 @@ int ilog2(int x) {
 // Validate a cache descriptor and build its device view.
 int make_view(const ca_cache* c, ca::CacheView* v, const char* what) {
   if (c == nullptr) return fail(CA_ERR_ARG, "%s: cache descriptor is NULL", what);
-  if (c->format < CA_F32 || c->format > CA_E4M3) return fail(CA_ERR_DTYPE, "%s: unknown cache format %d", what, c->format);
+  if (c->format < CA_F32 || c->format > CA_FP4) return fail(CA_ERR_DTYPE, "%s: unknown cache format %d", what, c->format);
   if (c->dim <= 0 || c->dim > 1024) return fail(CA_ERR_UNSUPPORTED, "%s: dim %d outside 1..1024", what, c->dim);
   if (c->rope_dim < 0 || c->rope_dim > c->dim || (c->rope_dim & 1))
     return fail(CA_ERR_ARG, "%s: rope_dim %d must be even and <= dim", what, c->rope_dim);
   if (c->format == CA_FP8MIX && ((c->dim - c->rope_dim) % 64 != 0))
     return fail(CA_ERR_UNSUPPORTED, "%s: fp8-mixed records need (dim - rope_dim) %% 64 == 0", what);
-  if (c->format == CA_E4M3 && c->rope_dim != 0) return fail(CA_ERR_ARG, "%s: indexer pools have rope_dim 0", what);
+  if ((c->format == CA_E4M3 || c->format == CA_FP4) && c->rope_dim != 0)
+    return fail(CA_ERR_ARG, "%s: indexer pools have rope_dim 0", what);
+  if (c->format == CA_FP4 && c->dim % 32 != 0)
+    return fail(CA_ERR_UNSUPPORTED, "%s: FP4 pools need dim %% 32 == 0 (one scale per 32 channels)", what);
   if (!pow2(c->page_size)) return fail(CA_ERR_ARG, "%s: page_size %d must be a power of two", what, c->page_size);
   if (c->n_pages < 0 || c->n_seqs < 0 || c->max_pages < 0) return fail(CA_ERR_ARG, "%s: negative sizes", what);
   if (c->n_pages > 0 && c->pool == nullptr) return fail(CA_ERR_ARG, "%s: pool is NULL", what);
@@ -102,12 +105,12 @@ extern "C" {
 const char* ca_last_error(void) { return g_err; }
 
 int64_t ca_record_stride(int32_t format, int32_t dim, int32_t rope_dim) {
-  if (format < CA_F32 || format > CA_E4M3 || dim <= 0) return -1;
+  if (format < CA_F32 || format > CA_FP4 || dim <= 0 || (format == CA_FP4 && dim % 32 != 0)) return -1;
   return ca::record_stride(format, dim, rope_dim);
 }
 
 int64_t ca_page_bytes(int32_t format, int32_t dim, int32_t rope_dim, int32_t page_size) {
-  if (format < CA_F32 || format > CA_E4M3 || dim <= 0 || page_size <= 0) return -1;
+  if (format < CA_F32 || format > CA_FP4 || dim <= 0 || page_size <= 0 || (format == CA_FP4 && dim % 32 != 0)) return -1;
   return ca::page_bytes(format, dim, rope_dim, page_size);
 }
 
@@ -198,8 +201,8 @@ static int index_common(const ca_index_params* p, const void* qI, const float* w
   if (p == nullptr) return fail(CA_ERR_ARG, "%s: params NULL", what);
   ca::CacheView cv;
   if (int e = make_view(idx_cache, &cv, what)) return e;
-  if (idx_cache->format != CA_F32 && idx_cache->format != CA_E4M3)
-    return fail(CA_ERR_DTYPE, "%s: indexer pool must be F32 or E4M3", what);
+  if (idx_cache->format != CA_F32 && idx_cache->format != CA_E4M3 && idx_cache->format != CA_FP4)
+    return fail(CA_ERR_DTYPE, "%s: indexer pool must be F32, E4M3 or FP4", what);
   if (p->dim != idx_cache->dim) return fail(CA_ERR_ARG, "%s: params dim %d != cache dim %d", what, p->dim, idx_cache->dim);
   if (p->n_heads <= 0 || p->dim <= 0 || p->ratio <= 0 || p->k <= 0) return fail(CA_ERR_ARG, "%s: bad params", what);
   if ((int64_t)p->n_heads * p->dim > 16384) return fail(CA_ERR_UNSUPPORTED, "%s: n_heads*dim > 16384", what);

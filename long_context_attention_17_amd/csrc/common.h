@@ -59,6 +59,33 @@ __device__ __forceinline__ int pow2_exponent(float amax) {
   return f <= 0.875f ? ea - 9 : ea - 8;
 }
 
+// float -> OCP e2m1 (FP4) code: nearest of the magnitudes 0, .5, 1, 1.5, 2, 3,
+// 4, 6 by comparison with the midpoints between them, a midpoint going to the
+// code with mantissa bit 0; saturates to +-6; magnitude 0 is encoded +0.
+__device__ __forceinline__ uint32_t e2m1_encode(float x) {
+  const float a = fabsf(x);
+  const uint32_t c = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+                   : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.0f ? 6u : 7u;
+  return (x < 0.0f && c != 0u) ? (c | 8u) : c;
+}
+
+// e2m1 code -> float, exact.
+__device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
+  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
+  const float v = e == 0u ? 0.5f * (float)m : ldexpf(1.0f + 0.5f * (float)m, (int)e - 1);
+  return (c & 8u) ? -v : v;
+}
+
+// Smallest e with amax <= 6 * 2^e (0 when amax == 0), clamped to the E8M0
+// range [-127, 127]; exact.
+__device__ __forceinline__ int fp4_block_exponent(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  int ea;
+  const float f = frexpf(amax, &ea);    // amax = f * 2^ea, f in [0.5, 1); 6 = 0.75 * 2^3
+  const int e = f <= 0.75f ? ea - 3 : ea - 2;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
 // Two e4m3 codes (bytes 0,1 or, with HI, 2,3 of `word`) -> two floats, exact.
 template <bool HI = false>
 __device__ __forceinline__ f32x2 e4m3x2_to_f32(uint32_t word) {
@@ -81,12 +108,14 @@ __host__ __device__ __forceinline__ int64_t record_stride(int fmt, int D, int R)
       return (raw + 127) / 128 * 128;
     }
     case CA_E4M3: return D;
+    case CA_FP4: return D / 2;
   }
   return -1;
 }
 
 __host__ __device__ __forceinline__ int64_t page_bytes(int fmt, int D, int R, int P) {
   if (fmt == CA_E4M3) return (int64_t)P * D + 4 * (int64_t)P;
+  if (fmt == CA_FP4) return (int64_t)P * (D / 2) + (int64_t)P * (D / 32);
   return (int64_t)P * record_stride(fmt, D, R);
 }
 

@@ -87,6 +87,18 @@ __device__ void store_record(const CacheView& cv, int seq, int64_t i, float x, i
     int e = pow2_exponent(amax);
     page[(int64_t)slot * D + j] = (uint8_t)e4m3_encode(ldexpf(x, -e));
     if (j == 0) ((float*)(page + ((int64_t)D << cv.page_shift)))[slot] = ldexpf(1.0f, e);
+  } else if (cv.fmt == CA_FP4) {
+    // a 32-channel block is half a wavefront (D % 32 == 0): its maximum, the
+    // block exponent, then channel pairs (2c, 2c+1) packed into byte c
+    float amax = act ? fabsf(x) : 0.0f;
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    const int e = fp4_block_exponent(amax);
+    const uint32_t code = e2m1_encode(ldexpf(x, -e));
+    const uint32_t odd = __shfl_xor(code, 1, 64);
+    if (page == nullptr || !act) return;
+    if ((j & 1) == 0) page[(int64_t)slot * (D / 2) + (j >> 1)] = (uint8_t)(code | (odd << 4));
+    if ((j & 31) == 0) page[((int64_t)(D / 2) << cv.page_shift) + (int64_t)slot * (D / 32) + (j >> 5)] = (uint8_t)(e + 127);
   } else if (cv.fmt == CA_BF16) {
     if (page && act) ((uint16_t*)(page + slot * cv.stride))[j] = f32_to_bf16_bits(x);
   } else {

@@ -48,7 +48,7 @@ __global__ void index_scores_generic_kernel(CacheView cv, int nI, int cI, int m,
     int e = pow2_exponent(amax);
     for (int c = lane; c < cI; c += 64) {
       float v = load_act(qI, q_fmt, ((int64_t)r * nI + h) * cI + c);
-      if (cv.fmt == CA_E4M3) {
+      if (cv.fmt == CA_E4M3 || cv.fmt == CA_FP4) {
         uint32_t code = e4m3_encode(ldexpf(v, -e));
         v = ldexpf(e4m3x2_to_f32(code)[0], e);
       }
@@ -73,6 +73,21 @@ __global__ void index_scores_generic_kernel(CacheView cv, int nI, int cI, int m,
           d += qs[h * cI + c] * kv[0] + qs[h * cI + c + 1] * kv[1];
         }
         acc += w[(int64_t)r * nI + h] * fmaxf(d * ks, 0.0f);
+      }
+    } else if (cv.fmt == CA_FP4) {
+      const uint8_t* kp = page + (int64_t)slot * (cI / 2);
+      const uint8_t* sp = page + ((int64_t)(cI / 2) << cv.page_shift) + (int64_t)slot * (cI / 32);
+      for (int h = 0; h < nI; ++h) {
+        float d = 0.0f;
+        for (int b = 0; b < cI / 32; ++b) {
+          float db = 0.0f;
+          for (int c = 32 * b; c < 32 * b + 32; c += 2) {
+            const uint32_t byte = kp[c >> 1];
+            db += qs[h * cI + c] * e2m1_to_f32(byte & 15u) + qs[h * cI + c + 1] * e2m1_to_f32(byte >> 4);
+          }
+          d += ldexpf(db, (int)sp[b] - 127);
+        }
+        acc += w[(int64_t)r * nI + h] * fmaxf(d, 0.0f);
       }
     } else {
       const float* kp = (const float*)(page + slot * cv.stride);
@@ -100,11 +115,17 @@ constexpr int kHistBins = 4096;
 constexpr int kGroupBlocks = 8;          // MFMA blocks of 32 keys per load group (and per buffer)
 
 struct KeyGroup {
-  i32x4 v0[kGroupBlocks], v1[kGroupBlocks];
-  float ks[kGroupBlocks];
+  i32x4 v0[kGroupBlocks], v1[kGroupBlocks];   // e4m3: 32 code bytes; FP4: v0 = 16 code bytes
+  float ks[kGroupBlocks];                      // e4m3: the key's scale
+  int sc[kGroupBlocks];                        // FP4: the E8M0 byte of the lane's 32-channel block
   bool ok[kGroupBlocks];
 };
 
+// Loads of a group of kGroupBlocks MFMA blocks of 32 keys (key = lane % 32 of each).
+// e4m3 pages: lane half h takes the key's code bytes [32h, 32h + 32).  FP4 pages:
+// lane half h takes the bytes [16h, 16h + 16) (channels 32h .. 32h + 31) and the
+// E8M0 byte of block h.
+template <int KF>
 __device__ __forceinline__ void load_key_group(const CacheView& cv, const int* pt_s, int64_t k0, int64_t k1,
                                                int64_t gbase, int lane, KeyGroup& kg) {
   constexpr int cI = 64;
@@ -116,18 +137,31 @@ __device__ __forceinline__ void load_key_group(const CacheView& cv, const int* p
     kg.v0[u] = i32x4{0, 0, 0, 0};
     kg.v1[u] = kg.v0[u];
     kg.ks[u] = 0.0f;
+    kg.sc[u] = 127;
     if (kg.ok[u]) {
       const uint8_t* base = cv.pool + (int64_t)pg * cv.page_bytes;
       const int slot = cv.slot_of(s);
-      const i32x4* kp = (const i32x4*)(base + slot * cI + 32 * (lane >> 5));
-      kg.v0[u] = kp[0];
-      kg.v1[u] = kp[1];
-      kg.ks[u] = ((const float*)(base + (cI << cv.page_shift)))[slot];
+      if constexpr (KF == CA_FP4) {
+        kg.v0[u] = *(const i32x4*)(base + slot * (cI / 2) + 16 * (lane >> 5));
+        kg.sc[u] = base[((cI / 2) << cv.page_shift) + slot * (cI / 32) + (lane >> 5)];
+      } else {
+        const i32x4* kp = (const i32x4*)(base + slot * cI + 32 * (lane >> 5));
+        kg.v0[u] = kp[0];
+        kg.v1[u] = kp[1];
+        kg.ks[u] = ((const float*)(base + (cI << cv.page_shift)))[slot];
+      }
     }
   }
 }
 
-template <int QPW>
+// KF: key page format, CA_E4M3 (fp8 x fp8 products, the key's scale applied to
+// the accumulator) or CA_FP4 (fp8 queries x e2m1 keys with the E8M0 block scales
+// applied by the MFMA).  The e2m1 operand of the 32x32x64 MFMA holds, in lane
+// half h, K = 32h .. 32h + 31; the e4m3 operand facing it holds, in lane half h,
+// the 16 bytes of K = 16h .. 16h + 15 then those of K = 32 + 16h .. +15 (layout
+// measured on the device).  e4m3 x e4m3 products only need the same order on
+// both sides, which the plain 32-byte halves give.
+template <int QPW, int KF>
 __global__ void __launch_bounds__(256) index_scores_fp8_kernel(CacheView cv, int m, int q_fmt, const void* qI,
                                                                const float* w, const int32_t* pos, int seq_fixed,
                                                                int n_rows, float* scores, int64_t stride,
@@ -181,12 +215,18 @@ __global__ void __launch_bounds__(256) index_scores_fp8_kernel(CacheView cv, int
   }
   __syncthreads();
 
-  // A operand: row lane%32, bytes [32*(lane/32), +32)
+  // A operand: row lane%32; e4m3 keys: bytes [32*(lane/32), +32); FP4 keys: bytes
+  // [16*(lane/32), +16) then [32 + 16*(lane/32), +16)
   i32x8 a;
   {
-    const int* src = (const int*)(qcodes + (lane & 31) * cI + 32 * (lane >> 5));
+    const uint8_t* qrow = qcodes + (lane & 31) * cI;
+    const int* src0 = (const int*)(qrow + (KF == CA_FP4 ? 16 : 32) * (lane >> 5));
+    const int* src1 = (const int*)(qrow + (KF == CA_FP4 ? 32 + 16 * (lane >> 5) : 32 * (lane >> 5) + 16));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = src[i];
+    for (int i = 0; i < 4; ++i) {
+      a[i] = src0[i];
+      a[4 + i] = src1[i];
+    }
   }
   float wl[QPW][4];
 #pragma unroll
@@ -198,17 +238,20 @@ __global__ void __launch_bounds__(256) index_scores_fp8_kernel(CacheView cv, int
   constexpr int kGroupKeys = 32 * kGroupBlocks;
   constexpr int kGroups = kScoreChunk / 4 / kGroupKeys;  // groups per wave
   KeyGroup cur, nxt;
-  load_key_group(cv, pt_s, k0, k1, wbase, lane, cur);
+  load_key_group<KF>(cv, pt_s, k0, k1, wbase, lane, cur);
   for (int grp = 0; grp < kGroups; ++grp) {
     const int64_t gbase = wbase + kGroupKeys * grp;
     if (gbase >= k1) break;
-    if (grp + 1 < kGroups) load_key_group(cv, pt_s, k0, k1, gbase + kGroupKeys, lane, nxt);
+    if (grp + 1 < kGroups) load_key_group<KF>(cv, pt_s, k0, k1, gbase + kGroupKeys, lane, nxt);
 #pragma unroll
     for (int u = 0; u < kGroupBlocks; ++u) {
       const int64_t s = gbase + 32 * u + (lane & 31);
       const i32x8 bop = __builtin_shufflevector(cur.v0[u], cur.v1[u], 0, 1, 2, 3, 4, 5, 6, 7);
       f32x16 acc = {};
-      acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bop, acc, 0, 0, 0, 127, 0, 127);
+      if constexpr (KF == CA_FP4)
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bop, acc, 0, 4, 0, 127, 0, cur.sc[u]);
+      else
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bop, acc, 0, 0, 0, 127, 0, 127);
       // acc[v]: row 8*(v/4) + 4*(lane/32) + v%4 = (query v/4, head 4*(lane/32) + v%4), key lane%32
 #pragma unroll
       for (int qq = 0; qq < QPW; ++qq) {
@@ -216,7 +259,8 @@ __global__ void __launch_bounds__(256) index_scores_fp8_kernel(CacheView cv, int
 #pragma unroll
         for (int v = 0; v < 4; ++v) part += wl[qq][v] * fmaxf(acc[4 * qq + v], 0.0f);
         part += __shfl_xor(part, 32, 64);
-        if (lane < 32 && s < ne[qq]) scores[(int64_t)(r0 + qq) * stride + s] = cur.ok[u] ? part * cur.ks[u] : -INFINITY;
+        if (lane < 32 && s < ne[qq])
+          scores[(int64_t)(r0 + qq) * stride + s] = cur.ok[u] ? (KF == CA_FP4 ? part : part * cur.ks[u]) : -INFINITY;
       }
     }
     cur = nxt;
@@ -662,24 +706,34 @@ hipError_t launch_index_scores(const CacheView& cv, const ca_index_params& p, co
   const int64_t max_ne = max_pos / p.ratio;
   const bool long_rows = ws_long != nullptr && topk_use_long(stride, p.k);
   uint32_t* state = long_rows ? (uint32_t*)ws_long : nullptr;   // per-row histograms and counters
-  const bool fp8 = max_ne > 0 && cv.fmt == CA_E4M3 && p.n_heads == 8 && p.dim == 64 && cv.page_shift >= 4;
-  if (long_rows && !fp8) {  // (the fp8 scoring kernel clears them itself)
+  const bool mfma = max_ne > 0 && (cv.fmt == CA_E4M3 || cv.fmt == CA_FP4) && p.n_heads == 8 && p.dim == 64 &&
+                   cv.page_shift >= 4;
+  if (long_rows && !mfma) {  // (the MFMA scoring kernel clears them itself)
     const int64_t nz = (int64_t)n_rows * kRowWords;
     hipLaunchKernelGGL(topk_zero_kernel, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, st, state, nz);
   }
   if (max_ne == 0) return hipGetLastError();   // no entries yet: nothing to score
   hipEvent_t ev0, ev1;
   timer_events(CA_TIMED_INDEX_SCORES, st, &ev0, &ev1);
-  if (fp8) {
+  if (mfma) {
     const int64_t chunks = (max_ne + kScoreChunk - 1) / kScoreChunk;
+    const bool fp4 = cv.fmt == CA_FP4;
     if (seq_fixed >= 0) {
       dim3 grid((unsigned)((n_rows + 3) / 4), (unsigned)chunks);
-      CA_LAUNCH(index_scores_fp8_kernel<4>, grid, dim3(256), 0, st, ev0, ev1, cv, p.ratio, p.q_format, qI, w, pos,
-                seq_fixed, n_rows, scores, stride, state, kRowWords);
+      if (fp4)
+        CA_LAUNCH((index_scores_fp8_kernel<4, CA_FP4>), grid, dim3(256), 0, st, ev0, ev1, cv, p.ratio, p.q_format, qI,
+                  w, pos, seq_fixed, n_rows, scores, stride, state, kRowWords);
+      else
+        CA_LAUNCH((index_scores_fp8_kernel<4, CA_E4M3>), grid, dim3(256), 0, st, ev0, ev1, cv, p.ratio, p.q_format,
+                  qI, w, pos, seq_fixed, n_rows, scores, stride, state, kRowWords);
     } else {
       dim3 grid((unsigned)n_rows, (unsigned)chunks);
-      CA_LAUNCH(index_scores_fp8_kernel<1>, grid, dim3(256), 0, st, ev0, ev1, cv, p.ratio, p.q_format, qI, w, pos,
-                seq_fixed, n_rows, scores, stride, state, kRowWords);
+      if (fp4)
+        CA_LAUNCH((index_scores_fp8_kernel<1, CA_FP4>), grid, dim3(256), 0, st, ev0, ev1, cv, p.ratio, p.q_format, qI,
+                  w, pos, seq_fixed, n_rows, scores, stride, state, kRowWords);
+      else
+        CA_LAUNCH((index_scores_fp8_kernel<1, CA_E4M3>), grid, dim3(256), 0, st, ev0, ev1, cv, p.ratio, p.q_format,
+                  qI, w, pos, seq_fixed, n_rows, scores, stride, state, kRowWords);
     }
   } else {
     dim3 grid((unsigned)n_rows, (unsigned)((max_ne + 255) / 256));

@@ -83,12 +83,23 @@ def format_step(fmt: str, ref: np.ndarray, D: int = 0, R: int = 0) -> np.ndarray
         e = pow2_exponents(a.max(-1, keepdims=True))
         rel = np.maximum(a / 2.0 ** e, 2.0 ** -6)
         return 2.0 ** (np.floor(np.log2(rel)) - 3 + e)
+    if fmt == "fp4":
+        # blocks of 32 channels; e2m1 spacing 0.5 below 2, 1 below 4, 2 above
+        step = np.empty_like(a)
+        for b in range(a.shape[-1] // 32):
+            blk = a[..., 32 * b:32 * b + 32]
+            amax = blk.max(-1, keepdims=True)
+            e = np.array([[oracle.fp4_block_exponent(float(x))] for x in amax.reshape(-1)],
+                         np.float64).reshape(amax.shape)
+            rel = blk / 2.0 ** e
+            step[..., 32 * b:32 * b + 32] = np.where(rel < 2, 0.5, np.where(rel < 4, 1.0, 2.0)) * 2.0 ** e
+        return step
     raise ValueError(fmt)
 
 
 def check_stored(gpu_vals, orc_vals, fmt, D=0, R=0, what="entries", max_frac=0.02):
     """Stored entries: every element within one storage step at its magnitude (two for rare
-    fp8 tile-scale flips) plus a few fp32 ulps of its row's largest value, and only a small
+    fp8 / fp4 block-scale flips) plus a few fp32 ulps of its row's largest value, and only a small
     fraction of elements may differ at all."""
     if np.size(orc_vals) == 0:
         return 0.0
@@ -108,7 +119,7 @@ def check_stored(gpu_vals, orc_vals, fmt, D=0, R=0, what="entries", max_frac=0.0
         log(f"  {what}: {int(bad.sum())} elements beyond one step; e.g. " + "; ".join(
             f"{tuple(int(i) for i in w)}: gpu {gpu_vals[tuple(w)]:.8g} oracle {orc_vals[tuple(w)]:.8g} "
             f"step {step[tuple(w)]:.3g}" for w in where))
-    if fmt in ("fp8mix", "e4m3"):
+    if fmt in ("fp8mix", "e4m3", "fp4"):
         assert (diff <= 2.01 * step + 1e-30).all(), f"{what}: {int((diff > 2.01 * step).sum())} elements beyond two format steps"
         assert bad.mean() < 1e-3, f"{what}: {bad.mean():.2e} of elements beyond one format step"
     else:

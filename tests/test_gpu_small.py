@@ -133,6 +133,16 @@ def test_mfma_hca_prefill_bf16_ragged():
     run_hca_prefill(_cfg(L=1500, n_h=128))
 
 
+def test_mfma_csa_prefill_fp4_indexer():
+    """FP4 indexer keys: compressor store, scaled-MFMA scores and top-k against the oracle."""
+    run_csa_prefill(_cfg(name="fp4_idx", idx="fp4", L=777, seed=4343))
+
+
+def test_generic_csa_prefill_fp4_indexer():
+    """FP4 keys on the generic scoring kernel (4 heads x 32 channels: one scale block per key)."""
+    run_csa_prefill(_cfg(name="fp4_idx_generic", idx="fp4", nI=4, cI=32, L=530, seed=4344))
+
+
 def test_generic_path_bf16_small_dim():
     """D = 128 bf16 takes the generic kernels (MFMA path needs D = 512)."""
     run_csa_prefill(_cfg(D=128, R=16, n_h=4, L=300, k=16, n_win=32))
@@ -254,6 +264,12 @@ def run_decode(cfg, seqs=None, check_batch_invariance=True):
 def test_mfma_decode_fp8_small():
     cfg = _cfg(name="small_decode", phase="decode", kv="fp8mix", n_h=128, k=64, B=5, ctx_lo=300, ctx_hi=3000,
                L=0, seed=5151)
+    run_decode(cfg)
+
+
+def test_mfma_decode_fp4_indexer():
+    cfg = _cfg(name="small_decode_fp4", phase="decode", kv="fp8mix", idx="fp4", n_h=64, k=64, B=4, ctx_lo=300,
+               ctx_hi=3000, L=0, seed=5252)
     run_decode(cfg)
 
 

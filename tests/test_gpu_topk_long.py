@@ -12,11 +12,12 @@ from gpu_util import check_topk, f64, gpu_cache_from, log, to_np
 pytestmark = pytest.mark.gpu
 
 
-def _run(ctx, k, dup=None, seed=11):
+def _run(ctx, k, dup=None, seed=11, idx="e4m3"):
     from long_context_attention_17_amd import binding as ca, synth
     from long_context_attention_17_amd.configs import Config
     cfg = Config(name="topk_long", phase="decode", D=512, R=64, n_h=64, act="bf16", kv="fp8mix", m=4, k=k, n_win=128,
-                 nI=8, cI=64, idx="e4m3", B=len(ctx), ctx_lo=min(ctx), ctx_hi=max(ctx), seed=seed)
+                 nI=8, cI=64, idx=idx, B=len(ctx), ctx_lo=min(ctx), ctx_hi=max(ctx), seed=seed)
+    fmt = oracle.FMT_BY_NAME[idx]
     ctx = torch.tensor(ctx, dtype=torch.int64)
     n_e = [int(t) // cfg.m for t in ctx]
     pt, n_pool = synth.page_table([n + 1 for n in n_e], cfg.page, seed)
@@ -26,18 +27,18 @@ def _run(ctx, k, dup=None, seed=11):
         for b in range(len(n_e)):
             a, lo, hi = offs[b], dup[0], min(dup[1], n_e[b])
             keys[a + lo:a + hi] = keys[a + dup[2]]
-    pool = opl.new_pool(n_pool, oracle.FMT_E4M3, cfg.cI, 0, cfg.page)
+    pool = opl.new_pool(n_pool, fmt, cfg.cI, 0, cfg.page)
     for b in range(len(n_e)):
-        oracle.finish_store(oracle.FMT_E4M3, cfg.cI, 0, cfg.page, pool, to_np(pt)[b], 0, f64(keys[offs[b]:offs[b + 1]]),
+        oracle.finish_store(fmt, cfg.cI, 0, cfg.page, pool, to_np(pt)[b], 0, f64(keys[offs[b]:offs[b + 1]]),
                             norm=False, rope=False)
     qI = synth.normal((len(n_e), cfg.nI, cfg.cI), 1 / 8, seed, "qI", "cpu").to(torch.bfloat16)
     w = synth.normal((len(n_e), cfg.nI), 0.35, seed, "w", "cpu").abs()     # positive weights: ties stay ties
     pos = ctx.numpy()
-    qv = opl.indexer_query_values(f64(qI), "e4m3")
-    sc, ne = oracle.index_scores(qv, f64(w), pos, cfg.m, oracle.FMT_E4M3, cfg.page, pool, to_np(pt), n_e,
+    qv = opl.indexer_query_values(f64(qI), idx)
+    sc, ne = oracle.index_scores(qv, f64(w), pos, cfg.m, fmt, cfg.page, pool, to_np(pt), n_e,
                                  seq=np.arange(len(n_e)), n_cols=max(n_e))
     oidx, ocnt = oracle.topk(sc, ne, k)
-    ik = gpu_cache_from(pool, to_np(pt), oracle.FMT_E4M3, cfg.cI, 0, cfg.page)
+    ik = gpu_cache_from(pool, to_np(pt), fmt, cfg.cI, 0, cfg.page)
     from long_context_attention_17_amd import layers
     ip = layers.index_params(cfg)
     B = len(n_e)
@@ -84,3 +85,8 @@ def test_long_rows_small_tie_group():
     tied = [7] + list(range(3000, 3500))
     chosen = [t for t in tied if t in sel]
     assert chosen == tied[:len(chosen)]
+
+
+def test_long_rows_fp4_keys():
+    """FP4 indexer keys (e2m1 + E8M0 scale per 32 channels) through the scaled MFMA and the long top-k."""
+    _run([70000, 123457, 200003], 2048, seed=23, idx="fp4")
