@@ -106,31 +106,34 @@ __global__ void index_scores_generic_kernel(CacheView cv, int nI, int cI, int m,
 // Block: 256 threads (4 waves).  blockIdx.x = group of QPW query rows,
 // blockIdx.y = chunk of kScoreChunk keys (64 pages); wave w owns 1,024
 // consecutive keys (16 pages) as 32 MFMA blocks of 32 keys, processed in groups
-// of kGroupBlocks blocks with a register double buffer: the loads of group g+1
+// of G blocks with a register double buffer: the loads of group g+1
 // are in flight while group g is scored.  The chunk's slice of the page table is
 // staged in LDS once, so key loads never wait on a page-table load.
 constexpr int kScoreChunk = 4096;
 constexpr int kHistBins = 4096;
 
-constexpr int kGroupBlocks = 8;          // MFMA blocks of 32 keys per load group (and per buffer)
+// MFMA blocks of 32 keys per load group (and per buffer), for either key format
+// (16 for FP4 keys measured slower: fewer waves per SIMD)
+template <int KF> constexpr int group_blocks() { return 8; }
 
+template <int G>
 struct KeyGroup {
-  i32x4 v0[kGroupBlocks], v1[kGroupBlocks];   // e4m3: 32 code bytes; FP4: v0 = 16 code bytes
-  float ks[kGroupBlocks];                      // e4m3: the key's scale
-  int sc[kGroupBlocks];                        // FP4: the E8M0 byte of the lane's 32-channel block
-  bool ok[kGroupBlocks];
+  i32x4 v0[G], v1[G];   // e4m3: 32 code bytes; FP4: v0 = 16 code bytes
+  float ks[G];          // e4m3: the key's scale
+  int sc[G];            // FP4: the E8M0 byte of the lane's 32-channel block
+  bool ok[G];
 };
 
-// Loads of a group of kGroupBlocks MFMA blocks of 32 keys (key = lane % 32 of each).
+// Loads of a group of G MFMA blocks of 32 keys (key = lane % 32 of each).
 // e4m3 pages: lane half h takes the key's code bytes [32h, 32h + 32).  FP4 pages:
 // lane half h takes the bytes [16h, 16h + 16) (channels 32h .. 32h + 31) and the
 // E8M0 byte of block h.
-template <int KF>
+template <int KF, int G>
 __device__ __forceinline__ void load_key_group(const CacheView& cv, const int* pt_s, int64_t k0, int64_t k1,
-                                               int64_t gbase, int lane, KeyGroup& kg) {
+                                               int64_t gbase, int lane, KeyGroup<G>& kg) {
   constexpr int cI = 64;
 #pragma unroll
-  for (int u = 0; u < kGroupBlocks; ++u) {
+  for (int u = 0; u < G; ++u) {
     const int64_t s = gbase + 32 * u + (lane & 31);
     const int pg = s < k1 ? pt_s[(int)((s - k0) >> cv.page_shift)] : -1;
     kg.ok[u] = pg >= 0;
@@ -235,16 +238,17 @@ __global__ void __launch_bounds__(256) index_scores_fp8_kernel(CacheView cv, int
     for (int v = 0; v < 4; ++v) wl[qq][v] = wq[qq * nI + 4 * (lane >> 5) + v];
 
   const int64_t wbase = k0 + (kScoreChunk / 4) * wave;
-  constexpr int kGroupKeys = 32 * kGroupBlocks;
+  constexpr int G = group_blocks<KF>();
+  constexpr int kGroupKeys = 32 * G;
   constexpr int kGroups = kScoreChunk / 4 / kGroupKeys;  // groups per wave
-  KeyGroup cur, nxt;
-  load_key_group<KF>(cv, pt_s, k0, k1, wbase, lane, cur);
+  KeyGroup<G> cur, nxt;
+  load_key_group<KF, G>(cv, pt_s, k0, k1, wbase, lane, cur);
   for (int grp = 0; grp < kGroups; ++grp) {
     const int64_t gbase = wbase + kGroupKeys * grp;
     if (gbase >= k1) break;
-    if (grp + 1 < kGroups) load_key_group<KF>(cv, pt_s, k0, k1, gbase + kGroupKeys, lane, nxt);
+    if (grp + 1 < kGroups) load_key_group<KF, G>(cv, pt_s, k0, k1, gbase + kGroupKeys, lane, nxt);
 #pragma unroll
-    for (int u = 0; u < kGroupBlocks; ++u) {
+    for (int u = 0; u < G; ++u) {
       const int64_t s = gbase + 32 * u + (lane & 31);
       const i32x8 bop = __builtin_shufflevector(cur.v0[u], cur.v1[u], 0, 1, 2, 3, 4, 5, 6, 7);
       f32x16 acc = {};
