@@ -66,6 +66,16 @@ def index_kernel_symbol(cfg, qpw):
     return f"index_scores_fp8_kernel<{qpw}, {4 if cfg.idx == 'fp4' else 3}>"
 
 
+def kernel_roofline(bound, units, symbol, launch_ms):
+    """Achieved rate of one timed kernel against its peak (HBM bytes or bf16 MFMA flops)."""
+    if bound == "hbm":
+        achieved, peak, unit = units / (launch_ms / 1e3) / 1e9, PEAK_HBM_GBS, "GB/s"
+    else:
+        achieved, peak, unit = units / (launch_ms / 1e3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+    return {"kernel": symbol, "bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "launch_ms": round(launch_ms, 5), "work_per_launch": units}
+
+
 def decode_work(cfg, pos):
     """Per-step algorithmic bytes / flops of each stage, summed over the batch."""
     D, R, nh = cfg.D, cfg.R, cfg.n_h
@@ -271,6 +281,7 @@ def bench_decode(cfg, steps, warmup, replicas, args):
             "hca_attend": {"bound": "mfma", "achieved_TFLOPs": round(work["hca_flops"] / st["hca_attend"] / 1e9, 2)},
         },
         "kernel_launch_ms": {k: round(v[0], 5) for k, v in kt.items()},
+        "kernel_rooflines": {k: kernel_roofline(*roof_of[k], kt[k][0]) for k in roof_of},
         "kernel_timing_queued": queued,
         "wall_s_timed": round(wall, 4),
         "timing": "whole step: HIP-graph replays (one graph per cache replica); stages: per-stage graphs "
