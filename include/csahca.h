@@ -175,8 +175,9 @@ int ca_window_append(const ca_window_params* p, const void* kv_raw, const float*
 /* "Top-k selection and asymptotic scaling"; Ch.5 "Causal availability").   */
 /* For query row r at position t: for every block s < floor(t/m),           */
 /*   I[r, s] = sum_h w[r, h] * ReLU(qI[r, h, :] . K[s, :])                   */
-/* with K read from the indexer pool.  For CA_E4M3 pools the query is first */
-/* quantized to e4m3 with one power-of-two scale per (row, head), exactly.  */
+/* with K read from the indexer pool.  For CA_E4M3 and CA_FP4 pools the    */
+/* query is first quantized to e4m3 with one power-of-two scale per (row,   */
+/* head), exactly (FP4 pools: fp8 queries x FP4 keys, Ch.8).               */
 /* The min(k, floor(t/m)) blocks with the largest score are kept (ties: the */
 /* lower block index), written ascending to out_idx[r, :], padded with -1;  */
 /* out_cnt[r] is their number.  out_score (optional, [rows, k]) receives    */

@@ -10,7 +10,9 @@
 // padded for decode) and 32 keys per instruction as the B operand; each lane
 // loads 32 contiguous key bytes, so a wavefront streams 2 KB of key codes per
 // instruction.  The head combine (weights, ReLU) and the per-key power-of-two
-// scales are applied to the fp32 accumulators.
+// scales are applied to the fp32 accumulators.  FP4 keys (dsv4 book Ch.8: e2m1
+// with a 1-byte scale per 32 elements) use the same instruction with e2m1 B
+// operands, whose E8M0 block scales the instruction applies itself.
 //
 // Top-k is exact and deterministic: fp32 scores map to order-preserving
 // 32-bit keys (-0 folded onto +0), a 4 x 8-bit radix select finds the k-th
