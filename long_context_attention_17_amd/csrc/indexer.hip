@@ -396,9 +396,10 @@ __global__ void __launch_bounds__(kTopkThreads) topk_rows_kernel(const float* sc
 // spread the scan over many workgroups:
 //   1. histogram of the top 12 key bits per row (LDS histogram per chunk,
 //      nonzero bins added to the row's global histogram with integer atomics, so
-//      the counts are order independent), then one workgroup per row finds the bin
-//      b* holding the k-th largest key and the number of keys above it;
-//   2. every chunk appends its keys with bin >= b* to a per-row candidate list;
+//      the counts are order independent);
+//   2. every chunk finds, from the row's histogram, the bin b* holding the k-th
+//      largest key (and the number of keys above it), then appends its keys with
+//      bin >= b* to a per-row candidate list;
 //   3. one workgroup per row finishes the select among the candidates: two 10-bit
 //      radix passes over the keys in bin b* give the exact threshold key T, then
 //      the kept indices (every key above T, and the lowest-indexed keys equal to
@@ -489,47 +490,43 @@ __global__ void __launch_bounds__(256) topk_hist_kernel(const float* scores, int
     if (h[i]) atomicAdd(&g[i], h[i]);
 }
 
-// One workgroup per row: the threshold bin b* and the count of keys above it.
-__global__ void __launch_bounds__(256) topk_threshold_kernel(const int32_t* pos, int m, int k, int64_t stride,
-                                                             uint32_t* state) {
-  __shared__ uint32_t h[kHistBins];
-  __shared__ uint32_t part[256];
-  const int r = blockIdx.x, tid = threadIdx.x;
-  if (row_len(pos, r, m, stride) <= k) return;
-  uint32_t* g = state + (int64_t)r * kRowWords;
-  for (int i = tid; i < kHistBins; i += blockDim.x) h[i] = g[i];
-  __syncthreads();
-  uint32_t bin, above;
-  threshold_bin(h, k, part, &bin, &above);
-  if (tid == 0) {
-    g[kHistBins + 2] = bin;
-    g[kHistBins + 3] = above;
-  }
-}
-
 __global__ void __launch_bounds__(256) topk_gather_kernel(const float* scores, int64_t stride, const int32_t* pos,
                                                           int m, int k, uint32_t* state, uint32_t* cand_key,
                                                           uint32_t* cand_idx) {
   __shared__ uint32_t part[4];
   __shared__ uint32_t base_s;
+  __shared__ uint32_t hb[kHistBins];
+  __shared__ uint32_t hpart[256];
   const int r = blockIdx.x, tid = threadIdx.x;
   const int64_t n = row_len(pos, r, m, stride);
   const int64_t c0 = (int64_t)blockIdx.y * kChunk;
   if (n <= k || c0 >= n) return;
-  uint32_t* meta = state + (int64_t)r * kRowWords + kHistBins;
-  const uint32_t bstar = meta[2];
+  uint32_t* g = state + (int64_t)r * kRowWords;
+  uint32_t* meta = g + kHistBins;
   const float* row = scores + (int64_t)r * stride;
-  // each thread owns 16 consecutive keys of the chunk
+  // each thread owns 16 consecutive keys of the chunk; their loads go out first
   constexpr int kPer = kChunk / 256;
   const int64_t s0 = c0 + (int64_t)tid * kPer;
   uint32_t keys[kPer];
-  uint32_t mine = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int64_t s = s0 + i;
     keys[i] = s < n ? order_key(row[s]) : 0u;
-    mine += (s < n && (keys[i] >> 20) >= bstar) ? 1u : 0u;
   }
+  // the threshold bin b* of the row, from its histogram (every workgroup of the row
+  // finds the same one; the first also records it, and the count of keys above it,
+  // for the resolve launch)
+  for (int i = tid; i < kHistBins; i += 256) hb[i] = g[i];
+  __syncthreads();
+  uint32_t bstar, above;
+  threshold_bin(hb, k, hpart, &bstar, &above);
+  if (blockIdx.y == 0 && tid == 0) {
+    meta[2] = bstar;
+    meta[3] = above;
+  }
+  uint32_t mine = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) mine += (s0 + i < n && (keys[i] >> 20) >= bstar) ? 1u : 0u;
   // block-wide exclusive prefix of the per-thread counts, one reservation per block
   const int lane = tid & 63, wave = tid >> 6;
   uint32_t incl = mine;
@@ -774,8 +771,8 @@ hipError_t launch_topk(const float* scores, int64_t stride, const int32_t* pos, 
     uint32_t* cand_key = state + (int64_t)n_rows * kRowWords;
     uint32_t* cand_idx = cand_key + (int64_t)n_rows * stride;
     uint32_t* bm = cand_idx + (int64_t)n_rows * stride;
-    // the histogram was made by the scoring launch (see launch_index_scores)
-    hipLaunchKernelGGL(topk_threshold_kernel, dim3(n_rows), dim3(256), 0, st, pos, m, k, stride, state);
+    // the histogram was made by the scoring launch (see launch_index_scores); the
+    // gather workgroups find the threshold bin from it themselves
     const unsigned chunks = (unsigned)((stride + kChunk - 1) / kChunk);
     hipLaunchKernelGGL(topk_gather_kernel, dim3(n_rows, chunks), dim3(256), 0, st, scores, stride, pos, m, k, state,
                        cand_key, cand_idx);
