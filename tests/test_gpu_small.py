@@ -149,9 +149,9 @@ def test_generic_path_bf16_small_dim():
     run_hca_prefill(_cfg(D=128, R=16, n_h=4, L=300, m_hca=32, n_win=32))
 
 
-def _decode_case(cfg):
+def _decode_case(cfg, ctx=None):
     ca, configs, layers, synth = _ca()
-    ctx = synth.decode_contexts(cfg)
+    ctx = synth.decode_contexts(cfg) if ctx is None else torch.as_tensor(ctx, dtype=torch.int64)
     out = {}
     for layer in ("csa", "hca"):
         inp = synth.decode_layer(cfg, layer, "cuda", ctx)
@@ -159,9 +159,9 @@ def _decode_case(cfg):
     return ctx, out
 
 
-def run_decode(cfg, seqs=None, check_batch_invariance=True):
+def run_decode(cfg, seqs=None, check_batch_invariance=True, ctx=None):
     ca, configs, layers, synth = _ca()
-    ctx, inps = _decode_case(cfg)
+    ctx, inps = _decode_case(cfg, ctx)
     log(f"[decode] {cfg.name} B={cfg.B} ctx={ctx.tolist()[:8]} n_h={cfg.n_h} kv={cfg.kv}")
     results = {}
     for layer in ("csa", "hca"):
@@ -271,6 +271,17 @@ def test_mfma_decode_fp4_indexer():
     cfg = _cfg(name="small_decode_fp4", phase="decode", kv="fp8mix", idx="fp4", n_h=64, k=64, B=4, ctx_lo=300,
                ctx_hi=3000, L=0, seed=5252)
     run_decode(cfg)
+
+
+def test_decode_edge_contexts():
+    """Decode rows at the degenerate positions: the first token (no entries, a one-token
+    window), just before / at / after the first CSA and HCA block, k exactly filled and
+    just exceeded, for fp8 pages with e4m3 and FP4 indexer keys."""
+    ctx = [0, 3, 4, 127, 128, 256, 260, 1000]
+    for idx in ("e4m3", "fp4"):
+        cfg = _cfg(name=f"edge_decode_{idx}", phase="decode", kv="fp8mix", idx=idx, n_h=64, k=64, B=len(ctx),
+                   ctx_lo=min(ctx), ctx_hi=max(ctx), L=0, seed=5353)
+        run_decode(cfg, ctx=ctx)
 
 
 def test_generic_decode_fp32_small():
