@@ -131,10 +131,17 @@ typedef struct ca_compress_params {
 } ca_compress_params;
 
 /* Prefill: rows [L, cache->dim] of Ca, Za (and Cb, Zb when overlap) in
- * in_format; Ba, Bb float32 [ratio, dim]; writes entries 0..floor(L/ratio)-1
- * of sequence `seq`.  Cb, Zb, Bb may be NULL when overlap == 0. */
+ * in_format hold positions t0 .. t0+L-1 of sequence `seq`; Ba, Bb float32
+ * [ratio, dim].  Writes every entry completed by position t0+L-1 whose pooling
+ * window lies inside the rows: entries 0..floor(L/ratio)-1 for t0 = 0; for
+ * t0 > 0 (a prefill that continues a reused prefix, infra transcript: the
+ * compressed entries are reloaded and the tokens of the incomplete tail block
+ * recomputed) entries from ceil(t0/ratio) (+1 when overlapping: entry i also
+ * reads the block before it) on.  So to extend a cache holding entries
+ * < E, pass rows from t0 = ratio*E (HCA) or ratio*(E-1) (CSA, E >= 1).
+ * Cb, Zb, Bb may be NULL when overlap == 0. */
 int ca_compress_prefill(const ca_compress_params* p, const void* Ca, const void* Za, const void* Cb,
-                        const void* Zb, const float* Ba, const float* Bb, const float* gain, int64_t L,
+                        const void* Zb, const float* Ba, const float* Bb, const float* gain, int64_t L, int64_t t0,
                         int32_t seq, const ca_cache* cache, void* stream);
 
 /* Decode (dsv4 book Ch.5 "Decode-time cache state": bounded tail buffers).
@@ -196,11 +203,13 @@ typedef struct ca_index_params {
  * are at most max_pos. */
 size_t ca_index_topk_workspace(const ca_index_params* p, int32_t n_rows, int64_t max_pos);
 
-/* Prefill: rows are positions 0..L-1 of sequence `seq`; qI [L, n_I, c_I],
- * w float32 [L, n_I]. */
-int ca_index_topk_prefill(const ca_index_params* p, const void* qI, const float* w, int64_t L, int32_t seq,
-                          const ca_cache* idx_cache, int32_t* out_idx, int32_t* out_cnt, float* out_score,
-                          float* all_scores, int64_t all_scores_stride, void* ws, size_t ws_bytes, void* stream);
+/* Prefill: rows are positions t0..t0+L-1 of sequence `seq` (t0 > 0: the
+ * continuation of a prefix whose entries the cache already holds); qI
+ * [L, n_I, c_I], w float32 [L, n_I]; workspace sized for max_pos = t0+L-1. */
+int ca_index_topk_prefill(const ca_index_params* p, const void* qI, const float* w, int64_t L, int64_t t0,
+                          int32_t seq, const ca_cache* idx_cache, int32_t* out_idx, int32_t* out_cnt,
+                          float* out_score, float* all_scores, int64_t all_scores_stride, void* ws, size_t ws_bytes,
+                          void* stream);
 
 /* Decode: row b is sequence b at position pos[b] (device int32 [B]);
  * max_pos (host) bounds every pos[b]. */
@@ -243,11 +252,14 @@ typedef struct ca_attend_params {
  * most max_pos; k = top-k for CSA, 0 for HCA; ratio = m or m'. */
 size_t ca_attend_workspace(const ca_attend_params* p, int32_t n_rows, int64_t max_pos, int32_t k, int32_t ratio);
 
-/* CSA prefill: q [L, n_heads, D]; idx [L, k], cnt [L]; window [1, W, D]. */
+/* CSA prefill: rows are positions t0..t0+L-1 of sequence `seq`;
+ * q [L, n_heads, D]; idx [L, k], cnt [L]; window [1, W, D] holding position
+ * p at slot p % W for every p in [max(0, t0-n_win+1), t0+L), so
+ * W >= L + min(t0, n_win-1). */
 int ca_csa_attend_prefill(const ca_attend_params* p, const void* q, const float* q_gain, const ca_cache* kv,
                           int32_t seq, const int32_t* idx, const int32_t* cnt, int32_t k, int32_t ratio,
-                          const void* window, int32_t W, const float* sink, int64_t L, void* out, float* lse,
-                          void* ws, size_t ws_bytes, void* stream);
+                          const void* window, int32_t W, const float* sink, int64_t L, int64_t t0, void* out,
+                          float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* CSA decode: row b is sequence b at position pos[b]; q [B, n_heads, D];
  * idx [B, k], cnt [B]; window ring [B, W, D]; max_pos (host) bounds pos. */
@@ -256,10 +268,11 @@ int ca_csa_attend_decode(const ca_attend_params* p, const void* q, const float* 
                          int32_t B, int64_t max_pos, const void* window, int32_t W, const float* sink, void* out,
                          float* lse, void* ws, size_t ws_bytes, void* stream);
 
-/* HCA prefill: entries 0..floor(t/ratio)-1 of sequence `seq` for row t. */
+/* HCA prefill: rows t = t0..t0+L-1 of sequence `seq` attend entries
+ * 0..floor(t/ratio)-1 and the window (as for CSA prefill). */
 int ca_hca_attend_prefill(const ca_attend_params* p, const void* q, const float* q_gain, const ca_cache* kv,
                           int32_t seq, int32_t ratio, const void* window, int32_t W, const float* sink, int64_t L,
-                          void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+                          int64_t t0, void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* HCA decode: row b is sequence b at position pos[b]. */
 int ca_hca_attend_decode(const ca_attend_params* p, const void* q, const float* q_gain, const ca_cache* kv,

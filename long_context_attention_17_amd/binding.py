@@ -65,22 +65,22 @@ _SIGS = {
     "ca_record_stride": (_I64, [_I32, _I32, _I32]),
     "ca_page_bytes": (_I64, [_I32, _I32, _I32, _I32]),
     "ca_store_entries": (ctypes.c_int, [_PC, _I32, _I64, _I64, _P, _P, _F, _I32, _D, _I32, _P]),
-    "ca_compress_prefill": (ctypes.c_int, [ctypes.POINTER(CompressParams), _P, _P, _P, _P, _P, _P, _P, _I64, _I32,
-                                           _PC, _P]),
+    "ca_compress_prefill": (ctypes.c_int, [ctypes.POINTER(CompressParams), _P, _P, _P, _P, _P, _P, _P, _I64, _I64,
+                                           _I32, _PC, _P]),
     "ca_compress_decode": (ctypes.c_int, [ctypes.POINTER(CompressParams), _P, _P, _I32, _P, _P, _P, _P, _PC, _P]),
     "ca_window_append": (ctypes.c_int, [ctypes.POINTER(WindowParams), _P, _P, _P, _P, _I32, _P, _I32, _I32, _P]),
     "ca_index_topk_workspace": (_SZ, [ctypes.POINTER(IndexParams), _I32, _I64]),
-    "ca_index_topk_prefill": (ctypes.c_int, [ctypes.POINTER(IndexParams), _P, _P, _I64, _I32, _PC, _P, _P, _P, _P,
-                                             _I64, _P, _SZ, _P]),
+    "ca_index_topk_prefill": (ctypes.c_int, [ctypes.POINTER(IndexParams), _P, _P, _I64, _I64, _I32, _PC, _P, _P, _P,
+                                             _P, _I64, _P, _SZ, _P]),
     "ca_index_topk_decode": (ctypes.c_int, [ctypes.POINTER(IndexParams), _P, _P, _P, _I32, _I64, _PC, _P, _P, _P,
                                             _P, _I64, _P, _SZ, _P]),
     "ca_attend_workspace": (_SZ, [ctypes.POINTER(AttendParams), _I32, _I64, _I32, _I32]),
     "ca_csa_attend_prefill": (ctypes.c_int, [ctypes.POINTER(AttendParams), _P, _P, _PC, _I32, _P, _P, _I32, _I32,
-                                             _P, _I32, _P, _I64, _P, _P, _P, _SZ, _P]),
+                                             _P, _I32, _P, _I64, _I64, _P, _P, _P, _SZ, _P]),
     "ca_csa_attend_decode": (ctypes.c_int, [ctypes.POINTER(AttendParams), _P, _P, _PC, _P, _P, _I32, _I32, _P, _I32,
                                             _I64, _P, _I32, _P, _P, _P, _P, _SZ, _P]),
     "ca_hca_attend_prefill": (ctypes.c_int, [ctypes.POINTER(AttendParams), _P, _P, _PC, _I32, _I32, _P, _I32, _P,
-                                             _I64, _P, _P, _P, _SZ, _P]),
+                                             _I64, _I64, _P, _P, _P, _SZ, _P]),
     "ca_hca_attend_decode": (ctypes.c_int, [ctypes.POINTER(AttendParams), _P, _P, _PC, _I32, _P, _I32, _I64, _P,
                                             _I32, _P, _P, _P, _P, _SZ, _P]),
     "ca_timer_start": (ctypes.c_int, [ctypes.c_uint32, _I64]),
@@ -156,9 +156,11 @@ def store_entries(cache: Cache, seq: int, first: int, src: torch.Tensor, gain=No
                                  rope_base, pos_stride, _stream(stream)))
 
 
-def compress_prefill(p: CompressParams, Ca, Za, Cb, Zb, Ba, Bb, gain, L: int, seq: int, cache: Cache, stream=None):
+def compress_prefill(p: CompressParams, Ca, Za, Cb, Zb, Ba, Bb, gain, L: int, seq: int, cache: Cache, stream=None,
+                     t0: int = 0):
+    """Rows hold positions t0..t0+L-1 (t0 > 0: continuing a prefix whose entries the cache holds)."""
     _check(_lib.ca_compress_prefill(ctypes.byref(p), _ptr(Ca), _ptr(Za), _ptr(Cb), _ptr(Zb), _ptr(Ba), _ptr(Bb),
-                                    _ptr(gain), L, seq, cache.ref, _stream(stream)))
+                                    _ptr(gain), L, t0, seq, cache.ref, _stream(stream)))
 
 
 def compress_decode(p: CompressParams, new_rows, pos, tail, Ba, Bb, gain, cache: Cache, stream=None):
@@ -177,12 +179,13 @@ def index_topk_workspace(p: IndexParams, n_rows: int, max_pos: int) -> int:
 
 
 def index_topk_prefill(p: IndexParams, qI, w, seq: int, idx_cache: Cache, out_idx, out_cnt, out_score=None,
-                       all_scores=None, ws=None, stream=None):
+                       all_scores=None, ws=None, stream=None, t0: int = 0):
     L = qI.shape[0]
     if ws is None:
-        ws = torch.empty(max(1, index_topk_workspace(p, L, max(L - 1, 0))), dtype=torch.uint8, device=qI.device)
+        ws = torch.empty(max(1, index_topk_workspace(p, L, max(t0 + L - 1, 0))), dtype=torch.uint8,
+                         device=qI.device)
     st = all_scores.shape[1] if all_scores is not None else 0
-    _check(_lib.ca_index_topk_prefill(ctypes.byref(p), _ptr(qI), _ptr(w), L, seq, idx_cache.ref, _ptr(out_idx),
+    _check(_lib.ca_index_topk_prefill(ctypes.byref(p), _ptr(qI), _ptr(w), L, t0, seq, idx_cache.ref, _ptr(out_idx),
                                       _ptr(out_cnt), _ptr(out_score), _ptr(all_scores), st, _ptr(ws),
                                       0 if ws is None else ws.numel(), _stream(stream)))
 
@@ -203,11 +206,11 @@ def attend_workspace(p: AttendParams, n_rows: int, max_pos: int, k: int, ratio: 
 
 
 def csa_attend_prefill(p: AttendParams, q, q_gain, kv: Cache, seq: int, idx, cnt, ratio: int, window, sink, out,
-                       lse=None, stream=None):
+                       lse=None, stream=None, t0: int = 0):
     L, k = q.shape[0], idx.shape[1]
     _check(_lib.ca_csa_attend_prefill(ctypes.byref(p), _ptr(q), _ptr(q_gain), kv.ref, seq, _ptr(idx), _ptr(cnt), k,
-                                      ratio, _ptr(window), window.shape[1], _ptr(sink), L, _ptr(out), _ptr(lse), None,
-                                      0, _stream(stream)))
+                                      ratio, _ptr(window), window.shape[1], _ptr(sink), L, t0, _ptr(out), _ptr(lse),
+                                      None, 0, _stream(stream)))
 
 
 def csa_attend_decode(p: AttendParams, q, q_gain, kv: Cache, idx, cnt, ratio: int, pos, max_pos: int, window, sink,
@@ -221,10 +224,10 @@ def csa_attend_decode(p: AttendParams, q, q_gain, kv: Cache, idx, cnt, ratio: in
 
 
 def hca_attend_prefill(p: AttendParams, q, q_gain, kv: Cache, seq: int, ratio: int, window, sink, out, lse=None,
-                       stream=None):
+                       stream=None, t0: int = 0):
     L = q.shape[0]
     _check(_lib.ca_hca_attend_prefill(ctypes.byref(p), _ptr(q), _ptr(q_gain), kv.ref, seq, ratio, _ptr(window),
-                                      window.shape[1], _ptr(sink), L, _ptr(out), _ptr(lse), None, 0,
+                                      window.shape[1], _ptr(sink), L, t0, _ptr(out), _ptr(lse), None, 0,
                                       _stream(stream)))
 
 

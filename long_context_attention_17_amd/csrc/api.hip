@@ -140,19 +140,19 @@ static int check_compress(const ca_compress_params* p, const ca_cache* cache, ca
 }
 
 int ca_compress_prefill(const ca_compress_params* p, const void* Ca, const void* Za, const void* Cb,
-                        const void* Zb, const float* Ba, const float* Bb, const float* gain, int64_t L,
+                        const void* Zb, const float* Ba, const float* Bb, const float* gain, int64_t L, int64_t t0,
                         int32_t seq, const ca_cache* cache, void* stream) {
   ca::CacheView cv;
   if (int e = check_compress(p, cache, &cv, "ca_compress_prefill")) return e;
-  if (L < 0) return fail(CA_ERR_ARG, "ca_compress_prefill: negative L");
-  if (L / p->ratio == 0) return ok();
+  if (L < 0 || t0 < 0 || t0 + L > 0x7FFFFFFF) return fail(CA_ERR_ARG, "ca_compress_prefill: bad L / t0");
+  if ((t0 + L) / p->ratio <= ca::compress_first_entry(p->ratio, p->overlap, t0)) return ok();
   if (!Ca || !Za || !Ba) return fail(CA_ERR_ARG, "ca_compress_prefill: Ca/Za/Ba NULL");
   if (p->overlap && (!Cb || !Zb || !Bb)) return fail(CA_ERR_ARG, "ca_compress_prefill: Cb/Zb/Bb NULL with overlap");
   if (p->apply_norm && !gain) return fail(CA_ERR_ARG, "ca_compress_prefill: gain NULL with apply_norm");
   if (seq < 0 || seq >= cache->n_seqs) return fail(CA_ERR_ARG, "ca_compress_prefill: seq out of range");
-  if (L / p->ratio > (int64_t)cache->max_pages * cache->page_size)
-    return fail(CA_ERR_ARG, "ca_compress_prefill: page table holds fewer than L/ratio entries");
-  return hip_status(ca::launch_compress_prefill(cv, seq, *p, Ca, Za, Cb, Zb, Ba, Bb, gain, L, S(stream)),
+  if ((t0 + L) / p->ratio > (int64_t)cache->max_pages * cache->page_size)
+    return fail(CA_ERR_ARG, "ca_compress_prefill: page table holds fewer than (t0+L)/ratio entries");
+  return hip_status(ca::launch_compress_prefill(cv, seq, *p, Ca, Za, Cb, Zb, Ba, Bb, gain, L, t0, S(stream)),
                     "ca_compress_prefill");
 }
 
@@ -194,7 +194,8 @@ size_t ca_index_topk_workspace(const ca_index_params* p, int32_t n_rows, int64_t
   return bytes;
 }
 
-static int index_common(const ca_index_params* p, const void* qI, const float* w, const int32_t* pos, int seq_fixed,
+static int index_common(const ca_index_params* p, const void* qI, const float* w, const int32_t* pos, int64_t t0,
+                        int seq_fixed,
                         int64_t n_rows, int64_t max_pos, const ca_cache* idx_cache, int32_t* out_idx,
                         int32_t* out_cnt, float* out_score, float* all_scores, int64_t all_stride, void* ws,
                         size_t ws_bytes, void* stream, const char* what) {
@@ -232,19 +233,22 @@ static int index_common(const ca_index_params* p, const void* qI, const float* w
     if (ca::topk_use_long(stride, p->k))
       ws_long = (char*)ws + align256((size_t)n_rows * stride * sizeof(float));
   }
-  hipError_t e = ca::launch_index_scores(cv, *p, qI, w, pos, seq_fixed, (int)n_rows, max_pos, scores, stride,
+  const ca::RowPos rp{pos, (int)t0};
+  hipError_t e = ca::launch_index_scores(cv, *p, qI, w, rp, seq_fixed, (int)n_rows, max_pos, scores, stride,
                                          ws_long, S(stream));
   if (e != hipSuccess) return hip_status(e, what);
-  e = ca::launch_topk(scores, stride, pos, p->ratio, p->k, (int)n_rows, out_idx, out_cnt, out_score, ws_long,
+  e = ca::launch_topk(scores, stride, rp, p->ratio, p->k, (int)n_rows, out_idx, out_cnt, out_score, ws_long,
                       S(stream));
   return hip_status(e, what);
 }
 
-int ca_index_topk_prefill(const ca_index_params* p, const void* qI, const float* w, int64_t L, int32_t seq,
-                          const ca_cache* idx_cache, int32_t* out_idx, int32_t* out_cnt, float* out_score,
-                          float* all_scores, int64_t all_scores_stride, void* ws, size_t ws_bytes, void* stream) {
+int ca_index_topk_prefill(const ca_index_params* p, const void* qI, const float* w, int64_t L, int64_t t0,
+                          int32_t seq, const ca_cache* idx_cache, int32_t* out_idx, int32_t* out_cnt,
+                          float* out_score, float* all_scores, int64_t all_scores_stride, void* ws, size_t ws_bytes,
+                          void* stream) {
   if (idx_cache && (seq < 0 || seq >= idx_cache->n_seqs)) return fail(CA_ERR_ARG, "ca_index_topk_prefill: seq out of range");
-  return index_common(p, qI, w, nullptr, seq, L, L > 0 ? L - 1 : 0, idx_cache, out_idx, out_cnt, out_score,
+  if (t0 < 0 || L < 0 || t0 + L > 0x7FFFFFFF) return fail(CA_ERR_ARG, "ca_index_topk_prefill: bad L / t0");
+  return index_common(p, qI, w, nullptr, t0, seq, L, L > 0 ? t0 + L - 1 : 0, idx_cache, out_idx, out_cnt, out_score,
                       all_scores, all_scores_stride, ws, ws_bytes, stream, "ca_index_topk_prefill");
 }
 
@@ -255,7 +259,7 @@ int ca_index_topk_decode(const ca_index_params* p, const void* qI, const float* 
   if (pos == nullptr && B > 0) return fail(CA_ERR_ARG, "ca_index_topk_decode: pos NULL");
   if (idx_cache && B > idx_cache->n_seqs) return fail(CA_ERR_ARG, "ca_index_topk_decode: B exceeds page table rows");
   if (max_pos < 0) return fail(CA_ERR_ARG, "ca_index_topk_decode: negative max_pos");
-  return index_common(p, qI, w, pos, -1, B, max_pos, idx_cache, out_idx, out_cnt, out_score, all_scores,
+  return index_common(p, qI, w, pos, 0, -1, B, max_pos, idx_cache, out_idx, out_cnt, out_score, all_scores,
                       all_scores_stride, ws, ws_bytes, stream, "ca_index_topk_decode");
 }
 
@@ -272,7 +276,7 @@ size_t ca_attend_workspace(const ca_attend_params* p, int32_t n_rows, int64_t ma
 }
 
 static int attend_common(const ca_attend_params* p, const void* q, const float* q_gain, const ca_cache* kv,
-                         int mode, int seq_fixed, const int32_t* pos, int64_t n_rows, int64_t max_pos,
+                         int mode, int seq_fixed, const int32_t* pos, int64_t t0, int64_t n_rows, int64_t max_pos,
                          const int32_t* idx, const int32_t* cnt, int k, int ratio, const void* window, int W,
                          int win_rows, const float* sink, void* out, float* lse, void* ws, size_t ws_bytes,
                          void* stream, bool decode, const char* what) {
@@ -295,7 +299,9 @@ static int attend_common(const ca_attend_params* p, const void* q, const float* 
   if (!q || !q_gain || !window || !sink || !out) return fail(CA_ERR_ARG, "%s: NULL argument", what);
   if (mode == 0 && (!idx || !cnt)) return fail(CA_ERR_ARG, "%s: idx/cnt NULL", what);
   if (decode && !pos) return fail(CA_ERR_ARG, "%s: pos NULL", what);
-  if (!decode && W < n_rows) return fail(CA_ERR_ARG, "%s: prefill window needs W >= L", what);
+  if (!decode && (t0 < 0 || t0 + n_rows > 0x7FFFFFFF)) return fail(CA_ERR_ARG, "%s: bad L / t0", what);
+  if (!decode && W < n_rows + (t0 < p->n_win - 1 ? t0 : p->n_win - 1))
+    return fail(CA_ERR_ARG, "%s: prefill window needs W >= L + min(t0, n_win - 1)", what);
   if (decode && n_rows > kv->n_seqs) return fail(CA_ERR_ARG, "%s: more rows than page table rows", what);
   if (mode == 1 && max_pos / ratio > (int64_t)kv->max_pages * kv->page_size)
     return fail(CA_ERR_ARG, "%s: page table holds fewer than floor(max_pos/ratio) entries", what);
@@ -312,6 +318,7 @@ static int attend_common(const ca_attend_params* p, const void* q, const float* 
   a.base = p->rope_base;
   a.rope_step = p->rope_dim > 0 ? pow(p->rope_base, -2.0 / (double)p->rope_dim) : 1.0;
   a.pos = pos;
+  a.t0 = (int)t0;
   a.seq_fixed = seq_fixed;
   a.n_rows = (int)n_rows;
   a.mode = mode;
@@ -366,10 +373,10 @@ static int attend_common(const ca_attend_params* p, const void* q, const float* 
 
 int ca_csa_attend_prefill(const ca_attend_params* p, const void* q, const float* q_gain, const ca_cache* kv,
                           int32_t seq, const int32_t* idx, const int32_t* cnt, int32_t k, int32_t ratio,
-                          const void* window, int32_t W, const float* sink, int64_t L, void* out, float* lse,
-                          void* ws, size_t ws_bytes, void* stream) {
+                          const void* window, int32_t W, const float* sink, int64_t L, int64_t t0, void* out,
+                          float* lse, void* ws, size_t ws_bytes, void* stream) {
   if (kv && (seq < 0 || seq >= kv->n_seqs)) return fail(CA_ERR_ARG, "ca_csa_attend_prefill: seq out of range");
-  return attend_common(p, q, q_gain, kv, 0, seq, nullptr, L, L - 1, idx, cnt, k, ratio, window, W, 1, sink, out, lse,
+  return attend_common(p, q, q_gain, kv, 0, seq, nullptr, t0, L, t0 + L - 1, idx, cnt, k, ratio, window, W, 1, sink, out, lse,
                        ws, ws_bytes, stream, false, "ca_csa_attend_prefill");
 }
 
@@ -377,15 +384,15 @@ int ca_csa_attend_decode(const ca_attend_params* p, const void* q, const float* 
                          const int32_t* idx, const int32_t* cnt, int32_t k, int32_t ratio, const int32_t* pos,
                          int32_t B, int64_t max_pos, const void* window, int32_t W, const float* sink, void* out,
                          float* lse, void* ws, size_t ws_bytes, void* stream) {
-  return attend_common(p, q, q_gain, kv, 0, -1, pos, B, max_pos, idx, cnt, k, ratio, window, W, B, sink, out, lse, ws,
+  return attend_common(p, q, q_gain, kv, 0, -1, pos, 0, B, max_pos, idx, cnt, k, ratio, window, W, B, sink, out, lse, ws,
                        ws_bytes, stream, true, "ca_csa_attend_decode");
 }
 
 int ca_hca_attend_prefill(const ca_attend_params* p, const void* q, const float* q_gain, const ca_cache* kv,
                           int32_t seq, int32_t ratio, const void* window, int32_t W, const float* sink, int64_t L,
-                          void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+                          int64_t t0, void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
   if (kv && (seq < 0 || seq >= kv->n_seqs)) return fail(CA_ERR_ARG, "ca_hca_attend_prefill: seq out of range");
-  return attend_common(p, q, q_gain, kv, 1, seq, nullptr, L, L - 1, nullptr, nullptr, 0, ratio, window, W, 1, sink,
+  return attend_common(p, q, q_gain, kv, 1, seq, nullptr, t0, L, t0 + L - 1, nullptr, nullptr, 0, ratio, window, W, 1, sink,
                        out, lse, ws, ws_bytes, stream, false, "ca_hca_attend_prefill");
 }
 
@@ -393,7 +400,7 @@ int ca_hca_attend_decode(const ca_attend_params* p, const void* q, const float* 
                          int32_t ratio, const int32_t* pos, int32_t B, int64_t max_pos, const void* window,
                          int32_t W, const float* sink, void* out, float* lse, void* ws, size_t ws_bytes,
                          void* stream) {
-  return attend_common(p, q, q_gain, kv, 1, -1, pos, B, max_pos, nullptr, nullptr, 0, ratio, window, W, B, sink, out,
+  return attend_common(p, q, q_gain, kv, 1, -1, pos, 0, B, max_pos, nullptr, nullptr, 0, ratio, window, W, B, sink, out,
                        lse, ws, ws_bytes, stream, true, "ca_hca_attend_decode");
 }
 

@@ -31,7 +31,7 @@ struct RowInfo {
 
 __device__ __forceinline__ RowInfo row_info(const AttendArgs& a, int r) {
   RowInfo ri;
-  ri.t = a.pos ? a.pos[r] : r;
+  ri.t = a.pos ? a.pos[r] : a.t0 + r;
   ri.seq = a.seq_fixed >= 0 ? a.seq_fixed : r;
   ri.win_seq = a.seq_fixed >= 0 ? 0 : r;
   int nc;
@@ -745,7 +745,7 @@ __global__ void __launch_bounds__(256) attend_qprep_kernel(AttendArgs a) {
   const int r = blockIdx.x, h = blockIdx.y * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (h >= a.n_heads) return;
   constexpr int CC = kD - kR;
-  const int t = a.pos ? a.pos[r] : r;
+  const int t = a.pos ? a.pos[r] : a.t0 + r;
   const int64_t off = ((int64_t)r * a.n_heads + h) * kD + 8 * lane;
   const u32x4 w = *(const u32x4*)((const uint16_t*)a.q + off);
   float x[8];

@@ -119,6 +119,15 @@ __host__ __device__ __forceinline__ int64_t page_bytes(int fmt, int D, int R, in
   return (int64_t)P * record_stride(fmt, D, R);
 }
 
+// First entry a prefill whose rows start at position t0 emits: the first whose
+// pooling window (m rows, plus the m rows before them when overlapping, except
+// for entry 0) lies at or after t0.
+__host__ __device__ __forceinline__ int64_t compress_first_entry(int m, int overlap, int64_t t0) {
+  if (t0 <= 0) return 0;
+  const int64_t a = (t0 + m - 1) / m;                   // first block starting at or after t0
+  return overlap ? a + 1 : a;
+}
+
 // Device view of a paged pool.
 struct CacheView {
   uint8_t* pool;

@@ -126,20 +126,20 @@ struct Pool1 {
 __global__ void compress_prefill_kernel(CacheView cv, int seq, int m, int overlap, int in_fmt, const void* Ca,
                                         const void* Za, const void* Cb, const void* Zb, const float* Ba,
                                         const float* Bb, const float* gain, float eps, int apply_rope,
-                                        double base) {
+                                        double base, int64_t i0, int64_t t0) {
   __shared__ float red[16];
   const int D = cv.dim, j = threadIdx.x;
-  const int64_t i = blockIdx.x;
+  const int64_t i = i0 + blockIdx.x;                   // entry; row index = position - t0
   float x = 0.0f;
   if (j < D) {
     Pool1 acc;
     for (int t = 0; t < m; ++t) {
-      int64_t row = (int64_t)m * i + t;
+      int64_t row = (int64_t)m * i + t - t0;
       acc.add(load_act(Za, in_fmt, row * D + j) + Ba[t * D + j], load_act(Ca, in_fmt, row * D + j));
     }
     if (overlap && i > 0) {
       for (int t = 0; t < m; ++t) {
-        int64_t row = (int64_t)m * (i - 1) + t;
+        int64_t row = (int64_t)m * (i - 1) + t - t0;
         acc.add(load_act(Zb, in_fmt, row * D + j) + Bb[t * D + j], load_act(Cb, in_fmt, row * D + j));
       }
     }
@@ -217,12 +217,12 @@ static int block_for(int D) { return (D + 63) / 64 * 64; }
 
 hipError_t launch_compress_prefill(const CacheView& cv, int seq, const ca_compress_params& p, const void* Ca,
                                    const void* Za, const void* Cb, const void* Zb, const float* Ba,
-                                   const float* Bb, const float* gain, int64_t L, hipStream_t st) {
-  int64_t n = L / p.ratio;
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(compress_prefill_kernel, dim3((unsigned)n), dim3(block_for(cv.dim)), 0, st, cv, seq, p.ratio,
-                     p.overlap, p.in_format, Ca, Za, Cb, Zb, Ba, Bb, p.apply_norm ? gain : nullptr, p.eps,
-                     p.apply_rope, p.rope_base);
+                                   const float* Bb, const float* gain, int64_t L, int64_t t0, hipStream_t st) {
+  const int64_t i0 = compress_first_entry(p.ratio, p.overlap, t0), i1 = (t0 + L) / p.ratio;
+  if (i1 <= i0) return hipSuccess;
+  hipLaunchKernelGGL(compress_prefill_kernel, dim3((unsigned)(i1 - i0)), dim3(block_for(cv.dim)), 0, st, cv, seq,
+                     p.ratio, p.overlap, p.in_format, Ca, Za, Cb, Zb, Ba, Bb, p.apply_norm ? gain : nullptr, p.eps,
+                     p.apply_rope, p.rope_base, i0, t0);
   return hipGetLastError();
 }
 

@@ -34,11 +34,11 @@ __device__ __forceinline__ uint32_t order_key(float v) {
 // One thread per (row, key).  Query heads for the row sit in LDS (quantized to
 // e4m3 first when the pool is e4m3).
 __global__ void index_scores_generic_kernel(CacheView cv, int nI, int cI, int m, int q_fmt, const void* qI,
-                                            const float* w, const int32_t* pos, int seq_fixed, float* scores,
+                                            const float* w, RowPos pos, int seq_fixed, float* scores,
                                             int64_t stride) {
   extern __shared__ float qs[];                // [nI * cI] query values as the indexer sees them
   const int r = blockIdx.x;
-  const int t = pos ? pos[r] : r;
+  const int t = pos(r);
   const int seq = seq_fixed >= 0 ? seq_fixed : r;
   const int64_t ne = t / m < stride ? t / m : stride;   // never beyond the score row
   for (int h = threadIdx.x >> 6; h < nI; h += blockDim.x >> 6) {
@@ -168,7 +168,7 @@ __device__ __forceinline__ void load_key_group(const CacheView& cv, const int* p
 // both sides, which the plain 32-byte halves give.
 template <int QPW, int KF>
 __global__ void __launch_bounds__(256) index_scores_fp8_kernel(CacheView cv, int m, int q_fmt, const void* qI,
-                                                               const float* w, const int32_t* pos, int seq_fixed,
+                                                               const float* w, RowPos pos, int seq_fixed,
                                                                int n_rows, float* scores, int64_t stride,
                                                                uint32_t* clear, int clear_words) {
   constexpr int nI = 8, cI = 64;
@@ -183,7 +183,7 @@ __global__ void __launch_bounds__(256) index_scores_fp8_kernel(CacheView cv, int
 #pragma unroll
   for (int qq = 0; qq < QPW; ++qq) {
     int r = r0 + qq;
-    int t = r < n_rows ? (pos ? pos[r] : r) : 0;
+    int t = r < n_rows ? pos(r) : 0;
     ne[qq] = r < n_rows ? (t / m < stride ? t / m : stride) : 0;
     ne_max = ne[qq] > ne_max ? ne[qq] : ne_max;
   }
@@ -309,11 +309,11 @@ __device__ __forceinline__ uint32_t block_flag_prefix(bool f, uint32_t* wsum, ui
 }
 
 __global__ void __launch_bounds__(kTopkThreads) topk_rows_kernel(const float* scores, int64_t stride,
-                                                                 const int32_t* pos, int m, int k, int32_t* out_idx,
+                                                                 RowPos pos, int m, int k, int32_t* out_idx,
                                                                  int32_t* out_cnt, float* out_score) {
   __shared__ TopkShared sh;
   const int r = blockIdx.x;
-  const int t = pos ? pos[r] : r;
+  const int t = pos(r);
   const int64_t n = t / m < stride ? t / m : stride;
   const float* row = scores + (int64_t)r * stride;
   int32_t* oi = out_idx + (int64_t)r * k;
@@ -419,8 +419,8 @@ __global__ void topk_zero_kernel(uint32_t* p, int64_t n) {
   if (i < n) p[i] = 0u;
 }
 
-__device__ __forceinline__ int64_t row_len(const int32_t* pos, int r, int m, int64_t stride) {
-  int t = pos ? pos[r] : r;
+__device__ __forceinline__ int64_t row_len(RowPos pos, int r, int m, int64_t stride) {
+  int t = pos(r);
   int64_t n = t / m;
   return n < stride ? n : stride;
 }
@@ -472,7 +472,7 @@ __device__ void threshold_bin(const uint32_t* hb, int k, uint32_t* part, uint32_
   *above = sel_cum;
 }
 
-__global__ void __launch_bounds__(256) topk_hist_kernel(const float* scores, int64_t stride, const int32_t* pos,
+__global__ void __launch_bounds__(256) topk_hist_kernel(const float* scores, int64_t stride, RowPos pos,
                                                         int m, int k, uint32_t* state) {
   __shared__ uint32_t h[kHistBins];
   const int r = blockIdx.x, tid = threadIdx.x;
@@ -490,7 +490,7 @@ __global__ void __launch_bounds__(256) topk_hist_kernel(const float* scores, int
     if (h[i]) atomicAdd(&g[i], h[i]);
 }
 
-__global__ void __launch_bounds__(256) topk_gather_kernel(const float* scores, int64_t stride, const int32_t* pos,
+__global__ void __launch_bounds__(256) topk_gather_kernel(const float* scores, int64_t stride, RowPos pos,
                                                           int m, int k, uint32_t* state, uint32_t* cand_key,
                                                           uint32_t* cand_idx) {
   __shared__ uint32_t part[4];
@@ -590,7 +590,7 @@ __device__ __forceinline__ void select_digit(uint32_t c, uint32_t need, uint32_t
 }
 
 __global__ void __launch_bounds__(kResolveThreads) topk_resolve_kernel(const float* scores, int64_t stride,
-                                                                       const int32_t* pos, int m, int k,
+                                                                       RowPos pos, int m, int k,
                                                                        const uint32_t* state,
                                                                        const uint32_t* cand_key,
                                                                        const uint32_t* cand_idx, uint32_t* bm_ws,
@@ -703,7 +703,7 @@ __global__ void __launch_bounds__(kResolveThreads) topk_resolve_kernel(const flo
 
 // ------------------------------------------------------------------ launchers
 hipError_t launch_index_scores(const CacheView& cv, const ca_index_params& p, const void* qI, const float* w,
-                               const int32_t* pos, int seq_fixed, int n_rows, int64_t max_pos, float* scores,
+                               RowPos pos, int seq_fixed, int n_rows, int64_t max_pos, float* scores,
                                int64_t stride, void* ws_long, hipStream_t st) {
   if (n_rows == 0) return hipSuccess;
   const int64_t max_ne = max_pos / p.ratio;
@@ -763,7 +763,7 @@ size_t topk_long_workspace(int n_rows, int64_t stride) {
 
 bool topk_use_long(int64_t stride, int k) { return stride > kTopkLdsKeys && k <= kSortMax; }
 
-hipError_t launch_topk(const float* scores, int64_t stride, const int32_t* pos, int m, int k, int n_rows,
+hipError_t launch_topk(const float* scores, int64_t stride, RowPos pos, int m, int k, int n_rows,
                        int32_t* out_idx, int32_t* out_cnt, float* out_score, void* ws_long, hipStream_t st) {
   if (n_rows == 0) return hipSuccess;
   if (ws_long != nullptr && topk_use_long(stride, k)) {

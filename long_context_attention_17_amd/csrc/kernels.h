@@ -6,9 +6,11 @@
 
 namespace ca {
 
+// Rows Ca.. hold positions t0 .. t0+L-1; emits the entries whose pooling window lies
+// inside them (see ca_compress_prefill).
 hipError_t launch_compress_prefill(const CacheView& cv, int seq, const ca_compress_params& p, const void* Ca,
                                    const void* Za, const void* Cb, const void* Zb, const float* Ba,
-                                   const float* Bb, const float* gain, int64_t L, hipStream_t st);
+                                   const float* Bb, const float* gain, int64_t L, int64_t t0, hipStream_t st);
 hipError_t launch_compress_decode(const CacheView& cv, const ca_compress_params& p, const void* new_rows,
                                   const int32_t* pos, int B, float* tail, const float* Ba, const float* Bb,
                                   const float* gain, hipStream_t st);
@@ -18,16 +20,23 @@ hipError_t launch_store_entries(const CacheView& cv, int seq, int64_t first, int
 hipError_t launch_window_append(const ca_window_params& p, const void* raw, const float* gain, const int32_t* pos,
                                 const int32_t* seq, int T, void* window, int W, int S, hipStream_t st);
 
+// Position of query row r: pos[r] (decode), or t0 + r (prefill rows of one sequence).
+struct RowPos {
+  const int32_t* pos;
+  int t0;
+  __device__ __forceinline__ int operator()(int r) const { return pos ? pos[r] : t0 + r; }
+};
+
 // Scores of every eligible block.  With ws_long (the multi-workgroup top-k state,
 // used when the rows are long) the per-row key histograms are also cleared and filled.
 hipError_t launch_index_scores(const CacheView& cv, const ca_index_params& p, const void* qI, const float* w,
-                               const int32_t* pos, int seq_fixed, int n_rows, int64_t max_pos, float* scores,
+                               RowPos pos, int seq_fixed, int n_rows, int64_t max_pos, float* scores,
                                int64_t stride, void* ws_long, hipStream_t st);
 // Top-k over score rows.  With ws_long (topk_long_workspace bytes) and rows longer than
 // one workgroup's LDS, the multi-workgroup histogram / gather / resolve path runs.
 size_t topk_long_workspace(int n_rows, int64_t stride);
 bool topk_use_long(int64_t stride, int k);
-hipError_t launch_topk(const float* scores, int64_t stride, const int32_t* pos, int m, int k, int n_rows,
+hipError_t launch_topk(const float* scores, int64_t stride, RowPos pos, int m, int k, int n_rows,
                        int32_t* out_idx, int32_t* out_cnt, float* out_score, void* ws_long, hipStream_t st);
 
 // Everything an attention launch needs (CSA or HCA, prefill or decode).
@@ -39,7 +48,8 @@ struct AttendArgs {
   float eps;
   double base;
   double rope_step;    // base^(-2/R): the rotary frequency of pair p is rope_step^p
-  const int32_t* pos;  // nullptr: position == row (prefill)
+  const int32_t* pos;  // nullptr: position == t0 + row (prefill)
+  int t0;              // position of row 0 when pos == nullptr
   int seq_fixed;       // >= 0: every row is this cache sequence (prefill); < 0: row r is sequence r
   int n_rows;
   CacheView kv;

@@ -53,7 +53,8 @@ def index_cache(cfg: Config, page_table: torch.Tensor, n_pages: int, device="cud
 
 # ------------------------------------------------------------------ prefill
 class CSAPrefill:
-    """CSA prefill of one sequence; each stage can run on its own."""
+    """CSA prefill of one sequence; each stage can run on its own, over all rows or
+    over positions [t0, t1) (continuing a prefix whose entries the cache holds)."""
 
     def __init__(self, cfg, inp: dict, page_table: torch.Tensor, n_pages: int):
         self.cfg = cfg = get(cfg)
@@ -69,24 +70,31 @@ class CSAPrefill:
                               dtype=torch.uint8, device=dev)
         self.ap, self.ip = attend_params(cfg), index_params(cfg)
 
-    def compress(self):
+    def compress(self, t0: int = 0, t1: int | None = None):
+        """Entries whose pooling window lies in rows [t0, t1) (all of them for t0 = 0)."""
         c, i = self.cfg, self.inp
-        ca.compress_prefill(compress_params(c, c.m, True, True), i["Ca"], i["Za"], i["Cb"], i["Zb"], i["Ba"],
-                            i["Bb"], i["g_kv"], self.L, 0, self.kv)
-        ca.compress_prefill(compress_params(c, c.m, True, False), i["ICa"], i["IZa"], i["ICb"], i["IZb"], i["IBa"],
-                            i["IBb"], None, self.L, 0, self.ik)
+        t1 = self.L if t1 is None else t1
+        r = slice(t0, t1)
+        ca.compress_prefill(compress_params(c, c.m, True, True), i["Ca"][r], i["Za"][r], i["Cb"][r], i["Zb"][r],
+                            i["Ba"], i["Bb"], i["g_kv"], t1 - t0, 0, self.kv, t0=t0)
+        ca.compress_prefill(compress_params(c, c.m, True, False), i["ICa"][r], i["IZa"][r], i["ICb"][r], i["IZb"][r],
+                            i["IBa"], i["IBb"], None, t1 - t0, 0, self.ik, t0=t0)
 
-    def window_append(self):
-        ca.window_append(window_params(self.cfg), self.inp["kv_raw"], self.inp["g_w"], self.window)
+    def window_append(self, t0: int = 0, t1: int | None = None):
+        _window_rows(self, t0, t1)
 
-    def index_topk(self, out_score=None, all_scores=None):
-        ca.index_topk_prefill(self.ip, self.inp["qI"], self.inp["w"], 0, self.ik, self.idx, self.cnt, out_score,
-                              all_scores, self.ws if all_scores is None else None)
+    def index_topk(self, out_score=None, all_scores=None, t0: int = 0, t1: int | None = None):
+        t1 = self.L if t1 is None else t1
+        r = slice(t0, t1)
+        ca.index_topk_prefill(self.ip, self.inp["qI"][r], self.inp["w"][r], 0, self.ik, self.idx[r], self.cnt[r],
+                              out_score, all_scores, self.ws if all_scores is None else None, t0=t0)
 
-    def attend(self, idx=None, cnt=None, lse=None):
-        ca.csa_attend_prefill(self.ap, self.inp["q"], self.inp["g_q"], self.kv, 0, self.idx if idx is None else idx,
-                              self.cnt if cnt is None else cnt, self.cfg.m, self.window, self.inp["sink"], self.out,
-                              lse)
+    def attend(self, idx=None, cnt=None, lse=None, t0: int = 0, t1: int | None = None):
+        t1 = self.L if t1 is None else t1
+        r = slice(t0, t1)
+        ca.csa_attend_prefill(self.ap, self.inp["q"][r], self.inp["g_q"], self.kv, 0,
+                              (self.idx if idx is None else idx)[r], (self.cnt if cnt is None else cnt)[r], self.cfg.m,
+                              self.window, self.inp["sink"], self.out[r], lse, t0=t0)
 
     def run(self):
         self.compress()
@@ -94,6 +102,17 @@ class CSAPrefill:
         self.index_topk()
         self.attend()
         return self.out
+
+
+def _window_rows(layer, t0, t1):
+    """Window rows of positions [t0, t1) (all positions by default) into the layer's window."""
+    t1 = layer.L if t1 is None else t1
+    raw = layer.inp["kv_raw"]
+    if t0 == 0 and t1 == layer.L:
+        ca.window_append(window_params(layer.cfg), raw, layer.inp["g_w"], layer.window)
+        return
+    pos = torch.arange(t0, t1, dtype=torch.int32, device=raw.device)
+    ca.window_append(window_params(layer.cfg), raw[t0:t1], layer.inp["g_w"], layer.window, pos=pos)
 
 
 class HCAPrefill:
@@ -106,17 +125,21 @@ class HCAPrefill:
         self.out = torch.empty(self.L, cfg.n_h, cfg.D, dtype=act_dtype(cfg), device=dev)
         self.ap = attend_params(cfg)
 
-    def compress(self):
+    def compress(self, t0: int = 0, t1: int | None = None):
         c, i = self.cfg, self.inp
-        ca.compress_prefill(compress_params(c, c.m_hca, False, True), i["C"], i["Z"], None, None, i["B"], None,
-                            i["g_kv"], self.L, 0, self.kv)
+        t1 = self.L if t1 is None else t1
+        r = slice(t0, t1)
+        ca.compress_prefill(compress_params(c, c.m_hca, False, True), i["C"][r], i["Z"][r], None, None, i["B"], None,
+                            i["g_kv"], t1 - t0, 0, self.kv, t0=t0)
 
-    def window_append(self):
-        ca.window_append(window_params(self.cfg), self.inp["kv_raw"], self.inp["g_w"], self.window)
+    def window_append(self, t0: int = 0, t1: int | None = None):
+        _window_rows(self, t0, t1)
 
-    def attend(self, lse=None):
-        ca.hca_attend_prefill(self.ap, self.inp["q"], self.inp["g_q"], self.kv, 0, self.cfg.m_hca, self.window,
-                              self.inp["sink"], self.out, lse)
+    def attend(self, lse=None, t0: int = 0, t1: int | None = None):
+        t1 = self.L if t1 is None else t1
+        r = slice(t0, t1)
+        ca.hca_attend_prefill(self.ap, self.inp["q"][r], self.inp["g_q"], self.kv, 0, self.cfg.m_hca, self.window,
+                              self.inp["sink"], self.out[r], lse, t0=t0)
 
     def run(self):
         self.compress()

@@ -54,7 +54,7 @@ def test_argument_errors_are_reported_without_launching():
     from long_context_attention_17_amd import binding as ca
     lib = ca.lib()
     p = ca.CompressParams(0, 1, ca.BF16, 1, 1, 1e-6, 1e4)
-    rc = lib.ca_compress_prefill(ctypes.byref(p), None, None, None, None, None, None, None, 16, 0, None, None)
+    rc = lib.ca_compress_prefill(ctypes.byref(p), None, None, None, None, None, None, None, 16, 0, 0, None, None)
     assert rc == -1 and b"cache descriptor is NULL" in lib.ca_last_error()
     cache = ca._Cache(ca.FP8MIX, 500, 64, 64, None, 0, None, 0, 0)
     rc = lib.ca_store_entries(ctypes.byref(cache), 0, 0, 0, None, None, 1e-6, 1, 1e4, 1, None)
@@ -75,8 +75,13 @@ def test_argument_errors_are_reported_without_launching():
     # empty inputs are valid no-ops
     cache = ca._Cache(ca.BF16, 512, 64, 64, None, 0, None, 1, 0)
     p = ca.CompressParams(4, 1, ca.BF16, 1, 1, 1e-6, 1e4)
-    assert lib.ca_compress_prefill(ctypes.byref(p), None, None, None, None, None, None, None, 3, 0,
+    assert lib.ca_compress_prefill(ctypes.byref(p), None, None, None, None, None, None, None, 3, 0, 0,
                                    ctypes.byref(cache), None) == 0
+    # a continuation whose rows complete no new entry is a valid no-op too
+    assert lib.ca_compress_prefill(ctypes.byref(p), None, None, None, None, None, None, None, 3, 5, 0,
+                                   ctypes.byref(cache), None) == 0
+    assert lib.ca_compress_prefill(ctypes.byref(p), None, None, None, None, None, None, None, 3, -1, 0,
+                                   ctypes.byref(cache), None) == -1
 
 
 def test_timer_argument_errors_need_no_device():

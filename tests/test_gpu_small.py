@@ -500,3 +500,45 @@ def test_launch_timer_counts_and_caps_launches():
     # after stop nothing is timed and reads report zero
     hca.attend()
     assert ca.timer_read(ca.TIMED_HCA_ATTEND) == (0.0, 0)
+
+
+def test_prefix_reuse_continues_a_prefill():
+    """A prefill continued from a stored prefix (the pages' prefix reuse: the compressed
+    entries are reloaded, the tokens of the unfinished block and the window are recomputed).
+    The prefix's entries come from a prefill of the prefix alone; the continuation passes
+    rows from the block the first missing entry needs (one block earlier for the CSA
+    overlap) and the window from P - n_win + 1.  Pools, index sets and outputs must equal
+    a one-pass prefill bit for bit, and the oracle within tolerance."""
+    ca, configs, layers, synth = _ca()
+    for idx_fmt, P in (("e4m3", 517), ("fp4", 640)):
+        cfg = _cfg(name=f"prefix_{idx_fmt}", idx=idx_fmt, L=901, k=96, seed=4646)
+        L = cfg.L
+        log(f"[prefix reuse] idx={idx_fmt} L={L} prefix P={P}")
+        for layer in ("csa", "hca"):
+            inp, pt, n_pool = _prefill_case(cfg, layer)
+            Cls = layers.CSAPrefill if layer == "csa" else layers.HCAPrefill
+            full = Cls(cfg, inp, pt.cuda(), n_pool)
+            full.run()
+            cont = Cls(cfg, inp, pt.cuda(), n_pool)
+            cont.compress(0, P)                                # the stored prefix
+            ratio = cfg.m if layer == "csa" else cfg.m_hca
+            E = P // ratio
+            t0 = ratio * max(E - 1, 0) if layer == "csa" else ratio * E
+            cont.compress(t0, L)                               # entries E.. of the continuation
+            cont.window_append(max(0, P - cfg.n_win + 1), L)
+            if layer == "csa":
+                cont.index_topk(t0=P, t1=L)
+            cont.attend(t0=P, t1=L)
+            torch.cuda.synchronize()
+            assert torch.equal(cont.kv.pool, full.kv.pool), f"{layer}: main pool differs"
+            if layer == "csa":
+                assert torch.equal(cont.ik.pool, full.ik.pool), "indexer pool differs"
+                assert torch.equal(cont.idx[P:], full.idx[P:]) and torch.equal(cont.cnt[P:], full.cnt[P:])
+            assert torch.equal(cont.out[P:].view(torch.int16), full.out[P:].view(torch.int16)), f"{layer}: out differs"
+            rows = np.arange(P, L)
+            orc = (opl.csa_prefill if layer == "csa" else opl.hca_prefill)(cfg, inp, to_np(pt)[0], n_pool, rows=rows)
+            if layer == "csa":
+                same = np.array([np.array_equal(to_np(cont.idx)[P + i], orc["idx"][i]) for i in range(L - P)])
+            else:
+                same = np.ones(L - P, bool)
+            check_out(f64(cont.out[P:])[same], orc["out"][same], cfg.act, f"{layer} continuation ({same.sum()} rows)")
