@@ -37,7 +37,11 @@ PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 # workload -> config number, or (config number, overrides): decode_1m_fp4idx is the million-token
 # decode with the indexer keys stored in FP4 (e2m1 + E8M0 per 32 channels) instead of e4m3
 WORKLOADS = {"decode_1m": 5, "decode_mixed": 4, "prefill_csa_32k": 2, "prefill_hca_128k": 3, "tiny": 1,
-             "decode_1m_fp4idx": (5, {"idx": "fp4", "name": "million_decode_b8_fp4idx"})}
+             "decode_1m_fp4idx": (5, {"idx": "fp4", "name": "million_decode_b8_fp4idx"}),
+             # prefills that continue a stored prefix (its entries reloaded; the unfinished block,
+             # the window and the new rows computed)
+             "prefill_csa_32k_after_16k": (2, {"prefix": 16384, "name": "csa_prefill_32k_after_16k_prefix"}),
+             "prefill_hca_128k_after_64k": (3, {"prefix": 65536, "name": "hca_prefill_128k_after_64k_prefix"})}
 # sources that define each timed kernel (its counter readings go stale when they change)
 KERNEL_SOURCES = {"attend_mx_kernel": ["attend.hip", "common.h", "kernels.h"],
                   "index_scores_fp8_kernel": ["indexer.hip", "common.h", "kernels.h"]}
@@ -96,8 +100,9 @@ def decode_work(cfg, pos):
 
 
 def prefill_work(cfg):
+    """Flops of the rows a prefill computes (positions prefix..L-1)."""
     L, D, nh = cfg.L, cfg.D, cfg.n_h
-    t = torch.arange(L, dtype=torch.float64)
+    t = torch.arange(cfg.prefix, L, dtype=torch.float64)
     nw = torch.clamp(t + 1, max=cfg.n_win)
     w = {}
     if cfg.csa:
@@ -310,12 +315,29 @@ def bench_prefill(cfg, steps, warmup, replicas, args):
         pt, n_pool = synth.page_table([cfg.L // cfg.m_hca], cfg.page, cfg.seed)
         objs.append(("hca", layers.HCAPrefill(cfg, inp, pt.cuda(), n_pool)))
 
+    P = cfg.prefix
+
+    def first_row(name):
+        """First projection row a continuation needs: the block the first missing entry pools from."""
+        if P == 0:
+            return 0
+        ratio = cfg.m if name == "csa" else cfg.m_hca
+        E = P // ratio
+        return ratio * max(E - 1, 0) if name == "csa" else ratio * E
+
+    if P > 0:   # the stored prefix: its entries are in the cache before the timed prefill
+        for name, o in objs:
+            o.compress(0, P)
+        torch.cuda.synchronize()
+
     def step(timer=None):
         for name, o in objs:
-            stages = [(f"{name}_compress", o.compress), (f"{name}_window_append", o.window_append)]
+            stages = [(f"{name}_compress", lambda o=o, name=name: o.compress(first_row(name), cfg.L)),
+                      (f"{name}_window_append", lambda o=o: o.window_append(max(0, P - cfg.n_win + 1) if P else 0,
+                                                                           cfg.L))]
             if name == "csa":
-                stages.append(("csa_index_topk", o.index_topk))
-            stages.append((f"{name}_attend", o.attend))
+                stages.append(("csa_index_topk", lambda o=o: o.index_topk(t0=P, t1=cfg.L)))
+            stages.append((f"{name}_attend", lambda o=o: o.attend(t0=P, t1=cfg.L)))
             for sname, fn in stages:
                 timer.run(sname, fn) if timer else fn()
 
@@ -337,7 +359,7 @@ def bench_prefill(cfg, steps, warmup, replicas, args):
     torch.cuda.synchronize()
     st = timer.means_ms()
     work = prefill_work(cfg)
-    value = cfg.L / (ms_step / 1e3)
+    value = (cfg.L - P) / (ms_step / 1e3)
     # per-kernel launch durations (library-recorded HIP events) and the dominant kernel's roofline
     from long_context_attention_17_amd import binding as ca
     progress("kernel timing")
@@ -359,8 +381,11 @@ def bench_prefill(cfg, steps, warmup, replicas, args):
              "kernel_launch_ms": {k: round(v[0], 5) for k, v in kt.items()}, "kernel_timing_queued": queued,
              "wall_s_timed": round(wall, 4), "algorithmic_flops": work}
     config = {"workload": f"{cfg.name}: prefill of {'CSA' if cfg.csa else ''}{'+' if cfg.csa and cfg.hca else ''}"
-                          f"{'HCA' if cfg.hca else ''}, L={cfg.L}, {cfg.n_h} heads, D={cfg.D}, kv {cfg.kv}",
+                          f"{'HCA' if cfg.hca else ''}, L={cfg.L}, {cfg.n_h} heads, D={cfg.D}, kv {cfg.kv}"
+                          + (f", continuing a stored prefix of {P} tokens (rows {P}..{cfg.L - 1})" if P else ""),
               "seq_len": cfg.L}
+    if P:
+        config["prefix"] = P
     return value, ms_step, config, roof, extra, objs
 
 

@@ -37,6 +37,8 @@ class Config:
     eps: float = 1e-6
     rope_base: float = 10000.0
     seed: int = 0
+    prefix: int = 0            # prefill only: positions 0..prefix-1 are a stored prefix (their entries are
+                               # in the cache); the prefill computes positions prefix..L-1
     notes: str = field(default="", compare=False)
 
 
