@@ -149,19 +149,21 @@ def test_generic_path_bf16_small_dim():
     run_hca_prefill(_cfg(D=128, R=16, n_h=4, L=300, m_hca=32, n_win=32))
 
 
-def _decode_case(cfg, ctx=None):
+def _decode_case(cfg, ctx=None, mutate=None):
     ca, configs, layers, synth = _ca()
     ctx = synth.decode_contexts(cfg) if ctx is None else torch.as_tensor(ctx, dtype=torch.int64)
     out = {}
     for layer in ("csa", "hca"):
         inp = synth.decode_layer(cfg, layer, "cuda", ctx)
+        if mutate is not None:
+            mutate(layer, inp)
         out[layer] = inp
     return ctx, out
 
 
-def run_decode(cfg, seqs=None, check_batch_invariance=True, ctx=None):
+def run_decode(cfg, seqs=None, check_batch_invariance=True, ctx=None, mutate=None):
     ca, configs, layers, synth = _ca()
-    ctx, inps = _decode_case(cfg, ctx)
+    ctx, inps = _decode_case(cfg, ctx, mutate)
     log(f"[decode] {cfg.name} B={cfg.B} ctx={ctx.tolist()[:8]} n_h={cfg.n_h} kv={cfg.kv}")
     results = {}
     for layer in ("csa", "hca"):
@@ -542,3 +544,54 @@ def test_prefix_reuse_continues_a_prefill():
             else:
                 same = np.ones(L - P, bool)
             check_out(f64(cont.out[P:])[same], orc["out"][same], cfg.act, f"{layer} continuation ({same.sum()} rows)")
+
+
+def test_sharp_needles_decode():
+    """The sharp parity variant: per sequence 16 planted needle entries whose indexer keys
+    point along the query of the head with the largest weight (clear top-k winners) plus 4
+    exact duplicates of a weaker needle that straddle the top-k boundary (k = 18: the two
+    lowest-indexed duplicates must win), and one main entry whose content channels point
+    along head 0's query, so that head 0 puts most of its mass on it."""
+    cfg = _cfg(name="sharp", phase="decode", kv="fp8mix", idx="e4m3", n_h=64, k=18, B=4, ctx_lo=2000, ctx_hi=6000,
+               L=0, seed=6161)
+    CC = cfg.D - cfg.R
+    rng = np.random.default_rng(6161)
+    picks = {}
+
+    def mutate(layer, inp):
+        offs, n_ent = inp["entry_offsets"], inp["n_entries"]
+        for b in range(cfg.B):
+            n = n_ent[b]
+            if b not in picks:
+                sel = rng.choice(n, size=20, replace=False)
+                picks[b] = (np.sort(sel[:16]), np.sort(sel[16:]))
+            uniq, dup = picks[b]
+            qc = inp["q"][b, 0, :CC].float()
+            # one dominant entry for head 0 (the compressed layer has far fewer entries)
+            inp["entries"][int(uniq[0]) % n + offs[b], :CC] = 3.0 * qc
+            if layer == "csa":
+                w = inp["w"][b]
+                h = int(torch.argmax(w))
+                w[h] = w[h].abs() + 0.5
+                qi = inp["qI"][b, h].float()
+                inp["ikeys"][torch.as_tensor(uniq + offs[b], device=qi.device)] = 8.0 * qi
+                inp["ikeys"][torch.as_tensor(dup + offs[b], device=qi.device)] = 5.0 * qi
+
+    res = run_decode(cfg, mutate=mutate)
+    gl, st, step = res["csa"]
+    for b in range(cfg.B):
+        uniq, dup = picks[b]
+        want = np.sort(np.concatenate([uniq, np.sort(dup)[:2]]))
+        assert np.array_equal(step["idx"][b, :18], want), f"oracle top-k of seq {b} is not the planted set"
+        assert np.array_equal(to_np(gl.idx)[b, :18], want), f"GPU top-k of seq {b} is not the planted set"
+    # the variant is sharp: head 0's output is (almost) the planted entry's value, i.e. its
+    # attention probability on that entry is far above one half
+    for layer in ("csa", "hca"):
+        gl, st, step = res[layer]
+        for b in range(cfg.B):
+            n = int(st["n_avail"][b])
+            ent = oracle.load_entries(oracle.FMT_BY_NAME[cfg.kv], cfg.D, cfg.R, cfg.page, st["pool"],
+                                      st["page_table"][b], 0, n)
+            v = ent[int(picks[b][0][0]) % n, :CC]
+            frac = float(step["out"][b, 0, :CC] @ v / (v @ v))
+            assert frac > 0.5, f"{layer} seq {b}: planted entry carries {frac:.3f} of head 0's output"
