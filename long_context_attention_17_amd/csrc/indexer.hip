@@ -166,12 +166,17 @@ __device__ __forceinline__ void load_key_group(const CacheView& cv, const int* p
 // the 16 bytes of K = 16h .. 16h + 15 then those of K = 32 + 16h .. +15 (layout
 // measured on the device).  e4m3 x e4m3 products only need the same order on
 // both sides, which the plain 32-byte halves give.
+// hist (QPW == 1 only, else null): the row's long-top-k state, already zeroed;
+// when the row has more than hist_k keys, the workgroup adds the histogram of its
+// chunk's scores (top 12 bits of the order-preserving keys) to it, from an LDS
+// histogram in dynamic shared memory (kHistBins words).
 template <int QPW, int KF>
 __global__ void __launch_bounds__(256) index_scores_fp8_kernel(CacheView cv, int m, int q_fmt, const void* qI,
                                                                const float* w, RowPos pos, int seq_fixed,
                                                                int n_rows, float* scores, int64_t stride,
-                                                               uint32_t* clear, int clear_words) {
+                                                               uint32_t* hist, int hist_words, int hist_k) {
   constexpr int nI = 8, cI = 64;
+  extern __shared__ uint32_t hs[];
   __shared__ __attribute__((aligned(16))) uint8_t qcodes[32 * cI];  // A operand rows: (query, head)
   __shared__ float wq[32];                                          // w * query scale per row
   __shared__ int pt_s[kScoreChunk / 16];                            // page ids of the chunk (>= 64 pages)
@@ -187,11 +192,11 @@ __global__ void __launch_bounds__(256) index_scores_fp8_kernel(CacheView cv, int
     ne[qq] = r < n_rows ? (t / m < stride ? t / m : stride) : 0;
     ne_max = ne[qq] > ne_max ? ne[qq] : ne_max;
   }
-  if (clear != nullptr && blockIdx.y == 0)             // the long top-k's per-row counters (read by later launches)
-    for (int qq = 0; qq < QPW && r0 + qq < n_rows; ++qq)
-      for (int i = threadIdx.x; i < clear_words; i += 256) clear[(int64_t)(r0 + qq) * clear_words + i] = 0u;
   const int64_t k0 = (int64_t)blockIdx.y * kScoreChunk;
   if (k0 >= ne_max) return;                            // uniform over the block
+  const bool want_hist = QPW == 1 && hist != nullptr && ne[0] > hist_k;   // uniform
+  if (want_hist)
+    for (int i = threadIdx.x; i < kHistBins; i += 256) hs[i] = 0u;
   const int64_t k1 = (k0 + kScoreChunk < ne_max) ? k0 + kScoreChunk : ne_max;
   const int seq = seq_fixed >= 0 ? seq_fixed : r0;     // decode: one row per group, row == sequence
 
@@ -265,11 +270,22 @@ __global__ void __launch_bounds__(256) index_scores_fp8_kernel(CacheView cv, int
 #pragma unroll
         for (int v = 0; v < 4; ++v) part += wl[qq][v] * fmaxf(acc[4 * qq + v], 0.0f);
         part += __shfl_xor(part, 32, 64);
-        if (lane < 32 && s < ne[qq])
-          scores[(int64_t)(r0 + qq) * stride + s] = cur.ok[u] ? (KF == CA_FP4 ? part : part * cur.ks[u]) : -INFINITY;
+        if (lane < 32 && s < ne[qq]) {
+          const float sc = cur.ok[u] ? (KF == CA_FP4 ? part : part * cur.ks[u]) : -INFINITY;
+          scores[(int64_t)(r0 + qq) * stride + s] = sc;
+          if (want_hist) atomicAdd(&hs[order_key(sc) >> 20], 1u);
+        }
       }
     }
     cur = nxt;
+  }
+  if (want_hist) {   // the chunk's nonzero bins into the row's histogram (integer adds: order free)
+    __syncthreads();
+    uint32_t* g = hist + (int64_t)r0 * hist_words;
+    for (int i = threadIdx.x; i < kHistBins; i += 256) {
+      const uint32_t c = hs[i];
+      if (c) atomicAdd(&g[i], c);
+    }
   }
 }
 
@@ -396,7 +412,8 @@ __global__ void __launch_bounds__(kTopkThreads) topk_rows_kernel(const float* sc
 // spread the scan over many workgroups:
 //   1. histogram of the top 12 key bits per row (LDS histogram per chunk,
 //      nonzero bins added to the row's global histogram with integer atomics, so
-//      the counts are order independent);
+//      the counts are order independent), made by the scoring kernel itself when
+//      it runs one row per workgroup, else by a pass of its own;
 //   2. every chunk finds, from the row's histogram, the bin b* holding the k-th
 //      largest key (and the number of keys above it), then appends its keys with
 //      bin >= b* to a per-row candidate list;
@@ -711,13 +728,14 @@ hipError_t launch_index_scores(const CacheView& cv, const ca_index_params& p, co
   uint32_t* state = long_rows ? (uint32_t*)ws_long : nullptr;   // per-row histograms and counters
   const bool mfma = max_ne > 0 && (cv.fmt == CA_E4M3 || cv.fmt == CA_FP4) && p.n_heads == 8 && p.dim == 64 &&
                    cv.page_shift >= 4;
-  if (long_rows && !mfma) {  // (the MFMA scoring kernel clears them itself)
+  if (long_rows) {   // cleared before the scoring launch, which may add to the histograms
     const int64_t nz = (int64_t)n_rows * kRowWords;
     hipLaunchKernelGGL(topk_zero_kernel, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, st, state, nz);
   }
   if (max_ne == 0) return hipGetLastError();   // no entries yet: nothing to score
   hipEvent_t ev0, ev1;
   timer_events(CA_TIMED_INDEX_SCORES, st, &ev0, &ev1);
+  bool hist_done = false;   // the one-row-per-workgroup MFMA kernel makes the histogram itself
   if (mfma) {
     const int64_t chunks = (max_ne + kScoreChunk - 1) / kScoreChunk;
     const bool fp4 = cv.fmt == CA_FP4;
@@ -725,18 +743,20 @@ hipError_t launch_index_scores(const CacheView& cv, const ca_index_params& p, co
       dim3 grid((unsigned)((n_rows + 3) / 4), (unsigned)chunks);
       if (fp4)
         CA_LAUNCH((index_scores_fp8_kernel<4, CA_FP4>), grid, dim3(256), 0, st, ev0, ev1, cv, p.ratio, p.q_format, qI,
-                  w, pos, seq_fixed, n_rows, scores, stride, state, kRowWords);
+                  w, pos, seq_fixed, n_rows, scores, stride, nullptr, 0, 0);
       else
         CA_LAUNCH((index_scores_fp8_kernel<4, CA_E4M3>), grid, dim3(256), 0, st, ev0, ev1, cv, p.ratio, p.q_format,
-                  qI, w, pos, seq_fixed, n_rows, scores, stride, state, kRowWords);
+                  qI, w, pos, seq_fixed, n_rows, scores, stride, nullptr, 0, 0);
     } else {
       dim3 grid((unsigned)n_rows, (unsigned)chunks);
+      const size_t lds = state != nullptr ? kHistBins * sizeof(uint32_t) : 0;
       if (fp4)
-        CA_LAUNCH((index_scores_fp8_kernel<1, CA_FP4>), grid, dim3(256), 0, st, ev0, ev1, cv, p.ratio, p.q_format, qI,
-                  w, pos, seq_fixed, n_rows, scores, stride, state, kRowWords);
+        CA_LAUNCH((index_scores_fp8_kernel<1, CA_FP4>), grid, dim3(256), lds, st, ev0, ev1, cv, p.ratio, p.q_format,
+                  qI, w, pos, seq_fixed, n_rows, scores, stride, state, kRowWords, p.k);
       else
-        CA_LAUNCH((index_scores_fp8_kernel<1, CA_E4M3>), grid, dim3(256), 0, st, ev0, ev1, cv, p.ratio, p.q_format,
-                  qI, w, pos, seq_fixed, n_rows, scores, stride, state, kRowWords);
+        CA_LAUNCH((index_scores_fp8_kernel<1, CA_E4M3>), grid, dim3(256), lds, st, ev0, ev1, cv, p.ratio, p.q_format,
+                  qI, w, pos, seq_fixed, n_rows, scores, stride, state, kRowWords, p.k);
+      hist_done = true;
     }
   } else {
     dim3 grid((unsigned)n_rows, (unsigned)((max_ne + 255) / 256));
@@ -744,7 +764,7 @@ hipError_t launch_index_scores(const CacheView& cv, const ca_index_params& p, co
     CA_LAUNCH(index_scores_generic_kernel, grid, dim3(256), sm, st, ev0, ev1, cv, p.n_heads, p.dim, p.ratio,
               p.q_format, qI, w, pos, seq_fixed, scores, stride);
   }
-  if (state != nullptr) {  // histogram of the scores for the long top-k
+  if (state != nullptr && !hist_done) {  // histogram of the scores for the long top-k
     const unsigned chunks = (unsigned)((stride + kChunk - 1) / kChunk);
     hipLaunchKernelGGL(topk_hist_kernel, dim3(n_rows, chunks), dim3(256), 0, st, scores, stride, pos, p.ratio, p.k,
                        state);
