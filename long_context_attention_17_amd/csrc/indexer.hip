@@ -183,6 +183,25 @@ __global__ void __launch_bounds__(256) index_scores_fp8_kernel(CacheView cv, int
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r0 = blockIdx.x * QPW;
 
+  const int seq = seq_fixed >= 0 ? seq_fixed : r0;     // decode: one row per group, row == sequence
+  const int64_t k0 = (int64_t)blockIdx.y * kScoreChunk;
+
+  // The loads that do not depend on the row positions go out first: the chunk's page
+  // ids (one per thread: n_pg <= 256 pages as page_shift >= 4) and the query rows.
+  const int n_pg = kScoreChunk >> cv.page_shift;
+  int pg = -1;
+  if (threadIdx.x < n_pg) {
+    const int64_t pi = (k0 >> cv.page_shift) + threadIdx.x;
+    if (pi < cv.max_pages) pg = cv.page_table[(int64_t)seq * cv.max_pages + pi];
+  }
+  constexpr int kRowsPerWave = 32 / 4;                 // query-head rows (query, head) of each wave
+  float qv[kRowsPerWave];
+#pragma unroll
+  for (int j = 0; j < kRowsPerWave; ++j) {
+    const int row = wave + 4 * j, qq = row / nI, h = row % nI, r = r0 + qq;
+    qv[j] = (qq < QPW && r < n_rows) ? load_act(qI, q_fmt, ((int64_t)r * nI + h) * cI + lane) : 0.0f;
+  }
+
   int64_t ne[QPW];
   int64_t ne_max = 0;
 #pragma unroll
@@ -192,29 +211,19 @@ __global__ void __launch_bounds__(256) index_scores_fp8_kernel(CacheView cv, int
     ne[qq] = r < n_rows ? (t / m < stride ? t / m : stride) : 0;
     ne_max = ne[qq] > ne_max ? ne[qq] : ne_max;
   }
-  const int64_t k0 = (int64_t)blockIdx.y * kScoreChunk;
   if (k0 >= ne_max) return;                            // uniform over the block
   const bool want_hist = QPW == 1 && hist != nullptr && ne[0] > hist_k;   // uniform
   if (want_hist)
     for (int i = threadIdx.x; i < kHistBins; i += 256) hs[i] = 0u;
   const int64_t k1 = (k0 + kScoreChunk < ne_max) ? k0 + kScoreChunk : ne_max;
-  const int seq = seq_fixed >= 0 ? seq_fixed : r0;     // decode: one row per group, row == sequence
 
-  // prologue: the chunk's page ids, and QPW*8 query-head rows quantized to e4m3
-  const int n_pg = kScoreChunk >> cv.page_shift;
-  for (int i = threadIdx.x; i < n_pg; i += 256) {
-    const int64_t pi = (k0 >> cv.page_shift) + i;
-    int pg = -1;
-    if (pi < cv.max_pages) {
-      pg = cv.page_table[(int64_t)seq * cv.max_pages + pi];
-      if (pg >= cv.n_pages) pg = -1;
-    }
-    pt_s[i] = pg;
-  }
-  for (int row = wave; row < 32; row += 4) {
-    const int qq = row / nI, h = row % nI, r = r0 + qq;
+  // prologue: the chunk's page ids into LDS, and QPW*8 query-head rows quantized to e4m3
+  if (threadIdx.x < n_pg) pt_s[threadIdx.x] = pg < cv.n_pages ? pg : -1;
+#pragma unroll
+  for (int j = 0; j < kRowsPerWave; ++j) {
+    const int row = wave + 4 * j, qq = row / nI, h = row % nI, r = r0 + qq;
     if (qq < QPW && r < n_rows) {                      // (uniform) rows past the group's queries stay zero
-      const float v = load_act(qI, q_fmt, ((int64_t)r * nI + h) * cI + lane);
+      const float v = qv[j];
       const int e = pow2_exponent(wave_max(fabsf(v)));
       qcodes[row * cI + lane] = (uint8_t)e4m3_encode(ldexpf(v, -e));
       if (lane == 0) wq[row] = w[(int64_t)r * nI + h] * ldexpf(1.0f, e);
