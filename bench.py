@@ -6,7 +6,10 @@ compressor tail update, lightning indexer + top-k over 262,144 compressed
 entries, gathered attention over 2,048 + 128 items) and one HCA layer step
 (window append, compressor tail update, dense attention over 8,192 + 128
 items).  Other presets: --workload decode_mixed | prefill_csa_32k |
-prefill_hca_128k | tiny.
+prefill_hca_128k | tiny, the million-token decode with FP4 indexer keys
+(decode_1m_fp4idx) or FP4 keys and queries (decode_1m_fp4qk), and prefills
+that continue a stored prefix (prefill_csa_32k_after_16k,
+prefill_hca_128k_after_64k).
 
 Prints ONE JSON line.  Inputs are resident in HBM before the timed region; the
 timed region rotates independent replicas of every cache (so the per-step
@@ -35,16 +38,19 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 # workload -> config number, or (config number, overrides): decode_1m_fp4idx is the million-token
-# decode with the indexer keys stored in FP4 (e2m1 + E8M0 per 32 channels) instead of e4m3
+# decode with the indexer keys stored in FP4 (e2m1 + E8M0 per 32 channels) instead of e4m3, and
+# decode_1m_fp4qk the same with the indexer queries in FP4 too
 WORKLOADS = {"decode_1m": 5, "decode_mixed": 4, "prefill_csa_32k": 2, "prefill_hca_128k": 3, "tiny": 1,
              "decode_1m_fp4idx": (5, {"idx": "fp4", "name": "million_decode_b8_fp4idx"}),
+             "decode_1m_fp4qk": (5, {"idx": "fp4", "idx_q": "fp4", "name": "million_decode_b8_fp4_indexer"}),
              # prefills that continue a stored prefix (its entries reloaded; the unfinished block,
              # the window and the new rows computed)
              "prefill_csa_32k_after_16k": (2, {"prefix": 16384, "name": "csa_prefill_32k_after_16k_prefix"}),
              "prefill_hca_128k_after_64k": (3, {"prefix": 65536, "name": "hca_prefill_128k_after_64k_prefix"})}
 # sources that define each timed kernel (its counter readings go stale when they change)
 KERNEL_SOURCES = {"attend_mx_kernel": ["attend.hip", "common.h", "kernels.h"],
-                  "index_scores_fp8_kernel": ["indexer.hip", "common.h", "kernels.h"]}
+                  "index_scores_fp8_kernel": ["indexer.hip", "common.h", "kernels.h"],
+                  "index_scores_fp4_kernel": ["indexer.hip", "common.h", "kernels.h"]}
 
 
 def progress(msg):
@@ -67,6 +73,8 @@ def index_key_bytes(cfg):
 
 
 def index_kernel_symbol(cfg, qpw):
+    if cfg.idx_q == "fp4":
+        return f"index_scores_fp4_kernel<{qpw}>"
     return f"index_scores_fp8_kernel<{qpw}, {4 if cfg.idx == 'fp4' else 3}>"
 
 

@@ -184,7 +184,11 @@ int ca_window_append(const ca_window_params* p, const void* kv_raw, const float*
 /*   I[r, s] = sum_h w[r, h] * ReLU(qI[r, h, :] . K[s, :])                   */
 /* with K read from the indexer pool.  For CA_E4M3 and CA_FP4 pools the    */
 /* query is first quantized to e4m3 with one power-of-two scale per (row,   */
-/* head), exactly (FP4 pools: fp8 queries x FP4 keys, Ch.8).               */
+/* head), exactly (FP4 pools: fp8 queries x FP4 keys, Ch.8).  With         */
+/* q_quant = CA_FP4 (FP4 pools only) the query is quantized like the keys  */
+/* instead: e2m1 codes rounded to nearest (ties to even) with one E8M0     */
+/* power of two per 32 channels, the smallest that keeps the block maximum  */
+/* within 6 times it (Ch.6 "The lightning indexer": the indexer in FP4).    */
 /* The min(k, floor(t/m)) blocks with the largest score are kept (ties: the */
 /* lower block index), written ascending to out_idx[r, :], padded with -1;  */
 /* out_cnt[r] is their number.  out_score (optional, [rows, k]) receives    */
@@ -197,6 +201,8 @@ typedef struct ca_index_params {
   int32_t ratio;     /* m */
   int32_t k;         /* top-k */
   int32_t q_format;  /* CA_F32 or CA_BF16 storage of qI */
+  int32_t q_quant;   /* 0: e4m3 queries for E4M3 / FP4 pools (none for F32);
+                        CA_FP4: FP4 queries (FP4 pools only; else CA_ERR_ARG) */
 } ca_index_params;
 
 /* Workspace for either indexer call with n_rows query rows whose positions

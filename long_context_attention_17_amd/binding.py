@@ -51,7 +51,8 @@ class WindowParams(ctypes.Structure):
 
 
 class IndexParams(ctypes.Structure):
-    _fields_ = [("n_heads", _I32), ("dim", _I32), ("ratio", _I32), ("k", _I32), ("q_format", _I32)]
+    _fields_ = [("n_heads", _I32), ("dim", _I32), ("ratio", _I32), ("k", _I32), ("q_format", _I32),
+                ("q_quant", _I32)]
 
 
 class AttendParams(ctypes.Structure):

@@ -27,6 +27,7 @@ class Config:
     nI: int = 0                # indexer heads
     cI: int = 0                # indexer head dim
     idx: str = "e4m3"          # indexer storage: "f32" | "e4m3" | "fp4" (e2m1 + E8M0 scale per 32 channels)
+    idx_q: str = "e4m3"        # indexer queries for e4m3 / fp4 keys: "e4m3", or "fp4" (fp4 keys only)
     hca: bool = False
     m_hca: int = 128           # HCA compression ratio
     L: int = 0                 # prefill length
@@ -40,6 +41,10 @@ class Config:
     prefix: int = 0            # prefill only: positions 0..prefix-1 are a stored prefix (their entries are
                                # in the cache); the prefill computes positions prefix..L-1
     notes: str = field(default="", compare=False)
+
+    def __post_init__(self):
+        if self.idx_q not in ("e4m3", "fp4") or (self.idx_q == "fp4" and self.idx != "fp4"):
+            raise ValueError(f"idx_q={self.idx_q!r} with idx={self.idx!r}: fp4 queries need fp4 keys")
 
 
 CONFIGS = {

@@ -208,6 +208,8 @@ static int index_common(const ca_index_params* p, const void* qI, const float* w
   if (p->n_heads <= 0 || p->dim <= 0 || p->ratio <= 0 || p->k <= 0) return fail(CA_ERR_ARG, "%s: bad params", what);
   if ((int64_t)p->n_heads * p->dim > 16384) return fail(CA_ERR_UNSUPPORTED, "%s: n_heads*dim > 16384", what);
   if (!is_act(p->q_format)) return fail(CA_ERR_DTYPE, "%s: q_format must be F32/BF16", what);
+  if (p->q_quant != 0 && !(p->q_quant == CA_FP4 && idx_cache->format == CA_FP4))
+    return fail(CA_ERR_ARG, "%s: q_quant must be 0, or CA_FP4 with an FP4 indexer pool", what);
   if (n_rows < 0 || n_rows > 0x7FFFFFFF) return fail(CA_ERR_ARG, "%s: bad row count", what);
   if (n_rows == 0) return ok();
   if (!qI || !w || !out_idx || !out_cnt) return fail(CA_ERR_ARG, "%s: NULL argument", what);

@@ -31,11 +31,12 @@ __device__ __forceinline__ uint32_t order_key(float v) {
 }
 
 // ------------------------------------------------------------------ scores, generic (fp32 math)
-// One thread per (row, key).  Query heads for the row sit in LDS (quantized to
-// e4m3 first when the pool is e4m3).
+// One thread per (row, key).  Query heads for the row sit in LDS (quantized first
+// when the pool is e4m3 or FP4: to e4m3 per head, or with q_fp4 to FP4 per
+// 32-channel block).
 __global__ void index_scores_generic_kernel(CacheView cv, int nI, int cI, int m, int q_fmt, const void* qI,
                                             const float* w, RowPos pos, int seq_fixed, float* scores,
-                                            int64_t stride) {
+                                            int64_t stride, int q_fp4) {
   extern __shared__ float qs[];                // [nI * cI] query values as the indexer sees them
   const int r = blockIdx.x;
   const int t = pos(r);
@@ -44,6 +45,17 @@ __global__ void index_scores_generic_kernel(CacheView cv, int nI, int cI, int m,
   for (int h = threadIdx.x >> 6; h < nI; h += blockDim.x >> 6) {
     // one wavefront per head: load, optionally quantize exactly like the MFMA path
     int lane = threadIdx.x & 63;
+    if (q_fp4) {   // (uniform) 32-channel blocks are the wavefront's halves (c_I % 32 == 0)
+      for (int c0 = 0; c0 < cI; c0 += 64) {
+        const int c = c0 + lane;
+        const float v = c < cI ? load_act(qI, q_fmt, ((int64_t)r * nI + h) * cI + c) : 0.0f;
+        float bmax = fabsf(v);
+        for (int o = 16; o > 0; o >>= 1) bmax = fmaxf(bmax, __shfl_xor(bmax, o, 64));
+        const int e = fp4_block_exponent(bmax);
+        if (c < cI) qs[h * cI + c] = ldexpf(e2m1_to_f32(e2m1_encode(ldexpf(v, -e))), e);
+      }
+      continue;
+    }
     float amax = 0.0f;
     for (int c = lane; c < cI; c += 64) amax = fmaxf(amax, fabsf(load_act(qI, q_fmt, ((int64_t)r * nI + h) * cI + c)));
     amax = wave_max(amax);
@@ -166,19 +178,25 @@ __device__ __forceinline__ void load_key_group(const CacheView& cv, const int* p
 // the 16 bytes of K = 16h .. 16h + 15 then those of K = 32 + 16h .. +15 (layout
 // measured on the device).  e4m3 x e4m3 products only need the same order on
 // both sides, which the plain 32-byte halves give.
+// QF: query format, CA_E4M3 (one power-of-two scale per (query, head), folded
+// into w) or CA_FP4 (FP4 keys only: e2m1 codes with one E8M0 byte per 32
+// channels, applied by the MFMA as the A scale; an e2m1 A operand holds, in lane
+// half h, K = 32h .. 32h + 31 like the B operand, measured on the device).
 // hist (QPW == 1 only, else null): the row's long-top-k state, already zeroed;
 // when the row has more than hist_k keys, the workgroup adds the histogram of its
 // chunk's scores (top 12 bits of the order-preserving keys) to it, from an LDS
 // histogram in dynamic shared memory (kHistBins words).
-template <int QPW, int KF>
-__global__ void __launch_bounds__(256) index_scores_fp8_kernel(CacheView cv, int m, int q_fmt, const void* qI,
-                                                               const float* w, RowPos pos, int seq_fixed,
-                                                               int n_rows, float* scores, int64_t stride,
-                                                               uint32_t* hist, int hist_words, int hist_k) {
+template <int QPW, int KF, int QF>
+__device__ __forceinline__ void index_scores_mfma(CacheView cv, int m, int q_fmt, const void* qI, const float* w,
+                                                  RowPos pos, int seq_fixed, int n_rows, float* scores,
+                                                  int64_t stride, uint32_t* hist, int hist_words, int hist_k) {
+  static_assert(QF == CA_E4M3 || (QF == CA_FP4 && KF == CA_FP4), "FP4 queries meet FP4 keys");
   constexpr int nI = 8, cI = 64;
+  constexpr int kQBytes = QF == CA_FP4 ? cI / 2 : cI;              // code bytes per query-head row
   extern __shared__ uint32_t hs[];
   __shared__ __attribute__((aligned(16))) uint8_t qcodes[32 * cI];  // A operand rows: (query, head)
-  __shared__ float wq[32];                                          // w * query scale per row
+  __shared__ uint8_t qsc[32][2];                                    // FP4 queries: E8M0 byte per block
+  __shared__ float wq[32];                                          // w (* query scale for e4m3) per row
   __shared__ int pt_s[kScoreChunk / 16];                            // page ids of the chunk (>= 64 pages)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r0 = blockIdx.x * QPW;
@@ -224,20 +242,45 @@ __global__ void __launch_bounds__(256) index_scores_fp8_kernel(CacheView cv, int
     const int row = wave + 4 * j, qq = row / nI, h = row % nI, r = r0 + qq;
     if (qq < QPW && r < n_rows) {                      // (uniform) rows past the group's queries stay zero
       const float v = qv[j];
-      const int e = pow2_exponent(wave_max(fabsf(v)));
-      qcodes[row * cI + lane] = (uint8_t)e4m3_encode(ldexpf(v, -e));
-      if (lane == 0) wq[row] = w[(int64_t)r * nI + h] * ldexpf(1.0f, e);
+      if constexpr (QF == CA_FP4) {
+        // the 32-channel blocks are the wavefront's halves: block maximum, exponent,
+        // then channel pairs (2c, 2c+1) packed into byte c, low nibble first
+        float amax = fabsf(v);
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+        const int e = fp4_block_exponent(amax);
+        const uint32_t code = e2m1_encode(ldexpf(v, -e));
+        const uint32_t odd = __shfl_xor(code, 1, 64);
+        if ((lane & 1) == 0) qcodes[row * kQBytes + (lane >> 1)] = (uint8_t)(code | (odd << 4));
+        if ((lane & 31) == 0) qsc[row][lane >> 5] = (uint8_t)(e + 127);
+        if (lane == 0) wq[row] = w[(int64_t)r * nI + h];
+      } else {
+        const int e = pow2_exponent(wave_max(fabsf(v)));
+        qcodes[row * cI + lane] = (uint8_t)e4m3_encode(ldexpf(v, -e));
+        if (lane == 0) wq[row] = w[(int64_t)r * nI + h] * ldexpf(1.0f, e);
+      }
     } else {
-      qcodes[row * cI + lane] = 0;
+      if (lane < kQBytes) qcodes[row * kQBytes + lane] = 0;
+      if (lane < 2) qsc[row][lane] = 127;
       if (lane == 0) wq[row] = 0.0f;
     }
   }
   __syncthreads();
 
-  // A operand: row lane%32; e4m3 keys: bytes [32*(lane/32), +32); FP4 keys: bytes
-  // [16*(lane/32), +16) then [32 + 16*(lane/32), +16)
+  // A operand: row lane%32.  e4m3 queries, e4m3 keys: bytes [32*(lane/32), +32);
+  // e4m3 queries, FP4 keys: bytes [16*(lane/32), +16) then [32 + 16*(lane/32), +16);
+  // FP4 queries: the 16 code bytes [16*(lane/32), +16) and the block's scale byte
   i32x8 a;
-  {
+  int a_scale = 127;
+  if constexpr (QF == CA_FP4) {
+    const int* src = (const int*)(qcodes + (lane & 31) * kQBytes + 16 * (lane >> 5));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = src[i];
+      a[4 + i] = 0;
+    }
+    a_scale = qsc[lane & 31][lane >> 5];
+  } else {
     const uint8_t* qrow = qcodes + (lane & 31) * cI;
     const int* src0 = (const int*)(qrow + (KF == CA_FP4 ? 16 : 32) * (lane >> 5));
     const int* src1 = (const int*)(qrow + (KF == CA_FP4 ? 32 + 16 * (lane >> 5) : 32 * (lane >> 5) + 16));
@@ -268,7 +311,9 @@ __global__ void __launch_bounds__(256) index_scores_fp8_kernel(CacheView cv, int
       const int64_t s = gbase + 32 * u + (lane & 31);
       const i32x8 bop = __builtin_shufflevector(cur.v0[u], cur.v1[u], 0, 1, 2, 3, 4, 5, 6, 7);
       f32x16 acc = {};
-      if constexpr (KF == CA_FP4)
+      if constexpr (QF == CA_FP4)
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bop, acc, 4, 4, 0, a_scale, 0, cur.sc[u]);
+      else if constexpr (KF == CA_FP4)
         acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bop, acc, 0, 4, 0, 127, 0, cur.sc[u]);
       else
         acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bop, acc, 0, 0, 0, 127, 0, 127);
@@ -296,6 +341,26 @@ __global__ void __launch_bounds__(256) index_scores_fp8_kernel(CacheView cv, int
       if (c) atomicAdd(&g[i], c);
     }
   }
+}
+
+// e4m3 queries against e4m3 or FP4 keys
+template <int QPW, int KF>
+__global__ void __launch_bounds__(256) index_scores_fp8_kernel(CacheView cv, int m, int q_fmt, const void* qI,
+                                                               const float* w, RowPos pos, int seq_fixed,
+                                                               int n_rows, float* scores, int64_t stride,
+                                                               uint32_t* hist, int hist_words, int hist_k) {
+  index_scores_mfma<QPW, KF, CA_E4M3>(cv, m, q_fmt, qI, w, pos, seq_fixed, n_rows, scores, stride, hist, hist_words,
+                                      hist_k);
+}
+
+// FP4 queries against FP4 keys
+template <int QPW>
+__global__ void __launch_bounds__(256) index_scores_fp4_kernel(CacheView cv, int m, int q_fmt, const void* qI,
+                                                               const float* w, RowPos pos, int seq_fixed,
+                                                               int n_rows, float* scores, int64_t stride,
+                                                               uint32_t* hist, int hist_words, int hist_k) {
+  index_scores_mfma<QPW, CA_FP4, CA_FP4>(cv, m, q_fmt, qI, w, pos, seq_fixed, n_rows, scores, stride, hist,
+                                         hist_words, hist_k);
 }
 
 // ------------------------------------------------------------------ top-k
@@ -747,10 +812,13 @@ hipError_t launch_index_scores(const CacheView& cv, const ca_index_params& p, co
   bool hist_done = false;   // the one-row-per-workgroup MFMA kernel makes the histogram itself
   if (mfma) {
     const int64_t chunks = (max_ne + kScoreChunk - 1) / kScoreChunk;
-    const bool fp4 = cv.fmt == CA_FP4;
+    const bool fp4 = cv.fmt == CA_FP4, qfp4 = p.q_quant == CA_FP4;
     if (seq_fixed >= 0) {
       dim3 grid((unsigned)((n_rows + 3) / 4), (unsigned)chunks);
-      if (fp4)
+      if (qfp4)
+        CA_LAUNCH((index_scores_fp4_kernel<4>), grid, dim3(256), 0, st, ev0, ev1, cv, p.ratio, p.q_format, qI, w, pos,
+                  seq_fixed, n_rows, scores, stride, nullptr, 0, 0);
+      else if (fp4)
         CA_LAUNCH((index_scores_fp8_kernel<4, CA_FP4>), grid, dim3(256), 0, st, ev0, ev1, cv, p.ratio, p.q_format, qI,
                   w, pos, seq_fixed, n_rows, scores, stride, nullptr, 0, 0);
       else
@@ -759,7 +827,10 @@ hipError_t launch_index_scores(const CacheView& cv, const ca_index_params& p, co
     } else {
       dim3 grid((unsigned)n_rows, (unsigned)chunks);
       const size_t lds = state != nullptr ? kHistBins * sizeof(uint32_t) : 0;
-      if (fp4)
+      if (qfp4)
+        CA_LAUNCH((index_scores_fp4_kernel<1>), grid, dim3(256), lds, st, ev0, ev1, cv, p.ratio, p.q_format, qI, w,
+                  pos, seq_fixed, n_rows, scores, stride, state, kRowWords, p.k);
+      else if (fp4)
         CA_LAUNCH((index_scores_fp8_kernel<1, CA_FP4>), grid, dim3(256), lds, st, ev0, ev1, cv, p.ratio, p.q_format,
                   qI, w, pos, seq_fixed, n_rows, scores, stride, state, kRowWords, p.k);
       else
@@ -771,7 +842,7 @@ hipError_t launch_index_scores(const CacheView& cv, const ca_index_params& p, co
     dim3 grid((unsigned)n_rows, (unsigned)((max_ne + 255) / 256));
     size_t sm = sizeof(float) * p.n_heads * p.dim;
     CA_LAUNCH(index_scores_generic_kernel, grid, dim3(256), sm, st, ev0, ev1, cv, p.n_heads, p.dim, p.ratio,
-              p.q_format, qI, w, pos, seq_fixed, scores, stride);
+              p.q_format, qI, w, pos, seq_fixed, scores, stride, p.q_quant == CA_FP4 ? 1 : 0);
   }
   if (state != nullptr && !hist_done) {  // histogram of the scores for the long top-k
     const unsigned chunks = (unsigned)((stride + kChunk - 1) / kChunk);

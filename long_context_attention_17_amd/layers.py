@@ -40,7 +40,7 @@ def window_params(cfg: Config) -> ca.WindowParams:
 
 
 def index_params(cfg: Config) -> ca.IndexParams:
-    return ca.IndexParams(cfg.nI, cfg.cI, cfg.m, cfg.k, act_format(cfg))
+    return ca.IndexParams(cfg.nI, cfg.cI, cfg.m, cfg.k, act_format(cfg), ca.FP4 if cfg.idx_q == "fp4" else 0)
 
 
 def main_cache(cfg: Config, page_table: torch.Tensor, n_pages: int, device="cuda") -> ca.Cache:

@@ -15,8 +15,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import (FMT_BY_NAME, FMT_E4M3, FMT_F32, attend, bf16_encode, compress, compress_entry,
-               dequantize_rows_e4m3, finish_store, index_scores, page_bytes, quantize_rows_e4m3,
+from . import (FMT_BY_NAME, FMT_E4M3, FMT_F32, FMT_FP4, attend, bf16_encode, compress, compress_entry,
+               dequantize_rows_e4m3, finish_store, index_scores, load_entries, page_bytes, quantize_rows_e4m3,
                topk, window_prep)
 
 
@@ -45,13 +45,29 @@ def store_window(values: np.ndarray, act: str) -> np.ndarray:
     return bf16_encode(values)
 
 
-def indexer_query_values(qI: np.ndarray, idx_fmt: str) -> np.ndarray:
+def indexer_query_values(qI: np.ndarray, idx_fmt: str, q_quant: str = "e4m3") -> np.ndarray:
     """The indexer query as the indexer sees it: e4m3 with one power-of-two
     scale per (token, head) for e4m3 and FP4 key pools (FP4 keys meet fp8
     queries, the mixed FP4 x FP8 product of the dsv4 book Ch.8 "FLOP
-    comparison" note), unchanged for fp32 ones."""
+    comparison" note), unchanged for fp32 ones.  With q_quant "fp4" (FP4 keys
+    only; Ch.6 "The lightning indexer" runs the whole indexer in FP4) every
+    (token, head) row is quantized exactly as an FP4 key is stored: e2m1 codes
+    with one power of two per 32 channels, encoded into an FP4 page and read
+    back with the same codec."""
     if idx_fmt == "f32":
         return qI
+    if q_quant == "fp4":
+        assert idx_fmt == "fp4", "FP4 queries meet FP4 keys"
+        shape = qI.shape
+        rows = np.ascontiguousarray(qI, np.float64).reshape(-1, shape[-1])
+        n, c = rows.shape
+        P = 64
+        pages = max(1, -(-n // P))
+        pool = new_pool(pages, FMT_FP4, c, 0, P)
+        pt = np.arange(pages, dtype=np.int32)
+        if n:
+            finish_store(FMT_FP4, c, 0, P, pool, pt, 0, rows, None, 0.0, 1.0, 1, False, False)
+        return load_entries(FMT_FP4, c, 0, P, pool, pt, 0, n).reshape(shape)
     codes, exps = quantize_rows_e4m3(qI)
     return dequantize_rows_e4m3(codes, exps)
 
@@ -83,7 +99,7 @@ def csa_prefill(cfg, inp: dict, pt_row, n_pool_pages: int, rows=None, idx_overri
     res["window"] = win
     rows = pos_all if rows is None else np.asarray(rows, np.int64)
     res["rows"] = rows
-    qI = indexer_query_values(take_rows(inp["qI"], rows), cfg.idx)
+    qI = indexer_query_values(take_rows(inp["qI"], rows), cfg.idx, getattr(cfg, "idx_q", "e4m3"))
     scores, n_elig = index_scores(qI, take_rows(inp["w"], rows), rows, m, idx_fmt, P, ipool, pt_row[None],
                                   [E.shape[0]], n_cols=max(1, E.shape[0]))
     idx, cnt = topk(scores, n_elig, cfg.k)
@@ -194,7 +210,7 @@ def csa_decode_step(cfg, inp: dict, state: dict, seqs=None) -> dict:
     B = state["page_table"].shape[0]
     seqs = np.arange(B) if seqs is None else np.asarray(seqs)
     pos = state["pos"][seqs]
-    qI = indexer_query_values(f64(inp["qI"])[seqs], cfg.idx)
+    qI = indexer_query_values(f64(inp["qI"])[seqs], cfg.idx, getattr(cfg, "idx_q", "e4m3"))
     n_cols = int(max(1, state["n_avail"].max()))
     scores, n_elig = index_scores(qI, f64(inp["w"])[seqs], pos, cfg.m, FMT_BY_NAME[cfg.idx], cfg.page,
                                   state["ipool"], state["page_table"], state["n_avail"], seq=seqs, n_cols=n_cols)

@@ -67,6 +67,10 @@ def test_argument_errors_are_reported_without_launching():
     rc = lib.ca_index_topk_decode(ctypes.byref(ip), None, None, None, 0, 0, ctypes.byref(cache), None, None, None,
                                   None, 0, None, 0, None)
     assert rc == -1                      # k must be positive
+    ip = ca.IndexParams(8, 64, 4, 16, ca.BF16, ca.FP4)
+    rc = lib.ca_index_topk_decode(ctypes.byref(ip), None, None, None, 0, 0, ctypes.byref(cache), None, None, None,
+                                  None, 0, None, 0, None)
+    assert rc == -1 and b"q_quant" in lib.ca_last_error()   # FP4 queries need an FP4 pool
     ap = ca.AttendParams(64, 512, 64, 128, ca.BF16, ca.BF16, ca.BF16, 0.04, 1e-6, 1e4)
     cache = ca._Cache(ca.E4M3, 512, 0, 64, None, 0, None, 0, 0)
     rc = lib.ca_hca_attend_decode(ctypes.byref(ap), None, None, ctypes.byref(cache), 128, None, 1, 0, None, 1, None,
@@ -99,3 +103,14 @@ def test_timer_argument_errors_need_no_device():
     assert lib.ca_timer_read(ca.TIMED_HCA_ATTEND, ctypes.byref(ms), ctypes.byref(n)) == 0
     assert (ms.value, n.value) == (0.0, 0)
     assert lib.ca_timer_stop() == 0
+
+
+def test_fp4_queries_need_fp4_keys():
+    from long_context_attention_17_amd.configs import CONFIGS
+    import dataclasses
+    cfg = dataclasses.replace(CONFIGS[5], idx="fp4", idx_q="fp4")
+    assert cfg.idx_q == "fp4"
+    with pytest.raises(ValueError):
+        dataclasses.replace(CONFIGS[5], idx_q="fp4")          # e4m3 keys
+    with pytest.raises(ValueError):
+        dataclasses.replace(CONFIGS[5], idx="fp4", idx_q="bf16")

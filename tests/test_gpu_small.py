@@ -143,6 +143,16 @@ def test_generic_csa_prefill_fp4_indexer():
     run_csa_prefill(_cfg(name="fp4_idx_generic", idx="fp4", nI=4, cI=32, L=530, seed=4344))
 
 
+def test_mfma_csa_prefill_fp4_queries():
+    """FP4 queries against FP4 keys (e2m1 x e2m1 MFMA, both block scales applied by it)."""
+    run_csa_prefill(_cfg(name="fp4_q", idx="fp4", idx_q="fp4", L=777, seed=4345))
+
+
+def test_generic_csa_prefill_fp4_queries():
+    """FP4 queries and keys on the generic scoring kernel."""
+    run_csa_prefill(_cfg(name="fp4_q_generic", idx="fp4", idx_q="fp4", nI=4, cI=32, L=530, seed=4346))
+
+
 def test_generic_path_bf16_small_dim():
     """D = 128 bf16 takes the generic kernels (MFMA path needs D = 512)."""
     run_csa_prefill(_cfg(D=128, R=16, n_h=4, L=300, k=16, n_win=32))
@@ -275,14 +285,20 @@ def test_mfma_decode_fp4_indexer():
     run_decode(cfg)
 
 
+def test_mfma_decode_fp4_queries():
+    cfg = _cfg(name="small_decode_fp4q", phase="decode", kv="fp8mix", idx="fp4", idx_q="fp4", n_h=64, k=64, B=4,
+               ctx_lo=300, ctx_hi=3000, L=0, seed=5253)
+    run_decode(cfg)
+
+
 def test_decode_edge_contexts():
     """Decode rows at the degenerate positions: the first token (no entries, a one-token
     window), just before / at / after the first CSA and HCA block, k exactly filled and
-    just exceeded, for fp8 pages with e4m3 and FP4 indexer keys."""
+    just exceeded, for fp8 pages with e4m3 and FP4 indexer keys (FP4 keys with e4m3 or FP4 queries)."""
     ctx = [0, 3, 4, 127, 128, 256, 260, 1000]
-    for idx in ("e4m3", "fp4"):
-        cfg = _cfg(name=f"edge_decode_{idx}", phase="decode", kv="fp8mix", idx=idx, n_h=64, k=64, B=len(ctx),
-                   ctx_lo=min(ctx), ctx_hi=max(ctx), L=0, seed=5353)
+    for idx, idx_q in (("e4m3", "e4m3"), ("fp4", "e4m3"), ("fp4", "fp4")):
+        cfg = _cfg(name=f"edge_decode_{idx}_{idx_q}", phase="decode", kv="fp8mix", idx=idx, idx_q=idx_q, n_h=64,
+                   k=64, B=len(ctx), ctx_lo=min(ctx), ctx_hi=max(ctx), L=0, seed=5353)
         run_decode(cfg, ctx=ctx)
 
 

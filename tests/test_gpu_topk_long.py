@@ -12,11 +12,11 @@ from gpu_util import check_topk, f64, gpu_cache_from, log, to_np
 pytestmark = pytest.mark.gpu
 
 
-def _run(ctx, k, dup=None, seed=11, idx="e4m3"):
+def _run(ctx, k, dup=None, seed=11, idx="e4m3", idx_q="e4m3"):
     from long_context_attention_17_amd import binding as ca, synth
     from long_context_attention_17_amd.configs import Config
     cfg = Config(name="topk_long", phase="decode", D=512, R=64, n_h=64, act="bf16", kv="fp8mix", m=4, k=k, n_win=128,
-                 nI=8, cI=64, idx=idx, B=len(ctx), ctx_lo=min(ctx), ctx_hi=max(ctx), seed=seed)
+                 nI=8, cI=64, idx=idx, idx_q=idx_q, B=len(ctx), ctx_lo=min(ctx), ctx_hi=max(ctx), seed=seed)
     fmt = oracle.FMT_BY_NAME[idx]
     ctx = torch.tensor(ctx, dtype=torch.int64)
     n_e = [int(t) // cfg.m for t in ctx]
@@ -34,7 +34,7 @@ def _run(ctx, k, dup=None, seed=11, idx="e4m3"):
     qI = synth.normal((len(n_e), cfg.nI, cfg.cI), 1 / 8, seed, "qI", "cpu").to(torch.bfloat16)
     w = synth.normal((len(n_e), cfg.nI), 0.35, seed, "w", "cpu").abs()     # positive weights: ties stay ties
     pos = ctx.numpy()
-    qv = opl.indexer_query_values(f64(qI), idx)
+    qv = opl.indexer_query_values(f64(qI), idx, idx_q)
     sc, ne = oracle.index_scores(qv, f64(w), pos, cfg.m, fmt, cfg.page, pool, to_np(pt), n_e,
                                  seq=np.arange(len(n_e)), n_cols=max(n_e))
     oidx, ocnt = oracle.topk(sc, ne, k)
@@ -90,3 +90,8 @@ def test_long_rows_small_tie_group():
 def test_long_rows_fp4_keys():
     """FP4 indexer keys (e2m1 + E8M0 scale per 32 channels) through the scaled MFMA and the long top-k."""
     _run([70000, 123457, 200003], 2048, seed=23, idx="fp4")
+
+
+def test_long_rows_fp4_queries():
+    """FP4 queries against FP4 keys (e2m1 x e2m1 MFMA) through the long top-k."""
+    _run([70000, 123457, 200003], 2048, seed=29, idx="fp4", idx_q="fp4")

@@ -603,3 +603,29 @@ def test_fp4_indexer_equals_f32_on_representable_keys(orc):
     s4, ne4 = orc.index_scores(q, w, t, m, oracle.FMT_FP4, P, pool4, np.stack([pt, pt]), [n, n], seq=[0, 1])
     assert list(ne32) == list(ne4)
     np.testing.assert_array_equal(np.nan_to_num(s32, nan=7.0), np.nan_to_num(s4, nan=7.0))
+
+
+def test_fp4_query_quantization_by_hand(orc):
+    """FP4 indexer queries, worked out by hand from the e2m1 grid (magnitudes 0, .5, 1, 1.5,
+    2, 3, 4, 6; a value halfway between two grid points goes to the one with mantissa bit 0)
+    and the block scale (the smallest power of two 2^e with block max <= 6 * 2^e):
+      block 0, max 6 -> e = 0:  2.5 -> 2, 0.25 -> 0, 0.3 -> 0.5, 1.25 -> 1, 1.75 -> 2, -0.75 -> -1,
+                                5 -> 4, 5.5 -> 6;
+      block 1, max 12 -> e = 1: x/2 = 6, 2.5, -3.5, 0.25, 0.8 -> 6, 2, -4, 0, 1 -> 12, 4, -8, 0, 2."""
+    q = np.zeros((1, 1, 64))
+    q[0, 0, :9] = [6.0, 2.5, 0.25, 0.3, 1.25, 1.75, -0.75, 5.0, 5.5]
+    q[0, 0, 32:37] = [12.0, 5.0, -7.0, 0.5, 1.6]
+    want = np.zeros(64)
+    want[:9] = [6.0, 2.0, 0.0, 0.5, 1.0, 2.0, -1.0, 4.0, 6.0]
+    want[32:37] = [12.0, 4.0, -8.0, 0.0, 2.0]
+    got = opl.indexer_query_values(q, "fp4", "fp4")
+    np.testing.assert_array_equal(got[0, 0], want)
+    # a block of tiny values keeps its shape: max 3e-3 -> e = -10 (6 * 2^-11 < 3e-3 <= 6 * 2^-10)
+    t = np.zeros((1, 1, 64))
+    t[0, 0, 40:42] = [3e-3, -1.5e-3]
+    got = opl.indexer_query_values(t, "fp4", "fp4")[0, 0]
+    assert got[40] == 3.0 * 2.0 ** -10 and got[41] == -1.5 * 2.0 ** -10
+    assert not got[:32].any()                                   # an all-zero block stays zero
+    # e4m3 queries (one scale per head, here 2^-5) are the default: 2.5 and 5 keep their values
+    e4 = opl.indexer_query_values(q, "fp4")[0, 0]
+    assert e4[1] == 2.5 and e4[7] == 5.0 and not np.array_equal(e4, want)
