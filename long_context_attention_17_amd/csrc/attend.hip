@@ -277,64 +277,90 @@ __global__ void __launch_bounds__(512) attend_combine_kernel(AttendArgs a) {
 // 32*pair + 8(v/4) + 4(lane/32) + v%4 of the group and channel 256*half + 32*cb +
 // lane%32.  Workgroup = (row, head group, half, cb); thread (pair, v/4, lane) reads
 // one 16-byte run per split (heads h0 .. h0+3, one channel), so every wavefront
-// load is 1 KB contiguous.
+// load is 1 KB contiguous.  The per-(split, head) weights exp2(m_s - M) and the
+// per-head denominators are formed once per workgroup in LDS (8 threads per head,
+// each over every 8th split, reduced in a fixed order), while the first splits'
+// partial rows are already in flight.
+constexpr int kCombineLdsSplits = 64;   // splits whose weights sit in LDS (more: read from the partials)
+
 __global__ void __launch_bounds__(512) attend_combine_acc_kernel(AttendArgs a) {
   constexpr int D = 512, C = D - 64;
+  __shared__ float w_s[kCombineLdsSplits][64];         // exp2(m_s - M) per (split, head of the group)
+  __shared__ float red[8][64];                         // per (split group, head) partial max / sum
+  __shared__ float M_s[64], den_s[64];
   const int r = blockIdx.x, n_hg = a.n_heads >> 6;
   const int hg = blockIdx.y >> 4, half = (blockIdx.y >> 3) & 1, cb = blockIdx.y & 7;
   const int t = threadIdx.x, pair = t >> 8, vq = (t >> 6) & 3, lane = t & 63;
-  const int h0 = hg * 64 + 32 * pair + 8 * vq + 4 * (lane >> 5);   // heads h0 .. h0+3
+  const int hq = 32 * pair + 8 * vq + 4 * (lane >> 5);  // first of the thread's 4 heads in the group
+  const int h0 = hg * 64 + hq;                          // heads h0 .. h0+3
   const int c = 256 * half + 32 * cb + (lane & 31);
   const RowInfo ri = row_info(a, r);
   const int ns = n_splits_of(a, ri.total);
-  const f32x4 sk = *(const f32x4*)(a.sink + h0) * kLog2e;
-  f32x4 M = sk, den = {0.0f, 0.0f, 0.0f, 0.0f}, acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  float ms[kCombineUnroll][4], ls[kCombineUnroll][4];
+  auto o_at = [&](int s) {
+    return *(const f32x4*)(a.part_o + (((int64_t)r * a.max_splits + s) * n_hg + hg) * (64 * D) +
+                           (pair * 2 + half) * 8192 + (cb * 4 + vq) * 256 + 4 * lane);
+  };
+  // the first splits' partial rows go out first
   f32x4 os[kCombineUnroll];
 #pragma unroll
-  for (int s = 0; s < kCombineUnroll; ++s) {
-    if (s < ns) {
-      const int64_t b = ((int64_t)r * a.max_splits + s) * a.n_heads + h0;
-      const f32x4 ml0 = *(const f32x4*)(a.part_ml + 2 * b), ml1 = *(const f32x4*)(a.part_ml + 2 * b + 4);
-      ms[s][0] = ml0[0]; ls[s][0] = ml0[1]; ms[s][1] = ml0[2]; ls[s][1] = ml0[3];
-      ms[s][2] = ml1[0]; ls[s][2] = ml1[1]; ms[s][3] = ml1[2]; ls[s][3] = ml1[3];
-      os[s] = *(const f32x4*)(a.part_o + (((int64_t)r * a.max_splits + s) * n_hg + hg) * (64 * D) +
-                              (pair * 2 + half) * 8192 + (cb * 4 + vq) * 256 + 4 * lane);
-    }
-  }
-#pragma unroll
   for (int s = 0; s < kCombineUnroll; ++s)
-    if (s < ns)
+    if (s < ns) os[s] = o_at(s);
+
+  // per head of the group: M = max(sink, m_s), den = exp2(sink - M) + sum_s l_s exp2(m_s - M)
+  {
+    const int hh = t & 63, g = t >> 6;
+    const int64_t base = ((int64_t)r * a.max_splits) * a.n_heads + hg * 64 + hh;
+    float mx = -INFINITY;
+    for (int s = g; s < ns; s += 8) mx = fmaxf(mx, a.part_ml[2 * (base + (int64_t)s * a.n_heads)]);
+    red[g][hh] = mx;
+    __syncthreads();
+    float M = a.sink[hg * 64 + hh] * kLog2e;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) M[e] = fmaxf(M[e], ms[s][e]);
-  for (int s = kCombineUnroll; s < ns; ++s) {
+    for (int i = 0; i < 8; ++i) M = fmaxf(M, red[i][hh]);
+    __syncthreads();                                   // every thread has read the maxima
+    float dp = 0.0f;
+    for (int s = g; s < ns; s += 8) {
+      const float w = exp2f(a.part_ml[2 * (base + (int64_t)s * a.n_heads)] - M);
+      dp += a.part_ml[2 * (base + (int64_t)s * a.n_heads) + 1] * w;
+      if (s < kCombineLdsSplits) w_s[s][hh] = w;
+    }
+    red[g][hh] = dp;
+    if (g == 0) M_s[hh] = M;
+    __syncthreads();
+    if (g == 0) {
+      float den = exp2f(a.sink[hg * 64 + hh] * kLog2e - M);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) den += red[i][hh];
+      den_s[hh] = den;
+    }
+    __syncthreads();
+  }
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f}, M, den;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    M[e] = M_s[hq + e];
+    den[e] = den_s[hq + e];
+  }
+  auto weights = [&](int s) {
+    if (s < kCombineLdsSplits) return *(const f32x4*)&w_s[s][hq];
+    f32x4 w;
     const int64_t b = ((int64_t)r * a.max_splits + s) * a.n_heads + h0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) M[e] = fmaxf(M[e], a.part_ml[2 * (b + e)]);
-  }
-#pragma unroll
-  for (int e = 0; e < 4; ++e) den[e] = exp2f(sk[e] - M[e]);
+    for (int e = 0; e < 4; ++e) w[e] = exp2f(a.part_ml[2 * (b + e)] - M[e]);
+    return w;
+  };
 #pragma unroll
   for (int s = 0; s < kCombineUnroll; ++s) {
     if (s < ns) {
+      const f32x4 w = weights(s);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float w = exp2f(ms[s][e] - M[e]);
-        den[e] += ls[s][e] * w;
-        acc[e] += os[s][e] * w;
-      }
+      for (int e = 0; e < 4; ++e) acc[e] += os[s][e] * w[e];
     }
   }
   for (int s = kCombineUnroll; s < ns; ++s) {
-    const int64_t b = ((int64_t)r * a.max_splits + s) * a.n_heads + h0;
-    const f32x4 o = *(const f32x4*)(a.part_o + (((int64_t)r * a.max_splits + s) * n_hg + hg) * (64 * D) +
-                                    (pair * 2 + half) * 8192 + (cb * 4 + vq) * 256 + 4 * lane);
+    const f32x4 o = o_at(s), w = weights(s);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float w = exp2f(a.part_ml[2 * (b + e)] - M[e]);
-      den[e] += a.part_ml[2 * (b + e) + 1] * w;
-      acc[e] += o[e] * w;
-    }
+    for (int e = 0; e < 4; ++e) acc[e] += o[e] * w[e];
   }
   f32x4 v;
 #pragma unroll
