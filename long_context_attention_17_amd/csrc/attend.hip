@@ -297,8 +297,12 @@ __global__ void __launch_bounds__(512) attend_combine_acc_kernel(AttendArgs a) {
   const RowInfo ri = row_info(a, r);
   const int ns = n_splits_of(a, ri.total);
   auto o_at = [&](int s) {
-    return *(const f32x4*)(a.part_o + (((int64_t)r * a.max_splits + s) * n_hg + hg) * (64 * D) +
-                           (pair * 2 + half) * 8192 + (cb * 4 + vq) * 256 + 4 * lane);
+    const int64_t e = (((int64_t)r * a.max_splits + s) * n_hg + hg) * (64 * D) + (pair * 2 + half) * 8192 +
+                      (cb * 4 + vq) * 256 + 4 * lane;   // element offset (fp32 or bf16 partials)
+    if (!a.part_bf16) return *(const f32x4*)(a.part_o + e);
+    const u32x2 w = *(const u32x2*)((const uint16_t*)a.part_o + e);
+    return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u), __uint_as_float(w[1] << 16),
+                 __uint_as_float(w[1] & 0xFFFF0000u)};
   };
   // the first splits' partial rows go out first
   f32x4 os[kCombineUnroll];
@@ -1072,14 +1076,28 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
       a.part_ml[2 * (pbase + hl)] = m_run;
       a.part_ml[2 * (pbase + hl) + 1] = l_tot;
     }
-    float* blk = a.part_o + (((int64_t)r * a.max_splits + split) * n_hg + hg) * (64 * kD) +
-                 (pair * 2 + half) * (8 * 4 * 64 * 4) + 4 * lane;
+    const int64_t blk = (((int64_t)r * a.max_splits + split) * n_hg + hg) * (64 * kD) +
+                        (pair * 2 + half) * (8 * 4 * 64 * 4) + 4 * lane;   // element offset
+    if (a.part_bf16) {   // (uniform) 8 B per lane: each store instruction writes 512 B contiguous
+      uint16_t* pb = (uint16_t*)a.part_o + blk;
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb)
+      for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
-      for (int vq = 0; vq < 4; ++vq)
-        *(f32x4*)(blk + (cb * 4 + vq) * 256) =
-            f32x4{oacc[cb][4 * vq], oacc[cb][4 * vq + 1], oacc[cb][4 * vq + 2], oacc[cb][4 * vq + 3]};
+        for (int vq = 0; vq < 4; ++vq) {
+          u32x2 w;
+          w[0] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)oacc[cb][4 * vq], (__bf16)oacc[cb][4 * vq + 1]});
+          w[1] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)oacc[cb][4 * vq + 2], (__bf16)oacc[cb][4 * vq + 3]});
+          *(u32x2*)(pb + (cb * 4 + vq) * 256) = w;
+        }
+    } else {
+      float* pf = a.part_o + blk;
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb)
+#pragma unroll
+        for (int vq = 0; vq < 4; ++vq)
+          *(f32x4*)(pf + (cb * 4 + vq) * 256) =
+              f32x4{oacc[cb][4 * vq], oacc[cb][4 * vq + 1], oacc[cb][4 * vq + 2], oacc[cb][4 * vq + 3]};
+    }
     __syncthreads();                                   // the next unit reuses the LDS
     continue;
   }
@@ -1156,6 +1174,7 @@ hipError_t launch_attend(const AttendArgs& args, hipStream_t st) {
   if (args.n_rows == 0) return hipSuccess;
   AttendArgs a = args;
   a.part_acc = attend_mfma_supported(a) ? 1 : 0;
+  a.part_bf16 = a.part_acc && a.out_fmt == CA_BF16 ? 1 : 0;   // partials no finer than the output
   const int splits = a.split_items > 0 ? a.max_splits : 1;
   hipEvent_t ev0, ev1;
   timer_events(a.mode == 0 ? CA_TIMED_CSA_ATTEND : CA_TIMED_HCA_ATTEND, st, &ev0, &ev1);

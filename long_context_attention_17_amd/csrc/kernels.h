@@ -70,6 +70,7 @@ struct AttendArgs {
   float* part_o;       // [rows, max_splits, n_heads, D]
   float* part_ml;      // [rows, max_splits, n_heads, 2]
   int part_acc;        // 1: part_o is in the MFMA kernel's accumulator layout (see attend_combine_kernel)
+  int part_bf16;       // 1 (accumulator layout, bf16 output): part_o holds bf16 values, same element offsets
   uint16_t* q_prep;    // nullptr, or bf16 [rows, n_heads, D]: queries normalized, rotated and scaled
                        // once per row by a prep kernel (split rows of the MFMA path)
 };
