@@ -1,11 +1,11 @@
 """Benchmark of the CSA + HCA hot path on one MI355X.
 
 Default workload: the million-token decode step (batch 8, context 2^20, 128
-query heads, D = 512, fp8-mixed pages): one CSA layer step (window append,
-compressor tail update, lightning indexer + top-k over 262,144 compressed
-entries, gathered attention over 2,048 + 128 items) and one HCA layer step
-(window append, compressor tail update, dense attention over 8,192 + 128
-items).  Other presets: --workload decode_mixed | prefill_csa_32k |
+query heads, D = 512, fp8-mixed pages): one CSA layer step (window append and
+compressor tail updates in one launch, lightning indexer + top-k over 262,144
+compressed entries, gathered attention over 2,048 + 128 items) and one HCA
+layer step (window append and compressor tail update in one launch, dense
+attention over 8,192 + 128 items).  Other presets: --workload decode_mixed | prefill_csa_32k |
 prefill_hca_128k | tiny, the million-token decode with FP4 indexer keys
 (decode_1m_fp4idx) or FP4 keys and queries (decode_1m_fp4qk), and prefills
 that continue a stored prefix (prefill_csa_32k_after_16k,
@@ -202,9 +202,9 @@ def bench_decode(cfg, steps, warmup, replicas, args):
     def stages_of(i):
         c = layer_objs["csa"][i % replicas]
         h = layer_objs["hca"][i % replicas]
-        return [("csa_window_append", c.append_token), ("csa_compress", c.compress),
-                ("csa_index_topk", c.index_topk), ("csa_attend", c.attend),
-                ("hca_window_append", h.append_token), ("hca_compress", h.compress), ("hca_attend", h.attend)]
+        # append: the new token's window append and compressor step(s) in one launch
+        return [("csa_append", c.append), ("csa_index_topk", c.index_topk), ("csa_attend", c.attend),
+                ("hca_append", h.append), ("hca_attend", h.attend)]
 
     def step(i):
         for _, fn in stages_of(i):

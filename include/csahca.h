@@ -178,6 +178,33 @@ int ca_window_append(const ca_window_params* p, const void* kv_raw, const float*
                      const int32_t* seq, int32_t T, void* window, int32_t W, int32_t S, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Fused decode append: one decode step's token-level cache updates of one  */
+/* layer in a single launch (Ch.5 "Decode-time cache state": the window and */
+/* the bounded tail buffers).  For every row b (sequence b, position        */
+/* pos[b]) it does exactly what these calls do, bit for bit:                */
+/*   ca_window_append(wp, kv_raw, w_gain, pos, seq = {0, 1, .., B-1}, B,     */
+/*                    window, W, S, stream), and for each of the n_jobs      */
+/*   (1 or 2) jobs ca_compress_decode(&job.params, job.new_rows, pos, B,     */
+/*                    job.tail, job.Ba, job.Bb, job.gain, job.cache, stream) */
+/* (CSA: the main entry and the indexer key; HCA: the entry).  The jobs     */
+/* must not share a tail ring or a cache.  S >= B.  Errors: as the separate */
+/* calls (job index in the message); nothing is launched on an error.       */
+/* ------------------------------------------------------------------------ */
+typedef struct ca_decode_entry_job {
+  ca_compress_params params;
+  const void* new_rows;   /* [B, narr, dim] as for ca_compress_decode */
+  float* tail;            /* [B, span, narr, dim] float32 tail ring */
+  const float* Ba;        /* [ratio, dim] */
+  const float* Bb;        /* [ratio, dim] (overlap only, else may be NULL) */
+  const float* gain;      /* [dim] (apply_norm only, else may be NULL) */
+  const ca_cache* cache;
+} ca_decode_entry_job;
+
+int ca_decode_append(const ca_window_params* wp, const void* kv_raw, const float* w_gain, const int32_t* pos,
+                     int32_t B, void* window, int32_t W, int32_t S, const ca_decode_entry_job* jobs, int32_t n_jobs,
+                     void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Lightning indexer + top-k (dsv4 book Ch.6 "The lightning indexer",       */
 /* "Top-k selection and asymptotic scaling"; Ch.5 "Causal availability").   */
 /* For query row r at position t: for every block s < floor(t/m),           */

@@ -61,6 +61,13 @@ class AttendParams(ctypes.Structure):
 
 
 _PC = ctypes.POINTER(_Cache)
+
+
+class DecodeEntryJob(ctypes.Structure):
+    _fields_ = [("params", CompressParams), ("new_rows", _P), ("tail", _P), ("Ba", _P), ("Bb", _P), ("gain", _P),
+                ("cache", _PC)]
+
+
 _SIGS = {
     "ca_last_error": (ctypes.c_char_p, []),
     "ca_record_stride": (_I64, [_I32, _I32, _I32]),
@@ -70,6 +77,8 @@ _SIGS = {
                                            _I32, _PC, _P]),
     "ca_compress_decode": (ctypes.c_int, [ctypes.POINTER(CompressParams), _P, _P, _I32, _P, _P, _P, _P, _PC, _P]),
     "ca_window_append": (ctypes.c_int, [ctypes.POINTER(WindowParams), _P, _P, _P, _P, _I32, _P, _I32, _I32, _P]),
+    "ca_decode_append": (ctypes.c_int, [ctypes.POINTER(WindowParams), _P, _P, _P, _I32, _P, _I32, _I32,
+                                        ctypes.POINTER(DecodeEntryJob), _I32, _P]),
     "ca_index_topk_workspace": (_SZ, [ctypes.POINTER(IndexParams), _I32, _I64]),
     "ca_index_topk_prefill": (ctypes.c_int, [ctypes.POINTER(IndexParams), _P, _P, _I64, _I64, _I32, _PC, _P, _P, _P,
                                              _P, _I64, _P, _SZ, _P]),
@@ -173,6 +182,20 @@ def window_append(p: WindowParams, kv_raw, gain, window, pos=None, seq=None, str
     S, W = window.shape[0], window.shape[1]
     _check(_lib.ca_window_append(ctypes.byref(p), _ptr(kv_raw), _ptr(gain), _ptr(pos), _ptr(seq), kv_raw.shape[0],
                                  _ptr(window), W, S, _stream(stream)))
+
+
+def decode_append(wp: WindowParams, kv_raw, w_gain, window, pos, jobs, stream=None):
+    """Window append of row b's token (sequence b) plus the compressor steps of `jobs`, each
+    (CompressParams, new_rows, tail, Ba, Bb, gain, Cache), in one launch."""
+    S, W = window.shape[0], window.shape[1]
+    arr = (DecodeEntryJob * len(jobs))()
+    keep = []
+    for q, (p, new_rows, tail, Ba, Bb, gain, cache) in enumerate(jobs):
+        arr[q] = DecodeEntryJob(p, _ptr(new_rows), _ptr(tail), _ptr(Ba), _ptr(Bb), _ptr(gain),
+                                ctypes.pointer(cache.desc))
+        keep.append(cache)
+    _check(_lib.ca_decode_append(ctypes.byref(wp), _ptr(kv_raw), _ptr(w_gain), _ptr(pos), pos.shape[0],
+                                 _ptr(window), W, S, arr, len(jobs), _stream(stream)))
 
 
 def index_topk_workspace(p: IndexParams, n_rows: int, max_pos: int) -> int:

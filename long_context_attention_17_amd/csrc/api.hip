@@ -184,6 +184,43 @@ int ca_window_append(const ca_window_params* p, const void* kv_raw, const float*
                     "ca_window_append");
 }
 
+int ca_decode_append(const ca_window_params* wp, const void* kv_raw, const float* w_gain, const int32_t* pos,
+                     int32_t B, void* window, int32_t W, int32_t S_, const ca_decode_entry_job* jobs, int32_t n_jobs,
+                     void* stream) {
+  const char* what = "ca_decode_append";
+  if (wp == nullptr) return fail(CA_ERR_ARG, "%s: window params NULL", what);
+  if (wp->dim <= 0 || wp->dim > 1024) return fail(CA_ERR_UNSUPPORTED, "%s: window dim outside 1..1024", what);
+  if (wp->rope_dim < 0 || wp->rope_dim > wp->dim || (wp->rope_dim & 1)) return fail(CA_ERR_ARG, "%s: bad rope_dim", what);
+  if (!is_act(wp->in_format) || !is_act(wp->win_format)) return fail(CA_ERR_DTYPE, "%s: formats must be F32/BF16", what);
+  if (n_jobs < 1 || n_jobs > 2 || jobs == nullptr) return fail(CA_ERR_ARG, "%s: n_jobs must be 1 or 2", what);
+  if (B < 0 || W <= 0 || S_ < B) return fail(CA_ERR_ARG, "%s: bad B/W/S (S must hold every row's sequence)", what);
+  ca::DecodeEntryJob ej[2];
+  for (int q = 0; q < n_jobs; ++q) {
+    const ca_decode_entry_job& j = jobs[q];
+    if (int e = check_compress(&j.params, j.cache, &ej[q].cv, what)) return e;
+    if (B > 0 && (!j.new_rows || !j.tail || !j.Ba)) return fail(CA_ERR_ARG, "%s: job %d: NULL argument", what, q);
+    if (B > 0 && j.params.overlap && !j.Bb) return fail(CA_ERR_ARG, "%s: job %d: Bb NULL with overlap", what, q);
+    if (B > 0 && j.params.apply_norm && !j.gain) return fail(CA_ERR_ARG, "%s: job %d: gain NULL with apply_norm", what, q);
+    if (B > j.cache->n_seqs) return fail(CA_ERR_ARG, "%s: job %d: B exceeds the page table rows", what, q);
+    ej[q].m = j.params.ratio;
+    ej[q].overlap = j.params.overlap;
+    ej[q].in_fmt = j.params.in_format;
+    ej[q].apply_rope = j.params.apply_rope;
+    ej[q].new_rows = j.new_rows;
+    ej[q].tail = j.tail;
+    ej[q].Ba = j.Ba;
+    ej[q].Bb = j.Bb;
+    ej[q].gain = j.params.apply_norm ? j.gain : nullptr;
+    ej[q].eps = j.params.eps;
+    ej[q].base = j.params.rope_base;
+  }
+  if (B == 0) return ok();
+  if (!kv_raw || !w_gain || !window || !pos) return fail(CA_ERR_ARG, "%s: NULL argument", what);
+  ca::DecodeWindowJob wj{wp->dim, wp->rope_dim, wp->in_format, wp->win_format, kv_raw, w_gain, window, W, S_,
+                         wp->eps, wp->rope_base};
+  return hip_status(ca::launch_decode_append(wj, ej, n_jobs, pos, B, S(stream)), what);
+}
+
 // ------------------------------------------------------------------ indexer
 // Workspace: the score rows, then (for long rows) the multi-workgroup top-k state.
 size_t ca_index_topk_workspace(const ca_index_params* p, int32_t n_rows, int64_t max_pos) {

@@ -150,11 +150,13 @@ __global__ void compress_prefill_kernel(CacheView cv, int seq, int m, int overla
 }
 
 // Tail ring: tail[b, slot, a, ch] (float32), narr arrays per slot.
-__global__ void compress_decode_kernel(CacheView cv, int m, int overlap, int in_fmt, const void* new_rows,
-                                       const int32_t* pos, float* tail, const float* Ba, const float* Bb,
-                                       const float* gain, float eps, int apply_rope, double base) {
-  __shared__ float red[16];
-  const int D = cv.dim, j = threadIdx.x, b = blockIdx.x;
+// Decode-time compressor step of sequence b (thread j = channel j; every thread of
+// the block takes part, channels j >= D hold nothing).
+__device__ __forceinline__ void compress_decode_row(const CacheView& cv, int m, int overlap, int in_fmt,
+                                                    const void* new_rows, const int32_t* pos, float* tail,
+                                                    const float* Ba, const float* Bb, const float* gain, float eps,
+                                                    int apply_rope, double base, int b, int j, float* red) {
+  const int D = cv.dim;
   const int narr = overlap ? 4 : 2;
   const int span = overlap ? 2 * m : m;
   const int t = pos[b];
@@ -187,6 +189,14 @@ __global__ void compress_decode_kernel(CacheView cv, int m, int overlap, int in_
   store_record(cv, b, i, x, j, red);
 }
 
+__global__ void compress_decode_kernel(CacheView cv, int m, int overlap, int in_fmt, const void* new_rows,
+                                       const int32_t* pos, float* tail, const float* Ba, const float* Bb,
+                                       const float* gain, float eps, int apply_rope, double base) {
+  __shared__ float red[16];
+  compress_decode_row(cv, m, overlap, in_fmt, new_rows, pos, tail, Ba, Bb, gain, eps, apply_rope, base, blockIdx.x,
+                      threadIdx.x, red);
+}
+
 __global__ void store_entries_kernel(CacheView cv, int seq, int64_t first, const float* src, const float* gain,
                                      float eps, int apply_rope, double base, int pos_stride) {
   __shared__ float red[16];
@@ -197,19 +207,44 @@ __global__ void store_entries_kernel(CacheView cv, int seq, int64_t first, const
   store_record(cv, seq, i, x, j, red);
 }
 
-__global__ void window_append_kernel(int D, int R, int in_fmt, int win_fmt, const void* raw, const float* gain,
-                                     const int32_t* pos, const int32_t* seq, void* window, int W, int S, float eps,
-                                     double base) {
-  __shared__ float red[16];
-  const int j = threadIdx.x, r = blockIdx.x;
+// Window append of raw row r (thread j = channel j; every thread of the block takes part).
+__device__ __forceinline__ void window_append_row(int D, int R, int in_fmt, int win_fmt, const void* raw,
+                                                  const float* gain, const int32_t* pos, const int32_t* seq,
+                                                  void* window, int W, int S, float eps, double base, int r, int j,
+                                                  float* red, bool row_is_seq = false) {
   const int t = pos ? pos[r] : r;
-  const int s = seq ? seq[r] : 0;
+  const int s = seq ? seq[r] : (row_is_seq ? r : 0);
   float x = j < D ? load_act(raw, in_fmt, (int64_t)r * D + j) : 0.0f;
   x = norm_rope(x, j, D, R, gain, eps, true, (double)t, base, red);
   if (j >= D || t < 0 || s < 0 || s >= S) return;
   int64_t o = ((int64_t)s * W + (t % W)) * D + j;
   if (win_fmt == CA_F32) ((float*)window)[o] = x;
   else ((uint16_t*)window)[o] = f32_to_bf16_bits(x);
+}
+
+__global__ void window_append_kernel(int D, int R, int in_fmt, int win_fmt, const void* raw, const float* gain,
+                                     const int32_t* pos, const int32_t* seq, void* window, int W, int S, float eps,
+                                     double base) {
+  __shared__ float red[16];
+  window_append_row(D, R, in_fmt, win_fmt, raw, gain, pos, seq, window, W, S, eps, base, blockIdx.x, threadIdx.x,
+                    red);
+}
+
+// One decode step's token-level updates of a layer in one launch: workgroup (b, 0)
+// appends sequence b's new token (row b) to its window, workgroup (b, 1 + q) runs entry job
+// q's compressor step for it.  Each workgroup does exactly what the workgroup of
+// the separate launch does, so the results are the same bit for bit.
+__global__ void decode_append_kernel(DecodeWindowJob wj, DecodeEntryJob e0, DecodeEntryJob e1, const int32_t* pos) {
+  __shared__ float red[16];
+  const int b = blockIdx.x, j = threadIdx.x;
+  if (blockIdx.y == 0) {
+    window_append_row(wj.D, wj.R, wj.in_fmt, wj.win_fmt, wj.raw, wj.gain, pos, nullptr, wj.window, wj.W, wj.S,
+                      wj.eps, wj.base, b, j, red, true);
+    return;
+  }
+  const DecodeEntryJob& e = blockIdx.y == 1 ? e0 : e1;
+  compress_decode_row(e.cv, e.m, e.overlap, e.in_fmt, e.new_rows, pos, e.tail, e.Ba, e.Bb, e.gain, e.eps,
+                      e.apply_rope, e.base, b, j, red);
 }
 
 // ----------------------------------------------------------------- launchers
@@ -242,6 +277,16 @@ hipError_t launch_store_entries(const CacheView& cv, int seq, int64_t first, int
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(store_entries_kernel, dim3((unsigned)n), dim3(block_for(cv.dim)), 0, st, cv, seq, first, src,
                      gain, eps, apply_rope, base, pos_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_append(const DecodeWindowJob& wj, const DecodeEntryJob* jobs, int n_jobs,
+                                const int32_t* pos, int B, hipStream_t st) {
+  if (B == 0) return hipSuccess;
+  int threads = block_for(wj.D);
+  for (int q = 0; q < n_jobs; ++q) threads = block_for(jobs[q].cv.dim) > threads ? block_for(jobs[q].cv.dim) : threads;
+  hipLaunchKernelGGL(decode_append_kernel, dim3(B, 1 + n_jobs), dim3(threads), 0, st, wj, jobs[0],
+                     n_jobs > 1 ? jobs[1] : jobs[0], pos);
   return hipGetLastError();
 }
 

@@ -20,6 +20,29 @@ hipError_t launch_store_entries(const CacheView& cv, int seq, int64_t first, int
 hipError_t launch_window_append(const ca_window_params& p, const void* raw, const float* gain, const int32_t* pos,
                                 const int32_t* seq, int T, void* window, int W, int S, hipStream_t st);
 
+// The fused decode append (ca_decode_append): the window append of every row b
+// (sequence b) plus one or two compressor steps, in one launch.
+struct DecodeWindowJob {
+  int D, R, in_fmt, win_fmt;
+  const void* raw;
+  const float* gain;
+  void* window;
+  int W, S;
+  float eps;
+  double base;
+};
+struct DecodeEntryJob {
+  CacheView cv;
+  int m, overlap, in_fmt, apply_rope;
+  const void* new_rows;
+  float* tail;
+  const float *Ba, *Bb, *gain;   // gain: nullptr unless the epilogue normalizes
+  float eps;
+  double base;
+};
+hipError_t launch_decode_append(const DecodeWindowJob& wj, const DecodeEntryJob* jobs, int n_jobs,
+                                const int32_t* pos, int B, hipStream_t st);
+
 // Position of query row r: pos[r] (decode), or t0 + r (prefill rows of one sequence).
 struct RowPos {
   const int32_t* pos;

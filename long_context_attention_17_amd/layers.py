@@ -206,6 +206,20 @@ class DecodeLayer:
         self.out = torch.empty(B, cfg.n_h, cfg.D, dtype=act_dtype(cfg), device=dev)
 
     # individual stages
+    def append(self):
+        """The new token's window append and compressor step(s) in one launch: the same
+        results, bit for bit, as append_token() followed by compress()."""
+        c, i = self.cfg, self.inp
+        if self.layer == "csa":
+            jobs = [(compress_params(c, c.m, True, True), self.new_rows, self.tail, i["Ba"], i["Bb"], i["g_kv"],
+                     self.kv),
+                    (compress_params(c, c.m, True, False), self.new_irows, self.itail, i["IBa"], i["IBb"], None,
+                     self.ik)]
+        else:
+            jobs = [(compress_params(c, c.m_hca, False, True), self.new_rows, self.tail, i["B"], None, i["g_kv"],
+                     self.kv)]
+        ca.decode_append(window_params(c), self.new_kv, i["g_w"], self.window, self.pos, jobs)
+
     def append_token(self):
         ca.window_append(window_params(self.cfg), self.new_kv, self.inp["g_w"], self.window, pos=self.pos,
                          seq=self.seq_ids)
@@ -235,8 +249,7 @@ class DecodeLayer:
                                  self.max_pos, self.window, self.inp["sink"], self.out, lse, self.aws)
 
     def step(self):
-        self.append_token()
-        self.compress()
+        self.append()
         if self.layer == "csa":
             self.index_topk()
         self.attend()

@@ -71,6 +71,14 @@ def test_argument_errors_are_reported_without_launching():
     rc = lib.ca_index_topk_decode(ctypes.byref(ip), None, None, None, 0, 0, ctypes.byref(cache), None, None, None,
                                   None, 0, None, 0, None)
     assert rc == -1 and b"q_quant" in lib.ca_last_error()   # FP4 queries need an FP4 pool
+    wp = ca.WindowParams(512, 64, ca.BF16, ca.BF16, 1e-6, 1e4)
+    rc = lib.ca_decode_append(ctypes.byref(wp), None, None, None, 0, None, 128, 1, None, 0, None)
+    assert rc == -1 and b"n_jobs" in lib.ca_last_error()
+    job = ca.DecodeEntryJob(ca.CompressParams(4, 1, ca.BF16, 1, 1, 1e-6, 1e4), None, None, None, None, None,
+                            ctypes.pointer(ca._Cache(ca.FP8MIX, 512, 64, 64, None, 0, None, 8, 0)))
+    rc = lib.ca_decode_append(ctypes.byref(wp), None, None, None, 8, None, 128, 8, ctypes.byref(job), 1, None)
+    assert rc == -1 and b"NULL" in lib.ca_last_error()      # missing rows / ring
+    assert lib.ca_decode_append(ctypes.byref(wp), None, None, None, 0, None, 128, 1, ctypes.byref(job), 1, None) == 0
     ap = ca.AttendParams(64, 512, 64, 128, ca.BF16, ca.BF16, ca.BF16, 0.04, 1e-6, 1e4)
     cache = ca._Cache(ca.E4M3, 512, 0, 64, None, 0, None, 0, 0)
     rc = lib.ca_hca_attend_decode(ctypes.byref(ap), None, None, ctypes.byref(cache), 128, None, 1, 0, None, 1, None,

@@ -189,6 +189,17 @@ def run_decode(cfg, seqs=None, check_batch_invariance=True, ctx=None, mutate=Non
             ov = oracle.load_entries(oracle.FMT_BY_NAME[cfg.kv], cfg.D, cfg.R, cfg.page, st["pool"],
                                      st["page_table"][b], 0, n)
             check_stored(gv, ov, cfg.kv, cfg.D, cfg.R, f"{layer} cache seq {b}")
+        # the fused append (one launch) leaves bitwise the state of the separate stages below:
+        # run it, keep its result, restore the state, then run the separate stages
+        state = {"window": gl.window, "tail": gl.tail, "kv": gl.kv.pool}
+        if layer == "csa":
+            state.update(itail=gl.itail, ik=gl.ik.pool)
+        before = {k: v.clone() for k, v in state.items()}
+        gl.append()
+        fused = {k: v.clone() for k, v in state.items()}
+        for k, v in state.items():
+            v.copy_(before[k])
+        del before
         # window ring after the step's append
         gl.append_token()
         torch.cuda.synchronize()
@@ -217,6 +228,9 @@ def run_decode(cfg, seqs=None, check_batch_invariance=True, ctx=None, mutate=Non
                 ov = oracle.load_entries(fmtn, dim, rope_dim, cfg.page, tmp, ptr, i, 1)
                 gv = pool_values(cache, b, i + 1)[i:i + 1]
                 check_stored(gv, ov, fmt_name, dim, rope_dim, f"{layer} decode-emitted entry seq {b}", max_frac=0.05)
+        for k, v in state.items():
+            assert torch.equal(fused[k], v), f"{layer}: fused decode append differs from the separate stages in {k}"
+        del fused
         if layer == "csa":
             step = opl.csa_decode_step(cfg, inp, st)
             ik_o = gpu_cache_from(st["ipool"], st["page_table"], oracle.FMT_BY_NAME[cfg.idx], cfg.cI, 0, cfg.page)
