@@ -120,3 +120,11 @@ def test_cfg5_million_token_decode_fp4_indexer():
     from long_context_attention_17_amd.configs import CONFIGS
     from test_gpu_small import run_decode
     run_decode(dataclasses.replace(CONFIGS[5], idx="fp4", name="million_decode_b8_fp4idx"))
+
+
+def test_cfg5_million_token_decode_fp4_queries():
+    """The million-token decode with FP4 indexer keys and queries (e2m1 x e2m1 scaled MFMA)."""
+    import dataclasses
+    from long_context_attention_17_amd.configs import CONFIGS
+    from test_gpu_small import run_decode
+    run_decode(dataclasses.replace(CONFIGS[5], idx="fp4", idx_q="fp4", name="million_decode_b8_fp4_indexer"))
