@@ -207,8 +207,10 @@ def bench_decode(cfg, steps, warmup, replicas, args):
                 ("hca_append", h.append), ("hca_attend", h.attend)]
 
     def step(i):
-        for _, fn in stages_of(i):
-            fn()
+        # each layer's step is one library call (ca_csa_decode_step / ca_hca_decode_step): the
+        # stages above, with the query preparation and top-k state clearing in the append launch
+        layer_objs["csa"][i % replicas].fused_step()
+        layer_objs["hca"][i % replicas].fused_step()
 
     progress("warmup (eager)")
     for i in range(warmup):
@@ -297,9 +299,10 @@ def bench_decode(cfg, steps, warmup, replicas, args):
         "kernel_rooflines": {k: kernel_roofline(*roof_of[k], kt[k][0]) for k in roof_of},
         "kernel_timing_queued": queued,
         "wall_s_timed": round(wall, 4),
-        "timing": "whole step: HIP-graph replays (one graph per cache replica); stages: per-stage graphs "
-                  "replayed back to back between HIP events; kernels: HIP events recorded by the library "
-                  "around each eager launch on its stream",
+        "timing": "whole step: HIP-graph replays (one graph per cache replica) of one ca_csa_decode_step "
+                  "and one ca_hca_decode_step call; stages: the separate calls (append, index_topk, attend), "
+                  "per-stage graphs replayed back to back between HIP events; kernels: HIP events recorded by "
+                  "the library around each eager launch on its stream",
     }
     config = {"workload": f"{cfg.name}: decode step of one CSA + one HCA layer, batch {cfg.B}, "
                           f"context {cfg.ctx_lo}-{cfg.ctx_hi}, {cfg.n_h} heads, D={cfg.D}, kv {cfg.kv}, "

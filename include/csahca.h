@@ -339,6 +339,35 @@ int ca_timer_read(int32_t kernel, double* total_ms, int64_t* launches);
 /* Waits for pending timed launches, destroys the events, stops timing. */
 int ca_timer_stop(void);
 
+/* ------------------------------------------------------------------------ */
+/* Decode steps: a layer's whole decode step in one call, for callers that  */
+/* run the layer as one unit (Ch.5 "Decode-time cache state", Ch.6, Ch.7).  */
+/* ca_csa_decode_step does what these calls do, in this order, with the    */
+/* same results bit for bit:                                                */
+/*   ca_decode_append(wp, kv_raw, w_gain, pos, B, window, W, S, jobs, 2)    */
+/*     (jobs[0]: the main entry, jobs[1]: the indexer key);                 */
+/*   ca_index_topk_decode(ip, qI, wI, pos, B, max_pos, jobs[1].cache, idx,  */
+/*     cnt, NULL, NULL, 0, iws, iws_bytes);                                 */
+/*   ca_csa_attend_decode(ap, q, q_gain, jobs[0].cache, idx, cnt, ip->k,    */
+/*     jobs[0].params.ratio, pos, B, max_pos, window, W, sink, out, lse,    */
+/*     ws, ws_bytes).                                                       */
+/* ca_hca_decode_step likewise runs ca_decode_append with its one job and   */
+/* ca_hca_attend_decode.  Fewer launches: the append launch also prepares   */
+/* the attention queries of split rows and clears the long top-k state.    */
+/* Arguments, workspaces and errors: those of the calls above (checked      */
+/* before anything is launched); ip->ratio must equal both jobs' ratios.    */
+/* ------------------------------------------------------------------------ */
+int ca_csa_decode_step(const ca_window_params* wp, const void* kv_raw, const float* w_gain, void* window, int32_t W,
+                       int32_t S, const ca_decode_entry_job* jobs, const ca_index_params* ip, const void* qI,
+                       const float* wI, int32_t* idx, int32_t* cnt, void* iws, size_t iws_bytes,
+                       const ca_attend_params* ap, const void* q, const float* q_gain, const int32_t* pos, int32_t B,
+                       int64_t max_pos, const float* sink, void* out, float* lse, void* ws, size_t ws_bytes,
+                       void* stream);
+int ca_hca_decode_step(const ca_window_params* wp, const void* kv_raw, const float* w_gain, void* window, int32_t W,
+                       int32_t S, const ca_decode_entry_job* job, const ca_attend_params* ap, const void* q,
+                       const float* q_gain, const int32_t* pos, int32_t B, int64_t max_pos, const float* sink,
+                       void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -93,6 +93,13 @@ _SIGS = {
                                              _I64, _I64, _P, _P, _P, _SZ, _P]),
     "ca_hca_attend_decode": (ctypes.c_int, [ctypes.POINTER(AttendParams), _P, _P, _PC, _I32, _P, _I32, _I64, _P,
                                             _I32, _P, _P, _P, _P, _SZ, _P]),
+    "ca_csa_decode_step": (ctypes.c_int, [ctypes.POINTER(WindowParams), _P, _P, _P, _I32, _I32,
+                                          ctypes.POINTER(DecodeEntryJob), ctypes.POINTER(IndexParams), _P, _P, _P, _P,
+                                          _P, _SZ, ctypes.POINTER(AttendParams), _P, _P, _P, _I32, _I64, _P, _P, _P,
+                                          _P, _SZ, _P]),
+    "ca_hca_decode_step": (ctypes.c_int, [ctypes.POINTER(WindowParams), _P, _P, _P, _I32, _I32,
+                                          ctypes.POINTER(DecodeEntryJob), ctypes.POINTER(AttendParams), _P, _P, _P,
+                                          _I32, _I64, _P, _P, _P, _P, _SZ, _P]),
     "ca_timer_start": (ctypes.c_int, [ctypes.c_uint32, _I64]),
     "ca_timer_read": (ctypes.c_int, [_I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64)]),
     "ca_timer_stop": (ctypes.c_int, []),
@@ -188,14 +195,40 @@ def decode_append(wp: WindowParams, kv_raw, w_gain, window, pos, jobs, stream=No
     """Window append of row b's token (sequence b) plus the compressor steps of `jobs`, each
     (CompressParams, new_rows, tail, Ba, Bb, gain, Cache), in one launch."""
     S, W = window.shape[0], window.shape[1]
+    _check(_lib.ca_decode_append(ctypes.byref(wp), _ptr(kv_raw), _ptr(w_gain), _ptr(pos), pos.shape[0],
+                                 _ptr(window), W, S, _jobs_array(jobs), len(jobs), _stream(stream)))
+
+
+def _jobs_array(jobs):
     arr = (DecodeEntryJob * len(jobs))()
-    keep = []
     for q, (p, new_rows, tail, Ba, Bb, gain, cache) in enumerate(jobs):
         arr[q] = DecodeEntryJob(p, _ptr(new_rows), _ptr(tail), _ptr(Ba), _ptr(Bb), _ptr(gain),
                                 ctypes.pointer(cache.desc))
-        keep.append(cache)
-    _check(_lib.ca_decode_append(ctypes.byref(wp), _ptr(kv_raw), _ptr(w_gain), _ptr(pos), pos.shape[0],
-                                 _ptr(window), W, S, arr, len(jobs), _stream(stream)))
+    return arr
+
+
+def csa_decode_step(wp: WindowParams, kv_raw, w_gain, window, jobs, ip: IndexParams, qI, wI, idx, cnt, iws,
+                    ap: AttendParams, q, q_gain, pos, max_pos: int, sink, out, ws, lse=None, stream=None):
+    """A CSA layer's decode step in one call (jobs: the main entry's and the indexer key's
+    (CompressParams, new_rows, tail, Ba, Bb, gain, Cache)); the same results as
+    decode_append + index_topk_decode + csa_attend_decode."""
+    S, W = window.shape[0], window.shape[1]
+    _check(_lib.ca_csa_decode_step(ctypes.byref(wp), _ptr(kv_raw), _ptr(w_gain), _ptr(window), W, S,
+                                   _jobs_array(jobs), ctypes.byref(ip), _ptr(qI), _ptr(wI), _ptr(idx), _ptr(cnt),
+                                   _ptr(iws), iws.numel(), ctypes.byref(ap), _ptr(q), _ptr(q_gain), _ptr(pos),
+                                   pos.shape[0], max_pos, _ptr(sink), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
+                                   _stream(stream)))
+
+
+def hca_decode_step(wp: WindowParams, kv_raw, w_gain, window, job, ap: AttendParams, q, q_gain, pos, max_pos: int,
+                    sink, out, ws, lse=None, stream=None):
+    """An HCA layer's decode step in one call; the same results as decode_append +
+    hca_attend_decode."""
+    S, W = window.shape[0], window.shape[1]
+    _check(_lib.ca_hca_decode_step(ctypes.byref(wp), _ptr(kv_raw), _ptr(w_gain), _ptr(window), W, S,
+                                   _jobs_array([job]), ctypes.byref(ap), _ptr(q), _ptr(q_gain), _ptr(pos),
+                                   pos.shape[0], max_pos, _ptr(sink), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
+                                   _stream(stream)))
 
 
 def index_topk_workspace(p: IndexParams, n_rows: int, max_pos: int) -> int:

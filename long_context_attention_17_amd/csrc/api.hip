@@ -184,17 +184,16 @@ int ca_window_append(const ca_window_params* p, const void* kv_raw, const float*
                     "ca_window_append");
 }
 
-int ca_decode_append(const ca_window_params* wp, const void* kv_raw, const float* w_gain, const int32_t* pos,
-                     int32_t B, void* window, int32_t W, int32_t S_, const ca_decode_entry_job* jobs, int32_t n_jobs,
-                     void* stream) {
-  const char* what = "ca_decode_append";
+// Validates a decode append (ca_decode_append's checks) and fills its launch jobs.
+static int append_plan(const ca_window_params* wp, const void* kv_raw, const float* w_gain, const int32_t* pos,
+                       int32_t B, void* window, int32_t W, int32_t S_, const ca_decode_entry_job* jobs,
+                       int32_t n_jobs, ca::DecodeWindowJob* wjob, ca::DecodeEntryJob* ej, const char* what) {
   if (wp == nullptr) return fail(CA_ERR_ARG, "%s: window params NULL", what);
   if (wp->dim <= 0 || wp->dim > 1024) return fail(CA_ERR_UNSUPPORTED, "%s: window dim outside 1..1024", what);
   if (wp->rope_dim < 0 || wp->rope_dim > wp->dim || (wp->rope_dim & 1)) return fail(CA_ERR_ARG, "%s: bad rope_dim", what);
   if (!is_act(wp->in_format) || !is_act(wp->win_format)) return fail(CA_ERR_DTYPE, "%s: formats must be F32/BF16", what);
   if (n_jobs < 1 || n_jobs > 2 || jobs == nullptr) return fail(CA_ERR_ARG, "%s: n_jobs must be 1 or 2", what);
   if (B < 0 || W <= 0 || S_ < B) return fail(CA_ERR_ARG, "%s: bad B/W/S (S must hold every row's sequence)", what);
-  ca::DecodeEntryJob ej[2];
   for (int q = 0; q < n_jobs; ++q) {
     const ca_decode_entry_job& j = jobs[q];
     if (int e = check_compress(&j.params, j.cache, &ej[q].cv, what)) return e;
@@ -214,10 +213,21 @@ int ca_decode_append(const ca_window_params* wp, const void* kv_raw, const float
     ej[q].eps = j.params.eps;
     ej[q].base = j.params.rope_base;
   }
-  if (B == 0) return ok();
+  if (B == 0) return CA_OK;
   if (!kv_raw || !w_gain || !window || !pos) return fail(CA_ERR_ARG, "%s: NULL argument", what);
-  ca::DecodeWindowJob wj{wp->dim, wp->rope_dim, wp->in_format, wp->win_format, kv_raw, w_gain, window, W, S_,
-                         wp->eps, wp->rope_base};
+  *wjob = ca::DecodeWindowJob{wp->dim, wp->rope_dim, wp->in_format, wp->win_format, kv_raw, w_gain, window, W, S_,
+                              wp->eps, wp->rope_base};
+  return CA_OK;
+}
+
+int ca_decode_append(const ca_window_params* wp, const void* kv_raw, const float* w_gain, const int32_t* pos,
+                     int32_t B, void* window, int32_t W, int32_t S_, const ca_decode_entry_job* jobs, int32_t n_jobs,
+                     void* stream) {
+  const char* what = "ca_decode_append";
+  ca::DecodeWindowJob wj;
+  ca::DecodeEntryJob ej[2];
+  if (int e = append_plan(wp, kv_raw, w_gain, pos, B, window, W, S_, jobs, n_jobs, &wj, ej, what)) return e;
+  if (B == 0) return ok();
   return hip_status(ca::launch_decode_append(wj, ej, n_jobs, pos, B, S(stream)), what);
 }
 
@@ -231,11 +241,38 @@ size_t ca_index_topk_workspace(const ca_index_params* p, int32_t n_rows, int64_t
   return bytes;
 }
 
+// A validated indexer call, ready to launch (n_rows == 0: nothing to do).
+struct IndexPlan {
+  ca::CacheView cv;
+  ca_index_params p;
+  const void* qI;
+  const float* w;
+  ca::RowPos rp;
+  int seq_fixed, n_rows;
+  int64_t max_pos;
+  float* scores;
+  int64_t stride;
+  void* ws_long;
+  int32_t *out_idx, *out_cnt;
+  float* out_score;
+};
+
+static hipError_t launch_index_plan(const IndexPlan& ip, hipStream_t st, bool state_zeroed) {
+  if (ip.n_rows == 0) return hipSuccess;
+  hipError_t e = ca::launch_index_scores(ip.cv, ip.p, ip.qI, ip.w, ip.rp, ip.seq_fixed, ip.n_rows, ip.max_pos,
+                                         ip.scores, ip.stride, ip.ws_long, st, state_zeroed);
+  if (e != hipSuccess) return e;
+  return ca::launch_topk(ip.scores, ip.stride, ip.rp, ip.p.ratio, ip.p.k, ip.n_rows, ip.out_idx, ip.out_cnt,
+                         ip.out_score, ip.ws_long, st);
+}
+
+// Validates an indexer call; launches it, or (plan != nullptr) only describes it.
 static int index_common(const ca_index_params* p, const void* qI, const float* w, const int32_t* pos, int64_t t0,
                         int seq_fixed,
                         int64_t n_rows, int64_t max_pos, const ca_cache* idx_cache, int32_t* out_idx,
                         int32_t* out_cnt, float* out_score, float* all_scores, int64_t all_stride, void* ws,
-                        size_t ws_bytes, void* stream, const char* what) {
+                        size_t ws_bytes, void* stream, const char* what, IndexPlan* plan = nullptr) {
+  if (plan) plan->n_rows = 0;
   if (p == nullptr) return fail(CA_ERR_ARG, "%s: params NULL", what);
   ca::CacheView cv;
   if (int e = make_view(idx_cache, &cv, what)) return e;
@@ -272,13 +309,13 @@ static int index_common(const ca_index_params* p, const void* qI, const float* w
     if (ca::topk_use_long(stride, p->k))
       ws_long = (char*)ws + align256((size_t)n_rows * stride * sizeof(float));
   }
-  const ca::RowPos rp{pos, (int)t0};
-  hipError_t e = ca::launch_index_scores(cv, *p, qI, w, rp, seq_fixed, (int)n_rows, max_pos, scores, stride,
-                                         ws_long, S(stream));
-  if (e != hipSuccess) return hip_status(e, what);
-  e = ca::launch_topk(scores, stride, rp, p->ratio, p->k, (int)n_rows, out_idx, out_cnt, out_score, ws_long,
-                      S(stream));
-  return hip_status(e, what);
+  IndexPlan ip{cv, *p, qI, w, ca::RowPos{pos, (int)t0}, seq_fixed, (int)n_rows, max_pos, scores, stride, ws_long,
+               out_idx, out_cnt, out_score};
+  if (plan) {
+    *plan = ip;
+    return CA_OK;
+  }
+  return hip_status(launch_index_plan(ip, S(stream), false), what);
 }
 
 int ca_index_topk_prefill(const ca_index_params* p, const void* qI, const float* w, int64_t L, int64_t t0,
@@ -318,7 +355,8 @@ static int attend_common(const ca_attend_params* p, const void* q, const float* 
                          int mode, int seq_fixed, const int32_t* pos, int64_t t0, int64_t n_rows, int64_t max_pos,
                          const int32_t* idx, const int32_t* cnt, int k, int ratio, const void* window, int W,
                          int win_rows, const float* sink, void* out, float* lse, void* ws, size_t ws_bytes,
-                         void* stream, bool decode, const char* what) {
+                         void* stream, bool decode, const char* what, ca::AttendArgs* plan = nullptr) {
+  if (plan) plan->n_rows = 0;
   if (p == nullptr) return fail(CA_ERR_ARG, "%s: params NULL", what);
   ca::AttendArgs a;
   if (int e = make_view(kv, &a.kv, what)) return e;
@@ -407,6 +445,10 @@ static int attend_common(const ca_attend_params* p, const void* q, const float* 
     a.part_ml = (float*)((char*)ws + po);
     if (ca::attend_mfma_supported(a)) a.q_prep = (uint16_t*)((char*)ws + po + pm);
   }
+  if (plan) {
+    *plan = a;
+    return CA_OK;
+  }
   return hip_status(ca::launch_attend(a, S(stream)), what);
 }
 
@@ -441,6 +483,62 @@ int ca_hca_attend_decode(const ca_attend_params* p, const void* q, const float* 
                          void* stream) {
   return attend_common(p, q, q_gain, kv, 1, -1, pos, 0, B, max_pos, nullptr, nullptr, 0, ratio, window, W, B, sink, out,
                        lse, ws, ws_bytes, stream, true, "ca_hca_attend_decode");
+}
+
+// ------------------------------------------------------------------ decode steps
+// A layer's whole decode step: append (+ CSA indexer and top-k) + attention, with
+// the query preparation and the top-k state clearing done by the append launch.
+static int decode_step(const ca_window_params* wp, const void* kv_raw, const float* w_gain, void* window, int32_t W,
+                       int32_t S_, const ca_decode_entry_job* jobs, int32_t n_jobs, const ca_index_params* ip,
+                       const void* qI, const float* wI, int32_t* idx, int32_t* cnt, void* iws, size_t iws_bytes,
+                       const ca_attend_params* ap, const void* q, const float* q_gain, const int32_t* pos, int32_t B,
+                       int64_t max_pos, const float* sink, void* out, float* lse, void* ws, size_t ws_bytes,
+                       void* stream, bool csa, const char* what) {
+  ca::DecodeWindowJob wj;
+  ca::DecodeEntryJob ej[2];
+  if (int e = append_plan(wp, kv_raw, w_gain, pos, B, window, W, S_, jobs, n_jobs, &wj, ej, what)) return e;
+  if (max_pos < 0) return fail(CA_ERR_ARG, "%s: negative max_pos", what);
+  IndexPlan iplan;
+  iplan.n_rows = 0;
+  if (csa) {
+    if (ip == nullptr) return fail(CA_ERR_ARG, "%s: index params NULL", what);
+    if (ip->ratio != jobs[0].params.ratio || ip->ratio != jobs[1].params.ratio)
+      return fail(CA_ERR_ARG, "%s: indexer and compressor ratios differ", what);
+    if (int e = index_common(ip, qI, wI, pos, 0, -1, B, max_pos, jobs[1].cache, idx, cnt, nullptr, nullptr, 0, iws,
+                             iws_bytes, stream, what, &iplan))
+      return e;
+  }
+  ca::AttendArgs aplan;
+  if (int e = attend_common(ap, q, q_gain, jobs[0].cache, csa ? 0 : 1, -1, pos, 0, B, max_pos, idx, cnt,
+                            csa ? ip->k : 0, jobs[0].params.ratio, window, W, B, sink, out, lse, ws, ws_bytes, stream,
+                            true, what, &aplan))
+    return e;
+  if (B == 0) return ok();
+  uint32_t* zero = iplan.n_rows > 0 && iplan.ws_long != nullptr ? (uint32_t*)iplan.ws_long : nullptr;
+  hipError_t e = ca::launch_decode_front(wj, ej, n_jobs, pos, B, aplan.q_prep ? &aplan : nullptr, zero,
+                                         zero ? ca::kTopkRowWords : 0, S(stream));
+  if (e == hipSuccess && csa) e = launch_index_plan(iplan, S(stream), zero != nullptr);
+  if (e == hipSuccess) e = ca::launch_attend(aplan, S(stream), aplan.q_prep != nullptr);
+  return hip_status(e, what);
+}
+
+int ca_csa_decode_step(const ca_window_params* wp, const void* kv_raw, const float* w_gain, void* window, int32_t W,
+                       int32_t S_, const ca_decode_entry_job* jobs, const ca_index_params* ip, const void* qI,
+                       const float* wI, int32_t* idx, int32_t* cnt, void* iws, size_t iws_bytes,
+                       const ca_attend_params* ap, const void* q, const float* q_gain, const int32_t* pos, int32_t B,
+                       int64_t max_pos, const float* sink, void* out, float* lse, void* ws, size_t ws_bytes,
+                       void* stream) {
+  return decode_step(wp, kv_raw, w_gain, window, W, S_, jobs, 2, ip, qI, wI, idx, cnt, iws, iws_bytes, ap, q, q_gain,
+                     pos, B, max_pos, sink, out, lse, ws, ws_bytes, stream, true, "ca_csa_decode_step");
+}
+
+int ca_hca_decode_step(const ca_window_params* wp, const void* kv_raw, const float* w_gain, void* window, int32_t W,
+                       int32_t S_, const ca_decode_entry_job* job, const ca_attend_params* ap, const void* q,
+                       const float* q_gain, const int32_t* pos, int32_t B, int64_t max_pos, const float* sink,
+                       void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return decode_step(wp, kv_raw, w_gain, window, W, S_, job, 1, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                     0, ap, q, q_gain, pos, B, max_pos, sink, out, lse, ws, ws_bytes, stream, false,
+                     "ca_hca_decode_step");
 }
 
 }  // extern "C"

@@ -22,6 +22,7 @@
 //   per (row, head), items streamed from global memory; used for fp32 caches.
 #include "common.h"
 #include "kernels.h"
+#include "qprep.h"
 
 namespace ca {
 
@@ -768,53 +769,11 @@ __device__ __forceinline__ float mx_probs(const float* sv, float m_run, bf16x8* 
 }
 
 // Queries of every (row, head) prepared once per row for rows whose items are
-// split over several workgroups: RMSNorm with gain, RoPE at the row's position,
-// logit scale * log2(e), in bf16 (the arithmetic of the MFMA kernel's own query
-// transform).  One wavefront per (row, head), lane l holding channels 8l .. 8l+7.
+// split over several workgroups (qprep_head): one wavefront per (row, head).
 __global__ void __launch_bounds__(256) attend_qprep_kernel(AttendArgs a) {
-  const int r = blockIdx.x, h = blockIdx.y * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
   if (h >= a.n_heads) return;
-  constexpr int CC = kD - kR;
-  const int t = a.pos ? a.pos[r] : a.t0 + r;
-  const int64_t off = ((int64_t)r * a.n_heads + h) * kD + 8 * lane;
-  const u32x4 w = *(const u32x4*)((const uint16_t*)a.q + off);
-  float x[8];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    x[2 * e] = __uint_as_float(w[e] << 16);
-    x[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
-  }
-  float ss = 0.0f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
-  const float inv = 1.0f / sqrtf(ss / (float)kD + a.eps);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] *= inv * a.q_gain[8 * lane + e];
-  if (8 * lane >= CC) {
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const int p = (8 * lane + e - CC) >> 1;
-      double th = 1.0, bp = a.rope_step;
-#pragma unroll
-      for (int k = 0; k < 5; ++k) {
-        th = ((p >> k) & 1) ? th * bp : th;
-        bp *= bp;
-      }
-      const double rev = (double)t * th * 0.15915494309189535;   // 1 / (2 pi)
-      const float fr = (float)(rev - floor(rev));
-      const float c = __builtin_amdgcn_cosf(fr), sn = __builtin_amdgcn_sinf(fr);
-      const float x0 = x[e], x1 = x[e + 1];
-      x[e] = x0 * c - x1 * sn;
-      x[e + 1] = x0 * sn + x1 * c;
-    }
-  }
-  u32x4 o;
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    o[e] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)(x[2 * e] * a.scale_log2), (__bf16)(x[2 * e + 1] * a.scale_log2)});
-  *(u32x4*)(a.q_prep + off) = o;
+  qprep_head(a, blockIdx.x, h, threadIdx.x & 63);
 }
 
 // MODE 0: CSA (the row's selected entries), 1: HCA (all of the row's entries);
@@ -1170,7 +1129,7 @@ bool attend_mfma_supported(const AttendArgs& a) {
          (a.kv.fmt == CA_BF16 || a.kv.fmt == CA_FP8MIX) && fits;
 }
 
-hipError_t launch_attend(const AttendArgs& args, hipStream_t st) {
+hipError_t launch_attend(const AttendArgs& args, hipStream_t st, bool q_prepared) {
   if (args.n_rows == 0) return hipSuccess;
   AttendArgs a = args;
   a.part_acc = attend_mfma_supported(a) ? 1 : 0;
@@ -1179,7 +1138,7 @@ hipError_t launch_attend(const AttendArgs& args, hipStream_t st) {
   hipEvent_t ev0, ev1;
   timer_events(a.mode == 0 ? CA_TIMED_CSA_ATTEND : CA_TIMED_HCA_ATTEND, st, &ev0, &ev1);
   if (attend_mfma_supported(a)) {
-    if (a.q_prep != nullptr)
+    if (a.q_prep != nullptr && !q_prepared)
       hipLaunchKernelGGL(attend_qprep_kernel, dim3(a.n_rows, a.n_heads / 4), dim3(256), 0, st, a);
     const long units = (long)a.n_rows * (a.n_heads / 64) * splits;
     dim3 grid((unsigned)(units < cu_count() ? units : cu_count()));

@@ -15,6 +15,7 @@
 // bound by HBM reads of the rows; they are a small share of any step.
 #include "common.h"
 #include "kernels.h"
+#include "qprep.h"
 
 namespace ca {
 
@@ -230,21 +231,35 @@ __global__ void window_append_kernel(int D, int R, int in_fmt, int win_fmt, cons
                     red);
 }
 
-// One decode step's token-level updates of a layer in one launch: workgroup (b, 0)
-// appends sequence b's new token (row b) to its window, workgroup (b, 1 + q) runs entry job
-// q's compressor step for it.  Each workgroup does exactly what the workgroup of
-// the separate launch does, so the results are the same bit for bit.
-__global__ void decode_append_kernel(DecodeWindowJob wj, DecodeEntryJob e0, DecodeEntryJob e1, const int32_t* pos) {
+// The front of a decode step of a layer in one launch.  For row b (sequence b):
+// workgroup (b, 0) appends the new token to its window, (b, 1 + q) runs entry job q's
+// compressor step, then (optionally) ceil(n_heads / waves) workgroups prepare the
+// row's attention queries (one wavefront per head), and one clears the row's long
+// top-k state.  Each workgroup does exactly what the workgroup of the separate
+// launch does, so the results are the same bit for bit.
+__global__ void decode_front_kernel(DecodeWindowJob wj, DecodeEntryJob e0, DecodeEntryJob e1, int n_jobs,
+                                    AttendArgs qa, uint32_t* zero, int zero_words, const int32_t* pos) {
   __shared__ float red[16];
-  const int b = blockIdx.x, j = threadIdx.x;
-  if (blockIdx.y == 0) {
+  const int b = blockIdx.x, j = threadIdx.x, y = blockIdx.y;
+  if (y == 0) {
     window_append_row(wj.D, wj.R, wj.in_fmt, wj.win_fmt, wj.raw, wj.gain, pos, nullptr, wj.window, wj.W, wj.S,
                       wj.eps, wj.base, b, j, red, true);
     return;
   }
-  const DecodeEntryJob& e = blockIdx.y == 1 ? e0 : e1;
-  compress_decode_row(e.cv, e.m, e.overlap, e.in_fmt, e.new_rows, pos, e.tail, e.Ba, e.Bb, e.gain, e.eps,
-                      e.apply_rope, e.base, b, j, red);
+  if (y <= n_jobs) {
+    const DecodeEntryJob& e = y == 1 ? e0 : e1;
+    compress_decode_row(e.cv, e.m, e.overlap, e.in_fmt, e.new_rows, pos, e.tail, e.Ba, e.Bb, e.gain, e.eps,
+                        e.apply_rope, e.base, b, j, red);
+    return;
+  }
+  const int hpb = blockDim.x >> 6;                     // heads per workgroup
+  const int n_q = qa.q_prep != nullptr ? (qa.n_heads + hpb - 1) / hpb : 0;
+  if (y <= n_jobs + n_q) {
+    const int h = (y - 1 - n_jobs) * hpb + (j >> 6);
+    if (h < qa.n_heads) qprep_head(qa, b, h, j & 63);
+    return;
+  }
+  for (int i = j; i < zero_words; i += blockDim.x) zero[(int64_t)b * zero_words + i] = 0u;
 }
 
 // ----------------------------------------------------------------- launchers
@@ -280,14 +295,24 @@ hipError_t launch_store_entries(const CacheView& cv, int seq, int64_t first, int
   return hipGetLastError();
 }
 
-hipError_t launch_decode_append(const DecodeWindowJob& wj, const DecodeEntryJob* jobs, int n_jobs,
-                                const int32_t* pos, int B, hipStream_t st) {
+hipError_t launch_decode_front(const DecodeWindowJob& wj, const DecodeEntryJob* jobs, int n_jobs,
+                               const int32_t* pos, int B, const AttendArgs* qa, uint32_t* zero, int zero_words,
+                               hipStream_t st) {
   if (B == 0) return hipSuccess;
   int threads = block_for(wj.D);
   for (int q = 0; q < n_jobs; ++q) threads = block_for(jobs[q].cv.dim) > threads ? block_for(jobs[q].cv.dim) : threads;
-  hipLaunchKernelGGL(decode_append_kernel, dim3(B, 1 + n_jobs), dim3(threads), 0, st, wj, jobs[0],
-                     n_jobs > 1 ? jobs[1] : jobs[0], pos);
+  AttendArgs a{};
+  if (qa != nullptr && qa->q_prep != nullptr) a = *qa;
+  const int n_q = a.q_prep != nullptr ? (a.n_heads + threads / 64 - 1) / (threads / 64) : 0;
+  const int n_zero = zero != nullptr && zero_words > 0 ? 1 : 0;
+  hipLaunchKernelGGL(decode_front_kernel, dim3(B, 1 + n_jobs + n_q + n_zero), dim3(threads), 0, st, wj, jobs[0],
+                     n_jobs > 1 ? jobs[1] : jobs[0], n_jobs, a, n_zero ? zero : nullptr, n_zero ? zero_words : 0, pos);
   return hipGetLastError();
+}
+
+hipError_t launch_decode_append(const DecodeWindowJob& wj, const DecodeEntryJob* jobs, int n_jobs,
+                                const int32_t* pos, int B, hipStream_t st) {
+  return launch_decode_front(wj, jobs, n_jobs, pos, B, nullptr, nullptr, 0, st);
 }
 
 hipError_t launch_window_append(const ca_window_params& p, const void* raw, const float* gain, const int32_t* pos,

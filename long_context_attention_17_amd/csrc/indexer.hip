@@ -502,6 +502,7 @@ constexpr int kResolveThreads = 1024;
 constexpr int kSortMax = 8192;        // largest k of the long path
 constexpr int kMetaWords = 4;         // per row: candidates appended, (spare), b*, keys above b*
 constexpr int kRowWords = kHistBins + kMetaWords;   // per-row state: histogram, then the counters
+static_assert(kRowWords == kTopkRowWords, "per-row long top-k state size");
 constexpr int kRegCand = 4;            // candidates per resolve thread held in registers
 constexpr int kBitmapLdsWords = 16384;  // two LDS bitmaps of rows up to 262,144 keys (larger rows: workspace)
 
@@ -795,14 +796,14 @@ __global__ void __launch_bounds__(kResolveThreads) topk_resolve_kernel(const flo
 // ------------------------------------------------------------------ launchers
 hipError_t launch_index_scores(const CacheView& cv, const ca_index_params& p, const void* qI, const float* w,
                                RowPos pos, int seq_fixed, int n_rows, int64_t max_pos, float* scores,
-                               int64_t stride, void* ws_long, hipStream_t st) {
+                               int64_t stride, void* ws_long, hipStream_t st, bool state_zeroed) {
   if (n_rows == 0) return hipSuccess;
   const int64_t max_ne = max_pos / p.ratio;
   const bool long_rows = ws_long != nullptr && topk_use_long(stride, p.k);
   uint32_t* state = long_rows ? (uint32_t*)ws_long : nullptr;   // per-row histograms and counters
   const bool mfma = max_ne > 0 && (cv.fmt == CA_E4M3 || cv.fmt == CA_FP4) && p.n_heads == 8 && p.dim == 64 &&
                    cv.page_shift >= 4;
-  if (long_rows) {   // cleared before the scoring launch, which may add to the histograms
+  if (long_rows && !state_zeroed) {   // cleared before the scoring launch, which may add to the histograms
     const int64_t nz = (int64_t)n_rows * kRowWords;
     hipLaunchKernelGGL(topk_zero_kernel, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, st, state, nz);
   }

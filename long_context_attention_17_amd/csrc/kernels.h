@@ -40,8 +40,6 @@ struct DecodeEntryJob {
   float eps;
   double base;
 };
-hipError_t launch_decode_append(const DecodeWindowJob& wj, const DecodeEntryJob* jobs, int n_jobs,
-                                const int32_t* pos, int B, hipStream_t st);
 
 // Position of query row r: pos[r] (decode), or t0 + r (prefill rows of one sequence).
 struct RowPos {
@@ -51,10 +49,12 @@ struct RowPos {
 };
 
 // Scores of every eligible block.  With ws_long (the multi-workgroup top-k state,
-// used when the rows are long) the per-row key histograms are also cleared and filled.
+// used when the rows are long) the per-row key histograms are also cleared (unless
+// state_zeroed: the caller cleared the kTopkRowWords words per row already) and filled.
+constexpr int kTopkRowWords = 4096 + 4;   // per-row long top-k state: histogram bins, then 4 counters
 hipError_t launch_index_scores(const CacheView& cv, const ca_index_params& p, const void* qI, const float* w,
                                RowPos pos, int seq_fixed, int n_rows, int64_t max_pos, float* scores,
-                               int64_t stride, void* ws_long, hipStream_t st);
+                               int64_t stride, void* ws_long, hipStream_t st, bool state_zeroed = false);
 // Top-k over score rows.  With ws_long (topk_long_workspace bytes) and rows longer than
 // one workgroup's LDS, the multi-workgroup histogram / gather / resolve path runs.
 size_t topk_long_workspace(int n_rows, int64_t stride);
@@ -105,7 +105,18 @@ constexpr int kDecodeMaxSplits = 16;
 
 bool attend_mfma_supported(const AttendArgs& a);
 int attend_mfma_max_items();  // items one MFMA workgroup handles without splitting
-hipError_t launch_attend(const AttendArgs& a, hipStream_t st);
+// q_prepared: split rows' queries are already in a.q_prep (no query-prep launch).
+hipError_t launch_attend(const AttendArgs& a, hipStream_t st, bool q_prepared = false);
+
+// The front of a decode step (ca_decode_append, ca_*_decode_step): the window append
+// of every row b (sequence b) and one or two compressor steps, plus optionally the
+// query preparation of qa (when qa->q_prep != nullptr) and the clearing of
+// zero_words words per row at zero, in one launch.
+hipError_t launch_decode_front(const DecodeWindowJob& wj, const DecodeEntryJob* jobs, int n_jobs,
+                               const int32_t* pos, int B, const AttendArgs* qa, uint32_t* zero, int zero_words,
+                               hipStream_t st);
+hipError_t launch_decode_append(const DecodeWindowJob& wj, const DecodeEntryJob* jobs, int n_jobs,
+                                const int32_t* pos, int B, hipStream_t st);
 
 // Launch timing of the timed kernels (ids: ca_timed_kernel): the start / stop
 // events for the next launch of `kernel` on `st`, or false (both null) when it

@@ -206,19 +206,36 @@ class DecodeLayer:
         self.out = torch.empty(B, cfg.n_h, cfg.D, dtype=act_dtype(cfg), device=dev)
 
     # individual stages
-    def append(self):
-        """The new token's window append and compressor step(s) in one launch: the same
-        results, bit for bit, as append_token() followed by compress()."""
+    def _append_jobs(self):
         c, i = self.cfg, self.inp
         if self.layer == "csa":
-            jobs = [(compress_params(c, c.m, True, True), self.new_rows, self.tail, i["Ba"], i["Bb"], i["g_kv"],
+            return [(compress_params(c, c.m, True, True), self.new_rows, self.tail, i["Ba"], i["Bb"], i["g_kv"],
                      self.kv),
                     (compress_params(c, c.m, True, False), self.new_irows, self.itail, i["IBa"], i["IBb"], None,
                      self.ik)]
+        return [(compress_params(c, c.m_hca, False, True), self.new_rows, self.tail, i["B"], None, i["g_kv"],
+                 self.kv)]
+
+    def append(self):
+        """The new token's window append and compressor step(s) in one launch: the same
+        results, bit for bit, as append_token() followed by compress()."""
+        ca.decode_append(window_params(self.cfg), self.new_kv, self.inp["g_w"], self.window, self.pos,
+                         self._append_jobs())
+
+    def fused_step(self):
+        """The whole decode step in one library call (ca_csa_decode_step / ca_hca_decode_step):
+        the same results as step(), with the query preparation and the top-k state clearing
+        folded into the append launch."""
+        c, i = self.cfg, self.inp
+        jobs = self._append_jobs()
+        if self.layer == "csa":
+            ca.csa_decode_step(window_params(c), self.new_kv, i["g_w"], self.window, jobs, self.ip, i["qI"], i["w"],
+                               self.idx, self.cnt, self.iws, self.ap, i["q"], i["g_q"], self.pos, self.max_pos,
+                               i["sink"], self.out, self.aws)
         else:
-            jobs = [(compress_params(c, c.m_hca, False, True), self.new_rows, self.tail, i["B"], None, i["g_kv"],
-                     self.kv)]
-        ca.decode_append(window_params(c), self.new_kv, i["g_w"], self.window, self.pos, jobs)
+            ca.hca_decode_step(window_params(c), self.new_kv, i["g_w"], self.window, jobs[0], self.ap, i["q"],
+                               i["g_q"], self.pos, self.max_pos, i["sink"], self.out, self.aws)
+        return self.out
 
     def append_token(self):
         ca.window_append(window_params(self.cfg), self.new_kv, self.inp["g_w"], self.window, pos=self.pos,

@@ -199,7 +199,6 @@ def run_decode(cfg, seqs=None, check_batch_invariance=True, ctx=None, mutate=Non
         fused = {k: v.clone() for k, v in state.items()}
         for k, v in state.items():
             v.copy_(before[k])
-        del before
         # window ring after the step's append
         gl.append_token()
         torch.cuda.synchronize()
@@ -230,7 +229,6 @@ def run_decode(cfg, seqs=None, check_batch_invariance=True, ctx=None, mutate=Non
                 check_stored(gv, ov, fmt_name, dim, rope_dim, f"{layer} decode-emitted entry seq {b}", max_frac=0.05)
         for k, v in state.items():
             assert torch.equal(fused[k], v), f"{layer}: fused decode append differs from the separate stages in {k}"
-        del fused
         if layer == "csa":
             step = opl.csa_decode_step(cfg, inp, st)
             ik_o = gpu_cache_from(st["ipool"], st["page_table"], oracle.FMT_BY_NAME[cfg.idx], cfg.cI, 0, cfg.page)
@@ -283,6 +281,27 @@ def run_decode(cfg, seqs=None, check_batch_invariance=True, ctx=None, mutate=Non
         else:
             same = np.ones(B, bool)
         check_out(f64(gl.out)[same], step["out"][same], cfg.act, f"{layer} decode end-to-end ({same.sum()} rows)")
+        # the whole step in one library call (ca_*_decode_step) gives bitwise the outputs, index
+        # lists and caches of the separate calls above, from the same starting state
+        bits = (lambda t: t.view(torch.int16)) if cfg.act == "bf16" else (lambda t: t)
+        ref = {k: v.clone() for k, v in state.items()}
+        ref["out"] = bits(gl.out).clone()
+        if layer == "csa":
+            ref.update(idx=gl.idx.clone(), cnt=gl.cnt.clone())
+        for k, v in state.items():
+            v.copy_(before[k])
+        gl.out.zero_()
+        if layer == "csa":
+            gl.idx.fill_(-7)
+            gl.cnt.fill_(-7)
+        gl.fused_step()
+        torch.cuda.synchronize()
+        got = dict(state, out=bits(gl.out))
+        if layer == "csa":
+            got.update(idx=gl.idx, cnt=gl.cnt)
+        for k, v in ref.items():
+            assert torch.equal(got[k], v), f"{layer}: the one-call decode step differs from the separate calls in {k}"
+        del before, ref, fused
         results[layer] = (gl, st, step)
     return results
 
