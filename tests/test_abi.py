@@ -79,6 +79,18 @@ def test_argument_errors_are_reported_without_launching():
     rc = lib.ca_decode_append(ctypes.byref(wp), None, None, None, 8, None, 128, 8, ctypes.byref(job), 1, None)
     assert rc == -1 and b"NULL" in lib.ca_last_error()      # missing rows / ring
     assert lib.ca_decode_append(ctypes.byref(wp), None, None, None, 0, None, 128, 1, ctypes.byref(job), 1, None) == 0
+    # one-call decode steps: the checks of the calls they combine, before any launch
+    jobs = (ca.DecodeEntryJob * 2)(job, job)
+    ip = ca.IndexParams(8, 64, 8, 16, ca.BF16, 0)                          # ratio 8 vs the jobs' 4
+    ap = ca.AttendParams(64, 512, 64, 128, ca.BF16, ca.BF16, ca.BF16, 0.04, 1e-6, 1e4)
+    rc = lib.ca_csa_decode_step(ctypes.byref(wp), None, None, None, 128, 8, jobs, ctypes.byref(ip), None, None, None,
+                                None, None, 0, ctypes.byref(ap), None, None, None, 0, 0, None, None, None, None, 0, None)
+    assert rc == -1 and b"ratios differ" in lib.ca_last_error()
+    rc = lib.ca_hca_decode_step(ctypes.byref(wp), None, None, None, 128, 8, jobs, None, None, None, None, 0, 0,
+                                None, None, None, None, 0, None)
+    assert rc == -1 and b"params NULL" in lib.ca_last_error()
+    assert lib.ca_hca_decode_step(ctypes.byref(wp), None, None, None, 128, 8, jobs, ctypes.byref(ap), None, None,
+                                  None, 0, 0, None, None, None, None, 0, None) == 0          # B = 0: nothing to do
     ap = ca.AttendParams(64, 512, 64, 128, ca.BF16, ca.BF16, ca.BF16, 0.04, 1e-6, 1e4)
     cache = ca._Cache(ca.E4M3, 512, 0, 64, None, 0, None, 0, 0)
     rc = lib.ca_hca_attend_decode(ctypes.byref(ap), None, None, ctypes.byref(cache), 128, None, 1, 0, None, 1, None,
