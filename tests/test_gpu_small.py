@@ -367,6 +367,46 @@ def test_decode_batch_invariance():
     assert torch.equal(full.out[b].view(torch.int16), one.out[0].view(torch.int16))
 
 
+def test_decode_step_graph_replays():
+    """The one-call decode steps captured in a HIP graph: several replays, with eager work
+    between them, each give bitwise the eager step's outputs, index lists and caches.
+    Contexts above 65,536 tokens put the CSA rows on the multi-workgroup top-k (its state
+    is cleared by a kernel inside the step, never by a memset)."""
+    ca, configs, layers, synth = _ca()
+    cfg = _cfg(name="graph_steps", phase="decode", kv="fp8mix", n_h=64, k=512, B=3, ctx_lo=60000, ctx_hi=80000,
+               L=0, seed=5150)
+    ctx = synth.decode_contexts(cfg)
+    for layer in ("csa", "hca"):
+        log(f"[graph replays] {layer} ctx={ctx.tolist()}")
+        dl = layers.DecodeLayer(cfg, synth.decode_layer(cfg, layer, "cuda", ctx))
+
+        def snap():
+            torch.cuda.synchronize()
+            d = {"out": dl.out.view(torch.int16).clone(), "window": dl.window.view(torch.int16).clone(),
+                 "kv": dl.kv.pool.clone(), "tail": dl.tail.clone()}
+            if layer == "csa":
+                d.update(idx=dl.idx.clone(), cnt=dl.cnt.clone(), ik=dl.ik.pool.clone(), itail=dl.itail.clone())
+            return d
+
+        dl.fused_step()
+        ref = snap()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            dl.fused_step()
+        for i in range(3):
+            dl.out.zero_()
+            if layer == "csa":
+                dl.idx.fill_(-7)
+                dl.cnt.fill_(-7)
+            torch.cuda.synchronize()
+            g.replay()
+            got = snap()
+            for key, v in ref.items():
+                assert torch.equal(got[key], v), f"{layer}: graph replay {i} differs in {key}"
+            dl.step()                                   # eager work between the replays (separate calls)
+            torch.cuda.synchronize()
+
+
 def test_edge_cases_prefill():
     """Ragged and degenerate prefill shapes: fewer tokens than one block (no entries), a length
     that is not a multiple of the ratio, and k larger than every row's eligible count."""
