@@ -186,8 +186,10 @@ int ca_window_append(const ca_window_params* p, const void* kv_raw, const float*
 /*                    window, W, S, stream), and for each of the n_jobs      */
 /*   (1 or 2) jobs ca_compress_decode(&job.params, job.new_rows, pos, B,     */
 /*                    job.tail, job.Ba, job.Bb, job.gain, job.cache, stream) */
-/* (CSA: the main entry and the indexer key; HCA: the entry).  The jobs     */
-/* must not share a tail ring or a cache.  S >= B.  Errors: as the separate */
+/* (CSA: the main entry and the indexer key; HCA: the entry).  kv_raw:     */
+/* [B, wp->dim] raw rows of the new tokens (wp->in_format); window:         */
+/* [S, W, wp->dim] ring (wp->win_format); pos: [B] int32.  The jobs must    */
+/* not share a tail ring or a cache.  S >= B.  Errors: as the separate      */
 /* calls (job index in the message); nothing is launched on an error.       */
 /* ------------------------------------------------------------------------ */
 typedef struct ca_decode_entry_job {
