@@ -477,8 +477,8 @@ def main():
                          "kernel for scaling HBM counter readings")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU's share of the workload; runs on more than one GPU are not "
-              "part of this build (see the sharding notes in DESIGN.md).", file=sys.stderr)
+        print("bench.py measures one GPU's share of the workload and runs on one GPU only (--gpus 1); "
+              "the library has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
     from long_context_attention_17_amd.configs import CONFIGS
     wl = WORKLOADS[args.workload]
