@@ -75,6 +75,7 @@ def lib():
             "orc_attend": (I, [I64, I, I, I, D, D, D, P, P, P, P, I, I, P, P, I, P, I, I, P, P, I,
                               I, I, P, I, P, P, P]),
             "orc_num_threads": (I, []),
+            "orc_set_num_threads": (None, [I]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -94,6 +95,11 @@ def _f64(a):
 
 def num_threads() -> int:
     return lib().orc_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads the oracle's parallel loops use from now on."""
+    lib().orc_set_num_threads(int(n))
 
 
 # ---------------------------------------------------------------- codecs

@@ -435,20 +435,21 @@ int orc_index_scores(int64_t n_rows, int nI, int cI, int m, const double* qI, co
                      const int32_t* page_table, int max_pages, const int64_t* n_avail,
                      int64_t row_stride, double* scores, int64_t* n_elig) {
   int bad = 0;
+  /* rows one after another; the keys of a row are shared out among the threads
+   * (each score is computed by one thread, in the order written above) */
+  for (int64_t r = 0; r < n_rows; ++r) {
+    int s_id = seq ? seq[r] : 0;
+    int64_t ne = pos[r] / m;
+    if (ne > n_avail[s_id]) {
+      bad = 1;
+      ne = n_avail[s_id];
+    }
+    n_elig[r] = ne;
+    const int32_t* pt = page_table + (int64_t)s_id * max_pages;
 #pragma omp parallel
-  {
-    double* key = (double*)malloc(sizeof(double) * cI);
-#pragma omp for schedule(dynamic, 1)
-    for (int64_t r = 0; r < n_rows; ++r) {
-      int s_id = seq ? seq[r] : 0;
-      int64_t ne = pos[r] / m;
-      if (ne > n_avail[s_id]) {
-#pragma omp atomic write
-        bad = 1;
-        ne = n_avail[s_id];
-      }
-      n_elig[r] = ne;
-      const int32_t* pt = page_table + (int64_t)s_id * max_pages;
+    {
+      double* key = (double*)malloc(sizeof(double) * cI);
+#pragma omp for schedule(static, 256)
       for (int64_t s = 0; s < ne; ++s) {
         orc_load_entry(idx_fmt, cI, 0, P, pool, pt, s, key);
         double acc = 0;
@@ -460,8 +461,8 @@ int orc_index_scores(int64_t n_rows, int nI, int cI, int m, const double* qI, co
         }
         scores[r * row_stride + s] = acc;
       }
+      free(key);
     }
-    free(key);
   }
   return bad ? -1 : 0;
 }
@@ -526,43 +527,47 @@ int orc_attend(int64_t n_rows, int nh, int D, int R, double base, double scale, 
                int n_win, int win_fmt, const void* win, int W, const double* sink,
                double* out, double* lse) {
   int bad = 0;
-#pragma omp parallel
-  {
-    int64_t cap = 0;
-    double* X = NULL;
-    double* z = NULL;
-    double* qh = (double*)malloc(sizeof(double) * D);
-#pragma omp for schedule(dynamic, 1)
-    for (int64_t r = 0; r < n_rows; ++r) {
-      int s_id = seq ? seq[r] : 0;
-      int64_t t = pos[r];
-      const int32_t* pt = page_table + (int64_t)s_id * max_pages;
-      int64_t ne = mode == 0 ? cnt[r] : t / ratio;
-      int64_t w0 = t - n_win + 1 < 0 ? 0 : t - n_win + 1;
-      int64_t nw = t - w0 + 1;
-      int64_t nx = ne + nw;
-      if (nx > cap) {
-        cap = nx;
-        X = (double*)realloc(X, sizeof(double) * D * cap);
-        z = (double*)realloc(z, sizeof(double) * cap);
-      }
-      int ok = 1;
-      for (int64_t j = 0; j < ne; ++j) {
-        int64_t e = mode == 0 ? idx[r * (int64_t)k + j] : j;
-        if (e < 0 || e >= n_avail[s_id] || (mode == 0 && e >= t / ratio)) { ok = 0; e = 0; }
-        orc_load_entry(kv_fmt, D, R, P, kv_pool, pt, e, X + j * (int64_t)D);
-      }
-      for (int64_t j = 0; j < nw; ++j) {
-        int64_t p = w0 + j;
-        int64_t slot = ((int64_t)s_id * W + p % W) * D;
-        double* x = X + (ne + j) * (int64_t)D;
-        if (win_fmt == 0) for (int d = 0; d < D; ++d) x[d] = ((const float*)win)[slot + d];
-        else for (int d = 0; d < D; ++d) x[d] = orc_bf16_decode(((const uint16_t*)win)[slot + d]);
-      }
-      if (!ok) {
+  int64_t cap = 0;
+  double* X = NULL;
+  /* rows one after another: a row's items are decoded once (shared out among the
+   * threads), then its heads are shared out among the threads, each head computed
+   * by one thread in the order written here */
+  for (int64_t r = 0; r < n_rows; ++r) {
+    int s_id = seq ? seq[r] : 0;
+    int64_t t = pos[r];
+    const int32_t* pt = page_table + (int64_t)s_id * max_pages;
+    int64_t ne = mode == 0 ? cnt[r] : t / ratio;
+    int64_t w0 = t - n_win + 1 < 0 ? 0 : t - n_win + 1;
+    int64_t nw = t - w0 + 1;
+    int64_t nx = ne + nw;
+    if (nx > cap) {
+      cap = nx;
+      X = (double*)realloc(X, sizeof(double) * D * cap);
+    }
+    int ok = 1;
+#pragma omp parallel for schedule(static, 64)
+    for (int64_t j = 0; j < ne; ++j) {
+      int64_t e = mode == 0 ? idx[r * (int64_t)k + j] : j;
+      if (e < 0 || e >= n_avail[s_id] || (mode == 0 && e >= t / ratio)) {
 #pragma omp atomic write
-        bad = 1;
+        ok = 0;
+        e = 0;
       }
+      orc_load_entry(kv_fmt, D, R, P, kv_pool, pt, e, X + j * (int64_t)D);
+    }
+    for (int64_t j = 0; j < nw; ++j) {
+      int64_t p = w0 + j;
+      int64_t slot = ((int64_t)s_id * W + p % W) * D;
+      double* x = X + (ne + j) * (int64_t)D;
+      if (win_fmt == 0) for (int d = 0; d < D; ++d) x[d] = ((const float*)win)[slot + d];
+      else for (int d = 0; d < D; ++d) x[d] = orc_bf16_decode(((const uint16_t*)win)[slot + d]);
+    }
+    if (!ok) bad = 1;
+#pragma omp parallel
+    {
+      double* z = (double*)malloc(sizeof(double) * (nx > 0 ? nx : 1));
+      double* qh = (double*)malloc(sizeof(double) * D);
+#pragma omp for schedule(dynamic, 1)
       for (int h = 0; h < nh; ++h) {
         orc_rmsnorm(D, q + (r * nh + h) * (int64_t)D, gq, eps, qh);
         if (R > 0) orc_rope(D, R, base, (double)t, 1, qh);
@@ -585,11 +590,11 @@ int orc_attend(int64_t n_rows, int nh, int D, int R, double base, double scale, 
         if (R > 0) orc_rope(D, R, base, (double)t, -1, o);
         if (lse) lse[r * nh + h] = mx + log(den);
       }
+      free(z);
+      free(qh);
     }
-    free(X);
-    free(z);
-    free(qh);
   }
+  free(X);
   return bad ? -1 : 0;
 }
 
@@ -599,5 +604,15 @@ int orc_num_threads(void) {
   return omp_get_max_threads();
 #else
   return 1;
+#endif
+}
+
+/* Threads of the later parallel regions (n >= 1); used to time the oracle on one core. */
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+  extern void omp_set_num_threads(int);
+  omp_set_num_threads(n > 0 ? n : 1);
+#else
+  (void)n;
 #endif
 }

@@ -629,3 +629,133 @@ def test_fp4_query_quantization_by_hand(orc):
     # e4m3 queries (one scale per head, here 2^-5) are the default: 2.5 and 5 keep their values
     e4 = opl.indexer_query_values(q, "fp4")[0, 0]
     assert e4[1] == 2.5 and e4[7] == 5.0 and not np.array_equal(e4, want)
+
+
+# ------------------------------------------------------------------ e4m3 indexer pages (fmt 3)
+def _torch_e4m3(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def test_e4m3_indexer_page_decodes_by_hand(orc):
+    """An indexer page written byte by byte per the layout ([P*c e4m3 codes][P fp32 scales],
+    structure of arrays) decodes to torch's e4m3 value of each code times the entry's stored
+    fp32 scale."""
+    c, P = 64, 4
+    rng = np.random.default_rng(41)
+    pb = orc.page_bytes(oracle.FMT_E4M3, c, 0, P)
+    assert pb == P * c + 4 * P
+    pool = rng.integers(0, 256, size=2 * pb, dtype=np.uint8)
+    codes = pool[pb:pb + P * c]
+    codes[(codes & 0x7F) == 0x7F] = 0x33                  # no NaN codes
+    scales = (2.0 ** rng.integers(-12, 4, size=P)).astype(np.float32)
+    pool[pb + P * c:pb + P * c + 4 * P] = scales.view(np.uint8)
+    pt = np.array([1, 0], np.int32)                        # entries 0..3 live in page 1
+    back = orc.load_entries(oracle.FMT_E4M3, c, 0, P, pool, pt, 0, P)
+    want = _torch_e4m3(codes).reshape(P, c) * scales.astype(np.float64)[:, None]
+    np.testing.assert_array_equal(back, want)
+
+
+def test_e4m3_indexer_store_matches_torch_rne(orc):
+    """Storing keys into an e4m3 indexer page: the entry's scale is the smallest power of two
+    2^e with amax <= 448 * 2^e (written as fp32 in the scale array), and every code is torch's
+    round-to-nearest-even e4m3 of x / 2^e; the round trip is within half an e4m3 step."""
+    c, P = 64, 4
+    rng = np.random.default_rng(42)
+    x = rng.normal(size=(6, c)) * np.exp(rng.normal(size=(6, 1)) * 4)
+    x[3] = 0.0                                              # all-zero key: scale 2^0, codes 0
+    pool = np.zeros(2 * orc.page_bytes(oracle.FMT_E4M3, c, 0, P), np.uint8)
+    pt = np.array([1, 0], np.int32)
+    oracle.finish_store(oracle.FMT_E4M3, c, 0, P, pool, pt, 0, x, norm=False, rope=False)
+    pb = orc.page_bytes(oracle.FMT_E4M3, c, 0, P)
+    for i in range(6):
+        page, slot = pt[i // P], i % P
+        base = page * pb
+        amax = np.abs(x[i]).max()
+        e = 0 if amax == 0 else int(np.ceil(np.log2(amax / 448.0)))
+        if amax > 0:                                        # the closed form, corrected at exact powers
+            e += int(amax > 448.0 * 2.0 ** e) - int(amax <= 448.0 * 2.0 ** (e - 1))
+        sc = pool[base + P * c + 4 * slot: base + P * c + 4 * slot + 4].view(np.float32)[0]
+        assert sc == np.float32(2.0 ** e), (i, sc, e)
+        want = torch.from_numpy(x[i] / 2.0 ** e).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        np.testing.assert_array_equal(pool[base + slot * c: base + (slot + 1) * c], want)
+    back = orc.load_entries(oracle.FMT_E4M3, c, 0, P, pool, pt, 0, 6)
+    for i in range(6):
+        a = np.abs(x[i])
+        e = orc.pow2_exponent(a.max())
+        # half an e4m3 step at each value's binade (2^-4 relative for normals; 2^-10 absolute
+        # below the smallest normal 2^-6), in units of the scale
+        rel = a / 2.0 ** e
+        half = np.where(rel >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(rel, 1e-300))) - 4), 2.0 ** -10)
+        assert (np.abs(back[i] - x[i]) <= half * 2.0 ** e * (1 + 1e-12)).all()
+    assert (back[3] == 0).all()
+
+
+def test_quantize_rows_e4m3_matches_torch(orc):
+    """Indexer queries: one power-of-two exponent per row (the smallest e with
+    amax <= 448 * 2^e) and torch's RNE e4m3 codes of x / 2^e."""
+    rng = np.random.default_rng(43)
+    x = rng.normal(size=(3, 5, 64)) * np.exp(rng.normal(size=(3, 5, 1)) * 3)
+    x[1, 2] = 0.0
+    x[2, 4, 7] = 448.0 * 2.0 ** -3                       # amax exactly at a power-of-two boundary
+    codes, exps = orc.quantize_rows_e4m3(x)
+    for idx in np.ndindex(3, 5):
+        a = np.abs(x[idx]).max()
+        e = exps[idx]
+        if a == 0:
+            assert e == 0 and not codes[idx].any()
+            continue
+        assert a <= 448.0 * 2.0 ** e and a > 448.0 * 2.0 ** (e - 1)
+        want = torch.from_numpy(x[idx] / 2.0 ** e).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        np.testing.assert_array_equal(codes[idx], want)
+    assert exps[2, 4] == -3
+    np.testing.assert_array_equal(orc.dequantize_rows_e4m3(codes, exps), _torch_e4m3(codes) * 2.0 ** exps[..., None])
+
+
+# ------------------------------------------------------------------ attention lse
+def test_lse_of_the_sink_worked_example(orc):
+    """Ch.7 "Learned attention sinks": real items with total exp mass 4 and a sink with
+    e^{z'} = 6.  lse is the log of the whole softmax denominator, log(4 + 6), and the
+    weight on the real items is exp(log 4 - lse) = 0.4."""
+    st = gold("sink_worked_example.json")["stated"]
+    D, n_real = 8, st["real_entries_total_exp_mass"]
+    vals = np.zeros((n_real, D))
+    vals[:, 1:] = np.random.default_rng(12).normal(size=(n_real, D - 1))
+    pool, pt = _f32_pool(orc, vals[:3], norm=False, rope=False)
+    t = 3
+    win = np.zeros((1, t + 1, D), np.float32)
+    win[0, t] = vals[3]
+    q = np.zeros((1, 2, D))
+    q[0, :, 0] = 1.0
+    sinks = [math.log(st["sink_exp"]), -50.0]               # head 1: a negligible sink
+    out, lse = orc.attend(q, [t], oracle.FMT_F32, 4, pool, pt[None], [3], 0, 1, win, 1, sinks, 0,
+                          idx=np.array([[0, 1, 2]]), cnt=[3], want_lse=True)
+    assert abs(lse[0, 0] - math.log(n_real + st["sink_exp"])) < 1e-12
+    assert abs(math.exp(math.log(n_real) - lse[0, 0]) - st["weight_on_real_entries"]) < 1e-12
+    assert abs(lse[0, 1] - math.log(n_real + math.exp(-50.0))) < 1e-12
+
+
+def test_lse_closed_form_with_scaled_logits(orc):
+    """lse = log(sum_x e^{scale q^.x} + e^{sink}) computed directly from the items the row
+    reads (an independent numpy evaluation of the definition on normalized, rotated
+    queries built by hand: a query a * e_h with RMSNorm gain 1 and no rotary channels
+    normalizes to a / sqrt(a^2 / D + eps) * e_h)."""
+    rng = np.random.default_rng(13)
+    D, n, nh = 16, 5, 3
+    vals = rng.normal(size=(n, D))
+    pool, pt = _f32_pool(orc, vals, norm=False, rope=False)
+    t = 4 * n                                               # m = 4: every entry eligible
+    win = np.zeros((1, t + 1, D), np.float32)
+    wtok = rng.normal(size=D).astype(np.float32)
+    win[0, t] = wtok
+    q = np.zeros((1, nh, D))
+    for h in range(nh):
+        q[0, h, h] = 2.5                                    # RMSNorm -> sqrt(D) e_h
+    sink = rng.normal(size=nh)
+    out, lse = orc.attend(q, [t], oracle.FMT_F32, 4, pool, pt[None], [n], 1, 4, win, 1, sink, 0, want_lse=True)
+    stored = vals.astype(np.float32).astype(np.float64)     # the fp32 pool holds the rounded values
+    items = np.concatenate([stored, wtok[None].astype(np.float64)])
+    scale = 1.0 / math.sqrt(D)
+    for h in range(nh):
+        z = scale * 2.5 / math.sqrt(2.5 ** 2 / D + 1e-6) * items[:, h]
+        want = math.log(np.exp(z).sum() + math.exp(sink[h]))
+        assert abs(lse[0, h] - want) < 1e-12, (h, lse[0, h], want)
