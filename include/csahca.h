@@ -20,7 +20,7 @@
  *  - Row-major layouts throughout.  "bf16" is bfloat16, "e4m3" is OCP FP8
  *    E4M3 (fn variant: no infinities, max 448).
  *  - Results are bitwise deterministic and, for decode, independent of which
- *    other sequences share the batch.
+ *    other sequences share the batch and of the host max_pos bound.
  */
 #ifndef CSAHCA_H
 #define CSAHCA_H
@@ -40,6 +40,17 @@ typedef enum {
   CA_ERR_WORKSPACE = -4,    /* workspace too small */
   CA_ERR_HIP = -5           /* a HIP launch failed */
 } ca_status;
+
+/* Device status bits.  Calls whose params carry a `status` pointer (a device
+ * int32 owned by the caller) OR these bits into it from the kernels, for
+ * conditions the host cannot see because they depend on device data.  The
+ * library never clears the word; nothing is reported when `status` is NULL.
+ *   CA_STATUS_POS_RANGE: a decode row's position pos[b] is negative or larger
+ *     than the call's max_pos.  The row is out of contract and treated as
+ *     empty: the indexer keeps no entry for it (cnt 0, idx all -1) and the
+ *     attention writes a zero output row (lse = the sink logit); nothing
+ *     outside the caller's buffers is read or written. */
+enum { CA_STATUS_POS_RANGE = 1 };
 
 /* Storage formats. */
 typedef enum {
@@ -161,7 +172,7 @@ int ca_compress_decode(const ca_compress_params* p, const void* new_rows, const 
 /* window"): each raw token KV row is RMSNorm-ed with `gain`, its last      */
 /* rope_dim channels rotated at the token's own position, and stored at     */
 /* window[seq, pos % W, :] (window is [S, W, dim] in win_format).  Prefill  */
-/* uses W >= L (one slot per position); decode uses a ring of W = n_win.    */
+/* uses W >= L (one slot per position); decode a ring of W >= n_win slots. */
 /* ------------------------------------------------------------------------ */
 typedef struct ca_window_params {
   int32_t dim;
@@ -232,6 +243,7 @@ typedef struct ca_index_params {
   int32_t q_format;  /* CA_F32 or CA_BF16 storage of qI */
   int32_t q_quant;   /* 0: e4m3 queries for E4M3 / FP4 pools (none for F32);
                         CA_FP4: FP4 queries (FP4 pools only; else CA_ERR_ARG) */
+  int32_t* status;   /* optional device int32 status word (CA_STATUS_* bits), or NULL */
 } ca_index_params;
 
 /* Workspace for either indexer call with n_rows query rows whose positions
@@ -247,7 +259,8 @@ int ca_index_topk_prefill(const ca_index_params* p, const void* qI, const float*
                           void* stream);
 
 /* Decode: row b is sequence b at position pos[b] (device int32 [B]);
- * max_pos (host) bounds every pos[b]. */
+ * max_pos (host) bounds every pos[b] (a row outside [0, max_pos] is kept
+ * empty and raises CA_STATUS_POS_RANGE). */
 int ca_index_topk_decode(const ca_index_params* p, const void* qI, const float* w, const int32_t* pos,
                          int32_t B, int64_t max_pos, const ca_cache* idx_cache, int32_t* out_idx,
                          int32_t* out_cnt, float* out_score, float* all_scores, int64_t all_scores_stride,
@@ -281,6 +294,7 @@ typedef struct ca_attend_params {
   float scale;         /* logit scale, 1/sqrt(D) */
   float eps;           /* RMSNorm eps of the query */
   double rope_base;
+  int32_t* status;     /* optional device int32 status word (CA_STATUS_* bits), or NULL */
 } ca_attend_params;
 
 /* Workspace for an attention call over n_rows rows whose positions are at
@@ -297,7 +311,12 @@ int ca_csa_attend_prefill(const ca_attend_params* p, const void* q, const float*
                           float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* CSA decode: row b is sequence b at position pos[b]; q [B, n_heads, D];
- * idx [B, k], cnt [B]; window ring [B, W, D]; max_pos (host) bounds pos. */
+ * idx [B, k], cnt [B]; window ring [B, W, D] with W >= n_win (CA_ERR_ARG
+ * otherwise: slots would alias); max_pos (host) bounds pos (a row outside
+ * [0, max_pos] gets a zero output and raises CA_STATUS_POS_RANGE).
+ * Decode splits each row's items into chunks by a plan that depends on the
+ * row's own item count only, so a row's result is bitwise the same whatever
+ * other rows share the batch (and whatever max_pos is). */
 int ca_csa_attend_decode(const ca_attend_params* p, const void* q, const float* q_gain, const ca_cache* kv,
                          const int32_t* idx, const int32_t* cnt, int32_t k, int32_t ratio, const int32_t* pos,
                          int32_t B, int64_t max_pos, const void* window, int32_t W, const float* sink, void* out,
@@ -309,7 +328,15 @@ int ca_hca_attend_prefill(const ca_attend_params* p, const void* q, const float*
                           int32_t seq, int32_t ratio, const void* window, int32_t W, const float* sink, int64_t L,
                           int64_t t0, void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
-/* HCA decode: row b is sequence b at position pos[b]. */
+/* Host: the split plan decode attention uses for a row of `total` items (its
+ * entries plus its window tokens): *chunk_len items per chunk (the last one
+ * shorter) and *n_chunks chunks.  A function of `total` alone; each chunk's
+ * partial result is merged in chunk order.  *max_chunks (optional) receives
+ * the most chunks any row of at most `total` items gets (what the workspace
+ * holds per row).  CA_ERR_ARG for total < 0 or NULL outputs. */
+int ca_attend_decode_plan(int64_t total, int32_t* chunk_len, int32_t* n_chunks, int32_t* max_chunks);
+
+/* HCA decode: row b is sequence b at position pos[b] (as for CSA decode). */
 int ca_hca_attend_decode(const ca_attend_params* p, const void* q, const float* q_gain, const ca_cache* kv,
                          int32_t ratio, const int32_t* pos, int32_t B, int64_t max_pos, const void* window,
                          int32_t W, const float* sink, void* out, float* lse, void* ws, size_t ws_bytes,

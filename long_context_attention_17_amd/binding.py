@@ -17,6 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcsahca.so")
 
 F32, BF16, FP8MIX, E4M3, FP4 = 0, 1, 2, 3, 4
+STATUS_POS_RANGE = 1   # device status bit: a decode row's position outside [0, max_pos]
 FORMATS = {"f32": F32, "bf16": BF16, "fp8mix": FP8MIX, "e4m3": E4M3, "fp4": FP4}
 
 
@@ -52,12 +53,13 @@ class WindowParams(ctypes.Structure):
 
 class IndexParams(ctypes.Structure):
     _fields_ = [("n_heads", _I32), ("dim", _I32), ("ratio", _I32), ("k", _I32), ("q_format", _I32),
-                ("q_quant", _I32)]
+                ("q_quant", _I32), ("status", _P)]
 
 
 class AttendParams(ctypes.Structure):
     _fields_ = [("n_heads", _I32), ("dim", _I32), ("rope_dim", _I32), ("n_win", _I32), ("q_format", _I32),
-                ("win_format", _I32), ("out_format", _I32), ("scale", _F), ("eps", _F), ("rope_base", _D)]
+                ("win_format", _I32), ("out_format", _I32), ("scale", _F), ("eps", _F), ("rope_base", _D),
+                ("status", _P)]
 
 
 _PC = ctypes.POINTER(_Cache)
@@ -100,6 +102,8 @@ _SIGS = {
     "ca_hca_decode_step": (ctypes.c_int, [ctypes.POINTER(WindowParams), _P, _P, _P, _I32, _I32,
                                           ctypes.POINTER(DecodeEntryJob), ctypes.POINTER(AttendParams), _P, _P, _P,
                                           _I32, _I64, _P, _P, _P, _P, _SZ, _P]),
+    "ca_attend_decode_plan": (ctypes.c_int, [_I64, ctypes.POINTER(_I32), ctypes.POINTER(_I32),
+                                             ctypes.POINTER(_I32)]),
     "ca_timer_start": (ctypes.c_int, [ctypes.c_uint32, _I64]),
     "ca_timer_read": (ctypes.c_int, [_I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64)]),
     "ca_timer_stop": (ctypes.c_int, []),
@@ -256,6 +260,13 @@ def index_topk_decode(p: IndexParams, qI, w, pos, max_pos: int, idx_cache: Cache
     _check(_lib.ca_index_topk_decode(ctypes.byref(p), _ptr(qI), _ptr(w), _ptr(pos), B, max_pos, idx_cache.ref,
                                      _ptr(out_idx), _ptr(out_cnt), _ptr(out_score), _ptr(all_scores), st, _ptr(ws),
                                      0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def attend_decode_plan(total: int):
+    """(chunk length, chunks, most chunks of any row up to `total` items) of the decode split plan."""
+    ln, n, mx = _I32(0), _I32(0), _I32(0)
+    _check(_lib.ca_attend_decode_plan(total, ctypes.byref(ln), ctypes.byref(n), ctypes.byref(mx)))
+    return ln.value, n.value, mx.value
 
 
 def attend_workspace(p: AttendParams, n_rows: int, max_pos: int, k: int, ratio: int) -> int:

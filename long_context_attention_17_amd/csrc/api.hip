@@ -81,21 +81,17 @@ int64_t score_stride(int64_t max_pos, int ratio) {
   return (ne + 63) / 64 * 64;
 }
 
-// Divisor of the split plan for rows of up to max_items items: kDecodeMaxSplits,
-// raised only when a chunk would exceed one MFMA workgroup's item table.
-int split_div_for(int64_t max_items) {
-  const int64_t cap = ca::attend_mfma_max_items();
-  const int64_t need = (max_items + cap - 1) / cap;
-  return (int)(need > ca::kDecodeMaxSplits ? need : ca::kDecodeMaxSplits);
+// Items of the longest row of an attention call: its entries (k for CSA, the
+// eligible entries at max_pos for HCA) plus the window.
+int64_t max_items_of(int64_t max_pos, int n_win, int k, int ratio) {
+  return (k > 0 ? (int64_t)k : max_pos / ratio) + n_win;
 }
 
-// Splits per row of the decode plan (an upper bound for the prefill split too).
+// Splits per row the decode plan can make (an upper bound for the prefill plan too,
+// whose chunks are never shorter than the decode plan's for the same row).
 int max_splits_for(int64_t max_pos, int n_win, int k, int ratio) {
-  int64_t entries = k > 0 ? k : max_pos / ratio;
-  int64_t items = entries + n_win;
-  const int64_t by_len = (items + ca::kDecodeSplitItems - 1) / ca::kDecodeSplitItems;
-  const int64_t div = split_div_for(items);
-  return (int)(by_len < div ? (by_len > 0 ? by_len : 1) : div);
+  return ca::plan_max_splits(max_items_of(max_pos, n_win, k, ratio), ca::kDecodeSplitItems, ca::kDecodeMaxSplits,
+                             ca::attend_mfma_max_items());
 }
 
 }  // namespace
@@ -285,6 +281,7 @@ static int index_common(const ca_index_params* p, const void* qI, const float* w
   if (p->q_quant != 0 && !(p->q_quant == CA_FP4 && idx_cache->format == CA_FP4))
     return fail(CA_ERR_ARG, "%s: q_quant must be 0, or CA_FP4 with an FP4 indexer pool", what);
   if (n_rows < 0 || n_rows > 0x7FFFFFFF) return fail(CA_ERR_ARG, "%s: bad row count", what);
+  if (max_pos > 0x7FFFFFFF) return fail(CA_ERR_ARG, "%s: max_pos beyond 2^31 - 1", what);
   if (n_rows == 0) return ok();
   if (!qI || !w || !out_idx || !out_cnt) return fail(CA_ERR_ARG, "%s: NULL argument", what);
   if (max_pos / p->ratio > (int64_t)idx_cache->max_pages * idx_cache->page_size)
@@ -309,8 +306,8 @@ static int index_common(const ca_index_params* p, const void* qI, const float* w
     if (ca::topk_use_long(stride, p->k))
       ws_long = (char*)ws + align256((size_t)n_rows * stride * sizeof(float));
   }
-  IndexPlan ip{cv, *p, qI, w, ca::RowPos{pos, (int)t0}, seq_fixed, (int)n_rows, max_pos, scores, stride, ws_long,
-               out_idx, out_cnt, out_score};
+  IndexPlan ip{cv, *p, qI, w, ca::RowPos{pos, (int)t0, (int)max_pos, p->status}, seq_fixed, (int)n_rows, max_pos,
+               scores, stride, ws_long, out_idx, out_cnt, out_score};
   if (plan) {
     *plan = ip;
     return CA_OK;
@@ -351,6 +348,16 @@ size_t ca_attend_workspace(const ca_attend_params* p, int32_t n_rows, int64_t ma
   return align256(po) + align256(pm) + align256(pq);
 }
 
+int ca_attend_decode_plan(int64_t total, int32_t* chunk_len, int32_t* n_chunks, int32_t* max_chunks) {
+  if (total < 0 || total > 0x7FFFFFFF || chunk_len == nullptr || n_chunks == nullptr)
+    return fail(CA_ERR_ARG, "ca_attend_decode_plan: bad arguments");
+  const int cap = ca::attend_mfma_max_items();
+  *chunk_len = ca::split_plan_len(total, ca::kDecodeSplitItems, ca::kDecodeMaxSplits, cap);
+  *n_chunks = ca::split_plan_count(total, ca::kDecodeSplitItems, ca::kDecodeMaxSplits, cap);
+  if (max_chunks) *max_chunks = ca::plan_max_splits(total, ca::kDecodeSplitItems, ca::kDecodeMaxSplits, cap);
+  return ok();
+}
+
 static int attend_common(const ca_attend_params* p, const void* q, const float* q_gain, const ca_cache* kv,
                          int mode, int seq_fixed, const int32_t* pos, int64_t t0, int64_t n_rows, int64_t max_pos,
                          const int32_t* idx, const int32_t* cnt, int k, int ratio, const void* window, int W,
@@ -380,6 +387,8 @@ static int attend_common(const ca_attend_params* p, const void* q, const float* 
   if (!decode && W < n_rows + (t0 < p->n_win - 1 ? t0 : p->n_win - 1))
     return fail(CA_ERR_ARG, "%s: prefill window needs W >= L + min(t0, n_win - 1)", what);
   if (decode && n_rows > kv->n_seqs) return fail(CA_ERR_ARG, "%s: more rows than page table rows", what);
+  if (decode && W < p->n_win) return fail(CA_ERR_ARG, "%s: window ring W = %d < n_win = %d", what, W, p->n_win);
+  if (max_pos > 0x7FFFFFFF) return fail(CA_ERR_ARG, "%s: max_pos beyond 2^31 - 1", what);
   if (mode == 1 && max_pos / ratio > (int64_t)kv->max_pages * kv->page_size)
     return fail(CA_ERR_ARG, "%s: page table holds fewer than floor(max_pos/ratio) entries", what);
   (void)win_rows;
@@ -410,26 +419,28 @@ static int attend_common(const ca_attend_params* p, const void* q, const float* 
   a.out = out;
   a.out_fmt = p->out_format;
   a.lse = lse;
-  a.split_items = 0;
+  a.max_pos = (int)max_pos;
+  a.status = p->status;
+  a.split_min = 0;
   a.split_div = 1;
+  a.split_cap = ca::attend_mfma_max_items();
   a.max_splits = 1;
   a.part_o = nullptr;
   a.part_ml = nullptr;
   a.q_prep = nullptr;
-  // Split the item list of each row into fixed chunks: always for decode (a plan that
-  // depends on the sequence alone), and for prefill rows longer than one MFMA
-  // workgroup's item table.
-  const int64_t max_items = (mode == 0 ? (int64_t)k : max_pos / ratio) + p->n_win;
+  // Split the item list of each row into chunks by a plan that depends on the row
+  // alone (ca::split_plan_len): always for decode, and for prefill when a row can be
+  // longer than one MFMA workgroup's item table.
+  const int64_t max_items = max_items_of(max_pos, p->n_win, mode == 0 ? k : 0, ratio);
   int split = 0, div = 1, ms = 1;
   if (decode) {
     split = ca::kDecodeSplitItems;
-    div = split_div_for(max_items);
-    ms = max_splits_for(max_pos, p->n_win, mode == 0 ? k : 0, ratio);
+    div = ca::kDecodeMaxSplits;
   } else if (ca::attend_mfma_supported(a) && max_items > ca::attend_mfma_max_items()) {
-    split = ca::attend_mfma_max_items();
-    ms = (int)((max_items + split - 1) / split);
-    div = ms;
+    split = 64;
+    div = 1;
   }
+  if (split > 0) ms = ca::plan_max_splits(max_items, split, div, a.split_cap);
   if (split > 0) {
     const size_t po = align256((size_t)n_rows * ms * p->n_heads * p->dim * sizeof(float));
     const size_t pm = align256((size_t)n_rows * ms * p->n_heads * 2 * sizeof(float));
@@ -438,7 +449,7 @@ static int attend_common(const ca_attend_params* p, const void* q, const float* 
     if (ws_bytes < need || ws == nullptr)
       return fail(CA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes (rows of up to %lld items are split)", what,
                   ws_bytes, need, (long long)max_items);
-    a.split_items = split;
+    a.split_min = split;
     a.split_div = div;
     a.max_splits = ms;
     a.part_o = (float*)ws;

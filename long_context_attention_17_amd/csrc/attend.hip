@@ -30,9 +30,22 @@ struct RowInfo {
   int t, seq, win_seq, n_c, w0, total;
 };
 
+// A decode row whose position lies outside [0, max_pos] is out of contract: it gets
+// no items (so nothing is read for it and its output is zero), position 0, and the
+// call's status word receives CA_STATUS_POS_RANGE.
 __device__ __forceinline__ RowInfo row_info(const AttendArgs& a, int r) {
   RowInfo ri;
-  ri.t = a.pos ? a.pos[r] : a.t0 + r;
+  bool ok = true;
+  if (a.pos) {
+    ri.t = a.pos[r];
+    ok = ri.t >= 0 && ri.t <= a.max_pos;
+    if (!ok) {
+      if (threadIdx.x == 0) raise_status(a.status, CA_STATUS_POS_RANGE);
+      ri.t = 0;
+    }
+  } else {
+    ri.t = a.t0 + r;
+  }
   ri.seq = a.seq_fixed >= 0 ? a.seq_fixed : r;
   ri.win_seq = a.seq_fixed >= 0 ? 0 : r;
   int nc;
@@ -40,11 +53,11 @@ __device__ __forceinline__ RowInfo row_info(const AttendArgs& a, int r) {
     nc = a.cnt[r];
     nc = nc < 0 ? 0 : (nc > a.k ? a.k : nc);
   } else {
-    nc = ri.t >= 0 ? ri.t / a.ratio : 0;
+    nc = ri.t / a.ratio;
   }
-  ri.n_c = nc;
+  ri.n_c = ok ? nc : 0;
   ri.w0 = ri.t - a.n_win + 1 > 0 ? ri.t - a.n_win + 1 : 0;
-  ri.total = ri.t >= 0 ? nc + (ri.t - ri.w0 + 1) : 0;
+  ri.total = ok ? ri.n_c + (ri.t - ri.w0 + 1) : 0;
   return ri;
 }
 
@@ -63,26 +76,23 @@ __device__ __forceinline__ const uint8_t* item_ptr(const AttendArgs& a, const Ro
   return (const uint8_t*)a.win + ((int64_t)ri.win_seq * a.W + p % a.W) * a.D * esz;
 }
 
-// Split length of a row of `total` items: a function of the row alone.
+// Split length of a row of `total` items: a function of the row alone (never
+// longer than split_cap).
 __device__ __forceinline__ int split_len_of(const AttendArgs& a, int total) {
-  int len = (total + a.split_div - 1) / a.split_div;
-  len = (len + 63) & ~63;
-  return len > a.split_items ? len : a.split_items;
+  return split_plan_len(total, a.split_min, a.split_div, a.split_cap);
 }
 
-// Splits of a row; never more than the workspace holds (a row whose position
-// exceeds the caller's max_pos is truncated rather than overrunning it).
+// Splits of a row.  Rows within the call's max_pos never need more than the
+// workspace holds (plan_max_splits); the cap only guards the workspace.
 __device__ __forceinline__ int n_splits_of(const AttendArgs& a, int total) {
-  if (a.split_items <= 0) return 1;
-  const int len = split_len_of(a, total);
-  int n = (total + len - 1) / len;
-  n = n > 0 ? n : 1;
+  if (a.split_min <= 0) return 1;
+  const int n = split_plan_count(total, a.split_min, a.split_div, a.split_cap);
   return n < a.max_splits ? n : a.max_splits;
 }
 
 // Item range [j0, j1) of split `split` of a row.
 __device__ __forceinline__ void split_range(const AttendArgs& a, int total, int split, int* j0, int* j1) {
-  if (a.split_items <= 0) {
+  if (a.split_min <= 0) {
     *j0 = 0;
     *j1 = total;
     return;
@@ -158,7 +168,7 @@ __global__ void __launch_bounds__(64) attend_generic_kernel(AttendArgs a) {
     m = mn;
   }
   const int hh = h;
-  if (a.split_items > 0) {
+  if (a.split_min > 0) {
     int64_t base = ((int64_t)r * a.max_splits + split) * a.n_heads + hh;
 #pragma unroll
     for (int i = 0; i < NPL; ++i) a.part_o[base * D + lane + 64 * i] = o[i];
@@ -575,7 +585,7 @@ struct MxIssue {
     uint32_t off = kNoItem;
     if (lane < C::kLoadsPerWave) {
       const int j = j0 + tile_no * kRows + wave + 4 * lane;
-      // the host guarantees j1 - j0 <= kMaxItems (longer rows are split)
+      // j1 - j0 <= kMaxItems (the kernel caps it), so j - j0 indexes the item table
       off = j < j1 ? sh.items[j - j0] : kNoItem;
     }
     const uint64_t ok = __ballot(off != kNoItem);
@@ -790,7 +800,7 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
   const int pair = wave >> 1, half = wave & 1, partner = wave ^ 1;
   // Persistent workgroups: unit = (row, head group of 64, split), taken with a
   // static stride so that the work of a launch does not depend on scheduling.
-  const int n_hg = a.n_heads / 64, n_sp = a.split_items > 0 ? a.max_splits : 1;
+  const int n_hg = a.n_heads / 64, n_sp = a.split_min > 0 ? a.max_splits : 1;
   const int n_units = a.n_rows * n_hg * n_sp;
   constexpr int CC = kD - kR;
   for (int i = tid; i < kD; i += 256) sh.gain[i] = a.q_gain[i];
@@ -860,6 +870,7 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
   if (split >= ns) continue;
   int j0, j1;
   split_range(a, ri.total, split, &j0, &j1);
+  j1 = j1 - j0 > kMaxItems ? j0 + kMaxItems : j1;      // (the plan never exceeds the item table)
   const int ntiles = (j1 - j0 + kRows - 1) / kRows;
   const int head0 = hg * 64 + 32 * pair;               // first head of this pair
   const int hl = lane & 31;                            // head (within the block) of this lane's S^T column
@@ -1025,7 +1036,7 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
   constexpr int kStage = 260;
   static_assert(sizeof(sh.ring) + sizeof(sh.tile) >= 4 * 32 * kStage * 4, "staging buffer");
   float* stage = (float*)&sh.ring[0][0] + wave * 32 * kStage;
-  const bool split_out = a.split_items > 0;
+  const bool split_out = a.split_min > 0;
   if (split_out) {
     // split partials go out in the accumulator layout (the combine kernel reads it):
     // per (row, split, head group) a block [pair][half][cb][v/4][lane][v%4] of fp32,
@@ -1134,7 +1145,7 @@ hipError_t launch_attend(const AttendArgs& args, hipStream_t st, bool q_prepared
   AttendArgs a = args;
   a.part_acc = attend_mfma_supported(a) ? 1 : 0;
   a.part_bf16 = a.part_acc && a.out_fmt == CA_BF16 ? 1 : 0;   // partials no finer than the output
-  const int splits = a.split_items > 0 ? a.max_splits : 1;
+  const int splits = a.split_min > 0 ? a.max_splits : 1;
   hipEvent_t ev0, ev1;
   timer_events(a.mode == 0 ? CA_TIMED_CSA_ATTEND : CA_TIMED_HCA_ATTEND, st, &ev0, &ev1);
   if (attend_mfma_supported(a)) {
@@ -1171,7 +1182,7 @@ hipError_t launch_attend(const AttendArgs& args, hipStream_t st, bool q_prepared
     }
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.split_items <= 0) return e;
+  if (e != hipSuccess || a.split_min <= 0) return e;
   if (a.part_acc) {
     hipLaunchKernelGGL(attend_combine_acc_kernel, dim3(a.n_rows, (a.n_heads / 64) * 16), dim3(512), 0, st, a);
   } else {

@@ -41,11 +41,28 @@ struct DecodeEntryJob {
   double base;
 };
 
+// Device status bits (ca_status_bits in the header): OR-ed into a caller's status word.
+__device__ __forceinline__ void raise_status(int32_t* status, int32_t bits) {
+  if (status != nullptr) atomicOr(status, bits);
+}
+
 // Position of query row r: pos[r] (decode), or t0 + r (prefill rows of one sequence).
+// A decode position outside [0, max_pos] is out of contract: it reads as -1 (a row
+// with no eligible entries) and raises CA_STATUS_POS_RANGE in *status.
 struct RowPos {
   const int32_t* pos;
   int t0;
-  __device__ __forceinline__ int operator()(int r) const { return pos ? pos[r] : t0 + r; }
+  int max_pos;
+  int32_t* status;
+  __device__ __forceinline__ int operator()(int r) const {
+    if (pos == nullptr) return t0 + r;
+    const int t = pos[r];
+    if (t < 0 || t > max_pos) {
+      raise_status(status, CA_STATUS_POS_RANGE);
+      return -1;
+    }
+    return t;
+  }
 };
 
 // Scores of every eligible block.  With ws_long (the multi-workgroup top-k state,
@@ -87,8 +104,12 @@ struct AttendArgs {
   void* out;
   int out_fmt;
   float* lse;
-  int split_items;     // 0: one split per row (direct epilogue); else the minimum split length
-  int split_div;       // a row of n items is split into chunks of max(split_items, ceil64(n / split_div))
+  int max_pos;         // decode: the caller's bound on pos[r]; rows beyond it (or negative) are
+                       // out of contract (no items, zero output, CA_STATUS_POS_RANGE raised)
+  int32_t* status;     // optional device status word (CA_STATUS_* bits are OR-ed in)
+  int split_min;       // 0: one split per row (direct epilogue); else the minimum split length
+  int split_div;       // chunks a row is split into at least (when long enough), see split_plan_len
+  int split_cap;       // the longest chunk (one MFMA workgroup's item table)
   int max_splits;      // splits per row the workspace holds (never exceeded)
   float* part_o;       // [rows, max_splits, n_heads, D]
   float* part_ml;      // [rows, max_splits, n_heads, 2]
@@ -98,10 +119,34 @@ struct AttendArgs {
                        // once per row by a prep kernel (split rows of the MFMA path)
 };
 
-// Decode split plan: chunks of at least kDecodeSplitItems items, at most
-// kDecodeMaxSplits chunks per row (a function of the row alone).
-constexpr int kDecodeSplitItems = 256;
-constexpr int kDecodeMaxSplits = 16;
+// Split plan of a row of `total` items, a function of the row alone (so a decode
+// row's accumulation order does not depend on the batch): d = max(split_div,
+// ceil(total / split_cap)) chunks of ceil64(total / d) items, but never shorter
+// than split_min.  A chunk never exceeds split_cap (a multiple of 64), and a row
+// of at most max_items items has at most plan_max_splits(max_items) chunks.
+constexpr int kDecodeSplitItems = 256;   // decode: split_min
+constexpr int kDecodeMaxSplits = 16;     // decode: split_div
+__host__ __device__ __forceinline__ int split_plan_len(int64_t total, int split_min, int split_div, int split_cap) {
+  int64_t d = (total + split_cap - 1) / split_cap;
+  d = d > split_div ? d : split_div;
+  d = d > 0 ? d : 1;
+  int64_t len = (total + d - 1) / d;
+  len = (len + 63) & ~(int64_t)63;
+  return (int)(len > split_min ? len : split_min);
+}
+__host__ __device__ __forceinline__ int split_plan_count(int64_t total, int split_min, int split_div, int split_cap) {
+  const int64_t len = split_plan_len(total, split_min, split_div, split_cap);
+  const int64_t n = (total + len - 1) / len;
+  return (int)(n > 0 ? n : 1);
+}
+__host__ __device__ __forceinline__ int plan_max_splits(int64_t max_items, int split_min, int split_div,
+                                                        int split_cap) {
+  const int64_t by_len = (max_items + split_min - 1) / split_min;
+  int64_t d = (max_items + split_cap - 1) / split_cap;
+  d = d > split_div ? d : split_div;
+  const int64_t n = by_len < d ? by_len : d;
+  return (int)(n > 0 ? n : 1);
+}
 
 bool attend_mfma_supported(const AttendArgs& a);
 int attend_mfma_max_items();  // items one MFMA workgroup handles without splitting
