@@ -76,10 +76,11 @@ def new_pool(n_pages: int, fmt: int, D: int, R: int, P: int) -> np.ndarray:
     return np.zeros(n_pages * page_bytes(fmt, D, R, P), np.uint8)
 
 
-def csa_prefill(cfg, inp: dict, pt_row, n_pool_pages: int, rows=None, idx_override=None) -> dict:
+def csa_prefill(cfg, inp: dict, pt_row, n_pool_pages: int, rows=None, idx_override=None, want_lse=False) -> dict:
     """One CSA prefill layer over a single sequence.  `rows` restricts the
     indexer / top-k / attention to a subset of query rows; `idx_override`
-    (idx, cnt) replaces the oracle's own top-k in the attention step."""
+    (idx, cnt) replaces the oracle's own top-k in the attention step; with
+    want_lse the result also holds each row's log softmax denominator "lse"."""
     L, D, R, P, m = inp["L"], cfg.D, cfg.R, cfg.page, cfg.m
     kv_fmt, idx_fmt = FMT_BY_NAME[cfg.kv], FMT_BY_NAME[cfg.idx]
     pt_row = np.asarray(pt_row, np.int32)
@@ -103,15 +104,16 @@ def csa_prefill(cfg, inp: dict, pt_row, n_pool_pages: int, rows=None, idx_overri
     scores, n_elig = index_scores(qI, take_rows(inp["w"], rows), rows, m, idx_fmt, P, ipool, pt_row[None],
                                   [E.shape[0]], n_cols=max(1, E.shape[0]))
     idx, cnt = topk(scores, n_elig, cfg.k)
-    res.update(scores=scores, n_elig=n_elig, idx=idx, cnt=cnt)
+    res.update(scores=scores, n_elig=n_elig, idx=idx, cnt=cnt, qI=qI)
     a_idx, a_cnt = (idx, cnt) if idx_override is None else idx_override
-    res["out"] = attend(take_rows(inp["q"], rows), rows, kv_fmt, P, pool, pt_row[None], [E.shape[0]], 0, m, win,
-                        cfg.n_win, f64(inp["sink"]), R, gq=f64(inp["g_q"]), idx=a_idx, cnt=a_cnt,
-                        base=cfg.rope_base, eps=cfg.eps)
+    o = attend(take_rows(inp["q"], rows), rows, kv_fmt, P, pool, pt_row[None], [E.shape[0]], 0, m, win,
+               cfg.n_win, f64(inp["sink"]), R, gq=f64(inp["g_q"]), idx=a_idx, cnt=a_cnt,
+               base=cfg.rope_base, eps=cfg.eps, want_lse=want_lse)
+    res["out"], res["lse"] = o if want_lse else (o, None)
     return res
 
 
-def hca_prefill(cfg, inp: dict, pt_row, n_pool_pages: int, rows=None) -> dict:
+def hca_prefill(cfg, inp: dict, pt_row, n_pool_pages: int, rows=None, want_lse=False) -> dict:
     L, D, R, P, m = inp["L"], cfg.D, cfg.R, cfg.page, cfg.m_hca
     kv_fmt = FMT_BY_NAME[cfg.kv]
     pt_row = np.asarray(pt_row, np.int32)
@@ -122,9 +124,10 @@ def hca_prefill(cfg, inp: dict, pt_row, n_pool_pages: int, rows=None) -> dict:
     win = store_window(window_prep(f64(inp["kv_raw"]), pos_all, R, f64(inp["g_w"]), cfg.eps, cfg.rope_base),
                        cfg.act)[None]
     rows = pos_all if rows is None else np.asarray(rows, np.int64)
-    out = attend(take_rows(inp["q"], rows), rows, kv_fmt, P, pool, pt_row[None], [E.shape[0]], 1, m, win, cfg.n_win,
-                 f64(inp["sink"]), R, gq=f64(inp["g_q"]), base=cfg.rope_base, eps=cfg.eps)
-    return dict(entries_raw=E, pool=pool, window=win, rows=rows, out=out, n_entries=E.shape[0])
+    o = attend(take_rows(inp["q"], rows), rows, kv_fmt, P, pool, pt_row[None], [E.shape[0]], 1, m, win, cfg.n_win,
+               f64(inp["sink"]), R, gq=f64(inp["g_q"]), base=cfg.rope_base, eps=cfg.eps, want_lse=want_lse)
+    out, lse = o if want_lse else (o, None)
+    return dict(entries_raw=E, pool=pool, window=win, rows=rows, out=out, lse=lse, n_entries=E.shape[0])
 
 
 def decode_state(cfg, inp: dict, seqs=None) -> dict:
@@ -205,8 +208,9 @@ def decode_compress(cfg, inp: dict, b: int):
     return i, e_main, None
 
 
-def csa_decode_step(cfg, inp: dict, state: dict, seqs=None) -> dict:
-    """Indexer, top-k and attention for the new token of each sequence."""
+def csa_decode_step(cfg, inp: dict, state: dict, seqs=None, idx_override=None, want_lse=False) -> dict:
+    """Indexer, top-k and attention for the new token of each sequence
+    (`idx_override` (idx, cnt) replaces the oracle's own top-k in the attention)."""
     B = state["page_table"].shape[0]
     seqs = np.arange(B) if seqs is None else np.asarray(seqs)
     pos = state["pos"][seqs]
@@ -215,20 +219,24 @@ def csa_decode_step(cfg, inp: dict, state: dict, seqs=None) -> dict:
     scores, n_elig = index_scores(qI, f64(inp["w"])[seqs], pos, cfg.m, FMT_BY_NAME[cfg.idx], cfg.page,
                                   state["ipool"], state["page_table"], state["n_avail"], seq=seqs, n_cols=n_cols)
     idx, cnt = topk(scores, n_elig, cfg.k)
-    out = attend(f64(inp["q"])[seqs], pos, FMT_BY_NAME[cfg.kv], cfg.page, state["pool"], state["page_table"],
-                 state["n_avail"], 0, cfg.m, state["window"], cfg.n_win, f64(inp["sink"]), cfg.R,
-                 gq=f64(inp["g_q"]), seq=seqs, idx=idx, cnt=cnt, base=cfg.rope_base, eps=cfg.eps)
-    return dict(scores=scores, n_elig=n_elig, idx=idx, cnt=cnt, out=out, seqs=seqs)
+    a_idx, a_cnt = (idx, cnt) if idx_override is None else idx_override
+    o = attend(f64(inp["q"])[seqs], pos, FMT_BY_NAME[cfg.kv], cfg.page, state["pool"], state["page_table"],
+               state["n_avail"], 0, cfg.m, state["window"], cfg.n_win, f64(inp["sink"]), cfg.R,
+               gq=f64(inp["g_q"]), seq=seqs, idx=a_idx, cnt=a_cnt, base=cfg.rope_base, eps=cfg.eps,
+               want_lse=want_lse)
+    out, lse = o if want_lse else (o, None)
+    return dict(scores=scores, n_elig=n_elig, idx=idx, cnt=cnt, out=out, lse=lse, seqs=seqs, qI=qI)
 
 
-def hca_decode_step(cfg, inp: dict, state: dict, seqs=None) -> dict:
+def hca_decode_step(cfg, inp: dict, state: dict, seqs=None, want_lse=False) -> dict:
     B = state["page_table"].shape[0]
     seqs = np.arange(B) if seqs is None else np.asarray(seqs)
     pos = state["pos"][seqs]
-    out = attend(f64(inp["q"])[seqs], pos, FMT_BY_NAME[cfg.kv], cfg.page, state["pool"], state["page_table"],
-                 state["n_avail"], 1, cfg.m_hca, state["window"], cfg.n_win, f64(inp["sink"]), cfg.R,
-                 gq=f64(inp["g_q"]), seq=seqs, base=cfg.rope_base, eps=cfg.eps)
-    return dict(out=out, seqs=seqs)
+    o = attend(f64(inp["q"])[seqs], pos, FMT_BY_NAME[cfg.kv], cfg.page, state["pool"], state["page_table"],
+               state["n_avail"], 1, cfg.m_hca, state["window"], cfg.n_win, f64(inp["sink"]), cfg.R,
+               gq=f64(inp["g_q"]), seq=seqs, base=cfg.rope_base, eps=cfg.eps, want_lse=want_lse)
+    out, lse = o if want_lse else (o, None)
+    return dict(out=out, lse=lse, seqs=seqs)
 
 
 __all__ = ["f64", "take_rows", "csa_prefill", "hca_prefill", "decode_state", "decode_compress", "csa_decode_step",

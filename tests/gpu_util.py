@@ -162,3 +162,48 @@ def check_out(gpu, ref, act, what="out"):
     assert np.isfinite(g).all(), f"{what}: non-finite values"
     assert mx <= TOL_OUT[act], f"{what}: max-abs {mx:.3e} > {TOL_OUT[act]}"
     return mx, rel
+
+
+def check_scores(gpu_scores, orc_scores, n_elig, qv, w, keys_of_row, what="indexer scores", mfma=True):
+    """Indexer scores element by element.  Both sides quantize the queries and keys the
+    same way, so every product is exact; the oracle sums in fp64.  The error is bounded
+    relative to the magnitude sum M = sum_h |w_h| sum_j |q_hj k_j|:
+      - generic kernel (fp32 products and sums): recursive fp32 summation,
+        (2 c_I + n_I + 2) * 2^-24 * M, taken with a factor 2 margin;
+      - MFMA kernels: gfx950's fp8 / fp4 MFMA adds the 64 products of a block with fewer
+        mantissa bits than fp32 (differences up to ~2^-17 M were measured), so the bound
+        is 2^-14 M -- still ~30x below the 1e-3 band of the top-k rule for these scores.
+    keys_of_row(r) -> decoded keys [n_elig[r], c_I]."""
+    worst = 0.0
+    for r in range(len(n_elig)):
+        n = int(n_elig[r])
+        if n == 0:
+            continue
+        K = np.abs(keys_of_row(r)[:n])                      # [n, c]
+        Q = np.abs(np.asarray(qv[r], np.float64))           # [nI, c]
+        mag = (np.abs(np.asarray(w[r], np.float64))[:, None] * (Q @ K.T)).sum(0)   # [n]
+        nI, c = Q.shape
+        bound = (2.0 ** -14 if mfma else 2.0 * (2 * c + nI + 2) * 2.0 ** -24) * mag + 1e-30
+        g, o = np.asarray(gpu_scores[r][:n], np.float64), np.asarray(orc_scores[r][:n], np.float64)
+        assert np.isfinite(g).all() and np.isfinite(o).all(), f"{what} row {r}: non-finite scores"
+        d = np.abs(g - o)
+        bad = d > bound
+        assert not bad.any(), (f"{what} row {r}: {int(bad.sum())} scores beyond the fp32 summation bound, e.g. "
+                               f"key {int(np.argmax(d / bound))}: gpu {g[np.argmax(d / bound)]:.9g} oracle "
+                               f"{o[np.argmax(d / bound)]:.9g} bound {bound[np.argmax(d / bound)]:.3g}")
+        worst = max(worst, float((d / bound).max()))
+    log(f"  {what}: within the fp32 summation bound (worst {worst:.3f} of it)")
+    return worst
+
+
+def check_lse(gpu_lse, orc_lse, act, what="lse"):
+    """lse (log of the softmax denominator, sink included) against the oracle: 1e-4 for fp32
+    storage; for bf16 storage 2e-2 (the bf16 rounding of the normalized query moves each
+    logit by ~2^-9 of its size)."""
+    g = np.asarray(gpu_lse, np.float64)
+    d = np.abs(g - orc_lse)
+    mx = float(d.max()) if d.size else 0.0
+    log(f"  {what}: max-abs {mx:.3e}")
+    assert np.isfinite(g).all(), f"{what}: non-finite values"
+    assert mx <= TOL_OUT[act], f"{what}: max-abs {mx:.3e} > {TOL_OUT[act]}"
+    return mx
