@@ -397,6 +397,28 @@ int ca_hca_decode_step(const ca_window_params* wp, const void* kv_raw, const flo
                        const float* q_gain, const int32_t* pos, int32_t B, int64_t max_pos, const float* sink,
                        void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* Allocation-free HCA decode step, for callers that cannot allocate device  */
+/* memory at all (code under HIP graph capture, tight serving loops,         */
+/* harnesses that forbid hipMalloc): ca_hca_decode_step with the attention   */
+/* workspace taken from a static device array of the library instead of a   */
+/* `ws` argument.  Same arguments (minus ws / ws_bytes), results (bit for    */
+/* bit) and errors as ca_hca_decode_step; CA_ERR_WORKSPACE when the step     */
+/* needs more than ca_static_scratch_bytes() of scratch                      */
+/* (ca_attend_workspace(ap, B, max_pos, 0, job->params.ratio) bytes: 64 MiB  */
+/* cover e.g. 8 rows x 128 heads at 2^20 tokens or 64 rows x 64 heads at     */
+/* 128K tokens).  It calls no allocator.  Each GPU holds one such array      */
+/* (from its first call on that device until the process ends) and every    */
+/* call on that GPU shares it: calls that overlap on one GPU (concurrent     */
+/* streams, threads) race and must be serialized by the caller.  The first  */
+/* call on a device looks up the array's device address (host work only).  */
+/* ------------------------------------------------------------------------ */
+size_t ca_static_scratch_bytes(void);
+int ca_hca_decode_step_noalloc(const ca_window_params* wp, const void* kv_raw, const float* w_gain, void* window,
+                               int32_t W, int32_t S, const ca_decode_entry_job* job, const ca_attend_params* ap,
+                               const void* q, const float* q_gain, const int32_t* pos, int32_t B, int64_t max_pos,
+                               const float* sink, void* out, float* lse, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -104,6 +104,10 @@ _SIGS = {
                                           _I32, _I64, _P, _P, _P, _P, _SZ, _P]),
     "ca_attend_decode_plan": (ctypes.c_int, [_I64, ctypes.POINTER(_I32), ctypes.POINTER(_I32),
                                              ctypes.POINTER(_I32)]),
+    "ca_static_scratch_bytes": (_SZ, []),
+    "ca_hca_decode_step_noalloc": (ctypes.c_int, [ctypes.POINTER(WindowParams), _P, _P, _P, _I32, _I32,
+                                                  ctypes.POINTER(DecodeEntryJob), ctypes.POINTER(AttendParams), _P,
+                                                  _P, _P, _I32, _I64, _P, _P, _P, _P]),
     "ca_timer_start": (ctypes.c_int, [ctypes.c_uint32, _I64]),
     "ca_timer_read": (ctypes.c_int, [_I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64)]),
     "ca_timer_stop": (ctypes.c_int, []),
@@ -233,6 +237,21 @@ def hca_decode_step(wp: WindowParams, kv_raw, w_gain, window, job, ap: AttendPar
                                    _jobs_array([job]), ctypes.byref(ap), _ptr(q), _ptr(q_gain), _ptr(pos),
                                    pos.shape[0], max_pos, _ptr(sink), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
                                    _stream(stream)))
+
+
+def static_scratch_bytes() -> int:
+    return int(_lib.ca_static_scratch_bytes())
+
+
+def hca_decode_step_noalloc(wp: WindowParams, kv_raw, w_gain, window, job, ap: AttendParams, q, q_gain, pos,
+                            max_pos: int, sink, out, lse=None, stream=None):
+    """hca_decode_step with the library's static device scratch instead of a workspace
+    (nothing is allocated; calls that overlap on one GPU race)."""
+    S, W = window.shape[0], window.shape[1]
+    _check(_lib.ca_hca_decode_step_noalloc(ctypes.byref(wp), _ptr(kv_raw), _ptr(w_gain), _ptr(window), W, S,
+                                           _jobs_array([job]), ctypes.byref(ap), _ptr(q), _ptr(q_gain), _ptr(pos),
+                                           pos.shape[0], max_pos, _ptr(sink), _ptr(out), _ptr(lse),
+                                           _stream(stream)))
 
 
 def index_topk_workspace(p: IndexParams, n_rows: int, max_pos: int) -> int:

@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/csahca.h"
 #include "common.h"
 #include "kernels.h"
@@ -550,6 +552,64 @@ int ca_hca_decode_step(const ca_window_params* wp, const void* kv_raw, const flo
   return decode_step(wp, kv_raw, w_gain, window, W, S_, job, 1, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                      0, ap, q, q_gain, pos, B, max_pos, sink, out, lse, ws, ws_bytes, stream, false,
                      "ca_hca_decode_step");
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ static scratch
+// Device scratch of the allocation-free HCA decode step: a file-scope array that
+// every device the library runs on holds until the process ends.  In host code its
+// name is only a stand-in; its device address is looked up once per device (with
+// that device current) and only that address is ever passed to kernels.
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on first use).
+int scratch_of_current_device(void** out, const char* what) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(CA_ERR_HIP, "%s: hipGetDevice: %s", what, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(CA_ERR_UNSUPPORTED, "%s: device %d beyond %d", what, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(CA_ERR_HIP, "%s: hipGetSymbolAddress(scratch) on device %d: %s", what, dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return CA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t ca_static_scratch_bytes(void) { return kStaticScratchBytes; }
+
+int ca_hca_decode_step_noalloc(const ca_window_params* wp, const void* kv_raw, const float* w_gain, void* window,
+                               int32_t W, int32_t S_, const ca_decode_entry_job* job, const ca_attend_params* ap,
+                               const void* q, const float* q_gain, const int32_t* pos, int32_t B, int64_t max_pos,
+                               const float* sink, void* out, float* lse, void* stream) {
+  const char* what = "ca_hca_decode_step_noalloc";
+  if (job == nullptr || ap == nullptr) return fail(CA_ERR_ARG, "%s: job or attention params NULL", what);
+  if (B < 0 || max_pos < 0) return fail(CA_ERR_ARG, "%s: negative B or max_pos", what);
+  const size_t need = B > 0 ? ca_attend_workspace(ap, B, max_pos, 0, job->params.ratio) : 0;
+  if (need > kStaticScratchBytes)
+    return fail(CA_ERR_WORKSPACE, "%s: the step needs %zu bytes of scratch, the static scratch holds %zu", what, need,
+                kStaticScratchBytes);
+  if (B == 0) return decode_step(wp, kv_raw, w_gain, window, W, S_, job, 1, nullptr, nullptr, nullptr, nullptr,
+                                 nullptr, nullptr, 0, ap, q, q_gain, pos, B, max_pos, sink, out, lse, nullptr, 0,
+                                 stream, false, what);
+  void* ws = nullptr;
+  if (int e = scratch_of_current_device(&ws, what)) return e;
+  return decode_step(wp, kv_raw, w_gain, window, W, S_, job, 1, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                     0, ap, q, q_gain, pos, B, max_pos, sink, out, lse, ws, kStaticScratchBytes, stream, false, what);
 }
 
 }  // extern "C"

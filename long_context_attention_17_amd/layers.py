@@ -237,6 +237,15 @@ class DecodeLayer:
                                i["g_q"], self.pos, self.max_pos, i["sink"], self.out, self.aws)
         return self.out
 
+    def fused_step_noalloc(self):
+        """HCA only: fused_step() with the library's static device scratch instead of the
+        layer's attention workspace (ca_hca_decode_step_noalloc)."""
+        c, i = self.cfg, self.inp
+        assert self.layer == "hca", "the allocation-free step is the HCA layer's"
+        ca.hca_decode_step_noalloc(window_params(c), self.new_kv, i["g_w"], self.window, self._append_jobs()[0],
+                                   self.ap, i["q"], i["g_q"], self.pos, self.max_pos, i["sink"], self.out)
+        return self.out
+
     def append_token(self):
         ca.window_append(window_params(self.cfg), self.new_kv, self.inp["g_w"], self.window, pos=self.pos,
                          seq=self.seq_ids)
