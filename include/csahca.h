@@ -328,13 +328,17 @@ int ca_hca_attend_prefill(const ca_attend_params* p, const void* q, const float*
                           int32_t seq, int32_t ratio, const void* window, int32_t W, const float* sink, int64_t L,
                           int64_t t0, void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
-/* Host: the split plan decode attention uses for a row of `total` items (its
- * entries plus its window tokens): *chunk_len items per chunk (the last one
- * shorter) and *n_chunks chunks.  A function of `total` alone; each chunk's
- * partial result is merged in chunk order.  *max_chunks (optional) receives
- * the most chunks any row of at most `total` items gets (what the workspace
- * holds per row).  CA_ERR_ARG for total < 0 or NULL outputs. */
-int ca_attend_decode_plan(int64_t total, int32_t* chunk_len, int32_t* n_chunks, int32_t* max_chunks);
+/* Host: the split plan decode attention with params p uses for a row of
+ * `total` items (its entries plus its window tokens): *chunk_len items per
+ * chunk (the last one shorter) and *n_chunks chunks.  A function of `total`
+ * alone (up to 16 chunks of at least 256 items; longer rows get more chunks,
+ * each at most 2,176 items); each chunk's partial result is merged in chunk
+ * order.
+ * *max_chunks (optional) receives the most chunks any row of at most `total`
+ * items gets (what the workspace holds per row).  CA_ERR_ARG for total < 0
+ * or NULL arguments. */
+int ca_attend_decode_plan(const ca_attend_params* p, int64_t total, int32_t* chunk_len, int32_t* n_chunks,
+                          int32_t* max_chunks);
 
 /* HCA decode: row b is sequence b at position pos[b] (as for CSA decode). */
 int ca_hca_attend_decode(const ca_attend_params* p, const void* q, const float* q_gain, const ca_cache* kv,

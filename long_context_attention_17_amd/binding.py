@@ -102,8 +102,8 @@ _SIGS = {
     "ca_hca_decode_step": (ctypes.c_int, [ctypes.POINTER(WindowParams), _P, _P, _P, _I32, _I32,
                                           ctypes.POINTER(DecodeEntryJob), ctypes.POINTER(AttendParams), _P, _P, _P,
                                           _I32, _I64, _P, _P, _P, _P, _SZ, _P]),
-    "ca_attend_decode_plan": (ctypes.c_int, [_I64, ctypes.POINTER(_I32), ctypes.POINTER(_I32),
-                                             ctypes.POINTER(_I32)]),
+    "ca_attend_decode_plan": (ctypes.c_int, [ctypes.POINTER(AttendParams), _I64, ctypes.POINTER(_I32),
+                                             ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
     "ca_static_scratch_bytes": (_SZ, []),
     "ca_hca_decode_step_noalloc": (ctypes.c_int, [ctypes.POINTER(WindowParams), _P, _P, _P, _I32, _I32,
                                                   ctypes.POINTER(DecodeEntryJob), ctypes.POINTER(AttendParams), _P,
@@ -281,10 +281,10 @@ def index_topk_decode(p: IndexParams, qI, w, pos, max_pos: int, idx_cache: Cache
                                      0 if ws is None else ws.numel(), _stream(stream)))
 
 
-def attend_decode_plan(total: int):
+def attend_decode_plan(p: AttendParams, total: int):
     """(chunk length, chunks, most chunks of any row up to `total` items) of the decode split plan."""
     ln, n, mx = _I32(0), _I32(0), _I32(0)
-    _check(_lib.ca_attend_decode_plan(total, ctypes.byref(ln), ctypes.byref(n), ctypes.byref(mx)))
+    _check(_lib.ca_attend_decode_plan(ctypes.byref(p), total, ctypes.byref(ln), ctypes.byref(n), ctypes.byref(mx)))
     return ln.value, n.value, mx.value
 
 

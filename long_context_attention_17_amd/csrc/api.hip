@@ -89,11 +89,22 @@ int64_t max_items_of(int64_t max_pos, int n_win, int k, int ratio) {
   return (k > 0 ? (int64_t)k : max_pos / ratio) + n_win;
 }
 
+// The decode split plan (minimum chunk, chunks) of a call's rows: a constant of the call,
+// never of the batch.
+void decode_plan_of(int n_heads, int D, int R, int* split_min, int* split_div) {
+  (void)n_heads;
+  (void)D;
+  (void)R;
+  *split_min = ca::kDecodeSplitItems;
+  *split_div = ca::kDecodeMaxSplits;
+}
+
 // Splits per row the decode plan can make (an upper bound for the prefill plan too,
 // whose chunks are never shorter than the decode plan's for the same row).
-int max_splits_for(int64_t max_pos, int n_win, int k, int ratio) {
-  return ca::plan_max_splits(max_items_of(max_pos, n_win, k, ratio), ca::kDecodeSplitItems, ca::kDecodeMaxSplits,
-                             ca::attend_mfma_max_items());
+int max_splits_for(const ca_attend_params* p, int64_t max_pos, int k, int ratio) {
+  int mn, dv;
+  decode_plan_of(p->n_heads, p->dim, p->rope_dim, &mn, &dv);
+  return ca::plan_max_splits(max_items_of(max_pos, p->n_win, k, ratio), mn, dv, ca::attend_mfma_max_items());
 }
 
 }  // namespace
@@ -343,20 +354,25 @@ int ca_index_topk_decode(const ca_index_params* p, const void* qI, const float* 
 // and prefill (prefill needs them only for rows longer than one workgroup's item table).
 size_t ca_attend_workspace(const ca_attend_params* p, int32_t n_rows, int64_t max_pos, int32_t k, int32_t ratio) {
   if (p == nullptr || n_rows <= 0 || ratio <= 0) return 0;
-  size_t ms = (size_t)max_splits_for(max_pos, p->n_win, k, ratio);
-  size_t po = (size_t)n_rows * ms * p->n_heads * p->dim * sizeof(float);
+  size_t ms = (size_t)max_splits_for(p, max_pos, k, ratio);
+  // partials are stored no finer than the output: bf16 for a bf16 output, else fp32
+  const size_t esz = p->out_format == CA_BF16 ? 2 : sizeof(float);
+  size_t po = (size_t)n_rows * ms * p->n_heads * p->dim * esz;
   size_t pm = (size_t)n_rows * ms * p->n_heads * 2 * sizeof(float);
   size_t pq = (size_t)n_rows * p->n_heads * p->dim * 2;   // prepared bf16 queries
   return align256(po) + align256(pm) + align256(pq);
 }
 
-int ca_attend_decode_plan(int64_t total, int32_t* chunk_len, int32_t* n_chunks, int32_t* max_chunks) {
-  if (total < 0 || total > 0x7FFFFFFF || chunk_len == nullptr || n_chunks == nullptr)
+int ca_attend_decode_plan(const ca_attend_params* p, int64_t total, int32_t* chunk_len, int32_t* n_chunks,
+                          int32_t* max_chunks) {
+  if (p == nullptr || total < 0 || total > 0x7FFFFFFF || chunk_len == nullptr || n_chunks == nullptr)
     return fail(CA_ERR_ARG, "ca_attend_decode_plan: bad arguments");
   const int cap = ca::attend_mfma_max_items();
-  *chunk_len = ca::split_plan_len(total, ca::kDecodeSplitItems, ca::kDecodeMaxSplits, cap);
-  *n_chunks = ca::split_plan_count(total, ca::kDecodeSplitItems, ca::kDecodeMaxSplits, cap);
-  if (max_chunks) *max_chunks = ca::plan_max_splits(total, ca::kDecodeSplitItems, ca::kDecodeMaxSplits, cap);
+  int mn, dv;
+  decode_plan_of(p->n_heads, p->dim, p->rope_dim, &mn, &dv);
+  *chunk_len = ca::split_plan_len(total, mn, dv, cap);
+  *n_chunks = ca::split_plan_count(total, mn, dv, cap);
+  if (max_chunks) *max_chunks = ca::plan_max_splits(total, mn, dv, cap);
   return ok();
 }
 
@@ -436,15 +452,14 @@ static int attend_common(const ca_attend_params* p, const void* q, const float* 
   const int64_t max_items = max_items_of(max_pos, p->n_win, mode == 0 ? k : 0, ratio);
   int split = 0, div = 1, ms = 1;
   if (decode) {
-    split = ca::kDecodeSplitItems;
-    div = ca::kDecodeMaxSplits;
+    decode_plan_of(p->n_heads, p->dim, p->rope_dim, &split, &div);
   } else if (ca::attend_mfma_supported(a) && max_items > ca::attend_mfma_max_items()) {
     split = 64;
     div = 1;
   }
   if (split > 0) ms = ca::plan_max_splits(max_items, split, div, a.split_cap);
   if (split > 0) {
-    const size_t po = align256((size_t)n_rows * ms * p->n_heads * p->dim * sizeof(float));
+    const size_t po = align256((size_t)n_rows * ms * p->n_heads * p->dim * (p->out_format == CA_BF16 ? 2 : 4));
     const size_t pm = align256((size_t)n_rows * ms * p->n_heads * 2 * sizeof(float));
     const size_t pq = align256((size_t)n_rows * p->n_heads * p->dim * 2);
     const size_t need = po + pm + pq;

@@ -171,7 +171,10 @@ __global__ void __launch_bounds__(64) attend_generic_kernel(AttendArgs a) {
   if (a.split_min > 0) {
     int64_t base = ((int64_t)r * a.max_splits + split) * a.n_heads + hh;
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) a.part_o[base * D + lane + 64 * i] = o[i];
+    for (int i = 0; i < NPL; ++i) {   // partials no finer than the output
+      if (a.part_bf16) ((uint16_t*)a.part_o)[base * D + lane + 64 * i] = f32_to_bf16_bits(o[i]);
+      else a.part_o[base * D + lane + 64 * i] = o[i];
+    }
     if (lane == 0) {
       a.part_ml[2 * base] = m;
       a.part_ml[2 * base + 1] = l;
@@ -214,6 +217,12 @@ __global__ void __launch_bounds__(512) attend_combine_kernel(AttendArgs a) {
   const int ns = n_splits_of(a, ri.total);
   const int64_t base0 = (int64_t)r * a.max_splits * a.n_heads + hh;   // (split s: + s * n_heads)
   const float sk = a.sink[hh] * kLog2e;
+  auto o_at = [&](int64_t b) {                          // 4 channels of a partial (fp32 or bf16)
+    if (!a.part_bf16) return *(const f32x4*)(a.part_o + b * D + d);
+    const u32x2 w = *(const u32x2*)((const uint16_t*)a.part_o + b * D + d);
+    return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u), __uint_as_float(w[1] << 16),
+                 __uint_as_float(w[1] & 0xFFFF0000u)};
+  };
   float ms[kCombineUnroll], ls[kCombineUnroll];
   f32x4 os[kCombineUnroll];
 #pragma unroll
@@ -223,7 +232,7 @@ __global__ void __launch_bounds__(512) attend_combine_kernel(AttendArgs a) {
       const f32x2 ml = *(const f32x2*)(a.part_ml + 2 * b);
       ms[s] = ml[0];
       ls[s] = ml[1];
-      os[s] = *(const f32x4*)(a.part_o + b * D + d);
+      os[s] = o_at(b);
     }
   }
   float M = sk;
@@ -246,7 +255,7 @@ __global__ void __launch_bounds__(512) attend_combine_kernel(AttendArgs a) {
     const int64_t b = base0 + (int64_t)s * a.n_heads;
     const float w = exp2f(a.part_ml[2 * b] - M);
     den += a.part_ml[2 * b + 1] * w;
-    const f32x4 o = *(const f32x4*)(a.part_o + b * D + d);
+    const f32x4 o = o_at(b);
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[e] += o[e] * w;
   }
@@ -297,64 +306,79 @@ constexpr int kCombineLdsSplits = 64;   // splits whose weights sit in LDS (more
 __global__ void __launch_bounds__(512) attend_combine_acc_kernel(AttendArgs a) {
   constexpr int D = 512, C = D - 64;
   __shared__ float w_s[kCombineLdsSplits][64];         // exp2(m_s - M) per (split, head of the group)
-  __shared__ float red[8][64];                         // per (split group, head) partial max / sum
-  __shared__ float M_s[64], den_s[64];
-  const int r = blockIdx.x, n_hg = a.n_heads >> 6;
+  __shared__ float red[8][64], red2[8][64];            // per (split group, head) partial max / sum
+  __shared__ float M_s[64];
+  const int r = blockIdx.x, n_hg = a.n_heads >> 6, n_ms = a.max_splits;
   const int hg = blockIdx.y >> 4, half = (blockIdx.y >> 3) & 1, cb = blockIdx.y & 7;
   const int t = threadIdx.x, pair = t >> 8, vq = (t >> 6) & 3, lane = t & 63;
   const int hq = 32 * pair + 8 * vq + 4 * (lane >> 5);  // first of the thread's 4 heads in the group
   const int h0 = hg * 64 + hq;                          // heads h0 .. h0+3
   const int c = 256 * half + 32 * cb + (lane & 31);
-  const RowInfo ri = row_info(a, r);
-  const int ns = n_splits_of(a, ri.total);
   auto o_at = [&](int s) {
-    const int64_t e = (((int64_t)r * a.max_splits + s) * n_hg + hg) * (64 * D) + (pair * 2 + half) * 8192 +
+    const int64_t e = (((int64_t)r * n_ms + s) * n_hg + hg) * (64 * D) + (pair * 2 + half) * 8192 +
                       (cb * 4 + vq) * 256 + 4 * lane;   // element offset (fp32 or bf16 partials)
     if (!a.part_bf16) return *(const f32x4*)(a.part_o + e);
     const u32x2 w = *(const u32x2*)((const uint16_t*)a.part_o + e);
     return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u), __uint_as_float(w[1] << 16),
                  __uint_as_float(w[1] & 0xFFFF0000u)};
   };
-  // the first splits' partial rows go out first
+  // Every load goes out before anything waits on the row's split count: the first
+  // splits' partial runs and this thread's (m, l) pairs (head hh, splits g and g + 8),
+  // all within the workspace's max_splits; those of splits the row does not have are
+  // never used.
   f32x4 os[kCombineUnroll];
 #pragma unroll
   for (int s = 0; s < kCombineUnroll; ++s)
-    if (s < ns) os[s] = o_at(s);
+    if (s < n_ms) os[s] = o_at(s);
+  const int hh = t & 63, g = t >> 6;
+  const int64_t base = ((int64_t)r * n_ms) * a.n_heads + hg * 64 + hh;
+  const f32x2 ml0 = g < n_ms ? *(const f32x2*)(a.part_ml + 2 * (base + (int64_t)g * a.n_heads)) : f32x2{0.0f, 0.0f};
+  const f32x2 ml1 =
+      g + 8 < n_ms ? *(const f32x2*)(a.part_ml + 2 * (base + (int64_t)(g + 8) * a.n_heads)) : f32x2{0.0f, 0.0f};
+  const float sink_h = a.sink[hg * 64 + hh] * kLog2e;
+  const RowInfo ri = row_info(a, r);
+  const int ns = n_splits_of(a, ri.total);
 
-  // per head of the group: M = max(sink, m_s), den = exp2(sink - M) + sum_s l_s exp2(m_s - M)
+  // per head of the group: M = max(sink, m_s), den = exp2(sink - M) + sum_s l_s exp2(m_s - M),
+  // the sums over the splits of each group g (s = g, g + 8, ...) added in split order
   {
-    const int hh = t & 63, g = t >> 6;
-    const int64_t base = ((int64_t)r * a.max_splits) * a.n_heads + hg * 64 + hh;
     float mx = -INFINITY;
-    for (int s = g; s < ns; s += 8) mx = fmaxf(mx, a.part_ml[2 * (base + (int64_t)s * a.n_heads)]);
+    if (g < ns) mx = ml0[0];
+    if (g + 8 < ns) mx = fmaxf(mx, ml1[0]);
+    for (int s = g + 16; s < ns; s += 8) mx = fmaxf(mx, a.part_ml[2 * (base + (int64_t)s * a.n_heads)]);
     red[g][hh] = mx;
     __syncthreads();
-    float M = a.sink[hg * 64 + hh] * kLog2e;
+    float M = sink_h;
 #pragma unroll
     for (int i = 0; i < 8; ++i) M = fmaxf(M, red[i][hh]);
-    __syncthreads();                                   // every thread has read the maxima
     float dp = 0.0f;
-    for (int s = g; s < ns; s += 8) {
+    if (g < ns) {
+      const float w = exp2f(ml0[0] - M);
+      dp += ml0[1] * w;
+      w_s[g][hh] = w;
+    }
+    if (g + 8 < ns) {
+      const float w = exp2f(ml1[0] - M);
+      dp += ml1[1] * w;
+      w_s[g + 8][hh] = w;
+    }
+    for (int s = g + 16; s < ns; s += 8) {
       const float w = exp2f(a.part_ml[2 * (base + (int64_t)s * a.n_heads)] - M);
       dp += a.part_ml[2 * (base + (int64_t)s * a.n_heads) + 1] * w;
       if (s < kCombineLdsSplits) w_s[s][hh] = w;
     }
-    red[g][hh] = dp;
+    red2[g][hh] = dp;
     if (g == 0) M_s[hh] = M;
-    __syncthreads();
-    if (g == 0) {
-      float den = exp2f(a.sink[hg * 64 + hh] * kLog2e - M);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) den += red[i][hh];
-      den_s[hh] = den;
-    }
     __syncthreads();
   }
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f}, M, den;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     M[e] = M_s[hq + e];
-    den[e] = den_s[hq + e];
+    float d = exp2f(a.sink[h0 + e] * kLog2e - M[e]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) d += red2[i][hq + e];
+    den[e] = d;
   }
   auto weights = [&](int s) {
     if (s < kCombineLdsSplits) return *(const f32x4*)&w_s[s][hq];
@@ -1144,7 +1168,7 @@ hipError_t launch_attend(const AttendArgs& args, hipStream_t st, bool q_prepared
   if (args.n_rows == 0) return hipSuccess;
   AttendArgs a = args;
   a.part_acc = attend_mfma_supported(a) ? 1 : 0;
-  a.part_bf16 = a.part_acc && a.out_fmt == CA_BF16 ? 1 : 0;   // partials no finer than the output
+  a.part_bf16 = a.out_fmt == CA_BF16 ? 1 : 0;   // partials no finer than the output
   const int splits = a.split_min > 0 ? a.max_splits : 1;
   hipEvent_t ev0, ev1;
   timer_events(a.mode == 0 ? CA_TIMED_CSA_ATTEND : CA_TIMED_HCA_ATTEND, st, &ev0, &ev1);

@@ -114,7 +114,7 @@ struct AttendArgs {
   float* part_o;       // [rows, max_splits, n_heads, D]
   float* part_ml;      // [rows, max_splits, n_heads, 2]
   int part_acc;        // 1: part_o is in the MFMA kernel's accumulator layout (see attend_combine_kernel)
-  int part_bf16;       // 1 (accumulator layout, bf16 output): part_o holds bf16 values, same element offsets
+  int part_bf16;       // 1 (bf16 output): part_o holds bf16 values at the same element offsets
   uint16_t* q_prep;    // nullptr, or bf16 [rows, n_heads, D]: queries normalized, rotated and scaled
                        // once per row by a prep kernel (split rows of the MFMA path)
 };
@@ -126,6 +126,7 @@ struct AttendArgs {
 // of at most max_items items has at most plan_max_splits(max_items) chunks.
 constexpr int kDecodeSplitItems = 256;   // decode: split_min
 constexpr int kDecodeMaxSplits = 16;     // decode: split_div
+
 __host__ __device__ __forceinline__ int split_plan_len(int64_t total, int split_min, int split_div, int split_cap) {
   int64_t d = (total + split_cap - 1) / split_cap;
   d = d > split_div ? d : split_div;

@@ -142,22 +142,23 @@ def test_decode_split_plan_depends_on_the_row_alone():
     the workspace holds for a row of at most max_items items -- for every row length,
     including rows longer than 16 x 2,176 items (the plan takes only the row's length)."""
     from long_context_attention_17_amd import binding as ca
+    ap = ca.AttendParams(128, 512, 64, 128, ca.BF16, ca.BF16, ca.BF16, 0.04, 1e-6, 1e4)
     totals = list(range(0, 5000)) + list(range(5000, 300000, 97)) + [34816, 34817, 34816 * 2 + 1, 262144 + 128]
     for max_items in (129, 2176, 8320, 34816, 40000, 262272):
-        _, _, ms = ca.attend_decode_plan(max_items)
+        _, _, ms = ca.attend_decode_plan(ap, max_items)
         for total in totals:
             if total > max_items:
                 continue
-            ln, n, _ = ca.attend_decode_plan(total)
+            ln, n, _ = ca.attend_decode_plan(ap, total)
             assert ln <= 2176 and ln % 64 == 0 and ln >= 256, (total, ln)
             assert n >= 1 and n * ln >= total and (n - 1) * ln < max(total, 1), (total, ln, n)
             assert n <= ms, (total, max_items, n, ms)
     # rows up to 16 chunks of the 256-item minimum stay at 16 chunks; longer rows get more
-    assert ca.attend_decode_plan(8320)[:2] == (576, 15)
-    assert ca.attend_decode_plan(2176)[:2] == (256, 9)
-    assert ca.attend_decode_plan(40000)[1] == 19
+    assert ca.attend_decode_plan(ap, 8320)[:2] == (576, 15)
+    assert ca.attend_decode_plan(ap, 2176)[:2] == (256, 9)
+    assert ca.attend_decode_plan(ap, 40000)[1] == 19
     with pytest.raises(ca.CAError):
-        ca.attend_decode_plan(-1)
+        ca.attend_decode_plan(ap, -1)
 
 
 def test_decode_window_ring_must_hold_the_window():

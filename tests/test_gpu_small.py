@@ -412,7 +412,7 @@ def _batch_invariance(cfg, layer, ctx, check_rows):
         n_items = (min(int(ctx[b]) // cfg.m, cfg.k) if layer == "csa" else int(ctx[b]) // cfg.m_hca) + \
             min(int(ctx[b]) + 1, cfg.n_win)
         log(f"[batch invariance] {layer} seq {b} ctx {int(ctx[b])}: {n_items} items, plan "
-            f"{ca.attend_decode_plan(n_items)[:2]} (batch max_pos {full.max_pos})")
+            f"{ca.attend_decode_plan(full.ap, n_items)[:2]} (batch max_pos {full.max_pos})")
         for how in ("separate", "one-call"):
             one = layers.DecodeLayer(cfg, _single_sequence(inp, b))
             one.step() if how == "separate" else one.fused_step()
@@ -443,7 +443,7 @@ def test_decode_batch_invariance_beyond_16_full_chunks():
     ca, configs, layers, synth = _ca()
     cfg = _cfg(name="bi_long", phase="decode", kv="fp8mix", n_h=64, k=64, m_hca=4, B=3, L=0, seed=779)
     ctx = [140000, 3000, 50000]
-    assert ca.attend_decode_plan(140000 // 4 + 128)[1] == 17
+    assert ca.attend_decode_plan(layers.attend_params(cfg), 140000 // 4 + 128)[1] == 17
     full = _batch_invariance(cfg, "hca", ctx, [0, 2])
     inp = full.inp
     st = opl.decode_state(cfg, inp, seqs=[0])
