@@ -347,6 +347,44 @@ int ca_hca_attend_decode(const ca_attend_params* p, const void* q, const float* 
                          void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Decode state save / restore (dsv4 book Ch.5 "Decode-time cache state";    */
+/* infra transcript: the KV cache is split into a classical cache of        */
+/* compressed entries and a state cache -- the recent uncompressed window   */
+/* and the compressors' unfinished blocks -- and reused prefixes reload     */
+/* them).  One layer's decode state of sequence `seq` after it has consumed */
+/* `pos` tokens (its next token sits at position pos) is: its window ring   */
+/* row window[seq] ([W, win_dim] in win_format), for each of the layer's    */
+/* n_jobs compressors its tail ring tail[j][seq] ([span, narr, dim] fp32,   */
+/* tail_floats[j] floats) and the pages holding its pos / ratio[j]          */
+/* completed entries of cache[j] (whole pages, in page-table order).        */
+/* ca_state_save copies them into one flat device buffer; ca_state_load     */
+/* copies such a buffer into sequence `seq` of a layer with the same        */
+/* shapes, whose page table may name other pages (resume in another slot or */
+/* after the pages were given away).  Decode then continues bit for bit as  */
+/* it would have without the round trip (the buffer can go through host     */
+/* memory or storage in between: it holds no pointers).  Pages missing on   */
+/* the side read from or written to are skipped.  Both calls only enqueue   */
+/* one copy kernel on `stream`; buffer: ca_state_bytes(...) bytes.          */
+/* ------------------------------------------------------------------------ */
+typedef struct ca_decode_state {
+  void* window;                 /* device [S, W, win_dim] ring of the layer */
+  int32_t W, S, win_dim, win_format;
+  int32_t n_jobs;               /* 1 (HCA) or 2 (CSA: main entries, indexer keys) */
+  float* tail[2];               /* device [S, tail_floats[j]] fp32 tail rings */
+  int64_t tail_floats[2];       /* span * narr * dim of each job's ring per sequence */
+  const ca_cache* cache[2];     /* the jobs' paged caches */
+  int32_t ratio[2];             /* entries completed after pos tokens: pos / ratio[j] */
+} ca_decode_state;
+
+/* Bytes of the flat buffer for a sequence that has consumed pos tokens; -1 on
+ * invalid arguments (see ca_last_error). */
+int64_t ca_state_bytes(const ca_decode_state* st, int64_t pos);
+int ca_state_save(const ca_decode_state* st, int32_t seq, int64_t pos, void* buffer, int64_t buffer_bytes,
+                  void* stream);
+int ca_state_load(const ca_decode_state* st, int32_t seq, int64_t pos, const void* buffer, int64_t buffer_bytes,
+                  void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Launch timing (diagnostics, not part of the method).  While a kernel's   */
 /* bit is set, every eager launch of it is bracketed by two HIP events       */
 /* recorded on the stream it is launched on; launches inside a stream        */

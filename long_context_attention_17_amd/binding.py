@@ -70,6 +70,12 @@ class DecodeEntryJob(ctypes.Structure):
                 ("cache", _PC)]
 
 
+class DecodeState(ctypes.Structure):
+    _fields_ = [("window", _P), ("W", _I32), ("S", _I32), ("win_dim", _I32), ("win_format", _I32),
+                ("n_jobs", _I32), ("tail", _P * 2), ("tail_floats", _I64 * 2), ("cache", _PC * 2),
+                ("ratio", _I32 * 2)]
+
+
 _SIGS = {
     "ca_last_error": (ctypes.c_char_p, []),
     "ca_record_stride": (_I64, [_I32, _I32, _I32]),
@@ -108,6 +114,9 @@ _SIGS = {
     "ca_hca_decode_step_noalloc": (ctypes.c_int, [ctypes.POINTER(WindowParams), _P, _P, _P, _I32, _I32,
                                                   ctypes.POINTER(DecodeEntryJob), ctypes.POINTER(AttendParams), _P,
                                                   _P, _P, _I32, _I64, _P, _P, _P, _P]),
+    "ca_state_bytes": (_I64, [ctypes.POINTER(DecodeState), _I64]),
+    "ca_state_save": (ctypes.c_int, [ctypes.POINTER(DecodeState), _I32, _I64, _P, _I64, _P]),
+    "ca_state_load": (ctypes.c_int, [ctypes.POINTER(DecodeState), _I32, _I64, _P, _I64, _P]),
     "ca_timer_start": (ctypes.c_int, [ctypes.c_uint32, _I64]),
     "ca_timer_read": (ctypes.c_int, [_I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64)]),
     "ca_timer_stop": (ctypes.c_int, []),
@@ -252,6 +261,37 @@ def hca_decode_step_noalloc(wp: WindowParams, kv_raw, w_gain, window, job, ap: A
                                            _jobs_array([job]), ctypes.byref(ap), _ptr(q), _ptr(q_gain), _ptr(pos),
                                            pos.shape[0], max_pos, _ptr(sink), _ptr(out), _ptr(lse),
                                            _stream(stream)))
+
+
+def decode_state(window, win_format: int, jobs):
+    """Descriptor of one layer's decode state: the window ring [S, W, dim] and, per job,
+    (tail ring [S, span, narr, dim] fp32, Cache, ratio)."""
+    st = DecodeState()
+    st.window, st.S, st.W, st.win_dim, st.win_format = window.data_ptr(), window.shape[0], window.shape[1], \
+        window.shape[2], win_format
+    st.n_jobs = len(jobs)
+    st._keep = [c for _, c, _ in jobs]
+    for j, (tail, cache, ratio) in enumerate(jobs):
+        st.tail[j] = tail.data_ptr()
+        st.tail_floats[j] = tail[0].numel()
+        st.cache[j] = ctypes.pointer(cache.desc)
+        st.ratio[j] = ratio
+    return st
+
+
+def state_bytes(st: DecodeState, pos: int) -> int:
+    n = int(_lib.ca_state_bytes(ctypes.byref(st), pos))
+    if n < 0:
+        raise CAError(-1, _lib.ca_last_error().decode())
+    return n
+
+
+def state_save(st: DecodeState, seq: int, pos: int, buffer, stream=None):
+    _check(_lib.ca_state_save(ctypes.byref(st), seq, pos, _ptr(buffer), buffer.numel(), _stream(stream)))
+
+
+def state_load(st: DecodeState, seq: int, pos: int, buffer, stream=None):
+    _check(_lib.ca_state_load(ctypes.byref(st), seq, pos, _ptr(buffer), buffer.numel(), _stream(stream)))
 
 
 def index_topk_workspace(p: IndexParams, n_rows: int, max_pos: int) -> int:

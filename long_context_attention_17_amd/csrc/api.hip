@@ -363,6 +363,86 @@ size_t ca_attend_workspace(const ca_attend_params* p, int32_t n_rows, int64_t ma
   return align256(po) + align256(pm) + align256(pq);
 }
 
+// ------------------------------------------------------------------ decode state
+static int state_plan(const ca_decode_state* st, int32_t seq, int64_t pos, void* buffer, ca::StatePlan* plan,
+                      int64_t* total, const char* what) {
+  if (st == nullptr) return fail(CA_ERR_ARG, "%s: state descriptor NULL", what);
+  if (st->n_jobs < 1 || st->n_jobs > 2) return fail(CA_ERR_ARG, "%s: n_jobs must be 1 or 2", what);
+  if (st->W <= 0 || st->S <= 0 || st->win_dim <= 0 || !is_act(st->win_format))
+    return fail(CA_ERR_ARG, "%s: bad window shape or format", what);
+  if (seq < 0 || seq >= st->S) return fail(CA_ERR_ARG, "%s: seq %d outside the window's %d rows", what, seq, st->S);
+  if (pos < 0) return fail(CA_ERR_ARG, "%s: negative pos", what);
+  if (st->window == nullptr) return fail(CA_ERR_ARG, "%s: window NULL", what);
+  if (((uintptr_t)st->window | (uintptr_t)buffer | (uintptr_t)st->tail[0] | (uintptr_t)st->tail[1]) % 16)
+    return fail(CA_ERR_ARG, "%s: window, tails and buffer must be 16-byte aligned", what);
+  ca::StatePlan p{};
+  p.buffer = (uint8_t*)buffer;
+  int64_t off = 0;
+  auto add = [&](uint8_t* live, const int32_t* pt, int64_t n_pages, int64_t item_bytes, int64_t n_items) {
+    ca::StatePart& q = p.part[p.n_parts++];
+    q.live = live;
+    q.page_table = pt;
+    q.n_pages = n_pages;
+    q.item_bytes = item_bytes;
+    q.n_items = n_items;
+    q.chunks_per_item = (item_bytes + 4095) / 4096;
+    q.flat_offset = off;
+    off = align256(off + item_bytes * n_items);
+  };
+  const int64_t esz = st->win_format == CA_F32 ? 4 : 2;
+  const int64_t wrow = (int64_t)st->W * st->win_dim * esz;
+  if (wrow % 16) return fail(CA_ERR_UNSUPPORTED, "%s: window row bytes not a multiple of 16", what);
+  add((uint8_t*)st->window + seq * wrow, nullptr, 0, wrow, 1);
+  for (int j = 0; j < st->n_jobs; ++j) {
+    if (st->tail[j] == nullptr || st->tail_floats[j] <= 0 || (st->tail_floats[j] * 4) % 16)
+      return fail(CA_ERR_ARG, "%s: job %d: bad tail ring", what, j);
+    add((uint8_t*)(st->tail[j] + seq * st->tail_floats[j]), nullptr, 0, st->tail_floats[j] * 4, 1);
+  }
+  for (int j = 0; j < st->n_jobs; ++j) {
+    ca::CacheView cv;
+    if (int e = make_view(st->cache[j], &cv, what)) return e;
+    if (st->ratio[j] <= 0) return fail(CA_ERR_ARG, "%s: job %d: ratio must be positive", what, j);
+    if (seq >= st->cache[j]->n_seqs) return fail(CA_ERR_ARG, "%s: job %d: seq beyond the page table", what, j);
+    const int64_t n_e = pos / st->ratio[j];
+    const int64_t n_pg = (n_e + st->cache[j]->page_size - 1) / st->cache[j]->page_size;
+    if (n_pg > st->cache[j]->max_pages) return fail(CA_ERR_ARG, "%s: job %d: %lld pages beyond the page table", what, j,
+                                                    (long long)n_pg);
+    if (cv.page_bytes % 16 || (uintptr_t)cv.pool % 16)
+      return fail(CA_ERR_UNSUPPORTED, "%s: job %d: pool or page bytes not 16-byte aligned", what, j);
+    add(cv.pool, cv.page_table + (int64_t)seq * cv.max_pages, cv.n_pages, cv.page_bytes, n_pg);
+  }
+  if (plan) *plan = p;
+  *total = off;
+  return CA_OK;
+}
+
+int64_t ca_state_bytes(const ca_decode_state* st, int64_t pos) {
+  int64_t total = 0;
+  if (state_plan(st, 0, pos, nullptr, nullptr, &total, "ca_state_bytes")) return -1;
+  ok();
+  return total;
+}
+
+static int state_copy(const ca_decode_state* st, int32_t seq, int64_t pos, void* buffer, int64_t bytes, int to_buffer,
+                      void* stream, const char* what) {
+  ca::StatePlan p;
+  int64_t total = 0;
+  if (int e = state_plan(st, seq, pos, buffer, &p, &total, what)) return e;
+  if (buffer == nullptr || bytes < total)
+    return fail(CA_ERR_WORKSPACE, "%s: buffer of %lld bytes < %lld needed", what, (long long)bytes, (long long)total);
+  return hip_status(ca::launch_state_copy(p, to_buffer, S(stream)), what);
+}
+
+int ca_state_save(const ca_decode_state* st, int32_t seq, int64_t pos, void* buffer, int64_t buffer_bytes,
+                  void* stream) {
+  return state_copy(st, seq, pos, buffer, buffer_bytes, 1, stream, "ca_state_save");
+}
+
+int ca_state_load(const ca_decode_state* st, int32_t seq, int64_t pos, const void* buffer, int64_t buffer_bytes,
+                  void* stream) {
+  return state_copy(st, seq, pos, (void*)buffer, buffer_bytes, 0, stream, "ca_state_load");
+}
+
 int ca_attend_decode_plan(const ca_attend_params* p, int64_t total, int32_t* chunk_len, int32_t* n_chunks,
                           int32_t* max_chunks) {
   if (p == nullptr || total < 0 || total > 0x7FFFFFFF || chunk_len == nullptr || n_chunks == nullptr)

@@ -164,6 +164,24 @@ hipError_t launch_decode_front(const DecodeWindowJob& wj, const DecodeEntryJob* 
 hipError_t launch_decode_append(const DecodeWindowJob& wj, const DecodeEntryJob* jobs, int n_jobs,
                                 const int32_t* pos, int B, hipStream_t st);
 
+// One sequence's decode state as parts copied between their live storage and a flat
+// buffer (state.hip).  A part is n_items items of item_bytes (a multiple of 16) each,
+// contiguous in live storage, or (page_table != nullptr) one page each, found through
+// the sequence's page-table row.
+struct StatePart {
+  uint8_t* live;
+  const int32_t* page_table;   // the sequence's row, or nullptr
+  int64_t n_pages;
+  int64_t item_bytes, n_items, chunks_per_item;   // chunks of 4 KB
+  int64_t flat_offset;
+};
+struct StatePlan {
+  uint8_t* buffer;
+  int n_parts;
+  StatePart part[5];
+};
+hipError_t launch_state_copy(const StatePlan& p, int to_buffer, hipStream_t st);
+
 // Launch timing of the timed kernels (ids: ca_timed_kernel): the start / stop
 // events for the next launch of `kernel` on `st`, or false (both null) when it
 // is not being timed.  CA_LAUNCH launches through hipExtLaunchKernelGGL with

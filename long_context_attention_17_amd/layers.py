@@ -246,6 +246,13 @@ class DecodeLayer:
                                    self.ap, i["q"], i["g_q"], self.pos, self.max_pos, i["sink"], self.out)
         return self.out
 
+    def state(self):
+        """Descriptor of this layer's decode state (ca_state_save / ca_state_load)."""
+        jobs = [(self.tail, self.kv, self.ratio)]
+        if self.layer == "csa":
+            jobs.append((self.itail, self.ik, self.ratio))
+        return ca.decode_state(self.window, act_format(self.cfg), jobs)
+
     def append_token(self):
         ca.window_append(window_params(self.cfg), self.new_kv, self.inp["g_w"], self.window, pos=self.pos,
                          seq=self.seq_ids)

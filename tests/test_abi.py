@@ -196,3 +196,31 @@ def test_no_alloc_step_rejects_a_step_beyond_its_scratch():
     rc = lib.ca_hca_decode_step_noalloc(ctypes.byref(wp), d, d, d, 128, 64, ctypes.byref(job), ctypes.byref(ap), d, d,
                                         d, 64, 1 << 22, d, d, None, None)
     assert rc == -4 and b"static scratch" in lib.ca_last_error()
+
+
+def test_decode_state_sizes_and_errors():
+    """ca_state_bytes: the window row, each tail ring and the whole pages holding pos/ratio
+    entries of each cache, every part 256-byte aligned; bad arguments are refused on the host."""
+    from long_context_attention_17_amd import binding as ca
+    lib = ca.lib()
+    d = 256                                                # an aligned non-null stand-in address
+    st = ca.DecodeState()
+    st.window, st.W, st.S, st.win_dim, st.win_format, st.n_jobs = d, 128, 4, 512, ca.BF16, 2
+    c0 = ca._Cache(ca.FP8MIX, 512, 64, 64, ctypes.c_void_p(d), 100, ctypes.c_void_p(d), 4, 50)
+    c1 = ca._Cache(ca.E4M3, 64, 0, 64, ctypes.c_void_p(d), 100, ctypes.c_void_p(d), 4, 50)
+    st.tail[0], st.tail[1] = d, d
+    st.tail_floats[0], st.tail_floats[1] = 8 * 4 * 512, 8 * 4 * 64
+    st.cache[0], st.cache[1] = ctypes.pointer(c0), ctypes.pointer(c1)
+    st.ratio[0], st.ratio[1] = 4, 4
+    pos = 1001                                             # 250 entries: 4 pages of 64
+    want = 128 * 512 * 2 + 8 * 4 * 512 * 4 + 8 * 4 * 64 * 4 + 4 * 64 * 640 + 4 * (64 * 64 + 64 * 4)
+    assert ca.state_bytes(st, pos) == want
+    assert ca.state_bytes(st, 0) == 128 * 512 * 2 + 8 * 4 * 512 * 4 + 8 * 4 * 64 * 4
+    assert lib.ca_state_bytes(ctypes.byref(st), 64 * 50 * 4 + 4) == -1     # more pages than the table holds
+    assert b"beyond the page table" in lib.ca_last_error()
+    rc = lib.ca_state_save(ctypes.byref(st), 4, pos, ctypes.c_void_p(d), want, None)
+    assert rc == -1 and b"seq 4" in lib.ca_last_error()
+    rc = lib.ca_state_save(ctypes.byref(st), 0, pos, ctypes.c_void_p(d), want - 1, None)
+    assert rc == -4
+    st.window = 264                                        # misaligned
+    assert lib.ca_state_bytes(ctypes.byref(st), pos) == -1 and b"aligned" in lib.ca_last_error()

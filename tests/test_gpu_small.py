@@ -815,3 +815,111 @@ def test_sharp_needles_decode():
             v = ent[int(picks[b][0][0]) % n, :CC]
             frac = float(step["out"][b, 0, :CC] @ v / (v @ v))
             assert frac > 0.5, f"{layer} seq {b}: planted entry carries {frac:.3f} of head 0's output"
+
+
+def _step_inputs(cfg, layer, B, step, device="cuda"):
+    """Fresh per-step inputs of a decode layer (new token's raw rows, queries, indexer)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(90000 + 100 * step + (0 if layer == "csa" else 50))
+    sd = 1.0 / math.sqrt(cfg.D)
+
+    def n(*shape, std=sd):
+        return (torch.randn(*shape, generator=g) * std).to(device)
+
+    out = {"q": n(B, cfg.n_h, cfg.D).to(torch.bfloat16), "kv": n(B, cfg.D).to(torch.bfloat16)}
+    if layer == "csa":
+        si = 1.0 / math.sqrt(cfg.cI)
+        out.update(rows=n(B, 4, cfg.D).to(torch.bfloat16), irows=n(B, 4, cfg.cI, std=si).to(torch.bfloat16),
+                   qI=n(B, cfg.nI, cfg.cI, std=si).to(torch.bfloat16), w=n(B, cfg.nI, std=1 / math.sqrt(cfg.nI)))
+    else:
+        out["rows"] = n(B, 2, cfg.D).to(torch.bfloat16)
+    return out
+
+
+def _advance(dl, inp, rows=None):
+    """Feed a decode layer the inputs of its next token (rows: which batch rows of inp)."""
+    pick = (lambda t: t) if rows is None else (lambda t: t[rows].contiguous())
+    dl.inp = dict(dl.inp, q=pick(inp["q"]))
+    dl.new_kv = pick(inp["kv"])
+    dl.new_rows = pick(inp["rows"])
+    if dl.layer == "csa":
+        dl.inp.update(qI=pick(inp["qI"]), w=pick(inp["w"]))
+        dl.new_irows = pick(inp["irows"])
+
+
+def _headroom(dl, extra):
+    """Workspaces for positions up to extra tokens beyond the layer's current max_pos."""
+    ca = _ca()[0]
+    mp = dl.max_pos + extra
+    if dl.layer == "csa":
+        dl.iws = torch.empty(ca.index_topk_workspace(dl.ip, dl.B, mp), dtype=torch.uint8, device="cuda")
+    k = dl.cfg.k if dl.layer == "csa" else 0
+    dl.aws = torch.empty(ca.attend_workspace(dl.ap, dl.B, mp, k, dl.ratio), dtype=torch.uint8, device="cuda")
+
+
+def test_decode_state_save_and_resume():
+    """A sequence's decode state (window ring, compressor tail rings, cache pages) saved
+    after some steps, taken through host memory and loaded into another slot whose page
+    table names other pages, continues bit for bit: outputs, index lists and the final
+    state equal those of the uninterrupted batch."""
+    ca, configs, layers, synth = _ca()
+    cfg = _cfg(name="resume", phase="decode", kv="fp8mix", n_h=64, k=64, B=3, L=0, seed=781)
+    ctx = torch.tensor([1001, 2050, 1500])
+    b, n_before, n_after = 1, 3, 6
+    for layer in ("csa", "hca"):
+        inp = synth.decode_layer(cfg, layer, "cuda", ctx)
+        ref = layers.DecodeLayer(cfg, inp)
+        _headroom(ref, n_before + n_after)
+        outs = []
+        for step in range(n_before + n_after):
+            si = _step_inputs(cfg, layer, cfg.B, step)
+            _advance(ref, si)
+            ref.fused_step()
+            torch.cuda.synchronize()
+            outs.append((ref.out[b].view(torch.int16).clone(), ref.idx[b].clone() if layer == "csa" else None))
+            if step == n_before - 1:                     # save sequence b after n_before steps
+                st = ref.state()
+                pos_next = int(ctx[b]) + n_before
+                nbytes = ca.state_bytes(st, pos_next)
+                buf = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+                ca.state_save(st, b, pos_next, buf)
+                host = buf.cpu()                         # through host memory
+                log(f"[resume] {layer}: saved seq {b} at position {pos_next}: {nbytes} bytes")
+            ref.pos += 1
+            ref.max_pos += 1
+        # resume: a batch of one whose page table names other pages of a fresh pool
+        sub = _single_sequence(inp, b)
+        pt = sub["page_table"].clone()
+        used = pt[0][pt[0] >= 0]
+        perm = torch.randperm(int(inp["n_pool_pages"]), generator=torch.Generator().manual_seed(7))[:used.numel()]
+        pt[0, :used.numel()] = perm.to(pt.dtype).to(pt.device)
+        sub["page_table"] = pt
+        one = layers.DecodeLayer(cfg, sub)
+        _headroom(one, n_before + n_after)
+        one.window.fill_(3.0)                            # garbage everywhere the state will be loaded
+        one.tail.fill_(-5.0)
+        one.kv.pool.fill_(0x5A)
+        if layer == "csa":
+            one.itail.fill_(7.0)
+            one.ik.pool.fill_(0x33)
+        ca.state_load(one.state(), 0, pos_next, host.cuda())
+        one.pos.fill_(pos_next)
+        one.max_pos = pos_next
+        for step in range(n_before, n_before + n_after):
+            _advance(one, _step_inputs(cfg, layer, cfg.B, step), rows=[b])
+            one.fused_step()
+            torch.cuda.synchronize()
+            want_out, want_idx = outs[step]
+            assert torch.equal(one.out[0].view(torch.int16), want_out), f"{layer}: output of step {step} differs"
+            if layer == "csa":
+                assert torch.equal(one.idx[0], want_idx), f"csa: index list of step {step} differs"
+            one.pos += 1
+            one.max_pos += 1
+        # the final state equals the uninterrupted sequence's
+        pos_end = int(ctx[b]) + n_before + n_after
+        a_buf = torch.zeros(ca.state_bytes(ref.state(), pos_end), dtype=torch.uint8, device="cuda")
+        c_buf = torch.zeros_like(a_buf)
+        ca.state_save(ref.state(), b, pos_end, a_buf)
+        ca.state_save(one.state(), 0, pos_end, c_buf)
+        torch.cuda.synchronize()
+        assert torch.equal(a_buf, c_buf), f"{layer}: final state differs"
