@@ -394,7 +394,8 @@ typedef enum {
   CA_TIMED_CSA_ATTEND = 0,    /* gathered-entry attention kernel of CSA (one launch per attend call) */
   CA_TIMED_HCA_ATTEND = 1,    /* dense compressed-entry attention kernel of HCA */
   CA_TIMED_INDEX_SCORES = 2,  /* indexer scoring kernel of ca_index_topk_* */
-  CA_TIMED_KERNELS = 3
+  CA_TIMED_PROJ_GEMM = 3,     /* GEMM kernel of ca_query_proj / ca_out_proj (each GEMM stage one launch) */
+  CA_TIMED_KERNELS = 4
 } ca_timed_kernel;
 
 /* Start timing the kernels whose bits (1 << ca_timed_kernel) are set in
@@ -460,6 +461,62 @@ int ca_hca_decode_step_noalloc(const ca_window_params* wp, const void* kv_raw, c
                                int32_t W, int32_t S, const ca_decode_entry_job* job, const ca_attend_params* ap,
                                const void* q, const float* q_gain, const int32_t* pos, int32_t B, int64_t max_pos,
                                const float* sink, void* out, float* lse, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* The attention sublayer around CSA / HCA (dsv4 book Ch.6 "Low-rank query   */
+/* generation", "The lightning indexer" and "Grouped output projections";    */
+/* Ch.4 "Query head scaling and grouped output projections").  Plain linear  */
+/* maps, no bias; bf16 storage, fp32 accumulation.  Weights are [out][in]    */
+/* row-major bf16 arrays (the transpose of the pages' x W form), 16-byte     */
+/* aligned.  Every width that is summed over (d, d_c, 8 c) must be a         */
+/* multiple of 64 (else CA_ERR_UNSUPPORTED); T up to 2^31 - 1 rows.          */
+/* ------------------------------------------------------------------------ */
+typedef struct ca_query_proj_params {
+  int32_t d;          /* hidden width */
+  int32_t d_c;        /* query latent width */
+  int32_t n_q;        /* main query channels n_h * c */
+  int32_t n_qi;       /* indexer query channels n_I * c_I (0: no indexer, HCA) */
+  int32_t n_i;        /* indexer heads n_I (combiner weights; 0 with n_qi == 0) */
+  const void* w_dq;   /* bf16 [d_c][d]     (W^{DQ}) */
+  const void* w_uq;   /* bf16 [n_q][d_c]   (W^{UQ}) */
+  const void* w_iuq;  /* bf16 [n_qi][d_c]  (W^{IUQ}) */
+  const void* w_w;    /* bf16 [n_i][d]     (W^w) */
+} ca_query_proj_params;
+
+/* Low-rank query generation for T tokens (Ch.6 "Low-rank query generation",
+ * "The lightning indexer"): from h [T][d] bf16 computes, in two GEMM stages,
+ *   c_q [T][d_c]  bf16  = h W^{DQ}            (the shared latent, stored bf16)
+ *   w_i [T][n_i]  fp32  = h W^w               (indexer combiner weights)
+ *   q   [T][n_q]  bf16  = c_q W^{UQ}          (n_h heads of c, head-major)
+ *   q_i [T][n_qi] bf16  = c_q W^{IUQ}         (n_I heads of c_I)
+ * q and q_i are the query inputs the indexer and attend calls take.  All
+ * outputs are caller-owned device buffers (q_i / w_i may be NULL when n_qi == 0);
+ * workspace: ca_query_proj_workspace() bytes of device memory (NULL when 0).
+ * Errors: CA_ERR_ARG (NULL pointer, bad sizes, misaligned pointer),
+ * CA_ERR_UNSUPPORTED (d or d_c not a multiple of 64), CA_ERR_WORKSPACE. */
+size_t ca_query_proj_workspace(const ca_query_proj_params* p, int64_t T);
+int ca_query_proj(const ca_query_proj_params* p, const void* h, int64_t T, void* c_q, void* q, void* q_i, float* w_i,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+typedef struct ca_out_proj_params {
+  int32_t n_h;        /* query heads; 8 heads a group, g = n_h / 8 groups */
+  int32_t c;          /* head width (8 c a multiple of 64) */
+  int32_t d_g;        /* width of each group's bottleneck */
+  int32_t d;          /* output (hidden) width */
+  const void* w_o1;   /* bf16 [g][d_g][8 c]  (group j's projection of heads 8j .. 8j+7) */
+  const void* w_o2;   /* bf16 [d][g d_g]     (the concatenated groups to d) */
+} ca_out_proj_params;
+
+/* Grouped output projection for T tokens (Ch.6 "Grouped output projections"):
+ * o [T][n_h c] bf16 (the attention output, heads concatenated in head order)
+ *   u [T][g d_g] bf16: u[:, j d_g .. (j+1) d_g) = o[:, 8 j c .. 8 (j+1) c) W1_j
+ *   y [T][d]     bf16 = u W2
+ * u and y are caller-owned device buffers; workspace as ca_out_proj_workspace().
+ * Errors as ca_query_proj (n_h not a multiple of 8, g d_g not a multiple of 64:
+ * CA_ERR_UNSUPPORTED). */
+size_t ca_out_proj_workspace(const ca_out_proj_params* p, int64_t T);
+int ca_out_proj(const ca_out_proj_params* p, const void* o, int64_t T, void* u, void* y, void* workspace,
+                size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -76,6 +76,15 @@ class DecodeState(ctypes.Structure):
                 ("ratio", _I32 * 2)]
 
 
+class QueryProjParams(ctypes.Structure):
+    _fields_ = [("d", _I32), ("d_c", _I32), ("n_q", _I32), ("n_qi", _I32), ("n_i", _I32), ("w_dq", _P), ("w_uq", _P),
+                ("w_iuq", _P), ("w_w", _P)]
+
+
+class OutProjParams(ctypes.Structure):
+    _fields_ = [("n_h", _I32), ("c", _I32), ("d_g", _I32), ("d", _I32), ("w_o1", _P), ("w_o2", _P)]
+
+
 _SIGS = {
     "ca_last_error": (ctypes.c_char_p, []),
     "ca_record_stride": (_I64, [_I32, _I32, _I32]),
@@ -117,6 +126,10 @@ _SIGS = {
     "ca_state_bytes": (_I64, [ctypes.POINTER(DecodeState), _I64]),
     "ca_state_save": (ctypes.c_int, [ctypes.POINTER(DecodeState), _I32, _I64, _P, _I64, _P]),
     "ca_state_load": (ctypes.c_int, [ctypes.POINTER(DecodeState), _I32, _I64, _P, _I64, _P]),
+    "ca_query_proj_workspace": (_SZ, [ctypes.POINTER(QueryProjParams), _I64]),
+    "ca_query_proj": (ctypes.c_int, [ctypes.POINTER(QueryProjParams), _P, _I64, _P, _P, _P, _P, _P, _SZ, _P]),
+    "ca_out_proj_workspace": (_SZ, [ctypes.POINTER(OutProjParams), _I64]),
+    "ca_out_proj": (ctypes.c_int, [ctypes.POINTER(OutProjParams), _P, _I64, _P, _P, _P, _SZ, _P]),
     "ca_timer_start": (ctypes.c_int, [ctypes.c_uint32, _I64]),
     "ca_timer_read": (ctypes.c_int, [_I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64)]),
     "ca_timer_stop": (ctypes.c_int, []),
@@ -369,7 +382,7 @@ def hca_attend_decode(p: AttendParams, q, q_gain, kv: Cache, ratio: int, pos, ma
 
 
 # ---------------------------------------------------------------- launch timing (diagnostics)
-TIMED_CSA_ATTEND, TIMED_HCA_ATTEND, TIMED_INDEX_SCORES = 0, 1, 2
+TIMED_CSA_ATTEND, TIMED_HCA_ATTEND, TIMED_INDEX_SCORES, TIMED_PROJ_GEMM = 0, 1, 2, 3
 
 
 def timer_start(kernels, max_launches: int = 4096):
@@ -389,3 +402,46 @@ def timer_read(kernel: int):
 
 def timer_stop():
     _check(_lib.ca_timer_stop())
+
+
+# ------------------------------------------------------------ sublayer projections
+class QueryProj:
+    """Weights of the low-rank query projections (bf16 [out, in] tensors on the device):
+    w_dq [d_c, d], w_uq [n_h c, d_c], w_iuq [n_I c_I, d_c] and w_w [n_I, d] (the last two
+    None for an HCA layer, which has no indexer)."""
+
+    def __init__(self, w_dq, w_uq, w_iuq=None, w_w=None):
+        self.w = (w_dq, w_uq, w_iuq, w_w)
+        n_qi = 0 if w_iuq is None else w_iuq.shape[0]
+        n_i = 0 if w_w is None else w_w.shape[0]
+        self.p = QueryProjParams(w_dq.shape[1], w_dq.shape[0], w_uq.shape[0], n_qi, n_i, _ptr(w_dq), _ptr(w_uq),
+                                 _ptr(w_iuq), _ptr(w_w))
+
+    def workspace(self, T: int) -> int:
+        return int(_lib.ca_query_proj_workspace(ctypes.byref(self.p), T))
+
+    def __call__(self, h, c_q, q, q_i=None, w_i=None, ws=None, stream=None):
+        T = h.shape[0]
+        if ws is None:
+            ws = torch.empty(max(1, self.workspace(T)), dtype=torch.uint8, device=h.device)
+        _check(_lib.ca_query_proj(ctypes.byref(self.p), _ptr(h), T, _ptr(c_q), _ptr(q), _ptr(q_i), _ptr(w_i),
+                                  _ptr(ws), ws.numel(), _stream(stream)))
+
+
+class OutProj:
+    """Weights of the grouped output projection: w_o1 [g, d_g, 8 c] and w_o2 [d, g d_g] (bf16)."""
+
+    def __init__(self, w_o1, w_o2, c: int):
+        self.w = (w_o1, w_o2)
+        g, d_g, _ = w_o1.shape
+        self.p = OutProjParams(8 * g, c, d_g, w_o2.shape[0], _ptr(w_o1), _ptr(w_o2))
+
+    def workspace(self, T: int) -> int:
+        return int(_lib.ca_out_proj_workspace(ctypes.byref(self.p), T))
+
+    def __call__(self, o, u, y, ws=None, stream=None):
+        T = o.shape[0]
+        if ws is None:
+            ws = torch.empty(max(1, self.workspace(T)), dtype=torch.uint8, device=o.device)
+        _check(_lib.ca_out_proj(ctypes.byref(self.p), _ptr(o), T, _ptr(u), _ptr(y), _ptr(ws), ws.numel(),
+                                _stream(stream)))

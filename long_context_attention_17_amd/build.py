@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcsahca.so")
-SOURCES = ["compress.hip", "indexer.hip", "attend.hip", "api.hip", "timer.hip", "state.hip"]
+SOURCES = ["compress.hip", "indexer.hip", "attend.hip", "api.hip", "timer.hip", "state.hip", "proj.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",

@@ -70,3 +70,25 @@ CONFIGS = {
 
 def get(cfg) -> Config:
     return CONFIGS[cfg] if isinstance(cfg, int) else cfg
+
+
+@dataclass(frozen=True)
+class SublayerDims:
+    """Widths of the attention sublayer's projections (dsv4 book Ch.6 "Low-rank query
+    generation", "Grouped output projections"): hidden d, query latent d_c, n_h heads of
+    c, n_i indexer heads of c_i, g groups of 8 heads each projected to d_g."""
+    name: str
+    d: int
+    d_c: int
+    n_h: int
+    c: int
+    n_i: int
+    c_i: int
+    g: int
+    d_g: int
+
+
+SUBLAYERS = {
+    "flash": SublayerDims("flash", d=4096, d_c=1024, n_h=64, c=512, n_i=64, c_i=128, g=8, d_g=1024),
+    "pro": SublayerDims("pro", d=7168, d_c=1536, n_h=128, c=512, n_i=64, c_i=128, g=16, d_g=1024),
+}

@@ -708,3 +708,146 @@ int ca_hca_decode_step_noalloc(const ca_window_params* wp, const void* kv_raw, c
 }
 
 }  // extern "C"
+
+// --------------------------------------------------------------- sublayer GEMMs
+namespace {
+
+bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+ca::GemmSeg gemm_seg(const void* W, void* C, int N, int c_f32, int64_t ldw, int64_t ldc, int64_t w_batch = 0,
+                     int64_t c_batch = 0) {
+  ca::GemmSeg s{};
+  s.W = W;
+  s.C = C;
+  s.N = N;
+  s.c_f32 = c_f32;
+  s.ldw = ldw;
+  s.ldc = ldc;
+  s.w_batch = w_batch;
+  s.c_batch = c_batch;
+  return s;
+}
+
+ca::GemmArgs gemm_args(const void* A, int64_t lda, int M, int K, int batch = 1, int64_t a_batch = 0) {
+  ca::GemmArgs g{};
+  g.A = A;
+  g.lda = lda;
+  g.a_batch = a_batch;
+  g.M = M;
+  g.K = K;
+  g.batch = batch;
+  return g;
+}
+
+// The two GEMM stages of the low-rank query projections (pointers may be null when
+// only the plan is wanted).
+void query_stages(const ca_query_proj_params* p, int M, const void* h, void* c_q, void* q, void* q_i, float* w_i,
+                  ca::GemmArgs* g) {
+  g[0] = gemm_args(h, p->d, M, p->d);
+  g[0].seg[0] = gemm_seg(p->w_dq, c_q, p->d_c, 0, p->d, p->d_c);
+  g[0].seg[1] = gemm_seg(p->w_w, w_i, p->n_i, 1, p->d, p->n_i);
+  g[0].n_seg = p->n_i > 0 ? 2 : 1;
+  g[1] = gemm_args(c_q, p->d_c, M, p->d_c);
+  g[1].seg[0] = gemm_seg(p->w_uq, q, p->n_q, 0, p->d_c, p->n_q);
+  g[1].seg[1] = gemm_seg(p->w_iuq, q_i, p->n_qi, 0, p->d_c, p->n_qi);
+  g[1].n_seg = p->n_qi > 0 ? 2 : 1;
+}
+
+void out_stages(const ca_out_proj_params* p, int M, const void* o, void* u, void* y, ca::GemmArgs* g) {
+  const int G = p->n_h / 8, width = 8 * p->c;
+  g[0] = gemm_args(o, (int64_t)p->n_h * p->c, M, width, G, width);
+  g[0].seg[0] = gemm_seg(p->w_o1, u, p->d_g, 0, width, (int64_t)G * p->d_g, (int64_t)p->d_g * width, p->d_g);
+  g[0].n_seg = 1;
+  g[1] = gemm_args(u, (int64_t)G * p->d_g, M, G * p->d_g);
+  g[1].seg[0] = gemm_seg(p->w_o2, y, p->d, 0, (int64_t)G * p->d_g, p->d);
+  g[1].n_seg = 1;
+}
+
+size_t stages_workspace(ca::GemmArgs* g, int n) {
+  int64_t f = 0;
+  for (int i = 0; i < n; ++i) {
+    ca::gemm_plan(g[i]);
+    f = g[i].part_floats > f ? g[i].part_floats : f;
+  }
+  return (size_t)f * sizeof(float);
+}
+
+int check_query(const ca_query_proj_params* p, int64_t T, const char* what) {
+  if (p == nullptr) return fail(CA_ERR_ARG, "%s: params NULL", what);
+  if (T < 0 || T > INT32_MAX) return fail(CA_ERR_ARG, "%s: T outside 0..2^31-1", what);
+  if (p->d <= 0 || p->d_c <= 0 || p->n_q <= 0 || p->n_qi < 0 || p->n_i < 0 || (p->n_qi > 0) != (p->n_i > 0))
+    return fail(CA_ERR_ARG, "%s: bad widths (n_qi and n_i are both 0 or both positive)", what);
+  if (p->d % 64 || p->d_c % 64) return fail(CA_ERR_UNSUPPORTED, "%s: d and d_c must be multiples of 64", what);
+  if (!p->w_dq || !p->w_uq || (p->n_qi > 0 && (!p->w_iuq || !p->w_w)))
+    return fail(CA_ERR_ARG, "%s: NULL weight", what);
+  if (!al16(p->w_dq) || !al16(p->w_uq) || (p->n_qi > 0 && (!al16(p->w_iuq) || !al16(p->w_w))))
+    return fail(CA_ERR_ARG, "%s: weights must be 16-byte aligned", what);
+  return 0;
+}
+
+int check_out(const ca_out_proj_params* p, int64_t T, const char* what) {
+  if (p == nullptr) return fail(CA_ERR_ARG, "%s: params NULL", what);
+  if (T < 0 || T > INT32_MAX) return fail(CA_ERR_ARG, "%s: T outside 0..2^31-1", what);
+  if (p->n_h <= 0 || p->c <= 0 || p->d_g <= 0 || p->d <= 0) return fail(CA_ERR_ARG, "%s: bad widths", what);
+  if (p->n_h % 8) return fail(CA_ERR_UNSUPPORTED, "%s: n_h must be a multiple of 8 (8 heads a group)", what);
+  if ((8 * p->c) % 64 || ((p->n_h / 8) * p->d_g) % 64)
+    return fail(CA_ERR_UNSUPPORTED, "%s: 8 c and g d_g must be multiples of 64", what);
+  if (!p->w_o1 || !p->w_o2) return fail(CA_ERR_ARG, "%s: NULL weight", what);
+  if (!al16(p->w_o1) || !al16(p->w_o2)) return fail(CA_ERR_ARG, "%s: weights must be 16-byte aligned", what);
+  return 0;
+}
+
+int run_stages(ca::GemmArgs* g, int n, void* ws, size_t ws_bytes, void* stream, const char* what) {
+  const size_t need = stages_workspace(g, n);
+  if (need > 0 && (ws == nullptr || ws_bytes < need))
+    return fail(CA_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu", what, ws_bytes, need);
+  for (int i = 0; i < n; ++i) {
+    g[i].part = (float*)ws;
+    if (int e = hip_status(ca::launch_gemm(g[i], S(stream)), what)) return e;
+  }
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ca_query_proj_workspace(const ca_query_proj_params* p, int64_t T) {
+  if (check_query(p, T, "ca_query_proj_workspace")) return 0;
+  ca::GemmArgs g[2];
+  query_stages(p, (int)T, nullptr, nullptr, nullptr, nullptr, nullptr, g);
+  return stages_workspace(g, 2);
+}
+
+int ca_query_proj(const ca_query_proj_params* p, const void* h, int64_t T, void* c_q, void* q, void* q_i, float* w_i,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  const char* what = "ca_query_proj";
+  if (int e = check_query(p, T, what)) return e;
+  if (T == 0) return ok();
+  if (!h || !c_q || !q || (p->n_qi > 0 && (!q_i || !w_i))) return fail(CA_ERR_ARG, "%s: NULL buffer", what);
+  if (!al16(h) || !al16(c_q)) return fail(CA_ERR_ARG, "%s: h and c_q must be 16-byte aligned", what);
+  ca::GemmArgs g[2];
+  query_stages(p, (int)T, h, c_q, q, q_i, w_i, g);
+  return run_stages(g, 2, workspace, workspace_bytes, stream, what);
+}
+
+size_t ca_out_proj_workspace(const ca_out_proj_params* p, int64_t T) {
+  if (check_out(p, T, "ca_out_proj_workspace")) return 0;
+  ca::GemmArgs g[2];
+  out_stages(p, (int)T, nullptr, nullptr, nullptr, g);
+  return stages_workspace(g, 2);
+}
+
+int ca_out_proj(const ca_out_proj_params* p, const void* o, int64_t T, void* u, void* y, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  const char* what = "ca_out_proj";
+  if (int e = check_out(p, T, what)) return e;
+  if (T == 0) return ok();
+  if (!o || !u || !y) return fail(CA_ERR_ARG, "%s: NULL buffer", what);
+  if (!al16(o) || !al16(u)) return fail(CA_ERR_ARG, "%s: o and u must be 16-byte aligned", what);
+  ca::GemmArgs g[2];
+  out_stages(p, (int)T, o, u, y, g);
+  return run_stages(g, 2, workspace, workspace_bytes, stream, what);
+}
+
+}  // extern "C"

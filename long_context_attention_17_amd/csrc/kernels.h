@@ -164,6 +164,33 @@ hipError_t launch_decode_front(const DecodeWindowJob& wj, const DecodeEntryJob* 
 hipError_t launch_decode_append(const DecodeWindowJob& wj, const DecodeEntryJob* jobs, int n_jobs,
                                 const int32_t* pos, int B, hipStream_t st);
 
+// C_b = A_b W_b^T for b < batch (bf16 operands, both K-contiguous; fp32 accumulation).
+// A_b [M, K]: row stride lda, batch stride a_batch (elements).  Up to two N segments
+// share A, each with its own W_b [N, K] (ldw, w_batch) and C_b [M, N] (ldc, c_batch,
+// bf16 or fp32).  K % 64 == 0; A, W 16-byte aligned with lda, ldw, a_batch, w_batch
+// multiples of 8.  part: fp32 workspace of part_floats floats (set by gemm_plan) for the
+// K splits, nullptr when that is 0.
+struct GemmSeg {
+  const void* W;
+  void* C;
+  int N, c_f32;
+  int64_t ldw, ldc, w_batch, c_batch;
+  int n_tiles;          // set by gemm_plan
+  int64_t part_off;     // set by gemm_plan
+};
+struct GemmArgs {
+  const void* A;
+  int64_t lda, a_batch;
+  int M, K, batch, n_seg;
+  GemmSeg seg[2];
+  float* part;
+  // set by gemm_plan
+  int m_tiles, n_tiles, k_tiles, k_splits;
+  int64_t part_floats, grid_blocks;
+};
+void gemm_plan(GemmArgs& g);
+hipError_t launch_gemm(GemmArgs g, hipStream_t st);
+
 // One sequence's decode state as parts copied between their live storage and a flat
 // buffer (state.hip).  A part is n_items items of item_bytes (a multiple of 16) each,
 // contiguous in live storage, or (page_table != nullptr) one page each, found through

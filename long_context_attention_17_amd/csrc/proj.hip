@@ -1,0 +1,231 @@
+// The attention sublayer around CSA / HCA: the low-rank query projections and the
+// grouped output projection (dsv4 book Ch.6 "Low-rank query generation", "The
+// lightning indexer" and "Grouped output projections"; Ch.4 "Query head scaling and
+// grouped output projections").  All of it is dense bf16 contraction, run here on
+// one hand-written MFMA GEMM, C[m, n] = sum_k A[m, k] W[n, k] (both operands
+// K-contiguous, fp32 accumulation):
+//   - up to two N segments per launch that share A (W^DQ and W^w both read h; W^UQ
+//     and W^IUQ both read the latent), each with its own weights and output;
+//   - a batch dimension with strides (the g group projections of the output);
+//   - a K split into fp32 partials, added in split order by a second kernel, when the
+//     output alone has too few tiles to fill the chip (decode-sized M).
+#include "common.h"
+#include "kernels.h"
+
+namespace ca {
+
+namespace {
+
+constexpr int kGN = 128, kGK = 64, kGP = kGK + 8;   // N tile, K tile, LDS row pitch (bf16)
+constexpr int kGroupM = 8;                           // M tiles per group of the tile order
+
+template <int MT>
+struct GemmShape {
+  static constexpr int kWavesM = MT >= 64 ? 2 : 1, kWavesN = 4 / kWavesM;
+  static constexpr int kWM = MT / kWavesM, kWN = kGN / kWavesN;      // one wavefront's tile
+  static constexpr int kBM = kWM / 32, kBN = kWN / 32;                // 32x32 MFMA blocks per wavefront
+  static constexpr int kAChunks = MT * kGK / 8 / 256;                 // 16-byte loads per thread
+  static constexpr int kWChunks = kGN * kGK / 8 / 256;
+};
+
+// Rows row0 .. row0 + rows - 1 of a K-contiguous operand, columns k0 .. k0 + 63, into
+// registers: chunk i = threadIdx.x + 256 j is row i / 8, columns 8 (i % 8) .. +7.  Rows past
+// max_row re-read the last row (their products land in rows / columns never stored).
+template <int NCH>
+__device__ __forceinline__ void tile_load(const uint16_t* base, int64_t ld, int row0, int max_row, int k0,
+                                          u32x4* regs) {
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int i = threadIdx.x + 256 * j;
+    int r = row0 + i / 8;
+    r = r < max_row ? r : max_row - 1;
+    regs[j] = *(const u32x4*)(base + (int64_t)r * ld + k0 + 8 * (i % 8));
+  }
+}
+
+template <int NCH>
+__device__ __forceinline__ void tile_store(uint16_t* lds, const u32x4* regs) {
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int i = threadIdx.x + 256 * j;
+    *(u32x4*)(lds + (i / 8) * kGP + 8 * (i % 8)) = regs[j];
+  }
+}
+
+struct TileCoord {
+  int b, s, m_tile, n_tile;
+};
+
+// Block -> tile.  Blocks are dealt to the 8 XCDs round robin; block id i runs on XCD i % 8,
+// so the logical tile is taken as (i % 8) * per_xcd + i / 8: each XCD walks its own
+// contiguous range of the tile order, and within it groups of kGroupM M tiles sweep the N
+// tiles together (an N tile of W is reused by kGroupM neighbours in the XCD's L2).
+__device__ __forceinline__ bool tile_of(const GemmArgs& g, TileCoord& t) {
+  const int64_t id = blockIdx.x;
+  const int64_t per_xcd = g.grid_blocks / 8;
+  const int64_t u_all = (id % 8) * per_xcd + id / 8;
+  const int64_t per_z = (int64_t)g.m_tiles * g.n_tiles;
+  if (u_all >= per_z * g.batch * g.k_splits) return false;
+  const int z = (int)(u_all / per_z);
+  const int64_t u = u_all % per_z;
+  const int64_t in_group = (int64_t)kGroupM * g.n_tiles;
+  const int first_m = (int)(u / in_group) * kGroupM;
+  const int gsize = min(g.m_tiles - first_m, kGroupM);
+  t.m_tile = first_m + (int)((u % in_group) % gsize);
+  t.n_tile = (int)((u % in_group) / gsize);
+  t.b = z / g.k_splits;
+  t.s = z % g.k_splits;
+  return true;
+}
+
+template <int MT>
+__global__ void __launch_bounds__(256) gemm_nt_kernel(GemmArgs g) {
+  using S = GemmShape<MT>;
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][MT * kGP];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws[2][kGN * kGP];
+  TileCoord tc;
+  if (!tile_of(g, tc)) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / S::kWavesN, wn = wave % S::kWavesN;
+  const int sg = tc.n_tile >= g.seg[0].n_tiles ? 1 : 0;
+  const GemmSeg& seg = g.seg[sg];
+  const int m0 = tc.m_tile * MT, n0 = (tc.n_tile - (sg ? g.seg[0].n_tiles : 0)) * kGN;
+  const uint16_t* A = (const uint16_t*)g.A + tc.b * g.a_batch;
+  const uint16_t* W = (const uint16_t*)seg.W + tc.b * seg.w_batch;
+  const int kt0 = (int)((int64_t)tc.s * g.k_tiles / g.k_splits);
+  const int kt1 = (int)((int64_t)(tc.s + 1) * g.k_tiles / g.k_splits);
+
+  f32x16 acc[S::kBM][S::kBN];
+#pragma unroll
+  for (int i = 0; i < S::kBM; ++i)
+#pragma unroll
+    for (int j = 0; j < S::kBN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  u32x4 ra[S::kAChunks], rw[S::kWChunks];
+  tile_load<S::kAChunks>(A, g.lda, m0, g.M, kt0 * kGK, ra);
+  tile_load<S::kWChunks>(W, seg.ldw, n0, seg.N, kt0 * kGK, rw);
+  tile_store<S::kAChunks>(As[0], ra);
+  tile_store<S::kWChunks>(Ws[0], rw);
+  __syncthreads();
+  for (int kt = kt0; kt < kt1; ++kt) {
+    const int cur = (kt - kt0) & 1;
+    const bool more = kt + 1 < kt1;
+    if (more) {                                            // the next K tile into registers
+      tile_load<S::kAChunks>(A, g.lda, m0, g.M, (kt + 1) * kGK, ra);
+      tile_load<S::kWChunks>(W, seg.ldw, n0, seg.N, (kt + 1) * kGK, rw);
+    }
+    const uint16_t* as = As[cur] + (wm * S::kWM + (lane & 31)) * kGP + 8 * (lane >> 5);
+    const uint16_t* ws = Ws[cur] + (wn * S::kWN + (lane & 31)) * kGP + 8 * (lane >> 5);
+#pragma unroll
+    for (int kk = 0; kk < kGK; kk += 16) {
+      bf16x8 af[S::kBM], wf[S::kBN];
+#pragma unroll
+      for (int i = 0; i < S::kBM; ++i) af[i] = *(const bf16x8*)(as + 32 * i * kGP + kk);
+#pragma unroll
+      for (int j = 0; j < S::kBN; ++j) wf[j] = *(const bf16x8*)(ws + 32 * j * kGP + kk);
+#pragma unroll
+      for (int i = 0; i < S::kBM; ++i)
+#pragma unroll
+        for (int j = 0; j < S::kBN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], wf[j], acc[i][j], 0, 0, 0);
+    }
+    if (more) {
+      tile_store<S::kAChunks>(As[cur ^ 1], ra);
+      tile_store<S::kWChunks>(Ws[cur ^ 1], rw);
+    }
+    __syncthreads();
+  }
+  // acc[i][j] element v of lane l: row 32 i + 8 (v / 4) + 4 (l / 32) + v % 4 and column
+  // 32 j + l % 32 of the wavefront's tile
+  float* part = g.k_splits > 1 ? g.part + seg.part_off + ((int64_t)tc.s * g.batch + tc.b) * g.M * seg.N : nullptr;
+#pragma unroll
+  for (int j = 0; j < S::kBN; ++j) {
+    const int n = n0 + wn * S::kWN + 32 * j + (lane & 31);
+    if (n >= seg.N) continue;
+#pragma unroll
+    for (int i = 0; i < S::kBM; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = m0 + wm * S::kWM + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (m >= g.M) continue;
+        if (part) {
+          part[(int64_t)m * seg.N + n] = acc[i][j][v];
+        } else {
+          const int64_t o = tc.b * seg.c_batch + (int64_t)m * seg.ldc + n;
+          if (seg.c_f32) ((float*)seg.C)[o] = acc[i][j][v];
+          else ((uint16_t*)seg.C)[o] = f32_to_bf16_bits(acc[i][j][v]);
+        }
+      }
+  }
+}
+
+// C_b[m, n] = sum_s part[s][b][m][n], the splits added in order; both segments.
+__global__ void __launch_bounds__(256) gemm_reduce_kernel(GemmArgs g) {
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  int sg = 0;
+  const int64_t n0 = (int64_t)g.batch * g.M * g.seg[0].N;
+  if (i >= n0) {
+    i -= n0;
+    sg = 1;
+    if (g.n_seg < 2 || i >= (int64_t)g.batch * g.M * g.seg[1].N) return;
+  }
+  const GemmSeg& seg = g.seg[sg];
+  const int64_t per = (int64_t)g.M * seg.N;
+  const int64_t b = i / per, mn = i % per, m = mn / seg.N, n = mn % seg.N;
+  const float* p = g.part + seg.part_off + b * per + mn;
+  float v = 0.0f;
+  for (int s = 0; s < g.k_splits; ++s) v += p[(int64_t)s * g.batch * per];
+  const int64_t o = b * seg.c_batch + m * seg.ldc + n;
+  if (seg.c_f32) ((float*)seg.C)[o] = v;
+  else ((uint16_t*)seg.C)[o] = f32_to_bf16_bits(v);
+}
+
+int m_tile_of(int M) { return M <= 32 ? 32 : 128; }
+
+}  // namespace
+
+void gemm_plan(GemmArgs& g) {
+  const int mt = m_tile_of(g.M);
+  g.m_tiles = (g.M + mt - 1) / mt;
+  g.n_tiles = 0;
+  for (int s = 0; s < 2; ++s) {
+    g.seg[s].n_tiles = s < g.n_seg ? (g.seg[s].N + kGN - 1) / kGN : 0;
+    g.n_tiles += g.seg[s].n_tiles;
+  }
+  g.k_tiles = g.K / kGK;
+  const int64_t tiles = (int64_t)g.m_tiles * g.n_tiles * g.batch;
+  int s = 1;
+  while (tiles * s < 1024 && 2 * s * 4 <= g.k_tiles && s < 32) s *= 2;   // keep >= 4 K tiles a split
+  g.k_splits = s;
+  int64_t off = 0;
+  for (int q = 0; q < g.n_seg; ++q) {
+    g.seg[q].part_off = off;
+    off += s > 1 ? (int64_t)s * g.batch * g.M * g.seg[q].N : 0;
+  }
+  g.part_floats = off;
+  const int64_t total = tiles * s;
+  g.grid_blocks = (total + 7) / 8 * 8;
+}
+
+hipError_t launch_gemm(GemmArgs g, hipStream_t st) {
+  if (g.M == 0) return hipSuccess;
+  gemm_plan(g);
+  if (g.n_tiles == 0) return hipSuccess;
+  if (g.k_splits > 1 && g.part == nullptr) return hipErrorInvalidValue;
+  if (g.grid_blocks > INT32_MAX) return hipErrorInvalidConfiguration;
+  hipEvent_t ev0, ev1;
+  timer_events(CA_TIMED_PROJ_GEMM, st, &ev0, &ev1);
+  const dim3 grid((unsigned)g.grid_blocks);
+  if (m_tile_of(g.M) == 32) CA_LAUNCH(gemm_nt_kernel<32>, grid, dim3(256), 0, st, ev0, ev1, g);
+  else CA_LAUNCH(gemm_nt_kernel<128>, grid, dim3(256), 0, st, ev0, ev1, g);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || g.k_splits == 1) return e;
+  int64_t n = 0;
+  for (int q = 0; q < g.n_seg; ++q) n += (int64_t)g.batch * g.M * g.seg[q].N;
+  hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, g);
+  return hipGetLastError();
+}
+
+}  // namespace ca

@@ -12,6 +12,8 @@ is seeded with seed * 1000 + id on the device the tensor is made on):
   indexer projections / queries / raw keys: N(0,1)/sqrt(c_I)
   indexer combiner weights w: N(0,1)/sqrt(n_I);  attention sinks: N(0,1)
   RMSNorm gains: 1
+  sublayer: hidden states h and attention outputs o: N(0,1); every projection
+      weight ([out, in]): N(0,1)/sqrt(in); all bf16
   decode contexts: uniform integers in [ctx_lo, ctx_hi] (the new token sits at
       t = ctx); page tables: a random permutation of a pool holding the
       needed pages plus 10%.
@@ -31,6 +33,7 @@ _IDS = {
     "C": 18, "Z": 19, "B": 20,
     "entries": 21, "ikeys": 22, "ctx": 23, "pages": 24,
     "tail": 25, "itail": 26, "new_rows": 27, "new_irows": 28,
+    "h": 29, "w_dq": 30, "w_uq": 31, "w_iuq": 32, "w_w": 33, "w_o1": 34, "w_o2": 35, "o": 36,
 }
 
 
@@ -156,3 +159,22 @@ def decode_layer(cfg, layer: str, device, ctx: torch.Tensor | None = None) -> di
     ones = torch.ones(D, device=device, dtype=torch.float32)
     out["g_kv"], out["g_q"], out["g_w"] = ones, ones.clone(), ones.clone()
     return out
+
+
+def sublayer_weights(dims, seed: int, device, indexer: bool = True) -> dict:
+    """Random projection weights of the attention sublayer, bf16 [out, in] (see configs.SublayerDims)."""
+    d = dims
+    bf = torch.bfloat16
+    w = {"w_dq": normal((d.d_c, d.d), 1.0 / math.sqrt(d.d), seed, "w_dq", device, bf),
+         "w_uq": normal((d.n_h * d.c, d.d_c), 1.0 / math.sqrt(d.d_c), seed, "w_uq", device, bf),
+         "w_o1": normal((d.g, d.d_g, 8 * d.c), 1.0 / math.sqrt(8 * d.c), seed, "w_o1", device, bf),
+         "w_o2": normal((d.d, d.g * d.d_g), 1.0 / math.sqrt(d.g * d.d_g), seed, "w_o2", device, bf)}
+    if indexer:
+        w["w_iuq"] = normal((d.n_i * d.c_i, d.d_c), 1.0 / math.sqrt(d.d_c), seed, "w_iuq", device, bf)
+        w["w_w"] = normal((d.n_i, d.d), 1.0 / math.sqrt(d.d), seed, "w_w", device, bf)
+    return w
+
+
+def hidden(T: int, width: int, seed: int, device, name: str = "h") -> torch.Tensor:
+    """T rows of N(0,1) activations (bf16): hidden states ("h") or attention outputs ("o")."""
+    return normal((T, width), 1.0, seed, name, device, torch.bfloat16)

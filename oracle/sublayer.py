@@ -51,31 +51,39 @@ def store(x, act: str) -> np.ndarray:
     raise ValueError(act)
 
 
+def project(x, w, act):
+    """One linear map of the sublayer, x [T, in] -> x W (w given as [out, in]), stored in act."""
+    return store(np.asarray(x, np.float64) @ np.asarray(w, np.float64).T, act)
+
+
 def low_rank_query(h, w_dq, w_uq, w_iuq, w_w, act="bf16"):
     """Ch.6 "Low-rank query generation" and "The lightning indexer".
     h [T, d]; returns c^Q [T, d_c], q [T, n_h c], q^I [T, n_I c_I], w^I [T, n_I]."""
-    h = np.asarray(h, np.float64)
-    c = store(h @ np.asarray(w_dq, np.float64).T, act)           # shared latent
-    q = store(c @ np.asarray(w_uq, np.float64).T, act)           # main queries from the latent
-    qi = store(c @ np.asarray(w_iuq, np.float64).T, act)         # indexer queries from the same latent
-    wi = store(h @ np.asarray(w_w, np.float64).T, "f32" if act != "f64" else "f64")   # from h itself
-    return {"c": c, "q": q, "qI": qi, "w": wi}
+    c = project(h, w_dq, act)                                     # shared latent
+    return {"c": c,
+            "q": project(c, w_uq, act),                           # main queries from the latent
+            "qI": project(c, w_iuq, act),                         # indexer queries from the same latent
+            "w": project(h, w_w, "f32" if act != "f64" else "f64")}   # from h itself
 
 
-def grouped_out_proj(o, w_o1, w_o2, act="bf16"):
-    """Ch.6 "Grouped output projections".  o [T, n_h c] (heads concatenated in head
-    order); w_o1 [g, d_g, 8 c]; w_o2 [d, g d_g].  Returns u [T, g d_g] (the g group
-    outputs, concatenated) and y [T, d]."""
+def group_proj(o, w_o1, act="bf16"):
+    """The first stage of Ch.6 "Grouped output projections": o [T, n_h c] (heads in head
+    order), w_o1 [g, d_g, 8 c]; group j maps heads 8j .. 8j+7 to block j of u [T, g d_g]."""
     o = np.asarray(o, np.float64)
     w_o1 = np.asarray(w_o1, np.float64)
     g, d_g, width = w_o1.shape
     assert o.shape[1] == g * width, "the heads must split into g groups of the projection's width"
     u = np.empty((o.shape[0], g * d_g))
-    for j in range(g):                                            # group j: heads 8j .. 8j+7
+    for j in range(g):
         u[:, j * d_g:(j + 1) * d_g] = o[:, j * width:(j + 1) * width] @ w_o1[j].T
-    u = store(u, act)
-    y = store(u @ np.asarray(w_o2, np.float64).T, act)
-    return {"u": u, "y": y}
+    return store(u, act)
+
+
+def grouped_out_proj(o, w_o1, w_o2, act="bf16"):
+    """Ch.6 "Grouped output projections".  o [T, n_h c]; w_o1 [g, d_g, 8 c]; w_o2 [d, g d_g].
+    Returns u [T, g d_g] (the g group outputs, concatenated) and y [T, d]."""
+    u = group_proj(o, w_o1, act)
+    return {"u": u, "y": project(u, w_o2, act)}
 
 
 def weight_shapes(d, d_c, n_h, c, n_i, c_i, g, d_g):

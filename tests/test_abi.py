@@ -112,12 +112,12 @@ def test_timer_argument_errors_need_no_device():
     """The launch timer rejects bad arguments before it creates any HIP event."""
     from long_context_attention_17_amd import binding as ca
     lib = ca.lib()
-    assert lib.ca_timer_start(1 << 3, 16) == -1           # unknown kernel bit
+    assert lib.ca_timer_start(1 << 4, 16) == -1           # unknown kernel bit
     assert lib.ca_timer_start(1, 0) == -1                 # no launches to time
     assert lib.ca_timer_start(1, (1 << 20) + 1) == -1     # above the launch cap
     ms, n = ctypes.c_double(-1.0), ctypes.c_int64(-1)
     assert lib.ca_timer_read(-1, ctypes.byref(ms), ctypes.byref(n)) == -1
-    assert lib.ca_timer_read(ca.TIMED_INDEX_SCORES + 1, ctypes.byref(ms), ctypes.byref(n)) == -1
+    assert lib.ca_timer_read(ca.TIMED_PROJ_GEMM + 1, ctypes.byref(ms), ctypes.byref(n)) == -1
     assert lib.ca_timer_read(ca.TIMED_HCA_ATTEND, None, ctypes.byref(n)) == -1
     # nothing was timed: reading reports zero launches without touching the device
     assert lib.ca_timer_read(ca.TIMED_HCA_ATTEND, ctypes.byref(ms), ctypes.byref(n)) == 0
@@ -224,3 +224,33 @@ def test_decode_state_sizes_and_errors():
     assert rc == -4
     st.window = 264                                        # misaligned
     assert lib.ca_state_bytes(ctypes.byref(st), pos) == -1 and b"aligned" in lib.ca_last_error()
+
+
+def test_sublayer_projection_arguments_need_no_device():
+    """The projection entry points check their arguments and size their workspaces on the
+    host: bad widths and misaligned weights are rejected before any launch, T = 0 is a no-op,
+    and only decode-sized T (too few output tiles to fill the chip) needs K-split partials."""
+    from long_context_attention_17_amd import binding as ca
+    lib = ca.lib()
+    fake = 1 << 20                                   # aligned stand-in addresses (never dereferenced)
+    qp = ca.QueryProjParams(7168, 1536, 128 * 512, 64 * 128, 64, fake, fake, fake, fake)
+    op = ca.OutProjParams(128, 512, 1024, 7168, fake, fake)
+    assert lib.ca_query_proj(None, None, 0, None, None, None, None, None, 0, None) == -1
+    assert lib.ca_query_proj(ctypes.byref(qp), None, 0, None, None, None, None, None, 0, None) == 0
+    assert lib.ca_out_proj(ctypes.byref(op), None, 0, None, None, None, 0, None) == 0
+    assert lib.ca_query_proj(ctypes.byref(qp), None, 4, None, None, None, None, None, 0, None) == -1   # NULL buffers
+    assert lib.ca_query_proj(ctypes.byref(qp), None, -1, None, None, None, None, None, 0, None) == -1
+    bad = ca.QueryProjParams(7168 + 32, 1536, 128 * 512, 64 * 128, 64, fake, fake, fake, fake)
+    assert lib.ca_query_proj(ctypes.byref(bad), None, 0, None, None, None, None, None, 0, None) == -3
+    bad = ca.QueryProjParams(7168, 1536, 128 * 512, 64 * 128, 0, fake, fake, fake, fake)        # n_qi without n_i
+    assert lib.ca_query_proj(ctypes.byref(bad), None, 0, None, None, None, None, None, 0, None) == -1
+    bad = ca.QueryProjParams(7168, 1536, 128 * 512, 64 * 128, 64, fake + 2, fake, fake, fake)
+    assert lib.ca_query_proj(ctypes.byref(bad), None, 0, None, None, None, None, None, 0, None) == -1
+    assert "aligned" in lib.ca_last_error().decode()
+    bad = ca.OutProjParams(60, 512, 1024, 7168, fake, fake)                                    # 8 heads a group
+    assert lib.ca_out_proj(ctypes.byref(bad), None, 0, None, None, None, 0, None) == -3
+    assert lib.ca_query_proj_workspace(ctypes.byref(qp), 32768) == 0
+    assert lib.ca_out_proj_workspace(ctypes.byref(op), 32768) == 0
+    assert lib.ca_query_proj_workspace(ctypes.byref(qp), 8) > 0       # h W^DQ: 13 output tiles at T = 8
+    assert lib.ca_out_proj_workspace(ctypes.byref(op), 8) > 0
+    assert lib.ca_query_proj_workspace(None, 8) == 0
