@@ -9,7 +9,10 @@ attention over 8,192 + 128 items).  Other presets: --workload decode_mixed | pre
 prefill_hca_128k | tiny, the million-token decode with FP4 indexer keys
 (decode_1m_fp4idx) or FP4 keys and queries (decode_1m_fp4qk), and prefills
 that continue a stored prefix (prefill_csa_32k_after_16k,
-prefill_hca_128k_after_64k).
+prefill_hca_128k_after_64k).  The attention sublayer's projections (low-rank
+queries, grouped output projection) have workloads of their own:
+sublayer_pro_decode_b8, sublayer_flash_decode_b64, sublayer_flash_prefill_32k,
+sublayer_pro_prefill_32k.
 
 Prints ONE JSON line.  Inputs are resident in HBM before the timed region; the
 timed region rotates independent replicas of every cache (so the per-step
@@ -47,10 +50,16 @@ WORKLOADS = {"decode_1m": 5, "decode_mixed": 4, "prefill_csa_32k": 2, "prefill_h
              # the window and the new rows computed)
              "prefill_csa_32k_after_16k": (2, {"prefix": 16384, "name": "csa_prefill_32k_after_16k_prefix"}),
              "prefill_hca_128k_after_64k": (3, {"prefix": 65536, "name": "hca_prefill_128k_after_64k_prefix"})}
+# the attention sublayer's projections (low-rank queries, grouped output projection) at the
+# Flash / Pro widths: name -> (widths, tokens per step)
+SUBLAYER_WORKLOADS = {"sublayer_pro_decode_b8": ("pro", 8), "sublayer_flash_decode_b64": ("flash", 64),
+                      "sublayer_flash_prefill_32k": ("flash", 32768), "sublayer_pro_prefill_32k": ("pro", 32768)}
+SUBLAYER_METRIC = "attention sublayer projections (low-rank q + grouped output) tokens/s; % HBM/MFMA peak"
 # sources that define each timed kernel (its counter readings go stale when they change)
 KERNEL_SOURCES = {"attend_mx_kernel": ["attend.hip", "common.h", "kernels.h"],
                   "index_scores_fp8_kernel": ["indexer.hip", "common.h", "kernels.h"],
-                  "index_scores_fp4_kernel": ["indexer.hip", "common.h", "kernels.h"]}
+                  "index_scores_fp4_kernel": ["indexer.hip", "common.h", "kernels.h"],
+                  "gemm_nt_kernel": ["proj.hip", "common.h", "kernels.h"]}
 
 
 def progress(msg):
@@ -400,6 +409,116 @@ def bench_prefill(cfg, steps, warmup, replicas, args):
     return value, ms_step, config, roof, extra, objs
 
 
+def bench_sublayer(name, steps, warmup, replicas):
+    """One step = ca_query_proj + ca_out_proj for T tokens (synthetic weights of the model's
+    widths; `replicas` weight sets used in turn so that no step finds its weights in cache)."""
+    from long_context_attention_17_amd import binding as ca, synth
+    from long_context_attention_17_amd.configs import SUBLAYERS
+    dname, T = SUBLAYER_WORKLOADS[name]
+    d = SUBLAYERS[dname]
+    bf = torch.bfloat16
+    sets = []
+    for i in range(replicas):
+        w = synth.sublayer_weights(d, 100 + i, "cuda")
+        sets.append((w, ca.QueryProj(w["w_dq"], w["w_uq"], w["w_iuq"], w["w_w"]), ca.OutProj(w["w_o1"], w["w_o2"], d.c)))
+    h = synth.hidden(T, d.d, 7, "cuda")
+    o = synth.hidden(T, d.n_h * d.c, 7, "cuda", name="o")
+    c_q = torch.empty(T, d.d_c, dtype=bf, device="cuda")
+    q = torch.empty(T, d.n_h * d.c, dtype=bf, device="cuda")
+    qi = torch.empty(T, d.n_i * d.c_i, dtype=bf, device="cuda")
+    wi = torch.empty(T, d.n_i, dtype=torch.float32, device="cuda")
+    u = torch.empty(T, d.g * d.d_g, dtype=bf, device="cuda")
+    y = torch.empty(T, d.d, dtype=bf, device="cuda")
+    ws = torch.empty(max(1, sets[0][1].workspace(T), sets[0][2].workspace(T)), dtype=torch.uint8, device="cuda")
+
+    def step(i):
+        _, qp, op = sets[i % replicas]
+        qp(h, c_q, q, qi, wi, ws=ws)
+        op(o, u, y, ws=ws)
+
+    graphs = []
+    step(0)
+    torch.cuda.synchronize()
+    for i in range(replicas):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(i)
+        graphs.append(g)
+    for i in range(warmup):
+        graphs[i % replicas].replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        graphs[i % replicas].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    kt, queued = time_kernels(step, {"gemm": ca.TIMED_PROJ_GEMM}, max(steps, 10))
+    launch_ms, per_step = kt["gemm"]
+    flops = 2.0 * T * (d.d * (d.d_c + d.n_i) + d.d_c * (d.n_h * d.c + d.n_i * d.c_i)
+                       + d.n_h * d.c * d.d_g + d.g * d.d_g * d.d)
+    wbytes = 2 * sum(int(v.numel()) for v in sets[0][0].values())
+    abytes = T * (2 * (d.d + d.d_c + d.n_h * d.c + d.n_i * d.c_i + d.n_h * d.c + d.g * d.d_g + d.d) + 4 * d.n_i)
+    abytes += T * 2 * (d.d_c + d.g * d.d_g)             # the latent and u, read back by the second stages
+    gemm_ms = launch_ms * per_step
+    symbol = f"gemm_nt_kernel<{32 if T <= 32 else 128}>"
+    if T <= 256:
+        roof = kernel_roofline("hbm", wbytes + abytes, symbol, gemm_ms)
+        roof["work_unit"] = "bytes of weights and activations per step (all GEMM launches of the step)"
+    else:
+        roof = kernel_roofline("mfma", flops, symbol, gemm_ms)
+        roof["work_unit"] = "flops per step (all GEMM launches of the step)"
+    roof["launch_ms"] = round(launch_ms, 5)
+    roof["launches_per_step"] = per_step
+    roof["stage"] = "sublayer"
+    config = {"workload": f"{name}: low-rank query projections (d={d.d} -> d_c={d.d_c} -> {d.n_h}x{d.c} queries, "
+                          f"{d.n_i}x{d.c_i} indexer queries, {d.n_i} combiner weights) and grouped output projection "
+                          f"({d.g} groups of 8 heads -> d_g={d.d_g} -> d={d.d}) for {T} tokens, bf16, synthetic weights",
+              "tokens": T, "replicas": replicas}
+    extra = {"metric_note": SUBLAYER_METRIC, "kernel_timing_queued": queued,
+             "step_flops": flops, "step_weight_bytes": wbytes,
+             "timing": "whole step: HIP-graph replays (one graph per weight set); kernel: HIP events recorded by "
+                       "the library around each eager GEMM launch, summed over the step's launches"}
+    return T / (ms / 1e3), ms, config, roof, extra, (sets, graphs)
+
+
+def cpu_baseline_sublayer(name, budget_s=10.0):
+    """The oracle's sublayer (numpy fp64 matmuls) on a sample of rows, all host threads, then one thread."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from oracle import sublayer as osl
+    from long_context_attention_17_amd import synth
+    from long_context_attention_17_amd.configs import SUBLAYERS
+    dname, T = SUBLAYER_WORKLOADS[name]
+    d = SUBLAYERS[dname]
+    w = {k: v.double().numpy() for k, v in synth.sublayer_weights(d, 100, "cpu").items()}
+    n = min(T, 64)
+    h = synth.hidden(n, d.d, 7, "cpu").double().numpy()
+    o = synth.hidden(n, d.n_h * d.c, 7, "cpu", name="o").double().numpy()
+
+    def run(rows):
+        osl.low_rank_query(h[:rows], w["w_dq"], w["w_uq"], w["w_iuq"], w["w_w"], act="bf16")
+        osl.grouped_out_proj(o[:rows], w["w_o1"], w["w_o2"], act="bf16")
+
+    reps, t = 0, 0.0
+    while t < budget_s and reps < 20:
+        t0 = time.perf_counter()
+        run(n)
+        t += time.perf_counter() - t0
+        reps += 1
+    threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        run(max(1, n // 8))
+        t1 = time.perf_counter() - t0
+    return {"value": round(n * reps / t, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_threads": os.cpu_count(),
+            "sample": f"{n} of {T} rows, {reps} repeat(s), {t:.1f} s (numpy fp64 matmuls on {threads} BLAS threads)",
+            "one_thread": {"value": round(max(1, n // 8) / t1, 4), "unit": "tokens/s",
+                           "sample": f"{max(1, n // 8)} rows, {t1:.1f} s"}}
+
+
 # ------------------------------------------------------------------ CPU baseline (oracle)
 def cpu_baseline_decode(cfg, ctx_state, budget_s=12.0):
     """The oracle's decode step (indexer + top-k + CSA attention + HCA attention) for a
@@ -437,11 +556,38 @@ def cpu_baseline_decode(cfg, ctx_state, budget_s=12.0):
         if reps >= 50:
             break
     tok_s = len(seqs) * reps / t_total
-    cores = min(oracle.num_threads(), len(seqs))
+    cores = oracle.num_threads()
+    # the same step for one sequence on one thread (a few repeats)
+    progress("cpu baseline: one thread")
+    oracle.set_num_threads(1)
+    try:
+        reps1, t1 = 0, 0.0
+        while t1 < 3.0 and reps1 < 5:
+            t0 = time.perf_counter()
+            opl.csa_decode_step(cfg, states["csa"][0], states["csa"][1], seqs=seqs[:1])
+            opl.hca_decode_step(cfg, states["hca"][0], states["hca"][1], seqs=seqs[:1])
+            t1 += time.perf_counter() - t0
+            reps1 += 1
+    finally:
+        oracle.set_num_threads(cores)
     return {"value": round(tok_s, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_threads": os.cpu_count(),
             "sample": f"{len(seqs)} of {cfg.B} sequences (both layers' indexer, top-k and attention), {reps} repeat(s), "
-                      f"{t_total:.1f} s; the oracle parallelizes over query rows, so {cores} of "
-                      f"{oracle.num_threads()} host threads were busy"}
+                      f"{t_total:.1f} s; the oracle's loops run on {cores} threads (over keys in the indexer, "
+                      f"over heads in attention)",
+            "one_thread": {"value": round(reps1 / t1, 4), "unit": "tokens/s",
+                           "sample": f"sequence 0 only, {reps1} repeat(s), {t1:.1f} s"}}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline_prefill(cfg, budget_s=12.0):
@@ -459,9 +605,26 @@ def cpu_baseline_prefill(cfg, budget_s=12.0):
         (opl.csa_prefill if name == "csa" else opl.hca_prefill)(cfg, inp, pt.numpy()[0], n_pool, rows=rows)
         t_total += time.perf_counter() - t0
     n_rows = len(rows)
-    return {"value": round(n_rows / t_total, 4), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+    cores = oracle.num_threads()
+    rows1 = rows[::8]
+    oracle.set_num_threads(1)
+    try:
+        t1 = 0.0
+        for name in (["csa"] if cfg.csa else []) + (["hca"] if cfg.hca else []):
+            inp = synth.prefill_layer(cfg, name, "cpu")
+            ratio = cfg.m if name == "csa" else cfg.m_hca
+            pt, n_pool = synth.page_table([cfg.L // ratio], cfg.page, cfg.seed)
+            t0 = time.perf_counter()
+            (opl.csa_prefill if name == "csa" else opl.hca_prefill)(cfg, inp, pt.numpy()[0], n_pool, rows=rows1)
+            t1 += time.perf_counter() - t0
+    finally:
+        oracle.set_num_threads(cores)
+    return {"value": round(n_rows / t_total, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_threads": os.cpu_count(),
             "sample": f"{n_rows} query rows from the second half of the sequence (compression of the whole "
-                      f"sequence included), {t_total:.1f} s"}
+                      f"sequence included), {t_total:.1f} s on {cores} threads",
+            "one_thread": {"value": round(len(rows1) / t1, 4), "unit": "tokens/s",
+                           "sample": f"{len(rows1)} of those rows (compression included), {t1:.1f} s"}}
 
 
 def main():
@@ -469,7 +632,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode_1m", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="decode_1m", choices=sorted(WORKLOADS) + sorted(SUBLAYER_WORKLOADS))
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -481,9 +644,25 @@ def main():
               "the library has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
     from long_context_attention_17_amd.configs import CONFIGS
+    torch.cuda.set_device(0)
+    if args.workload in SUBLAYER_WORKLOADS:
+        value, ms, config, roof, extra, state = bench_sublayer(args.workload, args.steps, args.warmup,
+                                                               max(args.replicas, 3))
+        roof["traffic"] = None
+        line = {"metric": SUBLAYER_METRIC, "value": round(value, 3), "unit": "tokens/s", "n_gpus": 1,
+                "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+                "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": config,
+                "roofline": roof}
+        del state
+        torch.cuda.empty_cache()
+        if not args.no_cpu_baseline:
+            line["cpu_baseline"] = cpu_baseline_sublayer(args.workload)
+        line.update(extra)
+        line["kernel_source_hash"] = kernel_source_hash(roof["kernel"])
+        print(json.dumps(line), flush=True)
+        return
     wl = WORKLOADS[args.workload]
     cfg = CONFIGS[wl] if isinstance(wl, int) else dataclasses.replace(CONFIGS[wl[0]], **wl[1])
-    torch.cuda.set_device(0)
     if args.copy_calibration_mib > 0:
         src = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)

@@ -16,16 +16,22 @@ namespace ca {
 
 namespace {
 
-constexpr int kGN = 128, kGK = 64, kGP = kGK + 8;   // N tile, K tile, LDS row pitch (bf16)
+constexpr int kGK = 64, kGP = kGK + 8;               // K tile, LDS row pitch (bf16; 144 B rows)
 constexpr int kGroupM = 8;                           // M tiles per group of the tile order
 
-template <int MT>
+// Workgroup tile MT x 128 (4 wavefronts), one K tile of register prefetch:
+//   32 x 128 for decode-sized M: wavefronts side by side along N (32 x 32 each);
+//   128 x 128: wavefronts 2 x 2 of 64 x 64, two workgroups per CU (one's barrier and LDS
+//     stores overlap the other's MFMAs; a 256-row tile at one workgroup per CU measured slower).
+template <int MT, int NT>
 struct GemmShape {
-  static constexpr int kWavesM = MT >= 64 ? 2 : 1, kWavesN = 4 / kWavesM;
-  static constexpr int kWM = MT / kWavesM, kWN = kGN / kWavesN;      // one wavefront's tile
+  static constexpr int kWavesM = MT >= 128 ? 2 : 1, kWavesN = 4 / kWavesM;
+  static constexpr int kWM = MT / kWavesM, kWN = NT / kWavesN;       // one wavefront's tile
   static constexpr int kBM = kWM / 32, kBN = kWN / 32;                // 32x32 MFMA blocks per wavefront
   static constexpr int kAChunks = MT * kGK / 8 / 256;                 // 16-byte loads per thread
-  static constexpr int kWChunks = kGN * kGK / 8 / 256;
+  static constexpr int kWChunks = NT * kGK / 8 / 256;
+  static constexpr int kPF = 1;
+  static constexpr int kCPitch = NT + 8;                              // bf16 output staging row pitch
 };
 
 // Rows row0 .. row0 + rows - 1 of a K-contiguous operand, columns k0 .. k0 + 63, into
@@ -78,46 +84,42 @@ __device__ __forceinline__ bool tile_of(const GemmArgs& g, TileCoord& t) {
   return true;
 }
 
-template <int MT>
+template <int MT, int NT>
 __global__ void __launch_bounds__(256) gemm_nt_kernel(GemmArgs g) {
-  using S = GemmShape<MT>;
+  using S = GemmShape<MT, NT>;
   __shared__ __attribute__((aligned(16))) uint16_t As[2][MT * kGP];
-  __shared__ __attribute__((aligned(16))) uint16_t Ws[2][kGN * kGP];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws[2][NT * kGP];
   TileCoord tc;
   if (!tile_of(g, tc)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / S::kWavesN, wn = wave % S::kWavesN;
   const int sg = tc.n_tile >= g.seg[0].n_tiles ? 1 : 0;
   const GemmSeg& seg = g.seg[sg];
-  const int m0 = tc.m_tile * MT, n0 = (tc.n_tile - (sg ? g.seg[0].n_tiles : 0)) * kGN;
+  const int m0 = tc.m_tile * MT, n0 = (tc.n_tile - (sg ? g.seg[0].n_tiles : 0)) * NT;
   const uint16_t* A = (const uint16_t*)g.A + tc.b * g.a_batch;
   const uint16_t* W = (const uint16_t*)seg.W + tc.b * seg.w_batch;
   const int kt0 = (int)((int64_t)tc.s * g.k_tiles / g.k_splits);
-  const int kt1 = (int)((int64_t)(tc.s + 1) * g.k_tiles / g.k_splits);
+  const int n_kt = (int)((int64_t)(tc.s + 1) * g.k_tiles / g.k_splits) - kt0;
 
   f32x16 acc[S::kBM][S::kBN];
 #pragma unroll
   for (int i = 0; i < S::kBM; ++i)
 #pragma unroll
-    for (int j = 0; j < S::kBN; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    for (int j = 0; j < S::kBN; ++j) acc[i][j] = f32x16{};
 
-  u32x4 ra[S::kAChunks], rw[S::kWChunks];
-  tile_load<S::kAChunks>(A, g.lda, m0, g.M, kt0 * kGK, ra);
-  tile_load<S::kWChunks>(W, seg.ldw, n0, seg.N, kt0 * kGK, rw);
-  tile_store<S::kAChunks>(As[0], ra);
-  tile_store<S::kWChunks>(Ws[0], rw);
-  __syncthreads();
-  for (int kt = kt0; kt < kt1; ++kt) {
-    const int cur = (kt - kt0) & 1;
-    const bool more = kt + 1 < kt1;
-    if (more) {                                            // the next K tile into registers
-      tile_load<S::kAChunks>(A, g.lda, m0, g.M, (kt + 1) * kGK, ra);
-      tile_load<S::kWChunks>(W, seg.ldw, n0, seg.N, (kt + 1) * kGK, rw);
-    }
-    const uint16_t* as = As[cur] + (wm * S::kWM + (lane & 31)) * kGP + 8 * (lane >> 5);
-    const uint16_t* ws = Ws[cur] + (wn * S::kWN + (lane & 31)) * kGP + 8 * (lane >> 5);
+  // register stages of the K tiles in flight (PF of them)
+  u32x4 ra[S::kPF][S::kAChunks], rw[S::kPF][S::kWChunks];
+  auto load = [&](int p, int i) {
+    tile_load<S::kAChunks>(A, g.lda, m0, g.M, (kt0 + i) * kGK, ra[p]);
+    tile_load<S::kWChunks>(W, seg.ldw, n0, seg.N, (kt0 + i) * kGK, rw[p]);
+  };
+  auto store = [&](int p, int buf) {
+    tile_store<S::kAChunks>(As[buf], ra[p]);
+    tile_store<S::kWChunks>(Ws[buf], rw[p]);
+  };
+  auto mfmas = [&](int buf) {
+    const uint16_t* as = As[buf] + (wm * S::kWM + (lane & 31)) * kGP + 8 * (lane >> 5);
+    const uint16_t* ws = Ws[buf] + (wn * S::kWN + (lane & 31)) * kGP + 8 * (lane >> 5);
 #pragma unroll
     for (int kk = 0; kk < kGK; kk += 16) {
       bf16x8 af[S::kBM], wf[S::kBN];
@@ -131,34 +133,80 @@ __global__ void __launch_bounds__(256) gemm_nt_kernel(GemmArgs g) {
         for (int j = 0; j < S::kBN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], wf[j], acc[i][j], 0, 0, 0);
     }
-    if (more) {
-      tile_store<S::kAChunks>(As[cur ^ 1], ra);
-      tile_store<S::kWChunks>(Ws[cur ^ 1], rw);
-    }
+  };
+
+  // K tile i sits in register stage i % PF until it is stored to LDS buffer i % 2
+  load(0, 0);
+  if (S::kPF > 1 && n_kt > 1) load(S::kPF - 1, 1);
+  store(0, 0);
+  __syncthreads();
+  // step i (c = i % 2, a constant in each unrolled copy): refill the register stage that
+  // tile i left for tile i + PF, multiply tile i, store tile i + 1, barrier
+  auto step = [&](int i, int c) {
+    if (i + S::kPF < n_kt) load(S::kPF > 1 ? c : 0, i + S::kPF);
+    mfmas(c);
+    if (i + 1 < n_kt) store(S::kPF > 1 ? c ^ 1 : 0, c ^ 1);
     __syncthreads();
+  };
+  int i = 0;
+  for (; i + 1 < n_kt; i += 2) {
+    step(i, 0);
+    step(i + 1, 1);
   }
+  if (i < n_kt) step(i, 0);
+
   // acc[i][j] element v of lane l: row 32 i + 8 (v / 4) + 4 (l / 32) + v % 4 and column
   // 32 j + l % 32 of the wavefront's tile
-  float* part = g.k_splits > 1 ? g.part + seg.part_off + ((int64_t)tc.s * g.batch + tc.b) * g.M * seg.N : nullptr;
+  const int mw = wm * S::kWM + 4 * (lane >> 5), nw = wn * S::kWN + (lane & 31);
+  if (g.k_splits == 1 && !seg.c_f32) {
+    // bf16 output: the tile goes through LDS (free after the last barrier) so that the global
+    // stores are 16-byte runs along the rows of C
+    static_assert(S::kCPitch <= 2 * kGP, "output staging fits the A operand buffers");
+    uint16_t* ct = &As[0][0];
 #pragma unroll
-  for (int j = 0; j < S::kBN; ++j) {
-    const int n = n0 + wn * S::kWN + 32 * j + (lane & 31);
-    if (n >= seg.N) continue;
+    for (int i2 = 0; i2 < S::kBM; ++i2)
 #pragma unroll
-    for (int i = 0; i < S::kBM; ++i)
+      for (int j = 0; j < S::kBN; ++j) {
+        const f32x16 blk = acc[i2][j];
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          ct[(mw + 32 * i2 + 8 * (v >> 2) + (v & 3)) * S::kCPitch + nw + 32 * j] = f32_to_bf16_bits(blk[v]);
+      }
+    __syncthreads();
+    uint16_t* cbase = (uint16_t*)seg.C + tc.b * seg.c_batch;
+    const bool vec = ((seg.ldc | tc.b * seg.c_batch) & 7) == 0 && ((uintptr_t)seg.C & 15) == 0;
+    constexpr int kChunksRow = NT / 8;
+#pragma unroll
+    for (int p = 0; p < MT * kChunksRow / 256; ++p) {
+      const int q = threadIdx.x + 256 * p, r = q / kChunksRow, c = 8 * (q % kChunksRow);
+      const int m = m0 + r, n = n0 + c;
+      if (m >= g.M || n >= seg.N) continue;
+      const u32x4 x = *(const u32x4*)(ct + r * S::kCPitch + c);
+      uint16_t* dst = cbase + (int64_t)m * seg.ldc + n;
+      if (vec && n + 8 <= seg.N) {
+        *(u32x4*)dst = x;
+      } else {
+        for (int e = 0; e < 8 && n + e < seg.N; ++e) dst[e] = (uint16_t)(x[e >> 1] >> (16 * (e & 1)));
+      }
+    }
+    return;
+  }
+  const int64_t part_base = seg.part_off + ((int64_t)tc.s * g.batch + tc.b) * g.M * seg.N;
+#pragma unroll
+  for (int i2 = 0; i2 < S::kBM; ++i2)
+#pragma unroll
+    for (int j = 0; j < S::kBN; ++j) {
+      const f32x16 blk = acc[i2][j];
+      const int n = n0 + nw + 32 * j;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int m = m0 + wm * S::kWM + 32 * i + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (m >= g.M) continue;
-        if (part) {
-          part[(int64_t)m * seg.N + n] = acc[i][j][v];
-        } else {
-          const int64_t o = tc.b * seg.c_batch + (int64_t)m * seg.ldc + n;
-          if (seg.c_f32) ((float*)seg.C)[o] = acc[i][j][v];
-          else ((uint16_t*)seg.C)[o] = f32_to_bf16_bits(acc[i][j][v]);
+        const int m = m0 + mw + 32 * i2 + 8 * (v >> 2) + (v & 3);
+        if (m < g.M && n < seg.N) {
+          if (g.k_splits > 1) g.part[part_base + (int64_t)m * seg.N + n] = blk[v];
+          else ((float*)seg.C)[tc.b * seg.c_batch + (int64_t)m * seg.ldc + n] = blk[v];
         }
       }
-  }
+    }
 }
 
 // C_b[m, n] = sum_s part[s][b][m][n], the splits added in order; both segments.
@@ -182,22 +230,26 @@ __global__ void __launch_bounds__(256) gemm_reduce_kernel(GemmArgs g) {
   else ((uint16_t*)seg.C)[o] = f32_to_bf16_bits(v);
 }
 
+// Tile rows by M: 32 for decode-sized M, else 128.
 int m_tile_of(int M) { return M <= 32 ? 32 : 128; }
+int n_tile_of(int) { return 128; }
 
 }  // namespace
 
 void gemm_plan(GemmArgs& g) {
-  const int mt = m_tile_of(g.M);
+  const int mt = m_tile_of(g.M), nt = n_tile_of(g.M);
   g.m_tiles = (g.M + mt - 1) / mt;
   g.n_tiles = 0;
   for (int s = 0; s < 2; ++s) {
-    g.seg[s].n_tiles = s < g.n_seg ? (g.seg[s].N + kGN - 1) / kGN : 0;
+    g.seg[s].n_tiles = s < g.n_seg ? (g.seg[s].N + nt - 1) / nt : 0;
     g.n_tiles += g.seg[s].n_tiles;
   }
   g.k_tiles = g.K / kGK;
   const int64_t tiles = (int64_t)g.m_tiles * g.n_tiles * g.batch;
+  // K splits until the launch has ~1,000 workgroups (four per CU), each split keeping at
+  // least 4 K tiles
   int s = 1;
-  while (tiles * s < 1024 && 2 * s * 4 <= g.k_tiles && s < 32) s *= 2;   // keep >= 4 K tiles a split
+  while (tiles * s < 1024 && 2 * s * 4 <= g.k_tiles && s < 32) s *= 2;
   g.k_splits = s;
   int64_t off = 0;
   for (int q = 0; q < g.n_seg; ++q) {
@@ -218,8 +270,8 @@ hipError_t launch_gemm(GemmArgs g, hipStream_t st) {
   hipEvent_t ev0, ev1;
   timer_events(CA_TIMED_PROJ_GEMM, st, &ev0, &ev1);
   const dim3 grid((unsigned)g.grid_blocks);
-  if (m_tile_of(g.M) == 32) CA_LAUNCH(gemm_nt_kernel<32>, grid, dim3(256), 0, st, ev0, ev1, g);
-  else CA_LAUNCH(gemm_nt_kernel<128>, grid, dim3(256), 0, st, ev0, ev1, g);
+  if (m_tile_of(g.M) == 32) CA_LAUNCH((gemm_nt_kernel<32, 128>), grid, dim3(256), 0, st, ev0, ev1, g);
+  else CA_LAUNCH((gemm_nt_kernel<128, 128>), grid, dim3(256), 0, st, ev0, ev1, g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || g.k_splits == 1) return e;
   int64_t n = 0;

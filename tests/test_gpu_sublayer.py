@@ -110,14 +110,22 @@ def sample(T, n):
                                      np.linspace(0, T - 1, n).astype(np.int64)]))
 
 
-@pytest.mark.parametrize("T", [1, 5, 33, 300])
+@pytest.mark.parametrize("T", [1, 5, 33, 300, 2100])
 def test_query_proj_small_ragged(T):
     """Several M / N / K tiles with ragged edges: d = 2240 (35 K tiles, split 8 ways at small T),
-    d_c = 192 (1.5 N tiles), 8 combiner weights (one partial tile), T from 1 to 300."""
+    d_c = 192 (1.5 N tiles), 8 combiner weights (one partial tile), T from 1 to 2100 (both tile
+    shapes: 32 and 128 rows)."""
     run_query(_small_dims(), T)
 
 
-@pytest.mark.parametrize("T", [1, 5, 33, 300])
+@pytest.mark.parametrize("T", [5, 300])
+def test_query_proj_widths_off_the_store_granule(T):
+    """Output widths that are not multiples of 8 (100 query channels, 60 indexer channels, 3
+    weights): rows of C are not 16-byte aligned, and each row ends in a partial 8-column run."""
+    run_query(_small_dims(n_h=1, c=100, n_i=3, c_i=20), T)
+
+
+@pytest.mark.parametrize("T", [1, 5, 33, 300, 2100])
 def test_out_proj_small_ragged(T):
     run_out(_small_dims(), T)
 
