@@ -462,7 +462,7 @@ def bench_sublayer(name, steps, warmup, replicas):
     abytes = T * (2 * (d.d + d.d_c + d.n_h * d.c + d.n_i * d.c_i + d.n_h * d.c + d.g * d.d_g + d.d) + 4 * d.n_i)
     abytes += T * 2 * (d.d_c + d.g * d.d_g)             # the latent and u, read back by the second stages
     gemm_ms = launch_ms * per_step
-    symbol = f"gemm_nt_kernel<{32 if T <= 32 else 128}>"
+    symbol = f"gemm_nt_kernel<{32 if T <= 32 else 128}, 128>"
     if T <= 256:
         roof = kernel_roofline("hbm", wbytes + abytes, symbol, gemm_ms)
         roof["work_unit"] = "bytes of weights and activations per step (all GEMM launches of the step)"
