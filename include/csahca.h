@@ -282,6 +282,9 @@ int ca_index_topk_decode(const ca_index_params* p, const void* qI, const float* 
 /* ca_window_append.  CSA indices outside [0, floor(t/m)) or in missing     */
 /* pages are skipped.  lse (optional, float32 [rows, n_heads]) receives     */
 /* log(sum_x e^{scale q^.x} + e^{sink}).                                   */
+/* Limits: the pool's records (n_pages * page_size) and the window's rows   */
+/* (decode: rows * W; prefill: W) must number fewer than 2^31 - 1, else     */
+/* CA_ERR_UNSUPPORTED (items are addressed by 31-bit record / row index).  */
 /* ------------------------------------------------------------------------ */
 typedef struct ca_attend_params {
   int32_t n_heads;

@@ -489,6 +489,13 @@ static int attend_common(const ca_attend_params* p, const void* q, const float* 
   if (max_pos > 0x7FFFFFFF) return fail(CA_ERR_ARG, "%s: max_pos beyond 2^31 - 1", what);
   if (mode == 1 && max_pos / ratio > (int64_t)kv->max_pages * kv->page_size)
     return fail(CA_ERR_ARG, "%s: page table holds fewer than floor(max_pos/ratio) entries", what);
+  // the attention kernels address an item by pool record index (page * page_size + slot) or
+  // by window row, in 31 bits: every record and every window row must have an index below
+  // 2^31 - 1 (e.g. 1.37 TB of fp8 records)
+  if ((int64_t)kv->n_pages * kv->page_size >= 0x7FFFFFFF)
+    return fail(CA_ERR_UNSUPPORTED, "%s: pool holds 2^31 - 1 or more records", what);
+  if ((int64_t)(decode ? n_rows : 1) * W >= 0x7FFFFFFF)
+    return fail(CA_ERR_UNSUPPORTED, "%s: window holds 2^31 - 1 or more rows", what);
   (void)win_rows;
   a.q = q;
   a.q_gain = q_gain;

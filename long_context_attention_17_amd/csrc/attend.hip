@@ -482,7 +482,7 @@ struct MxShared {
   __attribute__((aligned(16))) uint8_t ring[C::kStages][C::kStageBytes];
   __attribute__((aligned(16))) __bf16 tile[C::kFp8 ? kRows * kPitch : 8];
   __attribute__((aligned(16))) bf16x8 pex[4][64][2];    // probabilities of each wavefront (A fragments)
-  uint32_t items[kMaxItems];            // item sources: 16 B units from the pool, | kWinFlag for the window
+  uint32_t items[kMaxItems];            // item sources: pool record index, or kWinFlag | window row
   uint32_t valid[C::kStages][4];        // bit u of valid[st][w]: ring row w + 4u holds a real item
   float tmx[4][32];                     // per-head tile max of each wavefront
   __attribute__((aligned(16))) int bump[4];   // wavefront wants to move its reference max
@@ -490,14 +490,6 @@ struct MxShared {
   float rope_cs[kR];                    // (cos, sin) of t * theta_p, p < R/2
   __attribute__((aligned(16))) float gain[kD];   // query RMSNorm gain
 };
-
-// Item j of a row as a 16-byte-unit offset (kNoItem: skip it).
-__device__ __forceinline__ uint32_t item_off(const AttendArgs& a, const RowInfo& ri, int r, int j) {
-  bool w;
-  const uint8_t* p = item_ptr(a, ri, r, j, &w);
-  if (p == nullptr) return kNoItem;
-  return w ? kWinFlag | (uint32_t)((p - (const uint8_t*)a.win) >> 4) : (uint32_t)((p - a.kv.pool) >> 4);
-}
 
 // Item table of a unit: items j0 .. j0 + n_tab - 1 as item_off gives them, built
 // in groups of kTabGroup items per thread, in phases, so that the dependent loads
@@ -551,10 +543,10 @@ __device__ __forceinline__ void mx_item_table(const AttendArgs& a, const RowInfo
           const int32_t p = pg[k];
           off = (p < 0 || p >= a.kv.n_pages)
                     ? kNoItem
-                    : (uint32_t)(((int64_t)p * a.kv.page_bytes + (int64_t)a.kv.slot_of(e[k]) * a.kv.stride) >> 4);
+                    : (uint32_t)(((int64_t)p << a.kv.page_shift) | a.kv.slot_of(e[k]));
         } else {
           const int w = ri.w0 + (j - ri.n_c);
-          off = kWinFlag | (uint32_t)((((int64_t)ri.win_seq * a.W + w % a.W) * kD * 2) >> 4);
+          off = kWinFlag | (uint32_t)((int64_t)ri.win_seq * a.W + w % a.W);
         }
         items[i] = off;
       }
@@ -562,9 +554,14 @@ __device__ __forceinline__ void mx_item_table(const AttendArgs& a, const RowInfo
   }
 }
 
+// Source of an item-table entry: record `off` of the pool in page order (page off >> shift,
+// slot off & (page size - 1)), or row off & ~kWinFlag of the bf16 window.  The host keeps
+// n_pages * page size and the window's rows below 2^31 - 1, so the flag bit and kNoItem
+// never collide with a real item.
 __device__ __forceinline__ const uint8_t* item_src(const AttendArgs& a, uint32_t off) {
-  return (off & kWinFlag) ? (const uint8_t*)a.win + ((uint64_t)(off & ~kWinFlag) << 4)
-                          : (const uint8_t*)a.kv.pool + ((uint64_t)off << 4);
+  return (off & kWinFlag) ? (const uint8_t*)a.win + (uint64_t)(off & ~kWinFlag) * (kD * 2)
+                          : (const uint8_t*)a.kv.pool + (uint64_t)(off >> a.kv.page_shift) * a.kv.page_bytes +
+                                (uint64_t)(off & ((1u << a.kv.page_shift) - 1u)) * a.kv.stride;
 }
 
 // One async global -> LDS load of 16 B per lane (lane l: g + 16 l -> LDS d + 16 l),

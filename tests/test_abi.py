@@ -254,3 +254,22 @@ def test_sublayer_projection_arguments_need_no_device():
     assert lib.ca_query_proj_workspace(ctypes.byref(qp), 8) > 0       # h W^DQ: 13 output tiles at T = 8
     assert lib.ca_out_proj_workspace(ctypes.byref(op), 8) > 0
     assert lib.ca_query_proj_workspace(None, 8) == 0
+
+
+def test_attention_rejects_pools_and_windows_beyond_31_bit_item_indices():
+    """Attention items are addressed by pool record index or window row in 31 bits: a pool of
+    2^31 - 1 or more records, or a decode window of 2^31 - 1 or more rows, is refused on the
+    host before any launch (fake, never dereferenced addresses)."""
+    from long_context_attention_17_amd import binding as ca
+    lib = ca.lib()
+    fake = 1 << 20
+    p = ca.AttendParams(64, 512, 64, 128, ca.BF16, ca.BF16, ca.BF16, 512 ** -0.5, 1e-6, 1e4, None)
+
+    def hca_decode(n_pages, W, B=1):
+        c = ca._Cache(ca.FP8MIX, 512, 64, 64, fake, n_pages, fake, B, 16)
+        return lib.ca_hca_attend_decode(ctypes.byref(p), fake, fake, ctypes.byref(c), 128, fake, B, 1024, fake, W,
+                                        fake, fake, None, fake, 1 << 30, None)
+
+    big = (1 << 31) // 64                           # pages of 64 records: 2^31 records
+    assert hca_decode(big, 128) == -3 and "records" in lib.ca_last_error().decode()
+    assert hca_decode(big - 1, (1 << 31) // 8, B=8) == -3 and "window" in lib.ca_last_error().decode()
