@@ -186,6 +186,21 @@ __device__ __forceinline__ void load_key_group(const CacheView& cv, const int* p
 // when the row has more than hist_k keys, the workgroup adds the histogram of its
 // chunk's scores (top 12 bits of the order-preserving keys) to it, from an LDS
 // histogram in dynamic shared memory (kHistBins words).
+// A chunk's LDS histogram hb[4096] (complete: after a barrier) into the row's state g:
+// the nonzero fine bins, and the 64 coarse bins (fine bins 64c .. 64c + 63 summed) that
+// follow the state's 4 counters.  256 threads; integer adds, so order free.
+__device__ __forceinline__ void add_row_histogram(const uint32_t* hb, uint32_t* g) {
+  for (int i = threadIdx.x; i < 4096; i += 256) {
+    const uint32_t c = hb[i];
+    if (c) atomicAdd(&g[i], c);
+  }
+  if (threadIdx.x < 64) {
+    uint32_t c = 0;
+    for (int i = 0; i < 64; ++i) c += hb[64 * threadIdx.x + ((i + threadIdx.x) & 63)];   // staggered: no bank clash
+    if (c) atomicAdd(&g[4096 + 4 + threadIdx.x], c);
+  }
+}
+
 template <int QPW, int KF, int QF>
 __device__ __forceinline__ void index_scores_mfma(CacheView cv, int m, int q_fmt, const void* qI, const float* w,
                                                   RowPos pos, int seq_fixed, int n_rows, float* scores,
@@ -336,10 +351,7 @@ __device__ __forceinline__ void index_scores_mfma(CacheView cv, int m, int q_fmt
   if (want_hist) {   // the chunk's nonzero bins into the row's histogram (integer adds: order free)
     __syncthreads();
     uint32_t* g = hist + (int64_t)r0 * hist_words;
-    for (int i = threadIdx.x; i < kHistBins; i += 256) {
-      const uint32_t c = hs[i];
-      if (c) atomicAdd(&g[i], c);
-    }
+    add_row_histogram(hs, g);
   }
 }
 
@@ -501,7 +513,8 @@ constexpr int kChunk = 4096;
 constexpr int kResolveThreads = 1024;
 constexpr int kSortMax = 8192;        // largest k of the long path
 constexpr int kMetaWords = 4;         // per row: candidates appended, (spare), b*, keys above b*
-constexpr int kRowWords = kHistBins + kMetaWords;   // per-row state: histogram, then the counters
+constexpr int kCoarseBins = 64;       // coarse histogram: the top 6 key bits
+constexpr int kRowWords = kHistBins + kMetaWords + kCoarseBins;   // per-row state: histogram, counters, coarse
 static_assert(kRowWords == kTopkRowWords, "per-row long top-k state size");
 constexpr int kRegCand = 4;            // candidates per resolve thread held in registers
 constexpr int kBitmapLdsWords = 16384;  // two LDS bitmaps of rows up to 262,144 keys (larger rows: workspace)
@@ -515,53 +528,6 @@ __device__ __forceinline__ int64_t row_len(RowPos pos, int r, int m, int64_t str
   int t = pos(r);
   int64_t n = t / m;
   return n < stride ? n : stride;
-}
-
-// Bin of a 256-thread block's histogram hb[kHistBins] (in LDS) holding the k-th
-// largest key, and the number of keys in higher bins: each thread sums 16 bins,
-// wave 0 finds the thread whose bins hold the k-th key by a suffix scan, and that
-// thread walks its 16 bins from the top.
-__device__ void threshold_bin(const uint32_t* hb, int k, uint32_t* part, uint32_t* bin, uint32_t* above) {
-  __shared__ uint32_t sel_owner, sel_above, sel_bin, sel_cum;
-  const int tid = threadIdx.x;
-  uint32_t sum = 0;
-  for (int i = 0; i < 16; ++i) sum += hb[16 * tid + i];
-  part[tid] = sum;
-  __syncthreads();
-  if (tid < 64) {
-    // lane L owns threads 4L..4L+3; suffix sums from the top thread down
-    uint32_t c[4] = {part[4 * tid], part[4 * tid + 1], part[4 * tid + 2], part[4 * tid + 3]};
-    uint32_t lsum = c[0] + c[1] + c[2] + c[3];
-    uint32_t incl = lsum;
-    for (int o = 1; o < 64; o <<= 1) {
-      uint32_t v = __shfl_down(incl, o, 64);
-      if (tid + o < 64) incl += v;
-    }
-    uint32_t cum = incl - lsum;
-    for (int d = 3; d >= 0; --d) {
-      uint32_t nxt = cum + c[d];
-      if (cum < (uint32_t)k && nxt >= (uint32_t)k) {
-        sel_owner = 4 * tid + d;
-        sel_above = cum;
-      }
-      cum = nxt;
-    }
-  }
-  __syncthreads();
-  if (tid == (int)sel_owner) {
-    uint32_t cum = sel_above;
-    for (int b = 16 * tid + 15; b >= 16 * tid; --b) {
-      if (cum + hb[b] >= (uint32_t)k) {
-        sel_bin = (uint32_t)b;
-        sel_cum = cum;
-        break;
-      }
-      cum += hb[b];
-    }
-  }
-  __syncthreads();
-  *bin = sel_bin;
-  *above = sel_cum;
 }
 
 __global__ void __launch_bounds__(256) topk_hist_kernel(const float* scores, int64_t stride, RowPos pos,
@@ -578,17 +544,30 @@ __global__ void __launch_bounds__(256) topk_hist_kernel(const float* scores, int
   for (int64_t s = c0 + tid; s < c1; s += blockDim.x) atomicAdd(&h[order_key(row[s]) >> 20], 1u);
   __syncthreads();
   uint32_t* g = state + (int64_t)r * kRowWords;
-  for (int i = tid; i < kHistBins; i += blockDim.x)
-    if (h[i]) atomicAdd(&g[i], h[i]);
+  add_row_histogram(h, g);
+}
+
+// Wavefront helper: lane l holds the count of bin l (bin 63 the highest keys).  Returns,
+// in every lane, the bin holding the need-th largest key (need >= 1, at most the total)
+// and the count of keys in the bins above it.
+__device__ __forceinline__ void top_bin_of_64(uint32_t c, uint32_t need, uint32_t* bin, uint32_t* above) {
+  const int lane = threadIdx.x & 63;
+  uint32_t incl = c;                                   // suffix sum: keys in bins >= lane
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t v = __shfl_down(incl, o, 64);
+    if (lane + o < 64) incl += v;
+  }
+  const uint64_t ge = __ballot(incl >= need);          // bins 0 .. b hold at least `need` keys at or above
+  const int b = 63 - __builtin_clzll(ge);
+  *bin = (uint32_t)b;
+  *above = __shfl(incl - c, b, 64);
 }
 
 __global__ void __launch_bounds__(256) topk_gather_kernel(const float* scores, int64_t stride, RowPos pos,
                                                           int m, int k, uint32_t* state, uint32_t* cand_key,
                                                           uint32_t* cand_idx) {
   __shared__ uint32_t part[4];
-  __shared__ uint32_t base_s;
-  __shared__ uint32_t hb[kHistBins];
-  __shared__ uint32_t hpart[256];
+  __shared__ uint32_t base_s, bstar_s;
   const int r = blockIdx.x, tid = threadIdx.x;
   const int64_t n = row_len(pos, r, m, stride);
   const int64_t c0 = (int64_t)blockIdx.y * kChunk;
@@ -605,17 +584,26 @@ __global__ void __launch_bounds__(256) topk_gather_kernel(const float* scores, i
     const int64_t s = s0 + i;
     keys[i] = s < n ? order_key(row[s]) : 0u;
   }
-  // the threshold bin b* of the row, from its histogram (every workgroup of the row
-  // finds the same one; the first also records it, and the count of keys above it,
-  // for the resolve launch)
-  for (int i = tid; i < kHistBins; i += 256) hb[i] = g[i];
-  __syncthreads();
-  uint32_t bstar, above;
-  threshold_bin(hb, k, hpart, &bstar, &above);
-  if (blockIdx.y == 0 && tid == 0) {
-    meta[2] = bstar;
-    meta[3] = above;
+  // the threshold bin b* of the row (every workgroup of the row finds the same one; the
+  // first also records it, and the count of keys above it, for the resolve launch):
+  // wavefront 0 finds the coarse bin holding the k-th largest key from the 64 coarse
+  // bins, then b* among that coarse bin's 64 fine bins
+  if (tid < 64) {
+    const uint32_t* coarse = meta + kMetaWords;
+    uint32_t cbin, above_c;
+    top_bin_of_64(coarse[tid], (uint32_t)k, &cbin, &above_c);
+    uint32_t fbin, above_f;
+    top_bin_of_64(g[64 * cbin + tid], (uint32_t)k - above_c, &fbin, &above_f);
+    if (tid == 0) {
+      bstar_s = 64 * cbin + fbin;
+      if (blockIdx.y == 0) {
+        meta[2] = 64 * cbin + fbin;
+        meta[3] = above_c + above_f;
+      }
+    }
   }
+  __syncthreads();
+  const uint32_t bstar = bstar_s;
   uint32_t mine = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) mine += (s0 + i < n && (keys[i] >> 20) >= bstar) ? 1u : 0u;

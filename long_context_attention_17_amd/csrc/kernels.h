@@ -68,7 +68,7 @@ struct RowPos {
 // Scores of every eligible block.  With ws_long (the multi-workgroup top-k state,
 // used when the rows are long) the per-row key histograms are also cleared (unless
 // state_zeroed: the caller cleared the kTopkRowWords words per row already) and filled.
-constexpr int kTopkRowWords = 4096 + 4;   // per-row long top-k state: histogram bins, then 4 counters
+constexpr int kTopkRowWords = 4096 + 4 + 64;   // per-row long top-k state: histogram bins, 4 counters, 64 coarse bins
 hipError_t launch_index_scores(const CacheView& cv, const ca_index_params& p, const void* qI, const float* w,
                                RowPos pos, int seq_fixed, int n_rows, int64_t max_pos, float* scores,
                                int64_t stride, void* ws_long, hipStream_t st, bool state_zeroed = false);
