@@ -694,17 +694,23 @@ __global__ void __launch_bounds__(kResolveThreads) topk_resolve_kernel(const flo
     return;
   }
   const uint32_t* meta = state + (int64_t)r * kRowWords + kHistBins;
-  const uint32_t nc = meta[0], bstar = meta[2], above = meta[3];
   const uint32_t* gk = cand_key + (int64_t)r * stride;
   const uint32_t* gi = cand_idx + (int64_t)r * stride;
-  // the first kRegCand * kResolveThreads candidates stay in registers for all three passes over them
+  // the first kRegCand * kResolveThreads candidate slots go into registers (kept for all
+  // three passes over them) in the same round trip as the row's counters: the slots lie
+  // inside the row's candidate arrays (stride > kTopkLdsKeys > kRegCand * kResolveThreads),
+  // and those at or past the candidate count are masked once it is known
+  static_assert(kRegCand * kResolveThreads <= kTopkLdsKeys, "speculative candidate slots inside the row");
   uint32_t rk[kRegCand], ri[kRegCand];
 #pragma unroll
   for (int j = 0; j < kRegCand; ++j) {
-    const uint32_t i = tid + j * kResolveThreads;
-    rk[j] = i < nc ? gk[i] : 0u;
-    ri[j] = i < nc ? gi[i] : 0u;
+    rk[j] = gk[tid + j * kResolveThreads];
+    ri[j] = gi[tid + j * kResolveThreads];
   }
+  const uint32_t nc = meta[0], bstar = meta[2], above = meta[3];
+#pragma unroll
+  for (int j = 0; j < kRegCand; ++j)
+    if (tid + j * kResolveThreads >= nc) rk[j] = ri[j] = 0u;
   // two 10-bit radix passes over the candidates in bin b*: T and the count to take equal to T
   uint32_t need = (uint32_t)k - above, prefix = bstar;
   for (int pass = 0; pass < 2; ++pass) {
