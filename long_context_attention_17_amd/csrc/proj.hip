@@ -16,45 +16,45 @@ namespace ca {
 
 namespace {
 
-constexpr int kGK = 64, kGP = kGK + 8;               // K tile, LDS row pitch (bf16; 144 B rows)
 constexpr int kGroupM = 8;                           // M tiles per group of the tile order
 
-// Workgroup tile MT x 128 (4 wavefronts), one K tile of register prefetch:
-//   32 x 128 for decode-sized M: wavefronts side by side along N (32 x 32 each);
+// Workgroup tile MT x 128 (4 wavefronts), one K tile of register prefetch (M <= 32 runs
+// gemm_skinny_kernel below instead):
 //   128 x 128: wavefronts 2 x 2 of 64 x 64, two workgroups per CU (one's barrier and LDS
 //     stores overlap the other's MFMAs; a 256-row tile at one workgroup per CU measured slower).
-template <int MT, int NT>
+template <int MT, int NT, int KT>
 struct GemmShape {
+  static constexpr int kP = KT + 8;                                   // LDS row pitch (bf16)
   static constexpr int kWavesM = MT >= 128 ? 2 : 1, kWavesN = 4 / kWavesM;
   static constexpr int kWM = MT / kWavesM, kWN = NT / kWavesN;       // one wavefront's tile
   static constexpr int kBM = kWM / 32, kBN = kWN / 32;                // 32x32 MFMA blocks per wavefront
-  static constexpr int kAChunks = MT * kGK / 8 / 256;                 // 16-byte loads per thread
-  static constexpr int kWChunks = NT * kGK / 8 / 256;
+  static constexpr int kAChunks = MT * KT / 8 / 256;                  // 16-byte loads per thread
+  static constexpr int kWChunks = NT * KT / 8 / 256;
   static constexpr int kPF = 1;
   static constexpr int kCPitch = NT + 8;                              // bf16 output staging row pitch
 };
 
-// Rows row0 .. row0 + rows - 1 of a K-contiguous operand, columns k0 .. k0 + 63, into
-// registers: chunk i = threadIdx.x + 256 j is row i / 8, columns 8 (i % 8) .. +7.  Rows past
-// max_row re-read the last row (their products land in rows / columns never stored).
-template <int NCH>
+// Rows row0 .. of a K-contiguous operand, columns k0 .. k0 + KT - 1, into registers:
+// chunk i = threadIdx.x + 256 j is row i / (KT / 8), columns 8 (i % (KT / 8)) .. +7.  Rows
+// past max_row re-read the last row (their products land in rows / columns never stored).
+template <int NCH, int KT>
 __device__ __forceinline__ void tile_load(const uint16_t* base, int64_t ld, int row0, int max_row, int k0,
                                           u32x4* regs) {
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
     const int i = threadIdx.x + 256 * j;
-    int r = row0 + i / 8;
+    int r = row0 + i / (KT / 8);
     r = r < max_row ? r : max_row - 1;
-    regs[j] = *(const u32x4*)(base + (int64_t)r * ld + k0 + 8 * (i % 8));
+    regs[j] = *(const u32x4*)(base + (int64_t)r * ld + k0 + 8 * (i % (KT / 8)));
   }
 }
 
-template <int NCH>
+template <int NCH, int KT>
 __device__ __forceinline__ void tile_store(uint16_t* lds, const u32x4* regs) {
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
     const int i = threadIdx.x + 256 * j;
-    *(u32x4*)(lds + (i / 8) * kGP + 8 * (i % 8)) = regs[j];
+    *(u32x4*)(lds + (i / (KT / 8)) * (KT + 8) + 8 * (i % (KT / 8))) = regs[j];
   }
 }
 
@@ -84,11 +84,11 @@ __device__ __forceinline__ bool tile_of(const GemmArgs& g, TileCoord& t) {
   return true;
 }
 
-template <int MT, int NT>
+template <int MT, int NT, int KT>
 __global__ void __launch_bounds__(256) gemm_nt_kernel(GemmArgs g) {
-  using S = GemmShape<MT, NT>;
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][MT * kGP];
-  __shared__ __attribute__((aligned(16))) uint16_t Ws[2][NT * kGP];
+  using S = GemmShape<MT, NT, KT>;
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][MT * S::kP];
+  __shared__ __attribute__((aligned(16))) uint16_t Ws[2][NT * S::kP];
   TileCoord tc;
   if (!tile_of(g, tc)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -110,23 +110,23 @@ __global__ void __launch_bounds__(256) gemm_nt_kernel(GemmArgs g) {
   // register stages of the K tiles in flight (PF of them)
   u32x4 ra[S::kPF][S::kAChunks], rw[S::kPF][S::kWChunks];
   auto load = [&](int p, int i) {
-    tile_load<S::kAChunks>(A, g.lda, m0, g.M, (kt0 + i) * kGK, ra[p]);
-    tile_load<S::kWChunks>(W, seg.ldw, n0, seg.N, (kt0 + i) * kGK, rw[p]);
+    tile_load<S::kAChunks, KT>(A, g.lda, m0, g.M, (kt0 + i) * KT, ra[p]);
+    tile_load<S::kWChunks, KT>(W, seg.ldw, n0, seg.N, (kt0 + i) * KT, rw[p]);
   };
   auto store = [&](int p, int buf) {
-    tile_store<S::kAChunks>(As[buf], ra[p]);
-    tile_store<S::kWChunks>(Ws[buf], rw[p]);
+    tile_store<S::kAChunks, KT>(As[buf], ra[p]);
+    tile_store<S::kWChunks, KT>(Ws[buf], rw[p]);
   };
   auto mfmas = [&](int buf) {
-    const uint16_t* as = As[buf] + (wm * S::kWM + (lane & 31)) * kGP + 8 * (lane >> 5);
-    const uint16_t* ws = Ws[buf] + (wn * S::kWN + (lane & 31)) * kGP + 8 * (lane >> 5);
+    const uint16_t* as = As[buf] + (wm * S::kWM + (lane & 31)) * S::kP + 8 * (lane >> 5);
+    const uint16_t* ws = Ws[buf] + (wn * S::kWN + (lane & 31)) * S::kP + 8 * (lane >> 5);
 #pragma unroll
-    for (int kk = 0; kk < kGK; kk += 16) {
+    for (int kk = 0; kk < KT; kk += 16) {
       bf16x8 af[S::kBM], wf[S::kBN];
 #pragma unroll
-      for (int i = 0; i < S::kBM; ++i) af[i] = *(const bf16x8*)(as + 32 * i * kGP + kk);
+      for (int i = 0; i < S::kBM; ++i) af[i] = *(const bf16x8*)(as + 32 * i * S::kP + kk);
 #pragma unroll
-      for (int j = 0; j < S::kBN; ++j) wf[j] = *(const bf16x8*)(ws + 32 * j * kGP + kk);
+      for (int j = 0; j < S::kBN; ++j) wf[j] = *(const bf16x8*)(ws + 32 * j * S::kP + kk);
 #pragma unroll
       for (int i = 0; i < S::kBM; ++i)
 #pragma unroll
@@ -161,7 +161,7 @@ __global__ void __launch_bounds__(256) gemm_nt_kernel(GemmArgs g) {
   if (g.k_splits == 1 && !seg.c_f32) {
     // bf16 output: the tile goes through LDS (free after the last barrier) so that the global
     // stores are 16-byte runs along the rows of C
-    static_assert(S::kCPitch <= 2 * kGP, "output staging fits the A operand buffers");
+    static_assert(S::kCPitch <= 2 * S::kP, "output staging fits the A operand buffers");
     uint16_t* ct = &As[0][0];
 #pragma unroll
     for (int i2 = 0; i2 < S::kBM; ++i2)
@@ -209,6 +209,84 @@ __global__ void __launch_bounds__(256) gemm_nt_kernel(GemmArgs g) {
     }
 }
 
+// Decode-sized M (<= 32 MB): no LDS and no barriers.  Wavefront w of the workgroup owns output
+// columns n0 + 32 w .. +31 (MB 32 x 32 MFMA blocks, one per 32 rows; each W fragment feeds
+// all of them) and reads its operands straight from
+// global memory in the MFMA lane layout, a K group of 64 at a time: lane l holds row / column
+// l % 32 and the 32 contiguous elements 32 (l / 32) .. +31 of the group (64 bytes), which
+// feed four MFMAs (step s takes elements 8 s .. 8 s + 7 of each half: the same permutation of
+// K on both operands).  PF groups stay in flight per wavefront, so the weights stream with
+// many bytes outstanding per CU.
+template <int PF, int MB>
+__global__ void __launch_bounds__(256) gemm_skinny_kernel(GemmArgs g) {
+  TileCoord tc;
+  if (!tile_of(g, tc)) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sg = tc.n_tile >= g.seg[0].n_tiles ? 1 : 0;
+  const GemmSeg& seg = g.seg[sg];
+  const int n0 = (tc.n_tile - (sg ? g.seg[0].n_tiles : 0)) * 128 + 32 * wave;
+  if (n0 >= seg.N) return;                               // (wavefront-uniform; no barriers follow)
+  const int kg0 = (int)((int64_t)tc.s * g.k_tiles / g.k_splits);   // K groups of 64
+  const int n_kg = (int)((int64_t)(tc.s + 1) * g.k_tiles / g.k_splits) - kg0;
+  const int nr = min(n0 + (lane & 31), seg.N - 1);
+  const uint16_t* wrow = (const uint16_t*)seg.W + tc.b * seg.w_batch + (int64_t)nr * seg.ldw + 32 * (lane >> 5) +
+                         (int64_t)kg0 * 64;
+  const uint16_t* arow[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+    arow[mb] = (const uint16_t*)g.A + tc.b * g.a_batch + (int64_t)min(32 * mb + (lane & 31), g.M - 1) * g.lda +
+               32 * (lane >> 5) + (int64_t)kg0 * 64;
+  u32x4 wv[PF][4], av[PF][MB][4];
+  auto load = [&](int p, int i) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      wv[p][q] = *(const u32x4*)(wrow + (int64_t)i * 64 + 8 * q);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) av[p][mb][q] = *(const u32x4*)(arow[mb] + (int64_t)i * 64 + 8 * q);
+    }
+  };
+  f32x16 acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x16{};
+#pragma unroll
+  for (int p = 0; p < PF; ++p)
+    if (p < n_kg) load(p, p);
+  // group i sits in register stage i % PF (a constant in each unrolled copy)
+  auto step = [&](int i, int c) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[c][mb][q]),
+                                                          __builtin_bit_cast(bf16x8, wv[c][q]), acc[mb], 0, 0, 0);
+    if (i + PF < n_kg) load(c, i + PF);
+  };
+  int i = 0;
+  for (; i + PF <= n_kg; i += PF)
+#pragma unroll
+    for (int c = 0; c < PF; ++c) step(i + c, c);
+#pragma unroll
+  for (int c = 0; c < PF; ++c)
+    if (i + c < n_kg) step(i + c, c);
+  // acc[mb] element v of lane l: row 32 mb + 8 (v / 4) + 4 (l / 32) + v % 4, column n0 + l % 32
+  const int n = n0 + (lane & 31);
+  if (n >= seg.N) return;
+  const int64_t part_base = seg.part_off + ((int64_t)tc.s * g.batch + tc.b) * g.M * seg.N;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const f32x16 blk = acc[mb];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int m = 32 * mb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      if (m < g.M) {
+        if (g.k_splits > 1) g.part[part_base + (int64_t)m * seg.N + n] = blk[v];
+        else if (seg.c_f32) ((float*)seg.C)[tc.b * seg.c_batch + (int64_t)m * seg.ldc + n] = blk[v];
+        else ((uint16_t*)seg.C)[tc.b * seg.c_batch + (int64_t)m * seg.ldc + n] = f32_to_bf16_bits(blk[v]);
+      }
+    }
+  }
+}
+
 // C_b[m, n] = sum_s part[s][b][m][n], the splits added in order; both segments.
 __global__ void __launch_bounds__(256) gemm_reduce_kernel(GemmArgs g) {
   int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -230,26 +308,33 @@ __global__ void __launch_bounds__(256) gemm_reduce_kernel(GemmArgs g) {
   else ((uint16_t*)seg.C)[o] = f32_to_bf16_bits(v);
 }
 
-// Tile rows by M: 32 for decode-sized M, else 128.
-int m_tile_of(int M) { return M <= 32 ? 32 : 128; }
-int n_tile_of(int) { return 128; }
+struct TileShape {
+  int mt, nt, kt;
+};
+// Tile shape: M <= 32 runs gemm_skinny_kernel (32 rows, 128 columns, K groups of 64), larger
+// M the 128 x 128 x 64 tiles (a 64-row skinny variant measured slower at 64 rows: 1.97 vs
+// 2.26 TB/s of weights).
+constexpr int kSkinnyPF = 2;
+TileShape shape_of(int M) { return M <= 32 ? TileShape{32, 128, 64} : TileShape{128, 128, 64}; }
 
 }  // namespace
 
 void gemm_plan(GemmArgs& g) {
-  const int mt = m_tile_of(g.M), nt = n_tile_of(g.M);
+  const TileShape sh = shape_of(g.M);
+  const int mt = sh.mt, nt = sh.nt;
   g.m_tiles = (g.M + mt - 1) / mt;
   g.n_tiles = 0;
   for (int s = 0; s < 2; ++s) {
     g.seg[s].n_tiles = s < g.n_seg ? (g.seg[s].N + nt - 1) / nt : 0;
     g.n_tiles += g.seg[s].n_tiles;
   }
-  g.k_tiles = g.K / kGK;
+  g.k_tiles = g.K / sh.kt;
   const int64_t tiles = (int64_t)g.m_tiles * g.n_tiles * g.batch;
-  // K splits until the launch has ~1,000 workgroups (four per CU), each split keeping at
-  // least 4 K tiles
+  // K splits until the launch has ~1,000 workgroups (four per CU; decode-sized M: ~512, as
+  // each streams its weights with many loads in flight and fewer splits write fewer
+  // partials), each split keeping at least 256 of K
   int s = 1;
-  while (tiles * s < 1024 && 2 * s * 4 <= g.k_tiles && s < 32) s *= 2;
+  while (tiles * s < (mt == 32 ? 512 : 1024) && 2 * s * 256 <= g.k_tiles * sh.kt && s < 32) s *= 2;
   g.k_splits = s;
   int64_t off = 0;
   for (int q = 0; q < g.n_seg; ++q) {
@@ -270,8 +355,8 @@ hipError_t launch_gemm(GemmArgs g, hipStream_t st) {
   hipEvent_t ev0, ev1;
   timer_events(CA_TIMED_PROJ_GEMM, st, &ev0, &ev1);
   const dim3 grid((unsigned)g.grid_blocks);
-  if (m_tile_of(g.M) == 32) CA_LAUNCH((gemm_nt_kernel<32, 128>), grid, dim3(256), 0, st, ev0, ev1, g);
-  else CA_LAUNCH((gemm_nt_kernel<128, 128>), grid, dim3(256), 0, st, ev0, ev1, g);
+  if (g.M <= 32) CA_LAUNCH((gemm_skinny_kernel<kSkinnyPF, 1>), grid, dim3(256), 0, st, ev0, ev1, g);
+  else CA_LAUNCH((gemm_nt_kernel<128, 128, 64>), grid, dim3(256), 0, st, ev0, ev1, g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || g.k_splits == 1) return e;
   int64_t n = 0;
