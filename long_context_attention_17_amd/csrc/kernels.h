@@ -185,6 +185,7 @@ struct GemmArgs {
   GemmSeg seg[2];
   float* part;
   // set by gemm_plan
+  int tile_m, tile_n;   // workgroup tile: 32 x 128, 128 x 128 or 256 x 256
   int m_tiles, n_tiles, k_tiles, k_splits;
   int64_t part_floats, grid_blocks;
 };

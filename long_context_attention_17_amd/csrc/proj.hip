@@ -18,18 +18,22 @@ namespace {
 
 constexpr int kGroupM = 8;                           // M tiles per group of the tile order
 
-// Workgroup tile MT x 128 (4 wavefronts), one K tile of register prefetch (M <= 32 runs
+// Workgroup tile MT x NT of WAVES wavefronts, one K tile of register prefetch (M <= 32 runs
 // gemm_skinny_kernel below instead):
-//   128 x 128: wavefronts 2 x 2 of 64 x 64, two workgroups per CU (one's barrier and LDS
-//     stores overlap the other's MFMAs; a 256-row tile at one workgroup per CU measured slower).
-template <int MT, int NT, int KT>
+//   128 x 128, 4 wavefronts (2 x 2 of 64 x 64): two workgroups per CU, one's barrier and LDS
+//     stores overlapping the other's MFMAs;
+//   256 x 256, 8 wavefronts (2 x 4 of 128 x 64): one workgroup per CU, two wavefronts per
+//     SIMD; each A fragment read from LDS feeds two MFMAs and each W fragment four.
+//   (256 x 128 with 4 wavefronts, one per SIMD, measured slower: 420 vs 727 TF/s.)
+template <int MT, int NT, int KT, int WAVES = 4>
 struct GemmShape {
+  static constexpr int kThreads = 64 * WAVES;
   static constexpr int kP = KT + 8;                                   // LDS row pitch (bf16)
-  static constexpr int kWavesM = MT >= 128 ? 2 : 1, kWavesN = 4 / kWavesM;
+  static constexpr int kWavesM = MT >= 128 ? 2 : 1, kWavesN = WAVES / kWavesM;
   static constexpr int kWM = MT / kWavesM, kWN = NT / kWavesN;       // one wavefront's tile
   static constexpr int kBM = kWM / 32, kBN = kWN / 32;                // 32x32 MFMA blocks per wavefront
-  static constexpr int kAChunks = MT * KT / 8 / 256;                  // 16-byte loads per thread
-  static constexpr int kWChunks = NT * KT / 8 / 256;
+  static constexpr int kAChunks = MT * KT / 8 / kThreads;             // 16-byte loads per thread
+  static constexpr int kWChunks = NT * KT / 8 / kThreads;
   static constexpr int kPF = 1;
   static constexpr int kCPitch = NT + 8;                              // bf16 output staging row pitch
 };
@@ -37,23 +41,23 @@ struct GemmShape {
 // Rows row0 .. of a K-contiguous operand, columns k0 .. k0 + KT - 1, into registers:
 // chunk i = threadIdx.x + 256 j is row i / (KT / 8), columns 8 (i % (KT / 8)) .. +7.  Rows
 // past max_row re-read the last row (their products land in rows / columns never stored).
-template <int NCH, int KT>
+template <int NCH, int KT, int NT_ = 256>
 __device__ __forceinline__ void tile_load(const uint16_t* base, int64_t ld, int row0, int max_row, int k0,
                                           u32x4* regs) {
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
-    const int i = threadIdx.x + 256 * j;
+    const int i = threadIdx.x + NT_ * j;
     int r = row0 + i / (KT / 8);
     r = r < max_row ? r : max_row - 1;
     regs[j] = *(const u32x4*)(base + (int64_t)r * ld + k0 + 8 * (i % (KT / 8)));
   }
 }
 
-template <int NCH, int KT>
+template <int NCH, int KT, int NT_ = 256>
 __device__ __forceinline__ void tile_store(uint16_t* lds, const u32x4* regs) {
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
-    const int i = threadIdx.x + 256 * j;
+    const int i = threadIdx.x + NT_ * j;
     *(u32x4*)(lds + (i / (KT / 8)) * (KT + 8) + 8 * (i % (KT / 8))) = regs[j];
   }
 }
@@ -84,11 +88,12 @@ __device__ __forceinline__ bool tile_of(const GemmArgs& g, TileCoord& t) {
   return true;
 }
 
-template <int MT, int NT, int KT>
-__global__ void __launch_bounds__(256) gemm_nt_kernel(GemmArgs g) {
-  using S = GemmShape<MT, NT, KT>;
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][MT * S::kP];
-  __shared__ __attribute__((aligned(16))) uint16_t Ws[2][NT * S::kP];
+template <int MT, int NT, int KT, int WAVES>
+__global__ void __launch_bounds__(64 * WAVES) gemm_nt_kernel(GemmArgs g) {
+  using S = GemmShape<MT, NT, KT, WAVES>;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (MT + NT) * S::kP];
+  uint16_t* As[2] = {smem, smem + MT * S::kP};                    // A tiles, then W tiles
+  uint16_t* Ws[2] = {smem + 2 * MT * S::kP, smem + (2 * MT + NT) * S::kP};
   TileCoord tc;
   if (!tile_of(g, tc)) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -110,12 +115,12 @@ __global__ void __launch_bounds__(256) gemm_nt_kernel(GemmArgs g) {
   // register stages of the K tiles in flight (PF of them)
   u32x4 ra[S::kPF][S::kAChunks], rw[S::kPF][S::kWChunks];
   auto load = [&](int p, int i) {
-    tile_load<S::kAChunks, KT>(A, g.lda, m0, g.M, (kt0 + i) * KT, ra[p]);
-    tile_load<S::kWChunks, KT>(W, seg.ldw, n0, seg.N, (kt0 + i) * KT, rw[p]);
+    tile_load<S::kAChunks, KT, S::kThreads>(A, g.lda, m0, g.M, (kt0 + i) * KT, ra[p]);
+    tile_load<S::kWChunks, KT, S::kThreads>(W, seg.ldw, n0, seg.N, (kt0 + i) * KT, rw[p]);
   };
   auto store = [&](int p, int buf) {
-    tile_store<S::kAChunks, KT>(As[buf], ra[p]);
-    tile_store<S::kWChunks, KT>(Ws[buf], rw[p]);
+    tile_store<S::kAChunks, KT, S::kThreads>(As[buf], ra[p]);
+    tile_store<S::kWChunks, KT, S::kThreads>(Ws[buf], rw[p]);
   };
   auto mfmas = [&](int buf) {
     const uint16_t* as = As[buf] + (wm * S::kWM + (lane & 31)) * S::kP + 8 * (lane >> 5);
@@ -161,8 +166,8 @@ __global__ void __launch_bounds__(256) gemm_nt_kernel(GemmArgs g) {
   if (g.k_splits == 1 && !seg.c_f32) {
     // bf16 output: the tile goes through LDS (free after the last barrier) so that the global
     // stores are 16-byte runs along the rows of C
-    static_assert(S::kCPitch <= 2 * S::kP, "output staging fits the A operand buffers");
-    uint16_t* ct = &As[0][0];
+    static_assert(MT * S::kCPitch <= 2 * (MT + NT) * S::kP, "output staging fits the operand buffers");
+    uint16_t* ct = smem;
 #pragma unroll
     for (int i2 = 0; i2 < S::kBM; ++i2)
 #pragma unroll
@@ -177,8 +182,8 @@ __global__ void __launch_bounds__(256) gemm_nt_kernel(GemmArgs g) {
     const bool vec = ((seg.ldc | tc.b * seg.c_batch) & 7) == 0 && ((uintptr_t)seg.C & 15) == 0;
     constexpr int kChunksRow = NT / 8;
 #pragma unroll
-    for (int p = 0; p < MT * kChunksRow / 256; ++p) {
-      const int q = threadIdx.x + 256 * p, r = q / kChunksRow, c = 8 * (q % kChunksRow);
+    for (int p = 0; p < MT * kChunksRow / S::kThreads; ++p) {
+      const int q = threadIdx.x + S::kThreads * p, r = q / kChunksRow, c = 8 * (q % kChunksRow);
       const int m = m0 + r, n = n0 + c;
       if (m >= g.M || n >= seg.N) continue;
       const u32x4 x = *(const u32x4*)(ct + r * S::kCPitch + c);
@@ -308,33 +313,47 @@ __global__ void __launch_bounds__(256) gemm_reduce_kernel(GemmArgs g) {
   else ((uint16_t*)seg.C)[o] = f32_to_bf16_bits(v);
 }
 
-struct TileShape {
-  int mt, nt, kt;
-};
-// Tile shape: M <= 32 runs gemm_skinny_kernel (32 rows, 128 columns, K groups of 64), larger
-// M the 128 x 128 x 64 tiles (a 64-row skinny variant measured slower at 64 rows: 1.97 vs
-// 2.26 TB/s of weights).
+// Workgroup tile: M <= 32 runs gemm_skinny_kernel (32 rows, 128 columns, K groups of 64); a
+// 64-row skinny variant measured slower than the 128-row tile at 64 rows (1.97 vs 2.26 TB/s of
+// weights).  Otherwise 256 x 256 (eight wavefronts, one workgroup per CU) when that still
+// makes at least kBigTiles tiles, else 128 x 128: the big tile reads half the LDS bytes per
+// MFMA (7-16 % faster at 32K tokens) but idles CUs when tiles are few (Flash output
+// projection at 4K tokens: 0.77 -> 1.02 ms).
 constexpr int kSkinnyPF = 2;
-TileShape shape_of(int M) { return M <= 32 ? TileShape{32, 128, 64} : TileShape{128, 128, 64}; }
+constexpr int64_t kBigTiles = 1024;
+void tile_of_gemm(const GemmArgs& g, int* tm, int* tn) {
+  if (g.M <= 32) {
+    *tm = 32;
+    *tn = 128;
+    return;
+  }
+  int64_t n256 = 0;
+  for (int q = 0; q < g.n_seg; ++q) n256 += (g.seg[q].N + 255) / 256;
+  const bool big = (int64_t)((g.M + 255) / 256) * n256 * g.batch >= kBigTiles;
+  *tm = *tn = big ? 256 : 128;
+}
 
 }  // namespace
 
 void gemm_plan(GemmArgs& g) {
-  const TileShape sh = shape_of(g.M);
-  const int mt = sh.mt, nt = sh.nt;
+  int mt, nt;
+  tile_of_gemm(g, &mt, &nt);
+  g.tile_m = mt;
+  g.tile_n = nt;
+  constexpr int kt = 64;
   g.m_tiles = (g.M + mt - 1) / mt;
   g.n_tiles = 0;
   for (int s = 0; s < 2; ++s) {
     g.seg[s].n_tiles = s < g.n_seg ? (g.seg[s].N + nt - 1) / nt : 0;
     g.n_tiles += g.seg[s].n_tiles;
   }
-  g.k_tiles = g.K / sh.kt;
+  g.k_tiles = g.K / kt;
   const int64_t tiles = (int64_t)g.m_tiles * g.n_tiles * g.batch;
   // K splits until the launch has ~1,000 workgroups (four per CU; decode-sized M: ~512, as
   // each streams its weights with many loads in flight and fewer splits write fewer
   // partials), each split keeping at least 256 of K
   int s = 1;
-  while (tiles * s < (mt == 32 ? 512 : 1024) && 2 * s * 256 <= g.k_tiles * sh.kt && s < 32) s *= 2;
+  while (tiles * s < (mt == 32 ? 512 : 1024) && 2 * s * 256 <= g.k_tiles * kt && s < 32) s *= 2;
   g.k_splits = s;
   int64_t off = 0;
   for (int q = 0; q < g.n_seg; ++q) {
@@ -355,8 +374,9 @@ hipError_t launch_gemm(GemmArgs g, hipStream_t st) {
   hipEvent_t ev0, ev1;
   timer_events(CA_TIMED_PROJ_GEMM, st, &ev0, &ev1);
   const dim3 grid((unsigned)g.grid_blocks);
-  if (g.M <= 32) CA_LAUNCH((gemm_skinny_kernel<kSkinnyPF, 1>), grid, dim3(256), 0, st, ev0, ev1, g);
-  else CA_LAUNCH((gemm_nt_kernel<128, 128, 64>), grid, dim3(256), 0, st, ev0, ev1, g);
+  if (g.tile_m == 32) CA_LAUNCH((gemm_skinny_kernel<kSkinnyPF, 1>), grid, dim3(256), 0, st, ev0, ev1, g);
+  else if (g.tile_m == 256) CA_LAUNCH((gemm_nt_kernel<256, 256, 64, 8>), grid, dim3(512), 0, st, ev0, ev1, g);
+  else CA_LAUNCH((gemm_nt_kernel<128, 128, 64, 4>), grid, dim3(256), 0, st, ev0, ev1, g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || g.k_splits == 1) return e;
   int64_t n = 0;

@@ -125,6 +125,14 @@ def test_query_proj_widths_off_the_store_granule(T):
     run_query(_small_dims(n_h=1, c=100, n_i=3, c_i=20), T)
 
 
+def test_big_tiles_with_ragged_edges():
+    """Shapes large enough for the 256 x 256 tiles (at least 1,024 of them) with ragged edges in
+    M (8,200 rows) and N (8,480 query channels; group width 300)."""
+    rows = sample(8200, 48)
+    run_query(_small_dims(n_h=16, c=530), 8200, rows=rows)
+    run_out(_small_dims(n_h=128, c=64, g=16, d_g=300), 8200, rows=rows)
+
+
 @pytest.mark.parametrize("T", [1, 5, 33, 300, 2100])
 def test_out_proj_small_ragged(T):
     run_out(_small_dims(), T)
