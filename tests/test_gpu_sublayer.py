@@ -160,3 +160,58 @@ def test_sublayer_pro_prefill_ragged():
     T = 4096 + 37
     run_query(SUBLAYERS["pro"], T, rows=sample(T, 32))
     run_out(SUBLAYERS["pro"], T, rows=sample(T, 32))
+
+
+def test_sublayer_around_csa_prefill():
+    """The layers wired as the pages describe them: h -> low-rank queries (q as [L, n_h, c],
+    q^I as [L, n_I, c_I], w^I) -> CSA prefill (compressors, indexer, top-k, attention) ->
+    grouped output projection of the heads concatenated in head order.  Each stage is compared
+    with the oracle on its GPU input; the attention at the top-k rule and 2e-2."""
+    from long_context_attention_17_amd import binding as ca, layers, synth
+    from long_context_attention_17_amd.configs import Config
+    import oracle
+    from oracle import pipeline as opl
+    from gpu_util import check_out, check_topk
+    from test_gpu_small import check_swapped_rows_prefill
+    cfg = Config(name="sublayer_csa", phase="prefill", D=512, R=64, n_h=64, act="bf16", kv="bf16", csa=True, m=4,
+                 k=64, n_win=128, nI=8, cI=64, idx="e4m3", hca=False, L=777, seed=5151)
+    dims = _small_dims(d=1024, d_c=256, n_h=64, c=512, n_i=8, c_i=64, g=8, d_g=256)
+    L = cfg.L
+    w = synth.sublayer_weights(dims, 21, "cuda")
+    h = synth.hidden(L, dims.d, 21, "cuda")
+    qp = ca.QueryProj(w["w_dq"], w["w_uq"], w["w_iuq"], w["w_w"])
+    c_q = torch.empty(L, dims.d_c, dtype=torch.bfloat16, device="cuda")
+    q = torch.empty(L, dims.n_h * dims.c, dtype=torch.bfloat16, device="cuda")
+    q_i = torch.empty(L, dims.n_i * dims.c_i, dtype=torch.bfloat16, device="cuda")
+    w_i = torch.empty(L, dims.n_i, dtype=torch.float32, device="cuda")
+    qp(h, c_q, q, q_i, w_i)
+    inp = synth.prefill_layer(cfg, "csa", "cuda")
+    inp["q"], inp["qI"], inp["w"] = q.view(L, cfg.n_h, cfg.D), q_i.view(L, cfg.nI, cfg.cI), w_i
+    pt, n_pool = synth.page_table([L // cfg.m], cfg.page, cfg.seed)
+    gp = layers.CSAPrefill(cfg, inp, pt.cuda(), n_pool)
+    gp.run()
+    op = ca.OutProj(w["w_o1"], w["w_o2"], dims.c)
+    u = torch.empty(L, dims.g * dims.d_g, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty(L, dims.d, dtype=torch.bfloat16, device="cuda")
+    op(gp.out.view(L, cfg.n_h * cfg.D), u, y)
+    torch.cuda.synchronize()
+    log(f"[sublayer + csa prefill] L={L} d={dims.d} d_c={dims.d_c}")
+    W = {k: f64(v) for k, v in w.items()}
+    hv, cg = f64(h), f64(c_q)
+    orc_q = osl.low_rank_query(hv, W["w_dq"], W["w_uq"], W["w_iuq"], W["w_w"], act="bf16")
+    check_gemm(cg, hv, W["w_dq"], orc_q["c"], "bf16", "latent")
+    check_gemm(f64(q), cg, W["w_uq"], osl.project(cg, W["w_uq"], "bf16"), "bf16", "queries (GPU latent)")
+    check_gemm(f64(q_i), cg, W["w_iuq"], osl.project(cg, W["w_iuq"], "bf16"), "bf16", "indexer queries (GPU latent)")
+    check_gemm(f64(w_i), hv, W["w_w"], orc_q["w"], "f32", "combiner weights")
+    rows = sample(L, 96)
+    orc = opl.csa_prefill(cfg, inp, to_np(pt)[0], n_pool, rows=rows)
+    ridx = torch.from_numpy(rows).cuda()
+    swaps = check_topk(to_np(gp.idx[ridx]), to_np(gp.cnt[ridx]), orc["idx"], orc["cnt"], orc["scores"],
+                       orc["scores"], cfg.k)
+    same = np.array([np.array_equal(to_np(gp.idx[r]), orc["idx"][i]) for i, r in enumerate(rows)])
+    check_out(f64(gp.out[ridx])[same], orc["out"][same], "bf16", f"attention on the projected queries ({swaps} swaps)")
+    check_swapped_rows_prefill(cfg, inp, pt, n_pool, gp, same, rows=rows)
+    ov = f64(gp.out.view(L, cfg.n_h * cfg.D)[ridx])
+    orc_o = osl.grouped_out_proj(ov, f64(w["w_o1"]), W["w_o2"], act="bf16")
+    check_gemm(f64(y[ridx]), orc_o["u"], W["w_o2"], orc_o["y"], "bf16", "sublayer output y (GPU attention output)",
+               extra=2.0 ** -7)
