@@ -594,8 +594,9 @@ struct MxIssue {
   bool on;            // wavefront-uniform: a tile is being loaded
 
   // Row sources of this wavefront, and its valid bits in sh.valid[st][w].
-  __device__ __forceinline__ void prepare(const AttendArgs& a, int j0, int j1, int tile_no, int st,
-                                          MxShared<KV_FMT>& sh, const uint8_t* dummy, bool enable) {
+  template <class SH>
+  __device__ __forceinline__ void prepare(const AttendArgs& a, int j0, int j1, int tile_no, int st, SH& sh,
+                                          const uint8_t* dummy, bool enable) {
     typedef MxCfg<KV_FMT> C;
     typedef __attribute__((address_space(3))) uint8_t lds_u8;
     const int lane = threadIdx.x & 63;
@@ -1154,9 +1155,10 @@ static int cu_count() {
 }
 
 bool attend_mfma_supported(const AttendArgs& a) {
-  // item sources are 31-bit offsets in 16 B units
-  const bool fits = (uint64_t)a.kv.n_pages * (uint64_t)a.kv.page_bytes < (1ull << 35) &&
-                    (uint64_t)a.W * (uint64_t)(a.seq_fixed >= 0 ? 1 : a.n_rows) * kD * 2 < (1ull << 35);
+  // items are addressed by 31-bit pool record index or window row (the host keeps both below
+  // 2^31 - 1; checked again here)
+  const bool fits = ((int64_t)a.kv.n_pages << a.kv.page_shift) < 0x7FFFFFFF &&
+                    (int64_t)a.W * (a.seq_fixed >= 0 ? 1 : a.n_rows) < 0x7FFFFFFF;
   return a.D == kD && a.R == kR && a.n_heads % 64 == 0 && a.q_fmt == CA_BF16 && a.win_fmt == CA_BF16 &&
          (a.kv.fmt == CA_BF16 || a.kv.fmt == CA_FP8MIX) && fits;
 }
