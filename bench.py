@@ -59,7 +59,8 @@ SUBLAYER_METRIC = "attention sublayer projections (low-rank q + grouped output) 
 KERNEL_SOURCES = {"attend_mx_kernel": ["attend.hip", "common.h", "kernels.h"],
                   "index_scores_fp8_kernel": ["indexer.hip", "common.h", "kernels.h"],
                   "index_scores_fp4_kernel": ["indexer.hip", "common.h", "kernels.h"],
-                  "gemm_nt_kernel": ["proj.hip", "common.h", "kernels.h"]}
+                  "gemm_nt_kernel": ["proj.hip", "common.h", "kernels.h"],
+                  "gemm_skinny_kernel": ["proj.hip", "common.h", "kernels.h"]}
 
 
 def progress(msg):
@@ -462,7 +463,9 @@ def bench_sublayer(name, steps, warmup, replicas):
     abytes = T * (2 * (d.d + d.d_c + d.n_h * d.c + d.n_i * d.c_i + d.n_h * d.c + d.g * d.d_g + d.d) + 4 * d.n_i)
     abytes += T * 2 * (d.d_c + d.g * d.d_g)             # the latent and u, read back by the second stages
     gemm_ms = launch_ms * per_step
-    symbol = f"gemm_nt_kernel<{32 if T <= 32 else 128}, 128>"
+    # the step's GEMM launches: gemm_skinny_kernel for M <= 32, else gemm_nt_kernel with 128 x 128
+    # or 256 x 256 tiles (by the output's tile count); the roofline sums them all
+    symbol = "gemm_skinny_kernel<2, 1>" if T <= 32 else "gemm_nt_kernel"
     if T <= 256:
         roof = kernel_roofline("hbm", wbytes + abytes, symbol, gemm_ms)
         roof["work_unit"] = "bytes of weights and activations per step (all GEMM launches of the step)"
