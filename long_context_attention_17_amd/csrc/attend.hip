@@ -820,7 +820,7 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int pair = wave >> 1, half = wave & 1, partner = wave ^ 1;
-  // Persistent workgroups: unit = (row, head group of 64, split), taken with a
+  // Workgroups take units (split, row, head group of 64), numbered split-major, with a
   // static stride so that the work of a launch does not depend on scheduling.
   const int n_hg = a.n_heads / 64, n_sp = a.split_min > 0 ? a.max_splits : 1;
   const int n_units = a.n_rows * n_hg * n_sp;
@@ -886,7 +886,7 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
   constexpr int kPrologueTiles = C::kFp8 ? 2 : 1;
   float m_force = kNoMax;                              // != kNoMax: recompute the unit with this reference
   for (int unit = blockIdx.x; unit < n_units; unit += gridDim.x) {
-  const int r = unit / (n_hg * n_sp), hg = (unit / n_sp) % n_hg, split = unit % n_sp;
+  const int split = unit / (a.n_rows * n_hg), r = (unit / n_hg) % a.n_rows, hg = unit % n_hg;
   const RowInfo ri = row_info(a, r);
   const int ns = n_splits_of(a, ri.total);
   if (split >= ns) continue;
@@ -974,7 +974,7 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
       mx_scores(tl + 32 * half * kPitch, qf, s, [](int) {});
     if (!C::kFp8 && tile == ntiles - 1 && unit + (int)gridDim.x < n_units) {
       const int un = unit + gridDim.x;                 // prefetch the next unit's queries (bf16:
-      load_q(un / (n_hg * n_sp), (un / n_sp) % n_hg);  // right after the last QK)
+      load_q((un / n_hg) % a.n_rows, un % n_hg);      // right after the last QK)
     }
     float sv[16];
     float mx = -INFINITY;
@@ -1031,7 +1031,7 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
 
   if (C::kFp8 && unit + (int)gridDim.x < n_units) {   // prefetch the next unit's queries (fp8:
     const int un = unit + gridDim.x;                   // after the loop, whose top wait the
-    load_q(un / (n_hg * n_sp), (un / n_sp) % n_hg);    // compiler cannot see)
+    load_q((un / n_hg) % a.n_rows, un % n_hg);        // compiler cannot see)
   }
   if (__builtin_expect(redo && m_force == kNoMax, 0)) {  // workgroup-uniform
     // a logit overflowed the reference: recompute the unit against the exact maximum
@@ -1174,8 +1174,15 @@ hipError_t launch_attend(const AttendArgs& args, hipStream_t st, bool q_prepared
   if (attend_mfma_supported(a)) {
     if (a.q_prep != nullptr && !q_prepared)
       hipLaunchKernelGGL(attend_qprep_kernel, dim3(a.n_rows, a.n_heads / 4), dim3(256), 0, st, a);
+    // Persistent workgroups (one per CU) for prefill.  Split (decode) launches take one
+    // workgroup per unit up to 4 per CU: the unit space is every row's largest split count,
+    // numbered split-major (split 0 of every row and head group first), so the real units
+    // of a batch with short rows take the low workgroup ids that are dispatched first, and
+    // units a row does not have exit at once (a static stride would stack two real units
+    // on some workgroups).
     const long units = (long)a.n_rows * (a.n_heads / 64) * splits;
-    dim3 grid((unsigned)(units < cu_count() ? units : cu_count()));
+    const long cap = splits > 1 && units <= 4L * cu_count() ? units : cu_count();
+    dim3 grid((unsigned)(units < cap ? units : cap));
     const bool qp = a.q_prep != nullptr;
     if (a.kv.fmt == CA_FP8MIX) {
       if (a.mode == 0) {
