@@ -20,6 +20,8 @@
 // time; the MFMA section below describes the tiling.
 // Generic path (any D multiple of 64 up to 512, fp32 math): one wavefront
 //   per (row, head), items streamed from global memory; used for fp32 caches.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "qprep.h"
@@ -32,12 +34,13 @@ struct RowInfo {
 
 // A decode row whose position lies outside [0, max_pos] is out of contract: it gets
 // no items (so nothing is read for it and its output is zero), position 0, and the
-// call's status word receives CA_STATUS_POS_RANGE.
-__device__ __forceinline__ RowInfo row_info(const AttendArgs& a, int r) {
+// call's status word receives CA_STATUS_POS_RANGE.  pos_r and cnt_r: the row's
+// pos[r] and cnt[r] words as loaded (each read only when the call has that array).
+__device__ __forceinline__ RowInfo row_info_of(const AttendArgs& a, int r, int pos_r, int cnt_r) {
   RowInfo ri;
   bool ok = true;
   if (a.pos) {
-    ri.t = a.pos[r];
+    ri.t = pos_r;
     ok = ri.t >= 0 && ri.t <= a.max_pos;
     if (!ok) {
       if (threadIdx.x == 0) raise_status(a.status, CA_STATUS_POS_RANGE);
@@ -50,7 +53,7 @@ __device__ __forceinline__ RowInfo row_info(const AttendArgs& a, int r) {
   ri.win_seq = a.seq_fixed >= 0 ? 0 : r;
   int nc;
   if (a.mode == 0) {
-    nc = a.cnt[r];
+    nc = cnt_r;
     nc = nc < 0 ? 0 : (nc > a.k ? a.k : nc);
   } else {
     nc = ri.t / a.ratio;
@@ -59,6 +62,9 @@ __device__ __forceinline__ RowInfo row_info(const AttendArgs& a, int r) {
   ri.w0 = ri.t - a.n_win + 1 > 0 ? ri.t - a.n_win + 1 : 0;
   ri.total = ok ? ri.n_c + (ri.t - ri.w0 + 1) : 0;
   return ri;
+}
+__device__ __forceinline__ RowInfo row_info(const AttendArgs& a, int r) {
+  return row_info_of(a, r, a.pos != nullptr ? a.pos[r] : 0, a.mode == 0 ? a.cnt[r] : 0);
 }
 
 // Source of item j of a row; nullptr when the item must be skipped.
@@ -206,9 +212,28 @@ __global__ void __launch_bounds__(64) attend_generic_kernel(AttendArgs a) {
 // Merge of a row's split partials (m, l, o) in split order, with the sink in the
 // denominator, then de-rotation of the rotary channels.  A thread owns 4 channels
 // of one head (D/4 threads per head, 512 / (D/4) heads per workgroup); the partials
-// of up to kCombineUnroll splits are all loaded before any is combined.
+// of up to kCombineUnroll splits are all loaded before any is combined: the loads keep
+// the partials' own format (BF: bf16), widened only where they are used, so that no
+// load waits for the one before it.
 constexpr int kCombineUnroll = 16;
 
+// 4 partial values as loaded: 4 fp32, or (BF) 4 bf16 in two words.
+template <bool BF>
+using PartRun = typename std::conditional<BF, u32x2, f32x4>::type;
+template <bool BF>
+__device__ __forceinline__ PartRun<BF> load_part_run(const AttendArgs& a, int64_t e) {
+  if constexpr (BF) return *(const u32x2*)((const uint16_t*)a.part_o + e);
+  else return *(const f32x4*)(a.part_o + e);
+}
+template <bool BF>
+__device__ __forceinline__ f32x4 widen_part_run(PartRun<BF> w) {
+  if constexpr (BF)
+    return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u), __uint_as_float(w[1] << 16),
+                 __uint_as_float(w[1] & 0xFFFF0000u)};
+  else return w;
+}
+
+template <bool BF>
 __global__ void __launch_bounds__(512) attend_combine_kernel(AttendArgs a) {
   const int D = a.D, C = a.D - a.R, tph = D / 4;
   const int r = blockIdx.x, hh = blockIdx.y * (512 / tph) + threadIdx.x / tph, d = 4 * (threadIdx.x % tph);
@@ -217,23 +242,15 @@ __global__ void __launch_bounds__(512) attend_combine_kernel(AttendArgs a) {
   const int ns = n_splits_of(a, ri.total);
   const int64_t base0 = (int64_t)r * a.max_splits * a.n_heads + hh;   // (split s: + s * n_heads)
   const float sk = a.sink[hh] * kLog2e;
-  auto o_at = [&](int64_t b) {                          // 4 channels of a partial (fp32 or bf16)
-    if (!a.part_bf16) return *(const f32x4*)(a.part_o + b * D + d);
-    const u32x2 w = *(const u32x2*)((const uint16_t*)a.part_o + b * D + d);
-    return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u), __uint_as_float(w[1] << 16),
-                 __uint_as_float(w[1] & 0xFFFF0000u)};
-  };
   float ms[kCombineUnroll], ls[kCombineUnroll];
-  f32x4 os[kCombineUnroll];
+  PartRun<BF> os[kCombineUnroll];
 #pragma unroll
-  for (int s = 0; s < kCombineUnroll; ++s) {
-    if (s < ns) {
-      const int64_t b = base0 + (int64_t)s * a.n_heads;
-      const f32x2 ml = *(const f32x2*)(a.part_ml + 2 * b);
-      ms[s] = ml[0];
-      ls[s] = ml[1];
-      os[s] = o_at(b);
-    }
+  for (int s = 0; s < kCombineUnroll; ++s) {          // splits past ns load split ns - 1 again (unused)
+    const int64_t b = base0 + (int64_t)(s < ns ? s : ns - 1) * a.n_heads;
+    const f32x2 ml = *(const f32x2*)(a.part_ml + 2 * b);
+    ms[s] = ml[0];
+    ls[s] = ml[1];
+    os[s] = load_part_run<BF>(a, b * D + d);
   }
   float M = sk;
 #pragma unroll
@@ -247,15 +264,16 @@ __global__ void __launch_bounds__(512) attend_combine_kernel(AttendArgs a) {
     if (s < ns) {
       const float w = exp2f(ms[s] - M);
       den += ls[s] * w;
+      const f32x4 o = widen_part_run<BF>(os[s]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] += os[s][e] * w;
+      for (int e = 0; e < 4; ++e) acc[e] += o[e] * w;
     }
   }
   for (int s = kCombineUnroll; s < ns; ++s) {
     const int64_t b = base0 + (int64_t)s * a.n_heads;
     const float w = exp2f(a.part_ml[2 * b] - M);
     den += a.part_ml[2 * b + 1] * w;
-    const f32x4 o = o_at(b);
+    const f32x4 o = widen_part_run<BF>(load_part_run<BF>(a, b * D + d));
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[e] += o[e] * w;
   }
@@ -303,6 +321,7 @@ __global__ void __launch_bounds__(512) attend_combine_kernel(AttendArgs a) {
 // partial rows are already in flight.
 constexpr int kCombineLdsSplits = 64;   // splits whose weights sit in LDS (more: read from the partials)
 
+template <bool BF>
 __global__ void __launch_bounds__(512) attend_combine_acc_kernel(AttendArgs a) {
   constexpr int D = 512, C = D - 64;
   __shared__ float w_s[kCombineLdsSplits][64];         // exp2(m_s - M) per (split, head of the group)
@@ -314,29 +333,30 @@ __global__ void __launch_bounds__(512) attend_combine_acc_kernel(AttendArgs a) {
   const int hq = 32 * pair + 8 * vq + 4 * (lane >> 5);  // first of the thread's 4 heads in the group
   const int h0 = hg * 64 + hq;                          // heads h0 .. h0+3
   const int c = 256 * half + 32 * cb + (lane & 31);
-  auto o_at = [&](int s) {
+  auto o_at = [&](int s) {                             // the thread's run of split s, as loaded
     const int64_t e = (((int64_t)r * n_ms + s) * n_hg + hg) * (64 * D) + (pair * 2 + half) * 8192 +
-                      (cb * 4 + vq) * 256 + 4 * lane;   // element offset (fp32 or bf16 partials)
-    if (!a.part_bf16) return *(const f32x4*)(a.part_o + e);
-    const u32x2 w = *(const u32x2*)((const uint16_t*)a.part_o + e);
-    return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u), __uint_as_float(w[1] << 16),
-                 __uint_as_float(w[1] & 0xFFFF0000u)};
+                      (cb * 4 + vq) * 256 + 4 * lane;
+    return load_part_run<BF>(a, e);
   };
-  // Every load goes out before anything waits on the row's split count: the first
+  // Every load goes out before anything waits on the row's split count: the row's
+  // position and count words, the sinks, the first
   // splits' partial runs and this thread's (m, l) pairs (head hh, splits g and g + 8),
   // all within the workspace's max_splits; those of splits the row does not have are
-  // never used.
-  f32x4 os[kCombineUnroll];
-#pragma unroll
-  for (int s = 0; s < kCombineUnroll; ++s)
-    if (s < n_ms) os[s] = o_at(s);
+  // never used (past max_splits: split max_splits - 1 again).
   const int hh = t & 63, g = t >> 6;
+  const int pos_r = a.pos != nullptr ? a.pos[r] : 0, cnt_r = a.mode == 0 ? a.cnt[r] : 0;
+  const float sink_h = a.sink[hg * 64 + hh] * kLog2e;
+  f32x4 sink4;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) sink4[e] = a.sink[h0 + e] * kLog2e;
+  PartRun<BF> os[kCombineUnroll];
+#pragma unroll
+  for (int s = 0; s < kCombineUnroll; ++s) os[s] = o_at(s < n_ms ? s : n_ms - 1);
   const int64_t base = ((int64_t)r * n_ms) * a.n_heads + hg * 64 + hh;
   const f32x2 ml0 = g < n_ms ? *(const f32x2*)(a.part_ml + 2 * (base + (int64_t)g * a.n_heads)) : f32x2{0.0f, 0.0f};
   const f32x2 ml1 =
       g + 8 < n_ms ? *(const f32x2*)(a.part_ml + 2 * (base + (int64_t)(g + 8) * a.n_heads)) : f32x2{0.0f, 0.0f};
-  const float sink_h = a.sink[hg * 64 + hh] * kLog2e;
-  const RowInfo ri = row_info(a, r);
+  const RowInfo ri = row_info_of(a, r, pos_r, cnt_r);
   const int ns = n_splits_of(a, ri.total);
 
   // per head of the group: M = max(sink, m_s), den = exp2(sink - M) + sum_s l_s exp2(m_s - M),
@@ -375,7 +395,7 @@ __global__ void __launch_bounds__(512) attend_combine_acc_kernel(AttendArgs a) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     M[e] = M_s[hq + e];
-    float d = exp2f(a.sink[h0 + e] * kLog2e - M[e]);
+    float d = exp2f(sink4[e] - M[e]);
 #pragma unroll
     for (int i = 0; i < 8; ++i) d += red2[i][hq + e];
     den[e] = d;
@@ -391,13 +411,13 @@ __global__ void __launch_bounds__(512) attend_combine_acc_kernel(AttendArgs a) {
 #pragma unroll
   for (int s = 0; s < kCombineUnroll; ++s) {
     if (s < ns) {
-      const f32x4 w = weights(s);
+      const f32x4 w = weights(s), o = widen_part_run<BF>(os[s]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] += os[s][e] * w[e];
+      for (int e = 0; e < 4; ++e) acc[e] += o[e] * w[e];
     }
   }
   for (int s = kCombineUnroll; s < ns; ++s) {
-    const f32x4 o = o_at(s), w = weights(s);
+    const f32x4 o = widen_part_run<BF>(o_at(s)), w = weights(s);
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[e] += o[e] * w[e];
   }
@@ -1214,10 +1234,14 @@ hipError_t launch_attend(const AttendArgs& args, hipStream_t st, bool q_prepared
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.split_min <= 0) return e;
   if (a.part_acc) {
-    hipLaunchKernelGGL(attend_combine_acc_kernel, dim3(a.n_rows, (a.n_heads / 64) * 16), dim3(512), 0, st, a);
+    const dim3 grid(a.n_rows, (a.n_heads / 64) * 16);
+    if (a.part_bf16) hipLaunchKernelGGL(attend_combine_acc_kernel<true>, grid, dim3(512), 0, st, a);
+    else hipLaunchKernelGGL(attend_combine_acc_kernel<false>, grid, dim3(512), 0, st, a);
   } else {
     const int hpb = 512 / (a.D / 4);                   // heads per combine workgroup
-    hipLaunchKernelGGL(attend_combine_kernel, dim3(a.n_rows, (a.n_heads + hpb - 1) / hpb), dim3(512), 0, st, a);
+    const dim3 grid(a.n_rows, (a.n_heads + hpb - 1) / hpb);
+    if (a.part_bf16) hipLaunchKernelGGL(attend_combine_kernel<true>, grid, dim3(512), 0, st, a);
+    else hipLaunchKernelGGL(attend_combine_kernel<false>, grid, dim3(512), 0, st, a);
   }
   return hipGetLastError();
 }
