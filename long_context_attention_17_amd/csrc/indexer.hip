@@ -431,8 +431,20 @@ __global__ void __launch_bounds__(kTopkThreads) topk_rows_kernel(const float* sc
     return;
   }
   const bool in_lds = n <= kTopkLdsKeys;
-  if (in_lds)
-    for (int64_t s = tid; s < n; s += blockDim.x) sh.keys[s] = order_key(row[s]);
+  if (in_lds) {   // every load issued before the first key is stored (slots past n re-read key n - 1)
+    constexpr int kPer = kTopkLdsKeys / kTopkThreads;
+    float v[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int64_t s = tid + (int64_t)i * kTopkThreads;
+      v[i] = row[s < n ? s : n - 1];
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int64_t s = tid + (int64_t)i * kTopkThreads;
+      if (s < n) sh.keys[s] = order_key(v[i]);
+    }
+  }
 
   uint32_t prefix = 0, krem = (uint32_t)k;
   for (int pass = 0; pass < 4; ++pass) {
@@ -540,8 +552,16 @@ __global__ void __launch_bounds__(256) topk_hist_kernel(const float* scores, int
   for (int i = tid; i < kHistBins; i += blockDim.x) h[i] = 0;
   __syncthreads();
   const float* row = scores + (int64_t)r * stride;
-  const int64_t c1 = c0 + kChunk < n ? c0 + kChunk : n;
-  for (int64_t s = c0 + tid; s < c1; s += blockDim.x) atomicAdd(&h[order_key(row[s]) >> 20], 1u);
+  constexpr int kPer = kChunk / 256;   // every load issued before the first is used
+  float v[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int64_t s = c0 + tid + 256 * i;
+    v[i] = row[s < n ? s : n - 1];
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    if (c0 + tid + 256 * i < n) atomicAdd(&h[order_key(v[i]) >> 20], 1u);
   __syncthreads();
   uint32_t* g = state + (int64_t)r * kRowWords;
   add_row_histogram(h, g);
@@ -575,15 +595,19 @@ __global__ void __launch_bounds__(256) topk_gather_kernel(const float* scores, i
   uint32_t* g = state + (int64_t)r * kRowWords;
   uint32_t* meta = g + kHistBins;
   const float* row = scores + (int64_t)r * stride;
-  // each thread owns 16 consecutive keys of the chunk; their loads go out first
+  // thread tid owns the chunk's keys tid + 256 i; all their loads go out first (slots
+  // past n re-read key n - 1 and are never used)
   constexpr int kPer = kChunk / 256;
-  const int64_t s0 = c0 + (int64_t)tid * kPer;
-  uint32_t keys[kPer];
+  const int64_t s0 = c0 + tid;
+  float v[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const int64_t s = s0 + i;
-    keys[i] = s < n ? order_key(row[s]) : 0u;
+    const int64_t s = s0 + 256 * i;
+    v[i] = row[s < n ? s : n - 1];
   }
+  uint32_t keys[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) keys[i] = order_key(v[i]);
   // the threshold bin b* of the row (every workgroup of the row finds the same one; the
   // first also records it, and the count of keys above it, for the resolve launch):
   // wavefront 0 finds the coarse bin holding the k-th largest key from the 64 coarse
@@ -606,7 +630,7 @@ __global__ void __launch_bounds__(256) topk_gather_kernel(const float* scores, i
   const uint32_t bstar = bstar_s;
   uint32_t mine = 0;
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) mine += (s0 + i < n && (keys[i] >> 20) >= bstar) ? 1u : 0u;
+  for (int i = 0; i < kPer; ++i) mine += (s0 + 256 * i < n && (keys[i] >> 20) >= bstar) ? 1u : 0u;
   // block-wide exclusive prefix of the per-thread counts, one reservation per block
   const int lane = tid & 63, wave = tid >> 6;
   uint32_t incl = mine;
@@ -626,7 +650,7 @@ __global__ void __launch_bounds__(256) topk_gather_kernel(const float* scores, i
   uint32_t o = base_s + before;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const int64_t s = s0 + i;
+    const int64_t s = s0 + 256 * i;
     if (s < n && (keys[i] >> 20) >= bstar) {
       cand_key[(int64_t)r * stride + o] = keys[i];
       cand_idx[(int64_t)r * stride + o] = (uint32_t)s;
