@@ -171,19 +171,28 @@ __device__ __forceinline__ void compress_decode_row(const CacheView& cv, int m, 
   float x = 0.0f;
   if (j < D) {
     Pool1 acc;
-    // a-branch (CSA arrays 0 = Ca, 2 = Za; HCA arrays 0 = C, 1 = Z)
-    for (int u = 0; u < m; ++u) {
-      int64_t p = (int64_t)m * i + u;
-      const float* slot = ring + (p % span) * narr * D;
-      acc.add(slot[(overlap ? 2 : 1) * D + j] + Ba[u * D + j], slot[j]);
-    }
-    if (overlap && i > 0) {
-      for (int u = 0; u < m; ++u) {
-        int64_t p = (int64_t)m * (i - 1) + u;
-        const float* slot = ring + (p % span) * narr * D;
-        acc.add(slot[3 * D + j] + Bb[u * D + j], slot[1 * D + j]);
+    // Positions u of entry e (c_arr / z_arr: the ring arrays of the values and the
+    // logits, B the bias rows), taken in order, kPoolBatch at a time with every load of
+    // a batch issued before the first is used (positions past m re-read u = m - 1 and
+    // are not added).
+    constexpr int kPoolBatch = 8;
+    auto pool = [&](int64_t e, int c_arr, int z_arr, const float* B) {
+      for (int u0 = 0; u0 < m; u0 += kPoolBatch) {
+        float z[kPoolBatch], c[kPoolBatch];
+#pragma unroll
+        for (int q = 0; q < kPoolBatch; ++q) {
+          const int u = u0 + q < m ? u0 + q : m - 1;
+          const float* slot = ring + (((int64_t)m * e + u) % span) * narr * D;
+          z[q] = slot[z_arr * D + j] + B[u * D + j];
+          c[q] = slot[c_arr * D + j];
+        }
+#pragma unroll
+        for (int q = 0; q < kPoolBatch; ++q)
+          if (u0 + q < m) acc.add(z[q], c[q]);
       }
-    }
+    };
+    pool(i, 0, overlap ? 2 : 1, Ba);                   // a-branch (CSA arrays 0 = Ca, 2 = Za; HCA 0 = C, 1 = Z)
+    if (overlap && i > 0) pool(i - 1, 1, 3, Bb);       // b-branch of the previous entry (arrays 1 = Cb, 3 = Zb)
     x = acc.value();
   }
   x = norm_rope(x, j, D, cv.rope, gain, eps, apply_rope != 0, (double)m * (double)i, base, red);
