@@ -391,23 +391,32 @@ __device__ __forceinline__ uint32_t get_key(const TopkShared& sh, bool in_lds, c
   return in_lds ? sh.keys[s] : order_key(row[s]);
 }
 
-// Exclusive prefix of 0/1 flags over the block (index order = thread order).
-// Returns the prefix for this thread; *total receives the block total.
-__device__ __forceinline__ uint32_t block_flag_prefix(bool f, uint32_t* wsum, uint32_t* total) {
+// The score of an order key (order_key's inverse; -0 comes back as +0).
+__device__ __forceinline__ float key_score(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key ^ 0x80000000u) : ~key);
+}
+
+// Exclusive prefix sum over the block of a 64-bit value, and the block total.
+__device__ __forceinline__ uint64_t block_excl_scan64(uint64_t v, uint32_t* wlo, uint32_t* whi, uint64_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  uint64_t b = __ballot(f);
-  uint32_t in_wave = __popcll(b & ((1ull << lane) - 1ull));
-  if (lane == 0) wsum[wave] = __popcll(b);
+  uint64_t incl = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint64_t u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) {
+    wlo[wave] = (uint32_t)incl;
+    whi[wave] = (uint32_t)(incl >> 32);
+  }
   __syncthreads();
-  uint32_t before = 0, tot = 0;
+  uint64_t before = incl - v, tot = 0;
   for (int i = 0; i < nw; ++i) {
-    uint32_t c = wsum[i];
+    const uint64_t c = ((uint64_t)whi[i] << 32) | wlo[i];
     before += i < wave ? c : 0;
     tot += c;
   }
-  __syncthreads();
   *total = tot;
-  return before + in_wave;
+  return before;
 }
 
 __global__ void __launch_bounds__(kTopkThreads) topk_rows_kernel(const float* scores, int64_t stride,
@@ -431,18 +440,23 @@ __global__ void __launch_bounds__(kTopkThreads) topk_rows_kernel(const float* sc
     return;
   }
   const bool in_lds = n <= kTopkLdsKeys;
-  if (in_lds) {   // every load issued before the first key is stored (slots past n re-read key n - 1)
-    constexpr int kPer = kTopkLdsKeys / kTopkThreads;
-    float v[kPer];
+  if (in_lds) {
+    // 8 keys per thread at a time, all 8 loads issued before the first is stored (slots
+    // past n re-read key n - 1); more at once would cost the second workgroup per CU its
+    // registers
+    constexpr int kBatch = 8;
+    for (int64_t b0 = 0; b0 < n; b0 += (int64_t)kBatch * kTopkThreads) {
+      float v[kBatch];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int64_t s = tid + (int64_t)i * kTopkThreads;
-      v[i] = row[s < n ? s : n - 1];
-    }
+      for (int i = 0; i < kBatch; ++i) {
+        const int64_t s = b0 + tid + (int64_t)i * kTopkThreads;
+        v[i] = row[s < n ? s : n - 1];
+      }
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int64_t s = tid + (int64_t)i * kTopkThreads;
-      if (s < n) sh.keys[s] = order_key(v[i]);
+      for (int i = 0; i < kBatch; ++i) {
+        const int64_t s = b0 + tid + (int64_t)i * kTopkThreads;
+        if (s < n) sh.keys[s] = order_key(v[i]);
+      }
     }
   }
 
@@ -483,23 +497,45 @@ __global__ void __launch_bounds__(kTopkThreads) topk_rows_kernel(const float* sc
     krem = sh.sel_krem;
     __syncthreads();
   }
-  // prefix == T (the k-th largest key); krem == how many keys equal to T to keep
+  // prefix == T (the k-th largest key); krem == how many keys equal to T to keep: every
+  // key > T and the krem lowest-indexed keys == T.  Thread tid owns the keys
+  // [tid * per, +per) (per a multiple of 4); one block scan of its counts of keys > T
+  // and == T gives the kept keys before its run: those > T, and min(krem, those == T).
   const uint32_t T = prefix, need_eq = krem;
-  uint32_t eq_seen = 0, taken = 0;
-  for (int64_t base = 0; base < n; base += blockDim.x) {
-    int64_t s = base + tid;
-    uint32_t key = s < n ? get_key(sh, in_lds, row, s) : 0u;
-    bool gt = s < n && key > T, eq = s < n && key == T;
-    uint32_t eq_tot, tk_tot;
-    uint32_t eq_rank = eq_seen + block_flag_prefix(eq, sh.wsum, &eq_tot);
-    bool take = gt || (eq && eq_rank < need_eq);
-    uint32_t o = taken + block_flag_prefix(take, sh.wsum2, &tk_tot);
-    if (take && o < (uint32_t)k) {
-      oi[o] = (int32_t)s;
-      if (os) os[o] = row[s];
+  const int64_t per = (n + 4 * kTopkThreads - 1) / (4 * kTopkThreads) * 4;
+  const int64_t s0 = tid * per, s1 = s0 + per < n ? s0 + per : n;
+  uint32_t n_gt = 0, n_eq = 0;
+  if (in_lds) {
+    for (int64_t s = s0; s < s1; s += 4) {
+      const u32x4 q = *(const u32x4*)&sh.keys[s];   // keys past n are never counted
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        n_gt += (s + e < s1 && q[e] > T) ? 1u : 0u;
+        n_eq += (s + e < s1 && q[e] == T) ? 1u : 0u;
+      }
     }
-    eq_seen += eq_tot;
-    taken += tk_tot;
+  } else {
+    for (int64_t s = s0; s < s1; ++s) {
+      const uint32_t key = order_key(row[s]);
+      n_gt += key > T ? 1u : 0u;
+      n_eq += key == T ? 1u : 0u;
+    }
+  }
+  uint64_t tot;
+  const uint64_t before = block_excl_scan64(((uint64_t)n_eq << 32) | n_gt, sh.wsum, sh.wsum2, &tot);
+  uint32_t eq_seen = (uint32_t)(before >> 32);
+  uint32_t o = (uint32_t)before + (eq_seen < need_eq ? eq_seen : need_eq);
+  for (int64_t s = s0; s < s1; ++s) {
+    const uint32_t key = get_key(sh, in_lds, row, s);
+    const bool take = key > T || (key == T && eq_seen < need_eq);
+    eq_seen += key == T ? 1u : 0u;
+    if (take) {
+      if (o < (uint32_t)k) {
+        oi[o] = (int32_t)s;
+        if (os) os[o] = key_score(key);
+      }
+      ++o;
+    }
   }
   if (tid == 0) out_cnt[r] = k;
 }
