@@ -733,25 +733,33 @@ __device__ __forceinline__ void mx_convert(const AttendArgs& a, const uint8_t* r
 }
 
 // S^T (32 items x 32 heads) = K Q^T over the 512 channels: 32 MFMAs in one
-// accumulation chain, K fragments (row l%32, 16 B at channel 16s + 8(l/32)) read
-// kPf steps ahead; between(u) runs after every second MFMA (u = 0..15).
+// accumulation chain (TWO: two chains, even and odd channel steps, added at the end),
+// K fragments (row l%32, 16 B at channel 16s + 8(l/32)) read kPf steps ahead;
+// between(u) runs after every second MFMA (u = 0..15).  Two chains measure faster
+// with fp8 entries and prepared queries (decode), slower with bf16 entries, and
+// do not fit the registers of the fp8 raw-query variant.
 constexpr int kPf = 4;
-template <class F>
+template <bool TWO, class F>
 __device__ __forceinline__ void mx_scores(const __bf16* kt, const bf16x8* qf, f32x16& s_out, const F& between) {
   const int lane = threadIdx.x & 63;
   const __bf16* krow = kt + mx_row(lane & 31) * kPitch + 8 * (lane >> 5);
-  f32x16 acc;
+  f32x16 acc, acc1;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+  for (int v = 0; v < 16; ++v) acc[v] = acc1[v] = 0.0f;
   bf16x8 kf[kPf];
 #pragma unroll
   for (int s = 0; s < kPf; ++s) kf[s] = *(const bf16x8*)(krow + 16 * s);
 #pragma unroll
   for (int s = 0; s < 32; ++s) {
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s % kPf], qf[s], acc, 0, 0, 0);
+    if (TWO && (s & 1)) acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s % kPf], qf[s], acc1, 0, 0, 0);
+    else acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s % kPf], qf[s], acc, 0, 0, 0);
     if (s + kPf < 32) kf[s % kPf] = *(const bf16x8*)(krow + 16 * (s + kPf));
     if (s & 1) between(s >> 1);
     __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (TWO) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] += acc1[v];
   }
   s_out = acc;
 }
@@ -988,10 +996,11 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
     // the next tile's row loads go out between the QK MFMAs (one row after every
     // second MFMA), so that their issue overlaps the matrix work
     f32x16 s;
+    constexpr bool kTwoChains = C::kFp8 && qp;
     if (is.on)
-      mx_scores(tl + 32 * half * kPitch, qf, s, [&](int u) { is.row(u); });
+      mx_scores<kTwoChains>(tl + 32 * half * kPitch, qf, s, [&](int u) { is.row(u); });
     else
-      mx_scores(tl + 32 * half * kPitch, qf, s, [](int) {});
+      mx_scores<kTwoChains>(tl + 32 * half * kPitch, qf, s, [](int) {});
     if (!C::kFp8 && tile == ntiles - 1 && unit + (int)gridDim.x < n_units) {
       const int un = unit + gridDim.x;                 // prefetch the next unit's queries (bf16:
       load_q((un / n_hg) % a.n_rows, un % n_hg);      // right after the last QK)
