@@ -150,6 +150,31 @@ __global__ void compress_prefill_kernel(CacheView cv, int seq, int m, int overla
   store_record(cv, seq, i, x, j, red);
 }
 
+// Adds positions u = 0 .. m-1 of entry e to acc, in order, for channel j: logit
+// z_arr[u] + B[u], value c_arr[u] from the tail ring (position p of the sequence in
+// slot p % span, narr arrays of D floats per slot; span is m or 2m, so the m positions
+// of an entry sit in the consecutive slots from (m e) % span).  BATCH positions at a
+// time, every load of a batch issued before the first is used (positions past m
+// re-read u = m - 1 and are not added).
+template <int BATCH>
+__device__ __forceinline__ void pool_positions(Pool1& acc, const float* ring, int m, int span, int narr, int D, int j,
+                                               int64_t e, int c_arr, int z_arr, const float* B) {
+  const float* first = ring + (int64_t)(((int64_t)m * e) % span) * narr * D;
+  for (int u0 = 0; u0 < m; u0 += BATCH) {
+    float z[BATCH], c[BATCH];
+#pragma unroll
+    for (int q = 0; q < BATCH; ++q) {
+      const int u = u0 + q < m ? u0 + q : m - 1;
+      const float* slot = first + (int64_t)u * narr * D;
+      z[q] = slot[z_arr * D + j] + B[u * D + j];
+      c[q] = slot[c_arr * D + j];
+    }
+#pragma unroll
+    for (int q = 0; q < BATCH; ++q)
+      if (u0 + q < m) acc.add(z[q], c[q]);
+  }
+}
+
 // Tail ring: tail[b, slot, a, ch] (float32), narr arrays per slot.
 // Decode-time compressor step of sequence b (thread j = channel j; every thread of
 // the block takes part, channels j >= D hold nothing).
@@ -171,25 +196,11 @@ __device__ __forceinline__ void compress_decode_row(const CacheView& cv, int m, 
   float x = 0.0f;
   if (j < D) {
     Pool1 acc;
-    // Positions u of entry e (c_arr / z_arr: the ring arrays of the values and the
-    // logits, B the bias rows), taken in order, kPoolBatch at a time with every load of
-    // a batch issued before the first is used (positions past m re-read u = m - 1 and
-    // are not added).
-    constexpr int kPoolBatch = 8;
+    // entry e's positions (c_arr / z_arr: the ring arrays of the values and the logits,
+    // B the bias rows); long pooling windows (HCA) in batches of 32 loads, short ones of 8
     auto pool = [&](int64_t e, int c_arr, int z_arr, const float* B) {
-      for (int u0 = 0; u0 < m; u0 += kPoolBatch) {
-        float z[kPoolBatch], c[kPoolBatch];
-#pragma unroll
-        for (int q = 0; q < kPoolBatch; ++q) {
-          const int u = u0 + q < m ? u0 + q : m - 1;
-          const float* slot = ring + (((int64_t)m * e + u) % span) * narr * D;
-          z[q] = slot[z_arr * D + j] + B[u * D + j];
-          c[q] = slot[c_arr * D + j];
-        }
-#pragma unroll
-        for (int q = 0; q < kPoolBatch; ++q)
-          if (u0 + q < m) acc.add(z[q], c[q]);
-      }
+      if (m >= 32) pool_positions<32>(acc, ring, m, span, narr, D, j, e, c_arr, z_arr, B);
+      else pool_positions<8>(acc, ring, m, span, narr, D, j, e, c_arr, z_arr, B);
     };
     pool(i, 0, overlap ? 2 : 1, Ba);                   // a-branch (CSA arrays 0 = Ca, 2 = Za; HCA 0 = C, 1 = Z)
     if (overlap && i > 0) pool(i - 1, 1, 3, Bb);       // b-branch of the previous entry (arrays 1 = Cb, 3 = Zb)
