@@ -138,18 +138,21 @@ struct KeyGroup {
   bool ok[G];
 };
 
-// Loads of a group of G MFMA blocks of 32 keys (key = lane % 32 of each).
-// e4m3 pages: lane half h takes the key's code bytes [32h, 32h + 32).  FP4 pages:
-// lane half h takes the bytes [16h, 16h + 16) (channels 32h .. 32h + 31) and the
-// E8M0 byte of block h.
-template <int KF, int G>
-__device__ __forceinline__ void load_key_group(const CacheView& cv, const int* pt_s, int64_t k0, int64_t k1,
+// Loads of a group of G MFMA blocks of 32 keys (key = lane % 32 of each), of a
+// wavefront whose keys start at wbase: lane i of wpg holds the pool page of the
+// wavefront's i-th page (-1: none).  e4m3 pages: lane half h takes the key's code
+// bytes [32h, 32h + 32).  FP4 pages: lane half h takes the bytes [16h, 16h + 16)
+// (channels 32h .. 32h + 31) and the E8M0 byte of block h.  NT: e4m3 code bytes
+// loaded as non-temporal (keys read once per call, as in decode).
+template <int KF, int G, bool NT>
+__device__ __forceinline__ void load_key_group(const CacheView& cv, int wpg, int64_t wbase, int64_t k1,
                                                int64_t gbase, int lane, KeyGroup<G>& kg) {
   constexpr int cI = 64;
 #pragma unroll
   for (int u = 0; u < G; ++u) {
     const int64_t s = gbase + 32 * u + (lane & 31);
-    const int pg = s < k1 ? pt_s[(int)((s - k0) >> cv.page_shift)] : -1;
+    const int pgv = __shfl(wpg, (int)((s >> cv.page_shift) - (wbase >> cv.page_shift)), 64);
+    const int pg = s < k1 ? pgv : -1;
     kg.ok[u] = pg >= 0;
     kg.v0[u] = i32x4{0, 0, 0, 0};
     kg.v1[u] = kg.v0[u];
@@ -163,8 +166,8 @@ __device__ __forceinline__ void load_key_group(const CacheView& cv, const int* p
         kg.sc[u] = base[((cI / 2) << cv.page_shift) + slot * (cI / 32) + (lane >> 5)];
       } else {
         const i32x4* kp = (const i32x4*)(base + slot * cI + 32 * (lane >> 5));
-        kg.v0[u] = kp[0];
-        kg.v1[u] = kp[1];
+        kg.v0[u] = NT ? __builtin_nontemporal_load(kp) : kp[0];
+        kg.v1[u] = NT ? __builtin_nontemporal_load(kp + 1) : kp[1];
         kg.ks[u] = ((const float*)(base + (cI << cv.page_shift)))[slot];
       }
     }
@@ -201,6 +204,14 @@ __device__ __forceinline__ void add_row_histogram(const uint32_t* hb, uint32_t* 
   }
 }
 
+// Workgroup barrier ordering LDS only: global loads in flight stay in flight
+// (__syncthreads also waits for them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <int QPW, int KF, int QF>
 __device__ __forceinline__ void index_scores_mfma(CacheView cv, int m, int q_fmt, const void* qI, const float* w,
                                                   RowPos pos, int seq_fixed, int n_rows, float* scores,
@@ -212,27 +223,35 @@ __device__ __forceinline__ void index_scores_mfma(CacheView cv, int m, int q_fmt
   __shared__ __attribute__((aligned(16))) uint8_t qcodes[32 * cI];  // A operand rows: (query, head)
   __shared__ uint8_t qsc[32][2];                                    // FP4 queries: E8M0 byte per block
   __shared__ float wq[32];                                          // w (* query scale for e4m3) per row
-  __shared__ int pt_s[kScoreChunk / 16];                            // page ids of the chunk (>= 64 pages)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r0 = blockIdx.x * QPW;
 
   const int seq = seq_fixed >= 0 ? seq_fixed : r0;     // decode: one row per group, row == sequence
   const int64_t k0 = (int64_t)blockIdx.y * kScoreChunk;
 
-  // The loads that do not depend on the row positions go out first: the chunk's page
-  // ids (one per thread: n_pg <= 256 pages as page_shift >= 4) and the query rows.
-  const int n_pg = kScoreChunk >> cv.page_shift;
-  int pg = -1;
-  if (threadIdx.x < n_pg) {
-    const int64_t pi = (k0 >> cv.page_shift) + threadIdx.x;
-    if (pi < cv.max_pages) pg = cv.page_table[(int64_t)seq * cv.max_pages + pi];
-  }
+  // The prologue's loads go out together, each from an in-range address, and only
+  // then are they used: the rows' pos words (first: the first to be waited for), the
+  // pool pages of the wavefront's 1,024 keys (lane i: page i; at most 64 as
+  // page_shift >= 4; validity applied when used) and the query rows (rows past the
+  // group's queries read row r0 and are zeroed).
+  int praw[QPW];
+#pragma unroll
+  for (int qq = 0; qq < QPW; ++qq)
+    praw[qq] = pos.pos != nullptr ? pos.pos[r0 + qq < n_rows ? r0 + qq : r0] : 0;
+  const int64_t wbase = k0 + (kScoreChunk / 4) * wave;
+  const int n_wpg = ((kScoreChunk / 4) >> cv.page_shift) > 0 ? ((kScoreChunk / 4) >> cv.page_shift) : 1;
+  const int64_t pi = (wbase >> cv.page_shift) + (lane < n_wpg ? lane : 0);
+  const bool pi_ok = lane < n_wpg && pi < cv.max_pages;
+  const int praw_pg = cv.max_pages > 0 ? cv.page_table[(int64_t)seq * cv.max_pages + (pi_ok ? pi : 0)] : -1;
   constexpr int kRowsPerWave = 32 / 4;                 // query-head rows (query, head) of each wave
-  float qv[kRowsPerWave];
+  uint32_t qraw[kRowsPerWave];                         // as loaded: bf16 bits or fp32 bits
+  const bool q_bf16 = q_fmt == CA_BF16;
 #pragma unroll
   for (int j = 0; j < kRowsPerWave; ++j) {
     const int row = wave + 4 * j, qq = row / nI, h = row % nI, r = r0 + qq;
-    qv[j] = (qq < QPW && r < n_rows) ? load_act(qI, q_fmt, ((int64_t)r * nI + h) * cI + lane) : 0.0f;
+    const bool ok = qq < QPW && r < n_rows;
+    const int64_t i = ((int64_t)(ok ? r : r0) * nI + h) * cI + lane;
+    qraw[j] = q_bf16 ? (uint32_t)((const uint16_t*)qI)[i] : ((const uint32_t*)qI)[i];
   }
 
   int64_t ne[QPW];
@@ -240,23 +259,37 @@ __device__ __forceinline__ void index_scores_mfma(CacheView cv, int m, int q_fmt
 #pragma unroll
   for (int qq = 0; qq < QPW; ++qq) {
     int r = r0 + qq;
-    int t = r < n_rows ? pos(r) : 0;
+    int t = r < n_rows ? pos.of(r, praw[qq]) : 0;
     ne[qq] = r < n_rows ? (t / m < stride ? t / m : stride) : 0;
     ne_max = ne[qq] > ne_max ? ne[qq] : ne_max;
   }
+  const int wpg = pi_ok && praw_pg < cv.n_pages ? praw_pg : -1;
   if (k0 >= ne_max) return;                            // uniform over the block
   const bool want_hist = QPW == 1 && hist != nullptr && ne[0] > hist_k;   // uniform
   if (want_hist)
     for (int i = threadIdx.x; i < kHistBins; i += 256) hs[i] = 0u;
   const int64_t k1 = (k0 + kScoreChunk < ne_max) ? k0 + kScoreChunk : ne_max;
 
-  // prologue: the chunk's page ids into LDS, and QPW*8 query-head rows quantized to e4m3
-  if (threadIdx.x < n_pg) pt_s[threadIdx.x] = pg < cv.n_pages ? pg : -1;
+  // one-row (decode) workgroups: the wavefront's first two key groups go out before
+  // the query rows are prepared (with four rows the registers do not allow it), and
+  // the keys, read once, are loaded as non-temporal (prefill row groups re-read them)
+  constexpr int G = group_blocks<KF>();
+  constexpr int kGroupKeys = 32 * G;
+  constexpr int kGroups = kScoreChunk / 4 / kGroupKeys;  // groups per wave
+  static_assert(kGroups >= 2, "two key groups in flight");
+  constexpr bool kEarly = QPW == 1;
+  KeyGroup<G> cur, nxt;
+  if constexpr (kEarly) {
+    load_key_group<KF, G, kEarly>(cv, wpg, wbase, k1, wbase, lane, cur);
+    load_key_group<KF, G, kEarly>(cv, wpg, wbase, k1, wbase + kGroupKeys, lane, nxt);
+  }
+
+  // prologue: QPW*8 query-head rows quantized to e4m3
 #pragma unroll
   for (int j = 0; j < kRowsPerWave; ++j) {
     const int row = wave + 4 * j, qq = row / nI, h = row % nI, r = r0 + qq;
     if (qq < QPW && r < n_rows) {                      // (uniform) rows past the group's queries stay zero
-      const float v = qv[j];
+      const float v = __uint_as_float(q_bf16 ? qraw[j] << 16 : qraw[j]);
       if constexpr (QF == CA_FP4) {
         // the 32-channel blocks are the wavefront's halves: block maximum, exponent,
         // then channel pairs (2c, 2c+1) packed into byte c, low nibble first
@@ -280,7 +313,7 @@ __device__ __forceinline__ void index_scores_mfma(CacheView cv, int m, int q_fmt
       if (lane == 0) wq[row] = 0.0f;
     }
   }
-  __syncthreads();
+  lds_barrier();   // the query rows, their weights and the cleared histogram (LDS only)
 
   // A operand: row lane%32.  e4m3 queries, e4m3 keys: bytes [32*(lane/32), +32);
   // e4m3 queries, FP4 keys: bytes [16*(lane/32), +16) then [32 + 16*(lane/32), +16);
@@ -311,16 +344,11 @@ __device__ __forceinline__ void index_scores_mfma(CacheView cv, int m, int q_fmt
 #pragma unroll
     for (int v = 0; v < 4; ++v) wl[qq][v] = wq[qq * nI + 4 * (lane >> 5) + v];
 
-  const int64_t wbase = k0 + (kScoreChunk / 4) * wave;
-  constexpr int G = group_blocks<KF>();
-  constexpr int kGroupKeys = 32 * G;
-  constexpr int kGroups = kScoreChunk / 4 / kGroupKeys;  // groups per wave
-  KeyGroup<G> cur, nxt;
-  load_key_group<KF, G>(cv, pt_s, k0, k1, wbase, lane, cur);
+  if constexpr (!kEarly) load_key_group<KF, G, kEarly>(cv, wpg, wbase, k1, wbase, lane, cur);
   for (int grp = 0; grp < kGroups; ++grp) {
     const int64_t gbase = wbase + kGroupKeys * grp;
     if (gbase >= k1) break;
-    if (grp + 1 < kGroups) load_key_group<KF, G>(cv, pt_s, k0, k1, gbase + kGroupKeys, lane, nxt);
+    if (!kEarly && grp + 1 < kGroups) load_key_group<KF, G, kEarly>(cv, wpg, wbase, k1, gbase + kGroupKeys, lane, nxt);
 #pragma unroll
     for (int u = 0; u < G; ++u) {
       const int64_t s = gbase + 32 * u + (lane & 31);
@@ -347,6 +375,8 @@ __device__ __forceinline__ void index_scores_mfma(CacheView cv, int m, int q_fmt
       }
     }
     cur = nxt;
+    if (kEarly && grp + 2 < kGroups)   // groups grp + 1 and grp + 2 in flight while grp + 1 is scored
+      load_key_group<KF, G, kEarly>(cv, wpg, wbase, k1, gbase + 2 * kGroupKeys, lane, nxt);
   }
   if (want_hist) {   // the chunk's nonzero bins into the row's histogram (integer adds: order free)
     __syncthreads();

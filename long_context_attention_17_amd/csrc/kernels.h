@@ -54,14 +54,15 @@ struct RowPos {
   int t0;
   int max_pos;
   int32_t* status;
-  __device__ __forceinline__ int operator()(int r) const {
+  __device__ __forceinline__ int operator()(int r) const { return of(r, pos != nullptr ? pos[r] : 0); }
+  // The same from row r's pos word as already loaded (raw; ignored when pos == nullptr).
+  __device__ __forceinline__ int of(int r, int raw) const {
     if (pos == nullptr) return t0 + r;
-    const int t = pos[r];
-    if (t < 0 || t > max_pos) {
+    if (raw < 0 || raw > max_pos) {
       raise_status(status, CA_STATUS_POS_RANGE);
       return -1;
     }
-    return t;
+    return raw;
   }
 };
 
