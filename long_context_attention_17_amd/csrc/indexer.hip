@@ -595,7 +595,10 @@ constexpr int kCoarseBins = 64;       // coarse histogram: the top 6 key bits
 constexpr int kRowWords = kHistBins + kMetaWords + kCoarseBins;   // per-row state: histogram, counters, coarse
 static_assert(kRowWords == kTopkRowWords, "per-row long top-k state size");
 constexpr int kRegCand = 4;            // candidates per resolve thread held in registers
-constexpr int kBitmapLdsWords = 16384;  // two LDS bitmaps of rows up to 262,144 keys (larger rows: workspace)
+constexpr int kBitmapLdsWords = 16384;  // two LDS bitmaps of rows up to 524,288 keys (larger rows: workspace)
+
+// Words of an index bitmap of n bits, rounded up to a multiple of 4 (16 B).
+__host__ __device__ __forceinline__ int64_t bitmap_words(int64_t n) { return ((n + 31) / 32 + 3) & ~(int64_t)3; }
 
 __global__ void topk_zero_kernel(uint32_t* p, int64_t n) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -769,7 +772,7 @@ __global__ void __launch_bounds__(kResolveThreads) topk_resolve_kernel(const flo
   __shared__ uint32_t hist[1024];
   __shared__ uint32_t wsum[kResolveThreads / 64];
   __shared__ uint32_t sel[2];
-  __shared__ uint32_t bm_lds[2 * kBitmapLdsWords];
+  __shared__ __attribute__((aligned(16))) uint32_t bm_lds[2 * kBitmapLdsWords];
   const int r = blockIdx.x, tid = threadIdx.x;
   const int64_t n = row_len(pos, r, m, stride);
   const float* row = scores + (int64_t)r * stride;
@@ -822,12 +825,13 @@ __global__ void __launch_bounds__(kResolveThreads) topk_resolve_kernel(const flo
     __syncthreads();
   }
   const uint32_t T = prefix, need_eq = need;           // keep every key > T and the need_eq lowest indices == T
-  // bitmaps of the row's indices: kept (keys > T, then the chosen ties) and equal to T
-  const int64_t words = (n + 31) / 32;
-  uint32_t* bm = words <= kBitmapLdsWords ? bm_lds : bm_ws + (int64_t)r * 2 * ((stride + 31) / 32);
+  // bitmaps of the row's indices: kept (keys > T, then the chosen ties) and equal to T,
+  // each a multiple of 4 words, read and cleared 16 B at a time
+  const int64_t words = bitmap_words(n);
+  uint32_t* bm = words <= kBitmapLdsWords ? bm_lds : bm_ws + (int64_t)r * 2 * bitmap_words(stride);
   uint32_t* keep = bm;
   uint32_t* eq = bm + words;
-  for (int64_t i = tid; i < 2 * words; i += blockDim.x) bm[i] = 0;
+  for (int64_t i = tid; i < 2 * words / 4; i += blockDim.x) ((u32x4*)bm)[i] = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < kRegCand; ++j)
@@ -841,11 +845,19 @@ __global__ void __launch_bounds__(kResolveThreads) topk_resolve_kernel(const flo
     }
   }
   __syncthreads();
-  // each thread owns a contiguous run of bitmap words; ties taken in index order
-  const int64_t per = (words + kResolveThreads - 1) / kResolveThreads;
+  // each thread owns a contiguous run of bitmap words (a multiple of 4); ties taken in
+  // index order
+  const int64_t per = (words / 4 + kResolveThreads - 1) / kResolveThreads * 4;
   const int64_t w0 = (int64_t)tid * per, w1 = w0 + per < words ? w0 + per : words;
-  uint32_t cnt = 0;
-  for (int64_t w = w0; w < w1; ++w) cnt += __popc(eq[w]);
+  auto popc_run = [&](const uint32_t* b) {
+    uint32_t c = 0;
+    for (int64_t w = w0; w < w1; w += 4) {
+      const u32x4 q = *(const u32x4*)&b[w];
+      c += __popc(q[0]) + __popc(q[1]) + __popc(q[2]) + __popc(q[3]);
+    }
+    return c;
+  };
+  uint32_t cnt = popc_run(eq);
   uint32_t tot;
   uint32_t rank = block_excl_scan(cnt, wsum, &tot);
   for (int64_t w = w0; w < w1 && rank < need_eq; ++w) {
@@ -858,20 +870,23 @@ __global__ void __launch_bounds__(kResolveThreads) topk_resolve_kernel(const flo
     }
   }
   __syncthreads();
-  cnt = 0;
-  for (int64_t w = w0; w < w1; ++w) cnt += __popc(keep[w]);
+  cnt = popc_run(keep);
   uint32_t o = block_excl_scan(cnt, wsum, &tot);
-  for (int64_t w = w0; w < w1; ++w) {
-    uint32_t e = keep[w];
-    while (e) {
-      const int b = __ffs(e) - 1;
-      const uint32_t id = (uint32_t)(w * 32 + b);
-      if (o < (uint32_t)k) {
-        oi[o] = (int32_t)id;
-        if (os) os[o] = row[id];
+  for (int64_t w4 = w0; w4 < w1; w4 += 4) {
+    const u32x4 q = *(const u32x4*)&keep[w4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      uint32_t e = q[x];
+      while (e) {
+        const int b = __ffs(e) - 1;
+        const uint32_t id = (uint32_t)((w4 + x) * 32 + b);
+        if (o < (uint32_t)k) {
+          oi[o] = (int32_t)id;
+          if (os) os[o] = row[id];
+        }
+        ++o;
+        e &= e - 1;
       }
-      ++o;
-      e &= e - 1;
     }
   }
   if (tid == 0) out_cnt[r] = k;
@@ -941,7 +956,7 @@ hipError_t launch_index_scores(const CacheView& cv, const ca_index_params& p, co
 // indices [rows][stride] each, and [rows][2][stride/32] bitmaps for rows too long
 // for the LDS bitmaps.
 size_t topk_long_workspace(int n_rows, int64_t stride) {
-  const size_t words = (size_t)(stride + 31) / 32;
+  const size_t words = (size_t)bitmap_words(stride);
   return (size_t)n_rows * kRowWords * 4 + 2 * (size_t)n_rows * stride * 4 +
          2 * (size_t)n_rows * words * 4 + 256;
 }
