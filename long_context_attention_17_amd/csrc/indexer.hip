@@ -800,6 +800,14 @@ __global__ void __launch_bounds__(kResolveThreads) topk_resolve_kernel(const flo
     rk[j] = gk[tid + j * kResolveThreads];
     ri[j] = gi[tid + j * kResolveThreads];
   }
+  // bitmaps of the row's indices: kept (keys > T, then the chosen ties) and equal to T,
+  // each a multiple of 4 words, read and cleared 16 B at a time; cleared while the
+  // loads are in flight (the radix passes' barriers order it before the first use)
+  const int64_t words = bitmap_words(n);
+  uint32_t* bm = words <= kBitmapLdsWords ? bm_lds : bm_ws + (int64_t)r * 2 * bitmap_words(stride);
+  uint32_t* keep = bm;
+  uint32_t* eq = bm + words;
+  for (int64_t i = tid; i < 2 * words / 4; i += blockDim.x) ((u32x4*)bm)[i] = u32x4{0u, 0u, 0u, 0u};
   const uint32_t nc = meta[0], bstar = meta[2], above = meta[3];
 #pragma unroll
   for (int j = 0; j < kRegCand; ++j)
@@ -825,14 +833,6 @@ __global__ void __launch_bounds__(kResolveThreads) topk_resolve_kernel(const flo
     __syncthreads();
   }
   const uint32_t T = prefix, need_eq = need;           // keep every key > T and the need_eq lowest indices == T
-  // bitmaps of the row's indices: kept (keys > T, then the chosen ties) and equal to T,
-  // each a multiple of 4 words, read and cleared 16 B at a time
-  const int64_t words = bitmap_words(n);
-  uint32_t* bm = words <= kBitmapLdsWords ? bm_lds : bm_ws + (int64_t)r * 2 * bitmap_words(stride);
-  uint32_t* keep = bm;
-  uint32_t* eq = bm + words;
-  for (int64_t i = tid; i < 2 * words / 4; i += blockDim.x) ((u32x4*)bm)[i] = u32x4{0u, 0u, 0u, 0u};
-  __syncthreads();
 #pragma unroll
   for (int j = 0; j < kRegCand; ++j)
     if (tid + j * kResolveThreads < nc && rk[j] >= T)
