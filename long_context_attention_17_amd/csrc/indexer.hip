@@ -833,15 +833,18 @@ __global__ void __launch_bounds__(kResolveThreads) topk_resolve_kernel(const flo
     __syncthreads();
   }
   const uint32_t T = prefix, need_eq = need;           // keep every key > T and the need_eq lowest indices == T
+  // the last pass's bin of T counts the candidates equal to T: when every one of them
+  // is kept (the usual case) they go straight into the kept bitmap (uniform)
+  const bool all_eq = hist[T & 1023u] == need_eq;
 #pragma unroll
   for (int j = 0; j < kRegCand; ++j)
     if (tid + j * kResolveThreads < nc && rk[j] >= T)
-      atomicOr(rk[j] > T ? &keep[ri[j] >> 5] : &eq[ri[j] >> 5], 1u << (ri[j] & 31));
+      atomicOr(rk[j] > T || all_eq ? &keep[ri[j] >> 5] : &eq[ri[j] >> 5], 1u << (ri[j] & 31));
   for (uint32_t i = tid + kRegCand * kResolveThreads; i < nc; i += blockDim.x) {
     const uint32_t key = gk[i];
     if (key >= T) {
       const uint32_t id = gi[i];
-      atomicOr(key > T ? &keep[id >> 5] : &eq[id >> 5], 1u << (id & 31));
+      atomicOr(key > T || all_eq ? &keep[id >> 5] : &eq[id >> 5], 1u << (id & 31));
     }
   }
   __syncthreads();
@@ -857,19 +860,21 @@ __global__ void __launch_bounds__(kResolveThreads) topk_resolve_kernel(const flo
     }
     return c;
   };
-  uint32_t cnt = popc_run(eq);
-  uint32_t tot;
-  uint32_t rank = block_excl_scan(cnt, wsum, &tot);
-  for (int64_t w = w0; w < w1 && rank < need_eq; ++w) {
-    uint32_t e = eq[w];
-    while (e && rank < need_eq) {
-      const uint32_t b = e & (0u - e);
-      keep[w] |= b;
-      e ^= b;
-      ++rank;
+  uint32_t cnt, tot;
+  if (!all_eq) {
+    cnt = popc_run(eq);
+    uint32_t rank = block_excl_scan(cnt, wsum, &tot);
+    for (int64_t w = w0; w < w1 && rank < need_eq; ++w) {
+      uint32_t e = eq[w];
+      while (e && rank < need_eq) {
+        const uint32_t b = e & (0u - e);
+        keep[w] |= b;
+        e ^= b;
+        ++rank;
+      }
     }
+    __syncthreads();
   }
-  __syncthreads();
   cnt = popc_run(keep);
   uint32_t o = block_excl_scan(cnt, wsum, &tot);
   for (int64_t w4 = w0; w4 < w1; w4 += 4) {
