@@ -836,6 +836,12 @@ __global__ void __launch_bounds__(256) attend_qprep_kernel(AttendArgs a) {
   qprep_head(a, blockIdx.x, h, threadIdx.x & 63);
 }
 
+// Units of an MFMA attention launch: n_rows x n_splits (split, row) pairs padded to a
+// multiple of 8, times n_hg head groups (see attend_mx_kernel).
+__host__ __device__ __forceinline__ int mx_unit_count(int n_rows, int n_hg, int n_splits) {
+  return (n_rows * n_splits + 7) / 8 * 8 * n_hg;
+}
+
 // MODE 0: CSA (the row's selected entries), 1: HCA (all of the row's entries);
 // a compile-time copy of a.mode, so that the two attention kinds are distinct kernels.
 // QP: the queries come prepared in a.q_prep (no per-workgroup transform).
@@ -848,10 +854,22 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int pair = wave >> 1, half = wave & 1, partner = wave ^ 1;
-  // Workgroups take units (split, row, head group of 64), numbered split-major, with a
-  // static stride so that the work of a launch does not depend on scheduling.
+  // Workgroups take units (split, row, head group of 64) with a static stride, so that
+  // the work of a launch does not depend on scheduling.  The (split, row) pairs are
+  // numbered split-major; unit u is head group (u % 8n_hg) / 8 of pair 8(u / 8n_hg) +
+  // u % 8, so that the head groups of a pair, which read the same items, share u % 8:
+  // the XCD of a workgroup (with a grid that is a multiple of 8).  The unit space is
+  // padded to whole blocks of 8 pairs; padding units do nothing.
   const int n_hg = a.n_heads / 64, n_sp = a.split_min > 0 ? a.max_splits : 1;
-  const int n_units = a.n_rows * n_hg * n_sp;
+  const int n_pairs = a.n_rows * n_sp;
+  const int n_units = mx_unit_count(a.n_rows, n_hg, n_sp);
+  auto unit_of = [&](int u, int* split, int* r, int* hg) {
+    const int o = u % (8 * n_hg), p = u / (8 * n_hg) * 8 + (o & 7);
+    *hg = o >> 3;
+    *split = p / a.n_rows;
+    *r = p % a.n_rows;
+    return p < n_pairs;
+  };
   constexpr int CC = kD - kR;
   for (int i = tid; i < kD; i += 256) sh.gain[i] = a.q_gain[i];
 
@@ -914,7 +932,8 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
   constexpr int kPrologueTiles = C::kFp8 ? 2 : 1;
   float m_force = kNoMax;                              // != kNoMax: recompute the unit with this reference
   for (int unit = blockIdx.x; unit < n_units; unit += gridDim.x) {
-  const int split = unit / (a.n_rows * n_hg), r = (unit / n_hg) % a.n_rows, hg = unit % n_hg;
+  int split, r, hg;
+  if (!unit_of(unit, &split, &r, &hg)) continue;       // padding (workgroup-uniform)
   const RowInfo ri = row_info(a, r);
   const int ns = n_splits_of(a, ri.total);
   if (split >= ns) continue;
@@ -1002,8 +1021,8 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
     else
       mx_scores<kTwoChains>(tl + 32 * half * kPitch, qf, s, [](int) {});
     if (!C::kFp8 && tile == ntiles - 1 && unit + (int)gridDim.x < n_units) {
-      const int un = unit + gridDim.x;                 // prefetch the next unit's queries (bf16:
-      load_q((un / n_hg) % a.n_rows, un % n_hg);      // right after the last QK)
+      int s2, r2, h2;                                  // prefetch the next unit's queries (bf16:
+      if (unit_of(unit + gridDim.x, &s2, &r2, &h2)) load_q(r2, h2);   // right after the last QK)
     }
     float sv[16];
     float mx = -INFINITY;
@@ -1059,8 +1078,8 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
   }
 
   if (C::kFp8 && unit + (int)gridDim.x < n_units) {   // prefetch the next unit's queries (fp8:
-    const int un = unit + gridDim.x;                   // after the loop, whose top wait the
-    load_q((un / n_hg) % a.n_rows, un % n_hg);        // compiler cannot see)
+    int s2, r2, h2;                                    // after the loop, whose top wait the
+    if (unit_of(unit + gridDim.x, &s2, &r2, &h2)) load_q(r2, h2);   // compiler cannot see)
   }
   if (__builtin_expect(redo && m_force == kNoMax, 0)) {  // workgroup-uniform
     // a logit overflowed the reference: recompute the unit against the exact maximum
@@ -1209,7 +1228,7 @@ hipError_t launch_attend(const AttendArgs& args, hipStream_t st, bool q_prepared
     // of a batch with short rows take the low workgroup ids that are dispatched first, and
     // units a row does not have exit at once (a static stride would stack two real units
     // on some workgroups).
-    const long units = (long)a.n_rows * (a.n_heads / 64) * splits;
+    const long units = mx_unit_count(a.n_rows, a.n_heads / 64, splits);
     const long cap = splits > 1 && units <= 4L * cu_count() ? units : cu_count();
     dim3 grid((unsigned)(units < cap ? units : cap));
     const bool qp = a.q_prep != nullptr;
