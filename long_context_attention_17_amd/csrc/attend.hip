@@ -871,7 +871,8 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
     return p < n_pairs;
   };
   constexpr int CC = kD - kR;
-  for (int i = tid; i < kD; i += 256) sh.gain[i] = a.q_gain[i];
+  if constexpr (!QP)   // the query transform's gain (prepared queries have had it applied)
+    for (int i = tid; i < kD; i += 256) sh.gain[i] = a.q_gain[i];
 
   // Raw (or prepared) query rows (bf16 bits as B fragments: lane = head l%32, channels
   // 16s + 8(l/32) .. +7).  The next unit's rows are fetched early (after the last QK,
