@@ -511,16 +511,18 @@ struct MxShared {
   __attribute__((aligned(16))) float gain[kD];   // query RMSNorm gain
 };
 
-// Item table of a unit: items j0 .. j0 + n_tab - 1 as item_off gives them, built
+// Item table of a unit: items j0 .. j0 + n_tab - 1 as item_src reads them, built
 // in groups of kTabGroup items per thread, in phases, so that the dependent loads
 // of a group overlap (entry indices, CSA: the selected ones; then page-table
-// entries; then offsets).
+// entries; then offsets).  after_issue() runs once, right after the first group's
+// last loads are issued (the caller's own loads then queue behind them).
 constexpr int kTabGroup = 3;
-template <int MODE>
+template <int MODE, class F>
 __device__ __forceinline__ void mx_item_table(const AttendArgs& a, const RowInfo& ri, int r, int j0, int n_tab,
-                                              uint32_t* items) {
+                                              uint32_t* items, const F& after_issue) {
   const int tid = threadIdx.x;
   n_tab = __builtin_amdgcn_readfirstlane(n_tab);
+  if (n_tab <= 0) after_issue();
   for (int g0 = 0; g0 < n_tab; g0 += 256 * kTabGroup) {
     int32_t e[kTabGroup], pg[kTabGroup];
     // loads are unconditional (from clamped, in-range addresses) inside one
@@ -541,6 +543,7 @@ __device__ __forceinline__ void mx_item_table(const AttendArgs& a, const RowInfo
     }
 #pragma unroll
     for (int k = 0; k < kTabGroup; ++k) pg[k] = -1;
+    if (a.kv.max_pages <= 0 && g0 == 0) after_issue();
     if (a.kv.max_pages > 0) {
       int32_t x[kTabGroup];
       bool ok[kTabGroup];
@@ -551,6 +554,7 @@ __device__ __forceinline__ void mx_item_table(const AttendArgs& a, const RowInfo
         x[k] = a.kv.page_table[(int64_t)ri.seq * a.kv.max_pages + (ok[k] ? pi : 0)];
       }
       __builtin_amdgcn_sched_barrier(0);
+      if (g0 == 0) after_issue();
 #pragma unroll
       for (int k = 0; k < kTabGroup; ++k) pg[k] = ok[k] ? x[k] : -1;
     }
@@ -945,10 +949,10 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
   const int head0 = hg * 64 + 32 * pair;               // first head of this pair
   const int hl = lane & 31;                            // head (within the block) of this lane's S^T column
 
-  // ---- prologue.  Query loads (unless prefetched) go first: their latency overlaps
-  // the RoPE and item tables, and being older than the tile loads, waiting for them
+  // ---- prologue.  Query loads (unless prefetched) go out right behind the item
+  // table's last dependent loads (ahead of them they would delay that round trip):
+  // their transfer overlaps it, and being older than the tile loads, waiting for them
   // never waits for a tile.
-  if (q_row != r || q_hg != hg) load_q(r, hg);
   if (!qp && tid < kR / 2) {                           // (the table serves the transform and de-rotation)
     // angle t * theta_p with theta_p = rope_step^p (binary powering in fp64), taken in
     // revolutions and reduced exactly in fp64; the hardware sin / cos take revolutions
@@ -964,7 +968,11 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
     sh.rope_cs[2 * tid + 1] = __builtin_amdgcn_sinf(fr);
   }
   const int n_tab = (j1 - j0) < kMaxItems ? (j1 - j0) : kMaxItems;
-  mx_item_table<MODE>(a, ri, r, j0, n_tab, sh.items);
+  if (q_row != r || q_hg != hg)   // (workgroup-uniform; two straight-line copies, so that
+                                  // the wait for the table's loads does not wait for the queries)
+    mx_item_table<MODE>(a, ri, r, j0, n_tab, sh.items, [&]() { load_q(r, hg); });
+  else
+    mx_item_table<MODE>(a, ri, r, j0, n_tab, sh.items, []() {});
   // a valid, finite row used as the source of loads for rows without an item: the window token at t
   const uint8_t* dummy = (const uint8_t*)a.win + ((int64_t)ri.win_seq * a.W + ri.t % a.W) * kD * 2;
   __syncthreads();
