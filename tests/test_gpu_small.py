@@ -372,6 +372,17 @@ def test_decode_edge_contexts():
         run_decode(cfg, ctx=ctx)
 
 
+def test_decode_pooling_windows_off_the_load_batches():
+    """Compression ratios that are not multiples of the decode compressor's load batches
+    (8 positions at a time for short pooling windows, 32 for long ones): CSA m = 6 (twelve
+    positions with the overlap) and HCA m' = 48 (a batch of 32 and a partial one of 16), at
+    positions where one or both compressors emit an entry."""
+    ctx = [5, 47, 101, 143, 2399]
+    cfg = _cfg(name="odd_ratios", phase="decode", kv="fp8mix", n_h=64, m=6, m_hca=48, k=64, B=len(ctx),
+               ctx_lo=min(ctx), ctx_hi=max(ctx), L=0, seed=5454)
+    run_decode(cfg, ctx=ctx)
+
+
 def test_generic_decode_fp32_small():
     cfg = _cfg(name="small_decode_f32", phase="decode", D=64, R=8, n_h=8, act="f32", kv="f32", idx="f32", nI=4,
                cI=32, k=16, n_win=64, m_hca=64, B=4, ctx_lo=100, ctx_hi=900, L=0, seed=6161)
