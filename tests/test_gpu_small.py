@@ -383,6 +383,39 @@ def test_decode_pooling_windows_off_the_load_batches():
     run_decode(cfg, ctx=ctx)
 
 
+def test_decode_fp32_output_on_the_mfma_path():
+    """Split decode rows with an fp32 output and bf16 queries, window and entries: the MFMA
+    path with fp32 split partials and their combine.  They agree with the same call's bf16
+    output to bf16 rounding (of the output, and of the bf16 partials that call keeps)."""
+    ca, configs, layers, synth = _ca()
+    cfg = _cfg(name="f32_out_mfma", phase="decode", kv="fp8mix", n_h=128, k=512, m_hca=4, B=3, ctx_lo=2500,
+               ctx_hi=6000, L=0, seed=6262)
+    ctx = synth.decode_contexts(cfg)
+    for layer in ("hca", "csa"):
+        dl = layers.DecodeLayer(cfg, synth.decode_layer(cfg, layer, "cuda", ctx))
+        dl.step()
+        torch.cuda.synchronize()
+        n_items = (min(int(ctx.max()) // cfg.m, cfg.k) if layer == "csa" else int(ctx.max()) // cfg.m_hca) + cfg.n_win
+        assert ca.attend_decode_plan(dl.ap, n_items)[1] > 1, "the case must split rows"
+        p32 = ca.AttendParams.from_buffer_copy(dl.ap)
+        p32.out_format = ca.F32
+        out32 = torch.empty(dl.out.shape, dtype=torch.float32, device="cuda")
+        i = dl.inp
+        if layer == "csa":
+            ca.csa_attend_decode(p32, i["q"], i["g_q"], dl.kv, dl.idx, dl.cnt, cfg.m, dl.pos, dl.max_pos, dl.window,
+                                 i["sink"], out32)
+        else:
+            ca.hca_attend_decode(p32, i["q"], i["g_q"], dl.kv, cfg.m_hca, dl.pos, dl.max_pos, dl.window, i["sink"],
+                                 out32)
+        torch.cuda.synchronize()
+        ref = dl.out.float()
+        assert torch.isfinite(out32).all()
+        d = (out32 - ref).abs().max().item()
+        scale = ref.abs().max().item()
+        log(f"  {layer}: fp32 vs bf16 output max-abs {d:.3e} (output max {scale:.3e})")
+        assert d <= scale * 2.0 ** -7, f"{layer}: fp32-output decode differs beyond bf16 rounding"
+
+
 def test_generic_decode_fp32_small():
     cfg = _cfg(name="small_decode_f32", phase="decode", D=64, R=8, n_h=8, act="f32", kv="f32", idx="f32", nI=4,
                cI=32, k=16, n_win=64, m_hca=64, B=4, ctx_lo=100, ctx_hi=900, L=0, seed=6161)
