@@ -311,11 +311,11 @@ __global__ void __launch_bounds__(512) attend_combine_kernel(AttendArgs a) {
 
 // The same merge for partials of the MFMA path, which its epilogue writes in the
 // accumulator layout: per (row, split, 64-head group) a block
-// [pair][half][cb][v/4][lane][v%4] of fp32, element v of `lane` being head
-// 32*pair + 8(v/4) + 4(lane/32) + v%4 of the group and channel 256*half + 32*cb +
-// lane%32.  Workgroup = (row, head group, half, cb); thread (pair, v/4, lane) reads
-// one 16-byte run per split (heads h0 .. h0+3, one channel), so every wavefront
-// load is 1 KB contiguous.  The per-(split, head) weights exp2(m_s - M) and the
+// [pair][half][cb][v/4][lane][v%4] of fp32 (or bf16), element v of `lane` being
+// channel 256*half + 32*cb + 8(v/4) + 4(lane/32) + v%4 of head 32*pair + lane%32 of
+// the group.  Workgroup = (row, head group, half, cb); thread (pair, v/4, lane)
+// reads one run per split (4 channels of one head), so every wavefront load is 1 KB
+// (512 B) contiguous.  The per-(split, head) weights exp2(m_s - M) and the
 // per-head denominators are formed once per workgroup in LDS (8 threads per head,
 // each over every 8th split, reduced in a fixed order), while the first splits'
 // partial rows are already in flight.
@@ -330,9 +330,9 @@ __global__ void __launch_bounds__(512) attend_combine_acc_kernel(AttendArgs a) {
   const int r = blockIdx.x, n_hg = a.n_heads >> 6, n_ms = a.max_splits;
   const int hg = blockIdx.y >> 4, half = (blockIdx.y >> 3) & 1, cb = blockIdx.y & 7;
   const int t = threadIdx.x, pair = t >> 8, vq = (t >> 6) & 3, lane = t & 63;
-  const int hq = 32 * pair + 8 * vq + 4 * (lane >> 5);  // first of the thread's 4 heads in the group
-  const int h0 = hg * 64 + hq;                          // heads h0 .. h0+3
-  const int c = 256 * half + 32 * cb + (lane & 31);
+  const int hq = 32 * pair + (lane & 31);               // the thread's head in the group
+  const int h = hg * 64 + hq;
+  const int c = 256 * half + 32 * cb + 8 * vq + 4 * (lane >> 5);   // first of its 4 channels
   auto o_at = [&](int s) {                             // the thread's run of split s, as loaded
     const int64_t e = (((int64_t)r * n_ms + s) * n_hg + hg) * (64 * D) + (pair * 2 + half) * 8192 +
                       (cb * 4 + vq) * 256 + 4 * lane;
@@ -346,9 +346,7 @@ __global__ void __launch_bounds__(512) attend_combine_acc_kernel(AttendArgs a) {
   const int hh = t & 63, g = t >> 6;
   const int pos_r = a.pos != nullptr ? a.pos[r] : 0, cnt_r = a.mode == 0 ? a.cnt[r] : 0;
   const float sink_h = a.sink[hg * 64 + hh] * kLog2e;
-  f32x4 sink4;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) sink4[e] = a.sink[h0 + e] * kLog2e;
+  const float sink_own = a.sink[h] * kLog2e;
   PartRun<BF> os[kCombineUnroll];
 #pragma unroll
   for (int s = 0; s < kCombineUnroll; ++s) os[s] = o_at(s < n_ms ? s : n_ms - 1);
@@ -391,64 +389,60 @@ __global__ void __launch_bounds__(512) attend_combine_acc_kernel(AttendArgs a) {
     if (g == 0) M_s[hh] = M;
     __syncthreads();
   }
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f}, M, den;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  const float M = M_s[hq];
+  float den = exp2f(sink_own - M);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    M[e] = M_s[hq + e];
-    float d = exp2f(sink4[e] - M[e]);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) d += red2[i][hq + e];
-    den[e] = d;
-  }
-  auto weights = [&](int s) {
-    if (s < kCombineLdsSplits) return *(const f32x4*)&w_s[s][hq];
-    f32x4 w;
-    const int64_t b = ((int64_t)r * a.max_splits + s) * a.n_heads + h0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = exp2f(a.part_ml[2 * (b + e)] - M[e]);
-    return w;
+  for (int i = 0; i < 8; ++i) den += red2[i][hq];
+  auto weight = [&](int s) {
+    if (s < kCombineLdsSplits) return w_s[s][hq];
+    return exp2f(a.part_ml[2 * (((int64_t)r * a.max_splits + s) * a.n_heads + h)] - M);
   };
 #pragma unroll
   for (int s = 0; s < kCombineUnroll; ++s) {
     if (s < ns) {
-      const f32x4 w = weights(s), o = widen_part_run<BF>(os[s]);
+      const float w = weight(s);
+      const f32x4 o = widen_part_run<BF>(os[s]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] += o[e] * w[e];
+      for (int e = 0; e < 4; ++e) acc[e] += o[e] * w;
     }
   }
   for (int s = kCombineUnroll; s < ns; ++s) {
-    const f32x4 o = widen_part_run<BF>(o_at(s)), w = weights(s);
+    const f32x4 o = widen_part_run<BF>(o_at(s));
+    const float w = weight(s);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] += o[e] * w[e];
+    for (int e = 0; e < 4; ++e) acc[e] += o[e] * w;
   }
   f32x4 v;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) v[e] = acc[e] / den[e];
-  if (c >= C) {                                        // rotary pair (c & ~1, c | 1) sits in lanes l, l^1
-    const int p = (c - C) >> 1;
-    double th = 1.0, bp = a.rope_step;
-    for (int k = 0; (p >> k) != 0; ++k) {
-      th = ((p >> k) & 1) ? th * bp : th;
-      bp *= bp;
-    }
-    const double rev = (double)ri.t * th * 0.15915494309189535;   // 1 / (2 pi)
-    const float fr = (float)(rev - floor(rev));
-    const float co = __builtin_amdgcn_cosf(fr), sn = __builtin_amdgcn_sinf(fr);
+  for (int e = 0; e < 4; ++e) v[e] = acc[e] / den;
+  if (c >= C) {                                        // rotary pairs (c, c + 1), (c + 2, c + 3): rotate by R_{-t}
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float other = __shfl_xor(v[e], 1, 64);
-      v[e] = (lane & 1) ? v[e] * co - other * sn : v[e] * co + other * sn;
+    for (int e = 0; e < 4; e += 2) {
+      const int p = (c + e - C) >> 1;
+      double th = 1.0, bp = a.rope_step;
+      for (int k = 0; (p >> k) != 0; ++k) {
+        th = ((p >> k) & 1) ? th * bp : th;
+        bp *= bp;
+      }
+      const double rev = (double)ri.t * th * 0.15915494309189535;   // 1 / (2 pi)
+      const float fr = (float)(rev - floor(rev));
+      const float co = __builtin_amdgcn_cosf(fr), sn = __builtin_amdgcn_sinf(fr);
+      const float x0 = v[e], x1 = v[e + 1];
+      v[e] = x0 * co + x1 * sn;
+      v[e + 1] = x1 * co - x0 * sn;
     }
   }
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int64_t oi = ((int64_t)r * a.n_heads + h0 + e) * D + c;
-    if (a.out_fmt == CA_F32) ((float*)a.out)[oi] = v[e];
-    else ((uint16_t*)a.out)[oi] = f32_to_bf16_bits(v[e]);
+  const int64_t oi = ((int64_t)r * a.n_heads + h) * D + c;
+  if (a.out_fmt == CA_F32) {
+    *(f32x4*)((float*)a.out + oi) = v;
+  } else {
+    u32x2 w;
+    w[0] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)v[0], (__bf16)v[1]});
+    w[1] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)v[2], (__bf16)v[3]});
+    *(u32x2*)((uint16_t*)a.out + oi) = w;
   }
-  if (a.lse && half == 0 && cb == 0 && (lane & 31) == 0)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) a.lse[(int64_t)r * a.n_heads + h0 + e] = (M[e] + log2f(den[e])) / kLog2e;
+  if (a.lse && half == 0 && cb == 0 && vq == 0 && lane < 32) a.lse[(int64_t)r * a.n_heads + h] = (M + log2f(den)) / kLog2e;
 }
 
 // ======================================================================== MFMA (D = 512)
@@ -461,12 +455,16 @@ __global__ void __launch_bounds__(512) attend_combine_acc_kernel(AttendArgs a) {
 //   * scores the items 32*half .. +31 of the tile over all 512 channels:
 //     S^T = K Q^T, items on the rows, so element v of lane l is the logit of head
 //     l%32 for item 8*(v/4) + 4*(l/32) + v%4 (queries stay in registers);
-//   * accumulates O for the channels 256*half .. +255 over all 64 items, with its
-//     own probabilities and its partner's, swapped through LDS as bf16 A
-//     fragments.  The lane's 16 probabilities are directly the A operand for the
-//     k-slot order {items 0-3, 8-11 | 4-7, 12-15} (and +16); V is fed in the same
-//     order with LDS transpose loads (ds_read_b64_tr_b16: a 16-lane group reading
-//     a 4-row x 16-column block gets one column per lane).
+//   * accumulates O^T = V^T P^T for the channels 256*half .. +255 over all 64
+//     items, with its own probabilities and its partner's, swapped through LDS as
+//     bf16 fragments.  The lane's 16 probabilities are directly the B operand (P^T:
+//     column = head l%32) for the k-slot order {items 0-3, 8-11 | 4-7, 12-15} (and
+//     +16); V^T is the A operand, fed in the same order with LDS transpose loads
+//     (ds_read_b64_tr_b16: a 16-lane group reading a 4-row x 16-column block gets
+//     one column per lane).  Element v of lane l of column block cb is then channel
+//     32*cb + 8*(v/4) + 4*(l/32) + v%4 of head l%32: a lane holds runs of 4
+//     channels of its own head, so the epilogue scales, de-rotates and stores them
+//     with no exchange between lanes.
 // A pair keeps one softmax reference max; the rare move of it is decided
 // workgroup-wide so that its extra exchange can use a barrier.
 constexpr int kD = 512;
@@ -501,7 +499,7 @@ struct MxShared {
   typedef MxCfg<KV_FMT> C;
   __attribute__((aligned(16))) uint8_t ring[C::kStages][C::kStageBytes];
   __attribute__((aligned(16))) __bf16 tile[C::kFp8 ? kRows * kPitch : 8];
-  __attribute__((aligned(16))) bf16x8 pex[4][64][2];    // probabilities of each wavefront (A fragments)
+  __attribute__((aligned(16))) bf16x8 pex[4][64][2];    // probabilities of each wavefront (P^T fragments)
   uint32_t items[kMaxItems];            // item sources: pool record index, or kWinFlag | window row
   uint32_t valid[C::kStages][4];        // bit u of valid[st][w]: ring row w + 4u holds a real item
   float tmx[4][32];                     // per-head tile max of each wavefront
@@ -768,9 +766,9 @@ __device__ __forceinline__ void mx_scores(const __bf16* kt, const bf16x8* qf, f3
   s_out = acc;
 }
 
-// O (32 heads x 256 channels, 8 column blocks) += P V over the 64 items of a
+// O^T (256 channels in 8 blocks of 32 x 32 heads) += V^T P^T over the 64 items of a
 // tile: for each 32-item half (pown: this wavefront's items, ppar: its partner's),
-// two k-steps of 16 items x 8 column blocks; V fragments (two transpose loads
+// two k-steps of 16 items x 8 channel blocks; V fragments (two transpose loads
 // each) read kPf MFMAs ahead.
 __device__ __forceinline__ void mx_pv(const __bf16* tile, int half, const bf16x8* pown, const bf16x8* ppar,
                                       f32x16* o) {
@@ -798,7 +796,7 @@ __device__ __forceinline__ void mx_pv(const __bf16* tile, int half, const bf16x8
       vc[n % kPf] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vc0 + rowbase(m) * kPitch + 32 * (m & 7)));
     }
     const bf16x8 pa = (n >> 4) ? ppar[(n >> 3) & 1] : pown[(n >> 3) & 1];
-    o[n & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, vv, o[n & 7], 0, 0, 0);
+    o[n & 7] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pa, o[n & 7], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -814,10 +812,7 @@ __device__ __forceinline__ void mx_zero(f32x16* o) {
   for (int cb = 0; cb < 8; ++cb) o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(z, z, zc, 0, 0, 0);
 }
 
-// Head (within a 32-head block) of element v of a C-layout accumulator in `lane`.
-__device__ __forceinline__ int mx_row_of(int v, int lane) { return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3); }
-
-// exp2 of the masked logits against the reference, as bf16 A fragments; returns the fp32 sum.
+// exp2 of the masked logits against the reference, as bf16 P^T fragments; returns the fp32 sum.
 __device__ __forceinline__ float mx_probs(const float* sv, float m_run, bf16x8* pa) {
   float p[16];
 #pragma unroll
@@ -1109,17 +1104,11 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
   __syncthreads();                                     // also: every wavefront is done with the tiles
   const float l_tot = l_own + sh.lsum[partner][hl];
   const int c0 = 256 * half;                           // first channel of this wavefront's O
-  // O goes out through an LDS staging block per wavefront ([32 heads][256 channels]
-  // fp32, row pitch kStage floats; the ring is free now), so that global stores are
-  // whole 16 B (fp32) or 8 B (bf16) runs along the channels.
-  constexpr int kStage = 260;
-  static_assert(sizeof(sh.ring) + sizeof(sh.tile) >= 4 * 32 * kStage * 4, "staging buffer");
-  float* stage = (float*)&sh.ring[0][0] + wave * 32 * kStage;
   const bool split_out = a.split_min > 0;
   if (split_out) {
     // split partials go out in the accumulator layout (the combine kernel reads it):
-    // per (row, split, head group) a block [pair][half][cb][v/4][lane][v%4] of fp32,
-    // so that each store instruction writes 1 KB contiguous and nothing is staged
+    // per (row, split, head group) a block [pair][half][cb][v/4][lane][v%4] of fp32
+    // (or bf16), so that each store instruction writes 1 KB (512 B) contiguous
     const int64_t pbase = ((int64_t)r * a.max_splits + split) * a.n_heads + head0;
     if (half == 0 && lane < 32) {
       a.part_ml[2 * (pbase + hl)] = m_run;
@@ -1150,44 +1139,41 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
     __syncthreads();                                   // the next unit reuses the LDS
     continue;
   }
-  float fv[16];
-  {
-    const float sk_own = a.sink[head0 + hl] * kLog2e;
-    const float M_own = fmaxf(m_run, sk_own);
-    const float den_own = l_tot * __builtin_amdgcn_exp2f(m_run - M_own) + __builtin_amdgcn_exp2f(sk_own - M_own);
-    const float f_own = __builtin_amdgcn_exp2f(m_run - M_own) / den_own;
-    if (a.lse && half == 0 && lane < 32) a.lse[(int64_t)r * a.n_heads + head0 + hl] = (M_own + log2f(den_own)) / kLog2e;
+  // The lane's O^T elements are its own head's: scaled by the head's factor, the
+  // rotary channels 448..511 rotated by R_{-t} within the lane (pairs (2p, 2p + 1)
+  // are elements v, v + 1 with v even), and stored as runs of 4 channels (8 B bf16 or
+  // 16 B fp32; lanes l and l + 32 write adjacent runs).
+  const float sk_own = a.sink[head0 + hl] * kLog2e;
+  const float M_own = fmaxf(m_run, sk_own);
+  const float den_own = l_tot * __builtin_amdgcn_exp2f(m_run - M_own) + __builtin_amdgcn_exp2f(sk_own - M_own);
+  const float f_own = __builtin_amdgcn_exp2f(m_run - M_own) / den_own;
+  if (a.lse && half == 0 && lane < 32) a.lse[(int64_t)r * a.n_heads + head0 + hl] = (M_own + log2f(den_own)) / kLog2e;
+  const int64_t ob = ((int64_t)r * a.n_heads + head0 + hl) * kD + c0 + 4 * (lane >> 5);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) fv[v] = __shfl(f_own, mx_row_of(v, lane), 64);
-  }
+  for (int cb = 0; cb < 8; ++cb) {
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
+    for (int vq = 0; vq < 4; ++vq) {
+      f32x4 x;
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb) {
-      float x = oacc[cb][v] * fv[v];
-      if (c0 + 32 * cb >= CC) {                        // rotary channels 448..511: rotate by R_{-t}
-        const float other = __shfl_xor(x, 1, 64);
-        const int p = (c0 + 32 * cb + (lane & 31) - CC) >> 1;
-        const float c = sh.rope_cs[2 * p], sn = sh.rope_cs[2 * p + 1];
-        x = (lane & 1) ? x * c - other * sn : x * c + other * sn;
+      for (int e = 0; e < 4; ++e) x[e] = oacc[cb][4 * vq + e] * f_own;
+      if (c0 + 32 * cb >= CC) {                        // (wavefront-uniform)
+        const int p0 = (c0 + 32 * cb + 8 * vq + 4 * (lane >> 5) - CC) >> 1;
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+          const float c = sh.rope_cs[2 * (p0 + e / 2)], sn = sh.rope_cs[2 * (p0 + e / 2) + 1];
+          const float x0 = x[e], x1 = x[e + 1];
+          x[e] = x0 * c + x1 * sn;
+          x[e + 1] = x1 * c - x0 * sn;
+        }
       }
-      stage[mx_row_of(v, lane) * kStage + 32 * cb + (lane & 31)] = x;
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0xc07f);                  // lgkmcnt(0): this wavefront's staging writes
-  __builtin_amdgcn_wave_barrier();
-  // row h: 64 lanes x 4 channels
-  for (int h = 0; h < 32; ++h) {
-    const f32x4 x = *(const f32x4*)(stage + h * kStage + 4 * lane);
-    {
-      const int64_t ob = ((int64_t)r * a.n_heads + head0 + h) * kD + c0 + 4 * lane;
+      const int64_t o = ob + 32 * cb + 8 * vq;
       if (a.out_fmt == CA_F32) {
-        *(f32x4*)((float*)a.out + ob) = x;
+        *(f32x4*)((float*)a.out + o) = x;
       } else {
         u32x2 w;
         w[0] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)x[0], (__bf16)x[1]});
         w[1] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)x[2], (__bf16)x[3]});
-        *(u32x2*)((uint16_t*)a.out + ob) = w;
+        *(u32x2*)((uint16_t*)a.out + o) = w;
       }
     }
   }
