@@ -360,7 +360,8 @@ size_t ca_attend_workspace(const ca_attend_params* p, int32_t n_rows, int64_t ma
   size_t po = (size_t)n_rows * ms * p->n_heads * p->dim * esz;
   size_t pm = (size_t)n_rows * ms * p->n_heads * 2 * sizeof(float);
   size_t pq = (size_t)n_rows * p->n_heads * p->dim * 2;   // prepared bf16 queries
-  return align256(po) + align256(pm) + align256(pq);
+  size_t pi = (size_t)n_rows * p->n_heads * sizeof(float);  // their RMSNorm factors
+  return align256(po) + align256(pm) + align256(pq) + align256(pi);
 }
 
 // ------------------------------------------------------------------ decode state
@@ -533,6 +534,7 @@ static int attend_common(const ca_attend_params* p, const void* q, const float* 
   a.part_o = nullptr;
   a.part_ml = nullptr;
   a.q_prep = nullptr;
+  a.q_inv = nullptr;
   // Split the item list of each row into chunks by a plan that depends on the row
   // alone (ca::split_plan_len): always for decode, and for prefill when a row can be
   // longer than one MFMA workgroup's item table.
@@ -549,7 +551,8 @@ static int attend_common(const ca_attend_params* p, const void* q, const float* 
     const size_t po = align256((size_t)n_rows * ms * p->n_heads * p->dim * (p->out_format == CA_BF16 ? 2 : 4));
     const size_t pm = align256((size_t)n_rows * ms * p->n_heads * 2 * sizeof(float));
     const size_t pq = align256((size_t)n_rows * p->n_heads * p->dim * 2);
-    const size_t need = po + pm + pq;
+    const size_t pi = align256((size_t)n_rows * p->n_heads * sizeof(float));
+    const size_t need = po + pm + pq + pi;
     if (ws_bytes < need || ws == nullptr)
       return fail(CA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes (rows of up to %lld items are split)", what,
                   ws_bytes, need, (long long)max_items);
@@ -558,7 +561,10 @@ static int attend_common(const ca_attend_params* p, const void* q, const float* 
     a.max_splits = ms;
     a.part_o = (float*)ws;
     a.part_ml = (float*)((char*)ws + po);
-    if (ca::attend_mfma_supported(a)) a.q_prep = (uint16_t*)((char*)ws + po + pm);
+    if (ca::attend_mfma_supported(a)) {
+      a.q_prep = (uint16_t*)((char*)ws + po + pm);
+      a.q_inv = (float*)((char*)ws + po + pm + pq);
+    }
   }
   if (plan) {
     *plan = a;

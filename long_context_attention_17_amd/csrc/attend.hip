@@ -506,7 +506,7 @@ struct MxShared {
   __attribute__((aligned(16))) int bump[4];   // wavefront wants to move its reference max
   float lsum[4][32];                    // epilogue: per-head probability sums
   float rope_cs[kR];                    // (cos, sin) of t * theta_p, p < R/2
-  __attribute__((aligned(16))) float gain[kD];   // query RMSNorm gain
+  __attribute__((aligned(16))) float gain[kD];   // query RMSNorm gain x logit scale x log2(e)
 };
 
 // Item table of a unit: items j0 .. j0 + n_tab - 1 as item_src reads them, built
@@ -812,12 +812,13 @@ __device__ __forceinline__ void mx_zero(f32x16* o) {
   for (int cb = 0; cb < 8; ++cb) o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(z, z, zc, 0, 0, 0);
 }
 
-// exp2 of the masked logits against the reference, as bf16 P^T fragments; returns the fp32 sum.
-__device__ __forceinline__ float mx_probs(const float* sv, float m_run, bf16x8* pa) {
+// exp2 of the masked logits (times the head's factor qinv) against the reference, as
+// bf16 P^T fragments; returns the fp32 sum.
+__device__ __forceinline__ float mx_probs(const float* sv, float qinv, float m_run, bf16x8* pa) {
   float p[16];
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
-    p[v] = __builtin_amdgcn_exp2f(sv[v] - m_run);
+    p[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[v], qinv, -m_run));
     pa[v >> 3][v & 7] = (__bf16)p[v];
   }
 #pragma unroll
@@ -843,7 +844,8 @@ __host__ __device__ __forceinline__ int mx_unit_count(int n_rows, int n_hg, int 
 
 // MODE 0: CSA (the row's selected entries), 1: HCA (all of the row's entries);
 // a compile-time copy of a.mode, so that the two attention kinds are distinct kernels.
-// QP: the queries come prepared in a.q_prep (no per-workgroup transform).
+// QP: the queries come prepared in a.q_prep, their RMSNorm factors in a.q_inv (no
+// per-workgroup transform).
 template <int KV_FMT, int MODE, bool QP>
 __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
   a.mode = MODE;
@@ -870,37 +872,31 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
     return p < n_pairs;
   };
   constexpr int CC = kD - kR;
-  if constexpr (!QP)   // the query transform's gain (prepared queries have had it applied)
-    for (int i = tid; i < kD; i += 256) sh.gain[i] = a.q_gain[i];
+  if constexpr (!QP)   // the query transform's factors (prepared queries have had them applied)
+    for (int i = tid; i < kD; i += 256) sh.gain[i] = a.q_gain[i] * a.scale_log2;
 
   // Raw (or prepared) query rows (bf16 bits as B fragments: lane = head l%32, channels
   // 16s + 8(l/32) .. +7).  The next unit's rows are fetched early (after the last QK,
   // or after the tile loop), so their latency hides behind the unit's end.
   bf16x8 qf[32];
+  float qf_inv = 1.0f;                                 // prepared rows: the row's RMSNorm factor
   int q_row = -1, q_hg = -1;                           // rows held in qf
   constexpr bool qp = QP;                              // queries come prepared (split rows)
   auto load_q = [&](int rr, int hh) {
-    const uint16_t* qrow = (qp ? a.q_prep : (const uint16_t*)a.q) +
-                           ((int64_t)rr * a.n_heads + hh * 64 + 32 * pair + (lane & 31)) * kD + 8 * (lane >> 5);
+    const int64_t qi = (int64_t)rr * a.n_heads + hh * 64 + 32 * pair + (lane & 31);
+    const uint16_t* qrow = (qp ? a.q_prep : (const uint16_t*)a.q) + qi * kD + 8 * (lane >> 5);
+    if constexpr (qp) qf_inv = a.q_inv[qi];
 #pragma unroll
     for (int s = 0; s < 32; ++s) qf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qrow + 16 * s));
     q_row = rr;
     q_hg = hh;
   };
-  // RMSNorm with gain, RoPE at t (table in sh.rope_cs), logit scale * log2(e), in place.
+  // RMSNorm with gain, RoPE at t (table in sh.rope_cs), logit scale * log2(e), in place
+  // and in one pass: the rows are stored without the norm's 1 / rms (x * gain * scale,
+  // rotated), which is returned and applied to the head's logits instead (a per-head
+  // factor commutes with the rotation and the dot products).
   auto transform_q = [&]() {
     float ss = 0.0f;
-#pragma unroll
-    for (int s = 0; s < 32; ++s) {
-      const u32x4 w = __builtin_bit_cast(u32x4, qf[s]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float x0 = __uint_as_float(w[e] << 16), x1 = __uint_as_float(w[e] & 0xFFFF0000u);
-        ss += x0 * x0 + x1 * x1;
-      }
-    }
-    ss += __shfl_xor(ss, 32, 64);
-    const float inv = 1.0f / sqrtf(ss / (float)kD + a.eps);
 #pragma unroll
     for (int s = 0; s < 32; ++s) {
       const int d0 = 16 * s + 8 * (lane >> 5);
@@ -913,7 +909,10 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
         x[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] *= inv * (e < 4 ? g0[e] : g1[e - 4]);
+      for (int e = 0; e < 8; ++e) {
+        ss += x[e] * x[e];
+        x[e] *= e < 4 ? g0[e] : g1[e - 4];
+      }
       if (d0 >= CC) {
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
@@ -924,9 +923,13 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
           x[e + 1] = x0 * sn + x1 * c;
         }
       }
+      u32x4 o;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qf[s][e] = (__bf16)(x[e] * a.scale_log2);
+      for (int e = 0; e < 4; ++e) o[e] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)x[2 * e], (__bf16)x[2 * e + 1]});
+      qf[s] = __builtin_bit_cast(bf16x8, o);
     }
+    ss += __shfl_xor(ss, 32, 64);
+    return 1.0f / sqrtf(ss / (float)kD + a.eps);
   };
 
   constexpr int kPrologueTiles = C::kFp8 ? 2 : 1;
@@ -981,7 +984,8 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
     is.all();
   }
 
-  if constexpr (!qp) transform_q();
+  float qinv = qf_inv;                                 // logit factor of the lane's head (1 / rms)
+  if constexpr (!qp) qinv = transform_q();
   q_row = -1;                                          // qf now holds transformed queries
 
   // Softmax reference: m_run is set by the first tile with a valid item (O is still
@@ -1044,12 +1048,13 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
         mx = fmaxf(mx, sv[v]);
       }
     }
+    mx *= qinv;                                        // (sv: logits before the head's factor)
     // a logit above the reference by more than kBump anywhere in the workgroup?  (Any
     // lane's own maximum will do: no per-head maximum is formed on the common path.)
     const bool bump = __any(mx > m_run + kBump);
     m_loc = fmaxf(m_loc, mx);
     bf16x8 pown[2];
-    float psum = mx_probs(sv, m_run, pown);
+    float psum = mx_probs(sv, qinv, m_run, pown);
     *(bf16x8*)&sh.pex[wave][lane][0] = pown[0];
     *(bf16x8*)&sh.pex[wave][lane][1] = pown[1];
     if (lane == 0) sh.bump[wave] = bump;
@@ -1067,7 +1072,7 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
         if (lane < 32) sh.tmx[wave][lane] = tmax;
         __syncthreads();                               // every wavefront has read the exchange
         m_run = fmaxf(tmax, sh.tmx[partner][hl]);
-        psum = mx_probs(sv, m_run, pown);
+        psum = mx_probs(sv, qinv, m_run, pown);
         *(bf16x8*)&sh.pex[wave][lane][0] = pown[0];
         *(bf16x8*)&sh.pex[wave][lane][1] = pown[1];
         __syncthreads();

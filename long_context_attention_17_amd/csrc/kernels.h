@@ -116,8 +116,10 @@ struct AttendArgs {
   float* part_ml;      // [rows, max_splits, n_heads, 2]
   int part_acc;        // 1: part_o is in the MFMA kernel's accumulator layout (see attend_combine_kernel)
   int part_bf16;       // 1 (bf16 output): part_o holds bf16 values at the same element offsets
-  uint16_t* q_prep;    // nullptr, or bf16 [rows, n_heads, D]: queries normalized, rotated and scaled
-                       // once per row by a prep kernel (split rows of the MFMA path)
+  uint16_t* q_prep;    // nullptr, or bf16 [rows, n_heads, D]: queries times gain and logit scale,
+                       // rotated, once per row by a prep kernel (split rows of the MFMA path)
+  float* q_inv;        // with q_prep: [rows, n_heads], each query row's RMSNorm factor 1 / rms,
+                       // which scales its logits (q_prep holds the row without it)
 };
 
 // Split plan of a row of `total` items, a function of the row alone (so a decode

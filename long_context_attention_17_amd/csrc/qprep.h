@@ -1,8 +1,11 @@
 // Query preparation of split (decode) rows for the MFMA attention path, shared by
 // attend_qprep_kernel and the fused decode front kernel: RMSNorm with gain, RoPE at
-// the row's position, logit scale * log2(e), in bf16 -- once per (row, head) instead
-// of once per split (dsv4 book Ch.7 "Query and KV RMSNorm", "Partial RoPE and output
-// de-rotation").  One wavefront per (row, head), lane l holding channels 8l .. 8l+7.
+// the row's position, logit scale * log2(e) -- once per (row, head) instead of once
+// per split (dsv4 book Ch.7 "Query and KV RMSNorm", "Partial RoPE and output
+// de-rotation").  The row is stored in bf16 without the norm's factor 1 / rms
+// (x * gain * scale, rotated), which goes to q_inv and scales the head's logits: the
+// same rounding as the attention kernel's own transform of raw queries.  One
+// wavefront per (row, head), lane l holding channels 8l .. 8l+7.
 #pragma once
 #include "common.h"
 #include "kernels.h"
@@ -25,9 +28,9 @@ __device__ __forceinline__ void qprep_head(const AttendArgs& a, int r, int h, in
   for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
-  const float inv = 1.0f / sqrtf(ss / (float)kD + a.eps);
+  if (lane == 0) a.q_inv[(int64_t)r * a.n_heads + h] = 1.0f / sqrtf(ss / (float)kD + a.eps);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] *= inv * a.q_gain[8 * lane + e];
+  for (int e = 0; e < 8; ++e) x[e] *= a.q_gain[8 * lane + e] * a.scale_log2;
   if (8 * lane >= CC) {
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
@@ -49,7 +52,7 @@ __device__ __forceinline__ void qprep_head(const AttendArgs& a, int r, int h, in
   u32x4 o;
 #pragma unroll
   for (int e = 0; e < 4; ++e)
-    o[e] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)(x[2 * e] * a.scale_log2), (__bf16)(x[2 * e + 1] * a.scale_log2)});
+    o[e] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)x[2 * e], (__bf16)x[2 * e + 1]});
   *(u32x4*)(a.q_prep + off) = o;
 }
 
