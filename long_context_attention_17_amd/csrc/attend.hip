@@ -607,7 +607,8 @@ __device__ __forceinline__ void lds_load16(uint64_t g, uint32_t d) {
 // wavefront w, which issues exactly kLoadsPerWave instructions per tile, so
 // outstanding-load counts are the same for all tiles.  Rows without an item load
 // a finite dummy row and are masked.  fp8 stages take the first 592 B of every row
-// (a whole record); window rows of an fp8 workgroup are read by the dequantizer.
+// (a whole record); window rows of an fp8 workgroup reach the bf16 tile through
+// mx_convert's own loads (what their ring rows receive is never read).
 template <int KV_FMT>
 struct MxIssue {
   uint64_t src;       // lane u < kLoadsPerWave: source of row w + 4u
@@ -657,16 +658,18 @@ struct MxIssue {
 
 // fp8 records: dequantize a raw stage into the bf16 tile; wavefront w handles the
 // rows it = 4u + w (u < 16), whose LDS row is mx_row(it) = 16(u/4) + 4w + u%4.
-// Passes, each without a branch per row (a wavefront's LDS accesses take effect
-// in program order, so later passes overwrite earlier ones):
+// WIN: the tile reaches the window, whose rows (it >= n_c - jt: bf16 in global
+// memory) go straight into their bf16 tile rows as async global -> LDS loads,
+// issued first so that their one round trip overlaps the passes over the records
+// and awaited (vmcnt(0)) at the end; the passes then skip those rows.
+// Passes, each without a branch per row on the common path (a wavefront's LDS
+// accesses take effect in program order, so later passes overwrite earlier ones):
 //  1. content channels: lanes sl < 56 scale the 8 e4m3 codes of channels 8sl..8sl+7
 //     by the tile exponent of their 64-channel tile, in batches of four rows whose
 //     LDS reads are all issued before any conversion;
 //  2. rotary channels: the 16 rows' 128 B of bf16 copied by all 64 lanes;
-//  3. only for tiles with rows without an item: those rows are zeroed (finite V);
-//  4. only for tiles reaching the window: window rows (bf16 in global memory) are
-//     copied in, so that passes 1-3 have no global loads (nor waits on the loads
-//     in flight).
+//  3. only for tiles with rows without an item: those rows are zeroed (finite V).
+template <bool WIN>
 __device__ __forceinline__ void mx_convert(const AttendArgs& a, const uint8_t* raw, const uint32_t* valid,
                                            const uint32_t* items, int jt, int j0, int n_c, __bf16* tile) {
   constexpr int CC = kD - kR;
@@ -675,6 +678,25 @@ __device__ __forceinline__ void mx_convert(const AttendArgs& a, const uint8_t* r
   const uint8_t* rw = raw + wave * kRawPitch;            // row u of this wavefront: + 4u * kRawPitch
   __bf16* tw = tile + 4 * wave * kPitch;                 // row u: + (16(u/4) + u%4) * kPitch
   auto trow = [](int u) { return (16 * (u >> 2) + (u & 3)) * kPitch; };
+  int u_rec = kRows / 4;                                 // rows u < u_rec hold records (if valid)
+  if constexpr (WIN) {
+    const int n_rec = n_c - jt;                          // tile rows it < n_rec are records
+    u_rec = __builtin_amdgcn_readfirstlane(n_rec <= wave ? 0 : min(kRows / 4, (n_rec - wave + 3) >> 2));
+    // lane u < 16: source of row u if it is a window row (else window row 0, never loaded)
+    uint32_t off = kWinFlag;
+    if (sl < kRows / 4 && sl >= u_rec && ((vb >> sl) & 1u)) off = items[jt + 4 * sl + wave - j0];
+    const uint64_t src = (uint64_t)(uintptr_t)item_src(a, off);
+    typedef __attribute__((address_space(3))) __bf16 lds_bf16;
+    const uint32_t tb = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_bf16*)tw);
+#pragma unroll 1
+    for (int u = u_rec; u < kRows / 4; ++u) {
+      if ((vb >> u) & 1u) {                              // (wavefront-uniform)
+        const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)src, u);
+        const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(src >> 32), u);
+        lds_load16(((uint64_t)hi << 32) | lo, tb + 2u * (uint32_t)trow(u));
+      }
+    }
+  }
   if (sl < CC / 8) {
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
@@ -694,7 +716,7 @@ __device__ __forceinline__ void mx_convert(const AttendArgs& a, const uint8_t* r
         out[1] = __builtin_bit_cast(uint32_t, e4m3x2_to_bf16_scaled<true>(x[i][0], sc));
         out[2] = __builtin_bit_cast(uint32_t, e4m3x2_to_bf16_scaled<false>(x[i][1], sc));
         out[3] = __builtin_bit_cast(uint32_t, e4m3x2_to_bf16_scaled<true>(x[i][1], sc));
-        *(u32x4*)(tw + trow(4 * b + i) + 8 * sl) = out;
+        if (!WIN || 4 * b + i < u_rec) *(u32x4*)(tw + trow(4 * b + i) + 8 * sl) = out;
       }
     }
   }
@@ -703,35 +725,15 @@ __device__ __forceinline__ void mx_convert(const AttendArgs& a, const uint8_t* r
     const int c = sl & 7, u0 = sl >> 3;
     const u32x4 r0 = *(const u32x4*)(rw + 4 * u0 * kRawPitch + CC + 16 * c);
     const u32x4 r1 = *(const u32x4*)(rw + 4 * (u0 + 8) * kRawPitch + CC + 16 * c);
-    *(u32x4*)(tw + trow(u0) + CC + 8 * c) = r0;
-    *(u32x4*)(tw + trow(u0 + 8) + CC + 8 * c) = r1;
+    if (!WIN || u0 < u_rec) *(u32x4*)(tw + trow(u0) + CC + 8 * c) = r0;
+    if (!WIN || u0 + 8 < u_rec) *(u32x4*)(tw + trow(u0 + 8) + CC + 8 * c) = r1;
   }
   if (vb != 0xFFFFu) {                                   // rows without an item (uniform)
 #pragma unroll
     for (int u = 0; u < kRows / 4; ++u)
       if (!((vb >> u) & 1u)) *(u32x4*)(tw + trow(u) + 8 * sl) = u32x4{0u, 0u, 0u, 0u};
   }
-  const int n_rec = n_c - jt;                            // rows it < n_rec hold records (if valid)
-  if (jt + kRows > n_c) {                                // the tile reaches the window (uniform)
-    // groups of four rows: four unconditional loads (rows that are not window rows
-    // read the window's first row) out before the first store
-#pragma unroll 1
-    for (int b = 0; b < kRows / 16; ++b) {
-      u32x4 w[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int u = 4 * b + i, it = 4 * u + wave;
-        const bool win = it >= n_rec && ((vb >> u) & 1u);
-        const uint32_t off = items[win ? jt + it - j0 : 0];
-        w[i] = *(const u32x4*)(item_src(a, win ? off : kWinFlag) + 16 * sl);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int u = 4 * b + i, it = 4 * u + wave;
-        if (it >= n_rec && ((vb >> u) & 1u)) *(u32x4*)(tw + trow(u) + 8 * sl) = w[i];
-      }
-    }
-  }
+  if constexpr (WIN) __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the window rows have landed
 }
 
 // S^T (32 items x 32 heads) = K Q^T over the 512 channels: 32 MFMAs in one
@@ -1012,7 +1014,11 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
     const __bf16* tl;
     MxIssue<KV_FMT> is;
     if constexpr (C::kFp8) {
-      mx_convert(a, sh.ring[st], sh.valid[st], sh.items, j0 + tile * kRows, j0, ri.n_c, sh.tile);
+      const int jt = j0 + tile * kRows;
+      if (jt + kRows > ri.n_c)                         // (workgroup-uniform) the tile reaches the window
+        mx_convert<true>(a, sh.ring[st], sh.valid[st], sh.items, jt, j0, ri.n_c, sh.tile);
+      else
+        mx_convert<false>(a, sh.ring[st], sh.valid[st], sh.items, jt, j0, ri.n_c, sh.tile);
       __syncthreads();
       is.prepare(a, j0, j1, tile + 2, st, sh, dummy, tile + 2 < ntiles);
       tl = sh.tile;
