@@ -63,6 +63,18 @@ KERNEL_SOURCES = {"attend_mx_kernel": ["attend.hip", "common.h", "kernels.h"],
                   "gemm_skinny_kernel": ["proj.hip", "common.h", "kernels.h"]}
 
 
+def hca_dense_units(cfg, max_pos):
+    """Whether the HCA decode attention launch of this batch numbers its units densely: the
+    library does so for up to 64 rows when the padded unit space (rows x the most chunks
+    a row up to max_pos can get, in blocks of 8, per 64-head group) exceeds the CUs."""
+    from long_context_attention_17_amd import binding as ca, layers
+    if cfg.B > 64:
+        return False
+    max_chunks = ca.attend_decode_plan(layers.attend_params(cfg), max_pos // cfg.m_hca + cfg.n_win)[2]
+    units = (cfg.B * max_chunks + 7) // 8 * 8 * (cfg.n_h // 64)
+    return max_chunks > 1 and units > torch.cuda.get_device_properties(0).multi_processor_count
+
+
 def progress(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
@@ -283,10 +295,11 @@ def bench_decode(cfg, steps, warmup, replicas, args):
     kt, queued = time_kernels(step, {"csa_attend": ca.TIMED_CSA_ATTEND, "hca_attend": ca.TIMED_HCA_ATTEND,
                                      "index_scores": ca.TIMED_INDEX_SCORES}, max(steps, 20))
     fmt = 2 if cfg.kv == "fp8mix" else 1
+    dense = "true" if hca_dense_units(cfg, max(pos)) else "false"
     roof_of = {   # algorithmic work of one launch (the launch covers the whole batch)
         "index_scores": ("hbm", work["index_bytes"], index_kernel_symbol(cfg, 1)),
-        "csa_attend": ("mfma", work["csa_flops"], f"attend_mx_kernel<{fmt}, 0, true>"),
-        "hca_attend": ("mfma", work["hca_flops"], f"attend_mx_kernel<{fmt}, 1, true>"),
+        "csa_attend": ("mfma", work["csa_flops"], f"attend_mx_kernel<{fmt}, 0, true, false>"),
+        "hca_attend": ("mfma", work["hca_flops"], f"attend_mx_kernel<{fmt}, 1, true, {dense}>"),
     }
     dom = max(roof_of, key=lambda k: kt[k][0] * kt[k][1])
     bound, units, symbol = roof_of[dom]
@@ -395,7 +408,8 @@ def bench_prefill(cfg, steps, warmup, replicas, args):
     launch_ms = kt[dom][0]
     achieved = flops / (launch_ms / 1e3) / 1e12
     fmt = 2 if cfg.kv == "fp8mix" else 1
-    roof = {"kernel": f"attend_mx_kernel<{fmt}, {0 if dom == 'csa_attend' else 1}, false>", "stage": dom, "bound": "mfma",
+    roof = {"kernel": f"attend_mx_kernel<{fmt}, {0 if dom == 'csa_attend' else 1}, false, false>", "stage": dom,
+            "bound": "mfma",
             "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "launch_ms": round(launch_ms, 5), "work_per_launch": flops}
     extra = {"stages_ms": {k: round(v, 4) for k, v in st.items()},

@@ -34,16 +34,17 @@ struct RowInfo {
 
 // A decode row whose position lies outside [0, max_pos] is out of contract: it gets
 // no items (so nothing is read for it and its output is zero), position 0, and the
-// call's status word receives CA_STATUS_POS_RANGE.  pos_r and cnt_r: the row's
-// pos[r] and cnt[r] words as loaded (each read only when the call has that array).
-__device__ __forceinline__ RowInfo row_info_of(const AttendArgs& a, int r, int pos_r, int cnt_r) {
+// call's status word receives CA_STATUS_POS_RANGE (unless !report).  pos_r and cnt_r:
+// the row's pos[r] and cnt[r] words as loaded (each read only when the call has that array).
+__device__ __forceinline__ RowInfo row_info_of(const AttendArgs& a, int r, int pos_r, int cnt_r,
+                                               bool report = true) {
   RowInfo ri;
   bool ok = true;
   if (a.pos) {
     ri.t = pos_r;
     ok = ri.t >= 0 && ri.t <= a.max_pos;
     if (!ok) {
-      if (threadIdx.x == 0) raise_status(a.status, CA_STATUS_POS_RANGE);
+      if (report && threadIdx.x == 0) raise_status(a.status, CA_STATUS_POS_RANGE);
       ri.t = 0;
     }
   } else {
@@ -844,11 +845,49 @@ __host__ __device__ __forceinline__ int mx_unit_count(int n_rows, int n_hg, int 
   return (n_rows * n_splits + 7) / 8 * 8 * n_hg;
 }
 
+// Dense numbering of the real (split, row) pairs of a decode launch of at most 64
+// rows: pair q is split s of the k-th row, in row order, among the rows with more
+// than s splits.  Like the padded numbering it is split-major, but it leaves no gaps,
+// so the real units take the lowest workgroup ids and each XCD (block id mod 8) gets
+// an even share of them whatever the rows' lengths.  Every wavefront finds the same
+// answer on its own (lane = row; ballots, no LDS or barrier); *pos_r and *cnt_r
+// receive the row's words as loaded.
+__device__ __forceinline__ bool dense_pair(const AttendArgs& a, int q, int* split, int* r, int* pos_r,
+                                           int* cnt_r) {
+  const int lane = threadIdx.x & 63;
+  int ns = 0, pw = 0, cw = 0;
+  if (lane < a.n_rows) {
+    pw = a.pos[lane];
+    cw = a.mode == 0 ? a.cnt[lane] : 0;
+    const int n = split_plan_count32(row_info_of(a, lane, pw, cw, false).total, a.split_min, a.split_div,
+                                     a.split_cap);
+    ns = n < a.max_splits ? n : a.max_splits;         // as n_splits_of: 1 .. max_splits
+  }
+  int rem = q;
+  for (int s = 0; s < a.max_splits; ++s) {
+    const uint64_t b = __ballot(ns > s);               // the rows of level s
+    const int c = __popcll(b);
+    if (rem < c) {
+      // the rem-th set bit of b
+      const bool hit = ((b >> lane) & 1ull) && __popcll(b & ((1ull << lane) - 1ull)) == rem;
+      const int row = __ffsll((unsigned long long)__ballot(hit)) - 1;
+      *split = s;
+      *r = row;
+      *pos_r = __builtin_amdgcn_readlane(pw, row);
+      *cnt_r = __builtin_amdgcn_readlane(cw, row);
+      return true;
+    }
+    rem -= c;
+  }
+  return false;                                        // past the last real pair
+}
+
 // MODE 0: CSA (the row's selected entries), 1: HCA (all of the row's entries);
 // a compile-time copy of a.mode, so that the two attention kinds are distinct kernels.
 // QP: the queries come prepared in a.q_prep, their RMSNorm factors in a.q_inv (no
 // per-workgroup transform).
-template <int KV_FMT, int MODE, bool QP>
+// DENSE (HCA decode launches only): the real units are numbered by dense_pair.
+template <int KV_FMT, int MODE, bool QP, bool DENSE>
 __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
   a.mode = MODE;
   typedef MxCfg<KV_FMT> C;
@@ -863,12 +902,17 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
   // u % 8, so that the head groups of a pair, which read the same items, share u % 8:
   // the XCD of a workgroup (with a grid that is a multiple of 8).  The unit space is
   // padded to whole blocks of 8 pairs; padding units do nothing.
+  // Decode launches of up to 64 rows whose padded unit space exceeds the CUs number the
+  // pairs densely (dense_pair); the unit's row words then come from that search.
   const int n_hg = a.n_heads / 64, n_sp = a.split_min > 0 ? a.max_splits : 1;
   const int n_pairs = a.n_rows * n_sp;
   const int n_units = mx_unit_count(a.n_rows, n_hg, n_sp);
+  constexpr bool dense = DENSE;
+  int d_pos = 0, d_cnt = 0;
   auto unit_of = [&](int u, int* split, int* r, int* hg) {
     const int o = u % (8 * n_hg), p = u / (8 * n_hg) * 8 + (o & 7);
     *hg = o >> 3;
+    if (dense) return dense_pair(a, p, split, r, &d_pos, &d_cnt);
     *split = p / a.n_rows;
     *r = p % a.n_rows;
     return p < n_pairs;
@@ -939,7 +983,7 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
   for (int unit = blockIdx.x; unit < n_units; unit += gridDim.x) {
   int split, r, hg;
   if (!unit_of(unit, &split, &r, &hg)) continue;       // padding (workgroup-uniform)
-  const RowInfo ri = row_info(a, r);
+  const RowInfo ri = dense ? row_info_of(a, r, d_pos, d_cnt) : row_info(a, r);
   const int ns = n_splits_of(a, ri.total);
   if (split >= ns) continue;
   int j0, j1;
@@ -1034,7 +1078,7 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
       mx_scores<kTwoChains>(tl + 32 * half * kPitch, qf, s, [&](int u) { is.row(u); });
     else
       mx_scores<kTwoChains>(tl + 32 * half * kPitch, qf, s, [](int) {});
-    if (!C::kFp8 && tile == ntiles - 1 && unit + (int)gridDim.x < n_units) {
+    if (!C::kFp8 && !dense && tile == ntiles - 1 && unit + (int)gridDim.x < n_units) {
       int s2, r2, h2;                                  // prefetch the next unit's queries (bf16:
       if (unit_of(unit + gridDim.x, &s2, &r2, &h2)) load_q(r2, h2);   // right after the last QK)
     }
@@ -1092,7 +1136,7 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
     mx_pv(tl, half, pown, ppar, oacc);
   }
 
-  if (C::kFp8 && unit + (int)gridDim.x < n_units) {   // prefetch the next unit's queries (fp8:
+  if (C::kFp8 && !dense && unit + (int)gridDim.x < n_units) {   // prefetch the next unit's queries (fp8:
     int s2, r2, h2;                                    // after the loop, whose top wait the
     if (unit_of(unit + gridDim.x, &s2, &r2, &h2)) load_q(r2, h2);   // compiler cannot see)
   }
@@ -1236,25 +1280,41 @@ hipError_t launch_attend(const AttendArgs& args, hipStream_t st, bool q_prepared
     // on some workgroups).
     const long units = mx_unit_count(a.n_rows, a.n_heads / 64, splits);
     const long cap = splits > 1 && units <= 4L * cu_count() ? units : cu_count();
+    // Workgroups past the first one per CU start only as earlier ones finish, so when the
+    // padded unit space of a decode launch exceeds the CUs, rows with fewer splits than
+    // the most would leave gaps below that line and push real units above it: number the
+    // real units densely instead (dense_pair; up to 64 rows, one per lane).  HCA only:
+    // its rows' lengths follow their positions, while CSA rows from m * k tokens on all
+    // hold k + n_win items, so their padded numbering has no gaps (and the search would
+    // only add its cost).
+    a.dense_units = a.mode == 1 && a.pos != nullptr && splits > 1 && a.n_rows <= 64 && units > cu_count() ? 1 : 0;
     dim3 grid((unsigned)(units < cap ? units : cap));
     const bool qp = a.q_prep != nullptr;
+#define CA_MX(F, M, Q, DN) CA_LAUNCH((attend_mx_kernel<F, M, Q, DN>), grid, dim3(256), 0, st, ev0, ev1, a)
     if (a.kv.fmt == CA_FP8MIX) {
       if (a.mode == 0) {
-        if (qp) CA_LAUNCH((attend_mx_kernel<CA_FP8MIX, 0, true>), grid, dim3(256), 0, st, ev0, ev1, a);
-        else CA_LAUNCH((attend_mx_kernel<CA_FP8MIX, 0, false>), grid, dim3(256), 0, st, ev0, ev1, a);
+        if (qp) CA_MX(CA_FP8MIX, 0, true, false);
+        else CA_MX(CA_FP8MIX, 0, false, false);
+      } else if (a.dense_units) {
+        if (qp) CA_MX(CA_FP8MIX, 1, true, true);
+        else CA_MX(CA_FP8MIX, 1, false, true);
       } else {
-        if (qp) CA_LAUNCH((attend_mx_kernel<CA_FP8MIX, 1, true>), grid, dim3(256), 0, st, ev0, ev1, a);
-        else CA_LAUNCH((attend_mx_kernel<CA_FP8MIX, 1, false>), grid, dim3(256), 0, st, ev0, ev1, a);
+        if (qp) CA_MX(CA_FP8MIX, 1, true, false);
+        else CA_MX(CA_FP8MIX, 1, false, false);
       }
     } else {
       if (a.mode == 0) {
-        if (qp) CA_LAUNCH((attend_mx_kernel<CA_BF16, 0, true>), grid, dim3(256), 0, st, ev0, ev1, a);
-        else CA_LAUNCH((attend_mx_kernel<CA_BF16, 0, false>), grid, dim3(256), 0, st, ev0, ev1, a);
+        if (qp) CA_MX(CA_BF16, 0, true, false);
+        else CA_MX(CA_BF16, 0, false, false);
+      } else if (a.dense_units) {
+        if (qp) CA_MX(CA_BF16, 1, true, true);
+        else CA_MX(CA_BF16, 1, false, true);
       } else {
-        if (qp) CA_LAUNCH((attend_mx_kernel<CA_BF16, 1, true>), grid, dim3(256), 0, st, ev0, ev1, a);
-        else CA_LAUNCH((attend_mx_kernel<CA_BF16, 1, false>), grid, dim3(256), 0, st, ev0, ev1, a);
+        if (qp) CA_MX(CA_BF16, 1, true, false);
+        else CA_MX(CA_BF16, 1, false, false);
       }
     }
+#undef CA_MX
   } else {
     dim3 grid(a.n_rows, a.n_heads, splits);
     switch (a.D / 64) {

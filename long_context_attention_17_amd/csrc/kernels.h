@@ -116,6 +116,7 @@ struct AttendArgs {
   float* part_ml;      // [rows, max_splits, n_heads, 2]
   int part_acc;        // 1: part_o is in the MFMA kernel's accumulator layout (see attend_combine_kernel)
   int part_bf16;       // 1 (bf16 output): part_o holds bf16 values at the same element offsets
+  int dense_units;     // 1: the MFMA kernel numbers a decode launch's real units densely (set by launch_attend)
   uint16_t* q_prep;    // nullptr, or bf16 [rows, n_heads, D]: queries times gain and logit scale,
                        // rotated, once per row by a prep kernel (split rows of the MFMA path)
   float* q_inv;        // with q_prep: [rows, n_heads], each query row's RMSNorm factor 1 / rms,
@@ -137,6 +138,17 @@ __host__ __device__ __forceinline__ int split_plan_len(int64_t total, int split_
   int64_t len = (total + d - 1) / d;
   len = (len + 63) & ~(int64_t)63;
   return (int)(len > split_min ? len : split_min);
+}
+// The same count in 32-bit arithmetic, for totals below 2^31 - split_cap (one row per
+// lane when a decode launch numbers its units densely).
+__device__ __forceinline__ int split_plan_count32(int total, int split_min, int split_div, int split_cap) {
+  int d = (total + split_cap - 1) / split_cap;
+  d = d > split_div ? d : split_div;
+  d = d > 0 ? d : 1;
+  int len = ((total + d - 1) / d + 63) & ~63;
+  len = len > split_min ? len : split_min;
+  const int n = (total + len - 1) / len;
+  return n > 0 ? n : 1;
 }
 __host__ __device__ __forceinline__ int split_plan_count(int64_t total, int split_min, int split_div, int split_cap) {
   const int64_t len = split_plan_len(total, split_min, split_div, split_cap);

@@ -495,6 +495,41 @@ def test_decode_batch_invariance_beyond_16_full_chunks():
     check_out(f64(full.out[:1]), step["out"], cfg.act, "hca decode, 35,128-item row vs the oracle")
 
 
+def test_decode_dense_unit_numbering():
+    """An HCA decode launch whose padded unit space exceeds the CUs (48 rows x 6 chunks)
+    numbers its real units densely, so rows with fewer chunks leave no gaps: every row,
+    decoded alone (a small launch, padded numbering), gives bitwise the batch's output,
+    and the longest row matches the oracle.  The CSA launch of the same shape (56 rows x
+    5 chunks, padded numbering with gaps for the short rows) is checked the same way."""
+    ca, configs, layers, synth = _ca()
+    for layer, B, seed in (("hca", 48, 781), ("csa", 56, 782)):
+        cfg = _cfg(name=f"dense_{layer}", phase="decode", kv="fp8mix", n_h=64, k=1024, m_hca=16, B=B,
+                   ctx_lo=100, ctx_hi=20000, L=0, seed=seed)
+        ctx = synth.decode_contexts(cfg)
+        ctx[0] = 20000
+        inp = synth.decode_layer(cfg, layer, "cuda", ctx)
+        full = layers.DecodeLayer(cfg, inp)
+        full.step()
+        torch.cuda.synchronize()
+        n_items = [(min(int(c) // cfg.m, cfg.k) if layer == "csa" else int(c) // cfg.m_hca) + min(int(c) + 1, cfg.n_win)
+                   for c in ctx]
+        chunks = [ca.attend_decode_plan(full.ap, n)[1] for n in n_items]
+        log(f"[dense numbering] {layer}: {B} rows, chunks per row {sorted(chunks)}")
+        assert B * max(chunks) > 256 and min(chunks) < max(chunks)
+        ref = full.out.view(torch.int16).clone()
+        for b in range(B):
+            one = layers.DecodeLayer(cfg, _single_sequence(inp, b))
+            one.step()
+            torch.cuda.synchronize()
+            assert torch.equal(ref[b], one.out[0].view(torch.int16)), f"{layer} row {b}: output differs from the row alone"
+            if layer == "csa":
+                assert torch.equal(full.idx[b], one.idx[0]), f"csa row {b}: index list differs"
+        if layer == "hca":
+            st = opl.decode_state(cfg, inp, seqs=[0])
+            step = opl.hca_decode_step(cfg, inp, st, seqs=[0])
+            check_out(f64(full.out[:1]), step["out"], cfg.act, "hca decode, longest row of the dense launch vs the oracle")
+
+
 def test_out_of_contract_positions_raise_the_status_word():
     """A decode row whose position exceeds the call's max_pos (or is negative) is kept empty
     and raises CA_STATUS_POS_RANGE in the caller's status word; the other rows are unchanged.
