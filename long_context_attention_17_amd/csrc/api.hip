@@ -488,6 +488,9 @@ static int attend_common(const ca_attend_params* p, const void* q, const float* 
   if (decode && n_rows > kv->n_seqs) return fail(CA_ERR_ARG, "%s: more rows than page table rows", what);
   if (decode && W < p->n_win) return fail(CA_ERR_ARG, "%s: window ring W = %d < n_win = %d", what, W, p->n_win);
   if (max_pos > 0x7FFFFFFF) return fail(CA_ERR_ARG, "%s: max_pos beyond 2^31 - 1", what);
+  // the kernels take a row's split plan in 32-bit arithmetic
+  if (max_items_of(max_pos, p->n_win, mode == 0 ? k : 0, ratio) > 0x7FFFFFFF - 4096)
+    return fail(CA_ERR_UNSUPPORTED, "%s: a row may hold 2^31 - 4096 or more items", what);
   if (mode == 1 && max_pos / ratio > (int64_t)kv->max_pages * kv->page_size)
     return fail(CA_ERR_ARG, "%s: page table holds fewer than floor(max_pos/ratio) entries", what);
   // the attention kernels address an item by pool record index (page * page_size + slot) or

@@ -86,14 +86,14 @@ __device__ __forceinline__ const uint8_t* item_ptr(const AttendArgs& a, const Ro
 // Split length of a row of `total` items: a function of the row alone (never
 // longer than split_cap).
 __device__ __forceinline__ int split_len_of(const AttendArgs& a, int total) {
-  return split_plan_len(total, a.split_min, a.split_div, a.split_cap);
+  return split_plan_len32(total, a.split_min, a.split_div, a.split_cap);
 }
 
 // Splits of a row.  Rows within the call's max_pos never need more than the
 // workspace holds (plan_max_splits); the cap only guards the workspace.
 __device__ __forceinline__ int n_splits_of(const AttendArgs& a, int total) {
   if (a.split_min <= 0) return 1;
-  const int n = split_plan_count(total, a.split_min, a.split_div, a.split_cap);
+  const int n = split_plan_count32(total, a.split_min, a.split_div, a.split_cap);
   return n < a.max_splits ? n : a.max_splits;
 }
 

@@ -139,14 +139,17 @@ __host__ __device__ __forceinline__ int split_plan_len(int64_t total, int split_
   len = (len + 63) & ~(int64_t)63;
   return (int)(len > split_min ? len : split_min);
 }
-// The same count in 32-bit arithmetic, for totals below 2^31 - split_cap (one row per
-// lane when a decode launch numbers its units densely).
-__device__ __forceinline__ int split_plan_count32(int total, int split_min, int split_div, int split_cap) {
+// The same plan in 32-bit arithmetic for the kernels (a row's item count stays below
+// 2^31 - split_cap; 64-bit divisions are long instruction sequences on the GPU).
+__device__ __forceinline__ int split_plan_len32(int total, int split_min, int split_div, int split_cap) {
   int d = (total + split_cap - 1) / split_cap;
   d = d > split_div ? d : split_div;
   d = d > 0 ? d : 1;
-  int len = ((total + d - 1) / d + 63) & ~63;
-  len = len > split_min ? len : split_min;
+  const int len = ((total + d - 1) / d + 63) & ~63;
+  return len > split_min ? len : split_min;
+}
+__device__ __forceinline__ int split_plan_count32(int total, int split_min, int split_div, int split_cap) {
+  const int len = split_plan_len32(total, split_min, split_div, split_cap);
   const int n = (total + len - 1) / len;
   return n > 0 ? n : 1;
 }
