@@ -144,9 +144,14 @@ struct KeyGroup {
 // bytes [32h, 32h + 32).  FP4 pages: lane half h takes the bytes [16h, 16h + 16)
 // (channels 32h .. 32h + 31) and the E8M0 byte of block h.  NT: e4m3 code bytes
 // loaded as non-temporal (keys read once per call, as in decode).
+// Every lane loads, unconditionally: a lane without a key (past k1, or on a missing
+// page) reads the same bytes of `dummy` (at least 64 B of readable device memory)
+// and its key is masked by ok.  Unconditional loads let the compiler count them,
+// so the waits in the scoring loop are for one block's loads, not for every load in
+// flight.
 template <int KF, int G, bool NT>
 __device__ __forceinline__ void load_key_group(const CacheView& cv, int wpg, int64_t wbase, int64_t k1,
-                                               int64_t gbase, int lane, KeyGroup<G>& kg) {
+                                               int64_t gbase, int lane, const uint8_t* dummy, KeyGroup<G>& kg) {
   constexpr int cI = 64;
 #pragma unroll
   for (int u = 0; u < G; ++u) {
@@ -154,22 +159,19 @@ __device__ __forceinline__ void load_key_group(const CacheView& cv, int wpg, int
     const int pgv = __shfl(wpg, (int)((s >> cv.page_shift) - (wbase >> cv.page_shift)), 64);
     const int pg = s < k1 ? pgv : -1;
     kg.ok[u] = pg >= 0;
-    kg.v0[u] = i32x4{0, 0, 0, 0};
-    kg.v1[u] = kg.v0[u];
-    kg.ks[u] = 0.0f;
-    kg.sc[u] = 127;
-    if (kg.ok[u]) {
-      const uint8_t* base = cv.pool + (int64_t)pg * cv.page_bytes;
-      const int slot = cv.slot_of(s);
-      if constexpr (KF == CA_FP4) {
-        kg.v0[u] = *(const i32x4*)(base + slot * (cI / 2) + 16 * (lane >> 5));
-        kg.sc[u] = base[((cI / 2) << cv.page_shift) + slot * (cI / 32) + (lane >> 5)];
-      } else {
-        const i32x4* kp = (const i32x4*)(base + slot * cI + 32 * (lane >> 5));
-        kg.v0[u] = NT ? __builtin_nontemporal_load(kp) : kp[0];
-        kg.v1[u] = NT ? __builtin_nontemporal_load(kp + 1) : kp[1];
-        kg.ks[u] = ((const float*)(base + (cI << cv.page_shift)))[slot];
-      }
+    const uint8_t* base = cv.pool + (int64_t)(kg.ok[u] ? pg : 0) * cv.page_bytes;
+    const int slot = kg.ok[u] ? cv.slot_of(s) : 0;
+    if constexpr (KF == CA_FP4) {
+      const uint8_t* kp = kg.ok[u] ? base + slot * (cI / 2) + 16 * (lane >> 5) : dummy + 16 * (lane >> 5);
+      const uint8_t* sp = kg.ok[u] ? base + ((cI / 2) << cv.page_shift) + slot * (cI / 32) + (lane >> 5) : dummy;
+      kg.v0[u] = *(const i32x4*)kp;
+      kg.sc[u] = *sp;
+    } else {
+      const i32x4* kp = (const i32x4*)(kg.ok[u] ? base + slot * cI + 32 * (lane >> 5) : dummy + 32 * (lane >> 5));
+      const float* sp = kg.ok[u] ? (const float*)(base + (cI << cv.page_shift)) + slot : (const float*)dummy;
+      kg.v0[u] = NT ? __builtin_nontemporal_load(kp) : kp[0];
+      kg.v1[u] = NT ? __builtin_nontemporal_load(kp + 1) : kp[1];
+      kg.ks[u] = *sp;
     }
   }
 }
@@ -212,6 +214,8 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+constexpr int kIdxWaitVm0 = 0x0F70;     // s_waitcnt immediate: vmcnt(0), other counters unconstrained
+
 template <int QPW, int KF, int QF>
 __device__ __forceinline__ void index_scores_mfma(CacheView cv, int m, int q_fmt, const void* qI, const float* w,
                                                   RowPos pos, int seq_fixed, int n_rows, float* scores,
@@ -232,8 +236,10 @@ __device__ __forceinline__ void index_scores_mfma(CacheView cv, int m, int q_fmt
   // The prologue's loads go out together, each from an in-range address, and only
   // then are they used: the rows' pos words (first: the first to be waited for), the
   // pool pages of the wavefront's 1,024 keys (lane i: page i; at most 64 as
-  // page_shift >= 4; validity applied when used) and the query rows (rows past the
-  // group's queries read row r0 and are zeroed).
+  // page_shift >= 4; validity applied when used), the query rows and their head
+  // weights (rows past the group's queries read row r0 and are zeroed).  All of them
+  // are older than the key loads, so waiting for them never waits for a key group
+  // (loads complete in order).
   int praw[QPW];
 #pragma unroll
   for (int qq = 0; qq < QPW; ++qq)
@@ -245,6 +251,7 @@ __device__ __forceinline__ void index_scores_mfma(CacheView cv, int m, int q_fmt
   const int praw_pg = cv.max_pages > 0 ? cv.page_table[(int64_t)seq * cv.max_pages + (pi_ok ? pi : 0)] : -1;
   constexpr int kRowsPerWave = 32 / 4;                 // query-head rows (query, head) of each wave
   uint32_t qraw[kRowsPerWave];                         // as loaded: bf16 bits or fp32 bits
+  float wraw[kRowsPerWave];                            // the rows' head weights
   const bool q_bf16 = q_fmt == CA_BF16;
 #pragma unroll
   for (int j = 0; j < kRowsPerWave; ++j) {
@@ -252,6 +259,7 @@ __device__ __forceinline__ void index_scores_mfma(CacheView cv, int m, int q_fmt
     const bool ok = qq < QPW && r < n_rows;
     const int64_t i = ((int64_t)(ok ? r : r0) * nI + h) * cI + lane;
     qraw[j] = q_bf16 ? (uint32_t)((const uint16_t*)qI)[i] : ((const uint32_t*)qI)[i];
+    wraw[j] = w[(int64_t)(ok ? r : r0) * nI + h];
   }
 
   int64_t ne[QPW];
@@ -278,10 +286,18 @@ __device__ __forceinline__ void index_scores_mfma(CacheView cv, int m, int q_fmt
   constexpr int kGroups = kScoreChunk / 4 / kGroupKeys;  // groups per wave
   static_assert(kGroups >= 2, "two key groups in flight");
   constexpr bool kEarly = QPW == 1;
+  // the source of lanes without a key: the first 64 B of the query rows (a row holds
+  // nI * cI = 512 elements of at least 2 B), always readable
+  const uint8_t* kdummy = (const uint8_t*)qI;
   KeyGroup<G> cur, nxt;
   if constexpr (kEarly) {
-    load_key_group<KF, G, kEarly>(cv, wpg, wbase, k1, wbase, lane, cur);
-    load_key_group<KF, G, kEarly>(cv, wpg, wbase, k1, wbase + kGroupKeys, lane, nxt);
+    // every prologue load has arrived (the query words land with the page ids the key
+    // loads need): waited for here, as a builtin the compiler sees, no wait on them is
+    // left for after the key loads, where it would be a wait for the key groups too
+    // (the compiler cannot count the key loads, issued under conditions)
+    __builtin_amdgcn_s_waitcnt(kIdxWaitVm0);
+    load_key_group<KF, G, kEarly>(cv, wpg, wbase, k1, wbase, lane, kdummy, cur);
+    load_key_group<KF, G, kEarly>(cv, wpg, wbase, k1, wbase + kGroupKeys, lane, kdummy, nxt);
   }
 
   // prologue: QPW*8 query-head rows quantized to e4m3
@@ -301,11 +317,11 @@ __device__ __forceinline__ void index_scores_mfma(CacheView cv, int m, int q_fmt
         const uint32_t odd = __shfl_xor(code, 1, 64);
         if ((lane & 1) == 0) qcodes[row * kQBytes + (lane >> 1)] = (uint8_t)(code | (odd << 4));
         if ((lane & 31) == 0) qsc[row][lane >> 5] = (uint8_t)(e + 127);
-        if (lane == 0) wq[row] = w[(int64_t)r * nI + h];
+        if (lane == 0) wq[row] = wraw[j];
       } else {
         const int e = pow2_exponent(wave_max(fabsf(v)));
         qcodes[row * cI + lane] = (uint8_t)e4m3_encode(ldexpf(v, -e));
-        if (lane == 0) wq[row] = w[(int64_t)r * nI + h] * ldexpf(1.0f, e);
+        if (lane == 0) wq[row] = wraw[j] * ldexpf(1.0f, e);
       }
     } else {
       if (lane < kQBytes) qcodes[row * kQBytes + lane] = 0;
@@ -344,39 +360,68 @@ __device__ __forceinline__ void index_scores_mfma(CacheView cv, int m, int q_fmt
 #pragma unroll
     for (int v = 0; v < 4; ++v) wl[qq][v] = wq[qq * nI + 4 * (lane >> 5) + v];
 
-  if constexpr (!kEarly) load_key_group<KF, G, kEarly>(cv, wpg, wbase, k1, wbase, lane, cur);
-  for (int grp = 0; grp < kGroups; ++grp) {
-    const int64_t gbase = wbase + kGroupKeys * grp;
-    if (gbase >= k1) break;
-    if (!kEarly && grp + 1 < kGroups) load_key_group<KF, G, kEarly>(cv, wpg, wbase, k1, gbase + kGroupKeys, lane, nxt);
+  // scores of one key group held in kg (keys gbase ..): block u + 1's MFMA is issued
+  // before block u's results are read (two accumulators), so the matrix unit's latency
+  // overlaps the ReLU, weighting and stores
+  auto block_mfma = [&](const KeyGroup<G>& kg, int u) {
+    const i32x8 bop = __builtin_shufflevector(kg.v0[u], kg.v1[u], 0, 1, 2, 3, 4, 5, 6, 7);
+    const f32x16 z = {};
+    if constexpr (QF == CA_FP4)
+      return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bop, z, 4, 4, 0, a_scale, 0, kg.sc[u]);
+    else if constexpr (KF == CA_FP4)
+      return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bop, z, 0, 4, 0, 127, 0, kg.sc[u]);
+    else
+      return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bop, z, 0, 0, 0, 127, 0, 127);
+  };
+  auto score_group = [&](const KeyGroup<G>& kg, int64_t gbase) {
+    f32x16 acc_next = block_mfma(kg, 0);
 #pragma unroll
     for (int u = 0; u < G; ++u) {
       const int64_t s = gbase + 32 * u + (lane & 31);
-      const i32x8 bop = __builtin_shufflevector(cur.v0[u], cur.v1[u], 0, 1, 2, 3, 4, 5, 6, 7);
-      f32x16 acc = {};
-      if constexpr (QF == CA_FP4)
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bop, acc, 4, 4, 0, a_scale, 0, cur.sc[u]);
-      else if constexpr (KF == CA_FP4)
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bop, acc, 0, 4, 0, 127, 0, cur.sc[u]);
-      else
-        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, bop, acc, 0, 0, 0, 127, 0, 127);
+      const f32x16 acc = acc_next;
+      if (u + 1 < G) acc_next = block_mfma(kg, u + 1);
       // acc[v]: row 8*(v/4) + 4*(lane/32) + v%4 = (query v/4, head 4*(lane/32) + v%4), key lane%32
 #pragma unroll
       for (int qq = 0; qq < QPW; ++qq) {
         float part = 0.0f;
 #pragma unroll
         for (int v = 0; v < 4; ++v) part += wl[qq][v] * fmaxf(acc[4 * qq + v], 0.0f);
-        part += __shfl_xor(part, 32, 64);
+        // the two lane halves' heads: lanes l and l + 32 both get part(l % 32) + part(l % 32 + 32)
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+        part = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
         if (lane < 32 && s < ne[qq]) {
-          const float sc = cur.ok[u] ? (KF == CA_FP4 ? part : part * cur.ks[u]) : -INFINITY;
+          const float sc = kg.ok[u] ? (KF == CA_FP4 ? part : part * kg.ks[u]) : -INFINITY;
           scores[(int64_t)(r0 + qq) * stride + s] = sc;
           if (want_hist) atomicAdd(&hs[order_key(sc) >> 20], 1u);
         }
       }
     }
-    cur = nxt;
-    if (kEarly && grp + 2 < kGroups)   // groups grp + 1 and grp + 2 in flight while grp + 1 is scored
-      load_key_group<KF, G, kEarly>(cv, wpg, wbase, k1, gbase + 2 * kGroupKeys, lane, nxt);
+  };
+  if constexpr (kEarly) {
+    // Decode: two groups in flight (the first two already issued), taken in turn by the
+    // two register buffers (no copy between them, which would wait for the loads in
+    // flight).
+    static_assert(kGroups % 2 == 0, "key groups go in pairs");
+    for (int grp = 0; grp < kGroups; grp += 2) {
+      const int64_t g0 = wbase + kGroupKeys * grp, g1 = g0 + kGroupKeys;
+      if (g0 >= k1) break;
+      score_group(cur, g0);
+      if (grp + 2 < kGroups) load_key_group<KF, G, kEarly>(cv, wpg, wbase, k1, g1 + kGroupKeys, lane, kdummy, cur);
+      if (g1 >= k1) break;
+      score_group(nxt, g1);
+      if (grp + 3 < kGroups) load_key_group<KF, G, kEarly>(cv, wpg, wbase, k1, g1 + 2 * kGroupKeys, lane, kdummy, nxt);
+    }
+  } else {
+    // Prefill row groups (four query rows): one group ahead; two buffers taken in turn
+    // need more registers than two wavefronts per SIMD leave
+    load_key_group<KF, G, kEarly>(cv, wpg, wbase, k1, wbase, lane, kdummy, cur);
+    for (int grp = 0; grp < kGroups; ++grp) {
+      const int64_t gbase = wbase + kGroupKeys * grp;
+      if (gbase >= k1) break;
+      if (grp + 1 < kGroups) load_key_group<KF, G, kEarly>(cv, wpg, wbase, k1, gbase + kGroupKeys, lane, kdummy, nxt);
+      score_group(cur, gbase);
+      cur = nxt;
+    }
   }
   if (want_hist) {   // the chunk's nonzero bins into the row's histogram (integer adds: order free)
     __syncthreads();
