@@ -194,16 +194,26 @@ __device__ __forceinline__ void load_key_group(const CacheView& cv, int wpg, int
 // A chunk's LDS histogram hb[4096] (complete: after a barrier) into the row's state g:
 // the nonzero fine bins, and the 64 coarse bins (fine bins 64c .. 64c + 63 summed) that
 // follow the state's 4 counters.  256 threads; integer adds, so order free.
+// 256 threads.  Fine bins: thread t adds bins t, t + 256, ... (a wavefront's atomics
+// cover 64 consecutive bins each).  Coarse bins: thread t sums the fine bins
+// 16t .. 16t + 15 (four 16-byte LDS reads; hb 16-byte aligned), which lie in coarse
+// bin t / 4, and the four threads of a coarse bin add their sums with two lane swaps.
 __device__ __forceinline__ void add_row_histogram(const uint32_t* hb, uint32_t* g) {
-  for (int i = threadIdx.x; i < 4096; i += 256) {
+  const int t = threadIdx.x;
+  for (int i = t; i < 4096; i += 256) {
     const uint32_t c = hb[i];
     if (c) atomicAdd(&g[i], c);
   }
-  if (threadIdx.x < 64) {
-    uint32_t c = 0;
-    for (int i = 0; i < 64; ++i) c += hb[64 * threadIdx.x + ((i + threadIdx.x) & 63)];   // staggered: no bank clash
-    if (c) atomicAdd(&g[4096 + 4 + threadIdx.x], c);
-  }
+  const u32x4* src = (const u32x4*)hb + 4 * t;
+  u32x4 c[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c[i] = src[i];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sum += (c[i][0] + c[i][1]) + (c[i][2] + c[i][3]);
+  sum += __shfl_xor(sum, 1, 64);
+  sum += __shfl_xor(sum, 2, 64);
+  if ((t & 3) == 0 && sum) atomicAdd(&g[4096 + 4 + (t >> 2)], sum);
 }
 
 // Workgroup barrier ordering LDS only: global loads in flight stay in flight
@@ -223,7 +233,7 @@ __device__ __forceinline__ void index_scores_mfma(CacheView cv, int m, int q_fmt
   static_assert(QF == CA_E4M3 || (QF == CA_FP4 && KF == CA_FP4), "FP4 queries meet FP4 keys");
   constexpr int nI = 8, cI = 64;
   constexpr int kQBytes = QF == CA_FP4 ? cI / 2 : cI;              // code bytes per query-head row
-  extern __shared__ uint32_t hs[];
+  extern __shared__ __attribute__((aligned(16))) uint32_t hs[];
   __shared__ __attribute__((aligned(16))) uint8_t qcodes[32 * cI];  // A operand rows: (query, head)
   __shared__ uint8_t qsc[32][2];                                    // FP4 queries: E8M0 byte per block
   __shared__ float wq[32];                                          // w (* query scale for e4m3) per row
@@ -658,7 +668,7 @@ __device__ __forceinline__ int64_t row_len(RowPos pos, int r, int m, int64_t str
 
 __global__ void __launch_bounds__(256) topk_hist_kernel(const float* scores, int64_t stride, RowPos pos,
                                                         int m, int k, uint32_t* state) {
-  __shared__ uint32_t h[kHistBins];
+  __shared__ __attribute__((aligned(16))) uint32_t h[kHistBins];
   const int r = blockIdx.x, tid = threadIdx.x;
   const int64_t n = row_len(pos, r, m, stride);
   const int64_t c0 = (int64_t)blockIdx.y * kChunk;
