@@ -313,7 +313,7 @@ __device__ __forceinline__ void index_scores_mfma(CacheView cv, int m, int q_fmt
   // prologue: QPW*8 query-head rows quantized to e4m3
 #pragma unroll
   for (int j = 0; j < kRowsPerWave; ++j) {
-    const int row = wave + 4 * j, qq = row / nI, h = row % nI, r = r0 + qq;
+    const int row = wave + 4 * j, qq = row / nI, r = r0 + qq;
     if (qq < QPW && r < n_rows) {                      // (uniform) rows past the group's queries stay zero
       const float v = __uint_as_float(q_bf16 ? qraw[j] << 16 : qraw[j]);
       if constexpr (QF == CA_FP4) {
