@@ -273,3 +273,23 @@ def test_attention_rejects_pools_and_windows_beyond_31_bit_item_indices():
     big = (1 << 31) // 64                           # pages of 64 records: 2^31 records
     assert hca_decode(big, 128) == -3 and "records" in lib.ca_last_error().decode()
     assert hca_decode(big - 1, (1 << 31) // 8, B=8) == -3 and "window" in lib.ca_last_error().decode()
+
+
+def test_attention_rejects_rows_beyond_the_32_bit_split_plan():
+    """The kernels take a row's split plan in 32-bit arithmetic: a call whose rows may hold
+    2^31 - 4,096 or more items (here CSA with k near 2^31) is refused on the host before
+    any launch (fake, never dereferenced addresses); k + n_win below the limit passes
+    that check and fails later on the workspace instead."""
+    from long_context_attention_17_amd import binding as ca
+    lib = ca.lib()
+    fake = 1 << 20
+    p = ca.AttendParams(64, 512, 64, 128, ca.BF16, ca.BF16, ca.BF16, 512 ** -0.5, 1e-6, 1e4, None)
+    c = ca._Cache(ca.FP8MIX, 512, 64, 64, fake, 16, fake, 1, 16)
+
+    def csa_decode(k):
+        return lib.ca_csa_attend_decode(ctypes.byref(p), fake, fake, ctypes.byref(c), fake, fake, k, 4, fake, 1, 1024,
+                                        fake, 128, fake, fake, None, None, 0, None)
+
+    assert csa_decode((1 << 31) - 1024) == -3 and "2^31 - 4096 or more items" in lib.ca_last_error().decode()
+    rc = csa_decode((1 << 31) - 4096 - 256)
+    assert rc != 0 and "2^31 - 4096" not in lib.ca_last_error().decode()
