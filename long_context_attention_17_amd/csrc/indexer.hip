@@ -712,6 +712,7 @@ __global__ void __launch_bounds__(256) topk_gather_kernel(const float* scores, i
                                                           uint32_t* cand_idx) {
   __shared__ uint32_t part[4];
   __shared__ uint32_t base_s, bstar_s;
+  __shared__ uint32_t fine[kHistBins];
   const int r = blockIdx.x, tid = threadIdx.x;
   const int64_t n = row_len(pos, r, m, stride);
   const int64_t c0 = (int64_t)blockIdx.y * kChunk;
@@ -719,9 +720,15 @@ __global__ void __launch_bounds__(256) topk_gather_kernel(const float* scores, i
   uint32_t* g = state + (int64_t)r * kRowWords;
   uint32_t* meta = g + kHistBins;
   const float* row = scores + (int64_t)r * stride;
-  // thread tid owns the chunk's keys tid + 256 i; all their loads go out first (slots
-  // past n re-read key n - 1 and are never used)
+  // One round trip for everything the workgroup reads, all loads unconditional: the
+  // row's coarse bins (lane l of each wavefront: bin l), its 4,096 fine bins (thread tid:
+  // bins tid + 256 j, staged in LDS) and the chunk's scores (thread tid: keys tid + 256 i;
+  // slots past n re-read key n - 1 and are never used)
   constexpr int kPer = kChunk / 256;
+  const uint32_t cw = meta[kMetaWords + (tid & 63)];
+  uint32_t fw[kHistBins / 256];
+#pragma unroll
+  for (int j = 0; j < kHistBins / 256; ++j) fw[j] = g[tid + 256 * j];
   const int64_t s0 = c0 + tid;
   float v[kPer];
 #pragma unroll
@@ -729,19 +736,18 @@ __global__ void __launch_bounds__(256) topk_gather_kernel(const float* scores, i
     const int64_t s = s0 + 256 * i;
     v[i] = row[s < n ? s : n - 1];
   }
-  uint32_t keys[kPer];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i) keys[i] = order_key(v[i]);
+  for (int j = 0; j < kHistBins / 256; ++j) fine[tid + 256 * j] = fw[j];
+  lds_barrier();
   // the threshold bin b* of the row (every workgroup of the row finds the same one; the
   // first also records it, and the count of keys above it, for the resolve launch):
   // wavefront 0 finds the coarse bin holding the k-th largest key from the 64 coarse
   // bins, then b* among that coarse bin's 64 fine bins
   if (tid < 64) {
-    const uint32_t* coarse = meta + kMetaWords;
     uint32_t cbin, above_c;
-    top_bin_of_64(coarse[tid], (uint32_t)k, &cbin, &above_c);
+    top_bin_of_64(cw, (uint32_t)k, &cbin, &above_c);
     uint32_t fbin, above_f;
-    top_bin_of_64(g[64 * cbin + tid], (uint32_t)k - above_c, &fbin, &above_f);
+    top_bin_of_64(fine[64 * cbin + tid], (uint32_t)k - above_c, &fbin, &above_f);
     if (tid == 0) {
       bstar_s = 64 * cbin + fbin;
       if (blockIdx.y == 0) {
@@ -750,8 +756,11 @@ __global__ void __launch_bounds__(256) topk_gather_kernel(const float* scores, i
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
   const uint32_t bstar = bstar_s;
+  uint32_t keys[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) keys[i] = order_key(v[i]);
   uint32_t mine = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) mine += (s0 + 256 * i < n && (keys[i] >> 20) >= bstar) ? 1u : 0u;
@@ -829,6 +838,22 @@ __global__ void __launch_bounds__(kResolveThreads) topk_resolve_kernel(const flo
   __shared__ uint32_t sel[2];
   __shared__ __attribute__((aligned(16))) uint32_t bm_lds[2 * kBitmapLdsWords];
   const int r = blockIdx.x, tid = threadIdx.x;
+  const uint32_t* meta = state + (int64_t)r * kRowWords + kHistBins;
+  const uint32_t* gk = cand_key + (int64_t)r * stride;
+  const uint32_t* gi = cand_idx + (int64_t)r * stride;
+  // the first kRegCand * kResolveThreads candidate slots go into registers (kept for all
+  // three passes over them) in the same round trip as the row's position and counters:
+  // the slots lie inside the row's candidate arrays (stride > kTopkLdsKeys > kRegCand *
+  // kResolveThreads), and those at or past the candidate count are masked once it is
+  // known (a row that needs no resolve never reads them)
+  static_assert(kRegCand * kResolveThreads <= kTopkLdsKeys, "speculative candidate slots inside the row");
+  uint32_t rk[kRegCand], ri[kRegCand];
+#pragma unroll
+  for (int j = 0; j < kRegCand; ++j) {
+    rk[j] = gk[tid + j * kResolveThreads];
+    ri[j] = gi[tid + j * kResolveThreads];
+  }
+  const uint32_t nc = meta[0], bstar = meta[2], above = meta[3];
   const int64_t n = row_len(pos, r, m, stride);
   const float* row = scores + (int64_t)r * stride;
   int32_t* oi = out_idx + (int64_t)r * k;
@@ -841,20 +866,6 @@ __global__ void __launch_bounds__(kResolveThreads) topk_resolve_kernel(const flo
     if (tid == 0) out_cnt[r] = (int32_t)n;
     return;
   }
-  const uint32_t* meta = state + (int64_t)r * kRowWords + kHistBins;
-  const uint32_t* gk = cand_key + (int64_t)r * stride;
-  const uint32_t* gi = cand_idx + (int64_t)r * stride;
-  // the first kRegCand * kResolveThreads candidate slots go into registers (kept for all
-  // three passes over them) in the same round trip as the row's counters: the slots lie
-  // inside the row's candidate arrays (stride > kTopkLdsKeys > kRegCand * kResolveThreads),
-  // and those at or past the candidate count are masked once it is known
-  static_assert(kRegCand * kResolveThreads <= kTopkLdsKeys, "speculative candidate slots inside the row");
-  uint32_t rk[kRegCand], ri[kRegCand];
-#pragma unroll
-  for (int j = 0; j < kRegCand; ++j) {
-    rk[j] = gk[tid + j * kResolveThreads];
-    ri[j] = gi[tid + j * kResolveThreads];
-  }
   // bitmaps of the row's indices: kept (keys > T, then the chosen ties) and equal to T,
   // each a multiple of 4 words, read and cleared 16 B at a time; cleared while the
   // loads are in flight (the radix passes' barriers order it before the first use)
@@ -863,7 +874,6 @@ __global__ void __launch_bounds__(kResolveThreads) topk_resolve_kernel(const flo
   uint32_t* keep = bm;
   uint32_t* eq = bm + words;
   for (int64_t i = tid; i < 2 * words / 4; i += blockDim.x) ((u32x4*)bm)[i] = u32x4{0u, 0u, 0u, 0u};
-  const uint32_t nc = meta[0], bstar = meta[2], above = meta[3];
 #pragma unroll
   for (int j = 0; j < kRegCand; ++j)
     if (tid + j * kResolveThreads >= nc) rk[j] = ri[j] = 0u;
