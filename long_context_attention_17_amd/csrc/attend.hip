@@ -340,21 +340,23 @@ __global__ void __launch_bounds__(512) attend_combine_acc_kernel(AttendArgs a) {
     return load_part_run<BF>(a, e);
   };
   // Every load goes out before anything waits on the row's split count: the row's
-  // position and count words, the sinks, the first
-  // splits' partial runs and this thread's (m, l) pairs (head hh, splits g and g + 8),
-  // all within the workspace's max_splits; those of splits the row does not have are
-  // never used (past max_splits: split max_splits - 1 again).
+  // position and count words, the sinks, this thread's (m, l) pairs (head hh, splits g
+  // and g + 8) and the first splits' partial runs, all within the workspace's
+  // max_splits; those of splits the row does not have are never used (past max_splits:
+  // split max_splits - 1 again).
   const int hh = t & 63, g = t >> 6;
   const int pos_r = a.pos != nullptr ? a.pos[r] : 0, cnt_r = a.mode == 0 ? a.cnt[r] : 0;
   const float sink_h = a.sink[hg * 64 + hh] * kLog2e;
   const float sink_own = a.sink[h] * kLog2e;
+  // (m, l) pairs first and unconditionally (splits past max_splits read the last one,
+  // never used): the reduction that needs them then waits for them alone, the partial
+  // runs behind them staying in flight (loads complete in order)
+  const int64_t base = ((int64_t)r * n_ms) * a.n_heads + hg * 64 + hh;
+  const f32x2 ml0 = *(const f32x2*)(a.part_ml + 2 * (base + (int64_t)(g < n_ms ? g : n_ms - 1) * a.n_heads));
+  const f32x2 ml1 = *(const f32x2*)(a.part_ml + 2 * (base + (int64_t)(g + 8 < n_ms ? g + 8 : n_ms - 1) * a.n_heads));
   PartRun<BF> os[kCombineUnroll];
 #pragma unroll
   for (int s = 0; s < kCombineUnroll; ++s) os[s] = o_at(s < n_ms ? s : n_ms - 1);
-  const int64_t base = ((int64_t)r * n_ms) * a.n_heads + hg * 64 + hh;
-  const f32x2 ml0 = g < n_ms ? *(const f32x2*)(a.part_ml + 2 * (base + (int64_t)g * a.n_heads)) : f32x2{0.0f, 0.0f};
-  const f32x2 ml1 =
-      g + 8 < n_ms ? *(const f32x2*)(a.part_ml + 2 * (base + (int64_t)(g + 8) * a.n_heads)) : f32x2{0.0f, 0.0f};
   const RowInfo ri = row_info_of(a, r, pos_r, cnt_r);
   const int ns = n_splits_of(a, ri.total);
 
