@@ -497,6 +497,11 @@ struct MxCfg {
   static constexpr int kLoadsPerWave = kRows / 4;       // one row per load instruction
 };
 
+// Prefill (one sequence per call) with bf16 entries: the sequence's page-table row is
+// copied to LDS once per workgroup (rows of up to kLdsPages pages), so that the units'
+// item tables need no global page-table loads.  (fp8 workgroups have no LDS left.)
+constexpr int kLdsPages = 2048;
+
 template <int KV_FMT>
 struct MxShared {
   typedef MxCfg<KV_FMT> C;
@@ -504,6 +509,7 @@ struct MxShared {
   __attribute__((aligned(16))) __bf16 tile[C::kFp8 ? kRows * kPitch : 8];
   __attribute__((aligned(16))) bf16x8 pex[4][64][2];    // probabilities of each wavefront (P^T fragments)
   uint32_t items[kMaxItems];            // item sources: pool record index, or kWinFlag | window row
+  int32_t pt[C::kFp8 ? 1 : kLdsPages];  // bf16 prefill: the sequence's page-table row
   uint32_t valid[C::kStages][4];        // bit u of valid[st][w]: ring row w + 4u holds a real item
   float tmx[4][32];                     // per-head tile max of each wavefront
   __attribute__((aligned(16))) int bump[4];   // wavefront wants to move its reference max
@@ -520,7 +526,7 @@ struct MxShared {
 constexpr int kTabGroup = 3;
 template <int MODE, class F>
 __device__ __forceinline__ void mx_item_table(const AttendArgs& a, const RowInfo& ri, int r, int j0, int n_tab,
-                                              uint32_t* items, const F& after_issue) {
+                                              uint32_t* items, const int32_t* pt_lds, const F& after_issue) {
   const int tid = threadIdx.x;
   n_tab = __builtin_amdgcn_readfirstlane(n_tab);
   if (n_tab <= 0) after_issue();
@@ -552,7 +558,8 @@ __device__ __forceinline__ void mx_item_table(const AttendArgs& a, const RowInfo
       for (int k = 0; k < kTabGroup; ++k) {
         const int v = e[k], pi = v >> a.kv.page_shift;
         ok[k] = v >= 0 && (MODE != 0 || v < ri.t / a.ratio) && pi < a.kv.max_pages;
-        x[k] = a.kv.page_table[(int64_t)ri.seq * a.kv.max_pages + (ok[k] ? pi : 0)];
+        x[k] = pt_lds != nullptr ? pt_lds[ok[k] ? pi : 0]
+                                 : a.kv.page_table[(int64_t)ri.seq * a.kv.max_pages + (ok[k] ? pi : 0)];
       }
       __builtin_amdgcn_sched_barrier(0);
       if (g0 == 0) after_issue();
@@ -981,6 +988,13 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
   };
 
   constexpr int kPrologueTiles = C::kFp8 ? 2 : 1;
+  // bf16 prefill: the sequence's page-table row in LDS (see kLdsPages)
+  const int32_t* pt_l = nullptr;
+  if (!C::kFp8 && a.seq_fixed >= 0 && a.kv.max_pages > 0 && a.kv.max_pages <= kLdsPages) {   // (uniform)
+    for (int i = tid; i < a.kv.max_pages; i += 256) sh.pt[i] = a.kv.page_table[(int64_t)a.seq_fixed * a.kv.max_pages + i];
+    __syncthreads();
+    pt_l = sh.pt;
+  }
   float m_force = kNoMax;                              // != kNoMax: recompute the unit with this reference
   for (int unit = blockIdx.x; unit < n_units; unit += gridDim.x) {
   int split, r, hg;
@@ -1016,9 +1030,9 @@ __global__ void __launch_bounds__(256) attend_mx_kernel(AttendArgs a) {
   const int n_tab = (j1 - j0) < kMaxItems ? (j1 - j0) : kMaxItems;
   if (q_row != r || q_hg != hg)   // (workgroup-uniform; two straight-line copies, so that
                                   // the wait for the table's loads does not wait for the queries)
-    mx_item_table<MODE>(a, ri, r, j0, n_tab, sh.items, [&]() { load_q(r, hg); });
+    mx_item_table<MODE>(a, ri, r, j0, n_tab, sh.items, pt_l, [&]() { load_q(r, hg); });
   else
-    mx_item_table<MODE>(a, ri, r, j0, n_tab, sh.items, []() {});
+    mx_item_table<MODE>(a, ri, r, j0, n_tab, sh.items, pt_l, []() {});
   // a valid, finite row used as the source of loads for rows without an item: the window token at t
   const uint8_t* dummy = (const uint8_t*)a.win + ((int64_t)ri.win_seq * a.W + ri.t % a.W) * kD * 2;
   __syncthreads();
