@@ -304,7 +304,7 @@ __device__ __forceinline__ void index_scores_mfma(CacheView cv, int m, int q_fmt
     // every prologue load has arrived (the query words land with the page ids the key
     // loads need): waited for here, as a builtin the compiler sees, no wait on them is
     // left for after the key loads, where it would be a wait for the key groups too
-    // (the compiler cannot count the key loads, issued under conditions)
+    // (loads complete in order)
     __builtin_amdgcn_s_waitcnt(kIdxWaitVm0);
     load_key_group<KF, G, kEarly>(cv, wpg, wbase, k1, wbase, lane, kdummy, cur);
     load_key_group<KF, G, kEarly>(cv, wpg, wbase, k1, wbase + kGroupKeys, lane, kdummy, nxt);
@@ -845,7 +845,7 @@ __global__ void __launch_bounds__(kResolveThreads) topk_resolve_kernel(const flo
   // three passes over them) in the same round trip as the row's position and counters:
   // the slots lie inside the row's candidate arrays (stride > kTopkLdsKeys > kRegCand *
   // kResolveThreads), and those at or past the candidate count are masked once it is
-  // known (a row that needs no resolve never reads them)
+  // known (a row that needs no resolve loads them too and leaves them unused)
   static_assert(kRegCand * kResolveThreads <= kTopkLdsKeys, "speculative candidate slots inside the row");
   uint32_t rk[kRegCand], ri[kRegCand];
 #pragma unroll
