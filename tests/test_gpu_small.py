@@ -160,6 +160,28 @@ def test_mfma_hca_prefill_bf16_ragged():
     run_hca_prefill(_cfg(L=1500, n_h=128))
 
 
+def test_prefill_page_tables_wider_than_the_lds_copy():
+    """Prefill attention takes a sequence's page-table row from an LDS copy when the table
+    holds at most 2,048 pages per sequence, else from global memory: the same CSA and HCA
+    prefills with the page table padded to 2,100 columns (-1) give bitwise the same
+    outputs (and, for CSA, index lists)."""
+    ca, configs, layers, synth = _ca()
+    for layer, cfg in (("csa", _cfg(name="wide_pt_csa", L=777, seed=4545)),
+                       ("hca", _cfg(name="wide_pt_hca", L=1500, m_hca=16, seed=4546))):
+        inp, pt, n_pool = _prefill_case(cfg, layer)
+        wide = torch.cat([pt, torch.full((1, 2100 - pt.shape[1]), -1, dtype=pt.dtype)], dim=1)
+        res = []
+        for table in (pt, wide):
+            gp = (layers.CSAPrefill if layer == "csa" else layers.HCAPrefill)(cfg, inp, table.cuda(), n_pool)
+            gp.run()
+            torch.cuda.synchronize()
+            res.append((gp.out.view(torch.int16).clone(), gp.idx.clone() if layer == "csa" else None))
+        log(f"[wide page table] {layer}: {pt.shape[1]} vs {wide.shape[1]} columns")
+        assert torch.equal(res[0][0], res[1][0]), f"{layer}: outputs differ with the wide page table"
+        if layer == "csa":
+            assert torch.equal(res[0][1], res[1][1]), "csa: index lists differ with the wide page table"
+
+
 def test_mfma_csa_prefill_fp4_indexer():
     """FP4 indexer keys: compressor store, scaled-MFMA scores and top-k against the oracle."""
     run_csa_prefill(_cfg(name="fp4_idx", idx="fp4", L=777, seed=4343))
