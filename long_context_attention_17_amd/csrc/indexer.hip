@@ -15,7 +15,7 @@
 // operands, whose E8M0 block scales the instruction applies itself.
 //
 // Top-k is exact and deterministic: fp32 scores map to order-preserving
-// 32-bit keys (-0 folded onto +0), a 4 x 8-bit radix select finds the k-th
+// 32-bit keys (-0 folded onto +0), a radix select (11-, 11- and 10-bit digits for one row in LDS, a 12-bit histogram then two 10-bit passes over the candidates for long rows) finds the k-th
 // largest key T and how many keys equal to T are needed, and an ordered
 // compaction (ballot prefix counts) emits every key > T plus the lowest-index
 // keys == T, in ascending index order.
@@ -463,10 +463,11 @@ __global__ void __launch_bounds__(256) index_scores_fp4_kernel(CacheView cv, int
 // ------------------------------------------------------------------ top-k
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkLdsKeys = 16384;
+constexpr int kTopkBins = 2048;         // radix digits of 11, 11 and 10 bits
 
 struct TopkShared {
   uint32_t keys[kTopkLdsKeys];
-  uint32_t hist[256];
+  __attribute__((aligned(16))) uint32_t hist[kTopkBins];
   uint32_t wsum[kTopkThreads / 64];
   uint32_t wsum2[kTopkThreads / 64];
   uint32_t sel_digit, sel_krem;
@@ -545,36 +546,48 @@ __global__ void __launch_bounds__(kTopkThreads) topk_rows_kernel(const float* sc
     }
   }
 
+  // three radix passes over the keys, on bits 31..21, 20..10 and 9..0
   uint32_t prefix = 0, krem = (uint32_t)k;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 8));
-    for (int i = tid; i < 256; i += blockDim.x) sh.hist[i] = 0;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const int width = pass == 2 ? 10 : 11;
+    const uint32_t hi_mask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + width));
+    const uint32_t dmask = (1u << width) - 1u;
+    for (int i = tid; i < kTopkBins; i += blockDim.x) sh.hist[i] = 0;
     __syncthreads();
     for (int64_t s = tid; s < n; s += blockDim.x) {
       uint32_t key = get_key(sh, in_lds, row, s);
-      if ((key & hi_mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+      if ((key & hi_mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
     }
     __syncthreads();
     if (tid < 64) {
-      // lane L owns digits 4L..4L+3; suffix counts from the top digit down
-      uint32_t c0 = sh.hist[4 * tid], c1 = sh.hist[4 * tid + 1], c2 = sh.hist[4 * tid + 2], c3 = sh.hist[4 * tid + 3];
-      uint32_t lsum = c0 + c1 + c2 + c3;
+      // lane L owns digits 32L .. 32L + 31 (eight 16-byte LDS reads); suffix counts from
+      // the top digit down; the one lane whose range holds the krem-th key walks it
+      const u32x4* hb = (const u32x4*)&sh.hist[32 * tid];
+      uint32_t lsum = 0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const u32x4 c = hb[q];
+        lsum += (c[0] + c[1]) + (c[2] + c[3]);
+      }
       uint32_t incl = lsum;  // inclusive suffix sum over lanes >= tid
       for (int o = 1; o < 64; o <<= 1) {
-        uint32_t v = __shfl_down(incl, o, 64);
+        const uint32_t v = __shfl_down(incl, o, 64);
         if (tid + o < 64) incl += v;
       }
-      uint32_t suffix_above = incl - lsum;
-      uint32_t cnts[4] = {c0, c1, c2, c3};
-      uint32_t cum = suffix_above;  // keys with digit > 4*tid+3
-      for (int d = 3; d >= 0; --d) {
-        uint32_t nc = cum + cnts[d];
-        if (cum < krem && nc >= krem) {
-          sh.sel_digit = 4 * tid + d;
-          sh.sel_krem = krem - cum;
+      uint32_t cum = incl - lsum;  // keys with digit > 32 * tid + 31
+      if (cum < krem && incl >= krem) {
+        for (int q = 7; q >= 0; --q) {
+          const u32x4 c = hb[q];
+          for (int e = 3; e >= 0; --e) {
+            const uint32_t nc = cum + c[e];
+            if (cum < krem && nc >= krem) {
+              sh.sel_digit = 32 * tid + 4 * q + e;
+              sh.sel_krem = krem - cum;
+            }
+            cum = nc;
+          }
         }
-        cum = nc;
       }
     }
     __syncthreads();
